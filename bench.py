@@ -1,0 +1,197 @@
+"""Headline benchmark: Ring AllReduce, fp32, 8 virtual ranks x 256 MiB, one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--algo ring|rhd|dbt] [--exec persistent|step]
+
+A step is one whole AllReduce call (all 2(N-1) schedule steps) over the 8 rank
+buffers, in place, inputs resident in HBM.  Prints one JSON line:
+  value        busbw in GB/s = algbw * 2(N-1)/N, algbw = M / time per call
+               ("集合通信算法延迟公式", @tbl-model-algo-busbw-coef)
+  roofline     algorithmic bytes per launch (every row reads its source, a
+               reduce row also its destination, and writes its destination:
+               5(N-1)M for this call) / the row kernel's mean launch time,
+               against MI355X's 8 TB/s HBM peak
+  cpu_baseline the CPU oracle on the same inputs, one core
+Extra per-call detail goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "busbw GB/s & % HBM peak, Ring AllReduce fp32 N=8 M=256MiB (1 GPU)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_kernel_ring_allreduce_fp32_n8_256MiB.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "device_types.h"):
+        with open(os.path.join(ROOT, "collective_communication_algorithms_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(per_launch_bytes_expected: float):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(inputs_host, N: int, count: int, algo: str):
+    """The oracle as it stands, timed on the host on the same inputs."""
+    import numpy as np  # noqa: F401
+    from oracle.schedules import make_plan
+    from oracle.simulate import run_plan
+    plan = make_plan("allreduce", algo, N, count)
+    t0 = time.perf_counter()
+    run_plan(plan, "float32", "sum", inputs_host)
+    dt = time.perf_counter() - t0
+    M = count * 4
+    busbw = M / dt * 2 * (N - 1) / N / 1e9
+    return {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full workload ({N} x {M >> 20} MiB fp32, one {algo} AllReduce), "
+                      f"numpy single-threaded, {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--algo", default="ring", choices=["ring", "rhd", "dbt"])
+    ap.add_argument("--exec", default="persistent", choices=["persistent", "step"])
+    ap.add_argument("--nranks", type=int, default=8)
+    ap.add_argument("--mib", type=int, default=256, help="MiB per rank")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs N virtual ranks on one GPU; --gpus above 1 is not supported",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.steps > 40:
+        print("bench.py: --steps must be in [1, 40] (in-place sums grow 8x per call)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import collective_communication_algorithms_amd as coll
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+    N, M = args.nranks, args.mib << 20
+    count = M // 4
+    coll.coll_set_option("exec", 1 if args.exec == "step" else 0)
+
+    # inputs: 8 rank buffers of N(0,1) fp32 drawn by torch's seeded generator on the device
+    buf = torch.empty((N, count), dtype=torch.float32, device=dev)
+    ranks = si.device_rank_tensors(3, N, count, "float32", dev, out=buf)
+    torch.cuda.synchronize()
+    host_inputs = None
+    if not args.no_cpu_baseline:
+        host_inputs = [r.cpu().numpy() for r in ranks]
+
+    # parity on sampled columns before timing (bit-exact against the oracle)
+    from oracle.schedules import make_plan
+    from oracle.simulate import run_plan_columns
+    cols = np.unique(np.concatenate([np.arange(0, count, 4097), np.arange(0, 65536),
+                                     np.arange(count - 65536, count),
+                                     np.arange(count // N - 4096, count // N + 4096)]))
+    cols_t = torch.from_numpy(cols).to(dev)
+    sample_in = [r.index_select(0, cols_t).cpu().numpy() for r in ranks]
+    coll.coll_allreduce(ranks, algo=args.algo)
+    torch.cuda.synchronize()
+    want = run_plan_columns(make_plan("allreduce", args.algo, N, count), "float32", "sum", cols, sample_in)
+    parity = all(np.array_equal(r.index_select(0, cols_t).cpu().numpy().view(np.uint32), w.view(np.uint32))
+                 for r, w in zip(ranks, want))
+    if not parity:
+        print("bench.py: GPU result differs from the oracle on sampled columns", file=sys.stderr)
+        return 1
+    stats = coll.coll_get_stats()
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        coll.coll_allreduce(ranks, algo=args.algo)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_all0.record(stream)
+    for s, e in ev:
+        s.record(stream)
+        coll.coll_allreduce(ranks, algo=args.algo)
+        e.record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_call = [s.elapsed_time(e) for s, e in ev]
+    ms = total_ms / args.steps
+    if not bool(torch.isfinite(ranks[0][:1024]).all()):
+        print("bench.py: values overflowed", file=sys.stderr)
+        return 1
+
+    algbw = M / (ms * 1e-3) / 1e9
+    busbw = algbw * 2 * (N - 1) / N
+    hbm_bytes = stats["hbm_bytes"]                      # 5(N-1)M: schedule bytes of one call
+    launches = 1 if args.exec == "persistent" else stats["steps"]
+    launch_ms = float(np.mean(per_call)) / launches
+    achieved = hbm_bytes / launches / (launch_ms * 1e-3) / 1e9
+    traffic = load_traffic(hbm_bytes / launches)
+    from collective_communication_algorithms_amd import model
+    pred_ms = model.time("allreduce", args.algo, N, M, 5e-6, 450e9) * 1e3
+
+    result = {
+        "metric": METRIC,
+        "value": round(busbw, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: N(0,1) fp32 per rank from torch's seeded device generator",
+        "config": {"workload": f"{args.algo}_allreduce_fp32_n{N}_{args.mib}MiB", "nranks": N,
+                   "bytes_per_rank": M, "algo": args.algo, "op": "sum", "inplace": True,
+                   "exec": args.exec, "schedule_steps": stats["steps"]},
+        "algbw_GBps": round(algbw, 2),
+        "hbm_pct_of_peak": round(100 * hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": None,
+        "alpha_beta_page_model_ms": round(pred_ms, 4),
+        "parity": "bit-exact vs oracle on %d sampled columns per rank" % len(cols),
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps({"per_call_ms": [round(x, 4) for x in per_call], "launch_ms_mean": launch_ms,
+                      "schedule_hbm_bytes": hbm_bytes}), file=sys.stderr)
+    del buf, ranks
+    torch.cuda.empty_cache()
+    if host_inputs is not None:
+        result["cpu_baseline"] = cpu_baseline(host_inputs, N, count, args.algo)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

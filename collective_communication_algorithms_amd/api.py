@@ -1,0 +1,152 @@
+"""Python names for the C ABI of include/coll.h: argument marshalling only.
+
+Rank buffers are torch tensors on one GPU (PyTorch supplies device memory and
+the stream).  Every step of every collective runs in libcoll.so's kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import ALGOS, DTYPES, KINDS, OPS, OPTIONS, CollCounts, CollError, CollRow, check  # noqa: F401
+
+_TORCH_DT = None
+
+
+def _dtype_name(t) -> str:
+    global _TORCH_DT
+    import torch
+    if _TORCH_DT is None:
+        _TORCH_DT = {torch.int32: "int32", torch.uint8: "uint8", torch.float32: "float32",
+                     torch.bfloat16: "bfloat16"}
+    try:
+        return _TORCH_DT[t.dtype]
+    except KeyError:
+        raise CollError(_lib.COLL_ERR_INVALID_ARG, f"unsupported dtype {t.dtype}") from None
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _check_tensors(send, recv):
+    if len(send) == 0:
+        raise CollError(_lib.COLL_ERR_INVALID_ARG, "no rank buffers")
+    t0 = send[0]
+    for t in list(send) + list(recv or []):
+        if t.device != t0.device or t.dtype != t0.dtype or t.numel() != t0.numel() or not t.is_contiguous():
+            raise CollError(_lib.COLL_ERR_INVALID_ARG,
+                            "rank buffers must share device, dtype and size, and be contiguous")
+        if t.device.type != "cuda":
+            raise CollError(_lib.COLL_ERR_INVALID_ARG, "rank buffers must be GPU tensors")
+    if recv is not None and len(recv) != len(send):
+        raise CollError(_lib.COLL_ERR_INVALID_ARG, "one receive buffer per rank")
+
+
+def _stream_handle(device, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _collective(name, send, recv, op, algo, root, chunks, stream):
+    import torch
+    _check_tensors(send, recv)
+    lib = _lib.load()
+    dev = send[0].device
+    with torch.cuda.device(dev):
+        sp = _ptr_array(send)
+        rp = _ptr_array(recv) if recv is not None else None
+        st = getattr(lib, name)(sp, rp, len(send), send[0].numel(), DTYPES[_dtype_name(send[0])], OPS[op],
+                                ALGOS[algo], int(root), int(chunks), _stream_handle(dev, stream))
+    check(st)
+
+
+def coll_allreduce(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_allreduce", send, recv, op, algo, root, chunks, stream)
+
+
+def coll_reducescatter(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_reducescatter", send, recv, op, algo, root, chunks, stream)
+
+
+def coll_allgather(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_allgather", send, recv, op, algo, root, chunks, stream)
+
+
+def coll_broadcast(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_broadcast", send, recv, op, algo, root, chunks, stream)
+
+
+def coll_scatter(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_scatter", send, recv, op, algo, root, chunks, stream)
+
+
+def coll_gather(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_gather", send, recv, op, algo, root, chunks, stream)
+
+
+def coll_alltoall(send, recv, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_alltoall", send, recv, op, algo, root, chunks, stream)
+
+
+COLLECTIVE_FNS = {"allreduce": coll_allreduce, "reducescatter": coll_reducescatter, "allgather": coll_allgather,
+                  "broadcast": coll_broadcast, "scatter": coll_scatter, "gather": coll_gather,
+                  "alltoall": coll_alltoall}
+
+
+def coll_plan(kind, algo, nranks, count, dtype, root=0, chunks=1):
+    """(rows, counts) of the in-place schedule; rows are tuples
+    (step, src, dst, src_off, dst_off, n, reduce, local, from_send, staged)."""
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    counts = CollCounts()
+    check(lib.coll_plan(KINDS[kind], ALGOS[algo], nranks, count, DTYPES[dtype], root, chunks, None,
+                        ctypes.byref(n), ctypes.byref(counts)))
+    rows = (CollRow * max(n.value, 1))()
+    check(lib.coll_plan(KINDS[kind], ALGOS[algo], nranks, count, DTYPES[dtype], root, chunks, rows,
+                        ctypes.byref(n), ctypes.byref(counts)))
+    out = [(r.step, r.src, r.dst, r.src_off, r.dst_off, r.n, r.reduce, r.local, r.from_send, r.staged)
+           for r in rows[:n.value]]
+    return out, {"steps": counts.steps, "rows": counts.rows, "crit_bytes": counts.crit_bytes,
+                 "hbm_bytes": counts.hbm_bytes}
+
+
+def coll_get_stats():
+    lib = _lib.load()
+    c = CollCounts()
+    check(lib.coll_get_stats(ctypes.byref(c)))
+    return {"steps": c.steps, "rows": c.rows, "crit_bytes": c.crit_bytes, "hbm_bytes": c.hbm_bytes}
+
+
+def coll_set_checksums(sums=None):
+    """``sums``: an int64 GPU tensor (one slot per schedule row), or None to stop."""
+    lib = _lib.load()
+    if sums is None:
+        check(lib.coll_set_checksums(None, 0))
+    else:
+        check(lib.coll_set_checksums(ctypes.c_void_p(sums.data_ptr()), sums.numel()))
+
+
+def coll_set_option(name, value):
+    check(_lib.load().coll_set_option(OPTIONS[name], int(value)))
+
+
+def coll_finalize():
+    _lib.load().coll_finalize()
+
+
+def coll_calib_copy(dst, src, stream=None):
+    check(_lib.load().coll_calib_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src.data_ptr()),
+                                      dst.numel() * dst.element_size(), _stream_handle(dst.device, stream)))
+
+
+def coll_calib_add(dst, a, b, stream=None):
+    check(_lib.load().coll_calib_add(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(a.data_ptr()),
+                                     ctypes.c_void_p(b.data_ptr()), dst.numel() * dst.element_size(),
+                                     _stream_handle(dst.device, stream)))

@@ -1,0 +1,495 @@
+// The C ABI: argument checks, the schedule cache, launches.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "bind.h"
+#include "coll.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace coll {
+namespace {
+
+thread_local std::string t_err;
+thread_local coll_counts_t t_last{};
+thread_local uint64_t* t_sums = nullptr;
+thread_local size_t t_sums_cap = 0;
+
+std::atomic<int64_t> opt_exec{0};
+std::atomic<int64_t> opt_group{0};
+std::atomic<int64_t> opt_grid{0};
+std::atomic<int64_t> opt_nt{1};
+
+constexpr uint32_t PERM_LDS_BYTES = 64 * 1024;
+
+coll_status_t fail(coll_status_t st, const std::string& msg) {
+  t_err = msg;
+  return st;
+}
+
+coll_status_t hip_fail(hipError_t e, const char* what) {
+  t_err = std::string(what) + ": " + hipGetErrorString(e);
+  return COLL_ERR_HIP;
+}
+
+int elem_size(coll_dtype_t d) {
+  switch (d) {
+    case COLL_INT32: return 4;
+    case COLL_UINT8: return 1;
+    case COLL_FLOAT32: return 4;
+    case COLL_BFLOAT16: return 2;
+  }
+  return 0;
+}
+
+struct Key {
+  int dev, kind, algo, N;
+  int64_t count;
+  int sz, root, chunks, inplace;
+  bool operator==(const Key& o) const {
+    return dev == o.dev && kind == o.kind && algo == o.algo && N == o.N && count == o.count && sz == o.sz &&
+           root == o.root && chunks == o.chunks && inplace == o.inplace;
+  }
+};
+
+struct KeyHash {
+  size_t operator()(const Key& k) const {
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&](uint64_t v) { h = (h ^ v) * 1099511628211ull; };
+    mix(uint64_t(k.dev));
+    mix(uint64_t(k.kind));
+    mix(uint64_t(k.algo));
+    mix(uint64_t(k.N));
+    mix(uint64_t(k.count));
+    mix(uint64_t(k.sz));
+    mix(uint64_t(k.root));
+    mix(uint64_t(k.chunks));
+    mix(uint64_t(k.inplace));
+    return size_t(h);
+  }
+};
+
+struct Entry {
+  Bound bound;
+  DevItem* d_items = nullptr;
+  DevStep* d_steps = nullptr;
+  uint64_t last_use = 0;
+};
+
+struct DevInfo {
+  int cus = 0;
+  bool lds_set = false;
+};
+
+std::mutex g_mu;
+std::unordered_map<Key, std::unique_ptr<Entry>, KeyHash> g_cache;
+std::unordered_map<int, DevInfo> g_dev;
+std::unordered_map<uint64_t, int> g_occ;  // (kernel variant, device) -> blocks per CU
+uint64_t g_tick = 0;
+constexpr size_t CACHE_CAP = 512;
+
+void free_entry(Entry& e) {
+  if (e.d_items) (void)hipFree(e.d_items);
+  if (e.d_steps) (void)hipFree(e.d_steps);
+  e.d_items = nullptr;
+  e.d_steps = nullptr;
+}
+
+coll_status_t device_info(int dev, DevInfo*& out) {
+  auto it = g_dev.find(dev);
+  if (it == g_dev.end()) {
+    DevInfo di;
+    hipError_t e = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    e = set_perm_lds_limit(PERM_LDS_BYTES);
+    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
+    di.lds_set = true;
+    it = g_dev.emplace(dev, di).first;
+  }
+  out = &it->second;
+  return COLL_OK;
+}
+
+int occupancy_rows(int dev, int dt, int op, bool cks, bool nt) {
+  const uint64_t key = (uint64_t(dev) << 32) | uint64_t(dt * 64 + op * 4 + (cks ? 2 : 0) + (nt ? 1 : 0));
+  auto it = g_occ.find(key);
+  if (it != g_occ.end()) return it->second;
+  const int n = rows_blocks_per_cu(dt, op, cks, nt);
+  g_occ[key] = n;
+  return n;
+}
+
+int occupancy_perm(int dev, int unit, bool cks, bool nt) {
+  const uint64_t key = (uint64_t(dev) << 32) | (uint64_t(1) << 31) | uint64_t(unit * 4 + (cks ? 2 : 0) + (nt ? 1 : 0));
+  auto it = g_occ.find(key);
+  if (it != g_occ.end()) return it->second;
+  const int n = perm_blocks_per_cu(unit, cks, nt, PERM_LDS_BYTES);
+  g_occ[key] = n;
+  return n;
+}
+
+coll_status_t get_entry(const Key& k, Entry*& out) {
+  auto it = g_cache.find(k);
+  if (it != g_cache.end()) {
+    it->second->last_use = ++g_tick;
+    out = it->second.get();
+    return COLL_OK;
+  }
+  if (g_cache.size() >= CACHE_CAP) {
+    // evict the least recently used schedule; its tables may still be read by
+    // queued work, so wait for the device first
+    auto lru = g_cache.begin();
+    for (auto i = g_cache.begin(); i != g_cache.end(); ++i)
+      if (i->second->last_use < lru->second->last_use) lru = i;
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    free_entry(*lru->second);
+    g_cache.erase(lru);
+  }
+  Schedule s;
+  std::string err;
+  coll_status_t st = build_schedule(coll_kind_t(k.kind), coll_algo_t(k.algo), k.N, k.count, k.root, k.chunks, s, err);
+  if (st != COLL_OK) return fail(st, err);
+  const std::string hz = check_schedule(s);
+  if (!hz.empty()) return fail(COLL_ERR_UNSUPPORTED, "internal schedule conflict: " + hz);
+  auto e = std::make_unique<Entry>();
+  e->bound = bind_schedule(s, k.sz, k.inplace != 0);
+  const Bound& b = e->bound;
+  if (!b.items.empty()) {
+    hipError_t he = hipMalloc(reinterpret_cast<void**>(&e->d_items), b.items.size() * sizeof(DevItem));
+    if (he != hipSuccess) return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
+    he = hipMalloc(reinterpret_cast<void**>(&e->d_steps), b.steps.size() * sizeof(DevStep));
+    if (he != hipSuccess) {
+      free_entry(*e);
+      return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
+    }
+    he = hipMemcpy(e->d_items, b.items.data(), b.items.size() * sizeof(DevItem), hipMemcpyHostToDevice);
+    if (he == hipSuccess)
+      he = hipMemcpy(e->d_steps, b.steps.data(), b.steps.size() * sizeof(DevStep), hipMemcpyHostToDevice);
+    if (he != hipSuccess) {
+      free_entry(*e);
+      return hip_fail(he, "hipMemcpy");
+    }
+  }
+  e->last_use = ++g_tick;
+  out = e.get();
+  g_cache.emplace(k, std::move(e));
+  return COLL_OK;
+}
+
+// Pointer checks: non-null, element-aligned, no overlap between distinct rank
+// buffers, in place either for every rank or for none.
+coll_status_t check_buffers(void* const* send, void* const* recv, int N, int64_t count, int sz, bool a2a,
+                            bool& inplace) {
+  if (!send) return fail(COLL_ERR_INVALID_ARG, "sendbufs is NULL");
+  inplace = true;
+  if (recv) {
+    int same = 0;
+    for (int i = 0; i < N; ++i) same += recv[i] == send[i];
+    if (same != 0 && same != N) return fail(COLL_ERR_INVALID_ARG, "recvbufs alias sendbufs for some ranks only");
+    inplace = same == N;
+  }
+  if (a2a && inplace) return fail(COLL_ERR_INVALID_ARG, "alltoall must be out of place");
+  if (count == 0) return COLL_OK;
+  std::vector<std::pair<uint64_t, uint64_t>> iv;
+  const uint64_t bytes = uint64_t(count) * uint64_t(sz);
+  for (int side = 0; side < (inplace ? 1 : 2); ++side) {
+    void* const* v = side ? recv : send;
+    for (int i = 0; i < N; ++i) {
+      const uint64_t p = reinterpret_cast<uint64_t>(v[i]);
+      if (!p) return fail(COLL_ERR_INVALID_ARG, "a rank buffer is NULL");
+      if (p % uint64_t(sz)) return fail(COLL_ERR_INVALID_ARG, "a rank buffer is not aligned to the element size");
+      iv.push_back({p, p + bytes});
+    }
+  }
+  std::sort(iv.begin(), iv.end());
+  for (size_t i = 1; i < iv.size(); ++i)
+    if (iv[i].first < iv[i - 1].second) return fail(COLL_ERR_INVALID_ARG, "rank buffers overlap");
+  return COLL_OK;
+}
+
+uint32_t pick_group_tiles(uint64_t colspace, uint64_t max_groups) {
+  const int64_t forced = opt_group.load();
+  if (forced > 0) return uint32_t(forced);
+  // enough groups to give every resident work group at least one, up to 8 tiles per group
+  const uint64_t tiles = (colspace + TILE_BYTES - 1) / TILE_BYTES;
+  uint32_t gt = 8;
+  while (gt > 1 && tiles / gt < max_groups) gt >>= 1;
+  return gt;
+}
+
+coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N, size_t count_in, coll_dtype_t dtype,
+                  coll_op_t op, coll_algo_t algo, int root, int chunks, void* stream_v) {
+  const int sz = elem_size(dtype);
+  if (!sz) return fail(COLL_ERR_INVALID_ARG, "unknown dtype");
+  if (int(op) < 0 || int(op) > 2) return fail(COLL_ERR_INVALID_ARG, "unknown op");
+  if (N < 1) return fail(COLL_ERR_INVALID_ARG, "nranks must be at least 1");
+  if (N > COLL_MAX_RANKS) return fail(COLL_ERR_UNSUPPORTED, "nranks above COLL_MAX_RANKS");
+  if (count_in > (size_t(1) << 44) / size_t(sz)) return fail(COLL_ERR_INVALID_ARG, "count too large");
+  const int64_t count = int64_t(count_in);
+  bool inplace = true;
+  coll_status_t st = check_buffers(send, recv, N, count, sz, kind == COLL_K_ALLTOALL, inplace);
+  if (st != COLL_OK) return st;
+  // validate the algorithm and the scalars even when there is nothing to move
+  {
+    Schedule probe;
+    std::string err;
+    st = build_schedule(kind, algo, N, 0, root, 1, probe, err);
+    if (st != COLL_OK) return fail(st, err);
+    if ((algo == COLL_ALGO_CHAIN_PIPE || algo == COLL_ALGO_BINOMIAL_PIPE) && count > 0 &&
+        (chunks < 1 || int64_t(chunks) > count))
+      return fail(COLL_ERR_INVALID_ARG, "chunks must be in [1, count]");
+    if (kind == COLL_K_ALLTOALL && count % N) return fail(COLL_ERR_INVALID_ARG, "alltoall needs count divisible by nranks");
+  }
+  t_last = coll_counts_t{};
+  if (count == 0) return COLL_OK;
+
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevInfo* di = nullptr;
+  st = device_info(dev, di);
+  if (st != COLL_OK) return st;
+  const coll_algo_t ra = resolve_algo(kind, algo);
+  const bool rooted = kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER;
+  const bool pipe = ra == COLL_ALGO_CHAIN_PIPE || ra == COLL_ALGO_BINOMIAL_PIPE;
+  Key k{dev, int(kind), int(ra), N, count, sz, rooted ? root : 0, pipe ? chunks : 1, inplace ? 1 : 0};
+  Entry* e = nullptr;
+  st = get_entry(k, e);
+  if (st != COLL_OK) return st;
+  const Bound& b = e->bound;
+
+  const bool cks = t_sums != nullptr;
+  if (cks) {
+    if (size_t(b.nrows) > t_sums_cap) return fail(COLL_ERR_INVALID_ARG, "checksum buffer smaller than the schedule");
+    he = launch_fill_u64(t_sums, uint64_t(b.nrows), 0, stream);
+    if (he != hipSuccess) return hip_fail(he, "checksum clear");
+  }
+  const bool nt = opt_nt.load() != 0;
+  const bool step_mode = opt_exec.load() == 1;
+
+  RankPtrs ptrs;
+  bool bases16 = true;
+  uint64_t align_or = 0;
+  for (int i = 0; i < N; ++i) {
+    ptrs.send[i] = reinterpret_cast<uint64_t>(send[i]);
+    ptrs.recv[i] = reinterpret_cast<uint64_t>(inplace ? send[i] : recv[i]);
+    align_or |= ptrs.send[i] | ptrs.recv[i];
+  }
+  for (int i = N; i < COLL_MAX_RANKS; ++i) ptrs.send[i] = ptrs.recv[i] = 0;
+  bases16 = (align_or % 16) == 0;
+
+  const int dt = int(dtype) == COLL_INT32 ? DT_I32 : int(dtype) == COLL_UINT8 ? DT_U8
+               : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
+  for (const Phase& ph : b.phases) {
+    if (ph.kind == Phase::ROWS) {
+      RowsArgs a{};
+      a.items = e->d_items;
+      a.steps = e->d_steps;
+      a.sums = t_sums;
+      a.nontemporal = nt;
+      a.bases16 = bases16;
+      a.p = ptrs;
+      const uint64_t resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, nt));
+      uint64_t cap = resident;
+      if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
+      a.group_tiles = pick_group_tiles(ph.colspace, cap);
+      const uint64_t gbytes = uint64_t(a.group_tiles) * TILE_BYTES;
+      const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
+      const uint32_t grid = uint32_t(std::min(groups, cap));
+      for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
+        a.s0 = s0;
+        a.s1 = step_mode ? s0 + 1 : ph.s1;
+        he = launch_rows(a, dt, int(op), cks, grid, stream);
+        if (he != hipSuccess) return hip_fail(he, "row kernel launch");
+      }
+    } else {
+      PermArgs a{};
+      a.items = e->d_items;
+      a.steps = e->d_steps;
+      a.sums = t_sums;
+      a.nontemporal = nt;
+      a.p = ptrs;
+      int unit = b.perm_unit;
+      while (unit > 1 && (align_or % uint64_t(unit))) unit >>= 1;
+      a.ncols_units = uint32_t(ph.colspace / uint64_t(unit));
+      const uint32_t budget_units = PERM_LDS_BYTES / uint32_t(unit) / uint32_t(N);
+      uint32_t tu = budget_units >= 64 ? (budget_units / 64) * 64 : std::max<uint32_t>(1, budget_units);
+      tu = std::min<uint32_t>(tu, std::max<uint32_t>(a.ncols_units, 1));
+      a.tile_units = tu;
+      const uint32_t lds = tu * uint32_t(unit) * uint32_t(N);
+      const uint64_t ntiles = (uint64_t(a.ncols_units) + tu - 1) / tu;
+      uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, cks, nt));
+      if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
+      const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(ntiles, cap)));
+      for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
+        a.s0 = s0;
+        a.s1 = step_mode ? s0 + 1 : ph.s1;
+        he = launch_perm(a, unit, cks, grid, lds, stream);
+        if (he != hipSuccess) return hip_fail(he, "permutation kernel launch");
+      }
+    }
+  }
+  t_last = b.counts;
+  return COLL_OK;
+}
+
+}  // namespace
+}  // namespace coll
+
+using namespace coll;
+
+extern "C" {
+
+#define COLL_ENTRY(name, kind)                                                                                 \
+  coll_status_t name(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count, coll_dtype_t dtype, \
+                     coll_op_t op, coll_algo_t algo, int root, int chunks, void* stream) {                        \
+    try {                                                                                                       \
+      return run(kind, sendbufs, recvbufs, nranks, count, dtype, op, algo, root, chunks, stream);              \
+    } catch (const std::bad_alloc&) {                                                                           \
+      return fail(COLL_ERR_NO_MEMORY, "host allocation failed");                                               \
+    } catch (...) {                                                                                             \
+      return fail(COLL_ERR_INVALID_ARG, "unexpected host exception");                                         \
+    }                                                                                                           \
+  }
+
+COLL_ENTRY(coll_allreduce, COLL_K_ALLREDUCE)
+COLL_ENTRY(coll_reducescatter, COLL_K_REDUCESCATTER)
+COLL_ENTRY(coll_allgather, COLL_K_ALLGATHER)
+COLL_ENTRY(coll_broadcast, COLL_K_BROADCAST)
+COLL_ENTRY(coll_scatter, COLL_K_SCATTER)
+COLL_ENTRY(coll_gather, COLL_K_GATHER)
+COLL_ENTRY(coll_alltoall, COLL_K_ALLTOALL)
+
+coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t count, coll_dtype_t dtype, int root,
+                        int chunks, coll_row_t* rows, size_t* nrows, coll_counts_t* counts) {
+  try {
+    const int sz = elem_size(dtype);
+    if (!sz) return fail(COLL_ERR_INVALID_ARG, "unknown dtype");
+    if (!nrows) return fail(COLL_ERR_INVALID_ARG, "nrows is NULL");
+    if (count > (size_t(1) << 44) / size_t(sz)) return fail(COLL_ERR_INVALID_ARG, "count too large");
+    Schedule s;
+    std::string err;
+    coll_status_t st = build_schedule(kind, algo, nranks, int64_t(count), root, chunks, s, err);
+    if (st != COLL_OK) return fail(st, err);
+    const size_t cap = *nrows;
+    *nrows = s.rows.size();
+    if (counts) *counts = count_schedule(s, sz);
+    if (rows) {
+      if (cap < s.rows.size()) return fail(COLL_ERR_INVALID_ARG, "row capacity too small");
+      for (size_t i = 0; i < s.rows.size(); ++i) {
+        const Row& r = s.rows[i];
+        coll_row_t& o = rows[i];
+        o.step = r.step;
+        o.src = r.src;
+        o.dst = r.dst;
+        o.reduce = r.reduce;
+        o.local = r.local;
+        o.from_send = r.from_send;
+        o.staged = r.staged;
+        o.src_off = r.src_off;
+        o.dst_off = r.dst_off;
+        o.n = r.n;
+      }
+    }
+    return COLL_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(COLL_ERR_NO_MEMORY, "host allocation failed");
+  }
+}
+
+coll_status_t coll_get_stats(coll_counts_t* last) {
+  if (!last) return fail(COLL_ERR_INVALID_ARG, "NULL");
+  *last = t_last;
+  return COLL_OK;
+}
+
+coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity) {
+  if (dev_sums && capacity == 0) return fail(COLL_ERR_INVALID_ARG, "capacity is 0");
+  t_sums = dev_sums;
+  t_sums_cap = dev_sums ? capacity : 0;
+  return COLL_OK;
+}
+
+coll_status_t coll_set_option(coll_option_t key, int64_t value) {
+  switch (key) {
+    case COLL_OPT_EXEC:
+      if (value != 0 && value != 1) return fail(COLL_ERR_INVALID_ARG, "exec mode is 0 or 1");
+      opt_exec = value;
+      return COLL_OK;
+    case COLL_OPT_GROUP_TILES:
+      if (value < 0 || value > 64) return fail(COLL_ERR_INVALID_ARG, "group tiles in [0, 64]");
+      opt_group = value;
+      return COLL_OK;
+    case COLL_OPT_MAX_GRID:
+      if (value < 0 || value > (int64_t(1) << 20)) return fail(COLL_ERR_INVALID_ARG, "grid cap out of range");
+      opt_grid = value;
+      return COLL_OK;
+    case COLL_OPT_NONTEMPORAL:
+      opt_nt = value ? 1 : 0;
+      return COLL_OK;
+  }
+  return fail(COLL_ERR_INVALID_ARG, "unknown option");
+}
+
+const char* coll_status_string(coll_status_t s) {
+  switch (s) {
+    case COLL_OK: return "COLL_OK";
+    case COLL_ERR_INVALID_ARG: return "COLL_ERR_INVALID_ARG";
+    case COLL_ERR_UNSUPPORTED: return "COLL_ERR_UNSUPPORTED";
+    case COLL_ERR_HIP: return "COLL_ERR_HIP";
+    case COLL_ERR_NO_MEMORY: return "COLL_ERR_NO_MEMORY";
+  }
+  return "unknown status";
+}
+
+const char* coll_last_error(void) { return t_err.c_str(); }
+
+void coll_finalize(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto& kv : g_cache) free_entry(*kv.second);
+  g_cache.clear();
+  g_occ.clear();
+  g_dev.clear();
+}
+
+static coll_status_t calib(void* dst, const void* a, const void* b, size_t bytes, void* stream) {
+  if (!dst || !a) return fail(COLL_ERR_INVALID_ARG, "NULL buffer");
+  if (bytes % 16 || (reinterpret_cast<uint64_t>(dst) | reinterpret_cast<uint64_t>(a) | reinterpret_cast<uint64_t>(b)) % 16)
+    return fail(COLL_ERR_INVALID_ARG, "calibration needs 16-byte sizes and pointers");
+  if (bytes == 0) return COLL_OK;
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  int cus = 0;
+  he = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (he != hipSuccess) return hip_fail(he, "hipDeviceGetAttribute");
+  const uint64_t units = bytes / 16;
+  const uint64_t want = (units + BLOCK_THREADS * 4 - 1) / (BLOCK_THREADS * 4);
+  const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(want, uint64_t(cus) * 8)));
+  he = launch_calib(dst, a, b, bytes, grid, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "calibration launch");
+  return COLL_OK;
+}
+
+coll_status_t coll_calib_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  return calib(dst, src, nullptr, bytes, stream);
+}
+
+coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t bytes, void* stream) {
+  if (!b) return fail(COLL_ERR_INVALID_ARG, "NULL buffer");
+  return calib(dst, a, b, bytes, stream);
+}
+
+}  // extern "C"

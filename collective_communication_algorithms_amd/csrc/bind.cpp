@@ -1,0 +1,221 @@
+#include "bind.h"
+
+#include <algorithm>
+#include <iterator>
+#include <map>
+
+namespace coll {
+namespace {
+
+// Disjoint element intervals of one rank's receive buffer written so far.
+class Written {
+ public:
+  void add(int64_t a, int64_t b) {
+    if (a >= b) return;
+    auto it = iv_.upper_bound(a);
+    if (it != iv_.begin() && std::prev(it)->second >= a) {
+      --it;
+      a = it->first;
+    }
+    while (it != iv_.end() && it->first <= b) {
+      b = std::max(b, it->second);
+      it = iv_.erase(it);
+    }
+    iv_[a] = b;
+  }
+  // Boundaries inside (a, b) where written / unwritten changes.
+  void cuts(int64_t a, int64_t b, std::vector<int64_t>& out) const {
+    auto it = iv_.upper_bound(a);
+    if (it != iv_.begin()) --it;
+    for (; it != iv_.end() && it->first < b; ++it) {
+      if (it->first > a) out.push_back(it->first);
+      if (it->second > a && it->second < b) out.push_back(it->second);
+    }
+  }
+  bool covers(int64_t a, int64_t b) const {  // [a, b) entirely written (a < b)
+    auto it = iv_.upper_bound(a);
+    if (it == iv_.begin()) return false;
+    --it;
+    return it->first <= a && it->second >= b;
+  }
+  // Parts of [a, b) not yet written.
+  void gaps(int64_t a, int64_t b, std::vector<std::pair<int64_t, int64_t>>& out) const {
+    int64_t x = a;
+    auto it = iv_.upper_bound(a);
+    if (it != iv_.begin()) --it;
+    for (; it != iv_.end() && it->first < b; ++it) {
+      if (it->second <= x) continue;
+      if (it->first > x) out.push_back({x, std::min(it->first, b)});
+      x = std::max(x, it->second);
+      if (x >= b) break;
+    }
+    if (x < b) out.push_back({x, b});
+  }
+
+ private:
+  std::map<int64_t, int64_t> iv_;
+};
+
+uint32_t vec_flag(int64_t src_delta, int64_t dst_delta) {
+  return (src_delta % 16 == 0 && dst_delta % 16 == 0) ? ITEM_VEC : 0u;
+}
+
+uint32_t shift_flag(int64_t row_start_byte) {
+  return uint32_t(((-row_start_byte) % 4 + 4) % 4) << ITEM_CKS_SHIFT;
+}
+
+}  // namespace
+
+std::vector<std::pair<int64_t, int64_t>> defined_output(const Schedule& s, int rank) {
+  const int64_t lo = (int64_t(rank) * s.count) / s.N, hi = (int64_t(rank + 1) * s.count) / s.N;
+  switch (s.kind) {
+    case COLL_K_REDUCESCATTER:
+    case COLL_K_SCATTER: return {{lo, hi}};
+    case COLL_K_GATHER:
+      if (rank == s.root) return {{0, s.count}};
+      return {};
+    default: return {{0, s.count}};
+  }
+}
+
+Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
+  Bound b;
+  b.nrows = int64_t(s.rows.size());
+  b.counts = count_schedule(s, sz);
+  const bool a2a = s.kind == COLL_K_ALLTOALL;
+  const bool bruck = a2a && s.algo == COLL_ALGO_BRUCK;
+  std::vector<std::vector<DevItem>> per_step(s.steps.size());
+  std::vector<Written> written(a2a || inplace ? 0 : size_t(s.N));
+
+  for (size_t si = 0; si < s.steps.size(); ++si) {
+    const Step& st = s.steps[si];
+    const bool perm_step = bruck && si > 0;  // Bruck's shifts and final rotation
+    for (int64_t ri = st.first; ri < st.first + st.nrows; ++ri) {
+      const Row& r = s.rows[size_t(ri)];
+      DevItem it{};
+      it.row = uint32_t(ri);
+      it.src_rank = uint16_t(r.src);
+      it.dst_rank = uint16_t(r.dst);
+      const int64_t row_start = r.dst_off * sz;
+      if (perm_step) {
+        // column = byte offset inside the block; the item moves one whole block
+        it.col0 = 0;
+        it.col1 = uint64_t(r.n * sz);
+        it.src_delta = r.src_off * sz;
+        it.dst_delta = r.dst_off * sz;
+        it.flags = vec_flag(it.src_delta, it.dst_delta) | shift_flag(row_start);
+        per_step[si].push_back(it);
+        continue;
+      }
+      const int64_t sd = (r.src_off - r.dst_off) * sz;
+      it.src_delta = sd;
+      it.dst_delta = 0;
+      const uint32_t base = (r.reduce ? ITEM_REDUCE : 0u) | vec_flag(sd, 0) | shift_flag(row_start);
+      if (a2a || inplace) {
+        it.col0 = uint64_t(r.dst_off * sz);
+        it.col1 = uint64_t((r.dst_off + r.n) * sz);
+        it.flags = base | (r.from_send ? ITEM_SRC_SEND : 0u);
+        per_step[si].push_back(it);
+        continue;
+      }
+      // Out of place: split where the source or the old destination changes
+      // between "already written on the receive side" and "still only in send".
+      const int64_t a = r.dst_off, z = r.dst_off + r.n;
+      std::vector<int64_t> cut{a, z};
+      written[size_t(r.src)].cuts(r.src_off, r.src_off + r.n, cut);  // src_off == dst_off here
+      if (r.reduce) written[size_t(r.dst)].cuts(a, z, cut);
+      std::sort(cut.begin(), cut.end());
+      cut.erase(std::unique(cut.begin(), cut.end()), cut.end());
+      for (size_t k = 0; k + 1 < cut.size(); ++k) {
+        const int64_t lo = cut[k], hi = cut[k + 1];
+        DevItem p = it;
+        p.col0 = uint64_t(lo * sz);
+        p.col1 = uint64_t(hi * sz);
+        p.flags = base;
+        if (!written[size_t(r.src)].covers(lo + (r.src_off - r.dst_off), hi + (r.src_off - r.dst_off)))
+          p.flags |= ITEM_SRC_SEND;
+        if (r.reduce && !written[size_t(r.dst)].covers(lo, hi)) p.flags |= ITEM_DSRC_SEND;
+        per_step[si].push_back(p);
+      }
+      written[size_t(r.dst)].add(a, z);
+    }
+  }
+
+  if (!a2a && !inplace) {
+    // defined output that no row writes: copy it from send to receive
+    std::vector<DevItem> copies;
+    for (int rank = 0; rank < s.N; ++rank) {
+      for (auto& reg : defined_output(s, rank)) {
+        std::vector<std::pair<int64_t, int64_t>> g;
+        written[size_t(rank)].gaps(reg.first, reg.second, g);
+        for (auto& q : g) {
+          if (q.second <= q.first) continue;
+          DevItem it{};
+          it.row = NO_ROW;
+          it.src_rank = it.dst_rank = uint16_t(rank);
+          it.col0 = uint64_t(q.first * sz);
+          it.col1 = uint64_t(q.second * sz);
+          it.flags = ITEM_SRC_SEND | ITEM_VEC;
+          copies.push_back(it);
+          b.counts.hbm_bytes += 2 * (q.second - q.first) * sz;
+        }
+      }
+    }
+    if (!copies.empty()) {
+      if (per_step.empty()) per_step.emplace_back();
+      per_step[0].insert(per_step[0].end(), copies.begin(), copies.end());
+    }
+  }
+
+  uint64_t rows_cols = 0, perm_cols = 0;
+  for (size_t si = 0; si < per_step.size(); ++si) {
+    DevStep d{};
+    d.item0 = uint32_t(b.items.size());
+    d.nitems = uint32_t(per_step[si].size());
+    const bool perm_step = bruck && si > 0;
+    d.staged = perm_step && s.steps[si].staged ? 1u : 0u;
+    d.gsize = d.staged ? uint32_t(s.N) : 1u;
+    for (auto& it : per_step[si]) {
+      if (perm_step) perm_cols = std::max(perm_cols, it.col1);
+      else rows_cols = std::max(rows_cols, it.col1);
+      b.items.push_back(it);
+    }
+    b.steps.push_back(d);
+  }
+  const uint32_t nsteps = uint32_t(b.steps.size());
+  if (nsteps == 0 || b.items.empty()) return b;
+  if (bruck) {
+    Phase p1;
+    p1.kind = Phase::ROWS;
+    p1.s0 = 0;
+    p1.s1 = 1;
+    p1.colspace = rows_cols;
+    b.phases.push_back(p1);
+    if (nsteps > 1 && perm_cols > 0) {
+      Phase p2;
+      p2.kind = Phase::PERM;
+      p2.s0 = 1;
+      p2.s1 = nsteps;
+      p2.colspace = perm_cols;
+      b.phases.push_back(p2);
+    }
+    const int64_t blk = perm_cols > 0 ? int64_t(perm_cols) : 16;
+    b.perm_unit = 1;
+    for (int u : {16, 8, 4, 2}) {
+      if (blk % u == 0) {
+        b.perm_unit = u;
+        break;
+      }
+    }
+  } else {
+    Phase p;
+    p.kind = Phase::ROWS;
+    p.s0 = 0;
+    p.s1 = nsteps;
+    p.colspace = rows_cols;
+    b.phases.push_back(p);
+  }
+  return b;
+}
+
+}  // namespace coll

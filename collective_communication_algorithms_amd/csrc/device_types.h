@@ -1,0 +1,83 @@
+// Tables the host builds from a schedule and the kernels walk.
+//
+// Column space.  Every row of the Ring, Halving-Doubling, Double Binary Tree,
+// Broadcast, Scatter and Gather schedules keeps its elements at the same offset
+// on both ranks, so a byte offset in a rank buffer ("column") names the same
+// data position on every rank.  Each work item is a byte range of columns on
+// one (source rank -> destination rank) edge.  A thread of the row kernel owns
+// fixed 16-byte column units on every rank for the whole call, so every value a
+// thread reads was written by itself in an earlier step (or is input): steps
+// need no synchronisation between threads or work groups, only program order.
+// Pairwise AllToAll rows read only the send buffers, which no row writes.  The
+// Bruck kernel uses the offset inside a block as its column instead; every
+// Bruck row keeps that offset.
+#pragma once
+
+#include <stdint.h>
+
+#include "coll.h"
+
+namespace coll {
+
+enum : uint32_t {
+  ITEM_REDUCE = 1u << 0,     // dst <- dst (+) src, else dst <- src
+  ITEM_SRC_SEND = 1u << 1,   // source read from the send buffer of src_rank
+  ITEM_DSRC_SEND = 1u << 2,  // old destination value read from the send buffer of dst_rank
+  ITEM_VEC = 1u << 3,        // src_delta and dst_delta are multiples of 16
+  ITEM_CKS_SHIFT = 4,        // bits 4..5: (-row start byte) mod 4, for the row checksum
+};
+
+constexpr uint32_t NO_ROW = 0xFFFFFFFFu;
+
+struct DevItem {          // 48 bytes
+  uint64_t col0, col1;    // column bytes [col0, col1)
+  int64_t src_delta;      // source address = base(src) + column + src_delta
+  int64_t dst_delta;      // destination address = base(dst) + column + dst_delta
+  uint32_t row;           // schedule row (checksum slot) or NO_ROW
+  uint16_t src_rank, dst_rank;
+  uint32_t flags;
+  uint32_t pad;
+};
+
+struct DevStep {          // 16 bytes
+  uint32_t item0, nitems; // items [item0, item0 + nitems)
+  uint32_t gsize;         // staged steps: items per staging group (groups are contiguous)
+  uint32_t staged;
+};
+
+struct RankPtrs {
+  uint64_t send[COLL_MAX_RANKS];
+  uint64_t recv[COLL_MAX_RANKS];
+};
+
+enum DType : int { DT_I32 = 0, DT_U8 = 1, DT_F32 = 2, DT_BF16 = 3 };
+enum Op : int { OP_SUM = 0, OP_MAX = 1, OP_MIN = 2 };
+
+constexpr int TILE_BYTES = 4096;      // 256 threads x 16 bytes
+constexpr int BLOCK_THREADS = 256;
+
+struct RowsArgs {                     // row kernel (copy / recv_and_reduce)
+  const DevItem* items;
+  const DevStep* steps;
+  uint64_t* sums;                     // per-row checksums or nullptr
+  uint32_t s0, s1;                    // steps [s0, s1)
+  uint32_t group_tiles;               // 4 KiB tiles per owned group
+  uint32_t nontemporal;
+  uint32_t bases16;                   // all rank base pointers 16-byte aligned
+  uint32_t pad;
+  RankPtrs p;
+};
+
+struct PermArgs {                     // staged permutation kernel (Bruck)
+  const DevItem* items;
+  const DevStep* steps;
+  uint64_t* sums;
+  uint32_t s0, s1;
+  uint32_t tile_units;                // units per owned tile of the block column
+  uint32_t ncols_units;               // block width in units
+  uint32_t nontemporal;
+  uint32_t pad;
+  RankPtrs p;
+};
+
+}  // namespace coll

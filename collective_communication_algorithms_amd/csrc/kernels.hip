@@ -1,0 +1,518 @@
+// Device kernels for gfx950 (CDNA4, wave64).
+//
+//  rows_kernel  copy and recv_and_reduce rows of a schedule ("集合通信算法延迟公式",
+//               Ring ReduceScatter: each step a rank reduces the chunk it receives
+//               into its own; the HCCL blog's recv_and_reduce).  Persistent over a
+//               range of steps: 128-bit loads, nontemporal stores, per-thread
+//               ownership of 16-byte column units (see device_types.h), so no
+//               flags or barriers are needed between steps.
+//  perm_kernel  Bruck's in-place block shifts and rotation ("集合通信算法延迟公式",
+//               Bruck AllToAll): each staging group is read into LDS, then written
+//               permuted, so every read of a step precedes every write.
+//  fill / calib plain helpers: clear checksum slots, stream copy / add.
+//
+// No MFMA: nothing here is a contraction.  Every kernel is bound by HBM.
+#include <hip/hip_runtime.h>
+
+#include "device_types.h"
+#include "launch.h"
+
+namespace coll {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Rank buffers are plain device memory: address them in the global address
+// space (global_load / global_store rather than flat).  The item and step
+// tables never change during a launch: read them through the constant address
+// space so that uniform reads become scalar loads.
+#define GLOBAL __attribute__((address_space(1)))
+#define CONSTANT __attribute__((address_space(4)))
+
+template <class T>
+__device__ __forceinline__ const GLOBAL T* gptr(const char* p) {
+  return (const GLOBAL T*)(p);
+}
+template <class T>
+__device__ __forceinline__ GLOBAL T* gptr(char* p) {
+  return (GLOBAL T*)(p);
+}
+
+template <class T>
+__device__ __forceinline__ T cload(const T* p) {
+  return *(const CONSTANT T*)(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const char* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(gptr<u32x4>(p));
+  else return *gptr<u32x4>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st16(char* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, gptr<u32x4>(p));
+  else *gptr<u32x4>(p) = v;
+}
+
+// ---- element arithmetic ------------------------------------------------------
+
+// binary32 -> bfloat16, round to nearest even on the bit pattern: adding 0x7FFF
+// plus the lowest kept bit carries into the kept half exactly when the dropped
+// half is above one half-ulp, or equal to it with an odd kept part.  NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t pick_i32(uint32_t d, uint32_t s) {
+  if constexpr (OP == OP_SUM) return d + s;  // wraps modulo 2^32
+  else if constexpr (OP == OP_MAX) return int32_t(s) > int32_t(d) ? s : d;
+  else return int32_t(s) < int32_t(d) ? s : d;
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t pick_f32(uint32_t d, uint32_t s) {
+  const float fd = __uint_as_float(d), fs = __uint_as_float(s);
+  if constexpr (OP == OP_SUM) return __float_as_uint(fd + fs);
+  else if constexpr (OP == OP_MAX) return fs > fd ? s : d;
+  else return fs < fd ? s : d;
+}
+
+// one bfloat16 held in the low 16 bits
+template <int OP>
+__device__ __forceinline__ uint32_t pick_bf16(uint32_t d, uint32_t s) {
+  const float fd = __uint_as_float(d << 16), fs = __uint_as_float(s << 16);
+  if constexpr (OP == OP_SUM) return bf16_rne(fd + fs);
+  else if constexpr (OP == OP_MAX) return fs > fd ? s : d;
+  else return fs < fd ? s : d;
+}
+
+template <int OP>
+__device__ __forceinline__ uint32_t pick_u8(uint32_t d, uint32_t s) {
+  if constexpr (OP == OP_SUM) return (d + s) & 0xffu;
+  else if constexpr (OP == OP_MAX) return s > d ? s : d;
+  else return s < d ? s : d;
+}
+
+// One element (its bits in the low bits of the word).
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t combine_elem(uint32_t d, uint32_t s) {
+  if constexpr (DT == DT_I32) return pick_i32<OP>(d, s);
+  else if constexpr (DT == DT_F32) return pick_f32<OP>(d, s);
+  else if constexpr (DT == DT_BF16) return pick_bf16<OP>(d, s);
+  else return pick_u8<OP>(d, s);
+}
+
+// A 32-bit word of packed elements.
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t combine_word(uint32_t d, uint32_t s) {
+  if constexpr (DT == DT_I32 || DT == DT_F32) {
+    return combine_elem<DT, OP>(d, s);
+  } else if constexpr (DT == DT_BF16) {
+    const uint32_t lo = pick_bf16<OP>(d & 0xffffu, s & 0xffffu);
+    const uint32_t hi = pick_bf16<OP>(d >> 16, s >> 16);
+    return lo | (hi << 16);
+  } else {
+    uint32_t r = 0;
+#pragma unroll
+    for (int b = 0; b < 32; b += 8) r |= pick_u8<OP>((d >> b) & 0xffu, (s >> b) & 0xffu) << b;
+    return r;
+  }
+}
+
+template <int DT, int OP>
+__device__ __forceinline__ u32x4 combine16(u32x4 d, u32x4 s) {
+  u32x4 r;
+  r.x = combine_word<DT, OP>(d.x, s.x);
+  r.y = combine_word<DT, OP>(d.y, s.y);
+  r.z = combine_word<DT, OP>(d.z, s.z);
+  r.w = combine_word<DT, OP>(d.w, s.w);
+  return r;
+}
+
+// ---- checksum helpers (row checksum: sum of the row's little-endian uint32
+// words counted from the row's first byte).  A stored word at a 4-aligned column
+// holds the row's bytes rotated by the row start's misalignment.
+__device__ __forceinline__ uint32_t rotl32(uint32_t x, uint32_t r) {
+  return r ? (x << r) | (x >> (32u - r)) : x;
+}
+
+__device__ __forceinline__ uint64_t words16(u32x4 v, uint32_t rot) {
+  return uint64_t(rotl32(v.x, rot)) + rotl32(v.y, rot) + rotl32(v.z, rot) + rotl32(v.w, rot);
+}
+
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ void add_row_sum(uint64_t* sums, uint32_t row, uint64_t v) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63u) == 0 && row != NO_ROW)
+    __hip_atomic_fetch_add(sums + row, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- element loads / stores for the unaligned edges ------------------------------
+
+template <int DT>
+__device__ __forceinline__ uint32_t ld_elem(const char* p) {
+  if constexpr (DT == DT_I32 || DT == DT_F32) return *gptr<uint32_t>(p);
+  else if constexpr (DT == DT_BF16) return *gptr<uint16_t>(p);
+  else return *gptr<uint8_t>(p);
+}
+
+template <int DT>
+__device__ __forceinline__ void st_elem(char* p, uint32_t v) {
+  if constexpr (DT == DT_I32 || DT == DT_F32) *gptr<uint32_t>(p) = v;
+  else if constexpr (DT == DT_BF16) *gptr<uint16_t>(p) = uint16_t(v);
+  else *gptr<uint8_t>(p) = uint8_t(v);
+}
+
+template <int DT>
+constexpr int elem_size() { return DT == DT_BF16 ? 2 : (DT == DT_U8 ? 1 : 4); }
+
+// ---- row kernel --------------------------------------------------------------
+
+struct ItemView {
+  const char* src;   // address of column 0 on the source side
+  const char* dsrc;  // address of column 0 for the old destination value
+  char* dst;         // address of column 0 on the destination side
+  bool reduce;
+  uint32_t shift;    // (-row start) mod 4
+};
+
+// One 16-byte column unit x of the item, clipped to [lo, hi).
+template <int DT, int OP, bool CKS, bool NT>
+__device__ __forceinline__ void do_unit(const ItemView& v, uint64_t x, uint64_t lo, uint64_t hi, bool vec,
+                                        uint64_t& acc) {
+  if (x + 16 <= lo || x >= hi) return;
+  if (vec && x >= lo && x + 16 <= hi) {
+    u32x4 s = ld16<NT>(v.src + x);
+    if (v.reduce) s = combine16<DT, OP>(ld16<NT>(v.dsrc + x), s);
+    st16<NT>(v.dst + x, s);
+    if constexpr (CKS) acc += words16(s, v.shift * 8u);
+    return;
+  }
+  constexpr int SZ = elem_size<DT>();
+  const uint64_t a0 = x > lo ? x : lo, a1 = x + 16 < hi ? x + 16 : hi;
+  for (uint64_t y = a0; y < a1; y += SZ) {
+    uint32_t s = ld_elem<DT>(v.src + y);
+    if (v.reduce) s = combine_elem<DT, OP>(ld_elem<DT>(v.dsrc + y), s);
+    st_elem<DT>(v.dst + y, s);
+    if constexpr (CKS) acc += uint64_t(s << (8u * uint32_t((y + v.shift) & 3u)));
+  }
+}
+
+// U full, aligned units at x0, x0 + 4 KiB, ...: all loads issued before the stores.
+template <int U, int DT, int OP, bool CKS, bool NT>
+__device__ __forceinline__ void do_batch(const ItemView& v, uint64_t x0, uint64_t& acc) {
+  u32x4 s[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) s[k] = ld16<NT>(v.src + x0 + uint64_t(k) * TILE_BYTES);
+  if (v.reduce) {
+    u32x4 d[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) d[k] = ld16<NT>(v.dsrc + x0 + uint64_t(k) * TILE_BYTES);
+#pragma unroll
+    for (int k = 0; k < U; ++k) s[k] = combine16<DT, OP>(d[k], s[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    st16<NT>(v.dst + x0 + uint64_t(k) * TILE_BYTES, s[k]);
+    if constexpr (CKS) acc += words16(s[k], v.shift * 8u);
+  }
+}
+
+// Work group w owns the groups g = w, w + G, w + 2G, ... of `group_tiles`
+// consecutive 4 KiB column tiles; thread t owns bytes [16t, 16t + 16) of every
+// tile.  Items of a step are walked in row order, steps in order.
+template <int DT, int OP, bool CKS, bool NT>
+__global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
+  const uint32_t G = gridDim.x, w = blockIdx.x;
+  const uint32_t gt = a.group_tiles;
+  const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
+  const uint64_t tofs = uint64_t(threadIdx.x) * 16u;
+  for (uint32_t s = a.s0; s < a.s1; ++s) {
+    const DevStep st = cload(a.steps + s);
+    for (uint32_t i = st.item0, ie = st.item0 + st.nitems; i < ie; ++i) {
+      const DevItem it = cload(a.items + i);
+      if (it.col1 <= it.col0) continue;
+      const uint32_t gfirst = uint32_t(it.col0 / gbytes);
+      const uint32_t glast = uint32_t((it.col1 - 1) / gbytes);
+      uint32_t g = gfirst + (w + G - gfirst % G) % G;
+      if (g > glast) continue;
+      ItemView v;
+      v.src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
+                                                                       : a.p.recv[it.src_rank]) + it.src_delta;
+      v.dsrc = reinterpret_cast<const char*>((it.flags & ITEM_DSRC_SEND) ? a.p.send[it.dst_rank]
+                                                                         : a.p.recv[it.dst_rank]) + it.dst_delta;
+      v.dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
+      v.reduce = (it.flags & ITEM_REDUCE) != 0;
+      v.shift = (it.flags >> ITEM_CKS_SHIFT) & 3u;
+      const bool vec = a.bases16 && (it.flags & ITEM_VEC);
+      uint64_t acc = 0;
+      for (; g <= glast; g += G) {
+        const uint64_t gb = uint64_t(g) * gbytes;
+        const uint64_t lo = gb > it.col0 ? gb : it.col0;
+        const uint64_t hi = gb + gbytes < it.col1 ? gb + gbytes : it.col1;
+        if (vec && lo == gb && hi == gb + gbytes) {
+          uint32_t k = 0;
+          for (; k + 4 <= gt; k += 4) do_batch<4, DT, OP, CKS, NT>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
+          for (; k < gt; ++k) do_batch<1, DT, OP, CKS, NT>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
+        } else {
+          for (uint32_t k = 0; k < gt; ++k)
+            do_unit<DT, OP, CKS, NT>(v, gb + uint64_t(k) * TILE_BYTES + tofs, lo, hi, vec, acc);
+        }
+      }
+      if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
+    }
+  }
+}
+
+// ---- staged permutation kernel (Bruck) --------------------------------------------
+
+template <int U>
+struct UnitT;
+template <> struct UnitT<16> { typedef u32x4 T; };
+template <> struct UnitT<8> { typedef uint64_t T; };
+template <> struct UnitT<4> { typedef uint32_t T; };
+template <> struct UnitT<2> { typedef uint16_t T; };
+template <> struct UnitT<1> { typedef uint8_t T; };
+
+template <int U, bool NT>
+__device__ __forceinline__ typename UnitT<U>::T ld_unit(const char* p) {
+  typedef typename UnitT<U>::T T;
+  if constexpr (NT && U >= 4) return __builtin_nontemporal_load(gptr<T>(p));
+  else return *gptr<T>(p);
+}
+
+template <int U, bool NT>
+__device__ __forceinline__ void st_unit(char* p, typename UnitT<U>::T v) {
+  typedef typename UnitT<U>::T T;
+  if constexpr (NT && U >= 4) __builtin_nontemporal_store(v, gptr<T>(p));
+  else *gptr<T>(p) = v;
+}
+
+template <int U>
+__device__ __forceinline__ uint64_t unit_words(typename UnitT<U>::T v, uint64_t col) {
+  if constexpr (U == 16) return words16(v, 0);
+  else if constexpr (U == 8) return uint64_t(uint32_t(v)) + uint32_t(v >> 32);
+  else if constexpr (U == 4) return v;
+  else return uint64_t(uint32_t(v) << (8u * uint32_t(col & 3u)));
+}
+
+// Columns are unit indices inside a block.  Work group w owns tiles w, w+G, ...
+// of `tile_units` units.  Non-staged steps copy item by item; a staged step
+// reads each group's tile of all its items into LDS, waits, then writes them
+// to their destinations.  Every row keeps its offset inside the block (and
+// blocks start at unit boundaries), so only the owning work group ever touches
+// a tile's columns; a barrier at the end of each step orders the steps.
+template <int U, bool CKS, bool NT>
+__global__ __launch_bounds__(BLOCK_THREADS) void perm_kernel(const PermArgs a) {
+  typedef typename UnitT<U>::T T;
+  extern __shared__ __align__(16) char lds_raw[];
+  T* lds = reinterpret_cast<T*>(lds_raw);
+  const uint32_t G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
+  const uint32_t tu = a.tile_units, ncol = a.ncols_units;
+  const uint32_t ntiles = (ncol + tu - 1) / tu;
+  for (uint32_t s = a.s0; s < a.s1; ++s) {
+    const DevStep st = cload(a.steps + s);
+    if (!st.staged) {
+      for (uint32_t i = st.item0, ie = st.item0 + st.nitems; i < ie; ++i) {
+        const DevItem it = cload(a.items + i);
+        const char* src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
+                                                                                   : a.p.recv[it.src_rank]) + it.src_delta;
+        char* dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
+        uint64_t acc = 0;
+        for (uint32_t tile = w; tile < ntiles; tile += G) {
+          for (uint32_t u = t; u < tu; u += BLOCK_THREADS) {
+            const uint32_t c = tile * tu + u;
+            if (c < ncol) {
+              const T v = ld_unit<U, NT>(src + uint64_t(c) * U);
+              st_unit<U, NT>(dst + uint64_t(c) * U, v);
+              if constexpr (CKS) acc += unit_words<U>(v, uint64_t(c) * U);
+            }
+          }
+        }
+        if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
+      }
+    } else {
+      const uint32_t gs = st.gsize;
+      const uint32_t ngroups = st.nitems / gs;
+      for (uint32_t grp = 0; grp < ngroups; ++grp) {
+        const uint32_t ib = st.item0 + grp * gs;
+        for (uint32_t tile = w; tile < ntiles; tile += G) {
+          const uint32_t c0 = tile * tu;
+          for (uint32_t q = t; q < gs * tu; q += BLOCK_THREADS) {
+            const uint32_t m = q / tu, c = c0 + (q - m * tu);
+            if (c < ncol) {
+              const DevItem it = cload(a.items + ib + m);
+              const char* src = reinterpret_cast<const char*>(a.p.recv[it.src_rank]) + it.src_delta;
+              lds[q] = ld_unit<U, NT>(src + uint64_t(c) * U);
+            }
+          }
+          __syncthreads();
+          for (uint32_t q = t; q < gs * tu; q += BLOCK_THREADS) {
+            const uint32_t m = q / tu, c = c0 + (q - m * tu);
+            const DevItem it = cload(a.items + ib + m);
+            uint64_t acc = 0;
+            if (c < ncol) {
+              char* dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
+              st_unit<U, NT>(dst + uint64_t(c) * U, lds[q]);
+              if constexpr (CKS) acc = unit_words<U>(lds[q], uint64_t(c) * U);
+            }
+            if constexpr (CKS) {
+              // a wave covers one item when tu is a multiple of 64; otherwise fall back per lane
+              if ((tu & 63u) == 0) add_row_sum(a.sums, it.row, acc);
+              else if (acc && it.row != NO_ROW)
+                __hip_atomic_fetch_add(a.sums + it.row, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+          __syncthreads();
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---- helpers -----------------------------------------------------------------------
+
+__global__ void fill_u64_kernel(uint64_t* p, uint64_t n, uint64_t value) {
+  for (uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += uint64_t(gridDim.x) * blockDim.x)
+    *gptr<uint64_t>(reinterpret_cast<char*>(p + i)) = value;
+}
+
+template <bool ADD>
+__global__ __launch_bounds__(BLOCK_THREADS) void calib_kernel(char* dst, const char* a, const char* b, uint64_t units) {
+  const uint64_t stride = uint64_t(gridDim.x) * BLOCK_THREADS;
+  uint64_t i = uint64_t(blockIdx.x) * BLOCK_THREADS + threadIdx.x;
+  for (; i + 3 * stride < units; i += 4 * stride) {
+    u32x4 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = ld16<true>(a + (i + k * stride) * 16);
+    if constexpr (ADD) {
+      u32x4 y[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = ld16<true>(b + (i + k * stride) * 16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = combine16<DT_F32, OP_SUM>(x[k], y[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) st16<true>(dst + (i + k * stride) * 16, x[k]);
+  }
+  for (; i < units; i += stride) {
+    u32x4 x = ld16<true>(a + i * 16);
+    if constexpr (ADD) x = combine16<DT_F32, OP_SUM>(x, ld16<true>(b + i * 16));
+    st16<true>(dst + i * 16, x);
+  }
+}
+
+// ---- host-side dispatch ---------------------------------------------------------------
+
+typedef void (*RowsFn)(RowsArgs);
+
+template <int DT, int OP>
+static RowsFn rows_fn(bool cks, bool nt) {
+  if (cks) return nt ? rows_kernel<DT, OP, true, true> : rows_kernel<DT, OP, true, false>;
+  return nt ? rows_kernel<DT, OP, false, true> : rows_kernel<DT, OP, false, false>;
+}
+
+template <int DT>
+static RowsFn rows_fn_op(int op, bool cks, bool nt) {
+  switch (op) {
+    case OP_SUM: return rows_fn<DT, OP_SUM>(cks, nt);
+    case OP_MAX: return rows_fn<DT, OP_MAX>(cks, nt);
+    default: return rows_fn<DT, OP_MIN>(cks, nt);
+  }
+}
+
+static RowsFn pick_rows(int dtype, int op, bool cks, bool nt) {
+  switch (dtype) {
+    case DT_I32: return rows_fn_op<DT_I32>(op, cks, nt);
+    case DT_U8: return rows_fn_op<DT_U8>(op, cks, nt);
+    case DT_F32: return rows_fn_op<DT_F32>(op, cks, nt);
+    default: return rows_fn_op<DT_BF16>(op, cks, nt);
+  }
+}
+
+typedef void (*PermFn)(PermArgs);
+
+template <int U>
+static PermFn perm_fn(bool cks, bool nt) {
+  if (cks) return nt ? perm_kernel<U, true, true> : perm_kernel<U, true, false>;
+  return nt ? perm_kernel<U, false, true> : perm_kernel<U, false, false>;
+}
+
+static PermFn pick_perm(int unit, bool cks, bool nt) {
+  switch (unit) {
+    case 16: return perm_fn<16>(cks, nt);
+    case 8: return perm_fn<8>(cks, nt);
+    case 4: return perm_fn<4>(cks, nt);
+    case 2: return perm_fn<2>(cks, nt);
+    default: return perm_fn<1>(cks, nt);
+  }
+}
+
+hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t grid, hipStream_t stream) {
+  RowsFn f = pick_rows(dtype, op, cks, a.nontemporal != 0);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(BLOCK_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_perm(const PermArgs& a, int unit, bool cks, uint32_t grid, uint32_t lds_bytes,
+                       hipStream_t stream) {
+  PermFn f = pick_perm(unit, cks, a.nontemporal != 0);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(BLOCK_THREADS), lds_bytes, stream, a);
+  return hipGetLastError();
+}
+
+int rows_blocks_per_cu(int dtype, int op, bool cks, bool nt) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_rows(dtype, op, cks, nt), BLOCK_THREADS, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+int perm_blocks_per_cu(int unit, bool cks, bool nt, uint32_t lds_bytes) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_perm(unit, cks, nt), BLOCK_THREADS, lds_bytes) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+hipError_t set_perm_lds_limit(uint32_t lds_bytes) {
+  hipError_t e = hipSuccess;
+  const int units[] = {16, 8, 4, 2, 1};
+  for (int u : units)
+    for (int c = 0; c < 2; ++c)
+      for (int n = 0; n < 2; ++n) {
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(pick_perm(u, c, n)),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
+        if (r != hipSuccess) e = r;
+      }
+  return e;
+}
+
+hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const uint32_t grid = uint32_t(n < 256 * 1024 ? (n + BLOCK_THREADS - 1) / BLOCK_THREADS : 1024);
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid), dim3(BLOCK_THREADS), 0, stream, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, uint32_t grid, hipStream_t stream) {
+  const uint64_t units = bytes / 16;
+  if (b)
+    hipLaunchKernelGGL(calib_kernel<true>, dim3(grid), dim3(BLOCK_THREADS), 0, stream, reinterpret_cast<char*>(dst),
+                       reinterpret_cast<const char*>(a), reinterpret_cast<const char*>(b), units);
+  else
+    hipLaunchKernelGGL(calib_kernel<false>, dim3(grid), dim3(BLOCK_THREADS), 0, stream, reinterpret_cast<char*>(dst),
+                       reinterpret_cast<const char*>(a), nullptr, units);
+  return hipGetLastError();
+}
+
+}  // namespace coll

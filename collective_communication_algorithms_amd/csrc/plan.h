@@ -1,0 +1,50 @@
+// Schedules of the collectives as step-ordered row tables, their counts and
+// their hazard check.  Host-only C++; no HIP dependency.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "coll.h"
+
+namespace coll {
+
+struct Row {
+  int32_t step, src, dst;
+  uint8_t reduce, local, from_send, staged;
+  int64_t src_off, dst_off, n;  // elements
+};
+
+struct Step {
+  int64_t first = 0, nrows = 0;  // rows [first, first + nrows) of Schedule::rows
+  bool local = false;            // rank-internal rearrangement, not a counted step
+  bool staged = false;           // in-place permutation: every read precedes every write
+};
+
+struct Schedule {
+  coll_kind_t kind{};
+  coll_algo_t algo{};
+  int N = 0;
+  int64_t count = 0;
+  int root = 0;
+  int chunks = 1;
+  std::vector<Row> rows;    // step-major
+  std::vector<Step> steps;
+  int64_t counted_steps() const;
+};
+
+// The algorithm a COLL_ALGO_DEFAULT request stands for.
+coll_algo_t resolve_algo(coll_kind_t kind, coll_algo_t algo);
+
+// Validates (kind, algo, N, count, root, chunks) and builds the in-place
+// schedule.  Returns COLL_OK or an error status with a message in `err`.
+coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo, int N, int64_t count, int root,
+                             int chunks, Schedule& out, std::string& err);
+
+coll_counts_t count_schedule(const Schedule& s, int elem_size);
+
+// Empty when every step is free of conflicts inside the step; else a message.
+std::string check_schedule(const Schedule& s);
+
+}  // namespace coll

@@ -1,0 +1,208 @@
+/*
+ * coll.h — collective-communication schedules executed over N virtual ranks
+ * whose buffers all sit in one MI355X's HBM.
+ *
+ * Every collective is run as the step-by-step schedule its algorithm defines:
+ * in each step some ranks "send" a chunk to another rank, which either stores
+ * it (copy) or reduces it into its own chunk (recv_and_reduce).  On one GPU a
+ * send is a device-to-device move performed by this library's HIP kernels.
+ *
+ * Sources (pages, by title and section):
+ *   [P1] "一对多通信：Broadcast 与 Scatter" — Broadcast / Scatter semantics,
+ *        binomial and chunked-pipeline Broadcast, binomial Scatter, Gather.
+ *   [P2] HCCL blog on Ring / Mesh / Tree AllReduce — the hccl_allreduce call
+ *        (element count, data type, SUM / MAX / MIN, in place when sendbuf ==
+ *        recvbuf, stream-ordered), and the Ring chunk walk.
+ *   [P3] "集合通信算法延迟公式" — Ring / Recursive Halving-Doubling / Double
+ *        Binary Tree AllReduce, Ring AllGather / ReduceScatter, Pairwise and
+ *        Bruck AllToAll, busbw coefficients.
+ *
+ * Conventions shared by all seven collective calls
+ *   sendbufs[i], recvbufs[i]  device pointers of virtual rank i, each holding
+ *                `count` elements of `dtype` (the pages' message size M =
+ *                count * sizeof(dtype) bytes per rank).  Pointers must be
+ *                aligned to the element size; 16-byte alignment takes the
+ *                128-bit load/store path.
+ *   recvbufs == NULL, or recvbufs[i] == sendbufs[i] for every i: in place.
+ *                Mixing the two, or any overlap between distinct rank buffers,
+ *                is COLL_ERR_INVALID_ARG.  AllToAll must be out of place.
+ *   chunk c of a rank buffer = elements [c*count/N, (c+1)*count/N) (floor).
+ *   op     ignored by collectives that do not reduce.
+ *   root   used by broadcast / scatter / gather only; 0 <= root < N.
+ *   chunks pipeline chunk count k for COLL_ALGO_CHAIN_PIPE and
+ *          COLL_ALGO_BINOMIAL_PIPE (1 <= k <= count); ignored otherwise.
+ *   stream a hipStream_t; the work is enqueued on it and the call returns
+ *          without waiting (stream-ordered, like hccl_allreduce's stream).
+ *
+ * Ownership: the caller owns every buffer and keeps it alive until the stream
+ * work has finished.  The library never allocates, frees or retains user
+ * memory; it owns only its schedule cache (host and device copies), freed by
+ * coll_finalize().
+ *
+ * Errors: every argument is checked on the host before anything is enqueued,
+ * so an error return leaves no partial work.  No exception crosses the ABI.
+ * A failing HIP call returns COLL_ERR_HIP with the HIP error text in
+ * coll_last_error() (thread-local).
+ */
+#ifndef COLL_H
+#define COLL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COLL_OK = 0,
+  COLL_ERR_INVALID_ARG = 1,  /* bad pointer, size, root, chunks, aliasing          */
+  COLL_ERR_UNSUPPORTED = 2,  /* algorithm not defined for this collective or N    */
+  COLL_ERR_HIP = 3,          /* a HIP runtime call failed                         */
+  COLL_ERR_NO_MEMORY = 4     /* host or device allocation for the schedule failed */
+} coll_status_t;
+
+typedef enum { COLL_INT32 = 0, COLL_UINT8 = 1, COLL_FLOAT32 = 2, COLL_BFLOAT16 = 3 } coll_dtype_t;
+
+/* dst <- dst (+) src per element.  int32 / uint8 sums wrap; float32 is one
+ * IEEE binary32 add (round to nearest even, subnormals kept); bfloat16 widens
+ * both operands to binary32, adds once and rounds to nearest even (NaN ->
+ * 0x7FC0) after every row.  max / min pick src when it compares greater /
+ * smaller, else keep dst.  [P2] hccl_allreduce parameter list (SUM/MAX/MIN). */
+typedef enum { COLL_SUM = 0, COLL_MAX = 1, COLL_MIN = 2 } coll_op_t;
+
+typedef enum {
+  COLL_ALGO_DEFAULT = 0,       /* ring / binomial / pairwise for the collective */
+  COLL_ALGO_RING = 1,          /* [P3] Ring AllReduce, Ring AllGather / ReduceScatter          */
+  COLL_ALGO_RHD = 2,           /* [P3] Recursive Halving-Doubling; N must be a power of 2      */
+  COLL_ALGO_DBT = 3,           /* [P3] Double Binary Tree; N must be a power of 2              */
+  COLL_ALGO_BINOMIAL = 4,      /* [P1] binomial-tree Broadcast / Scatter / Gather              */
+  COLL_ALGO_CHAIN_PIPE = 5,    /* [P1] chunked chain pipeline Broadcast (k = 1: chain)         */
+  COLL_ALGO_BINOMIAL_PIPE = 6, /* [P1] chunked binomial-tree pipeline Broadcast (k = 1: tree)  */
+  COLL_ALGO_PAIRWISE = 7,      /* [P3] Pairwise AllToAll, N-1 rounds                           */
+  COLL_ALGO_BRUCK = 8          /* [P3] Bruck AllToAll, ceil(log2 N) rounds plus rotations      */
+} coll_algo_t;
+
+typedef enum {
+  COLL_K_ALLREDUCE = 0, COLL_K_REDUCESCATTER = 1, COLL_K_ALLGATHER = 2, COLL_K_BROADCAST = 3,
+  COLL_K_SCATTER = 4, COLL_K_GATHER = 5, COLL_K_ALLTOALL = 6
+} coll_kind_t;
+
+/* Largest N the kernels accept (all rank pointers travel as kernel arguments). */
+#define COLL_MAX_RANKS 128
+
+/* ------------------------------------------------------------------------- */
+/* The seven collectives.  Same parameters for all; see the conventions above. */
+
+/* [P3] AllReduce: every rank ends with the elementwise reduction over ranks.
+ * Input all of buf_i; output all of buf_i.  algo: RING (default), RHD, DBT. */
+coll_status_t coll_allreduce(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                             void* stream);
+
+/* [P3] ReduceScatter: rank i ends with chunk i of the reduction; its other
+ * chunks are left unspecified.  algo: RING (default), RHD. */
+coll_status_t coll_reducescatter(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                                 coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                                 void* stream);
+
+/* [P3] AllGather: rank i contributes chunk i of its buffer; every rank ends
+ * with all N chunks.  algo: RING (default), RHD. */
+coll_status_t coll_allgather(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                             void* stream);
+
+/* [P1] Broadcast (eq:onetoall-bcast-semantic): every buffer ends equal to the
+ * root's.  algo: BINOMIAL (default), CHAIN_PIPE, BINOMIAL_PIPE with `chunks`. */
+coll_status_t coll_broadcast(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                             void* stream);
+
+/* [P1] Scatter (eq:onetoall-scatter-semantic): the root's chunk i lands in
+ * chunk i of rank i; other chunks of non-root buffers are staging space and
+ * left unspecified.  algo: BINOMIAL. */
+coll_status_t coll_scatter(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                           coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                           void* stream);
+
+/* [P1] Gather (eq:onetoall-gather-scatter-duality, Scatter reversed): chunk i
+ * of rank i lands in chunk i of the root; non-root buffers are left
+ * unspecified.  algo: BINOMIAL. */
+coll_status_t coll_gather(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                          coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                          void* stream);
+
+/* [P3] AllToAll: send_i holds N blocks of count/N elements, block j meant for
+ * rank j; afterwards block i of recv_j = block j of send_i.  Out of place only;
+ * count must be a multiple of N.  algo: PAIRWISE (default), BRUCK. */
+coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                            coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                            void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Schedules and statistics (host only; no GPU needed). */
+
+/* One row of a schedule: in step `step`, rank `src` sends n elements at
+ * element offset src_off to rank `dst`, which stores them at dst_off
+ * (reduce = 0) or reduces them into its own elements there (reduce = 1).
+ * local: a rank-internal move (AllToAll rearrangement), not a counted step.
+ * from_send: the source is the send buffer (AllToAll).  staged: a step that
+ * permutes in place; all its reads happen before its writes. */
+typedef struct {
+  int32_t step, src, dst;
+  uint8_t reduce, local, from_send, staged;
+  int64_t src_off, dst_off, n;
+} coll_row_t;
+
+/* steps: counted communication steps (the pages' closed forms, e.g. 2(N-1)
+ * for Ring AllReduce); rows: schedule rows; crit_bytes: per step the largest
+ * byte total on one (src, dst) edge, summed over steps (the beta term of
+ * [P3]'s alpha-beta model); hbm_bytes: bytes the rows read and write (copy
+ * 2*n*size, reduce 3*n*size). */
+typedef struct { int64_t steps, rows, crit_bytes, hbm_bytes; } coll_counts_t;
+
+/* Build the in-place schedule of a collective.  rows may be NULL; *nrows is
+ * the capacity on input and the number of rows on output (COLL_ERR_INVALID_ARG
+ * if the capacity is too small, with *nrows set to what is needed).  counts
+ * may be NULL.  Validation as for the collective calls (without pointers). */
+coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t count, coll_dtype_t dtype,
+                        int root, int chunks, coll_row_t* rows, size_t* nrows, coll_counts_t* counts);
+
+/* Counts of the last successful collective call on this thread, as executed
+ * (an out-of-place call adds local copies to hbm_bytes). */
+coll_status_t coll_get_stats(coll_counts_t* last);
+
+/* Per-row checksums.  When `dev_sums` is non-NULL (a device array of
+ * `capacity` uint64), every later collective call on this thread first clears
+ * dev_sums[0 .. rows) and then adds, for schedule row r (in coll_plan's order),
+ * the sum modulo 2^64 of the little-endian uint32 words of the row's
+ * destination region right after the row (words counted from the region's
+ * first byte, the last one zero-padded).  A call with more rows than
+ * `capacity` fails with COLL_ERR_INVALID_ARG.  NULL switches checksums off. */
+coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
+
+/* Process-wide execution options. */
+typedef enum {
+  COLL_OPT_EXEC = 0,        /* 0: one persistent launch per call (default); 1: one launch per step */
+  COLL_OPT_GROUP_TILES = 1, /* 4 KiB tiles per work group group (0: automatic)                     */
+  COLL_OPT_MAX_GRID = 2,    /* cap on work groups per launch (0: automatic)                        */
+  COLL_OPT_NONTEMPORAL = 3  /* 1: nontemporal loads and stores (default); 0: ordinary              */
+} coll_option_t;
+coll_status_t coll_set_option(coll_option_t key, int64_t value);
+
+const char* coll_status_string(coll_status_t status);
+const char* coll_last_error(void);   /* thread-local detail of the last error */
+void coll_finalize(void);            /* frees the schedule cache; call with no work in flight */
+
+/* ------------------------------------------------------------------------- */
+/* Calibration kernels: plain streams over `bytes` bytes (multiple of 16) for
+ * measuring the achievable HBM rate beside the schedule kernels.
+ * copy: dst = src (1 read + 1 write); add: dst = a + b as float32 (2 reads + 1
+ * write). */
+coll_status_t coll_calib_copy(void* dst, const void* src, size_t bytes, void* stream);
+coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COLL_H */

@@ -140,3 +140,30 @@ def gather(arrays, dtype, root=0, algo="binomial", trace=False):
 def alltoall(send, dtype, algo="pairwise", trace=False):
     """recv_j block i = send_i block j (blocks of count/N elements)."""
     return _run("alltoall", algo, send, dtype, trace=trace)
+
+
+def run_plan_columns(plan: Plan, dtype: str, op: str, cols: np.ndarray, send_cols: list) -> list:
+    """The plan restricted to a set of columns (element offsets) of every rank.
+
+    Valid for every schedule whose rows keep their offset (src_off == dst_off),
+    i.e. all but AllToAll: output element x of a rank then depends only on
+    element x of the ranks, through exactly the rows that cover x.  ``cols`` is
+    sorted; ``send_cols[r]`` holds rank r's values at those columns.  Returns the
+    receive side at those columns, computed with the same snapshot-per-step rule
+    as ``run_plan``.
+    """
+    if plan.kind == "alltoall":
+        raise ValueError("alltoall rows move data between offsets")
+    recv = [np.array(a, copy=True) for a in send_cols]
+    for rows in plan.steps:
+        moves = []
+        for r in rows:
+            assert r.src_off == r.dst_off
+            a = np.searchsorted(cols, r.src_off, side="left")
+            b = np.searchsorted(cols, r.src_off + r.n, side="left")
+            if a < b:
+                moves.append((r, a, b, recv[r.src][a:b].copy()))
+        for r, a, b, s in moves:
+            d = recv[r.dst][a:b]
+            d[...] = numerics.combine(d, s, dtype, op) if r.reduce else s
+    return recv

@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports what include/coll.h declares, and rejects
+bad arguments before touching the GPU (CPU only: every case here returns
+before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from collective_communication_algorithms_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "coll.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(coll_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_symbols()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    for n in _lib.COLLECTIVES:
+        assert n in names
+
+
+def call(name, send, recv, N, count, dtype="int32", op="sum", algo="default", root=0, chunks=1):
+    lib = _lib.load()
+    P = ctypes.c_void_p * max(N, 1, len(send or []), len(recv or []))
+    sp = P(*send) if send is not None else None
+    rp = P(*recv) if recv is not None else None
+    return getattr(lib, name)(sp, rp, N, count, _lib.DTYPES[dtype], _lib.OPS[op], _lib.ALGOS[algo], root,
+                              chunks, None)
+
+
+def bufs(N, count, sz=4, base=1 << 32, gap=1 << 20):
+    return [base + i * gap for i in range(N)]
+
+
+INV, UNS, OK = _lib.COLL_ERR_INVALID_ARG, _lib.COLL_ERR_UNSUPPORTED, _lib.COLL_OK
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(name="coll_allreduce", send=None, recv=None, N=4, count=16), INV),
+    (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=0, count=16), INV),
+    (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=4, count=16, op="sum", dtype="int32",
+          algo="rhd"), OK),
+    (dict(name="coll_allreduce", send=bufs(6, 16), recv=None, N=6, count=0, algo="rhd"), UNS),
+    (dict(name="coll_allreduce", send=bufs(12, 16), recv=None, N=12, count=0, algo="dbt"), UNS),
+    (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=4, count=0, algo="pairwise"), UNS),
+    (dict(name="coll_broadcast", send=bufs(4, 16), recv=None, N=4, count=0, algo="binomial", root=4), INV),
+    (dict(name="coll_scatter", send=bufs(4, 16), recv=None, N=4, count=0, algo="binomial", root=-1), INV),
+    (dict(name="coll_broadcast", send=bufs(4, 16), recv=None, N=4, count=16, algo="chain_pipe", chunks=0), INV),
+    (dict(name="coll_broadcast", send=bufs(4, 16), recv=None, N=4, count=16, algo="chain_pipe", chunks=17), INV),
+    (dict(name="coll_alltoall", send=bufs(4, 16), recv=None, N=4, count=16), INV),
+    (dict(name="coll_alltoall", send=bufs(4, 16), recv=bufs(4, 16, base=1 << 40), N=4, count=18), INV),
+    (dict(name="coll_allreduce", send=[1 << 32, (1 << 32) + 2], recv=None, N=2, count=4), INV),
+    (dict(name="coll_allreduce", send=[1 << 32, (1 << 32) + 32], recv=None, N=2, count=16), INV),
+    (dict(name="coll_allreduce", send=[1 << 32, 1 << 33], recv=[1 << 32, 1 << 34], N=2, count=16), INV),
+    (dict(name="coll_allreduce", send=[1 << 32, 0], recv=None, N=2, count=16), INV),
+    (dict(name="coll_allreduce", send=bufs(129, 16), recv=None, N=129, count=16), UNS),
+    (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=4, count=0), OK),
+    (dict(name="coll_gather", send=bufs(4, 16), recv=bufs(4, 16, base=1 << 40), N=4, count=0,
+          algo="binomial"), OK),
+])
+def test_argument_errors(case, want):
+    name = case.pop("name")
+    if want == OK and case.get("count", 0) > 0:
+        pytest.skip("a valid non-empty call needs a GPU")
+    st = call(name, **case)
+    assert st == want, _lib.load().coll_last_error()
+    if st != OK:
+        assert len(_lib.load().coll_last_error()) > 0
+
+
+def test_options_and_strings():
+    lib = _lib.load()
+    assert lib.coll_set_option(0, 7) == INV
+    assert lib.coll_set_option(99, 0) == INV
+    assert lib.coll_set_option(1, 0) == OK
+    assert lib.coll_status_string(0) == b"COLL_OK"
+    assert lib.coll_status_string(2) == b"COLL_ERR_UNSUPPORTED"
+    assert lib.coll_set_checksums(None, 0) == OK
+    assert lib.coll_calib_copy(None, None, 16, None) == INV
+
+
+def test_plan_capacity_protocol():
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    assert lib.coll_plan(0, 1, 8, 64, 2, 0, 1, None, ctypes.byref(n), None) == OK
+    assert n.value == 112
+    rows = (_lib.CollRow * 10)()
+    n2 = ctypes.c_size_t(10)
+    assert lib.coll_plan(0, 1, 8, 64, 2, 0, 1, rows, ctypes.byref(n2), None) == INV
+    assert n2.value == 112

@@ -1,0 +1,69 @@
+"""The alpha-beta module against the numbers the pages print (CPU only)."""
+
+import json
+import os
+
+import pytest
+
+from collective_communication_algorithms_amd import model
+
+G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "alpha_beta_tables.json")))
+
+
+def test_allreduce_comparison_table_n8():
+    t = G["allreduce_compare_n8"]
+    for algo in ("ring", "rhd", "dbt"):
+        assert model.latency_steps("allreduce", algo, 8) == t[algo]["latency_alpha"]
+        assert model.bandwidth_coef("allreduce", algo, 8) == pytest.approx(t[algo]["bw_coef"])
+
+
+def test_latency_terms_at_large_n():
+    assert model.latency_steps("allreduce", "ring", 8) == G["ring_latency_terms"]["n8_alpha"]
+    assert model.latency_steps("allreduce", "ring", 1024) == G["ring_latency_terms"]["n1024_alpha"]
+    assert model.latency_steps("allreduce", "rhd", 64) == G["rhd_vs_ring_n64"]["rhd_alpha"]
+    assert model.latency_steps("allreduce", "ring", 64) == G["rhd_vs_ring_n64"]["ring_alpha"]
+
+
+def test_ring_dbt_crossover():
+    c = G["ring_dbt_crossover"]
+    m = model.ring_dbt_crossover(c["nranks"], c["alpha_us"] * 1e-6, c["beta_GBps"] * 1e9)
+    assert m / 1e6 == pytest.approx(c["M_star_MB"], rel=1e-3)
+    # at the crossover the two formulas agree
+    a, b = c["alpha_us"] * 1e-6, c["beta_GBps"] * 1e9
+    assert model.time("allreduce", "ring", 8, m, a, b) == pytest.approx(model.time("allreduce", "dbt", 8, m, a, b))
+
+
+@pytest.mark.parametrize("N", [2, 4, 8, 16, 64])
+def test_busbw_coefficients(N):
+    t = G["busbw_coefficients"]
+    import re
+    env = {"N": N}
+    for kind in ("allreduce", "allgather", "reducescatter", "alltoall", "broadcast", "reduce"):
+        expr = re.sub(r"(\d)\(", r"\1*(", t[kind])        # the table writes 2(N-1)/N
+        assert model.busbw_coef(kind, N) == pytest.approx(eval(expr, {}, env))
+
+
+@pytest.mark.parametrize("N", [2, 3, 8, 13, 64])
+def test_ring_identity(N):
+    """T_Ring-AR = T_Ring-RS + T_Ring-AG."""
+    a, b, M = 5e-6, 450e9, 1 << 24
+    assert model.time("allreduce", "ring", N, M, a, b) == pytest.approx(
+        model.time("reducescatter", "ring", N, M, a, b) + model.time("allgather", "ring", N, M, a, b))
+
+
+def test_pipelines_reduce_to_their_k1_forms():
+    a, b, M = 5e-6, 450e9, 1 << 20
+    assert model.time("broadcast", "chain_pipe", 8, M, a, b, 1) == pytest.approx(model.time("broadcast", "chain", 8, M, a, b))
+    assert model.time("broadcast", "binomial_pipe", 8, M, a, b, 1) == pytest.approx(model.time("broadcast", "binomial", 8, M, a, b))
+
+
+def test_best_chunks_is_the_argmin_of_the_formula():
+    a, b = 5e-6, 450e9
+    got = [model.best_chunks("chain_pipe", 8, m, a, b) for m in (1024, 65536, 4 << 20, 64 << 20)]
+    assert got == [1, 1, 3, 13]
+    got = [model.best_chunks("binomial_pipe", 8, m, a, b) for m in (1024, 65536, 4 << 20, 64 << 20)]
+    assert got == [1, 1, 2, 8]
+    for m in (1024, 4 << 20, 64 << 20):
+        k = model.best_chunks("chain_pipe", 8, m, a, b)
+        t = model.time("broadcast", "chain_pipe", 8, m, a, b, k)
+        assert all(model.time("broadcast", "chain_pipe", 8, m, a, b, j) >= t for j in range(1, 200))
