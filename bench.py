@@ -68,6 +68,31 @@ def cpu_baseline(inputs_host, N: int, count: int, algo: str):
                       f"numpy single-threaded, {dt:.2f} s"}
 
 
+def calibrate(dev, gib: int = 2, reps: int = 10) -> dict:
+    """Achievable HBM rate of plain streams: copy reads and writes each byte
+    once (2 x bytes moved), add reads two operands and writes one (3 x bytes)."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    n = (gib << 30) // 4
+    a = torch.randn(n, device=dev)
+    b = torch.randn(n, device=dev)
+    c = torch.empty(n, device=dev)
+    out = {}
+    for name, fn, moved in (("copy", lambda: coll.coll_calib_copy(c, a), 2),
+                            ("add", lambda: coll.coll_calib_add(c, a, b), 3)):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        out[name] = {"bytes": moved * n * 4, "ms": round(ms, 4), "GBps": round(moved * n * 4 / ms / 1e6, 1)}
+    return {"calibration": out, "buffer_GiB": gib}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +103,8 @@ def main() -> int:
     ap.add_argument("--nranks", type=int, default=8)
     ap.add_argument("--mib", type=int, default=256, help="MiB per rank")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure the plain copy (1R+1W) and add (2R+1W) streams and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs N virtual ranks on one GPU; --gpus above 1 is not supported",
@@ -94,6 +121,9 @@ def main() -> int:
     import seeded_inputs as si
 
     dev = torch.device("cuda:0")
+    if args.calibrate:
+        print(json.dumps(calibrate(dev)))
+        return 0
     N, M = args.nranks, args.mib << 20
     count = M // 4
     coll.coll_set_option("exec", 1 if args.exec == "step" else 0)

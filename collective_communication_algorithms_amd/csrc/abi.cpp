@@ -23,10 +23,12 @@ thread_local coll_counts_t t_last{};
 thread_local uint64_t* t_sums = nullptr;
 thread_local size_t t_sums_cap = 0;
 
-std::atomic<int64_t> opt_exec{0};
+std::atomic<int64_t> opt_exec{0};                       // 0 auto, 1 step, 2 persistent
 std::atomic<int64_t> opt_group{0};
 std::atomic<int64_t> opt_grid{0};
-std::atomic<int64_t> opt_nt{1};
+std::atomic<int64_t> opt_nt{NT_ALL};
+std::atomic<int64_t> opt_reverse{1};
+std::atomic<int64_t> opt_step_min{int64_t(128) << 20};  // auto: per-step launches from this many column bytes
 
 constexpr uint32_t PERM_LDS_BYTES = 64 * 1024;
 
@@ -118,8 +120,8 @@ coll_status_t device_info(int dev, DevInfo*& out) {
   return COLL_OK;
 }
 
-int occupancy_rows(int dev, int dt, int op, bool cks, bool nt) {
-  const uint64_t key = (uint64_t(dev) << 32) | uint64_t(dt * 64 + op * 4 + (cks ? 2 : 0) + (nt ? 1 : 0));
+int occupancy_rows(int dev, int dt, int op, bool cks, uint32_t nt) {
+  const uint64_t key = (uint64_t(dev) << 32) | uint64_t(dt * 256 + op * 32 + (cks ? 16 : 0) + nt);
   auto it = g_occ.find(key);
   if (it != g_occ.end()) return it->second;
   const int n = rows_blocks_per_cu(dt, op, cks, nt);
@@ -276,8 +278,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     he = launch_fill_u64(t_sums, uint64_t(b.nrows), 0, stream);
     if (he != hipSuccess) return hip_fail(he, "checksum clear");
   }
-  const bool nt = opt_nt.load() != 0;
-  const bool step_mode = opt_exec.load() == 1;
+  const uint32_t ntmask = uint32_t(opt_nt.load());
 
   RankPtrs ptrs;
   bool bases16 = true;
@@ -298,28 +299,35 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.items = e->d_items;
       a.steps = e->d_steps;
       a.sums = t_sums;
-      a.nontemporal = nt;
       a.bases16 = bases16;
+      a.reverse_odd = opt_reverse.load() != 0;
       a.p = ptrs;
-      const uint64_t resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, nt));
-      uint64_t cap = resident;
+      const int64_t xm = opt_exec.load();
+      const bool step_mode = xm == 1 || (xm == 0 && int64_t(ph.colspace) >= opt_step_min.load());
+      a.remap = step_mode;
+      const uint64_t resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, ntmask));
+      // one launch for all steps: at most the resident work groups (more would
+      // only queue behind the first wave); one launch per step: as many work
+      // groups as there are column groups, dispatched in waves
+      uint64_t cap = step_mode ? uint64_t(1) << 16 : resident;
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
-      a.group_tiles = pick_group_tiles(ph.colspace, cap);
+      a.group_tiles = pick_group_tiles(ph.colspace, step_mode ? resident : cap);
       const uint64_t gbytes = uint64_t(a.group_tiles) * TILE_BYTES;
       const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
       const uint32_t grid = uint32_t(std::min(groups, cap));
       for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
         a.s0 = s0;
         a.s1 = step_mode ? s0 + 1 : ph.s1;
-        he = launch_rows(a, dt, int(op), cks, grid, stream);
+        he = launch_rows(a, dt, int(op), cks, ntmask, grid, stream);
         if (he != hipSuccess) return hip_fail(he, "row kernel launch");
       }
     } else {
+      const bool step_mode = opt_exec.load() == 1;
       PermArgs a{};
       a.items = e->d_items;
       a.steps = e->d_steps;
       a.sums = t_sums;
-      a.nontemporal = nt;
+      a.nontemporal = ntmask;
       a.p = ptrs;
       int unit = b.perm_unit;
       while (unit > 1 && (align_or % uint64_t(unit))) unit >>= 1;
@@ -330,7 +338,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.tile_units = tu;
       const uint32_t lds = tu * uint32_t(unit) * uint32_t(N);
       const uint64_t ntiles = (uint64_t(a.ncols_units) + tu - 1) / tu;
-      uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, cks, nt));
+      uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, cks, ntmask != 0));
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
       const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(ntiles, cap)));
       for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
@@ -425,8 +433,15 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity) {
 coll_status_t coll_set_option(coll_option_t key, int64_t value) {
   switch (key) {
     case COLL_OPT_EXEC:
-      if (value != 0 && value != 1) return fail(COLL_ERR_INVALID_ARG, "exec mode is 0 or 1");
+      if (value < 0 || value > 2) return fail(COLL_ERR_INVALID_ARG, "exec mode is 0, 1 or 2");
       opt_exec = value;
+      return COLL_OK;
+    case COLL_OPT_REVERSE:
+      opt_reverse = value ? 1 : 0;
+      return COLL_OK;
+    case COLL_OPT_STEP_MIN_BYTES:
+      if (value < 0) return fail(COLL_ERR_INVALID_ARG, "negative size");
+      opt_step_min = value;
       return COLL_OK;
     case COLL_OPT_GROUP_TILES:
       if (value < 0 || value > 64) return fail(COLL_ERR_INVALID_ARG, "group tiles in [0, 64]");
@@ -437,7 +452,8 @@ coll_status_t coll_set_option(coll_option_t key, int64_t value) {
       opt_grid = value;
       return COLL_OK;
     case COLL_OPT_NONTEMPORAL:
-      opt_nt = value ? 1 : 0;
+      if (value < 0 || value > 7) return fail(COLL_ERR_INVALID_ARG, "nontemporal mask in [0, 7]");
+      opt_nt = value;
       return COLL_OK;
   }
   return fail(COLL_ERR_INVALID_ARG, "unknown option");

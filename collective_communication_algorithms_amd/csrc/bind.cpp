@@ -173,8 +173,20 @@ Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
     d.item0 = uint32_t(b.items.size());
     d.nitems = uint32_t(per_step[si].size());
     const bool perm_step = bruck && si > 0;
-    d.staged = perm_step && s.steps[si].staged ? 1u : 0u;
-    d.gsize = d.staged ? uint32_t(s.N) : 1u;
+    const bool staged = perm_step && s.steps[si].staged;
+    d.flags = staged ? STEP_STAGED : 0u;
+    d.gsize = staged ? uint32_t(s.N) : 1u;
+    // same-destination accumulation (a Double Binary Tree parent with two
+    // children) must keep row order; every other step may be walked backwards
+    if (!perm_step) {
+      std::vector<const DevItem*> v;
+      for (auto& it : per_step[si]) v.push_back(&it);
+      std::sort(v.begin(), v.end(), [](const DevItem* x, const DevItem* y) {
+        return x->dst_rank != y->dst_rank ? x->dst_rank < y->dst_rank : x->col0 < y->col0;
+      });
+      for (size_t x = 1; x < v.size(); ++x)
+        if (v[x]->dst_rank == v[x - 1]->dst_rank && v[x]->col0 < v[x - 1]->col1) d.flags |= STEP_ORDERED;
+    }
     for (auto& it : per_step[si]) {
       if (perm_step) perm_cols = std::max(perm_cols, it.col1);
       else rows_cols = std::max(rows_cols, it.col1);

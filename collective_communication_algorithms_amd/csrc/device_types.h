@@ -39,10 +39,15 @@ struct DevItem {          // 48 bytes
   uint32_t pad;
 };
 
+enum : uint32_t {
+  STEP_STAGED = 1u << 0,  // in-place permutation: all reads of a group before its writes
+  STEP_ORDERED = 1u << 1, // some items accumulate into the same destination: keep item order
+};
+
 struct DevStep {          // 16 bytes
   uint32_t item0, nitems; // items [item0, item0 + nitems)
   uint32_t gsize;         // staged steps: items per staging group (groups are contiguous)
-  uint32_t staged;
+  uint32_t flags;         // STEP_*
 };
 
 struct RankPtrs {
@@ -56,15 +61,18 @@ enum Op : int { OP_SUM = 0, OP_MAX = 1, OP_MIN = 2 };
 constexpr int TILE_BYTES = 4096;      // 256 threads x 16 bytes
 constexpr int BLOCK_THREADS = 256;
 
+// Nontemporal hints, per operand of a row.
+enum : uint32_t { NT_SRC = 1u << 0, NT_DSRC = 1u << 1, NT_DST = 1u << 2, NT_ALL = 7u };
+
 struct RowsArgs {                     // row kernel (copy / recv_and_reduce)
   const DevItem* items;
   const DevStep* steps;
   uint64_t* sums;                     // per-row checksums or nullptr
   uint32_t s0, s1;                    // steps [s0, s1)
   uint32_t group_tiles;               // 4 KiB tiles per owned group
-  uint32_t nontemporal;
   uint32_t bases16;                   // all rank base pointers 16-byte aligned
-  uint32_t pad;
+  uint32_t reverse_odd;               // walk odd steps backwards (short reuse distance)
+  uint32_t remap;                     // one launch per step: odd steps may also renumber groups
   RankPtrs p;
 };
 
@@ -75,7 +83,7 @@ struct PermArgs {                     // staged permutation kernel (Bruck)
   uint32_t s0, s1;
   uint32_t tile_units;                // units per owned tile of the block column
   uint32_t ncols_units;               // block width in units
-  uint32_t nontemporal;
+  uint32_t nontemporal;               // NT_* mask (loads: NT_SRC, stores: NT_DST)
   uint32_t pad;
   RankPtrs p;
 };

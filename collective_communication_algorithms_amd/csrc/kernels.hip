@@ -39,7 +39,11 @@ __device__ __forceinline__ GLOBAL T* gptr(char* p) {
 
 template <class T>
 __device__ __forceinline__ T cload(const T* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
   return *(const CONSTANT T*)(p);
+#else
+  return *p;  // the host pass only needs the kernels to parse
+#endif
 }
 
 template <bool NT>
@@ -185,14 +189,14 @@ struct ItemView {
 };
 
 // One 16-byte column unit x of the item, clipped to [lo, hi).
-template <int DT, int OP, bool CKS, bool NT>
+template <int DT, int OP, bool CKS, int NTM>
 __device__ __forceinline__ void do_unit(const ItemView& v, uint64_t x, uint64_t lo, uint64_t hi, bool vec,
                                         uint64_t& acc) {
   if (x + 16 <= lo || x >= hi) return;
   if (vec && x >= lo && x + 16 <= hi) {
-    u32x4 s = ld16<NT>(v.src + x);
-    if (v.reduce) s = combine16<DT, OP>(ld16<NT>(v.dsrc + x), s);
-    st16<NT>(v.dst + x, s);
+    u32x4 s = ld16<(NTM & NT_SRC) != 0>(v.src + x);
+    if (v.reduce) s = combine16<DT, OP>(ld16<(NTM & NT_DSRC) != 0>(v.dsrc + x), s);
+    st16<(NTM & NT_DST) != 0>(v.dst + x, s);
     if constexpr (CKS) acc += words16(s, v.shift * 8u);
     return;
   }
@@ -207,43 +211,66 @@ __device__ __forceinline__ void do_unit(const ItemView& v, uint64_t x, uint64_t 
 }
 
 // U full, aligned units at x0, x0 + 4 KiB, ...: all loads issued before the stores.
-template <int U, int DT, int OP, bool CKS, bool NT>
+template <int U, int DT, int OP, bool CKS, int NTM>
 __device__ __forceinline__ void do_batch(const ItemView& v, uint64_t x0, uint64_t& acc) {
   u32x4 s[U];
 #pragma unroll
-  for (int k = 0; k < U; ++k) s[k] = ld16<NT>(v.src + x0 + uint64_t(k) * TILE_BYTES);
+  for (int k = 0; k < U; ++k) s[k] = ld16<(NTM & NT_SRC) != 0>(v.src + x0 + uint64_t(k) * TILE_BYTES);
   if (v.reduce) {
     u32x4 d[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) d[k] = ld16<NT>(v.dsrc + x0 + uint64_t(k) * TILE_BYTES);
+    for (int k = 0; k < U; ++k) d[k] = ld16<(NTM & NT_DSRC) != 0>(v.dsrc + x0 + uint64_t(k) * TILE_BYTES);
 #pragma unroll
     for (int k = 0; k < U; ++k) s[k] = combine16<DT, OP>(d[k], s[k]);
   }
 #pragma unroll
   for (int k = 0; k < U; ++k) {
-    st16<NT>(v.dst + x0 + uint64_t(k) * TILE_BYTES, s[k]);
+    st16<(NTM & NT_DST) != 0>(v.dst + x0 + uint64_t(k) * TILE_BYTES, s[k]);
     if constexpr (CKS) acc += words16(s[k], v.shift * 8u);
+  }
+}
+
+template <int DT, int OP, bool CKS, int NTM>
+__device__ __forceinline__ void do_group(const ItemView& v, uint64_t gb, uint64_t gbytes, uint32_t gt,
+                                         uint64_t col0, uint64_t col1, bool vec, uint64_t tofs, uint64_t& acc) {
+  const uint64_t lo = gb > col0 ? gb : col0;
+  const uint64_t hi = gb + gbytes < col1 ? gb + gbytes : col1;
+  if (vec && lo == gb && hi == gb + gbytes) {
+    uint32_t k = 0;
+    for (; k + 4 <= gt; k += 4) do_batch<4, DT, OP, CKS, NTM>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
+    for (; k < gt; ++k) do_batch<1, DT, OP, CKS, NTM>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
+  } else {
+    for (uint32_t k = 0; k < gt; ++k)
+      do_unit<DT, OP, CKS, NTM>(v, gb + uint64_t(k) * TILE_BYTES + tofs, lo, hi, vec, acc);
   }
 }
 
 // Work group w owns the groups g = w, w + G, w + 2G, ... of `group_tiles`
 // consecutive 4 KiB column tiles; thread t owns bytes [16t, 16t + 16) of every
-// tile.  Items of a step are walked in row order, steps in order.
-template <int DT, int OP, bool CKS, bool NT>
+// tile.  Steps are walked in order.  With reverse_odd, odd steps walk the
+// items (unless some of them accumulate into the same destination) and each
+// item's groups backwards, so the columns a work group wrote last are the
+// first it reads again.  With remap (only when each launch runs one step, so
+// ownership may change between steps) odd steps also renumber the work groups
+// back to front, which reverses the order the groups are dispatched in.
+template <int DT, int OP, bool CKS, int NTM>
 __global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
-  const uint32_t G = gridDim.x, w = blockIdx.x;
+  const uint32_t G = gridDim.x;
   const uint32_t gt = a.group_tiles;
   const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
   const uint64_t tofs = uint64_t(threadIdx.x) * 16u;
   for (uint32_t s = a.s0; s < a.s1; ++s) {
     const DevStep st = cload(a.steps + s);
-    for (uint32_t i = st.item0, ie = st.item0 + st.nitems; i < ie; ++i) {
+    const bool rev = a.reverse_odd && (s & 1u);
+    const uint32_t w = (rev && a.remap) ? G - 1 - blockIdx.x : blockIdx.x;
+    const bool back = rev && !(st.flags & STEP_ORDERED);
+    for (uint32_t n = 0; n < st.nitems; ++n) {
+      const uint32_t i = st.item0 + (back ? st.nitems - 1 - n : n);
       const DevItem it = cload(a.items + i);
       if (it.col1 <= it.col0) continue;
       const uint32_t gfirst = uint32_t(it.col0 / gbytes);
       const uint32_t glast = uint32_t((it.col1 - 1) / gbytes);
-      uint32_t g = gfirst + (w + G - gfirst % G) % G;
-      if (g > glast) continue;
+      if (glast < w) continue;  // every owned group is >= w
       ItemView v;
       v.src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
                                                                        : a.p.recv[it.src_rank]) + it.src_delta;
@@ -254,18 +281,14 @@ __global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
       v.shift = (it.flags >> ITEM_CKS_SHIFT) & 3u;
       const bool vec = a.bases16 && (it.flags & ITEM_VEC);
       uint64_t acc = 0;
-      for (; g <= glast; g += G) {
-        const uint64_t gb = uint64_t(g) * gbytes;
-        const uint64_t lo = gb > it.col0 ? gb : it.col0;
-        const uint64_t hi = gb + gbytes < it.col1 ? gb + gbytes : it.col1;
-        if (vec && lo == gb && hi == gb + gbytes) {
-          uint32_t k = 0;
-          for (; k + 4 <= gt; k += 4) do_batch<4, DT, OP, CKS, NT>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
-          for (; k < gt; ++k) do_batch<1, DT, OP, CKS, NT>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
-        } else {
-          for (uint32_t k = 0; k < gt; ++k)
-            do_unit<DT, OP, CKS, NT>(v, gb + uint64_t(k) * TILE_BYTES + tofs, lo, hi, vec, acc);
-        }
+      if (!rev) {
+        for (uint32_t g = gfirst + (w + G - gfirst % G) % G; g <= glast; g += G)
+          do_group<DT, OP, CKS, NTM>(v, uint64_t(g) * gbytes, gbytes, gt, it.col0, it.col1, vec, tofs, acc);
+      } else {
+        // largest owned group <= glast, then downwards while >= gfirst
+        int64_t g = int64_t(glast) - int64_t((glast - w) % G);
+        for (; g >= int64_t(gfirst); g -= G)
+          do_group<DT, OP, CKS, NTM>(v, uint64_t(g) * gbytes, gbytes, gt, it.col0, it.col1, vec, tofs, acc);
       }
       if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
     }
@@ -320,7 +343,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void perm_kernel(const PermArgs a) {
   const uint32_t ntiles = (ncol + tu - 1) / tu;
   for (uint32_t s = a.s0; s < a.s1; ++s) {
     const DevStep st = cload(a.steps + s);
-    if (!st.staged) {
+    if (!(st.flags & STEP_STAGED)) {
       for (uint32_t i = st.item0, ie = st.item0 + st.nitems; i < ie; ++i) {
         const DevItem it = cload(a.items + i);
         const char* src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
@@ -415,14 +438,27 @@ __global__ __launch_bounds__(BLOCK_THREADS) void calib_kernel(char* dst, const c
 
 typedef void (*RowsFn)(RowsArgs);
 
+template <int DT, int OP, bool CKS>
+static RowsFn rows_fn_nt(uint32_t nt) {
+  switch (nt & 7u) {
+    case 0: return rows_kernel<DT, OP, CKS, 0>;
+    case 1: return rows_kernel<DT, OP, CKS, 1>;
+    case 2: return rows_kernel<DT, OP, CKS, 2>;
+    case 3: return rows_kernel<DT, OP, CKS, 3>;
+    case 4: return rows_kernel<DT, OP, CKS, 4>;
+    case 5: return rows_kernel<DT, OP, CKS, 5>;
+    case 6: return rows_kernel<DT, OP, CKS, 6>;
+    default: return rows_kernel<DT, OP, CKS, 7>;
+  }
+}
+
 template <int DT, int OP>
-static RowsFn rows_fn(bool cks, bool nt) {
-  if (cks) return nt ? rows_kernel<DT, OP, true, true> : rows_kernel<DT, OP, true, false>;
-  return nt ? rows_kernel<DT, OP, false, true> : rows_kernel<DT, OP, false, false>;
+static RowsFn rows_fn(bool cks, uint32_t nt) {
+  return cks ? rows_fn_nt<DT, OP, true>(nt) : rows_fn_nt<DT, OP, false>(nt);
 }
 
 template <int DT>
-static RowsFn rows_fn_op(int op, bool cks, bool nt) {
+static RowsFn rows_fn_op(int op, bool cks, uint32_t nt) {
   switch (op) {
     case OP_SUM: return rows_fn<DT, OP_SUM>(cks, nt);
     case OP_MAX: return rows_fn<DT, OP_MAX>(cks, nt);
@@ -430,7 +466,7 @@ static RowsFn rows_fn_op(int op, bool cks, bool nt) {
   }
 }
 
-static RowsFn pick_rows(int dtype, int op, bool cks, bool nt) {
+static RowsFn pick_rows(int dtype, int op, bool cks, uint32_t nt) {
   switch (dtype) {
     case DT_I32: return rows_fn_op<DT_I32>(op, cks, nt);
     case DT_U8: return rows_fn_op<DT_U8>(op, cks, nt);
@@ -457,8 +493,9 @@ static PermFn pick_perm(int unit, bool cks, bool nt) {
   }
 }
 
-hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t grid, hipStream_t stream) {
-  RowsFn f = pick_rows(dtype, op, cks, a.nontemporal != 0);
+hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, uint32_t grid,
+                       hipStream_t stream) {
+  RowsFn f = pick_rows(dtype, op, cks, nt);
   hipLaunchKernelGGL(f, dim3(grid), dim3(BLOCK_THREADS), 0, stream, a);
   return hipGetLastError();
 }
@@ -470,7 +507,7 @@ hipError_t launch_perm(const PermArgs& a, int unit, bool cks, uint32_t grid, uin
   return hipGetLastError();
 }
 
-int rows_blocks_per_cu(int dtype, int op, bool cks, bool nt) {
+int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt) {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_rows(dtype, op, cks, nt), BLOCK_THREADS, 0) != hipSuccess)
     return 1;

@@ -16,18 +16,18 @@ from tests.gpu_util import assert_parity
 pytestmark = pytest.mark.gpu
 
 
+DEFAULT_OPTIONS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": 7, "reverse": 1,
+                   "step_min_bytes": 128 << 20}
+
+
 @pytest.fixture(autouse=True)
 def _gpu(gpu_device):
     import collective_communication_algorithms_amd as coll
-    coll.coll_set_option("exec", 0)
-    coll.coll_set_option("group_tiles", 0)
-    coll.coll_set_option("max_grid", 0)
-    coll.coll_set_option("nontemporal", 1)
+    for k, v in DEFAULT_OPTIONS.items():
+        coll.coll_set_option(k, v)
     yield
-    coll.coll_set_option("exec", 0)
-    coll.coll_set_option("group_tiles", 0)
-    coll.coll_set_option("max_grid", 0)
-    coll.coll_set_option("nontemporal", 1)
+    for k, v in DEFAULT_OPTIONS.items():
+        coll.coll_set_option(k, v)
 
 
 # --- the configurations, at sizes the oracle finishes in seconds -------------------
@@ -193,30 +193,46 @@ def test_bf16_rounding_ties():
 
 # --- execution modes and launch shapes give identical results ------------------------
 
-@pytest.mark.parametrize("exec_mode", [0, 1])
+@pytest.mark.parametrize("reverse", [0, 1])
+@pytest.mark.parametrize("exec_mode", [1, 2])
 @pytest.mark.parametrize("group_tiles,max_grid", [(0, 0), (1, 0), (2, 5), (8, 3), (16, 1), (4, 7)])
-def test_launch_shapes(exec_mode, group_tiles, max_grid):
+def test_launch_shapes(exec_mode, group_tiles, max_grid, reverse):
     import collective_communication_algorithms_amd as coll
     coll.coll_set_option("exec", exec_mode)
+    coll.coll_set_option("reverse", reverse)
     coll.coll_set_option("group_tiles", group_tiles)
     coll.coll_set_option("max_grid", max_grid)
     N, count = 8, (3 << 20) // 4 + 12345
     a = si.rank_arrays(3, N, count, "float32")
-    for algo in ("ring", "dbt"):
+    for algo in ("ring", "rhd", "dbt"):
         assert_parity("allreduce", algo, a, "float32", checksums=True)
+    assert_parity("gather", "binomial", a, "float32", root=3, inplace=False)
     b = si.rank_arrays(5, 8, 8 * 20000, "bfloat16")
     assert_parity("alltoall", "bruck", b, "bfloat16", checksums=True)
     assert_parity("broadcast", "binomial_pipe", si.rank_arrays(2, 8, 300001, "uint8"), "uint8", k=8)
 
 
-@pytest.mark.parametrize("nt", [0, 1])
+@pytest.mark.parametrize("nt", list(range(8)))
 def test_nontemporal_switch(nt):
     import collective_communication_algorithms_amd as coll
     coll.coll_set_option("nontemporal", nt)
     a = si.rank_arrays(3, 8, 1 << 18, "float32")
     assert_parity("allreduce", "ring", a, "float32")
+    assert_parity("allreduce", "dbt", a, "float32")
     b = si.rank_arrays(5, 16, 16 * 4096, "bfloat16")
     assert_parity("alltoall", "bruck", b, "bfloat16")
+    assert_parity("alltoall", "pairwise", b, "bfloat16")
+
+
+def test_automatic_mode_switches_at_the_threshold():
+    """The automatic mode picks per-step launches from the threshold up; both
+    sides of the threshold give the oracle's result."""
+    import collective_communication_algorithms_amd as coll
+    a = si.rank_arrays(3, 8, (1 << 20) // 4, "float32")
+    for thr in (1, 1 << 40):
+        coll.coll_set_option("step_min_bytes", thr)
+        for algo in ("ring", "rhd", "dbt"):
+            assert_parity("allreduce", algo, a, "float32", checksums=True)
 
 
 def test_repeated_calls_reuse_cached_schedules():
