@@ -21,8 +21,7 @@ ALGOS = {"default": 0, "ring": 1, "rhd": 2, "dbt": 3, "binomial": 4, "chain_pipe
          "pairwise": 7, "bruck": 8}
 KINDS = {"allreduce": 0, "reducescatter": 1, "allgather": 2, "broadcast": 3, "scatter": 4, "gather": 5,
          "alltoall": 6}
-OPTIONS = {"exec": 0, "group_tiles": 1, "max_grid": 2, "nontemporal": 3, "reverse": 4,
-           "step_min_bytes": 5}
+OPTIONS = {"exec": 0, "group_tiles": 1, "max_grid": 2, "nontemporal": 3, "reverse": 4}
 MAX_RANKS = 128
 
 COLLECTIVES = ("coll_allreduce", "coll_reducescatter", "coll_allgather", "coll_broadcast", "coll_scatter",

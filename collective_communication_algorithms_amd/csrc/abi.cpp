@@ -23,14 +23,21 @@ thread_local coll_counts_t t_last{};
 thread_local uint64_t* t_sums = nullptr;
 thread_local size_t t_sums_cap = 0;
 
-std::atomic<int64_t> opt_exec{0};                       // 0 auto, 1 step, 2 persistent
-std::atomic<int64_t> opt_group{0};
-std::atomic<int64_t> opt_grid{0};
-std::atomic<int64_t> opt_nt{NT_ALL};
+std::atomic<int64_t> opt_exec{0};      // 0: one launch per phase, 1: one launch per step
+std::atomic<int64_t> opt_group{0};     // 0: automatic
+std::atomic<int64_t> opt_grid{0};      // 0: automatic
+std::atomic<int64_t> opt_nt{-1};       // -1: automatic, else an NT_* mask
 std::atomic<int64_t> opt_reverse{1};
-std::atomic<int64_t> opt_step_min{int64_t(128) << 20};  // auto: per-step launches from this many column bytes
 
-constexpr uint32_t PERM_LDS_BYTES = 64 * 1024;
+// Working sets up to the 256 MiB memory-side cache of MI355X stay there between
+// steps when accessed normally; larger ones stream, and then nontemporal source
+// loads (whose data is consumed once per step) keep the cache for the stores
+// the next step reads back.  Measured on the Ring / Halving-Doubling / tree
+// AllReduce, Broadcast and ReduceScatter / AllGather sweeps.
+constexpr uint64_t CACHE_RESIDENT_BYTES = uint64_t(256) << 20;
+
+uint32_t auto_nt(uint64_t footprint) { return footprint <= CACHE_RESIDENT_BYTES ? 0u : NT_SRC; }
+
 
 coll_status_t fail(coll_status_t st, const std::string& msg) {
   t_err = msg;
@@ -79,16 +86,25 @@ struct KeyHash {
   }
 };
 
+struct DevList {                // work lists of one row phase for one launch shape
+  size_t phase = 0;
+  uint32_t G = 0, gt = 0;
+  bool reverse = false, per_step = false;
+  uint32_t launches = 0;
+  uint32_t* d_off = nullptr;
+  DevItem* d_list = nullptr;
+};
+
 struct Entry {
   Bound bound;
   DevItem* d_items = nullptr;
   DevStep* d_steps = nullptr;
+  std::vector<DevList> lists;
   uint64_t last_use = 0;
 };
 
 struct DevInfo {
   int cus = 0;
-  bool lds_set = false;
 };
 
 std::mutex g_mu;
@@ -101,8 +117,59 @@ constexpr size_t CACHE_CAP = 512;
 void free_entry(Entry& e) {
   if (e.d_items) (void)hipFree(e.d_items);
   if (e.d_steps) (void)hipFree(e.d_steps);
+  for (DevList& l : e.lists) {
+    if (l.d_off) (void)hipFree(l.d_off);
+    if (l.d_list) (void)hipFree(l.d_list);
+  }
+  e.lists.clear();
   e.d_items = nullptr;
   e.d_steps = nullptr;
+}
+
+// The work lists of phase `pi` for this launch shape, built and uploaded on first use.
+coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool reverse, bool per_step, DevList*& out) {
+  for (DevList& l : e.lists)
+    if (l.phase == pi && l.G == G && l.gt == gt && l.reverse == reverse && l.per_step == per_step) {
+      out = &l;
+      return COLL_OK;
+    }
+  if (e.lists.size() >= 8) {  // a few launch shapes per schedule are plenty; drop the oldest
+    hipError_t he = hipDeviceSynchronize();
+    if (he != hipSuccess) return hip_fail(he, "hipDeviceSynchronize");
+    DevList& l = e.lists.front();
+    if (l.d_off) (void)hipFree(l.d_off);
+    if (l.d_list) (void)hipFree(l.d_list);
+    e.lists.erase(e.lists.begin());
+  }
+  std::vector<uint32_t> off;
+  std::vector<DevItem> list;
+  const Phase& ph = e.bound.phases[pi];
+  build_worklist(e.bound, ph, G, gt, reverse, per_step, off, list);
+  DevList l;
+  l.phase = pi;
+  l.G = G;
+  l.gt = gt;
+  l.reverse = reverse;
+  l.per_step = per_step;
+  l.launches = per_step ? ph.s1 - ph.s0 : 1;
+  hipError_t he = hipMalloc(reinterpret_cast<void**>(&l.d_off), off.size() * sizeof(uint32_t));
+  if (he != hipSuccess) return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
+  he = hipMalloc(reinterpret_cast<void**>(&l.d_list), std::max<size_t>(list.size(), 1) * sizeof(DevItem));
+  if (he != hipSuccess) {
+    (void)hipFree(l.d_off);
+    return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
+  }
+  he = hipMemcpy(l.d_off, off.data(), off.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+  if (he == hipSuccess && !list.empty())
+    he = hipMemcpy(l.d_list, list.data(), list.size() * sizeof(DevItem), hipMemcpyHostToDevice);
+  if (he != hipSuccess) {
+    (void)hipFree(l.d_off);
+    (void)hipFree(l.d_list);
+    return hip_fail(he, "hipMemcpy");
+  }
+  e.lists.push_back(l);
+  out = &e.lists.back();
+  return COLL_OK;
 }
 
 coll_status_t device_info(int dev, DevInfo*& out) {
@@ -111,9 +178,6 @@ coll_status_t device_info(int dev, DevInfo*& out) {
     DevInfo di;
     hipError_t e = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    e = set_perm_lds_limit(PERM_LDS_BYTES);
-    if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
-    di.lds_set = true;
     it = g_dev.emplace(dev, di).first;
   }
   out = &it->second;
@@ -129,11 +193,12 @@ int occupancy_rows(int dev, int dt, int op, bool cks, uint32_t nt) {
   return n;
 }
 
-int occupancy_perm(int dev, int unit, bool cks, bool nt) {
-  const uint64_t key = (uint64_t(dev) << 32) | (uint64_t(1) << 31) | uint64_t(unit * 4 + (cks ? 2 : 0) + (nt ? 1 : 0));
+int occupancy_perm(int dev, int unit, int slots, bool cks, bool nt) {
+  const uint64_t key = (uint64_t(dev) << 32) | (uint64_t(1) << 31) |
+                       uint64_t(slots * 256 + unit * 4 + (cks ? 2 : 0) + (nt ? 1 : 0));
   auto it = g_occ.find(key);
   if (it != g_occ.end()) return it->second;
-  const int n = perm_blocks_per_cu(unit, cks, nt, PERM_LDS_BYTES);
+  const int n = perm_blocks_per_cu(unit, slots, cks, nt);
   g_occ[key] = n;
   return n;
 }
@@ -278,7 +343,9 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     he = launch_fill_u64(t_sums, uint64_t(b.nrows), 0, stream);
     if (he != hipSuccess) return hip_fail(he, "checksum clear");
   }
-  const uint32_t ntmask = uint32_t(opt_nt.load());
+  const uint64_t footprint = uint64_t(N) * uint64_t(count) * uint64_t(sz) * (inplace ? 1u : 2u);
+  const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint) : uint32_t(opt_nt.load());
+  const bool step_mode = opt_exec.load() == 1;
 
   RankPtrs ptrs;
   bool bases16 = true;
@@ -293,36 +360,32 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
 
   const int dt = int(dtype) == COLL_INT32 ? DT_I32 : int(dtype) == COLL_UINT8 ? DT_U8
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
-  for (const Phase& ph : b.phases) {
+  for (size_t pi = 0; pi < b.phases.size(); ++pi) {
+    const Phase& ph = b.phases[pi];
     if (ph.kind == Phase::ROWS) {
-      RowsArgs a{};
-      a.items = e->d_items;
-      a.steps = e->d_steps;
-      a.sums = t_sums;
-      a.bases16 = bases16;
-      a.reverse_odd = opt_reverse.load() != 0;
-      a.p = ptrs;
-      const int64_t xm = opt_exec.load();
-      const bool step_mode = xm == 1 || (xm == 0 && int64_t(ph.colspace) >= opt_step_min.load());
-      a.remap = step_mode;
       const uint64_t resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, ntmask));
-      // one launch for all steps: at most the resident work groups (more would
-      // only queue behind the first wave); one launch per step: as many work
-      // groups as there are column groups, dispatched in waves
-      uint64_t cap = step_mode ? uint64_t(1) << 16 : resident;
+      // one launch for all steps: the resident work groups; one launch per
+      // step: several waves of them
+      uint64_t cap = step_mode ? 4 * resident : resident;
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
-      a.group_tiles = pick_group_tiles(ph.colspace, step_mode ? resident : cap);
-      const uint64_t gbytes = uint64_t(a.group_tiles) * TILE_BYTES;
+      const uint32_t gt = pick_group_tiles(ph.colspace, resident);
+      const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
       const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
       const uint32_t grid = uint32_t(std::min(groups, cap));
-      for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
-        a.s0 = s0;
-        a.s1 = step_mode ? s0 + 1 : ph.s1;
+      DevList* L = nullptr;
+      st = get_list(*e, pi, grid, gt, opt_reverse.load() != 0, step_mode, L);
+      if (st != COLL_OK) return st;
+      RowsArgs a{};
+      a.list = L->d_list;
+      a.sums = t_sums;
+      a.bases16 = bases16;
+      a.p = ptrs;
+      for (uint32_t j = 0; j < L->launches; ++j) {
+        a.off = L->d_off + size_t(j) * (grid + 1);
         he = launch_rows(a, dt, int(op), cks, ntmask, grid, stream);
         if (he != hipSuccess) return hip_fail(he, "row kernel launch");
       }
     } else {
-      const bool step_mode = opt_exec.load() == 1;
       PermArgs a{};
       a.items = e->d_items;
       a.steps = e->d_steps;
@@ -332,19 +395,22 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       int unit = b.perm_unit;
       while (unit > 1 && (align_or % uint64_t(unit))) unit >>= 1;
       a.ncols_units = uint32_t(ph.colspace / uint64_t(unit));
-      const uint32_t budget_units = PERM_LDS_BYTES / uint32_t(unit) / uint32_t(N);
-      uint32_t tu = budget_units >= 64 ? (budget_units / 64) * 64 : std::max<uint32_t>(1, budget_units);
-      tu = std::min<uint32_t>(tu, std::max<uint32_t>(a.ncols_units, 1));
-      a.tile_units = tu;
-      const uint32_t lds = tu * uint32_t(unit) * uint32_t(N);
+      // every staged Bruck step permutes groups of N rows; each of the 4 waves
+      // holds ceil(N/4) rows, 2^lg units per lane of each
+      const uint32_t ipw = uint32_t(N + 3) / 4;
+      const int slots = ipw <= 16 ? 16 : 32;
+      uint32_t lg = 0;
+      while ((ipw << (lg + 1)) <= uint32_t(slots) && (64u << (lg + 1)) <= std::max<uint32_t>(a.ncols_units, 64)) ++lg;
+      a.lg_upl = lg;
+      const uint64_t tu = uint64_t(64) << lg;
       const uint64_t ntiles = (uint64_t(a.ncols_units) + tu - 1) / tu;
-      uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, cks, ntmask != 0));
+      uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, slots, cks, ntmask != 0));
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
       const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(ntiles, cap)));
       for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
         a.s0 = s0;
         a.s1 = step_mode ? s0 + 1 : ph.s1;
-        he = launch_perm(a, unit, cks, grid, lds, stream);
+        he = launch_perm(a, unit, slots, cks, grid, stream);
         if (he != hipSuccess) return hip_fail(he, "permutation kernel launch");
       }
     }
@@ -433,15 +499,11 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity) {
 coll_status_t coll_set_option(coll_option_t key, int64_t value) {
   switch (key) {
     case COLL_OPT_EXEC:
-      if (value < 0 || value > 2) return fail(COLL_ERR_INVALID_ARG, "exec mode is 0, 1 or 2");
+      if (value != 0 && value != 1) return fail(COLL_ERR_INVALID_ARG, "exec mode is 0 or 1");
       opt_exec = value;
       return COLL_OK;
     case COLL_OPT_REVERSE:
       opt_reverse = value ? 1 : 0;
-      return COLL_OK;
-    case COLL_OPT_STEP_MIN_BYTES:
-      if (value < 0) return fail(COLL_ERR_INVALID_ARG, "negative size");
-      opt_step_min = value;
       return COLL_OK;
     case COLL_OPT_GROUP_TILES:
       if (value < 0 || value > 64) return fail(COLL_ERR_INVALID_ARG, "group tiles in [0, 64]");
@@ -452,7 +514,7 @@ coll_status_t coll_set_option(coll_option_t key, int64_t value) {
       opt_grid = value;
       return COLL_OK;
     case COLL_OPT_NONTEMPORAL:
-      if (value < 0 || value > 7) return fail(COLL_ERR_INVALID_ARG, "nontemporal mask in [0, 7]");
+      if (value < -1 || value > 7) return fail(COLL_ERR_INVALID_ARG, "nontemporal mask in [-1, 7]");
       opt_nt = value;
       return COLL_OK;
   }

@@ -230,4 +230,41 @@ Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
   return b;
 }
 
+void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
+                    bool per_step, std::vector<uint32_t>& off, std::vector<DevItem>& list) {
+  const uint64_t gbytes = uint64_t(group_tiles) * TILE_BYTES;
+  const uint32_t launches = per_step ? ph.s1 - ph.s0 : 1;
+  off.clear();
+  list.clear();
+  std::vector<std::vector<DevItem>> per(G);
+  for (uint32_t j = 0; j < launches; ++j) {
+    for (auto& v : per) v.clear();
+    const uint32_t sa = per_step ? ph.s0 + j : ph.s0, sb = per_step ? sa + 1 : ph.s1;
+    for (uint32_t s = sa; s < sb; ++s) {
+      const DevStep& st = b.steps[s];
+      const bool rev = reverse && (s & 1u);
+      const bool back = rev && !(st.flags & STEP_ORDERED);
+      for (uint32_t n = 0; n < st.nitems; ++n) {
+        const DevItem& it = b.items[st.item0 + (back ? st.nitems - 1 - n : n)];
+        if (it.col1 <= it.col0) continue;
+        const uint64_t g0 = it.col0 / gbytes, g1 = (it.col1 - 1) / gbytes;
+        for (uint64_t k = 0; k <= g1 - g0; ++k) {
+          const uint64_t g = rev ? g1 - k : g0 + k;
+          DevItem piece = it;
+          piece.col0 = std::max(it.col0, g * gbytes);
+          piece.col1 = std::min(it.col1, (g + 1) * gbytes);
+          uint32_t owner = uint32_t(g % G);
+          if (per_step && rev) owner = G - 1 - owner;
+          per[owner].push_back(piece);
+        }
+      }
+    }
+    for (uint32_t w = 0; w < G; ++w) {
+      off.push_back(uint32_t(list.size()));
+      list.insert(list.end(), per[w].begin(), per[w].end());
+    }
+    off.push_back(uint32_t(list.size()));
+  }
+}
+
 }  // namespace coll

@@ -31,6 +31,22 @@ struct Bound {
 // send to receive in the first step.
 Bound bind_schedule(const Schedule& s, int elem_size, bool inplace);
 
+// Work lists of one row phase on a grid of G work groups, with column groups
+// of `group_tiles` 4 KiB tiles.  Every item is cut at group boundaries and
+// each piece goes to the list of the work group that owns its group.
+//  one launch for the phase (per_step false): group g belongs to work group
+//    g mod G in every step, so each column is only ever touched by one work
+//    group and the steps need no synchronisation between work groups;
+//  one launch per step (per_step true): the same, except that with `reverse`
+//    odd steps hand group g to work group G-1-(g mod G), which reverses the
+//    order groups are dispatched in (the launches order the steps).
+// A list keeps step order and row order; with `reverse`, odd steps are listed
+// back to front (items too, unless the step accumulates several rows into one
+// destination).  Launch j gives work group w the pieces
+// off[j*(G+1) + w] .. off[j*(G+1) + w + 1] of `list`.
+void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
+                    bool per_step, std::vector<uint32_t>& off, std::vector<DevItem>& list);
+
 // The regions of rank i's receive buffer whose final value the collective
 // defines (element ranges).
 std::vector<std::pair<int64_t, int64_t>> defined_output(const Schedule& s, int rank);

@@ -65,14 +65,11 @@ constexpr int BLOCK_THREADS = 256;
 enum : uint32_t { NT_SRC = 1u << 0, NT_DSRC = 1u << 1, NT_DST = 1u << 2, NT_ALL = 7u };
 
 struct RowsArgs {                     // row kernel (copy / recv_and_reduce)
-  const DevItem* items;
-  const DevStep* steps;
+  const DevItem* list;                // this launch's work list (pieces inside one column group)
+  const uint32_t* off;                // G + 1 offsets into `list`, one slice per work group
   uint64_t* sums;                     // per-row checksums or nullptr
-  uint32_t s0, s1;                    // steps [s0, s1)
-  uint32_t group_tiles;               // 4 KiB tiles per owned group
   uint32_t bases16;                   // all rank base pointers 16-byte aligned
-  uint32_t reverse_odd;               // walk odd steps backwards (short reuse distance)
-  uint32_t remap;                     // one launch per step: odd steps may also renumber groups
+  uint32_t pad;
   RankPtrs p;
 };
 
@@ -81,9 +78,9 @@ struct PermArgs {                     // staged permutation kernel (Bruck)
   const DevStep* steps;
   uint64_t* sums;
   uint32_t s0, s1;
-  uint32_t tile_units;                // units per owned tile of the block column
+  uint32_t lg_upl;                    // log2 of the units each lane holds per row and tile
   uint32_t ncols_units;               // block width in units
-  uint32_t nontemporal;               // NT_* mask (loads: NT_SRC, stores: NT_DST)
+  uint32_t nontemporal;               // nonzero: nontemporal loads and stores
   uint32_t pad;
   RankPtrs p;
 };

@@ -230,68 +230,45 @@ __device__ __forceinline__ void do_batch(const ItemView& v, uint64_t x0, uint64_
   }
 }
 
+// One piece: columns [col0, col1) of one row, inside one column group.  Thread t
+// handles bytes [16t, 16t + 16) of every 4 KiB tile the piece touches.
 template <int DT, int OP, bool CKS, int NTM>
-__device__ __forceinline__ void do_group(const ItemView& v, uint64_t gb, uint64_t gbytes, uint32_t gt,
-                                         uint64_t col0, uint64_t col1, bool vec, uint64_t tofs, uint64_t& acc) {
-  const uint64_t lo = gb > col0 ? gb : col0;
-  const uint64_t hi = gb + gbytes < col1 ? gb + gbytes : col1;
-  if (vec && lo == gb && hi == gb + gbytes) {
-    uint32_t k = 0;
-    for (; k + 4 <= gt; k += 4) do_batch<4, DT, OP, CKS, NTM>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
-    for (; k < gt; ++k) do_batch<1, DT, OP, CKS, NTM>(v, gb + uint64_t(k) * TILE_BYTES + tofs, acc);
+__device__ __forceinline__ void do_piece(const RowsArgs& a, const DevItem& it, uint64_t tofs, uint64_t& acc) {
+  ItemView v;
+  v.src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
+                                                                   : a.p.recv[it.src_rank]) + it.src_delta;
+  v.dsrc = reinterpret_cast<const char*>((it.flags & ITEM_DSRC_SEND) ? a.p.send[it.dst_rank]
+                                                                     : a.p.recv[it.dst_rank]) + it.dst_delta;
+  v.dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
+  v.reduce = (it.flags & ITEM_REDUCE) != 0;
+  v.shift = (it.flags >> ITEM_CKS_SHIFT) & 3u;
+  const bool vec = a.bases16 && (it.flags & ITEM_VEC);
+  const uint64_t t0 = it.col0 / TILE_BYTES, t1 = (it.col1 - 1) / TILE_BYTES;
+  if (vec && it.col0 % TILE_BYTES == 0 && it.col1 % TILE_BYTES == 0) {
+    uint64_t t = t0;
+    for (; t + 3 <= t1; t += 4) do_batch<4, DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, acc);
+    for (; t <= t1; ++t) do_batch<1, DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, acc);
   } else {
-    for (uint32_t k = 0; k < gt; ++k)
-      do_unit<DT, OP, CKS, NTM>(v, gb + uint64_t(k) * TILE_BYTES + tofs, lo, hi, vec, acc);
+    for (uint64_t t = t0; t <= t1; ++t) do_unit<DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, it.col0, it.col1, vec, acc);
   }
 }
 
-// Work group w owns the groups g = w, w + G, w + 2G, ... of `group_tiles`
-// consecutive 4 KiB column tiles; thread t owns bytes [16t, 16t + 16) of every
-// tile.  Steps are walked in order.  With reverse_odd, odd steps walk the
-// items (unless some of them accumulate into the same destination) and each
-// item's groups backwards, so the columns a work group wrote last are the
-// first it reads again.  With remap (only when each launch runs one step, so
-// ownership may change between steps) odd steps also renumber the work groups
-// back to front, which reverses the order the groups are dispatched in.
+// Work group w walks its slice of the launch's work list in order (the host
+// built it in step order; every piece of one column group is in one slice, so
+// values written in one step are read back by the same threads in the next).
+// The next list entry is fetched before the current piece is processed.
 template <int DT, int OP, bool CKS, int NTM>
 __global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
-  const uint32_t G = gridDim.x;
-  const uint32_t gt = a.group_tiles;
-  const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
+  const uint32_t e0 = cload(a.off + blockIdx.x), e1 = cload(a.off + blockIdx.x + 1);
+  if (e0 >= e1) return;
   const uint64_t tofs = uint64_t(threadIdx.x) * 16u;
-  for (uint32_t s = a.s0; s < a.s1; ++s) {
-    const DevStep st = cload(a.steps + s);
-    const bool rev = a.reverse_odd && (s & 1u);
-    const uint32_t w = (rev && a.remap) ? G - 1 - blockIdx.x : blockIdx.x;
-    const bool back = rev && !(st.flags & STEP_ORDERED);
-    for (uint32_t n = 0; n < st.nitems; ++n) {
-      const uint32_t i = st.item0 + (back ? st.nitems - 1 - n : n);
-      const DevItem it = cload(a.items + i);
-      if (it.col1 <= it.col0) continue;
-      const uint32_t gfirst = uint32_t(it.col0 / gbytes);
-      const uint32_t glast = uint32_t((it.col1 - 1) / gbytes);
-      if (glast < w) continue;  // every owned group is >= w
-      ItemView v;
-      v.src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
-                                                                       : a.p.recv[it.src_rank]) + it.src_delta;
-      v.dsrc = reinterpret_cast<const char*>((it.flags & ITEM_DSRC_SEND) ? a.p.send[it.dst_rank]
-                                                                         : a.p.recv[it.dst_rank]) + it.dst_delta;
-      v.dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
-      v.reduce = (it.flags & ITEM_REDUCE) != 0;
-      v.shift = (it.flags >> ITEM_CKS_SHIFT) & 3u;
-      const bool vec = a.bases16 && (it.flags & ITEM_VEC);
-      uint64_t acc = 0;
-      if (!rev) {
-        for (uint32_t g = gfirst + (w + G - gfirst % G) % G; g <= glast; g += G)
-          do_group<DT, OP, CKS, NTM>(v, uint64_t(g) * gbytes, gbytes, gt, it.col0, it.col1, vec, tofs, acc);
-      } else {
-        // largest owned group <= glast, then downwards while >= gfirst
-        int64_t g = int64_t(glast) - int64_t((glast - w) % G);
-        for (; g >= int64_t(gfirst); g -= G)
-          do_group<DT, OP, CKS, NTM>(v, uint64_t(g) * gbytes, gbytes, gt, it.col0, it.col1, vec, tofs, acc);
-      }
-      if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
-    }
+  DevItem next = cload(a.list + e0);
+  for (uint32_t e = e0; e < e1; ++e) {
+    const DevItem it = next;
+    if (e + 1 < e1) next = cload(a.list + e + 1);
+    uint64_t acc = 0;
+    do_piece<DT, OP, CKS, NTM>(a, it, tofs, acc);
+    if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
   }
 }
 
@@ -327,74 +304,58 @@ __device__ __forceinline__ uint64_t unit_words(typename UnitT<U>::T v, uint64_t 
   else return uint64_t(uint32_t(v) << (8u * uint32_t(col & 3u)));
 }
 
-// Columns are unit indices inside a block.  Work group w owns tiles w, w+G, ...
-// of `tile_units` units.  Non-staged steps copy item by item; a staged step
-// reads each group's tile of all its items into LDS, waits, then writes them
-// to their destinations.  Every row keeps its offset inside the block (and
-// blocks start at unit boundaries), so only the owning work group ever touches
-// a tile's columns; a barrier at the end of each step orders the steps.
-template <int U, bool CKS, bool NT>
+// Columns are unit indices inside a block; every Bruck row keeps its offset
+// inside the block, so a tile of block columns is a closed world: work group w
+// owns tiles w, w + G, ... and nothing outside it ever reads or writes them.
+// A staging group is the gs rows that permute one set of cells (the N ranks'
+// copies of one block in a shift round, or the N blocks of one rank in the
+// final rotation).  Per group and tile, wave v takes rows v, v+4, ... of the
+// group; lane l holds units l, l+64, ... (upl of them) of each such row in
+// registers: all rows' sources are loaded, the work group meets at a barrier
+// (every read of the group precedes every write), then the same lanes store
+// the values to the rows' destinations.  A barrier ends each step.
+template <int U, int SLOTS, bool CKS, bool NT>
 __global__ __launch_bounds__(BLOCK_THREADS) void perm_kernel(const PermArgs a) {
   typedef typename UnitT<U>::T T;
-  extern __shared__ __align__(16) char lds_raw[];
-  T* lds = reinterpret_cast<T*>(lds_raw);
-  const uint32_t G = gridDim.x, w = blockIdx.x, t = threadIdx.x;
-  const uint32_t tu = a.tile_units, ncol = a.ncols_units;
+  const uint32_t G = gridDim.x, w = blockIdx.x;
+  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+  const uint32_t ncol = a.ncols_units;
+  const uint32_t lg = a.lg_upl;
+  const uint32_t tu = 64u << lg;            // units of one row in one tile
   const uint32_t ntiles = (ncol + tu - 1) / tu;
   for (uint32_t s = a.s0; s < a.s1; ++s) {
     const DevStep st = cload(a.steps + s);
-    if (!(st.flags & STEP_STAGED)) {
-      for (uint32_t i = st.item0, ie = st.item0 + st.nitems; i < ie; ++i) {
-        const DevItem it = cload(a.items + i);
-        const char* src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
-                                                                                   : a.p.recv[it.src_rank]) + it.src_delta;
-        char* dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
-        uint64_t acc = 0;
-        for (uint32_t tile = w; tile < ntiles; tile += G) {
-          for (uint32_t u = t; u < tu; u += BLOCK_THREADS) {
-            const uint32_t c = tile * tu + u;
-            if (c < ncol) {
-              const T v = ld_unit<U, NT>(src + uint64_t(c) * U);
-              st_unit<U, NT>(dst + uint64_t(c) * U, v);
-              if constexpr (CKS) acc += unit_words<U>(v, uint64_t(c) * U);
-            }
+    const uint32_t gs = st.gsize;
+    const uint32_t ngroups = st.nitems / gs;
+    for (uint32_t grp = 0; grp < ngroups; ++grp) {
+      const uint32_t ib = st.item0 + grp * gs;
+      for (uint32_t tile = w; tile < ntiles; tile += G) {
+        const uint32_t c0 = tile * tu;
+        T v[SLOTS];
+#pragma unroll
+        for (int r = 0; r < SLOTS; ++r) {
+          const uint32_t m = wave + 4u * (uint32_t(r) >> lg);
+          const uint32_t c = c0 + lane + 64u * (uint32_t(r) & ((1u << lg) - 1u));
+          if (m < gs && c < ncol) {
+            const DevItem it = cload(a.items + ib + m);
+            v[r] = ld_unit<U, NT>(reinterpret_cast<const char*>(a.p.recv[it.src_rank]) + it.src_delta +
+                                  uint64_t(c) * U);
           }
         }
-        if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
-      }
-    } else {
-      const uint32_t gs = st.gsize;
-      const uint32_t ngroups = st.nitems / gs;
-      for (uint32_t grp = 0; grp < ngroups; ++grp) {
-        const uint32_t ib = st.item0 + grp * gs;
-        for (uint32_t tile = w; tile < ntiles; tile += G) {
-          const uint32_t c0 = tile * tu;
-          for (uint32_t q = t; q < gs * tu; q += BLOCK_THREADS) {
-            const uint32_t m = q / tu, c = c0 + (q - m * tu);
-            if (c < ncol) {
-              const DevItem it = cload(a.items + ib + m);
-              const char* src = reinterpret_cast<const char*>(a.p.recv[it.src_rank]) + it.src_delta;
-              lds[q] = ld_unit<U, NT>(src + uint64_t(c) * U);
-            }
-          }
-          __syncthreads();
-          for (uint32_t q = t; q < gs * tu; q += BLOCK_THREADS) {
-            const uint32_t m = q / tu, c = c0 + (q - m * tu);
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < SLOTS; ++r) {
+          const uint32_t m = wave + 4u * (uint32_t(r) >> lg);
+          if (m < gs) {  // uniform across the wave
+            const uint32_t c = c0 + lane + 64u * (uint32_t(r) & ((1u << lg) - 1u));
             const DevItem it = cload(a.items + ib + m);
             uint64_t acc = 0;
             if (c < ncol) {
-              char* dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
-              st_unit<U, NT>(dst + uint64_t(c) * U, lds[q]);
-              if constexpr (CKS) acc = unit_words<U>(lds[q], uint64_t(c) * U);
+              st_unit<U, NT>(reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta + uint64_t(c) * U, v[r]);
+              if constexpr (CKS) acc = unit_words<U>(v[r], uint64_t(c) * U);
             }
-            if constexpr (CKS) {
-              // a wave covers one item when tu is a multiple of 64; otherwise fall back per lane
-              if ((tu & 63u) == 0) add_row_sum(a.sums, it.row, acc);
-              else if (acc && it.row != NO_ROW)
-                __hip_atomic_fetch_add(a.sums + it.row, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
           }
-          __syncthreads();
         }
       }
     }
@@ -477,20 +438,25 @@ static RowsFn pick_rows(int dtype, int op, bool cks, uint32_t nt) {
 
 typedef void (*PermFn)(PermArgs);
 
-template <int U>
+template <int U, int SLOTS>
 static PermFn perm_fn(bool cks, bool nt) {
-  if (cks) return nt ? perm_kernel<U, true, true> : perm_kernel<U, true, false>;
-  return nt ? perm_kernel<U, false, true> : perm_kernel<U, false, false>;
+  if (cks) return nt ? perm_kernel<U, SLOTS, true, true> : perm_kernel<U, SLOTS, true, false>;
+  return nt ? perm_kernel<U, SLOTS, false, true> : perm_kernel<U, SLOTS, false, false>;
 }
 
-static PermFn pick_perm(int unit, bool cks, bool nt) {
+template <int SLOTS>
+static PermFn pick_perm_slots(int unit, bool cks, bool nt) {
   switch (unit) {
-    case 16: return perm_fn<16>(cks, nt);
-    case 8: return perm_fn<8>(cks, nt);
-    case 4: return perm_fn<4>(cks, nt);
-    case 2: return perm_fn<2>(cks, nt);
-    default: return perm_fn<1>(cks, nt);
+    case 16: return perm_fn<16, SLOTS>(cks, nt);
+    case 8: return perm_fn<8, SLOTS>(cks, nt);
+    case 4: return perm_fn<4, SLOTS>(cks, nt);
+    case 2: return perm_fn<2, SLOTS>(cks, nt);
+    default: return perm_fn<1, SLOTS>(cks, nt);
   }
+}
+
+static PermFn pick_perm(int unit, int slots, bool cks, bool nt) {
+  return slots > 16 ? pick_perm_slots<32>(unit, cks, nt) : pick_perm_slots<16>(unit, cks, nt);
 }
 
 hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, uint32_t grid,
@@ -500,10 +466,9 @@ hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_perm(const PermArgs& a, int unit, bool cks, uint32_t grid, uint32_t lds_bytes,
-                       hipStream_t stream) {
-  PermFn f = pick_perm(unit, cks, a.nontemporal != 0);
-  hipLaunchKernelGGL(f, dim3(grid), dim3(BLOCK_THREADS), lds_bytes, stream, a);
+hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_t grid, hipStream_t stream) {
+  PermFn f = pick_perm(unit, slots, cks, a.nontemporal != 0);
+  hipLaunchKernelGGL(f, dim3(grid), dim3(BLOCK_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -514,24 +479,12 @@ int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt) {
   return n > 0 ? n : 1;
 }
 
-int perm_blocks_per_cu(int unit, bool cks, bool nt, uint32_t lds_bytes) {
+int perm_blocks_per_cu(int unit, int slots, bool cks, bool nt) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_perm(unit, cks, nt), BLOCK_THREADS, lds_bytes) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_perm(unit, slots, cks, nt), BLOCK_THREADS, 0) !=
+      hipSuccess)
     return 1;
   return n > 0 ? n : 1;
-}
-
-hipError_t set_perm_lds_limit(uint32_t lds_bytes) {
-  hipError_t e = hipSuccess;
-  const int units[] = {16, 8, 4, 2, 1};
-  for (int u : units)
-    for (int c = 0; c < 2; ++c)
-      for (int n = 0; n < 2; ++n) {
-        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(pick_perm(u, c, n)),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
-        if (r != hipSuccess) e = r;
-      }
-  return e;
 }
 
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream) {

@@ -9,11 +9,10 @@ namespace coll {
 
 hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, uint32_t grid,
                        hipStream_t stream);
-hipError_t launch_perm(const PermArgs& a, int unit, bool cks, uint32_t grid, uint32_t lds_bytes, hipStream_t stream);
+hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_t grid, hipStream_t stream);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream);
 hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, uint32_t grid, hipStream_t stream);
 int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt);
-int perm_blocks_per_cu(int unit, bool cks, bool nt, uint32_t lds_bytes);
-hipError_t set_perm_lds_limit(uint32_t lds_bytes);
+int perm_blocks_per_cu(int unit, int slots, bool cks, bool nt);
 
 }  // namespace coll

@@ -182,25 +182,25 @@ coll_status_t coll_get_stats(coll_counts_t* last);
 coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
 
 /* Process-wide execution options (defaults in brackets).
- * COLL_OPT_EXEC            0: automatic [0]: one launch per step when a rank
- *                          buffer spans at least COLL_OPT_STEP_MIN_BYTES, else
- *                          one launch for all steps; 1: always per step;
- *                          2: always one launch.
- * COLL_OPT_GROUP_TILES     4 KiB column tiles per work-group group, 1..64 [0: automatic].
+ * COLL_OPT_EXEC            0: one launch runs every step of a call [0]; each
+ *                          work group owns fixed columns, so the steps need
+ *                          no synchronisation between work groups.
+ *                          1: one launch per step (the launches order the steps).
+ * COLL_OPT_GROUP_TILES     4 KiB column tiles per work-group column group, 1..64 [0: automatic].
  * COLL_OPT_MAX_GRID        cap on work groups per launch [0: automatic].
  * COLL_OPT_NONTEMPORAL     bit mask of nontemporal accesses: 1 source loads,
- *                          2 old-destination loads, 4 stores [7].
+ *                          2 old-destination loads, 4 stores; -1: automatic
+ *                          [-1]: none while all rank buffers together fit the
+ *                          256 MiB memory-side cache, else source loads only.
  * COLL_OPT_REVERSE         1: odd steps walk their columns backwards, so data
  *                          written last is read first [1]; 0: always forwards.
- * COLL_OPT_STEP_MIN_BYTES  threshold of the automatic mode [128 MiB].
  * Every setting gives bit-identical results; they only change the speed. */
 typedef enum {
   COLL_OPT_EXEC = 0,
   COLL_OPT_GROUP_TILES = 1,
   COLL_OPT_MAX_GRID = 2,
   COLL_OPT_NONTEMPORAL = 3,
-  COLL_OPT_REVERSE = 4,
-  COLL_OPT_STEP_MIN_BYTES = 5
+  COLL_OPT_REVERSE = 4
 } coll_option_t;
 coll_status_t coll_set_option(coll_option_t key, int64_t value);
 

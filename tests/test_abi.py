@@ -82,6 +82,9 @@ def test_argument_errors(case, want):
 def test_options_and_strings():
     lib = _lib.load()
     assert lib.coll_set_option(0, 7) == INV
+    assert lib.coll_set_option(0, 2) == INV
+    assert lib.coll_set_option(3, 8) == INV
+    assert lib.coll_set_option(3, -1) == OK
     assert lib.coll_set_option(99, 0) == INV
     assert lib.coll_set_option(1, 0) == OK
     assert lib.coll_status_string(0) == b"COLL_OK"

@@ -16,8 +16,7 @@ from tests.gpu_util import assert_parity
 pytestmark = pytest.mark.gpu
 
 
-DEFAULT_OPTIONS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": 7, "reverse": 1,
-                   "step_min_bytes": 128 << 20}
+DEFAULT_OPTIONS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1}
 
 
 @pytest.fixture(autouse=True)
@@ -194,7 +193,7 @@ def test_bf16_rounding_ties():
 # --- execution modes and launch shapes give identical results ------------------------
 
 @pytest.mark.parametrize("reverse", [0, 1])
-@pytest.mark.parametrize("exec_mode", [1, 2])
+@pytest.mark.parametrize("exec_mode", [0, 1])
 @pytest.mark.parametrize("group_tiles,max_grid", [(0, 0), (1, 0), (2, 5), (8, 3), (16, 1), (4, 7)])
 def test_launch_shapes(exec_mode, group_tiles, max_grid, reverse):
     import collective_communication_algorithms_amd as coll
@@ -212,7 +211,7 @@ def test_launch_shapes(exec_mode, group_tiles, max_grid, reverse):
     assert_parity("broadcast", "binomial_pipe", si.rank_arrays(2, 8, 300001, "uint8"), "uint8", k=8)
 
 
-@pytest.mark.parametrize("nt", list(range(8)))
+@pytest.mark.parametrize("nt", list(range(-1, 8)))
 def test_nontemporal_switch(nt):
     import collective_communication_algorithms_amd as coll
     coll.coll_set_option("nontemporal", nt)
@@ -224,15 +223,17 @@ def test_nontemporal_switch(nt):
     assert_parity("alltoall", "pairwise", b, "bfloat16")
 
 
-def test_automatic_mode_switches_at_the_threshold():
-    """The automatic mode picks per-step launches from the threshold up; both
-    sides of the threshold give the oracle's result."""
+@pytest.mark.parametrize("exec_mode", [0, 1])
+def test_many_step_schedules(exec_mode):
+    """Pipelines with many chunks and 64-rank rings: hundreds of steps in one call."""
     import collective_communication_algorithms_amd as coll
-    a = si.rank_arrays(3, 8, (1 << 20) // 4, "float32")
-    for thr in (1, 1 << 40):
-        coll.coll_set_option("step_min_bytes", thr)
-        for algo in ("ring", "rhd", "dbt"):
-            assert_parity("allreduce", algo, a, "float32", checksums=True)
+    coll.coll_set_option("exec", exec_mode)
+    a = si.rank_arrays(2, 8, (1 << 20) + 77, "uint8")
+    for algo in ("chain_pipe", "binomial_pipe"):
+        for k in (64, 1000):
+            assert_parity("broadcast", algo, a, "uint8", root=5, k=k)
+    b = si.rank_arrays(4, 64, 64 * 300 + 17, "bfloat16", sigma=1e-3)
+    assert_parity("allreduce", "ring", b, "bfloat16", checksums=True)
 
 
 def test_repeated_calls_reuse_cached_schedules():
