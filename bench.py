@@ -32,10 +32,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_kernel_ring_allreduc
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and blank space removed), so
+    that the committed counter summary is dropped whenever the kernels change."""
+    import re
     h = hashlib.sha256()
     for f in ("kernels.hip", "device_types.h"):
-        with open(os.path.join(ROOT, "collective_communication_algorithms_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "collective_communication_algorithms_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -66,6 +72,41 @@ def cpu_baseline(inputs_host, N: int, count: int, algo: str):
     return {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the full workload ({N} x {M >> 20} MiB fp32, one {algo} AllReduce), "
                       f"numpy single-threaded, {dt:.2f} s"}
+
+
+def summarize_counters(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, kernel_prefix, out_json,
+                       calib_gib: int = 2) -> dict:
+    """Traffic per launch of the row kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
+    counter reads for the plain copy kernel (which reads and writes calib_gib
+    GiB): the factor is the copy's known bytes over its counter reading."""
+    import csv
+    import statistics
+
+    def mean_kib(path, prefix):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if r["Kernel_Name"].startswith(prefix)]
+        if not vals:
+            raise SystemExit(f"no dispatch of {prefix!r} in {path}")
+        return statistics.mean(vals), len(vals)
+
+    copy_prefix = "void coll::calib_kernel<false>"
+    known_kib = calib_gib << 20
+    cf, _ = mean_kib(calib_fetch_csv, copy_prefix)
+    cw, _ = mean_kib(calib_write_csv, copy_prefix)
+    f, nf = mean_kib(fetch_csv, kernel_prefix)
+    w, nw = mean_kib(write_csv, kernel_prefix)
+    ff, fw = known_kib / cf, known_kib / cw
+    traffic = (f * ff + w * fw) * 1024
+    out = {"kernel": kernel_prefix, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w, "dispatches": [nf, nw],
+           "copy_kernel_fetch_kib": cf, "copy_kernel_write_kib": cw, "copy_kernel_known_kib": known_kib,
+           "fetch_scale": ff, "write_scale": fw,
+           "traffic_bytes_per_launch": round(traffic)}
+    with open(out_json, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    return out
 
 
 def calibrate(dev, gib: int = 2, reps: int = 10) -> dict:
@@ -105,7 +146,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="only measure the plain copy (1R+1W) and add (2R+1W) streams and exit")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                               "COPY_WRITE_CSV"),
+                    help="write the traffic summary under profiles/ from rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        out = summarize_counters(*args.summarize_counters, "void coll::rows_kernel<2, 0, false, 1>", TRAFFIC_FILE)
+        print(json.dumps(out))
+        return 0
     if args.gpus != 1:
         print("bench.py: this build runs N virtual ranks on one GPU; --gpus above 1 is not supported",
               file=sys.stderr)

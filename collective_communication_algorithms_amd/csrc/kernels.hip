@@ -2,16 +2,18 @@
 //
 //  rows_kernel  copy and recv_and_reduce rows of a schedule ("集合通信算法延迟公式",
 //               Ring ReduceScatter: each step a rank reduces the chunk it receives
-//               into its own; the HCCL blog's recv_and_reduce).  Persistent over a
-//               range of steps: 128-bit loads, nontemporal stores, per-thread
-//               ownership of 16-byte column units (see device_types.h), so no
-//               flags or barriers are needed between steps.
-//  perm_kernel  Bruck's in-place block shifts and rotation ("集合通信算法延迟公式",
-//               Bruck AllToAll): each staging group is read into LDS, then written
-//               permuted, so every read of a step precedes every write.
+//               into its own; the HCCL blog's recv_and_reduce).  One launch can run
+//               every step of a call: each work group walks a host-built list of
+//               row pieces inside the column groups it owns (see device_types.h),
+//               so no flags or barriers are needed between steps.  128-bit loads
+//               and stores, nontemporal hints per operand.
+//  perm_kernel  Bruck's in-place block shifts and final rotation ("集合通信算法延迟公式",
+//               Bruck AllToAll): each staging group is read into registers, the
+//               work group meets at a barrier, then the values are written
+//               permuted, so every read of a group precedes every write.
 //  fill / calib plain helpers: clear checksum slots, stream copy / add.
 //
-// No MFMA: nothing here is a contraction.  Every kernel is bound by HBM.
+// No MFMA: nothing here is a contraction.  Every kernel is bound by memory.
 #include <hip/hip_runtime.h>
 
 #include "device_types.h"
