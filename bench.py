@@ -109,6 +109,161 @@ def summarize_counters(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, k
     return out
 
 
+def sweep(out_path: str, dev, quick: bool = False) -> None:
+    """Every configuration's calls, one JSON line each, into ``out_path``.
+
+    Protocol: 5 warm-up calls, then 20 calls, each timed alone with HIP events
+    on the call's stream; before every call the inputs are restored from a
+    pristine device copy (not timed).  Median and minimum are reported, with
+    algbw = M / t, busbw = algbw x the pages' coefficient, schedule bytes / t
+    against the 8 TB/s HBM spec, the pages' alpha-beta prediction (alpha 5 us,
+    beta 450 GB/s) and a least-squares fit t = steps * alpha_g + bytes / beta_g
+    over the fp32 Ring AllReduce sizes.  The oracle is timed on the host (one
+    core) on the same inputs where that takes seconds; larger calls give none.
+    """
+    import numpy as np
+    import torch
+
+    import collective_communication_algorithms_amd as coll
+    import seeded_inputs as si
+    from collective_communication_algorithms_amd import model
+
+    rows = []
+    stream = torch.cuda.current_stream(dev)
+    reps, warm = (5, 2) if quick else (20, 5)
+
+    def time_call(fn, pristine, live):
+        restore = (lambda: live.copy_(pristine)) if live is not pristine else (lambda: None)
+        for _ in range(warm):
+            restore()
+            fn()
+        ts = []
+        for _ in range(reps):
+            restore()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            e.synchronize()
+            ts.append(s.elapsed_time(e))
+        restore()
+        torch.cuda.synchronize()
+        return float(np.median(ts)), float(np.min(ts))
+
+    def oracle_time(kind, algo, host, dtype, root=0, k=1):
+        from oracle.schedules import make_plan
+        from oracle.simulate import run_plan
+        plan = make_plan(kind, algo, len(host), len(host[0]), root, k)
+        t0 = time.perf_counter()
+        run_plan(plan, dtype, "sum", host)
+        return time.perf_counter() - t0
+
+    def record(cfg, kind, algo, dtype, N, count, k, med, mn, oracle_s=None, root=0):
+        sz = si.ITEMSIZE[dtype]
+        M = count * sz
+        _, cnt = coll.coll_plan(kind, algo, N, count, dtype, root, k)
+        st = coll.coll_get_stats()
+        algbw = M / (med * 1e-3) / 1e9
+        r = {"config": cfg, "kind": kind, "algo": algo, "dtype": dtype, "N": N, "M": M, "k": k,
+             "steps": cnt["steps"], "sched_bytes": st["hbm_bytes"], "crit_bytes": cnt["crit_bytes"],
+             "t_med_us": round(med * 1e3, 2), "t_min_us": round(mn * 1e3, 2),
+             "algbw_GBps": round(algbw, 3), "busbw_GBps": round(algbw * model.busbw_coef(kind, N), 3),
+             "sched_TBps": round(st["hbm_bytes"] / (med * 1e-3) / 1e12, 3),
+             "pct_of_8TBps": round(100 * st["hbm_bytes"] / (med * 1e-3) / 8e12, 2)}
+        try:
+            mk = "broadcast" if kind == "broadcast" else kind
+            r["ab_page_us"] = round(model.time(mk, algo, N, M, 5e-6, 450e9, k) * 1e6, 2)
+        except ValueError:
+            pass
+        if oracle_s is not None:
+            r["oracle_s"] = round(oracle_s, 4)
+            r["oracle_cores"] = 1
+        rows.append(r)
+        with open(out_path, "a") as fh:
+            fh.write(json.dumps(r) + "\n")
+        print(json.dumps(r), file=sys.stderr, flush=True)
+
+    open(out_path, "w").close()
+
+    # C1: Ring / RHD / DBT AllReduce, 4 ranks x 1,024 int32
+    host = si.rank_arrays(1, 4, 1024, "int32")
+    pristine = torch.stack([si.host_to_tensor(x, "int32", dev) for x in host])
+    live = pristine.clone()
+    for algo in ("ring", "rhd", "dbt"):
+        med, mn = time_call(lambda: coll.coll_allreduce(list(live), algo=algo), pristine, live)
+        record("C1", "allreduce", algo, "int32", 4, 1024, 1, med, mn, oracle_time("allreduce", algo, host, "int32"))
+
+    # C2: Broadcast / Scatter / Gather, 8 ranks, uint8
+    for M in ((1 << 10, 1 << 16, 1 << 22) if quick else (1 << 10, 1 << 16, 1 << 22, 1 << 26)):
+        host = si.rank_arrays(2, 8, M, "uint8") if M <= (1 << 22) else None
+        pristine = (torch.stack([si.host_to_tensor(x, "uint8", dev) for x in host]) if host is not None else
+                    torch.stack(si.device_rank_tensors(2, 8, M, "uint8", dev)))
+        live = pristine.clone()
+        cases = [("broadcast", "binomial", 1)]
+        for algo in ("chain_pipe", "binomial_pipe"):
+            kstar = model.best_chunks(algo, 8, M, 5e-6, 450e9)
+            cases += [("broadcast", algo, k) for k in sorted({1, 8, 64, kstar}) if k <= M]
+        cases += [("scatter", "binomial", 1), ("gather", "binomial", 1)]
+        for kind, algo, k in cases:
+            fn = coll.COLLECTIVE_FNS[kind]
+            med, mn = time_call(lambda: fn(list(live), algo=algo, root=0, chunks=k), pristine, live)
+            ot = oracle_time(kind, algo, host, "uint8", 0, k) if host is not None else None
+            record("C2", kind, algo, "uint8", 8, M, k, med, mn, ot)
+        del pristine, live
+
+    # C3: AllReduce, 8 ranks, fp32 N(0,1) / bf16 N(0,0.02), 4 KiB .. 256 MiB
+    for dtype, sigma in (("float32", 1.0), ("bfloat16", 0.02)):
+        for lg in range(12, 29, 4 if quick else 1):
+            count = (1 << lg) // si.ITEMSIZE[dtype]
+            small = lg <= 24
+            host = si.rank_arrays(3, 8, count, dtype, sigma=sigma) if small else None
+            pristine = (torch.stack([si.host_to_tensor(x, dtype, dev) for x in host]) if small else
+                        torch.stack(si.device_rank_tensors(3, 8, count, dtype, dev, sigma=sigma)))
+            live = pristine.clone()
+            for algo in ("ring", "rhd", "dbt"):
+                med, mn = time_call(lambda: coll.coll_allreduce(list(live), algo=algo), pristine, live)
+                ot = oracle_time("allreduce", algo, host, dtype) if small and lg <= 22 else None
+                record("C3", "allreduce", algo, dtype, 8, count, 1, med, mn, ot)
+            del pristine, live
+            torch.cuda.empty_cache()
+
+    # C4: ReduceScatter and AllGather, 64 ranks x 256 MiB bf16 (16 GiB resident)
+    if not quick:
+        count = (256 << 20) // 2
+        pristine = torch.empty((64, count), dtype=torch.bfloat16, device=dev)
+        si.device_rank_tensors(4, 64, count, "bfloat16", dev, sigma=1e-3, out=pristine)
+        live = pristine.clone()
+        for algo in ("ring", "rhd"):
+            for kind in ("reducescatter", "allgather"):
+                fn = coll.COLLECTIVE_FNS[kind]
+                med, mn = time_call(lambda: fn(list(live), algo=algo), pristine, live)
+                record("C4", kind, algo, "bfloat16", 64, count, 1, med, mn)
+        del pristine, live
+        torch.cuda.empty_cache()
+
+    # C5: AllToAll, 32 ranks, 512 tokens x 4096 bf16 per peer
+    N, B = 32, 512 * 4096
+    pristine = torch.empty((N, N * B), dtype=torch.bfloat16, device=dev)
+    si.device_rank_tensors(5, N, N * B, "bfloat16", dev, out=pristine)
+    recv = torch.empty_like(pristine)
+    for algo in ("pairwise", "bruck"):
+        med, mn = time_call(lambda: coll.coll_alltoall(list(pristine), list(recv), algo=algo), pristine, pristine)
+        record("C5", "alltoall", algo, "bfloat16", N, N * B, 1, med, mn)
+    del pristine, recv
+    torch.cuda.empty_cache()
+
+    # alpha-beta fit on the fp32 Ring AllReduce sizes: t = steps * a + bytes / b
+    pts = [r for r in rows if r["config"] == "C3" and r["algo"] == "ring" and r["dtype"] == "float32"]
+    A = np.array([[r["steps"], r["sched_bytes"]] for r in pts], dtype=np.float64)
+    t = np.array([r["t_med_us"] * 1e-6 for r in pts])
+    coef, *_ = np.linalg.lstsq(A, t, rcond=None)
+    fit = {"fit": "t = steps * alpha_g + sched_bytes / beta_g over C3 fp32 Ring",
+           "alpha_g_us": round(coef[0] * 1e6, 3), "beta_g_TBps": round(1 / coef[1] / 1e12, 3) if coef[1] > 0 else None}
+    with open(out_path, "a") as fh:
+        fh.write(json.dumps(fit) + "\n")
+    print(json.dumps(fit), file=sys.stderr)
+
+
 def calibrate(dev, gib: int = 2, reps: int = 10) -> dict:
     """Achievable HBM rate of plain streams: copy reads and writes each byte
     once (2 x bytes moved), add reads two operands and writes one (3 x bytes)."""
@@ -146,6 +301,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="only measure the plain copy (1R+1W) and add (2R+1W) streams and exit")
+    ap.add_argument("--sweep", metavar="OUT_JSONL", help="time every configuration's calls and exit")
+    ap.add_argument("--quick", action="store_true", help="with --sweep: fewer sizes and repetitions")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                                "COPY_WRITE_CSV"),
                     help="write the traffic summary under profiles/ from rocprofv3 counter CSVs and exit")
@@ -171,6 +328,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.calibrate:
         print(json.dumps(calibrate(dev)))
+        return 0
+    if args.sweep:
+        sweep(args.sweep, dev, args.quick)
         return 0
     N, M = args.nranks, args.mib << 20
     count = M // 4

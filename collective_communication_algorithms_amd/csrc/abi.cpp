@@ -392,6 +392,8 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.sums = t_sums;
       a.nontemporal = ntmask;
       a.p = ptrs;
+      if (ph.colspace >= (uint64_t(1) << 31))
+        return fail(COLL_ERR_UNSUPPORTED, "Bruck blocks of 2 GiB or more");
       int unit = b.perm_unit;
       while (unit > 1 && (align_or % uint64_t(unit))) unit >>= 1;
       a.ncols_units = uint32_t(ph.colspace / uint64_t(unit));
@@ -406,7 +408,9 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       const uint64_t ntiles = (uint64_t(a.ncols_units) + tu - 1) / tu;
       uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, slots, cks, ntmask != 0));
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
-      const uint32_t grid = uint32_t(std::max<uint64_t>(1, std::min(ntiles, cap)));
+      // the same number of tiles for every work group
+      const uint64_t per_wg = std::max<uint64_t>(1, (ntiles + cap - 1) / cap);
+      const uint32_t grid = uint32_t(std::max<uint64_t>(1, (ntiles + per_wg - 1) / per_wg));
       for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
         a.s0 = s0;
         a.s1 = step_mode ? s0 + 1 : ph.s1;

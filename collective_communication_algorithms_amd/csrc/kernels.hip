@@ -246,13 +246,22 @@ __device__ __forceinline__ void do_piece(const RowsArgs& a, const DevItem& it, u
   v.shift = (it.flags >> ITEM_CKS_SHIFT) & 3u;
   const bool vec = a.bases16 && (it.flags & ITEM_VEC);
   const uint64_t t0 = it.col0 / TILE_BYTES, t1 = (it.col1 - 1) / TILE_BYTES;
-  if (vec && it.col0 % TILE_BYTES == 0 && it.col1 % TILE_BYTES == 0) {
-    uint64_t t = t0;
-    for (; t + 3 <= t1; t += 4) do_batch<4, DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, acc);
-    for (; t <= t1; ++t) do_batch<1, DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, acc);
-  } else {
-    for (uint64_t t = t0; t <= t1; ++t) do_unit<DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, it.col0, it.col1, vec, acc);
+  if (!vec) {
+    for (uint64_t t = t0; t <= t1; ++t) do_unit<DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, it.col0, it.col1, false, acc);
+    return;
   }
+  // whole tiles [m0, m1) go through batched loads; a partly covered first or
+  // last tile (a row that starts or ends inside a tile) unit by unit
+  const uint64_t m0 = (it.col0 + TILE_BYTES - 1) / TILE_BYTES, m1 = it.col1 / TILE_BYTES;
+  if (m0 >= m1) {
+    for (uint64_t t = t0; t <= t1; ++t) do_unit<DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, it.col0, it.col1, true, acc);
+    return;
+  }
+  if (t0 < m0) do_unit<DT, OP, CKS, NTM>(v, t0 * TILE_BYTES + tofs, it.col0, it.col1, true, acc);
+  uint64_t t = m0;
+  for (; t + 4 <= m1; t += 4) do_batch<4, DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, acc);
+  for (; t < m1; ++t) do_batch<1, DT, OP, CKS, NTM>(v, t * TILE_BYTES + tofs, acc);
+  if (t1 >= m1) do_unit<DT, OP, CKS, NTM>(v, t1 * TILE_BYTES + tofs, it.col0, it.col1, true, acc);
 }
 
 // Work group w walks its slice of the launch's work list in order (the host
@@ -320,7 +329,9 @@ template <int U, int SLOTS, bool CKS, bool NT>
 __global__ __launch_bounds__(BLOCK_THREADS) void perm_kernel(const PermArgs a) {
   typedef typename UnitT<U>::T T;
   const uint32_t G = gridDim.x, w = blockIdx.x;
-  const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+  // the wave index is the same for all 64 lanes: say so, so that row descriptors
+  // and base addresses live in scalar registers
+  const uint32_t lane = threadIdx.x & 63u, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t ncol = a.ncols_units;
   const uint32_t lg = a.lg_upl;
   const uint32_t tu = 64u << lg;            // units of one row in one tile
@@ -337,23 +348,24 @@ __global__ __launch_bounds__(BLOCK_THREADS) void perm_kernel(const PermArgs a) {
 #pragma unroll
         for (int r = 0; r < SLOTS; ++r) {
           const uint32_t m = wave + 4u * (uint32_t(r) >> lg);
-          const uint32_t c = c0 + lane + 64u * (uint32_t(r) & ((1u << lg) - 1u));
-          if (m < gs && c < ncol) {
+          if (m < gs) {  // uniform across the wave
+            const uint32_t c = c0 + lane + 64u * (uint32_t(r) & ((1u << lg) - 1u));
             const DevItem it = cload(a.items + ib + m);
-            v[r] = ld_unit<U, NT>(reinterpret_cast<const char*>(a.p.recv[it.src_rank]) + it.src_delta +
-                                  uint64_t(c) * U);
+            const char* base = reinterpret_cast<const char*>(a.p.recv[it.src_rank]) + it.src_delta;
+            if (c < ncol) v[r] = ld_unit<U, NT>(base + uint32_t(c * U));
           }
         }
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < SLOTS; ++r) {
           const uint32_t m = wave + 4u * (uint32_t(r) >> lg);
-          if (m < gs) {  // uniform across the wave
+          if (m < gs) {
             const uint32_t c = c0 + lane + 64u * (uint32_t(r) & ((1u << lg) - 1u));
             const DevItem it = cload(a.items + ib + m);
+            char* base = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
             uint64_t acc = 0;
             if (c < ncol) {
-              st_unit<U, NT>(reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta + uint64_t(c) * U, v[r]);
+              st_unit<U, NT>(base + uint32_t(c * U), v[r]);
               if constexpr (CKS) acc = unit_words<U>(v[r], uint64_t(c) * U);
             }
             if constexpr (CKS) add_row_sum(a.sums, it.row, acc);

@@ -1,0 +1,126 @@
+"""Parity at the configurations' full sizes, in the default launch configuration
+(the one bench.py times), on sampled outputs the oracle computes exactly.
+
+Every schedule except AllToAll keeps each element at its offset, so element x
+of every output depends only on element x of the inputs: the oracle restricted
+to a sample of columns (``run_plan_columns``) gives the exact expected values
+there.  AllToAll keeps the offset inside a block, so the oracle runs on blocks
+cut down to a sample of in-block offsets.  Inputs are drawn on the device by
+torch's seeded generator (never by the path under test).
+"""
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from oracle.schedules import make_plan
+from oracle.simulate import defined_regions, run_plan_columns
+from oracle import numerics
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(autouse=True)
+def _defaults(gpu_device):
+    import collective_communication_algorithms_amd as coll
+    for k, v in {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1}.items():
+        coll.coll_set_option(k, v)
+    yield
+
+
+def sample_columns(count, N, stride=4097, edge=65536, around=256):
+    parts = [np.arange(0, count, stride), np.arange(0, min(edge, count)), np.arange(max(0, count - edge), count)]
+    for c in range(1, N):
+        b = c * count // N
+        parts.append(np.arange(max(0, b - around), min(count, b + around)))
+    return np.unique(np.concatenate(parts))
+
+
+def gather_cols(tensors, cols, dtype):
+    import torch
+    idx = torch.from_numpy(cols).to(tensors[0].device)
+    return [si.tensor_to_host(t.index_select(0, idx), dtype) for t in tensors]
+
+
+def check_sampled(kind, algo, N, count, dtype, workload, sigma=1.0, root=0, k=1):
+    import torch
+    import collective_communication_algorithms_amd as coll
+    dev = torch.device("cuda:0")
+    buf = torch.empty((N, count), dtype=si.to_torch_dtype(dtype), device=dev)
+    ranks = si.device_rank_tensors(workload, N, count, dtype, dev, sigma=sigma, out=buf)
+    cols = sample_columns(count, N)
+    before = gather_cols(ranks, cols, dtype)
+    coll.COLLECTIVE_FNS[kind](ranks, op="sum", algo=algo, root=root, chunks=k)
+    torch.cuda.synchronize()
+    after = gather_cols(ranks, cols, dtype)
+    want = run_plan_columns(make_plan(kind, algo, N, count, root, k), dtype, "sum", cols, before)
+    for i, regs in enumerate(defined_regions(kind, N, count, root)):
+        for lo, hi in regs:
+            m = (cols >= lo) & (cols < hi)
+            assert np.array_equal(after[i][m].view(np.uint8), want[i][m].view(np.uint8)), \
+                (kind, algo, dtype, N, count, i, int(np.sum(after[i][m] != want[i][m])))
+    del buf, ranks
+    torch.cuda.empty_cache()
+    return before, after
+
+
+@pytest.mark.parametrize("algo", ["ring", "rhd", "dbt"])
+@pytest.mark.parametrize("dtype,sigma", [("float32", 1.0), ("bfloat16", 0.02)])
+def test_allreduce_n8_256MiB(algo, dtype, sigma):
+    count = (256 << 20) // si.ITEMSIZE[dtype]
+    before, after = check_sampled("allreduce", algo, 8, count, dtype, 3, sigma=sigma)
+    wide = [x.astype(np.float64) if dtype == "float32" else numerics.bf16_to_f32(x).astype(np.float64)
+            for x in before]
+    y64 = np.sum(wide, axis=0)
+    y = after[0].astype(np.float64) if dtype == "float32" else numerics.bf16_to_f32(after[0]).astype(np.float64)
+    assert np.linalg.norm(y - y64) / np.linalg.norm(y64) <= (1e-5 if dtype == "float32" else 1e-2)
+
+
+@pytest.mark.parametrize("algo,k", [("binomial", 1), ("chain_pipe", 1), ("chain_pipe", 8), ("chain_pipe", 13),
+                                    ("chain_pipe", 64), ("binomial_pipe", 1), ("binomial_pipe", 8),
+                                    ("binomial_pipe", 64)])
+def test_broadcast_n8_64MiB(algo, k):
+    check_sampled("broadcast", algo, 8, 64 << 20, "uint8", 2, k=k)
+
+
+@pytest.mark.parametrize("kind", ["scatter", "gather"])
+def test_scatter_gather_n8_64MiB(kind):
+    check_sampled(kind, "binomial", 8, 64 << 20, "uint8", 2)
+
+
+@pytest.mark.parametrize("kind", ["reducescatter", "allgather"])
+@pytest.mark.parametrize("algo", ["ring", "rhd"])
+def test_reducescatter_allgather_n64_256MiB(kind, algo):
+    """64 ranks x 256 MiB bf16 N(0, 1e-3): 16 GiB resident."""
+    check_sampled(kind, algo, 64, (256 << 20) // 2, "bfloat16", 4, sigma=1e-3)
+
+
+@pytest.mark.parametrize("algo", ["pairwise", "bruck"])
+def test_alltoall_n32_512x4096(algo):
+    """32 ranks; each sends 512 tokens x 4096 bf16 to every peer (128 MiB per rank)."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    import oracle
+    dev = torch.device("cuda:0")
+    N, B = 32, 512 * 4096
+    count = N * B
+    sbuf = torch.empty((N, count), dtype=torch.bfloat16, device=dev)
+    send = si.device_rank_tensors(5, N, count, "bfloat16", dev, out=sbuf)
+    rbuf = torch.empty_like(sbuf)
+    recv = [rbuf[i] for i in range(N)]
+    offs = np.unique(np.concatenate([np.arange(0, B, 1021), np.arange(0, 256), np.arange(B - 256, B)]))
+    S = len(offs)
+    cols = (np.arange(N)[:, None] * B + offs[None, :]).reshape(-1)
+    red_in = gather_cols(send, cols, "bfloat16")
+    coll.coll_alltoall(send, recv, algo=algo)
+    torch.cuda.synchronize()
+    got = gather_cols(recv, cols, "bfloat16")
+    want = oracle.alltoall(red_in, "bfloat16", algo)
+    for j in range(N):
+        assert np.array_equal(got[j], want[j]), (algo, j)
+    # and against the definition on the sample: recv_j block i = send_i block j
+    for j in (0, 17, 31):
+        for i in (0, 5, 31):
+            assert np.array_equal(got[j][i * S:(i + 1) * S], red_in[i][j * S:(j + 1) * S])
+    del sbuf, rbuf, send, recv
+    torch.cuda.empty_cache()
