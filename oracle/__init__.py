@@ -12,7 +12,7 @@ What it computes, from the pages it follows:
     Scatter with the data flow reversed (eq:onetoall-gather-scatter-duality).
   * "集合通信算法延迟公式" (t6page.pages.dev): Ring ReduceScatter + AllGather
     AllReduce, Recursive Halving-Doubling, Double Binary Tree, Pairwise and Bruck
-    AllToAll.
+    AllToAll, Tree Reduce.
   * The HCCL blog (agent.csdn.net): the Ring AllReduce chunk walk and the
     ``recv_and_reduce`` row, used for chunk indices only.
 
@@ -29,5 +29,5 @@ fp64 error bounds.  No function is left "parity unpinned".
 
 from . import numerics, schedules, simulate  # noqa: F401
 from .simulate import (allreduce, reducescatter, allgather, broadcast, scatter,  # noqa: F401
-                       gather, alltoall, run_plan)
+                       gather, alltoall, reduce, run_plan)
 from .schedules import make_plan  # noqa: F401

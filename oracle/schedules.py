@@ -35,9 +35,9 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 
 KINDS = ("allreduce", "reducescatter", "allgather", "broadcast", "scatter",
-         "gather", "alltoall")
+         "gather", "alltoall", "reduce")
 ALGOS = ("ring", "rhd", "dbt", "binomial", "chain_pipe", "binomial_pipe",
-         "pairwise", "bruck")
+         "pairwise", "bruck", "linear", "scatter_allgather")
 
 
 @dataclass(frozen=True)
@@ -316,6 +316,29 @@ def _bcast_binomial_pipe(b: _Builder, N, count, root, k):
                     b.row(st, (root + v) % N, (root + w) % N, lo, hi - lo)
 
 
+def _reduce_binomial(b: _Builder, N, count, root):
+    """Tree Reduce ("集合通信算法延迟公式", Tree Reduce: the mirror of the tree
+    Broadcast, log2 N steps of the whole message): at step j (distance
+    d = 2^(j-1)) every relative rank v whose lowest set bit is d sends its
+    partial result to v-d, which reduces it into its own."""
+    L = ceil_log2(N)
+    for j in range(1, L + 1):
+        d = 1 << (j - 1)
+        st = b.new_step()
+        for v in range(d, N, 2 * d):
+            b.row(st, (root + v) % N, (root + v - d) % N, 0, count, reduce=True)
+
+
+def _scatter_linear(b: _Builder, N, count, root):
+    """Naive Scatter ("一对多通信：Broadcast 与 Scatter", 逐个发送（Naive）):
+    the root sends each rank its chunk directly, one rank per step, N-1 steps."""
+    for i in range(1, N):
+        st = b.new_step()
+        a = (root + i) % N
+        lo, hi = part(count, N, a), part(count, N, a + 1)
+        b.row(st, root, a, lo, hi - lo)
+
+
 def _chunk_range_rows(b: _Builder, st, N, count, root, src_v, dst_v, rel_lo, rel_hi):
     """Rows moving relative chunks [rel_lo, rel_hi) from relative rank src_v to
     dst_v; absolute chunk = (root + rel) mod N, split where it wraps."""
@@ -399,7 +422,10 @@ VALID = {
     "scatter": ("binomial",),
     "gather": ("binomial",),
     "alltoall": ("pairwise", "bruck"),
+    "reduce": ("binomial",),
 }
+VALID["broadcast"] = VALID["broadcast"] + ("scatter_allgather",)
+VALID["scatter"] = VALID["scatter"] + ("linear",)
 
 
 def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
@@ -437,10 +463,18 @@ def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
             _bcast_binomial(b, N, count, root)
         elif algo == "chain_pipe":
             _bcast_chain_pipe(b, N, count, root, chunks)
-        else:
+        elif algo == "binomial_pipe":
             _bcast_binomial_pipe(b, N, count, root, chunks)
+        else:
+            # "一对多通信：Broadcast 与 Scatter", Broadcast 与 Scatter 的关系: Scatter
+            # then AllGather; the chunks stay at their offsets, so after the
+            # binomial Scatter rank i holds chunk i, which the Ring AllGather needs
+            _scatter_binomial(b, N, count, root)
+            _ring_ag(b, N, count)
     elif kind == "scatter":
-        _scatter_binomial(b, N, count, root)
+        (_scatter_binomial if algo == "binomial" else _scatter_linear)(b, N, count, root)
+    elif kind == "reduce":
+        _reduce_binomial(b, N, count, root)
     elif kind == "gather":
         _gather_binomial(b, N, count, root)
     else:

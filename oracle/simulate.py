@@ -86,7 +86,8 @@ def defined_regions(kind: str, nranks: int, count: int, root: int = 0):
     """Per rank, the element ranges whose final value the collective defines.
 
     AllReduce / AllGather / Broadcast / AllToAll: the whole buffer.
-    ReduceScatter and Scatter: chunk i of rank i.  Gather: all of the root.
+    ReduceScatter and Scatter: chunk i of rank i.  Gather and Reduce: all of
+    the root.
     """
     N = nranks
     out = []
@@ -95,7 +96,7 @@ def defined_regions(kind: str, nranks: int, count: int, root: int = 0):
             out.append([(0, count)])
         elif kind in ("reducescatter", "scatter"):
             out.append([(part(count, N, i), part(count, N, i + 1))])
-        elif kind == "gather":
+        elif kind in ("gather", "reduce"):
             out.append([(0, count)] if i == root else [])
         else:
             raise ValueError(kind)
@@ -135,6 +136,11 @@ def scatter(arrays, dtype, root=0, algo="binomial", trace=False):
 def gather(arrays, dtype, root=0, algo="binomial", trace=False):
     """The root collects chunk i of every rank i."""
     return _run("gather", algo, arrays, dtype, root=root, trace=trace)
+
+
+def reduce(arrays, dtype, op="sum", root=0, algo="binomial", trace=False):
+    """The root ends with the elementwise reduction over ranks."""
+    return _run("reduce", algo, arrays, dtype, op, root=root, trace=trace)
 
 
 def alltoall(send, dtype, algo="pairwise", trace=False):

@@ -290,3 +290,38 @@ def test_hazard_checker_rejects_planted_conflicts():
     bad.steps[1][1] = replace(r1, dst=r0.src, dst_off=r0.src_off, reduce=False)
     with pytest.raises(AssertionError):
         check_hazards(bad)
+
+
+# --- Tree Reduce, linear Scatter, Broadcast as Scatter + AllGather ---------------
+
+@pytest.mark.parametrize("N", NS)
+def test_reduce_and_linear_scatter_counts(N):
+    """Tree Reduce: log2 N steps of the whole message (eq:model-algo-reduce-tree);
+    naive Scatter: N-1 steps, (N-1)M/N bytes (eq:onetoall-scatter-naive);
+    Scatter + AllGather Broadcast: ceil(log2 N) + N-1 steps, 2(N-1)M/N bytes."""
+    sz, count = 4, N * 64 * 8
+    M, L = count * sz, ceil_log2(N)
+    for root in {0, N - 1}:
+        red = make_plan("reduce", "binomial", N, count, root)
+        assert red.nsteps == L
+        assert counts(red, sz)["crit_bytes"] == L * M
+        assert all(r.n == count and r.reduce for r in red.rows)
+        lin = make_plan("scatter", "linear", N, count, root)
+        assert lin.nsteps == N - 1
+        assert counts(lin, sz)["crit_bytes"] == (N - 1) * M // N
+        assert all(r.src == root for r in lin.rows)
+        sag = make_plan("broadcast", "scatter_allgather", N, count, root)
+        assert sag.nsteps == L + N - 1
+        assert counts(sag, sz)["crit_bytes"] == 2 * (N - 1) * M // N
+
+
+@pytest.mark.parametrize("N", NS)
+@pytest.mark.parametrize("root", [0, 3])
+def test_reduce_is_binomial_broadcast_reversed(N, root):
+    """Tree Reduce is the tree Broadcast run backwards ("对称操作")."""
+    if root >= N:
+        pytest.skip("root outside the ranks")
+    bc = make_plan("broadcast", "binomial", N, 10, root)
+    red = make_plan("reduce", "binomial", N, 10, root)
+    for b_rows, r_rows in zip(bc.steps, reversed(red.steps)):
+        assert sorted((r.src, r.dst) for r in b_rows) == sorted((r.dst, r.src) for r in r_rows)

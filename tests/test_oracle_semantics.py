@@ -322,6 +322,8 @@ def _mutants(plan):
                     replace(r, dst=(r.dst + 1) % plan.nranks) if (r.dst + 1) % plan.nranks != r.src else None,
                     replace(r, src_off=(r.src_off + r.n) % plan.count, dst_off=(r.dst_off + r.n) % plan.count),
                     replace(r, reduce=not r.reduce)):
+            if bad == r:
+                continue                      # a shift by the whole buffer changes nothing
             steps = [list(s) for s in plan.steps]
             st = steps[r.step]
             pos = st.index(r)
@@ -356,5 +358,65 @@ def test_planted_schedule_mistakes_are_caught(kind, algo):
         ok = all(np.array_equal(out[i][regions[i]], want[regions[i]]) for i in range(N))
         ok = ok and all(np.array_equal(fout[i][regions[i]].view(np.uint32),
                                        fwant[regions[i]].view(np.uint32)) for i in range(N))
+        caught += not ok
+    assert caught == len(muts)
+
+
+# --- Tree Reduce, linear Scatter, Broadcast as Scatter + AllGather ---------------
+
+@pytest.mark.parametrize("N", NS_SMALL)
+def test_reduce_linear_scatter_scatter_allgather_brute_force(N):
+    g = np.random.default_rng(300 + N)
+    for count in counts_for(N):
+        a = [g.integers(-(1 << 31), (1 << 31) - 1, count, endpoint=True, dtype=np.int32) for _ in range(N)]
+        want = wrap_sum(a) if count else np.zeros(0, np.int32)
+        for root in sorted({0, N // 2, N - 1}):
+            assert np.array_equal(oracle.reduce(a, "int32", root=root)[root], want)
+            for op, fn in (("max", np.max), ("min", np.min)):
+                if count:
+                    assert np.array_equal(oracle.reduce(a, "int32", op=op, root=root)[root], fn(np.stack(a), axis=0))
+            sc = oracle.scatter(a, "int32", root, algo="linear")
+            for i in range(N):
+                assert np.array_equal(sc[i][chunk(count, N, i)], a[root][chunk(count, N, i)])
+            for o in oracle.broadcast(a, "int32", root, algo="scatter_allgather"):
+                assert np.array_equal(o, a[root])
+
+
+def binomial_fold(a, dtype, N, root):
+    """Relative rank v's value after step j is its own folded with the subtree
+    [v + 2^(j-1), v + 2^j): R(v, j) = R(v, j-1) + R(v + 2^(j-1), j-1)."""
+    def R(v, j):
+        if j == 0:
+            return a[(root + v) % N]
+        d = 1 << (j - 1)
+        acc = R(v, j - 1)
+        return add(dtype, acc, R(v + d, j - 1)) if v + d < N else acc
+    L = 0
+    while (1 << L) < N:
+        L += 1
+    return R(0, L)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("N", [2, 3, 5, 8, 13, 16])
+def test_reduce_association_matches_binomial_fold(N, dtype):
+    count = 21 * N + 2
+    a = f32_rank(N, count, 50 + N) if dtype == "float32" else bf16_rank(N, count, 50 + N)
+    for root in (0, N - 1):
+        got = oracle.reduce(a, dtype, root=root)[root]
+        assert np.array_equal(got.view(np.uint8), binomial_fold(a, dtype, N, root).view(np.uint8))
+
+
+def test_planted_reduce_mistakes_are_caught():
+    N, count = 8, 40
+    a = rng_ints(N, count, 9)
+    f = f32_rank(N, count, 10)
+    plan = make_plan("reduce", "binomial", N, count, 2)
+    fwant = binomial_fold(f, "float32", N, 2)
+    muts = _mutants(plan)
+    caught = 0
+    for m in muts:
+        ok = np.array_equal(run_plan(m, "int32", "sum", a)[2], wrap_sum(a))
+        ok = ok and np.array_equal(run_plan(m, "float32", "sum", f)[2].view(np.uint32), fwant.view(np.uint32))
         caught += not ok
     assert caught == len(muts)
