@@ -203,7 +203,8 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
         for algo in ("chain_pipe", "binomial_pipe"):
             kstar = model.best_chunks(algo, 8, M, 5e-6, 450e9)
             cases += [("broadcast", algo, k) for k in sorted({1, 8, 64, kstar}) if k <= M]
-        cases += [("scatter", "binomial", 1), ("gather", "binomial", 1)]
+        cases += [("broadcast", "scatter_allgather", 1), ("scatter", "binomial", 1), ("scatter", "linear", 1),
+                  ("gather", "binomial", 1)]
         for kind, algo, k in cases:
             fn = coll.COLLECTIVE_FNS[kind]
             med, mn = time_call(lambda: fn(list(live), algo=algo, root=0, chunks=k), pristine, live)
@@ -226,6 +227,15 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
                 record("C3", "allreduce", algo, dtype, 8, count, 1, med, mn, ot)
             del pristine, live
             torch.cuda.empty_cache()
+
+    # Tree Reduce, 8 ranks, fp32 (the Reduce the pages pair with the tree Broadcast)
+    for lg in ((20, 28) if quick else (12, 16, 20, 24, 28)):
+        count = (1 << lg) // 4
+        pristine = torch.stack(si.device_rank_tensors(3, 8, count, "float32", dev))
+        live = pristine.clone()
+        med, mn = time_call(lambda: coll.coll_reduce(list(live), algo="binomial", root=0), pristine, live)
+        record("reduce", "reduce", "binomial", "float32", 8, count, 1, med, mn)
+        del pristine, live
 
     # C4: ReduceScatter and AllGather, 64 ranks x 256 MiB bf16 (16 GiB resident)
     if not quick:

@@ -95,9 +95,13 @@ def coll_alltoall(send, recv, op="sum", algo="default", root=0, chunks=1, stream
     _collective("coll_alltoall", send, recv, op, algo, root, chunks, stream)
 
 
+def coll_reduce(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    _collective("coll_reduce", send, recv, op, algo, root, chunks, stream)
+
+
 COLLECTIVE_FNS = {"allreduce": coll_allreduce, "reducescatter": coll_reducescatter, "allgather": coll_allgather,
                   "broadcast": coll_broadcast, "scatter": coll_scatter, "gather": coll_gather,
-                  "alltoall": coll_alltoall}
+                  "alltoall": coll_alltoall, "reduce": coll_reduce}
 
 
 def coll_plan(kind, algo, nranks, count, dtype, root=0, chunks=1):

@@ -329,7 +329,8 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   st = device_info(dev, di);
   if (st != COLL_OK) return st;
   const coll_algo_t ra = resolve_algo(kind, algo);
-  const bool rooted = kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER;
+  const bool rooted =
+      kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER || kind == COLL_K_REDUCE;
   const bool pipe = ra == COLL_ALGO_CHAIN_PIPE || ra == COLL_ALGO_BINOMIAL_PIPE;
   Key k{dev, int(kind), int(ra), N, count, sz, rooted ? root : 0, pipe ? chunks : 1, inplace ? 1 : 0};
   Entry* e = nullptr;
@@ -449,6 +450,7 @@ COLL_ENTRY(coll_broadcast, COLL_K_BROADCAST)
 COLL_ENTRY(coll_scatter, COLL_K_SCATTER)
 COLL_ENTRY(coll_gather, COLL_K_GATHER)
 COLL_ENTRY(coll_alltoall, COLL_K_ALLTOALL)
+COLL_ENTRY(coll_reduce, COLL_K_REDUCE)
 
 coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t count, coll_dtype_t dtype, int root,
                         int chunks, coll_row_t* rows, size_t* nrows, coll_counts_t* counts) {

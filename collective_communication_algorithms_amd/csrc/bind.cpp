@@ -72,6 +72,7 @@ std::vector<std::pair<int64_t, int64_t>> defined_output(const Schedule& s, int r
     case COLL_K_REDUCESCATTER:
     case COLL_K_SCATTER: return {{lo, hi}};
     case COLL_K_GATHER:
+    case COLL_K_REDUCE:
       if (rank == s.root) return {{0, s.count}};
       return {};
     default: return {{0, s.count}};

@@ -295,6 +295,29 @@ void gather_binomial(Emitter& e) {
   }
 }
 
+// eq:onetoall-scatter-naive: the root sends rank root+i its chunk at step i.
+void scatter_linear(Emitter& e) {
+  const int N = e.s.N, root = e.s.root;
+  for (int i = 1; i < N; ++i) {
+    e.step();
+    const int a = abs_rank(root, i, N);
+    e.chunks(root, a, a, a + 1, false);
+  }
+}
+
+// Tree Reduce ("集合通信算法延迟公式", eq:model-algo-reduce-tree): the tree
+// Broadcast run backwards; at step j every relative rank v with lowest set bit
+// 2^(j-1) reduces its partial result into v - 2^(j-1).
+void reduce_binomial(Emitter& e) {
+  const int N = e.s.N, L = ceil_log2(N), root = e.s.root;
+  for (int j = L; j >= 1; --j) {
+    e.step();
+    binomial_substep(N, j, [&](int v, int w, int) {
+      e.row(abs_rank(root, w, N), abs_rank(root, v, N), 0, 0, e.s.count, true);
+    });
+  }
+}
+
 // ---- AllToAll (eq:model-algo-a2a-pairwise / -bruck)
 void a2a_pairwise(Emitter& e) {
   const int N = e.s.N;
@@ -333,9 +356,11 @@ bool algo_valid(coll_kind_t kind, coll_algo_t a) {
     case COLL_K_REDUCESCATTER:
     case COLL_K_ALLGATHER: return a == COLL_ALGO_RING || a == COLL_ALGO_RHD;
     case COLL_K_BROADCAST:
-      return a == COLL_ALGO_BINOMIAL || a == COLL_ALGO_CHAIN_PIPE || a == COLL_ALGO_BINOMIAL_PIPE;
-    case COLL_K_SCATTER:
-    case COLL_K_GATHER: return a == COLL_ALGO_BINOMIAL;
+      return a == COLL_ALGO_BINOMIAL || a == COLL_ALGO_CHAIN_PIPE || a == COLL_ALGO_BINOMIAL_PIPE ||
+             a == COLL_ALGO_SCATTER_ALLGATHER;
+    case COLL_K_SCATTER: return a == COLL_ALGO_BINOMIAL || a == COLL_ALGO_LINEAR;
+    case COLL_K_GATHER:
+    case COLL_K_REDUCE: return a == COLL_ALGO_BINOMIAL;
     case COLL_K_ALLTOALL: return a == COLL_ALGO_PAIRWISE || a == COLL_ALGO_BRUCK;
   }
   return false;
@@ -357,7 +382,8 @@ coll_algo_t resolve_algo(coll_kind_t kind, coll_algo_t algo) {
     case COLL_K_ALLGATHER: return COLL_ALGO_RING;
     case COLL_K_BROADCAST:
     case COLL_K_SCATTER:
-    case COLL_K_GATHER: return COLL_ALGO_BINOMIAL;
+    case COLL_K_GATHER:
+    case COLL_K_REDUCE: return COLL_ALGO_BINOMIAL;
     case COLL_K_ALLTOALL: return COLL_ALGO_PAIRWISE;
   }
   return algo;
@@ -365,7 +391,7 @@ coll_algo_t resolve_algo(coll_kind_t kind, coll_algo_t algo) {
 
 coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64_t count, int root,
                              int chunks, Schedule& out, std::string& err) {
-  if (int(kind) < 0 || int(kind) > int(COLL_K_ALLTOALL)) {
+  if (int(kind) < 0 || int(kind) > int(COLL_K_REDUCE)) {
     err = "unknown collective";
     return COLL_ERR_INVALID_ARG;
   }
@@ -382,7 +408,7 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     return COLL_ERR_INVALID_ARG;
   }
   const coll_algo_t algo = resolve_algo(kind, algo_in);
-  if (int(algo) < 1 || int(algo) > int(COLL_ALGO_BRUCK) || !algo_valid(kind, algo)) {
+  if (int(algo) < 1 || int(algo) > int(COLL_ALGO_SCATTER_ALLGATHER) || !algo_valid(kind, algo)) {
     err = "algorithm not defined for this collective";
     return COLL_ERR_UNSUPPORTED;
   }
@@ -390,7 +416,8 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     err = "recursive halving-doubling and the double binary tree need a power-of-two N";
     return COLL_ERR_UNSUPPORTED;
   }
-  const bool rooted = kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER;
+  const bool rooted =
+      kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER || kind == COLL_K_REDUCE;
   if (rooted && (root < 0 || root >= N)) {
     err = "root outside [0, nranks)";
     return COLL_ERR_INVALID_ARG;
@@ -432,10 +459,20 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     case COLL_K_BROADCAST:
       if (algo == COLL_ALGO_BINOMIAL) bcast_binomial(e);
       else if (algo == COLL_ALGO_CHAIN_PIPE) bcast_chain_pipe(e);
-      else bcast_binomial_pipe(e);
+      else if (algo == COLL_ALGO_BINOMIAL_PIPE) bcast_binomial_pipe(e);
+      else {
+        // "一对多通信：Broadcast 与 Scatter", Broadcast 与 Scatter 的关系: chunks stay
+        // at their offsets, so after the Scatter rank i holds chunk i, which
+        // is what the Ring AllGather starts from
+        scatter_binomial(e);
+        ring_all_gather(e);
+      }
       break;
-    case COLL_K_SCATTER: scatter_binomial(e); break;
+    case COLL_K_SCATTER:
+      if (algo == COLL_ALGO_BINOMIAL) scatter_binomial(e); else scatter_linear(e);
+      break;
     case COLL_K_GATHER: gather_binomial(e); break;
+    case COLL_K_REDUCE: reduce_binomial(e); break;
     case COLL_K_ALLTOALL:
       if (algo == COLL_ALGO_PAIRWISE) a2a_pairwise(e); else a2a_bruck(e);
       break;

@@ -49,6 +49,13 @@ def time(kind: str, algo: str, N: int, M: float, alpha: float, beta: float, k: i
             return (L + k - 1) * (alpha + M / (k * beta))
     if kind in ("scatter", "gather") and algo == "binomial":
         return L * alpha + frac * M / beta
+    if kind == "scatter" and algo == "linear":
+        return (N - 1) * alpha + frac * M / beta          # eq:onetoall-scatter-naive
+    if kind == "broadcast" and algo == "scatter_allgather":
+        return (time("scatter", "binomial", N, M, alpha, beta) +
+                time("allgather", "ring", N, M, alpha, beta))
+    if kind == "reduce" and algo == "binomial":
+        return L * (alpha + M / beta)                      # eq:model-algo-reduce-tree
     if kind == "alltoall":
         if algo in ("pairwise", "ring"):
             return (N - 1) * alpha + frac * M / beta

@@ -28,7 +28,7 @@
  *                is COLL_ERR_INVALID_ARG.  AllToAll must be out of place.
  *   chunk c of a rank buffer = elements [c*count/N, (c+1)*count/N) (floor).
  *   op     ignored by collectives that do not reduce.
- *   root   used by broadcast / scatter / gather only; 0 <= root < N.
+ *   root   used by broadcast / scatter / gather / reduce only; 0 <= root < N.
  *   chunks pipeline chunk count k for COLL_ALGO_CHAIN_PIPE and
  *          COLL_ALGO_BINOMIAL_PIPE (1 <= k <= count); ignored otherwise.
  *   stream a hipStream_t; the work is enqueued on it and the call returns
@@ -80,12 +80,14 @@ typedef enum {
   COLL_ALGO_CHAIN_PIPE = 5,    /* [P1] chunked chain pipeline Broadcast (k = 1: chain)         */
   COLL_ALGO_BINOMIAL_PIPE = 6, /* [P1] chunked binomial-tree pipeline Broadcast (k = 1: tree)  */
   COLL_ALGO_PAIRWISE = 7,      /* [P3] Pairwise AllToAll, N-1 rounds                           */
-  COLL_ALGO_BRUCK = 8          /* [P3] Bruck AllToAll, ceil(log2 N) rounds plus rotations      */
+  COLL_ALGO_BRUCK = 8,         /* [P3] Bruck AllToAll, ceil(log2 N) rounds plus rotations      */
+  COLL_ALGO_LINEAR = 9,        /* [P1] naive Scatter: the root sends each chunk directly      */
+  COLL_ALGO_SCATTER_ALLGATHER = 10 /* [P1] Broadcast as binomial Scatter + Ring AllGather     */
 } coll_algo_t;
 
 typedef enum {
   COLL_K_ALLREDUCE = 0, COLL_K_REDUCESCATTER = 1, COLL_K_ALLGATHER = 2, COLL_K_BROADCAST = 3,
-  COLL_K_SCATTER = 4, COLL_K_GATHER = 5, COLL_K_ALLTOALL = 6
+  COLL_K_SCATTER = 4, COLL_K_GATHER = 5, COLL_K_ALLTOALL = 6, COLL_K_REDUCE = 7
 } coll_kind_t;
 
 /* Largest N the kernels accept (all rank pointers travel as kernel arguments). */
@@ -113,14 +115,16 @@ coll_status_t coll_allgather(void* const* sendbufs, void* const* recvbufs, int n
                              void* stream);
 
 /* [P1] Broadcast (eq:onetoall-bcast-semantic): every buffer ends equal to the
- * root's.  algo: BINOMIAL (default), CHAIN_PIPE, BINOMIAL_PIPE with `chunks`. */
+ * root's.  algo: BINOMIAL (default), CHAIN_PIPE, BINOMIAL_PIPE with `chunks`,
+ * SCATTER_ALLGATHER (binomial Scatter, then Ring AllGather; [P1] "Broadcast 与
+ * Scatter 的关系"). */
 coll_status_t coll_broadcast(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                              coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                              void* stream);
 
 /* [P1] Scatter (eq:onetoall-scatter-semantic): the root's chunk i lands in
  * chunk i of rank i; other chunks of non-root buffers are staging space and
- * left unspecified.  algo: BINOMIAL. */
+ * left unspecified.  algo: BINOMIAL (default), LINEAR (eq:onetoall-scatter-naive). */
 coll_status_t coll_scatter(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                            coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                            void* stream);
@@ -129,6 +133,13 @@ coll_status_t coll_scatter(void* const* sendbufs, void* const* recvbufs, int nra
  * of rank i lands in chunk i of the root; non-root buffers are left
  * unspecified.  algo: BINOMIAL. */
 coll_status_t coll_gather(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                          coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                          void* stream);
+
+/* [P3] Tree Reduce (eq:model-algo-reduce-tree, the mirror of the tree
+ * Broadcast): the root ends with the elementwise reduction over ranks; the
+ * other buffers hold partial results (unspecified).  algo: BINOMIAL. */
+coll_status_t coll_reduce(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                           coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                           void* stream);
 

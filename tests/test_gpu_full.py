@@ -83,9 +83,15 @@ def test_broadcast_n8_64MiB(algo, k):
     check_sampled("broadcast", algo, 8, 64 << 20, "uint8", 2, k=k)
 
 
-@pytest.mark.parametrize("kind", ["scatter", "gather"])
-def test_scatter_gather_n8_64MiB(kind):
-    check_sampled(kind, "binomial", 8, 64 << 20, "uint8", 2)
+@pytest.mark.parametrize("kind,algo", [("scatter", "binomial"), ("scatter", "linear"), ("gather", "binomial"),
+                                       ("broadcast", "scatter_allgather")])
+def test_scatter_gather_n8_64MiB(kind, algo):
+    check_sampled(kind, algo, 8, 64 << 20, "uint8", 2)
+
+
+@pytest.mark.parametrize("dtype,sigma", [("float32", 1.0), ("bfloat16", 0.02)])
+def test_reduce_n8_256MiB(dtype, sigma):
+    check_sampled("reduce", "binomial", 8, (256 << 20) // si.ITEMSIZE[dtype], dtype, 3, sigma=sigma, root=3)
 
 
 @pytest.mark.parametrize("kind", ["reducescatter", "allgather"])

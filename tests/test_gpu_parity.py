@@ -102,8 +102,8 @@ def _algos(kind, N):
     return {"allreduce": ["ring"] + (["rhd", "dbt"] if pow2 else []),
             "reducescatter": ["ring"] + (["rhd"] if pow2 else []),
             "allgather": ["ring"] + (["rhd"] if pow2 else []),
-            "broadcast": ["binomial", "chain_pipe", "binomial_pipe"],
-            "scatter": ["binomial"], "gather": ["binomial"],
+            "broadcast": ["binomial", "chain_pipe", "binomial_pipe", "scatter_allgather"],
+            "scatter": ["binomial", "linear"], "gather": ["binomial"], "reduce": ["binomial"],
             "alltoall": ["pairwise", "bruck"]}[kind]
 
 
@@ -112,12 +112,12 @@ def test_ragged_counts_every_collective(N):
     g = np.random.default_rng(N)
     for count in sorted({1, max(N - 1, 1), 3 * N + 1, 4099, 70001}):
         a = [g.integers(-1000, 1000, count, dtype=np.int32) for _ in range(N)]
-        for kind in ("allreduce", "reducescatter", "allgather", "broadcast", "scatter", "gather"):
+        for kind in ("allreduce", "reducescatter", "allgather", "broadcast", "scatter", "gather", "reduce"):
             for algo in _algos(kind, N):
                 for k in ([1, 3] if algo.endswith("_pipe") else [1]):
                     if k > count:
                         continue
-                    root = (N - 1) if kind in ("broadcast", "scatter", "gather") else 0
+                    root = (N - 1) if kind in ("broadcast", "scatter", "gather", "reduce") else 0
                     assert_parity(kind, algo, a, "int32", root=root, k=k, checksums=(count < 5000))
         if count % N == 0:
             for algo in _algos("alltoall", N):
@@ -129,9 +129,9 @@ def test_out_of_place_every_collective(N):
     g = np.random.default_rng(100 + N)
     count = 6 * N * 97
     a = [g.integers(-1000, 1000, count, dtype=np.int32) for _ in range(N)]
-    for kind in ("allreduce", "reducescatter", "allgather", "broadcast", "scatter", "gather"):
+    for kind in ("allreduce", "reducescatter", "allgather", "broadcast", "scatter", "gather", "reduce"):
         for algo in _algos(kind, N):
-            root = N // 2 if kind in ("broadcast", "scatter", "gather") else 0
+            root = N // 2 if kind in ("broadcast", "scatter", "gather", "reduce") else 0
             assert_parity(kind, algo, a, "int32", root=root, k=5 if algo.endswith("_pipe") else 1,
                           inplace=False, checksums=True)
 
@@ -161,6 +161,23 @@ def test_reduction_ops(dtype, op):
     a = si.rank_arrays(8, N, count, dtype)
     for algo in ("ring", "rhd", "dbt"):
         assert_parity("allreduce", algo, a, dtype, op=op)
+    for root in (0, 5):
+        assert_parity("reduce", "binomial", a, dtype, op=op, root=root, checksums=True)
+
+
+@pytest.mark.parametrize("N", [2, 5, 8, 13])
+def test_tree_reduce_float(N):
+    """Tree Reduce: the root's result is bit-exact with the oracle and within
+    the tolerance of the fp64 sum."""
+    count = 4096 * N + 7
+    for dtype, sigma in (("float32", 1.0), ("bfloat16", 0.02)):
+        a = si.rank_arrays(3, N, count, dtype, sigma=sigma)
+        got, _ = assert_parity("reduce", "binomial", a, dtype, root=N - 1, checksums=True)
+        wide = [x.astype(np.float64) if dtype == "float32" else numerics.bf16_to_f32(x).astype(np.float64)
+                for x in a]
+        y64 = np.sum(wide, axis=0)
+        y = got[N - 1].astype(np.float64) if dtype == "float32" else numerics.bf16_to_f32(got[N - 1]).astype(np.float64)
+        assert np.linalg.norm(y - y64) / np.linalg.norm(y64) <= (1e-5 if dtype == "float32" else 1e-2)
 
 
 def test_int32_sums_wrap():

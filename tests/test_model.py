@@ -67,3 +67,13 @@ def test_best_chunks_is_the_argmin_of_the_formula():
         k = model.best_chunks("chain_pipe", 8, m, a, b)
         t = model.time("broadcast", "chain_pipe", 8, m, a, b, k)
         assert all(model.time("broadcast", "chain_pipe", 8, m, a, b, j) >= t for j in range(1, 200))
+
+
+def test_reduce_and_scatter_formulas():
+    """Tree Reduce has the tree Broadcast's formula (eq:model-algo-reduce-tree);
+    naive Scatter is (N-1)(alpha + M/(N beta)) (eq:onetoall-scatter-naive)."""
+    a, b, M = 5e-6, 450e9, 1 << 24
+    for N in (2, 8, 16):
+        assert model.time("reduce", "binomial", N, M, a, b) == pytest.approx(model.time("broadcast", "binomial", N, M, a, b))
+        assert model.time("scatter", "linear", N, M, a, b) == pytest.approx((N - 1) * (a + M / (N * b)))
+        assert model.latency_steps("broadcast", "scatter_allgather", N) == (N - 1) + model.latency_steps("scatter", "binomial", N)

@@ -136,3 +136,12 @@ def test_plans_random_shapes():
         compare("scatter", "binomial", N, count, root, dtype="uint8")
         compare("gather", "binomial", N, count, root, dtype="uint8")
         compare("allreduce", "ring", N, count, dtype="int32")
+
+
+@pytest.mark.parametrize("N", NS)
+def test_reduce_linear_scatter_scatter_allgather_match(N):
+    for count in sorted({1, N, 5 * N + 3, 777}):
+        for root in sorted({0, 1 % N, N // 2, N - 1}):
+            compare("reduce", "binomial", N, count, root, dtype="float32")
+            compare("scatter", "linear", N, count, root, dtype="uint8")
+            compare("broadcast", "scatter_allgather", N, count, root, dtype="uint8")
