@@ -158,6 +158,52 @@ def _rhd_rs(b: _Builder, N: int, count: int):
     return seg
 
 
+def _rhd_ar_folded(b: _Builder, N: int, count: int):
+    """Recursive halving-doubling AllReduce for N that is not a power of two.
+
+    The page requires N = 2^n; the source it cites folds the surplus first.
+    With P the largest power of two below N and r = N - P: rank 2i reduces its
+    whole buffer into rank 2i+1 (i < r); the P ranks 2i+1 (i < r) and 2r..N-1
+    then run halving and doubling on the P-way partition of the buffer as core
+    ranks 0..P-1; finally rank 2i+1 copies the result back to rank 2i.
+    2 log2 P + 2 steps."""
+    P = 1 << (N.bit_length() - 1)
+    r = N - P
+    core = [2 * i + 1 for i in range(r)] + list(range(2 * r, N))
+    st = b.new_step()
+    for i in range(r):
+        b.row(st, 2 * i, 2 * i + 1, 0, count, reduce=True)
+    seg = [(0, P)] * P
+    d = P // 2
+    while d >= 1:
+        st = b.new_step()
+        new = list(seg)
+        for j in range(P):
+            lo, hi = seg[j]
+            mid = (lo + hi) // 2
+            keep = (lo, mid) if (j & d) == 0 else (mid, hi)
+            new[j] = keep
+            a, z = part(count, P, keep[0]), part(count, P, keep[1])
+            b.row(st, core[j ^ d], core[j], a, z - a, reduce=True)
+        seg = new
+        d //= 2
+    seg = [(j, j + 1) for j in range(P)]
+    d = 1
+    while d < P:
+        st = b.new_step()
+        new = list(seg)
+        for j in range(P):
+            lo, hi = seg[j ^ d]
+            a, z = part(count, P, lo), part(count, P, hi)
+            b.row(st, core[j ^ d], core[j], a, z - a)
+            new[j] = (min(seg[j][0], lo), max(seg[j][1], hi))
+        seg = new
+        d <<= 1
+    st = b.new_step()
+    for i in range(r):
+        b.row(st, 2 * i + 1, 2 * i, 0, count)
+
+
 def _rhd_ag(b: _Builder, N: int, count: int):
     """log2 N doubling rounds.  Round k: distance d = 2^k; each rank copies in its
     partner's current block of 2^k chunks; the block doubles."""
@@ -192,7 +238,8 @@ def dbt_trees(N: int):
     """The two complementary trees, as {node: [children]} with root noted.
 
     The page asks for two binary trees of height log2 N with different parent /
-    child relations, each carrying half the data.  Construction (for N = 2^n):
+    child relations, each carrying half the data.  Construction (any N >= 2;
+    for N = 2^n the two trees have complementary leaves):
     tree 1 has rank 0 as root whose only child is the root of build(1, N);
     build(lo, hi) takes as node the element of [lo, hi) with the most trailing
     zero bits (unique in a run of consecutive integers), with left subtree
@@ -244,7 +291,9 @@ def _heights_depths(root, tree):
 def _dbt_ar(b: _Builder, N: int, count: int):
     """Reduce up both trees (level by height, left child before right child,
     tree 1 before tree 2), then broadcast down (level by depth).  Tree 1 carries
-    elements [0, count//2), tree 2 [count//2, count).  2*log2 N steps."""
+    elements [0, count//2), tree 2 [count//2, count).  2*ceil(log2 N) steps.
+    When a node's children have different heights (N not a power of two) the
+    lower child's value arrives one step earlier and is reduced first."""
     H = ceil_log2(N)
     halves = [(0, count // 2), (count // 2, count)]
     trees = dbt_trees(N)
@@ -436,8 +485,8 @@ def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
         raise ValueError(f"{algo} is not an algorithm of {kind}")
     if N < 1:
         raise ValueError("nranks")
-    if algo in ("rhd", "dbt") and not is_pow2(N):
-        raise ValueError("recursive halving-doubling and the double binary tree need N = 2^n")
+    if algo == "rhd" and kind != "allreduce" and not is_pow2(N):
+        raise ValueError("recursive halving-doubling ReduceScatter / AllGather need N = 2^n")
     if kind == "alltoall" and count % N:
         raise ValueError("alltoall needs count divisible by N")
     if algo in ("chain_pipe", "binomial_pipe") and not (1 <= chunks <= max(count, 1)):
@@ -449,8 +498,11 @@ def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
             _ring_rs(b, N, count)
             _ring_ag(b, N, count)
         elif algo == "rhd":
-            _rhd_rs(b, N, count)
-            _rhd_ag(b, N, count)
+            if is_pow2(N):
+                _rhd_rs(b, N, count)
+                _rhd_ag(b, N, count)
+            else:
+                _rhd_ar_folded(b, N, count)
         else:
             if N >= 2:
                 _dbt_ar(b, N, count)

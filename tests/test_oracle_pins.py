@@ -325,3 +325,31 @@ def test_reduce_is_binomial_broadcast_reversed(N, root):
     red = make_plan("reduce", "binomial", N, 10, root)
     for b_rows, r_rows in zip(bc.steps, reversed(red.steps)):
         assert sorted((r.src, r.dst) for r in b_rows) == sorted((r.dst, r.src) for r in r_rows)
+
+
+# --- non-power-of-two N: folded halving-doubling, general double binary tree -----
+
+@pytest.mark.parametrize("N", [3, 5, 6, 7, 9, 12, 13, 31, 33])
+def test_folded_rhd_and_general_dbt_counts(N):
+    """RHD with N != 2^n: the r = N - P surplus ranks fold into a P = 2^floor(log2 N)
+    core, the core runs 2 log2 P halving / doubling rounds, the result is copied
+    back: 2 log2 P + 2 steps; bytes M + 2(P-1)M/P + M.  DBT: 2 ceil(log2 N) steps."""
+    P = 1 << (N.bit_length() - 1)
+    lP = P.bit_length() - 1
+    sz, count = 4, 64 * P * N
+    M = count * sz
+    rhd = make_plan("allreduce", "rhd", N, count)
+    assert rhd.nsteps == 2 * lP + 2
+    assert counts(rhd, sz)["crit_bytes"] == M + 2 * (P - 1) * M // P + M
+    assert {(r.src, r.dst) for r in rhd.steps[0]} == {(2 * i, 2 * i + 1) for i in range(N - P)}
+    assert {(r.src, r.dst) for r in rhd.steps[-1]} == {(2 * i + 1, 2 * i) for i in range(N - P)}
+    dbt = make_plan("allreduce", "dbt", N, count)
+    assert dbt.nsteps == 2 * ceil_log2(N)
+    for root, t in dbt_trees(N):
+        kids = [c for cs in t.values() for c in cs]
+        assert sorted(kids + [root]) == list(range(N))
+        assert all(len(cs) <= 2 for u, cs in t.items() if u != root)
+
+        def height(u):
+            return 0 if not t[u] else 1 + max(height(c) for c in t[u])
+        assert height(root) == ceil_log2(N)

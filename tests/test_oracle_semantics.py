@@ -174,17 +174,42 @@ def butterfly(a, dtype, N):
 
 
 def tree_fold(a, dtype, N):
-    """Each node's value is ((own + left subtree) + right subtree); tree 1 on
+    """Each node's value is its own folded with its children's subtree values in
+    the order they arrive: by subtree height, then left before right (for
+    N = 2^n siblings have equal height: ((own + left) + right)).  Tree 1 on
     the first half of the elements, tree 2 on the second."""
     count = len(a[0])
     out = np.empty_like(a[0])
     for (root, t), sl in zip(dbt_trees(N), (slice(0, count // 2), slice(count // 2, count))):
+        def height(u):
+            return 0 if not t[u] else 1 + max(height(c) for c in t[u])
+
         def fold(u):
             acc = a[u][sl]
-            for c in t[u]:
+            for _, _, c in sorted((height(c), i, c) for i, c in enumerate(t[u])):
                 acc = add(dtype, acc, fold(c))
             return acc
         out[sl] = fold(root)
+    return out
+
+
+def folded_butterfly(a, dtype, N):
+    """RHD for N != 2^n: v(2i+1) = a(2i+1) + a(2i) for i < r = N - P, the P core
+    ranks then fold as a butterfly (distance P/2 first) on the P-way partition;
+    every rank ends with the core's chunks."""
+    P = 1 << (N.bit_length() - 1)
+    r = N - P
+    core = [2 * i + 1 for i in range(r)] + list(range(2 * r, N))
+    v = [add(dtype, a[c], a[c - 1]) if k < r else a[c] for k, c in enumerate(core)]
+    d = P // 2
+    while d >= 1:
+        v = [add(dtype, v[j], v[j ^ d]) for j in range(P)]
+        d //= 2
+    count = len(a[0])
+    out = np.empty_like(a[0])
+    for c in range(P):
+        sl = slice(part(count, P, c), part(count, P, c + 1))
+        out[sl] = v[c][sl]
     return out
 
 
@@ -420,3 +445,43 @@ def test_planted_reduce_mistakes_are_caught():
         ok = ok and np.array_equal(run_plan(m, "float32", "sum", f)[2].view(np.uint32), fwant.view(np.uint32))
         caught += not ok
     assert caught == len(muts)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("N", [3, 5, 6, 7, 9, 12])
+def test_non_power_of_two_association(N, dtype):
+    count = 37 * N + 11
+    a = f32_rank(N, count, 70 + N) if dtype == "float32" else bf16_rank(N, count, 70 + N)
+    want = folded_butterfly(a, dtype, N)
+    for o in oracle.allreduce(a, dtype, algo="rhd"):
+        assert np.array_equal(o.view(np.uint8), want.view(np.uint8))
+    want = tree_fold(a, dtype, N)
+    for o in oracle.allreduce(a, dtype, algo="dbt"):
+        assert np.array_equal(o.view(np.uint8), want.view(np.uint8))
+
+
+@pytest.mark.parametrize("N", list(range(1, 20)) + [31, 33])
+def test_non_power_of_two_brute_force(N):
+    for count in (1, N, 5 * N + 2, 300):
+        a = rng_ints(N, count, 90 + N, lo=-(1 << 31), hi=(1 << 31) - 1)
+        for algo in ("rhd", "dbt"):
+            for o in oracle.allreduce(a, "int32", algo=algo):
+                assert np.array_equal(o, wrap_sum(a)), (algo, N, count)
+
+
+@pytest.mark.parametrize("N", [5, 6])
+def test_planted_non_power_of_two_mistakes_are_caught(N):
+    count = N * 12
+    a = rng_ints(N, count, 4)
+    f = f32_rank(N, count, 5)
+    for algo, fn in (("rhd", folded_butterfly), ("dbt", tree_fold)):
+        plan = make_plan("allreduce", algo, N, count)
+        fwant = fn(f, "float32", N)
+        muts = _mutants(plan)
+        caught = 0
+        for m in muts:
+            ok = all(np.array_equal(o, wrap_sum(a)) for o in run_plan(m, "int32", "sum", a))
+            ok = ok and all(np.array_equal(o.view(np.uint32), fwant.view(np.uint32))
+                            for o in run_plan(m, "float32", "sum", f))
+            caught += not ok
+        assert caught == len(muts), (algo, N)
