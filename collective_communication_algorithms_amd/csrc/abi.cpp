@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstring>
+#include <map>
 #include <memory>
 #include <mutex>
 #include <string>
@@ -28,6 +29,8 @@ std::atomic<int64_t> opt_group{0};     // 0: automatic
 std::atomic<int64_t> opt_grid{0};      // 0: automatic
 std::atomic<int64_t> opt_nt{-1};       // -1: automatic, else an NT_* mask
 std::atomic<int64_t> opt_reverse{1};
+std::atomic<int64_t> opt_alpha_ns{1180};   // COLL_ALGO_AUTO: fitted per-step cost on MI355X
+std::atomic<int64_t> opt_beta_gbps{7000};  // COLL_ALGO_AUTO: fitted schedule-byte rate on MI355X
 
 // Working sets up to the 256 MiB memory-side cache of MI355X stay there between
 // steps when accessed normally; larger ones stream, and then nontemporal source
@@ -113,6 +116,29 @@ std::unordered_map<int, DevInfo> g_dev;
 std::unordered_map<uint64_t, int> g_occ;  // (kernel variant, device) -> blocks per CU
 uint64_t g_tick = 0;
 constexpr size_t CACHE_CAP = 512;
+std::map<std::vector<int64_t>, coll_algo_t> g_auto;  // COLL_ALGO_AUTO decisions
+
+CostModel cost_model() {
+  CostModel m;
+  m.alpha_s = double(opt_alpha_ns.load()) * 1e-9;
+  m.beta_Bps = double(opt_beta_gbps.load()) * 1e9;
+  return m;
+}
+
+coll_status_t auto_algo(coll_kind_t kind, int N, int64_t count, int sz, int root, coll_algo_t& out) {
+  const std::vector<int64_t> key{int64_t(kind), N, count, sz, root, opt_alpha_ns.load(), opt_beta_gbps.load()};
+  auto it = g_auto.find(key);
+  if (it != g_auto.end()) {
+    out = it->second;
+    return COLL_OK;
+  }
+  std::string err;
+  const coll_status_t st = choose_algo(kind, N, count, sz, root, cost_model(), out, err);
+  if (st != COLL_OK) return fail(st, err);
+  if (g_auto.size() > 4096) g_auto.clear();
+  g_auto[key] = out;
+  return COLL_OK;
+}
 
 void free_entry(Entry& e) {
   if (e.d_items) (void)hipFree(e.d_items);
@@ -305,11 +331,13 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   bool inplace = true;
   coll_status_t st = check_buffers(send, recv, N, count, sz, kind == COLL_K_ALLTOALL, inplace);
   if (st != COLL_OK) return st;
+  const bool automatic = algo == COLL_ALGO_AUTO;
+  if (automatic) chunks = 1;
   // validate the algorithm and the scalars even when there is nothing to move
   {
     Schedule probe;
     std::string err;
-    st = build_schedule(kind, algo, N, 0, root, 1, probe, err);
+    st = build_schedule(kind, automatic ? COLL_ALGO_DEFAULT : algo, N, 0, root, 1, probe, err);
     if (st != COLL_OK) return fail(st, err);
     if ((algo == COLL_ALGO_CHAIN_PIPE || algo == COLL_ALGO_BINOMIAL_PIPE) && count > 0 &&
         (chunks < 1 || int64_t(chunks) > count))
@@ -328,7 +356,12 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   DevInfo* di = nullptr;
   st = device_info(dev, di);
   if (st != COLL_OK) return st;
-  const coll_algo_t ra = resolve_algo(kind, algo);
+  coll_algo_t chosen = algo;
+  if (automatic) {
+    st = auto_algo(kind, N, count, sz, root, chosen);
+    if (st != COLL_OK) return st;
+  }
+  const coll_algo_t ra = resolve_algo(kind, chosen);
   const bool rooted =
       kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER || kind == COLL_K_REDUCE;
   const bool pipe = ra == COLL_ALGO_CHAIN_PIPE || ra == COLL_ALGO_BINOMIAL_PIPE;
@@ -461,6 +494,13 @@ coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t c
     if (count > (size_t(1) << 44) / size_t(sz)) return fail(COLL_ERR_INVALID_ARG, "count too large");
     Schedule s;
     std::string err;
+    if (algo == COLL_ALGO_AUTO) {
+      coll_status_t st = build_schedule(kind, COLL_ALGO_DEFAULT, nranks, 0, root, 1, s, err);
+      if (st != COLL_OK) return fail(st, err);
+      st = choose_algo(kind, nranks, int64_t(count), sz, root, cost_model(), algo, err);
+      if (st != COLL_OK) return fail(st, err);
+      chunks = 1;
+    }
     coll_status_t st = build_schedule(kind, algo, nranks, int64_t(count), root, chunks, s, err);
     if (st != COLL_OK) return fail(st, err);
     const size_t cap = *nrows;
@@ -510,6 +550,14 @@ coll_status_t coll_set_option(coll_option_t key, int64_t value) {
       return COLL_OK;
     case COLL_OPT_REVERSE:
       opt_reverse = value ? 1 : 0;
+      return COLL_OK;
+    case COLL_OPT_MODEL_ALPHA_NS:
+      if (value < 0 || value > 1000000000) return fail(COLL_ERR_INVALID_ARG, "alpha out of range");
+      opt_alpha_ns = value;
+      return COLL_OK;
+    case COLL_OPT_MODEL_BETA_GBPS:
+      if (value < 1 || value > 1000000000) return fail(COLL_ERR_INVALID_ARG, "beta out of range");
+      opt_beta_gbps = value;
       return COLL_OK;
     case COLL_OPT_GROUP_TILES:
       if (value < 0 || value > 64) return fail(COLL_ERR_INVALID_ARG, "group tiles in [0, 64]");

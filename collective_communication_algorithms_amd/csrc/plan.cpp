@@ -133,6 +133,44 @@ void rhd_all_gather(Emitter& e) {
   }
 }
 
+// Halving-doubling AllReduce for N that is not a power of two (the page needs
+// N = 2^n; the source it cites folds the surplus first): with P the largest
+// power of two below N and r = N - P, rank 2i reduces its whole buffer into
+// rank 2i+1 (i < r); ranks 2i+1 (i < r) and 2r..N-1 form a core of P ranks
+// that halves and doubles over the P-way partition; rank 2i+1 then copies the
+// result back to rank 2i.
+void rhd_all_reduce_folded(Emitter& e) {
+  const int N = e.s.N;
+  int P = 1;
+  while (P * 2 <= N) P *= 2;
+  const int r = N - P;
+  std::vector<int> core;
+  for (int i = 0; i < r; ++i) core.push_back(2 * i + 1);
+  for (int i = 2 * r; i < N; ++i) core.push_back(i);
+  const int64_t count = e.s.count;
+  auto cut = [&](int64_t c) { return part_start(count, P, c); };
+  e.step();
+  for (int i = 0; i < r; ++i) e.row(2 * i, 2 * i + 1, 0, 0, count, true);
+  std::vector<int64_t> lo(P, 0), hi(P, P);
+  for (int d = P / 2; d >= 1; d /= 2) {
+    e.step();
+    for (int j = 0; j < P; ++j) {
+      const int64_t mid = (lo[j] + hi[j]) / 2;
+      if (j & d) lo[j] = mid; else hi[j] = mid;
+      e.row(core[j ^ d], core[j], cut(lo[j]), cut(lo[j]), cut(hi[j]) - cut(lo[j]), true);
+    }
+  }
+  for (int d = 1; d < P; d *= 2) {
+    e.step();
+    for (int j = 0; j < P; ++j) {
+      const int64_t start = (j ^ d) & ~(d - 1);
+      e.row(core[j ^ d], core[j], cut(start), cut(start), cut(start + d) - cut(start), false);
+    }
+  }
+  e.step();
+  for (int i = 0; i < r; ++i) e.row(2 * i + 1, 2 * i, 0, 0, count, false);
+}
+
 // ---- Double Binary Tree (eq:model-algo-dbt-ar)
 struct Tree {
   int root = 0;
@@ -408,12 +446,16 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     return COLL_ERR_INVALID_ARG;
   }
   const coll_algo_t algo = resolve_algo(kind, algo_in);
+  if (algo == COLL_ALGO_AUTO) {
+    err = "COLL_ALGO_AUTO is resolved before a schedule is built";
+    return COLL_ERR_INVALID_ARG;
+  }
   if (int(algo) < 1 || int(algo) > int(COLL_ALGO_SCATTER_ALLGATHER) || !algo_valid(kind, algo)) {
     err = "algorithm not defined for this collective";
     return COLL_ERR_UNSUPPORTED;
   }
-  if ((algo == COLL_ALGO_RHD || algo == COLL_ALGO_DBT) && !pow2(N)) {
-    err = "recursive halving-doubling and the double binary tree need a power-of-two N";
+  if (algo == COLL_ALGO_RHD && kind != COLL_K_ALLREDUCE && !pow2(N)) {
+    err = "recursive halving-doubling ReduceScatter / AllGather need a power-of-two N";
     return COLL_ERR_UNSUPPORTED;
   }
   const bool rooted =
@@ -447,7 +489,10 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
   switch (kind) {
     case COLL_K_ALLREDUCE:
       if (algo == COLL_ALGO_RING) { ring_reduce_scatter(e); ring_all_gather(e); }
-      else if (algo == COLL_ALGO_RHD) { rhd_reduce_scatter(e); rhd_all_gather(e); }
+      else if (algo == COLL_ALGO_RHD) {
+        if (pow2(N)) { rhd_reduce_scatter(e); rhd_all_gather(e); }
+        else rhd_all_reduce_folded(e);
+      }
       else dbt_all_reduce(e);
       break;
     case COLL_K_REDUCESCATTER:
@@ -478,6 +523,47 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
       break;
   }
   return COLL_OK;
+}
+
+coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size, int root, const CostModel& m,
+                          coll_algo_t& out, std::string& err) {
+  std::vector<coll_algo_t> cand;
+  switch (kind) {
+    case COLL_K_ALLREDUCE: cand = {COLL_ALGO_DBT, COLL_ALGO_RHD, COLL_ALGO_RING}; break;
+    case COLL_K_REDUCESCATTER:
+    case COLL_K_ALLGATHER:
+      if (pow2(N)) cand.push_back(COLL_ALGO_RHD);
+      cand.push_back(COLL_ALGO_RING);
+      break;
+    case COLL_K_BROADCAST: cand = {COLL_ALGO_BINOMIAL, COLL_ALGO_CHAIN_PIPE, COLL_ALGO_SCATTER_ALLGATHER}; break;
+    case COLL_K_SCATTER: cand = {COLL_ALGO_BINOMIAL, COLL_ALGO_LINEAR}; break;
+    case COLL_K_GATHER:
+    case COLL_K_REDUCE: cand = {COLL_ALGO_BINOMIAL}; break;
+    case COLL_K_ALLTOALL: cand = {COLL_ALGO_PAIRWISE, COLL_ALGO_BRUCK}; break;
+    default:
+      err = "unknown collective";
+      return COLL_ERR_INVALID_ARG;
+  }
+  double best = 0;
+  bool have = false;
+  for (coll_algo_t a : cand) {
+    Schedule s;
+    std::string e2;
+    const coll_status_t st = build_schedule(kind, a, N, count, root, 1, s, e2);
+    if (st != COLL_OK) {
+      err = e2;
+      if (!have && a == cand.back()) return st;
+      continue;
+    }
+    const coll_counts_t c = count_schedule(s, elem_size);
+    const double t = double(c.steps) * m.alpha_s + double(c.hbm_bytes) / m.beta_Bps;
+    if (!have || t < best) {
+      best = t;
+      out = a;
+      have = true;
+    }
+  }
+  return have ? COLL_OK : COLL_ERR_UNSUPPORTED;
 }
 
 coll_counts_t count_schedule(const Schedule& s, int elem_size) {

@@ -37,8 +37,21 @@ struct Schedule {
 // The algorithm a COLL_ALGO_DEFAULT request stands for.
 coll_algo_t resolve_algo(coll_kind_t kind, coll_algo_t algo);
 
+// alpha-beta constants for COLL_ALGO_AUTO: seconds per step, schedule bytes per second.
+struct CostModel {
+  double alpha_s = 1.18e-6;
+  double beta_Bps = 7.0e12;
+};
+
+// COLL_ALGO_AUTO: among the collective's candidate algorithms valid for N, the
+// one whose schedule minimises steps * alpha + schedule bytes / beta (first
+// candidate on ties).  Returns COLL_OK and the algorithm, or an error.
+coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size, int root, const CostModel& m,
+                          coll_algo_t& out, std::string& err);
+
 // Validates (kind, algo, N, count, root, chunks) and builds the in-place
 // schedule.  Returns COLL_OK or an error status with a message in `err`.
+// COLL_ALGO_AUTO must be resolved with choose_algo first.
 coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo, int N, int64_t count, int root,
                              int chunks, Schedule& out, std::string& err);
 

@@ -74,15 +74,23 @@ typedef enum { COLL_SUM = 0, COLL_MAX = 1, COLL_MIN = 2 } coll_op_t;
 typedef enum {
   COLL_ALGO_DEFAULT = 0,       /* ring / binomial / pairwise for the collective */
   COLL_ALGO_RING = 1,          /* [P3] Ring AllReduce, Ring AllGather / ReduceScatter          */
-  COLL_ALGO_RHD = 2,           /* [P3] Recursive Halving-Doubling; N must be a power of 2      */
-  COLL_ALGO_DBT = 3,           /* [P3] Double Binary Tree; N must be a power of 2              */
+  COLL_ALGO_RHD = 2,           /* [P3] Recursive Halving-Doubling; ReduceScatter / AllGather need
+                                  N = 2^n; AllReduce folds the surplus ranks of any N first     */
+  COLL_ALGO_DBT = 3,           /* [P3] Double Binary Tree (any N)                              */
   COLL_ALGO_BINOMIAL = 4,      /* [P1] binomial-tree Broadcast / Scatter / Gather              */
   COLL_ALGO_CHAIN_PIPE = 5,    /* [P1] chunked chain pipeline Broadcast (k = 1: chain)         */
   COLL_ALGO_BINOMIAL_PIPE = 6, /* [P1] chunked binomial-tree pipeline Broadcast (k = 1: tree)  */
   COLL_ALGO_PAIRWISE = 7,      /* [P3] Pairwise AllToAll, N-1 rounds                           */
   COLL_ALGO_BRUCK = 8,         /* [P3] Bruck AllToAll, ceil(log2 N) rounds plus rotations      */
   COLL_ALGO_LINEAR = 9,        /* [P1] naive Scatter: the root sends each chunk directly      */
-  COLL_ALGO_SCATTER_ALLGATHER = 10 /* [P1] Broadcast as binomial Scatter + Ring AllGather     */
+  COLL_ALGO_SCATTER_ALLGATHER = 10, /* [P1] Broadcast as binomial Scatter + Ring AllGather    */
+  COLL_ALGO_AUTO = 11          /* the candidate with the least predicted time, t = steps * alpha
+                                  + schedule bytes / beta ([P3]'s alpha-beta model with this
+                                  device's fitted constants, COLL_OPT_MODEL_*); ties go to the
+                                  first of: AllReduce DBT, RHD, Ring; ReduceScatter / AllGather
+                                  RHD, Ring; Broadcast binomial, chain, Scatter+AllGather;
+                                  Scatter binomial, linear; AllToAll Pairwise, Bruck.
+                                  `chunks` is ignored (one GPU moves the same bytes for any k). */
 } coll_algo_t;
 
 typedef enum {
@@ -205,13 +213,18 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          256 MiB memory-side cache, else source loads only.
  * COLL_OPT_REVERSE         1: odd steps walk their columns backwards, so data
  *                          written last is read first [1]; 0: always forwards.
- * Every setting gives bit-identical results; they only change the speed. */
+ * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1180].
+ * COLL_OPT_MODEL_BETA_GBPS schedule-byte rate used by COLL_ALGO_AUTO, in GB/s [7000].
+ * Every setting other than the model constants gives bit-identical results;
+ * they only change the speed. */
 typedef enum {
   COLL_OPT_EXEC = 0,
   COLL_OPT_GROUP_TILES = 1,
   COLL_OPT_MAX_GRID = 2,
   COLL_OPT_NONTEMPORAL = 3,
-  COLL_OPT_REVERSE = 4
+  COLL_OPT_REVERSE = 4,
+  COLL_OPT_MODEL_ALPHA_NS = 5,
+  COLL_OPT_MODEL_BETA_GBPS = 6
 } coll_option_t;
 coll_status_t coll_set_option(coll_option_t key, int64_t value);
 

@@ -51,8 +51,10 @@ INV, UNS, OK = _lib.COLL_ERR_INVALID_ARG, _lib.COLL_ERR_UNSUPPORTED, _lib.COLL_O
     (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=0, count=16), INV),
     (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=4, count=16, op="sum", dtype="int32",
           algo="rhd"), OK),
-    (dict(name="coll_allreduce", send=bufs(6, 16), recv=None, N=6, count=0, algo="rhd"), UNS),
-    (dict(name="coll_allreduce", send=bufs(12, 16), recv=None, N=12, count=0, algo="dbt"), UNS),
+    (dict(name="coll_reducescatter", send=bufs(6, 16), recv=None, N=6, count=0, algo="rhd"), UNS),
+    (dict(name="coll_allgather", send=bufs(12, 16), recv=None, N=12, count=0, algo="rhd"), UNS),
+    (dict(name="coll_allreduce", send=bufs(6, 16), recv=None, N=6, count=0, algo="rhd"), OK),
+    (dict(name="coll_allreduce", send=bufs(12, 16), recv=None, N=12, count=0, algo="dbt"), OK),
     (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=4, count=0, algo="pairwise"), UNS),
     (dict(name="coll_broadcast", send=bufs(4, 16), recv=None, N=4, count=0, algo="binomial", root=4), INV),
     (dict(name="coll_scatter", send=bufs(4, 16), recv=None, N=4, count=0, algo="binomial", root=-1), INV),

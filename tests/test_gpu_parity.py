@@ -11,7 +11,9 @@ import pytest
 
 import seeded_inputs as si
 from oracle import numerics
-from tests.gpu_util import assert_parity
+from oracle.schedules import make_plan
+from oracle.simulate import defined_regions, run_plan
+from tests.gpu_util import assert_parity, gpu_run
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +101,7 @@ EDGE_NS = [1, 2, 3, 5, 7, 8]
 
 def _algos(kind, N):
     pow2 = (N & (N - 1)) == 0
-    return {"allreduce": ["ring"] + (["rhd", "dbt"] if pow2 else []),
+    return {"allreduce": ["ring", "rhd", "dbt"],
             "reducescatter": ["ring"] + (["rhd"] if pow2 else []),
             "allgather": ["ring"] + (["rhd"] if pow2 else []),
             "broadcast": ["binomial", "chain_pipe", "binomial_pipe", "scatter_allgather"],
@@ -267,3 +269,42 @@ def test_repeated_calls_reuse_cached_schedules():
     assert np.array_equal(got, ((s + (1 << 31)) % (1 << 32)) - (1 << 31))
     st = coll.coll_get_stats()
     assert st["steps"] == 14 and st["hbm_bytes"] == 35 * count * 4
+
+
+@pytest.mark.parametrize("N", [3, 5, 6, 7, 12, 13])
+def test_non_power_of_two_rhd_dbt(N):
+    """Halving-doubling with the surplus folded into a power-of-two core, and
+    the double binary tree for any N: bit-exact for int32, fp32 and bf16."""
+    for dtype, sigma in (("int32", 1.0), ("float32", 1.0), ("bfloat16", 0.02)):
+        a = si.rank_arrays(6, N, 3000 * N + 5, dtype, sigma=sigma)
+        for algo in ("rhd", "dbt"):
+            assert_parity("allreduce", algo, a, dtype, checksums=True)
+            assert_parity("allreduce", algo, a, dtype, inplace=False)
+
+
+def test_auto_algorithm_matches_the_oracle():
+    """COLL_ALGO_AUTO runs the algorithm coll_plan reports for it; the result is
+    the oracle's for that algorithm."""
+    import collective_communication_algorithms_amd as coll
+    for kind, N, count, dtype in (("allreduce", 8, 8 * 5000, "float32"), ("allreduce", 6, 6 * 777, "int32"),
+                                  ("reducescatter", 8, 8 * 999, "bfloat16"), ("broadcast", 8, 1 << 16, "uint8"),
+                                  ("scatter", 8, 1 << 22, "uint8"), ("alltoall", 32, 32 * 64, "bfloat16"),
+                                  ("alltoall", 16, 16 * 8192, "int32")):
+        rows, _ = coll.coll_plan(kind, "auto", N, count, dtype)
+        chosen = None
+        for algo in ("dbt", "rhd", "ring", "binomial", "chain_pipe", "scatter_allgather", "linear",
+                     "pairwise", "bruck"):
+            try:
+                if coll.coll_plan(kind, algo, N, count, dtype)[0] == rows:
+                    chosen = algo
+                    break
+            except coll.CollError:
+                pass
+        assert chosen is not None
+        a = si.rank_arrays(9, N, count, dtype)
+        got, _ = gpu_run(kind, "auto", a, dtype)
+        plan = make_plan(kind, chosen, N, count)
+        want = run_plan(plan, dtype, "sum", a)
+        for i, regs in enumerate(defined_regions(kind, N, count, 0)):
+            for lo, hi in regs:
+                assert np.array_equal(got[i][lo:hi].view(np.uint8), want[i][lo:hi].view(np.uint8)), (kind, chosen)

@@ -56,7 +56,7 @@ NS = list(range(1, 13)) + [16, 31, 32, 64]
 def test_reduction_schedules_match(N):
     pow2 = (N & (N - 1)) == 0
     for count in sorted({0, 1, N - 1, N, 3 * N + 1, 1000}):
-        for kind, algos in (("allreduce", ["ring"] + (["rhd", "dbt"] if pow2 else [])),
+        for kind, algos in (("allreduce", ["ring", "rhd", "dbt"]),
                             ("reducescatter", ["ring"] + (["rhd"] if pow2 else [])),
                             ("allgather", ["ring"] + (["rhd"] if pow2 else []))):
             for algo in algos:
@@ -100,8 +100,8 @@ def test_config_scale_plans_match():
 
 
 @pytest.mark.parametrize("kind,algo,N,count,root,k,why", [
-    ("allreduce", "rhd", 6, 60, 0, 1, "unsupported"),
-    ("allreduce", "dbt", 12, 60, 0, 1, "unsupported"),
+    ("reducescatter", "rhd", 6, 60, 0, 1, "unsupported"),
+    ("allgather", "rhd", 12, 60, 0, 1, "unsupported"),
     ("allreduce", "binomial", 4, 60, 0, 1, "unsupported"),
     ("broadcast", "ring", 4, 60, 0, 1, "unsupported"),
     ("alltoall", "pairwise", 4, 61, 0, 1, "invalid"),
@@ -145,3 +145,57 @@ def test_reduce_linear_scatter_scatter_allgather_match(N):
             compare("reduce", "binomial", N, count, root, dtype="float32")
             compare("scatter", "linear", N, count, root, dtype="uint8")
             compare("broadcast", "scatter_allgather", N, count, root, dtype="uint8")
+
+
+CANDIDATES = {"allreduce": ["dbt", "rhd", "ring"], "reducescatter": ["rhd", "ring"], "allgather": ["rhd", "ring"],
+              "broadcast": ["binomial", "chain_pipe", "scatter_allgather"], "scatter": ["binomial", "linear"],
+              "gather": ["binomial"], "reduce": ["binomial"], "alltoall": ["pairwise", "bruck"]}
+
+
+def expected_auto(kind, N, count, dtype, alpha, beta):
+    best = None
+    for algo in CANDIDATES[kind]:
+        try:
+            _, c = coll_plan(kind, algo, N, count, dtype, 0, 1)
+        except CollError:
+            continue
+        t = c["steps"] * alpha + c["hbm_bytes"] / beta
+        if best is None or t < best[0]:
+            best = (t, algo)
+    return best[1]
+
+
+@pytest.mark.parametrize("kind", list(CANDIDATES))
+@pytest.mark.parametrize("N", [1, 2, 5, 8, 32])
+def test_auto_picks_the_least_predicted_time(kind, N):
+    """COLL_ALGO_AUTO = argmin over the candidates of steps * alpha + bytes / beta,
+    computed here from coll_plan's own counts (first candidate on ties)."""
+    from collective_communication_algorithms_amd import coll_set_option
+    try:
+        for alpha_ns, beta_gbps in ((1180, 7000), (10 ** 8, 7000), (0, 1)):
+            coll_set_option("model_alpha_ns", alpha_ns)
+            coll_set_option("model_beta_gbps", beta_gbps)
+            for count in (N, 64 * N, (1 << 20) * N):
+                dtype = "bfloat16"
+                if kind == "alltoall" and count % N:
+                    continue
+                want = expected_auto(kind, N, count, dtype, alpha_ns * 1e-9, beta_gbps * 1e9)
+                got = coll_plan(kind, "auto", N, count, dtype, 0, 1)
+                assert got == coll_plan(kind, want, N, count, dtype, 0, 1), (kind, N, count, alpha_ns, want)
+    finally:
+        coll_set_option("model_alpha_ns", 1180)
+        coll_set_option("model_beta_gbps", 7000)
+
+
+def test_auto_extremes():
+    """A huge alpha makes the fewest steps win; a tiny beta the fewest bytes."""
+    from collective_communication_algorithms_amd import coll_set_option
+    try:
+        coll_set_option("model_alpha_ns", 10 ** 8)
+        assert coll_plan("alltoall", "auto", 32, 32 * 4096, "bfloat16") == coll_plan("alltoall", "bruck", 32, 32 * 4096, "bfloat16")
+        coll_set_option("model_alpha_ns", 0)
+        assert coll_plan("alltoall", "auto", 32, 32 * 4096, "bfloat16") == coll_plan("alltoall", "pairwise", 32, 32 * 4096, "bfloat16")
+        assert coll_plan("scatter", "auto", 8, 8 << 20, "uint8") == coll_plan("scatter", "linear", 8, 8 << 20, "uint8")
+    finally:
+        coll_set_option("model_alpha_ns", 1180)
+        coll_set_option("model_beta_gbps", 7000)
