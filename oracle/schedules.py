@@ -37,7 +37,7 @@ from dataclasses import dataclass, field
 KINDS = ("allreduce", "reducescatter", "allgather", "broadcast", "scatter",
          "gather", "alltoall", "reduce")
 ALGOS = ("ring", "rhd", "dbt", "binomial", "chain_pipe", "binomial_pipe",
-         "pairwise", "bruck", "linear", "scatter_allgather")
+         "pairwise", "bruck", "linear", "scatter_allgather", "bidir_ring")
 
 
 @dataclass(frozen=True)
@@ -349,6 +349,24 @@ def _bcast_chain_pipe(b: _Builder, N, count, root, k):
                 b.row(st, (root + h) % N, (root + h + 1) % N, lo, hi - lo)
 
 
+def _bcast_bidir_ring(b: _Builder, N, count, root, k):
+    """Bidirectional ring ("一对多通信：Broadcast 与 Scatter", SCCL 的 Broadcast 实现):
+    the root sends both ways round the ring at once; the clockwise chain covers
+    relative ranks 1..ceil((N-1)/2), the counter-clockwise chain N-1 down to
+    ceil((N-1)/2)+1.  With k chunks, chunk c crosses hop h of each chain at step
+    c+h: ceil((N-1)/2)+k-1 steps."""
+    cw, ccw = N // 2, (N - 1) // 2
+    for t in range(cw + k - 1 if N > 1 else 0):
+        st = b.new_step()
+        for c in range(k):
+            h = t - c
+            lo, hi = part(count, k, c), part(count, k, c + 1)
+            if 0 <= h < cw:
+                b.row(st, (root + h) % N, (root + h + 1) % N, lo, hi - lo)
+            if 0 <= h < ccw:
+                b.row(st, (root - h) % N, (root - h - 1) % N, lo, hi - lo)
+
+
 def _bcast_binomial_pipe(b: _Builder, N, count, root, k):
     """Binomial tree, k chunks; chunk c takes binomial sub-step j+1 at step c+j;
     ceil(log2 N)+k-1 steps (eq:pipe-tree-bcast).  k = 1 is the binomial tree."""
@@ -473,7 +491,7 @@ VALID = {
     "alltoall": ("pairwise", "bruck"),
     "reduce": ("binomial",),
 }
-VALID["broadcast"] = VALID["broadcast"] + ("scatter_allgather",)
+VALID["broadcast"] = VALID["broadcast"] + ("scatter_allgather", "bidir_ring")
 VALID["scatter"] = VALID["scatter"] + ("linear",)
 
 
@@ -489,9 +507,10 @@ def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
         raise ValueError("recursive halving-doubling ReduceScatter / AllGather need N = 2^n")
     if kind == "alltoall" and count % N:
         raise ValueError("alltoall needs count divisible by N")
-    if algo in ("chain_pipe", "binomial_pipe") and not (1 <= chunks <= max(count, 1)):
+    pipelined = algo in ("chain_pipe", "binomial_pipe", "bidir_ring")
+    if pipelined and not (1 <= chunks <= max(count, 1)):
         raise ValueError("chunks")
-    p = Plan(kind, algo, N, count, root, chunks if algo.endswith("_pipe") else 1)
+    p = Plan(kind, algo, N, count, root, chunks if pipelined else 1)
     b = _Builder(p)
     if kind == "allreduce":
         if algo == "ring":
@@ -517,6 +536,8 @@ def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
             _bcast_chain_pipe(b, N, count, root, chunks)
         elif algo == "binomial_pipe":
             _bcast_binomial_pipe(b, N, count, root, chunks)
+        elif algo == "bidir_ring":
+            _bcast_bidir_ring(b, N, count, root, chunks)
         else:
             # "一对多通信：Broadcast 与 Scatter", Broadcast 与 Scatter 的关系: Scatter
             # then AllGather; the chunks stay at their offsets, so after the

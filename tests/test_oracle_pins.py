@@ -353,3 +353,43 @@ def test_folded_rhd_and_general_dbt_counts(N):
         def height(u):
             return 0 if not t[u] else 1 + max(height(c) for c in t[u])
         assert height(root) == ceil_log2(N)
+
+
+# --- bidirectional-ring Broadcast ---------------------------------------------------
+
+def test_bidir_ring_broadcast_matches_printed_4_chip_example():
+    g = golden("bidir_ring_bcast_n4.json")
+    p = make_plan("broadcast", "bidir_ring", g["nranks"], 4096, g["root"], 1)
+    assert p.nsteps == len(g["steps"]) == ceil_log2(g["nranks"])
+    for rows, want in zip(p.steps, g["steps"]):
+        assert edges(rows) == sorted(tuple(e) for e in want)
+        assert all(r.n == 4096 for r in rows)
+
+
+@pytest.mark.parametrize("N", NS)
+@pytest.mark.parametrize("k", [1, 2, 5])
+def test_bidir_ring_broadcast_counts_and_neighbour_edges(N, k):
+    """Both directions of the ring carry the message at once, so the farther half
+    is ceil((N-1)/2) hops away: ceil((N-1)/2) + k - 1 steps of M/k bytes with k
+    chunks; every edge joins ring neighbours; every rank but the root receives
+    every chunk exactly once, from a rank that already holds it."""
+    sz, count = 4, 64 * k * max(N, 1)
+    M = count * sz
+    for root in {0, N - 1}:
+        p = make_plan("broadcast", "bidir_ring", N, count, root, k)
+        H = (N - 1 + 1) // 2
+        assert p.nsteps == (H + k - 1 if N > 1 else 0)
+        assert counts(p, sz)["crit_bytes"] == p.nsteps * M // k
+        holds = {(root, c) for c in range(k)}
+        got = {}
+        for rows in p.steps:
+            new = set()
+            for r in rows:
+                assert (r.dst - r.src) % N in (1, N - 1)
+                c = r.src_off * k // count
+                assert (r.src, c) in holds and r.src_off == r.dst_off and r.n == count // k
+                got[(r.dst, c)] = got.get((r.dst, c), 0) + 1
+                new.add((r.dst, c))
+            holds |= new
+        assert got == {(d, c): 1 for d in range(N) if d != root for c in range(k)}
+        check_hazards(p)

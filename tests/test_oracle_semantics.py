@@ -81,7 +81,7 @@ def test_broadcast_scatter_gather_uint8(N):
         a = [g.integers(0, 256, count, dtype=np.uint8) for _ in range(N)]
         for root in sorted({0, N // 2, N - 1}):
             for algo, ks in (("binomial", [1]), ("chain_pipe", [1, 2, 7]),
-                             ("binomial_pipe", [1, 3, 8])):
+                             ("binomial_pipe", [1, 3, 8]), ("bidir_ring", [1, 2, 7])):
                 for k in ks:
                     if k > max(count, 1):
                         continue
@@ -485,3 +485,17 @@ def test_planted_non_power_of_two_mistakes_are_caught(N):
                             for o in run_plan(m, "float32", "sum", f))
             caught += not ok
         assert caught == len(muts), (algo, N)
+
+
+@pytest.mark.parametrize("N,k", [(4, 1), (7, 3), (8, 2)])
+def test_planted_bidir_ring_broadcast_mistakes_are_caught(N, k):
+    """A dropped, misrouted, shifted or reducing row of the bidirectional-ring
+    Broadcast leaves some rank with something other than the root's bytes."""
+    count = N * k * 5
+    a = rng_ints(N, count, 7)
+    plan = make_plan("broadcast", "bidir_ring", N, count, 1, k)
+    muts = _mutants(plan)
+    assert muts
+    for m in muts:
+        out = run_plan(m, "int32", "sum", a)
+        assert not all(np.array_equal(o, a[1]) for o in out)
