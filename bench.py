@@ -200,7 +200,7 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
                     torch.stack(si.device_rank_tensors(2, 8, M, "uint8", dev)))
         live = pristine.clone()
         cases = [("broadcast", "binomial", 1)]
-        for algo in ("chain_pipe", "binomial_pipe"):
+        for algo in ("chain_pipe", "binomial_pipe", "bidir_ring"):
             kstar = model.best_chunks(algo, 8, M, 5e-6, 450e9)
             cases += [("broadcast", algo, k) for k in sorted({1, 8, 64, kstar}) if k <= M]
         cases += [("broadcast", "scatter_allgather", 1), ("scatter", "binomial", 1), ("scatter", "linear", 1),

@@ -18,7 +18,8 @@ STATUS_NAMES = {0: "COLL_OK", 1: "COLL_ERR_INVALID_ARG", 2: "COLL_ERR_UNSUPPORTE
 DTYPES = {"int32": 0, "uint8": 1, "float32": 2, "bfloat16": 3}
 OPS = {"sum": 0, "max": 1, "min": 2}
 ALGOS = {"default": 0, "ring": 1, "rhd": 2, "dbt": 3, "binomial": 4, "chain_pipe": 5, "binomial_pipe": 6,
-         "pairwise": 7, "bruck": 8, "linear": 9, "scatter_allgather": 10, "auto": 11}
+         "pairwise": 7, "bruck": 8, "linear": 9, "scatter_allgather": 10, "auto": 11,
+         "bidir_ring": 12}
 KINDS = {"allreduce": 0, "reducescatter": 1, "allgather": 2, "broadcast": 3, "scatter": 4, "gather": 5,
          "alltoall": 6, "reduce": 7}
 OPTIONS = {"exec": 0, "group_tiles": 1, "max_grid": 2, "nontemporal": 3, "reverse": 4, "model_alpha_ns": 5,

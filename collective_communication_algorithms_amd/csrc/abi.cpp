@@ -339,7 +339,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     std::string err;
     st = build_schedule(kind, automatic ? COLL_ALGO_DEFAULT : algo, N, 0, root, 1, probe, err);
     if (st != COLL_OK) return fail(st, err);
-    if ((algo == COLL_ALGO_CHAIN_PIPE || algo == COLL_ALGO_BINOMIAL_PIPE) && count > 0 &&
+    if (algo_pipelined(algo) && count > 0 &&
         (chunks < 1 || int64_t(chunks) > count))
       return fail(COLL_ERR_INVALID_ARG, "chunks must be in [1, count]");
     if (kind == COLL_K_ALLTOALL && count % N) return fail(COLL_ERR_INVALID_ARG, "alltoall needs count divisible by nranks");
@@ -364,7 +364,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   const coll_algo_t ra = resolve_algo(kind, chosen);
   const bool rooted =
       kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER || kind == COLL_K_REDUCE;
-  const bool pipe = ra == COLL_ALGO_CHAIN_PIPE || ra == COLL_ALGO_BINOMIAL_PIPE;
+  const bool pipe = algo_pipelined(ra);
   Key k{dev, int(kind), int(ra), N, count, sz, rooted ? root : 0, pipe ? chunks : 1, inplace ? 1 : 0};
   Entry* e = nullptr;
   st = get_entry(k, e);

@@ -302,6 +302,25 @@ void bcast_binomial_pipe(Emitter& e) {
   }
 }
 
+// "一对多通信：Broadcast 与 Scatter", SCCL 的 Broadcast 实现: the root feeds both
+// directions of a bidirectional ring at once.  The clockwise chain reaches
+// relative ranks 1..floor(N/2), the counter-clockwise one N-1 down to
+// floor(N/2)+1; chunk c crosses hop h of either chain at step c+h.
+void bcast_bidir_ring(Emitter& e) {
+  const int N = e.s.N, k = e.s.chunks, root = e.s.root;
+  if (N < 2) return;
+  const int cw = N / 2, ccw = (N - 1) / 2;
+  for (int t = 0; t < cw + k - 1; ++t) {
+    e.step();
+    for (int c = std::max(0, t - (cw - 1)); c <= std::min(t, k - 1); ++c) {
+      const int h = t - c;
+      const int64_t lo = part_start(e.s.count, k, c), hi = part_start(e.s.count, k, c + 1);
+      e.row(abs_rank(root, h, N), abs_rank(root, h + 1, N), lo, lo, hi - lo, false);
+      if (h < ccw) e.row(abs_rank(root, N - h, N), abs_rank(root, N - h - 1, N), lo, lo, hi - lo, false);
+    }
+  }
+}
+
 // Relative chunks [a, b) between relative ranks, split where the absolute
 // chunk index wraps past N-1.
 void relative_chunks(Emitter& e, int v_src, int v_dst, int a, int b) {
@@ -395,7 +414,7 @@ bool algo_valid(coll_kind_t kind, coll_algo_t a) {
     case COLL_K_ALLGATHER: return a == COLL_ALGO_RING || a == COLL_ALGO_RHD;
     case COLL_K_BROADCAST:
       return a == COLL_ALGO_BINOMIAL || a == COLL_ALGO_CHAIN_PIPE || a == COLL_ALGO_BINOMIAL_PIPE ||
-             a == COLL_ALGO_SCATTER_ALLGATHER;
+             a == COLL_ALGO_SCATTER_ALLGATHER || a == COLL_ALGO_BIDIR_RING;
     case COLL_K_SCATTER: return a == COLL_ALGO_BINOMIAL || a == COLL_ALGO_LINEAR;
     case COLL_K_GATHER:
     case COLL_K_REDUCE: return a == COLL_ALGO_BINOMIAL;
@@ -450,7 +469,7 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     err = "COLL_ALGO_AUTO is resolved before a schedule is built";
     return COLL_ERR_INVALID_ARG;
   }
-  if (int(algo) < 1 || int(algo) > int(COLL_ALGO_SCATTER_ALLGATHER) || !algo_valid(kind, algo)) {
+  if (int(algo) < 1 || int(algo) > int(COLL_ALGO_BIDIR_RING) || !algo_valid(kind, algo)) {
     err = "algorithm not defined for this collective";
     return COLL_ERR_UNSUPPORTED;
   }
@@ -464,7 +483,7 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     err = "root outside [0, nranks)";
     return COLL_ERR_INVALID_ARG;
   }
-  const bool pipe = algo == COLL_ALGO_CHAIN_PIPE || algo == COLL_ALGO_BINOMIAL_PIPE;
+  const bool pipe = algo_pipelined(algo);
   if (pipe && count > 0 && (chunks < 1 || int64_t(chunks) > count)) {
     err = "chunks must be in [1, count]";
     return COLL_ERR_INVALID_ARG;
@@ -505,6 +524,7 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
       if (algo == COLL_ALGO_BINOMIAL) bcast_binomial(e);
       else if (algo == COLL_ALGO_CHAIN_PIPE) bcast_chain_pipe(e);
       else if (algo == COLL_ALGO_BINOMIAL_PIPE) bcast_binomial_pipe(e);
+      else if (algo == COLL_ALGO_BIDIR_RING) bcast_bidir_ring(e);
       else {
         // "一对多通信：Broadcast 与 Scatter", Broadcast 与 Scatter 的关系: chunks stay
         // at their offsets, so after the Scatter rank i holds chunk i, which
@@ -535,7 +555,9 @@ coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size,
       if (pow2(N)) cand.push_back(COLL_ALGO_RHD);
       cand.push_back(COLL_ALGO_RING);
       break;
-    case COLL_K_BROADCAST: cand = {COLL_ALGO_BINOMIAL, COLL_ALGO_CHAIN_PIPE, COLL_ALGO_SCATTER_ALLGATHER}; break;
+    case COLL_K_BROADCAST:
+      cand = {COLL_ALGO_BINOMIAL, COLL_ALGO_CHAIN_PIPE, COLL_ALGO_SCATTER_ALLGATHER, COLL_ALGO_BIDIR_RING};
+      break;
     case COLL_K_SCATTER: cand = {COLL_ALGO_BINOMIAL, COLL_ALGO_LINEAR}; break;
     case COLL_K_GATHER:
     case COLL_K_REDUCE: cand = {COLL_ALGO_BINOMIAL}; break;

@@ -37,6 +37,11 @@ struct Schedule {
 // The algorithm a COLL_ALGO_DEFAULT request stands for.
 coll_algo_t resolve_algo(coll_kind_t kind, coll_algo_t algo);
 
+// Algorithms that take the `chunks` pipeline count.
+inline bool algo_pipelined(coll_algo_t a) {
+  return a == COLL_ALGO_CHAIN_PIPE || a == COLL_ALGO_BINOMIAL_PIPE || a == COLL_ALGO_BIDIR_RING;
+}
+
 // alpha-beta constants for COLL_ALGO_AUTO: seconds per step, schedule bytes per second.
 struct CostModel {
   double alpha_s = 1.18e-6;

@@ -21,7 +21,8 @@ def time(kind: str, algo: str, N: int, M: float, alpha: float, beta: float, k: i
     Doubling (eq:model-algo-rhd-*), Double Binary Tree (eq:model-algo-dbt-ar),
     Pairwise / Bruck AllToAll (eq:model-algo-a2a-pairwise / -bruck), Broadcast
     ("一对多通信：Broadcast 与 Scatter", eq:chain-bcast, eq:binomial-bcast,
-    eq:pipe-chain-bcast, eq:pipe-tree-bcast), binomial Scatter / Gather
+    eq:pipe-chain-bcast, eq:pipe-tree-bcast, and the bidirectional ring of
+    "SCCL 的 Broadcast 实现"), binomial Scatter / Gather
     (eq:binomial-scatter, eq:onetoall-gather-scatter-duality).
     """
     L = _L(N)
@@ -47,6 +48,10 @@ def time(kind: str, algo: str, N: int, M: float, alpha: float, beta: float, k: i
             return (N + k - 2) * (alpha + M / (k * beta))
         if algo == "binomial_pipe":
             return (L + k - 1) * (alpha + M / (k * beta))
+        if algo == "bidir_ring":
+            # both ring directions from the root (SCCL's 4-chip scheme): the
+            # chain is ceil((N-1)/2) hops long, pipelined in k chunks
+            return (N // 2 + k - 1) * (alpha + M / (k * beta)) if N > 1 else 0.0
     if kind in ("scatter", "gather") and algo == "binomial":
         return L * alpha + frac * M / beta
     if kind == "scatter" and algo == "linear":

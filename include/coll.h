@@ -29,8 +29,9 @@
  *   chunk c of a rank buffer = elements [c*count/N, (c+1)*count/N) (floor).
  *   op     ignored by collectives that do not reduce.
  *   root   used by broadcast / scatter / gather / reduce only; 0 <= root < N.
- *   chunks pipeline chunk count k for COLL_ALGO_CHAIN_PIPE and
- *          COLL_ALGO_BINOMIAL_PIPE (1 <= k <= count); ignored otherwise.
+ *   chunks pipeline chunk count k for COLL_ALGO_CHAIN_PIPE,
+ *          COLL_ALGO_BINOMIAL_PIPE and COLL_ALGO_BIDIR_RING (1 <= k <= count);
+ *          ignored otherwise.
  *   stream a hipStream_t; the work is enqueued on it and the call returns
  *          without waiting (stream-ordered, like hccl_allreduce's stream).
  *
@@ -84,13 +85,16 @@ typedef enum {
   COLL_ALGO_BRUCK = 8,         /* [P3] Bruck AllToAll, ceil(log2 N) rounds plus rotations      */
   COLL_ALGO_LINEAR = 9,        /* [P1] naive Scatter: the root sends each chunk directly      */
   COLL_ALGO_SCATTER_ALLGATHER = 10, /* [P1] Broadcast as binomial Scatter + Ring AllGather    */
-  COLL_ALGO_AUTO = 11          /* the candidate with the least predicted time, t = steps * alpha
+  COLL_ALGO_AUTO = 11,         /* the candidate with the least predicted time, t = steps * alpha
                                   + schedule bytes / beta ([P3]'s alpha-beta model with this
                                   device's fitted constants, COLL_OPT_MODEL_*); ties go to the
                                   first of: AllReduce DBT, RHD, Ring; ReduceScatter / AllGather
-                                  RHD, Ring; Broadcast binomial, chain, Scatter+AllGather;
-                                  Scatter binomial, linear; AllToAll Pairwise, Bruck.
-                                  `chunks` is ignored (one GPU moves the same bytes for any k). */
+                                  RHD, Ring; Broadcast binomial, chain, Scatter+AllGather,
+                                  bidirectional ring; Scatter binomial, linear; AllToAll
+                                  Pairwise, Bruck.  `chunks` is ignored (one GPU moves the
+                                  same bytes for any k). */
+  COLL_ALGO_BIDIR_RING = 12    /* [P1] Broadcast over both directions of a ring at once (SCCL's
+                                  4-chip scheme, any N), pipelined in `chunks` chunks */
 } coll_algo_t;
 
 typedef enum {
@@ -125,7 +129,9 @@ coll_status_t coll_allgather(void* const* sendbufs, void* const* recvbufs, int n
 /* [P1] Broadcast (eq:onetoall-bcast-semantic): every buffer ends equal to the
  * root's.  algo: BINOMIAL (default), CHAIN_PIPE, BINOMIAL_PIPE with `chunks`,
  * SCATTER_ALLGATHER (binomial Scatter, then Ring AllGather; [P1] "Broadcast 与
- * Scatter 的关系"). */
+ * Scatter 的关系"), BIDIR_RING with `chunks` ([P1] "SCCL 的 Broadcast 实现":
+ * the root sends clockwise and counter-clockwise at once; floor(N/2) + k - 1
+ * steps of M/k bytes). */
 coll_status_t coll_broadcast(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                              coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                              void* stream);

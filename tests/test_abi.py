@@ -60,6 +60,7 @@ INV, UNS, OK = _lib.COLL_ERR_INVALID_ARG, _lib.COLL_ERR_UNSUPPORTED, _lib.COLL_O
     (dict(name="coll_scatter", send=bufs(4, 16), recv=None, N=4, count=0, algo="binomial", root=-1), INV),
     (dict(name="coll_broadcast", send=bufs(4, 16), recv=None, N=4, count=16, algo="chain_pipe", chunks=0), INV),
     (dict(name="coll_broadcast", send=bufs(4, 16), recv=None, N=4, count=16, algo="chain_pipe", chunks=17), INV),
+    (dict(name="coll_broadcast", send=bufs(4, 16), recv=None, N=4, count=16, algo="bidir_ring", chunks=17), INV),
     (dict(name="coll_alltoall", send=bufs(4, 16), recv=None, N=4, count=16), INV),
     (dict(name="coll_alltoall", send=bufs(4, 16), recv=bufs(4, 16, base=1 << 40), N=4, count=18), INV),
     (dict(name="coll_allreduce", send=[1 << 32, (1 << 32) + 2], recv=None, N=2, count=4), INV),

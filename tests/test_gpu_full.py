@@ -78,7 +78,8 @@ def test_allreduce_n8_256MiB(algo, dtype, sigma):
 
 @pytest.mark.parametrize("algo,k", [("binomial", 1), ("chain_pipe", 1), ("chain_pipe", 8), ("chain_pipe", 13),
                                     ("chain_pipe", 64), ("binomial_pipe", 1), ("binomial_pipe", 8),
-                                    ("binomial_pipe", 64)])
+                                    ("binomial_pipe", 64), ("bidir_ring", 1), ("bidir_ring", 8),
+                                    ("bidir_ring", 13)])
 def test_broadcast_n8_64MiB(algo, k):
     check_sampled("broadcast", algo, 8, 64 << 20, "uint8", 2, k=k)
 

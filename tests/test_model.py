@@ -77,3 +77,17 @@ def test_reduce_and_scatter_formulas():
         assert model.time("reduce", "binomial", N, M, a, b) == pytest.approx(model.time("broadcast", "binomial", N, M, a, b))
         assert model.time("scatter", "linear", N, M, a, b) == pytest.approx((N - 1) * (a + M / (N * b)))
         assert model.latency_steps("broadcast", "scatter_allgather", N) == (N - 1) + model.latency_steps("scatter", "binomial", N)
+
+
+def test_bidir_ring_broadcast_formula():
+    """The 4-chip bidirectional ring takes 2 iterations, the ceil(log2 N) lower
+    bound ("SCCL 的 Broadcast 实现"); in general the half-ring chain is
+    ceil((N-1)/2) hops, pipelined like eq:pipe-chain-bcast."""
+    a, b, M = 5e-6, 450e9, 1 << 22
+    assert model.latency_steps("broadcast", "bidir_ring", 4) == 2
+    for N in (2, 3, 5, 8, 9):
+        for k in (1, 4):
+            h = (N - 1 + 1) // 2
+            assert model.time("broadcast", "bidir_ring", N, M, a, b, k) == pytest.approx((h + k - 1) * (a + M / (k * b)))
+    # with N - 1 ranks past the root in one direction it would be the chain pipeline
+    assert model.time("broadcast", "bidir_ring", 8, M, a, b, 4) < model.time("broadcast", "chain_pipe", 8, M, a, b, 4)

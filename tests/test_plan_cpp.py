@@ -74,6 +74,7 @@ def test_rooted_schedules_match(N):
                 if k <= count:
                     compare("broadcast", "chain_pipe", N, count, root, k, dtype="uint8")
                     compare("broadcast", "binomial_pipe", N, count, root, k, dtype="uint8")
+                    compare("broadcast", "bidir_ring", N, count, root, k, dtype="uint8")
 
 
 @pytest.mark.parametrize("N", NS)
@@ -97,6 +98,7 @@ def test_config_scale_plans_match():
     for k in (1, 8, 64, 3, 13, 2):
         compare("broadcast", "chain_pipe", 8, 1 << 16, 0, k, dtype="uint8")
         compare("broadcast", "binomial_pipe", 8, 1 << 16, 0, k, dtype="uint8")
+        compare("broadcast", "bidir_ring", 8, 1 << 16, 0, k, dtype="uint8")
 
 
 @pytest.mark.parametrize("kind,algo,N,count,root,k,why", [
@@ -109,6 +111,8 @@ def test_config_scale_plans_match():
     ("scatter", "binomial", 4, 60, -1, 1, "invalid"),
     ("broadcast", "chain_pipe", 4, 60, 0, 0, "invalid"),
     ("broadcast", "chain_pipe", 4, 60, 0, 61, "invalid"),
+    ("broadcast", "bidir_ring", 4, 60, 0, 0, "invalid"),
+    ("scatter", "bidir_ring", 4, 60, 0, 1, "unsupported"),
     ("allreduce", "ring", 0, 60, 0, 1, "invalid"),
     ("allreduce", "ring", 129, 60, 0, 1, "unsupported"),
 ])
@@ -133,6 +137,7 @@ def test_plans_random_shapes():
         if k <= count:
             compare("broadcast", "binomial_pipe", N, count, root, k, dtype="uint8")
             compare("broadcast", "chain_pipe", N, count, root, k, dtype="uint8")
+            compare("broadcast", "bidir_ring", N, count, root, k, dtype="uint8")
         compare("scatter", "binomial", N, count, root, dtype="uint8")
         compare("gather", "binomial", N, count, root, dtype="uint8")
         compare("allreduce", "ring", N, count, dtype="int32")
@@ -148,7 +153,7 @@ def test_reduce_linear_scatter_scatter_allgather_match(N):
 
 
 CANDIDATES = {"allreduce": ["dbt", "rhd", "ring"], "reducescatter": ["rhd", "ring"], "allgather": ["rhd", "ring"],
-              "broadcast": ["binomial", "chain_pipe", "scatter_allgather"], "scatter": ["binomial", "linear"],
+              "broadcast": ["binomial", "chain_pipe", "scatter_allgather", "bidir_ring"], "scatter": ["binomial", "linear"],
               "gather": ["binomial"], "reduce": ["binomial"], "alltoall": ["pairwise", "bruck"]}
 
 
