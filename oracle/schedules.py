@@ -458,6 +458,29 @@ def _a2a_pairwise(b: _Builder, N, count):
             b.row(st, i, j, j * B, B, dst_off=i * B, from_send=True)
 
 
+def _a2a_ring(b: _Builder, N, count):
+    """Ring AllToAll ("集合通信算法延迟公式", Ring: each round only between ring
+    neighbours), read as store-and-forward: in round t = 1..N-1 every rank passes
+    to its successor the N-t blocks that have not yet reached their destination.
+    Storage: first tmp_i[j] = send_i[(i+j) mod N] (block j is t hops from home
+    after t rounds), round t moves slots t..N-1 one rank on, so slot t arrives;
+    last recv_i[(i-j) mod N] = tmp_i[j].  tmp is the receive buffer."""
+    B = count // N
+    st = b.new_step(local=True)
+    for i in range(N):
+        for j in range(N):
+            b.row(st, i, i, ((i + j) % N) * B, B, dst_off=j * B, from_send=True)
+    for t in range(1, N):
+        st = b.new_step(staged=True)
+        for j in range(t, N):
+            for i in range(N):
+                b.row(st, i, (i + 1) % N, j * B, B)
+    st = b.new_step(local=True, staged=True)
+    for i in range(N):
+        for j in range(N):
+            b.row(st, i, i, j * B, B, dst_off=((i - j) % N) * B)
+
+
 def _a2a_bruck(b: _Builder, N, count):
     """Phase 1 (local): tmp_i[j] = send_i[(i+j) mod N].  Round k = 0..L-1: every
     block index j with bit k set moves from rank i to rank i+2^k (all at once).
@@ -493,6 +516,7 @@ VALID = {
 }
 VALID["broadcast"] = VALID["broadcast"] + ("scatter_allgather", "bidir_ring")
 VALID["scatter"] = VALID["scatter"] + ("linear",)
+VALID["alltoall"] = VALID["alltoall"] + ("ring",)
 
 
 def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
@@ -551,7 +575,7 @@ def make_plan(kind: str, algo: str, nranks: int, count: int, root: int = 0,
     elif kind == "gather":
         _gather_binomial(b, N, count, root)
     else:
-        (_a2a_pairwise if algo == "pairwise" else _a2a_bruck)(b, N, count)
+        {"pairwise": _a2a_pairwise, "bruck": _a2a_bruck, "ring": _a2a_ring}[algo](b, N, count)
     return p
 
 

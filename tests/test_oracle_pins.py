@@ -393,3 +393,33 @@ def test_bidir_ring_broadcast_counts_and_neighbour_edges(N, k):
             holds |= new
         assert got == {(d, c): 1 for d in range(N) if d != root for c in range(k)}
         check_hazards(p)
+
+
+
+# --- Ring AllToAll (store-and-forward between neighbours) -----------------------------
+
+@pytest.mark.parametrize("N", NS)
+def test_ring_alltoall_rounds_hops_and_bytes(N):
+    """N-1 rounds, the latency term of eq:model-algo-a2a-ring; every round only
+    between ring neighbours i -> i+1.  Round t forwards the N-t blocks that are
+    still travelling, so the rows carry exactly sum_d d = N(N-1)/2 blocks per
+    rank in total: every block crosses the d links to its destination once and
+    takes no detour.  Per link that is (N-1)M/2 bytes, not the (N-1)M/N the
+    printed formula gives (no neighbour-only schedule can do better)."""
+    sz, B = 4, 24
+    count = N * B
+    M = count * sz
+    p = make_plan("alltoall", "ring", N, count)
+    assert p.nsteps == N - 1
+    rounds = [rows for rows, loc in zip(p.steps, p.local) if not loc]
+    assert len(rounds) == N - 1
+    hops = 0
+    for t, rows in enumerate(rounds, start=1):
+        per_edge = {}
+        for r in rows:
+            assert (r.dst - r.src) % N == 1 % N and r.src_off == r.dst_off
+            per_edge[(r.src, r.dst)] = per_edge.get((r.src, r.dst), 0) + r.n
+            hops += r.n
+        assert per_edge == {(i, (i + 1) % N): (N - t) * B for i in range(N)}
+    assert hops == N * (N * (N - 1) // 2) * B
+    assert counts(p, sz)["crit_bytes"] == (N - 1) * M // 2

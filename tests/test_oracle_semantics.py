@@ -100,7 +100,7 @@ def test_alltoall_is_block_transpose(N):
     B = 3
     count = N * B
     a = rng_ints(N, count, 7 * N)
-    for algo in ("pairwise", "bruck"):
+    for algo in ("pairwise", "bruck", "ring"):
         out = oracle.alltoall(a, "int32", algo)
         for j in range(N):
             for i in range(N):
@@ -499,3 +499,19 @@ def test_planted_bidir_ring_broadcast_mistakes_are_caught(N, k):
     for m in muts:
         out = run_plan(m, "int32", "sum", a)
         assert not all(np.array_equal(o, a[1]) for o in out)
+
+
+@pytest.mark.parametrize("N", [3, 5, 8])
+def test_planted_ring_alltoall_mistakes_are_caught(N):
+    """A dropped, misrouted, shifted or reducing row of the Ring AllToAll breaks
+    the block transpose."""
+    B = 4
+    a = rng_ints(N, N * B, 11)
+    plan = make_plan("alltoall", "ring", N, N * B)
+    muts = _mutants(plan)
+    assert muts
+    for m in muts:
+        out = run_plan(m, "int32", "sum", a, rng_ints(N, N * B, 12))   # receive buffers hold garbage
+        ok = all(np.array_equal(out[j][i * B:(i + 1) * B], a[i][j * B:(j + 1) * B])
+                 for i in range(N) for j in range(N))
+        assert not ok
