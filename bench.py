@@ -256,7 +256,7 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
     pristine = torch.empty((N, N * B), dtype=torch.bfloat16, device=dev)
     si.device_rank_tensors(5, N, N * B, "bfloat16", dev, out=pristine)
     recv = torch.empty_like(pristine)
-    for algo in ("pairwise", "bruck"):
+    for algo in ("pairwise", "bruck", "ring"):
         med, mn = time_call(lambda: coll.coll_alltoall(list(pristine), list(recv), algo=algo), pristine, pristine)
         record("C5", "alltoall", algo, "bfloat16", N, N * B, 1, med, mn)
     del pristine, recv

@@ -427,11 +427,11 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.nontemporal = ntmask;
       a.p = ptrs;
       if (ph.colspace >= (uint64_t(1) << 31))
-        return fail(COLL_ERR_UNSUPPORTED, "Bruck blocks of 2 GiB or more");
+        return fail(COLL_ERR_UNSUPPORTED, "AllToAll blocks of 2 GiB or more");
       int unit = b.perm_unit;
       while (unit > 1 && (align_or % uint64_t(unit))) unit >>= 1;
       a.ncols_units = uint32_t(ph.colspace / uint64_t(unit));
-      // every staged Bruck step permutes groups of N rows; each of the 4 waves
+      // every staged AllToAll step permutes groups of N rows; each of the 4 waves
       // holds ceil(N/4) rows, 2^lg units per lane of each
       const uint32_t ipw = uint32_t(N + 3) / 4;
       const int slots = ipw <= 16 ? 16 : 32;

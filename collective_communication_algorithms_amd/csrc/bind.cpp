@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <iterator>
 #include <map>
+#include <stdexcept>
 
 namespace coll {
 namespace {
@@ -84,13 +85,25 @@ Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
   b.nrows = int64_t(s.rows.size());
   b.counts = count_schedule(s, sz);
   const bool a2a = s.kind == COLL_K_ALLTOALL;
-  const bool bruck = a2a && s.algo == COLL_ALGO_BRUCK;
+  // staged AllToAll steps (Bruck's and the Ring's rounds, the final rotation)
+  // are block permutations: they run in the permutation kernel, which needs
+  // them after every ordinary step
+  auto perm = [&](size_t si) { return a2a && si < s.steps.size() && s.steps[si].staged; };
+  size_t first_perm = s.steps.size();
+  for (size_t si = 0; si < s.steps.size(); ++si)
+    if (perm(si)) {
+      first_perm = si;
+      break;
+    }
+  const bool has_perm = first_perm < s.steps.size();
+  for (size_t si = first_perm; si < s.steps.size(); ++si)
+    if (!perm(si)) throw std::logic_error("ordinary AllToAll step after a staged one");
   std::vector<std::vector<DevItem>> per_step(s.steps.size());
   std::vector<Written> written(a2a || inplace ? 0 : size_t(s.N));
 
   for (size_t si = 0; si < s.steps.size(); ++si) {
     const Step& st = s.steps[si];
-    const bool perm_step = bruck && si > 0;  // Bruck's shifts and final rotation
+    const bool perm_step = perm(si);
     for (int64_t ri = st.first; ri < st.first + st.nrows; ++ri) {
       const Row& r = s.rows[size_t(ri)];
       DevItem it{};
@@ -173,10 +186,9 @@ Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
     DevStep d{};
     d.item0 = uint32_t(b.items.size());
     d.nitems = uint32_t(per_step[si].size());
-    const bool perm_step = bruck && si > 0;
-    const bool staged = perm_step && s.steps[si].staged;
-    d.flags = staged ? STEP_STAGED : 0u;
-    d.gsize = staged ? uint32_t(s.N) : 1u;
+    const bool perm_step = perm(si);
+    d.flags = perm_step ? STEP_STAGED : 0u;
+    d.gsize = perm_step ? uint32_t(s.N) : 1u;
     // same-destination accumulation (a Double Binary Tree parent with two
     // children) must keep row order; every other step may be walked backwards
     if (!perm_step) {
@@ -197,17 +209,19 @@ Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
   }
   const uint32_t nsteps = uint32_t(b.steps.size());
   if (nsteps == 0 || b.items.empty()) return b;
-  if (bruck) {
-    Phase p1;
-    p1.kind = Phase::ROWS;
-    p1.s0 = 0;
-    p1.s1 = 1;
-    p1.colspace = rows_cols;
-    b.phases.push_back(p1);
-    if (nsteps > 1 && perm_cols > 0) {
+  if (has_perm) {
+    if (first_perm > 0) {
+      Phase p1;
+      p1.kind = Phase::ROWS;
+      p1.s0 = 0;
+      p1.s1 = uint32_t(first_perm);
+      p1.colspace = rows_cols;
+      b.phases.push_back(p1);
+    }
+    if (perm_cols > 0) {
       Phase p2;
       p2.kind = Phase::PERM;
-      p2.s0 = 1;
+      p2.s0 = uint32_t(first_perm);
       p2.s1 = nsteps;
       p2.colspace = perm_cols;
       b.phases.push_back(p2);

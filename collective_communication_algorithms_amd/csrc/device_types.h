@@ -9,8 +9,8 @@
 // thread reads was written by itself in an earlier step (or is input): steps
 // need no synchronisation between threads or work groups, only program order.
 // Pairwise AllToAll rows read only the send buffers, which no row writes.  The
-// Bruck kernel uses the offset inside a block as its column instead; every
-// Bruck row keeps that offset.
+// permutation kernel (Bruck's and the Ring AllToAll's staged steps) uses the
+// offset inside a block as its column instead; every such row keeps that offset.
 #pragma once
 
 #include <stdint.h>
@@ -73,7 +73,7 @@ struct RowsArgs {                     // row kernel (copy / recv_and_reduce)
   RankPtrs p;
 };
 
-struct PermArgs {                     // staged permutation kernel (Bruck)
+struct PermArgs {                     // staged permutation kernel (AllToAll)
   const DevItem* items;
   const DevStep* steps;
   uint64_t* sums;

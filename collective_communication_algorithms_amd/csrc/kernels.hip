@@ -7,8 +7,9 @@
 //               row pieces inside the column groups it owns (see device_types.h),
 //               so no flags or barriers are needed between steps.  128-bit loads
 //               and stores, nontemporal hints per operand.
-//  perm_kernel  Bruck's in-place block shifts and final rotation ("集合通信算法延迟公式",
-//               Bruck AllToAll): each staging group is read into registers, the
+//  perm_kernel  in-place block shifts of the Bruck and Ring AllToAll rounds and their
+//               final rotation ("集合通信算法延迟公式", AllToAll 算法怎么选): each
+//               staging group is read into registers, the
 //               work group meets at a barrier, then the values are written
 //               permuted, so every read of a group precedes every write.
 //  fill / calib plain helpers: clear checksum slots, stream copy / add.
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
   }
 }
 
-// ---- staged permutation kernel (Bruck) --------------------------------------------
+// ---- staged permutation kernel (AllToAll) -------------------------------------------
 
 template <int U>
 struct UnitT;
@@ -315,11 +316,11 @@ __device__ __forceinline__ uint64_t unit_words(typename UnitT<U>::T v, uint64_t 
   else return uint64_t(uint32_t(v) << (8u * uint32_t(col & 3u)));
 }
 
-// Columns are unit indices inside a block; every Bruck row keeps its offset
+// Columns are unit indices inside a block; every staged row keeps its offset
 // inside the block, so a tile of block columns is a closed world: work group w
 // owns tiles w, w + G, ... and nothing outside it ever reads or writes them.
 // A staging group is the gs rows that permute one set of cells (the N ranks'
-// copies of one block in a shift round, or the N blocks of one rank in the
+// copies of one block slot in a Bruck or Ring round, or the N blocks of one rank in the
 // final rotation).  Per group and tile, wave v takes rows v, v+4, ... of the
 // group; lane l holds units l, l+64, ... (upl of them) of each such row in
 // registers: all rows' sources are loaded, the work group meets at a barrier

@@ -13,7 +13,9 @@
 //    [lo, hi) is the element with most trailing zero bits; tree 2 = tree 1 + 1 mod N;
 //  * Scatter / Gather keep chunks at their in-place offsets;
 //  * Pairwise round k sends block (i+k) mod N of rank i to rank (i+k) mod N;
-//  * Bruck = rotate, log2 rounds of shifts by 2^k, rotate back.
+//  * Bruck = rotate, log2 rounds of shifts by 2^k, rotate back;
+//  * Ring AllToAll = rotate, N-1 store-and-forward rounds to the next rank
+//    (round t moves slots t..N-1), rotate back.
 #include "plan.h"
 
 #include <algorithm>
@@ -390,21 +392,53 @@ void a2a_pairwise(Emitter& e) {
   }
 }
 
+// Bruck's local phases, also the storage of the Ring AllToAll: rotate in,
+// tmp_i[j] = send_i[(i+j) mod N] (slot j holds the block for rank i+j), and
+// rotate out, recv_i[(i-j) mod N] = tmp_i[j].  tmp is the receive buffer.
+void a2a_rotate_in(Emitter& e, int64_t B) {
+  const int N = e.s.N;
+  e.step(true);
+  for (int i = 0; i < N; ++i)
+    for (int j = 0; j < N; ++j) e.row(i, i, int64_t((i + j) % N) * B, j * B, B, false, true);
+}
+
+void a2a_rotate_out(Emitter& e, int64_t B) {
+  const int N = e.s.N;
+  e.step(true, true);
+  for (int i = 0; i < N; ++i)
+    for (int j = 0; j < N; ++j) e.row(i, i, j * B, int64_t(mod(i - j, N)) * B, B, false);
+}
+
+// eq:model-algo-a2a-bruck: round k shifts every block index with bit k set by
+// 2^k ranks, all such blocks packed into one message.
 void a2a_bruck(Emitter& e) {
   const int N = e.s.N;
   const int64_t B = e.s.count / N;
-  e.step(true);  // rotation: tmp_i[j] = send_i[(i+j) mod N]
-  for (int i = 0; i < N; ++i)
-    for (int j = 0; j < N; ++j) e.row(i, i, int64_t((i + j) % N) * B, j * B, B, false, true);
-  for (int k = 0; (1 << k) < N; ++k) {  // shift every block index with bit k set by 2^k ranks
+  a2a_rotate_in(e, B);
+  for (int k = 0; (1 << k) < N; ++k) {
     e.step(false, true);
     for (int j = 0; j < N; ++j)
       if ((j >> k) & 1)
         for (int i = 0; i < N; ++i) e.row(i, (i + (1 << k)) % N, j * B, j * B, B, false);
   }
-  e.step(true, true);  // inverse rotation: recv_i[(i-j) mod N] = tmp_i[j]
-  for (int i = 0; i < N; ++i)
-    for (int j = 0; j < N; ++j) e.row(i, i, j * B, int64_t(mod(i - j, N)) * B, B, false);
+  a2a_rotate_out(e, B);
+}
+
+// eq:model-algo-a2a-ring: N-1 rounds between ring neighbours only, read as
+// store-and-forward.  In the rotated storage a block in slot j still has j
+// hops to go before round 1; round t moves slots t..N-1 one rank on, so the
+// block in slot t arrives and stays.  Each slot's move is a cyclic shift over
+// all N ranks (a closed group), as in Bruck's rounds.
+void a2a_ring(Emitter& e) {
+  const int N = e.s.N;
+  const int64_t B = e.s.count / N;
+  a2a_rotate_in(e, B);
+  for (int t = 1; t < N; ++t) {
+    e.step(false, true);
+    for (int j = t; j < N; ++j)
+      for (int i = 0; i < N; ++i) e.row(i, (i + 1) % N, j * B, j * B, B, false);
+  }
+  a2a_rotate_out(e, B);
 }
 
 bool algo_valid(coll_kind_t kind, coll_algo_t a) {
@@ -418,7 +452,7 @@ bool algo_valid(coll_kind_t kind, coll_algo_t a) {
     case COLL_K_SCATTER: return a == COLL_ALGO_BINOMIAL || a == COLL_ALGO_LINEAR;
     case COLL_K_GATHER:
     case COLL_K_REDUCE: return a == COLL_ALGO_BINOMIAL;
-    case COLL_K_ALLTOALL: return a == COLL_ALGO_PAIRWISE || a == COLL_ALGO_BRUCK;
+    case COLL_K_ALLTOALL: return a == COLL_ALGO_PAIRWISE || a == COLL_ALGO_BRUCK || a == COLL_ALGO_RING;
   }
   return false;
 }
@@ -539,7 +573,9 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     case COLL_K_GATHER: gather_binomial(e); break;
     case COLL_K_REDUCE: reduce_binomial(e); break;
     case COLL_K_ALLTOALL:
-      if (algo == COLL_ALGO_PAIRWISE) a2a_pairwise(e); else a2a_bruck(e);
+      if (algo == COLL_ALGO_PAIRWISE) a2a_pairwise(e);
+      else if (algo == COLL_ALGO_BRUCK) a2a_bruck(e);
+      else a2a_ring(e);
       break;
   }
   return COLL_OK;
@@ -561,7 +597,7 @@ coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size,
     case COLL_K_SCATTER: cand = {COLL_ALGO_BINOMIAL, COLL_ALGO_LINEAR}; break;
     case COLL_K_GATHER:
     case COLL_K_REDUCE: cand = {COLL_ALGO_BINOMIAL}; break;
-    case COLL_K_ALLTOALL: cand = {COLL_ALGO_PAIRWISE, COLL_ALGO_BRUCK}; break;
+    case COLL_K_ALLTOALL: cand = {COLL_ALGO_PAIRWISE, COLL_ALGO_BRUCK, COLL_ALGO_RING}; break;
     default:
       err = "unknown collective";
       return COLL_ERR_INVALID_ARG;

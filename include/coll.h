@@ -74,7 +74,8 @@ typedef enum { COLL_SUM = 0, COLL_MAX = 1, COLL_MIN = 2 } coll_op_t;
 
 typedef enum {
   COLL_ALGO_DEFAULT = 0,       /* ring / binomial / pairwise for the collective */
-  COLL_ALGO_RING = 1,          /* [P3] Ring AllReduce, Ring AllGather / ReduceScatter          */
+  COLL_ALGO_RING = 1,          /* [P3] Ring AllReduce, Ring AllGather / ReduceScatter, Ring
+                                  AllToAll (store-and-forward between neighbours)              */
   COLL_ALGO_RHD = 2,           /* [P3] Recursive Halving-Doubling; ReduceScatter / AllGather need
                                   N = 2^n; AllReduce folds the surplus ranks of any N first     */
   COLL_ALGO_DBT = 3,           /* [P3] Double Binary Tree (any N)                              */
@@ -91,7 +92,7 @@ typedef enum {
                                   first of: AllReduce DBT, RHD, Ring; ReduceScatter / AllGather
                                   RHD, Ring; Broadcast binomial, chain, Scatter+AllGather,
                                   bidirectional ring; Scatter binomial, linear; AllToAll
-                                  Pairwise, Bruck.  `chunks` is ignored (one GPU moves the
+                                  Pairwise, Bruck, Ring.  `chunks` is ignored (one GPU moves the
                                   same bytes for any k). */
   COLL_ALGO_BIDIR_RING = 12    /* [P1] Broadcast over both directions of a ring at once (SCCL's
                                   4-chip scheme, any N), pipelined in `chunks` chunks */
@@ -159,7 +160,10 @@ coll_status_t coll_reduce(void* const* sendbufs, void* const* recvbufs, int nran
 
 /* [P3] AllToAll: send_i holds N blocks of count/N elements, block j meant for
  * rank j; afterwards block i of recv_j = block j of send_i.  Out of place only;
- * count must be a multiple of N.  algo: PAIRWISE (default), BRUCK. */
+ * count must be a multiple of N.  algo: PAIRWISE (default), BRUCK, RING
+ * (eq:model-algo-a2a-ring: N-1 rounds between neighbours i -> i+1; round t
+ * forwards the N-t blocks still in transit, so each link carries (N-1)M/2
+ * bytes in all, against the printed formula's (N-1)M/N). */
 coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                             void* stream);

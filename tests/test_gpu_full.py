@@ -102,7 +102,7 @@ def test_reducescatter_allgather_n64_256MiB(kind, algo):
     check_sampled(kind, algo, 64, (256 << 20) // 2, "bfloat16", 4, sigma=1e-3)
 
 
-@pytest.mark.parametrize("algo", ["pairwise", "bruck"])
+@pytest.mark.parametrize("algo", ["pairwise", "bruck", "ring"])
 def test_alltoall_n32_512x4096(algo):
     """32 ranks; each sends 512 tokens x 4096 bf16 to every peer (128 MiB per rank)."""
     import torch

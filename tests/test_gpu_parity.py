@@ -83,7 +83,7 @@ def test_reducescatter_allgather_n64_bf16(algo):
     assert_parity("allgather", algo, a, "bfloat16", inplace=False)
 
 
-@pytest.mark.parametrize("algo", ["pairwise", "bruck"])
+@pytest.mark.parametrize("algo", ["pairwise", "bruck", "ring"])
 @pytest.mark.parametrize("block", [512, 4096 + 8, 33])
 def test_alltoall_n32_bf16(algo, block):
     """32 ranks, bf16 N(0, 1); one block per peer (scaled-down block)."""
@@ -106,7 +106,7 @@ def _algos(kind, N):
             "allgather": ["ring"] + (["rhd"] if pow2 else []),
             "broadcast": ["binomial", "chain_pipe", "binomial_pipe", "scatter_allgather", "bidir_ring"],
             "scatter": ["binomial", "linear"], "gather": ["binomial"], "reduce": ["binomial"],
-            "alltoall": ["pairwise", "bruck"]}[kind]
+            "alltoall": ["pairwise", "bruck", "ring"]}[kind]
 
 
 @pytest.mark.parametrize("N", EDGE_NS)
@@ -154,6 +154,7 @@ def test_unaligned_buffers(dtype, offset):
     assert_parity("broadcast", "chain_pipe", a, dtype, root=2, k=7, offset_elems=offset, checksums=True)
     b = [x[:N * 1250] for x in a]
     assert_parity("alltoall", "bruck", b, dtype, offset_elems=offset, checksums=True)
+    assert_parity("alltoall", "ring", b, dtype, offset_elems=offset, checksums=True)
 
 
 @pytest.mark.parametrize("op", ["max", "min", "sum"])
@@ -227,6 +228,7 @@ def test_launch_shapes(exec_mode, group_tiles, max_grid, reverse):
     assert_parity("gather", "binomial", a, "float32", root=3, inplace=False)
     b = si.rank_arrays(5, 8, 8 * 20000, "bfloat16")
     assert_parity("alltoall", "bruck", b, "bfloat16", checksums=True)
+    assert_parity("alltoall", "ring", b, "bfloat16", checksums=True)
     assert_parity("broadcast", "binomial_pipe", si.rank_arrays(2, 8, 300001, "uint8"), "uint8", k=8)
 
 
@@ -240,6 +242,7 @@ def test_nontemporal_switch(nt):
     b = si.rank_arrays(5, 16, 16 * 4096, "bfloat16")
     assert_parity("alltoall", "bruck", b, "bfloat16")
     assert_parity("alltoall", "pairwise", b, "bfloat16")
+    assert_parity("alltoall", "ring", b, "bfloat16")
 
 
 @pytest.mark.parametrize("exec_mode", [0, 1])

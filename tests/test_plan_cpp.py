@@ -82,6 +82,7 @@ def test_alltoall_schedules_match(N):
     for B in (1, 3, 16):
         compare("alltoall", "pairwise", N, N * B, dtype="bfloat16")
         compare("alltoall", "bruck", N, N * B, dtype="bfloat16")
+        compare("alltoall", "ring", N, N * B, dtype="bfloat16")
 
 
 def test_config_scale_plans_match():
@@ -93,7 +94,7 @@ def test_config_scale_plans_match():
     for algo in ("ring", "rhd"):
         compare("reducescatter", algo, 64, 64 * 1024, dtype="bfloat16")
         compare("allgather", algo, 64, 64 * 1024, dtype="bfloat16")
-    for algo in ("pairwise", "bruck"):
+    for algo in ("pairwise", "bruck", "ring"):
         compare("alltoall", algo, 32, 32 * 64, dtype="bfloat16")
     for k in (1, 8, 64, 3, 13, 2):
         compare("broadcast", "chain_pipe", 8, 1 << 16, 0, k, dtype="uint8")
@@ -154,7 +155,7 @@ def test_reduce_linear_scatter_scatter_allgather_match(N):
 
 CANDIDATES = {"allreduce": ["dbt", "rhd", "ring"], "reducescatter": ["rhd", "ring"], "allgather": ["rhd", "ring"],
               "broadcast": ["binomial", "chain_pipe", "scatter_allgather", "bidir_ring"], "scatter": ["binomial", "linear"],
-              "gather": ["binomial"], "reduce": ["binomial"], "alltoall": ["pairwise", "bruck"]}
+              "gather": ["binomial"], "reduce": ["binomial"], "alltoall": ["pairwise", "bruck", "ring"]}
 
 
 def expected_auto(kind, N, count, dtype, alpha, beta):
