@@ -3,8 +3,9 @@
 A schedule is a list of steps; a step is a list of rows; a row says "rank ``src``
 sends ``n`` elements at element offset ``src_off`` to rank ``dst``, which stores
 them at ``dst_off``, either overwriting (copy) or as ``dst <- dst (+) src``
-(reduce)".  All sends of one step leave from the state before the step (the
-pages' model sends them simultaneously: "每步中所有已有数据的节点同时向一个新节点发送").
+(reduce)".  All sends of one step leave from the state before the step: in the
+pages' model the sends of one step happen at once ("一对多通信：Broadcast 与
+Scatter", 二叉树 Broadcast: every rank that holds the data sends in the same step).
 
 Conventions (readings of points the pages leave open):
   * N equal chunks of one rank buffer use the floor partition

@@ -318,7 +318,7 @@ def test_reduce_and_linear_scatter_counts(N):
 @pytest.mark.parametrize("N", NS)
 @pytest.mark.parametrize("root", [0, 3])
 def test_reduce_is_binomial_broadcast_reversed(N, root):
-    """Tree Reduce is the tree Broadcast run backwards ("对称操作")."""
+    """Tree Reduce is the tree Broadcast run backwards ("集合通信算法延迟公式", Tree Reduce)."""
     if root >= N:
         pytest.skip("root outside the ranks")
     bc = make_plan("broadcast", "binomial", N, 10, root)
