@@ -299,6 +299,96 @@ def calibrate(dev, gib: int = 2, reps: int = 10) -> dict:
     return {"calibration": out, "buffer_GiB": gib}
 
 
+def overlap(out_path: str, dev) -> None:
+    """A collective on a side stream beside a stand-in compute kernel (the HCCL
+    blog, 延迟掩盖：计算与通信的Overlap and Overlap的性能收益).
+
+    Workload: Ring AllReduce fp32, 8 ranks, 64 MiB and 256 MiB per rank, in
+    place.  The compute is ``coll_calib_spin``: register-only FMA chains, sized
+    to 0.5x, 1x and 2x the collective's time, on 256 or 1,024 work groups.
+    Per configuration: compute alone, the collective alone, and both launched
+    together (compute on the current stream, the collective on a second stream
+    of default priority, each started after one event and joined by another),
+    median of 10 after 2 warm-ups; the inputs are restored from a pristine copy
+    before every run (not timed).  Reported beside the blog's estimate with and
+    without overlap, and the share of the collective's time that was hidden.
+    The collective is run at its default grid (every resident slot) and at
+    smaller grids that leave compute units to the compute kernel.
+    """
+    import numpy as np
+    import torch
+
+    import collective_communication_algorithms_amd as coll
+    import seeded_inputs as si
+    from collective_communication_algorithms_amd import model
+
+    main_s = torch.cuda.current_stream(dev)
+    side_s = torch.cuda.Stream(dev)
+    spin_out = torch.empty(1024 * 256, dtype=torch.float32, device=dev)
+    reps, warm = 10, 2
+
+    def run(fn_main, fn_side, restore):
+        ts = []
+        for i in range(warm + reps):
+            restore()
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(main_s)
+            side_s.wait_event(e0)
+            if fn_main is not None:
+                fn_main()
+            if fn_side is not None:
+                fn_side()
+            e1.record(side_s)
+            main_s.wait_event(e1)
+            e2.record(main_s)
+            e2.synchronize()
+            if i >= warm:
+                ts.append(e0.elapsed_time(e2))
+        return float(np.median(ts))
+
+    open(out_path, "w").close()
+    N = 8
+    for mib in (64, 256):
+        count = (mib << 20) // 4
+        pristine = torch.empty((N, count), dtype=torch.float32, device=dev)
+        si.device_rank_tensors(3, N, count, "float32", dev, out=pristine)
+        live = pristine.clone()
+        ranks = list(live)
+
+        def restore():
+            live.copy_(pristine)
+
+        def spin(iters, grid):
+            return lambda: coll.coll_calib_spin(spin_out, iters, grid, stream=main_s)
+
+        for spin_grid in (256, 1024):
+            probe = 1 << 16
+            t_probe = run(spin(probe, spin_grid), None, lambda: None)
+            for max_grid in (0, 1536, 1024):
+                coll.coll_set_option("max_grid", max_grid)
+                comm = lambda: coll.coll_allreduce(ranks, algo="ring", stream=side_s)  # noqa: E731
+                t_comm = run(None, comm, restore)
+                for ratio in (0.5, 1.0, 2.0):
+                    iters = int(min(1 << 28, max(1, probe * ratio * t_comm / t_probe)))
+                    t_comp = run(spin(iters, spin_grid), None, lambda: None)
+                    t_both = run(spin(iters, spin_grid), comm, restore)
+                    r = {"workload": f"ring_allreduce_fp32_n8_{mib}MiB", "spin_grid": spin_grid,
+                         "coll_max_grid": max_grid, "ratio": ratio, "spin_iters": iters,
+                         "t_compute_ms": round(t_comp, 4), "t_comm_ms": round(t_comm, 4),
+                         "t_both_ms": round(t_both, 4),
+                         "model_overlap_ms": round(model.estimate_iteration_time(t_comp, t_comm, True), 4),
+                         "model_no_overlap_ms": round(model.estimate_iteration_time(t_comp, t_comm, False), 4),
+                         "hidden_fraction": round(model.hidden_fraction(t_comp, t_comm, t_both), 3),
+                         "both_over_model": round(t_both / model.estimate_iteration_time(t_comp, t_comm, True), 3)}
+                    with open(out_path, "a") as fh:
+                        fh.write(json.dumps(r) + "\n")
+                    print(json.dumps(r), file=sys.stderr, flush=True)
+        coll.coll_set_option("max_grid", 0)
+        torch.cuda.synchronize()
+        del pristine, live, ranks
+        torch.cuda.empty_cache()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +403,8 @@ def main() -> int:
                     help="only measure the plain copy (1R+1W) and add (2R+1W) streams and exit")
     ap.add_argument("--sweep", metavar="OUT_JSONL", help="time every configuration's calls and exit")
     ap.add_argument("--quick", action="store_true", help="with --sweep: fewer sizes and repetitions")
+    ap.add_argument("--overlap", metavar="OUT_JSONL",
+                    help="time a collective on a side stream beside a stand-in compute kernel and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                                "COPY_WRITE_CSV"),
                     help="write the traffic summary under profiles/ from rocprofv3 counter CSVs and exit")
@@ -341,6 +433,9 @@ def main() -> int:
         return 0
     if args.sweep:
         sweep(args.sweep, dev, args.quick)
+        return 0
+    if args.overlap:
+        overlap(args.overlap, dev)
         return 0
     N, M = args.nranks, args.mib << 20
     count = M // 4

@@ -84,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.coll_finalize.restype = None
     lib.coll_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.coll_calib_copy.restype = ctypes.c_int
+    lib.coll_calib_spin.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    lib.coll_calib_spin.restype = ctypes.c_int
     lib.coll_calib_add.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_void_p]
     lib.coll_calib_add.restype = ctypes.c_int

@@ -150,6 +150,14 @@ def coll_calib_copy(dst, src, stream=None):
                                       dst.numel() * dst.element_size(), _stream_handle(dst.device, stream)))
 
 
+def coll_calib_spin(out, iters, grid, stream=None):
+    """``out``: a float32 GPU tensor of at least grid * 256 elements."""
+    if out.dtype.itemsize != 4 or out.numel() < int(grid) * 256:
+        raise CollError(_lib.COLL_ERR_INVALID_ARG, "out needs grid * 256 float32 elements")
+    check(_lib.load().coll_calib_spin(ctypes.c_void_p(out.data_ptr()), int(iters), int(grid),
+                                      _stream_handle(out.device, stream)))
+
+
 def coll_calib_add(dst, a, b, stream=None):
     check(_lib.load().coll_calib_add(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(a.data_ptr()),
                                      ctypes.c_void_p(b.data_ptr()), dst.numel() * dst.element_size(),

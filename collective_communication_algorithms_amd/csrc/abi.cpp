@@ -624,4 +624,14 @@ coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t byt
   return calib(dst, a, b, bytes, stream);
 }
 
+coll_status_t coll_calib_spin(float* out, uint32_t iters, uint32_t grid, void* stream) {
+  if (!out) return fail(COLL_ERR_INVALID_ARG, "NULL buffer");
+  if (reinterpret_cast<uint64_t>(out) % 4) return fail(COLL_ERR_INVALID_ARG, "out must be 4-byte aligned");
+  if (grid < 1 || grid > COLL_SPIN_MAX_GRID) return fail(COLL_ERR_INVALID_ARG, "grid outside [1, COLL_SPIN_MAX_GRID]");
+  if (iters > COLL_SPIN_MAX_ITERS) return fail(COLL_ERR_INVALID_ARG, "iters above COLL_SPIN_MAX_ITERS");
+  const hipError_t he = launch_spin(out, iters, grid, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "spin launch");
+  return COLL_OK;
+}
+
 }  // extern "C"

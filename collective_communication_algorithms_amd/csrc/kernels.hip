@@ -13,6 +13,7 @@
 //               work group meets at a barrier, then the values are written
 //               permuted, so every read of a group precedes every write.
 //  fill / calib plain helpers: clear checksum slots, stream copy / add.
+//  spin         a register-only stand-in for compute, for overlap measurements.
 //
 // No MFMA: nothing here is a contraction.  Every kernel is bound by memory.
 #include <hip/hip_runtime.h>
@@ -500,6 +501,28 @@ int perm_blocks_per_cu(int unit, int slots, bool cks, bool nt) {
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;
+}
+
+// Four independent fp32 FMA chains per thread, `iters` rounds, all in
+// registers; one float per thread is stored at the end so that the work cannot
+// be dropped.  No other memory traffic: the kernel occupies compute units and
+// issue slots only, like the compute a collective is meant to hide behind.
+__global__ __launch_bounds__(BLOCK_THREADS) void spin_kernel(float* out, uint32_t iters) {
+  const uint32_t t = blockIdx.x * BLOCK_THREADS + threadIdx.x;
+  float a0 = 1.0f + float(t & 1023u) * 1e-6f, a1 = a0 + 0.25f, a2 = a0 + 0.5f, a3 = a0 + 0.75f;
+  const float m = 0.9999999f, c = 1e-7f;
+  for (uint32_t i = 0; i < iters; ++i) {
+    a0 = __builtin_fmaf(a0, m, c);
+    a1 = __builtin_fmaf(a1, m, c);
+    a2 = __builtin_fmaf(a2, m, c);
+    a3 = __builtin_fmaf(a3, m, c);
+  }
+  *gptr<float>(reinterpret_cast<char*>(out + t)) = (a0 + a1) + (a2 + a3);
+}
+
+hipError_t launch_spin(float* out, uint32_t iters, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL(spin_kernel, dim3(grid), dim3(BLOCK_THREADS), 0, stream, out, iters);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream) {

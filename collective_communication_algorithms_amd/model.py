@@ -107,3 +107,20 @@ def best_chunks(algo: str, N: int, M: float, alpha: float, beta: float, kmax: in
     """Integer k minimising the pipeline formula (the page prints a closed-form
     k* for the chain that does not minimise its own formula; the argmin is used)."""
     return min(range(1, kmax + 1), key=lambda k: (time("broadcast", algo, N, M, alpha, beta, k), k))
+
+
+def estimate_iteration_time(compute: float, comm: float, overlap: bool = True) -> float:
+    """One iteration of compute plus a collective (the HCCL blog, Overlap的性能收益).
+
+    Without overlap the two add.  With the collective on its own stream, only
+    the part of it that outlasts the compute shows: compute + max(0, comm -
+    compute).  Times in any one unit."""
+    if overlap:
+        return compute + max(0.0, comm - compute)
+    return compute + comm
+
+
+def hidden_fraction(compute: float, comm: float, both: float) -> float:
+    """Share of the collective's time that a measured overlapped run hid:
+    (compute + comm - both) / comm; 1 means fully hidden, 0 none."""
+    return (compute + comm - both) / comm if comm > 0 else 0.0

@@ -250,6 +250,18 @@ void coll_finalize(void);            /* frees the schedule cache; call with no w
 coll_status_t coll_calib_copy(void* dst, const void* src, size_t bytes, void* stream);
 coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t bytes, void* stream);
 
+/* A stand-in for compute, for measuring how far a collective on a side stream
+ * hides behind it ([P2] 延迟掩盖：计算与通信的Overlap; Overlap的性能收益).
+ * `grid` work groups of 256 threads each run `iters` rounds of four dependent
+ * fp32 FMA chains in registers, then write one float per thread to
+ * out[0 .. grid*256); there is no other memory traffic.  The duration grows
+ * linearly with iters.  out: device memory of grid*256 floats, 4-byte aligned,
+ * owned by the caller.  Errors: INVALID_ARG for NULL or misaligned out, grid
+ * outside [1, COLL_SPIN_MAX_GRID] or iters above COLL_SPIN_MAX_ITERS. */
+#define COLL_SPIN_MAX_GRID 65536
+#define COLL_SPIN_MAX_ITERS (1u << 28)
+coll_status_t coll_calib_spin(float* out, uint32_t iters, uint32_t grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -96,6 +96,19 @@ def test_options_and_strings():
     assert lib.coll_calib_copy(None, None, 16, None) == INV
 
 
+def test_spin_argument_errors():
+    """The stand-in compute kernel rejects bad arguments before any HIP call."""
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(64)
+    addr = ctypes.addressof(buf)
+    aligned = addr + (-addr) % 16
+    assert lib.coll_calib_spin(None, 10, 1, None) == INV
+    assert lib.coll_calib_spin(ctypes.c_void_p(aligned + 2), 10, 1, None) == INV
+    assert lib.coll_calib_spin(ctypes.c_void_p(aligned), 10, 0, None) == INV
+    assert lib.coll_calib_spin(ctypes.c_void_p(aligned), 10, 65537, None) == INV
+    assert lib.coll_calib_spin(ctypes.c_void_p(aligned), (1 << 28) + 1, 1, None) == INV
+
+
 def test_plan_capacity_protocol():
     lib = _lib.load()
     n = ctypes.c_size_t(0)

@@ -91,3 +91,19 @@ def test_bidir_ring_broadcast_formula():
             assert model.time("broadcast", "bidir_ring", N, M, a, b, k) == pytest.approx((h + k - 1) * (a + M / (k * b)))
     # with N - 1 ranks past the root in one direction it would be the chain pipeline
     assert model.time("broadcast", "bidir_ring", 8, M, a, b, 4) < model.time("broadcast", "chain_pipe", 8, M, a, b, 4)
+
+
+def test_overlap_estimate_matches_printed_examples():
+    """The blog prints the estimate for ResNet-50 (150 / 50 ms) and BERT-Large
+    (100 / 80 ms); its prose elsewhere gives other figures (a contradiction
+    inside the page), the printed function's outputs are the pin."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "overlap_examples.json")))
+    for ex in g["examples"]:
+        assert model.estimate_iteration_time(ex["compute_ms"], ex["comm_ms"], False) == ex["no_overlap_ms"]
+        assert model.estimate_iteration_time(ex["compute_ms"], ex["comm_ms"], True) == ex["overlap_ms"]
+
+
+def test_hidden_fraction_limits():
+    assert model.hidden_fraction(100, 50, 100) == 1.0      # fully hidden
+    assert model.hidden_fraction(100, 50, 150) == 0.0      # serialised
+    assert model.hidden_fraction(30, 50, 50) == pytest.approx(0.6)
