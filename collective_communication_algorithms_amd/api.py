@@ -34,36 +34,45 @@ def _ptr_array(tensors):
 
 
 def _check_tensors(send, recv):
+    """Every rank buffer a contiguous GPU tensor of one device, dtype and size
+    (the C ABI trusts `count` elements behind every pointer)."""
     if len(send) == 0:
         raise CollError(_lib.COLL_ERR_INVALID_ARG, "no rank buffers")
-    t0 = send[0]
-    for t in list(send) + list(recv or []):
-        if t.device != t0.device or t.dtype != t0.dtype or t.numel() != t0.numel() or not t.is_contiguous():
-            raise CollError(_lib.COLL_ERR_INVALID_ARG,
-                            "rank buffers must share device, dtype and size, and be contiguous")
-        if t.device.type != "cuda":
-            raise CollError(_lib.COLL_ERR_INVALID_ARG, "rank buffers must be GPU tensors")
     if recv is not None and len(recv) != len(send):
         raise CollError(_lib.COLL_ERR_INVALID_ARG, "one receive buffer per rank")
+    t0 = send[0]
+    if not t0.is_cuda:
+        raise CollError(_lib.COLL_ERR_INVALID_ARG, "rank buffers must be GPU tensors")
+    dev, dt, n = t0.get_device(), t0.dtype, t0.numel()
+    for group in (send, recv or ()):
+        for t in group:
+            if t.get_device() != dev or t.dtype != dt or t.numel() != n or not t.is_contiguous():
+                raise CollError(_lib.COLL_ERR_INVALID_ARG,
+                                "rank buffers must share device, dtype and size, and be contiguous")
 
 
 def _stream_handle(device, stream):
     import torch
     if stream is None:
-        stream = torch.cuda.current_stream(device)
+        idx = device.index if isinstance(device, torch.device) else int(device)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)   # skips building a Stream object
+        return ctypes.c_void_p(raw(idx) if raw is not None else torch.cuda.current_stream(idx).cuda_stream)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _collective(name, send, recv, op, algo, root, chunks, stream):
     import torch
     _check_tensors(send, recv)
-    lib = _lib.load()
-    dev = send[0].device
-    with torch.cuda.device(dev):
-        sp = _ptr_array(send)
-        rp = _ptr_array(recv) if recv is not None else None
-        st = getattr(lib, name)(sp, rp, len(send), send[0].numel(), DTYPES[_dtype_name(send[0])], OPS[op],
-                                ALGOS[algo], int(root), int(chunks), _stream_handle(dev, stream))
+    fn = getattr(_lib.load(), name)
+    idx = send[0].get_device()
+    args = (_ptr_array(send), _ptr_array(recv) if recv is not None else None, len(send), send[0].numel(),
+            DTYPES[_dtype_name(send[0])], OPS[op], ALGOS[algo], int(root), int(chunks))
+    # the library works on the current device: make it the tensors' one
+    if torch._C._cuda_getDevice() == idx:
+        st = fn(*args, _stream_handle(idx, stream))
+    else:
+        with torch.cuda.device(idx):
+            st = fn(*args, _stream_handle(idx, stream))
     check(st)
 
 

@@ -245,6 +245,20 @@ Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
   return b;
 }
 
+// Waves of a work group with bytes in the piece: within a tile, wave w handles
+// bytes [w * WAVE_BYTES, (w + 1) * WAVE_BYTES).
+uint32_t wave_mask(const DevItem& x) {
+  const uint32_t waves = BLOCK_THREADS / 64;
+  if (x.col1 - x.col0 >= TILE_BYTES) return (1u << waves) - 1u;
+  uint32_t m = 0;
+  for (uint64_t t = x.col0 / TILE_BYTES; t <= (x.col1 - 1) / TILE_BYTES; ++t)
+    for (uint32_t w = 0; w < waves; ++w) {
+      const uint64_t lo = t * TILE_BYTES + w * WAVE_BYTES, hi = lo + WAVE_BYTES;
+      if (x.col0 < hi && lo < x.col1) m |= 1u << w;
+    }
+  return m;
+}
+
 void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
                     bool per_step, std::vector<uint32_t>& off, std::vector<DevItem>& list) {
   const uint64_t gbytes = uint64_t(group_tiles) * TILE_BYTES;
@@ -252,8 +266,31 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
   off.clear();
   list.clear();
   std::vector<std::vector<DevItem>> per(G);
+  // per work group: the entries of its current run (indices into per[w]) and the run's step
+  std::vector<std::vector<size_t>> run(G);
+  std::vector<uint32_t> run_step(G, ~0u);
+  auto one_tile = [](const DevItem& x) { return x.col0 / TILE_BYTES == (x.col1 - 1) / TILE_BYTES; };
+  auto push = [&](uint32_t w, uint32_t s, const DevItem& q) {
+    std::vector<DevItem>& P = per[w];
+    std::vector<size_t>& R = run[w];
+    bool join = !R.empty() && run_step[w] == s && R.size() < RUN_MAX && one_tile(q) && one_tile(P[R.back()]);
+    for (size_t i = 0; join && i < R.size(); ++i) {
+      const DevItem& p = P[R[i]];
+      // two accumulations into the same bytes must stay one after the other
+      if (p.dst_rank == q.dst_rank && p.col0 < q.col1 && q.col0 < p.col1) join = false;
+    }
+    if (join) {
+      P[R.back()].flags |= ITEM_BATCH_NEXT;
+      R.push_back(P.size());
+    } else {
+      R.assign(1, P.size());
+      run_step[w] = s;
+    }
+    P.push_back(q);
+  };
   for (uint32_t j = 0; j < launches; ++j) {
     for (auto& v : per) v.clear();
+    for (auto& v : run) v.clear();
     const uint32_t sa = per_step ? ph.s0 + j : ph.s0, sb = per_step ? sa + 1 : ph.s1;
     for (uint32_t s = sa; s < sb; ++s) {
       const DevStep& st = b.steps[s];
@@ -270,7 +307,9 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
           piece.col1 = std::min(it.col1, (g + 1) * gbytes);
           uint32_t owner = uint32_t(g % G);
           if (per_step && rev) owner = G - 1 - owner;
-          per[owner].push_back(piece);
+          piece.flags &= ~uint32_t(ITEM_BATCH_NEXT);
+          piece.pad = wave_mask(piece);
+          push(owner, s, piece);
         }
       }
     }

@@ -13,6 +13,9 @@
 // offset inside a block as its column instead; every such row keeps that offset.
 #pragma once
 
+// Longest run of ITEM_BATCH_NEXT-linked work-list entries the row kernel takes at once.
+#define RUN_MAX 4
+
 #include <stdint.h>
 
 #include "coll.h"
@@ -25,6 +28,9 @@ enum : uint32_t {
   ITEM_DSRC_SEND = 1u << 2,  // old destination value read from the send buffer of dst_rank
   ITEM_VEC = 1u << 3,        // src_delta and dst_delta are multiples of 16
   ITEM_CKS_SHIFT = 4,        // bits 4..5: (-row start byte) mod 4, for the row checksum
+  ITEM_BATCH_NEXT = 1u << 6, // work lists only: the next entry of this list joins this one's
+                             // run (same step, both inside one tile, no common destination
+                             // bytes); a run's loads are all issued before its stores
 };
 
 constexpr uint32_t NO_ROW = 0xFFFFFFFFu;
@@ -36,8 +42,10 @@ struct DevItem {          // 48 bytes
   uint32_t row;           // schedule row (checksum slot) or NO_ROW
   uint16_t src_rank, dst_rank;
   uint32_t flags;
-  uint32_t pad;
+  uint32_t pad;           // work lists: bit w set if wave w of the work group has bytes in
+                          // the piece (wave w handles bytes [1024w, 1024w + 1024) of a tile)
 };
+static_assert(sizeof(DevItem) == 48, "work-list entries are 12 words");
 
 enum : uint32_t {
   STEP_STAGED = 1u << 0,  // in-place permutation: all reads of a group before its writes
@@ -60,6 +68,7 @@ enum Op : int { OP_SUM = 0, OP_MAX = 1, OP_MIN = 2 };
 
 constexpr int TILE_BYTES = 4096;      // 256 threads x 16 bytes
 constexpr int BLOCK_THREADS = 256;
+constexpr int WAVE_BYTES = TILE_BYTES / (BLOCK_THREADS / 64);  // one wave's bytes of a tile
 
 // Nontemporal hints, per operand of a row.
 enum : uint32_t { NT_SRC = 1u << 0, NT_DSRC = 1u << 1, NT_DST = 1u << 2, NT_ALL = 7u };

@@ -234,10 +234,7 @@ __device__ __forceinline__ void do_batch(const ItemView& v, uint64_t x0, uint64_
   }
 }
 
-// One piece: columns [col0, col1) of one row, inside one column group.  Thread t
-// handles bytes [16t, 16t + 16) of every 4 KiB tile the piece touches.
-template <int DT, int OP, bool CKS, int NTM>
-__device__ __forceinline__ void do_piece(const RowsArgs& a, const DevItem& it, uint64_t tofs, uint64_t& acc) {
+__device__ __forceinline__ ItemView view_of(const RowsArgs& a, const DevItem& it) {
   ItemView v;
   v.src = reinterpret_cast<const char*>((it.flags & ITEM_SRC_SEND) ? a.p.send[it.src_rank]
                                                                    : a.p.recv[it.src_rank]) + it.src_delta;
@@ -246,6 +243,14 @@ __device__ __forceinline__ void do_piece(const RowsArgs& a, const DevItem& it, u
   v.dst = reinterpret_cast<char*>(a.p.recv[it.dst_rank]) + it.dst_delta;
   v.reduce = (it.flags & ITEM_REDUCE) != 0;
   v.shift = (it.flags >> ITEM_CKS_SHIFT) & 3u;
+  return v;
+}
+
+// One piece: columns [col0, col1) of one row, inside one column group.  Thread t
+// handles bytes [16t, 16t + 16) of every 4 KiB tile the piece touches.
+template <int DT, int OP, bool CKS, int NTM>
+__device__ __forceinline__ void do_piece(const RowsArgs& a, const DevItem& it, uint64_t tofs, uint64_t& acc) {
+  const ItemView v = view_of(a, it);
   const bool vec = a.bases16 && (it.flags & ITEM_VEC);
   const uint64_t t0 = it.col0 / TILE_BYTES, t1 = (it.col1 - 1) / TILE_BYTES;
   if (!vec) {
@@ -266,22 +271,157 @@ __device__ __forceinline__ void do_piece(const RowsArgs& a, const DevItem& it, u
   if (t1 >= m1) do_unit<DT, OP, CKS, NTM>(v, t1 * TILE_BYTES + tofs, it.col0, it.col1, true, acc);
 }
 
+__device__ __forceinline__ bool one_tile(const DevItem& it) {
+  return it.col0 / TILE_BYTES == (it.col1 - 1) / TILE_BYTES;
+}
+
+// A run of up to RUN_MAX pieces that each lie inside one tile and may run
+// together (same step, no common destination bytes: ITEM_BATCH_NEXT); bit k
+// of `mine` is set for the members this wave has bytes in.  Every lane issues
+// the loads of its whole unit in every such piece first, then combines and
+// stores, so the run costs one memory round trip, not one per piece.  Units a
+// piece covers only in part take the element path afterwards.
+template <int DT, int OP, bool CKS, int NTM>
+__device__ __forceinline__ void do_run(const RowsArgs& a, const DevItem (&r)[RUN_MAX], uint32_t mine, uint64_t tofs) {
+  u32x4 s[RUN_MAX], d[RUN_MAX];
+  bool whole[RUN_MAX];
+#pragma unroll
+  for (uint32_t k = 0; k < RUN_MAX; ++k) {
+    whole[k] = false;
+    if (mine & (1u << k)) {
+      const ItemView v = view_of(a, r[k]);
+      const uint64_t x = (r[k].col0 / TILE_BYTES) * TILE_BYTES + tofs;
+      whole[k] = a.bases16 && (r[k].flags & ITEM_VEC) && x >= r[k].col0 && x + 16 <= r[k].col1;
+      if (whole[k]) {
+        s[k] = ld16<(NTM & NT_SRC) != 0>(v.src + x);
+        if (v.reduce) d[k] = ld16<(NTM & NT_DSRC) != 0>(v.dsrc + x);
+      }
+    }
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < RUN_MAX; ++k) {
+    if (mine & (1u << k)) {
+      const ItemView v = view_of(a, r[k]);
+      const uint64_t x = (r[k].col0 / TILE_BYTES) * TILE_BYTES + tofs;
+      uint64_t acc = 0;
+      if (whole[k]) {
+        u32x4 y = s[k];
+        if (v.reduce) y = combine16<DT, OP>(d[k], y);
+        st16<(NTM & NT_DST) != 0>(v.dst + x, y);
+        if constexpr (CKS) acc += words16(y, v.shift * 8u);
+      } else {
+        do_unit<DT, OP, CKS, NTM>(v, x, r[k].col0, r[k].col1, false, acc);
+      }
+      if constexpr (CKS) add_row_sum(a.sums, r[k].row, acc);
+    }
+  }
+}
+
+// Work-list entries held across a wave: lane l keeps the 12 words of entry
+// base + l.  One coalesced load fills 64 entries; an entry is then read into
+// scalar registers with v_readlane, so walking a list of many small pieces
+// costs no memory round trip per entry (a load of the entry inside the loop
+// would be a vector load, and waiting for it would also wait for the stores
+// of the piece before).
+struct LaneList {
+  uint32_t w[12];
+  uint32_t base;
+};
+
+__device__ __forceinline__ void lane_fill(LaneList& c, const DevItem* list, uint32_t base, uint32_t e1) {
+  c.base = base;
+  const uint32_t i = base + (threadIdx.x & 63u);
+#pragma unroll
+  for (int q = 0; q < 12; ++q) c.w[q] = 0;
+  if (i < e1) {
+    const char* p = reinterpret_cast<const char*>(list + i);
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const u32x4 v = *gptr<u32x4>(p + 16 * q);
+      c.w[4 * q] = v.x;
+      c.w[4 * q + 1] = v.y;
+      c.w[4 * q + 2] = v.z;
+      c.w[4 * q + 3] = v.w;
+    }
+  }
+}
+
+// word q of entry e (10: flags, 11: the wave mask)
+template <int Q>
+__device__ __forceinline__ uint32_t lane_word(const LaneList& c, uint32_t e) {
+  return __builtin_amdgcn_readlane(c.w[Q], e - c.base);
+}
+
+__device__ __forceinline__ DevItem lane_get(const LaneList& c, uint32_t e) {
+  const uint32_t j = e - c.base;
+  uint32_t x[12];
+#pragma unroll
+  for (int q = 0; q < 12; ++q) x[q] = __builtin_amdgcn_readlane(c.w[q], j);
+  DevItem it;
+  __builtin_memcpy(&it, x, sizeof(it));
+  return it;
+}
+
 // Work group w walks its slice of the launch's work list in order (the host
 // built it in step order; every piece of one column group is in one slice, so
 // values written in one step are read back by the same threads in the next).
-// The next list entry is fetched before the current piece is processed.
-template <int DT, int OP, bool CKS, int NTM>
+//
+// FINE = false (lists of large pieces): the next entry is fetched before the
+// current piece is processed; every piece goes alone.
+// FINE = true (lists of small pieces; more registers, so launched only for
+// them): entries come from a LaneList; a wave reads only the flags and wave
+// mask of an entry it has no bytes in and moves on; a run of
+// ITEM_BATCH_NEXT-linked pieces (each inside one tile, as the host builds
+// them) is processed together.  Both orders are correct: runs never hold two
+// pieces with common destination bytes.
+template <int DT, int OP, bool CKS, int NTM, bool FINE>
 __global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
   const uint32_t e0 = cload(a.off + blockIdx.x), e1 = cload(a.off + blockIdx.x + 1);
   if (e0 >= e1) return;
   const uint64_t tofs = uint64_t(threadIdx.x) * 16u;
-  DevItem next = cload(a.list + e0);
-  for (uint32_t e = e0; e < e1; ++e) {
-    const DevItem it = next;
-    if (e + 1 < e1) next = cload(a.list + e + 1);
-    uint64_t acc = 0;
-    do_piece<DT, OP, CKS, NTM>(a, it, tofs, acc);
-    if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
+  if constexpr (FINE) {
+    const uint32_t wbit = 1u << __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    LaneList c;
+    lane_fill(c, a.list, e0, e1);
+    uint32_t e = e0;
+    while (e < e1) {
+      if (e + RUN_MAX > c.base + 64u) lane_fill(c, a.list, e, e1);
+      const uint32_t avail = e1 - e < RUN_MAX ? e1 - e : RUN_MAX;
+      uint32_t n = 1, mine = (lane_word<11>(c, e) & wbit) ? 1u : 0u;
+      uint32_t fl = lane_word<10>(c, e);
+#pragma unroll
+      for (uint32_t k = 1; k < RUN_MAX; ++k) {
+        if (n == k && k < avail && (fl & ITEM_BATCH_NEXT)) {
+          fl = lane_word<10>(c, e + k);
+          if (lane_word<11>(c, e + k) & wbit) mine |= 1u << k;
+          n = k + 1;
+        }
+      }
+      if (n == 1) {
+        if (mine) {
+          const DevItem it = lane_get(c, e);
+          uint64_t acc = 0;
+          do_piece<DT, OP, CKS, NTM>(a, it, tofs, acc);
+          if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
+        }
+      } else if (mine) {
+        // members are read whole (scalar registers); `mine` decides which run
+        DevItem r[RUN_MAX];
+#pragma unroll
+        for (uint32_t k = 0; k < RUN_MAX; ++k) r[k] = lane_get(c, e + (k < n ? k : 0));
+        do_run<DT, OP, CKS, NTM>(a, r, mine, tofs);
+      }
+      e += n;
+    }
+  } else {
+    DevItem next = cload(a.list + e0);
+    for (uint32_t e = e0; e < e1; ++e) {
+      const DevItem it = next;
+      if (e + 1 < e1) next = cload(a.list + e + 1);
+      uint64_t acc = 0;
+      do_piece<DT, OP, CKS, NTM>(a, it, tofs, acc);
+      if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
+    }
   }
 }
 
@@ -416,39 +556,42 @@ __global__ __launch_bounds__(BLOCK_THREADS) void calib_kernel(char* dst, const c
 typedef void (*RowsFn)(RowsArgs);
 
 template <int DT, int OP, bool CKS>
-static RowsFn rows_fn_nt(uint32_t nt) {
+static RowsFn rows_fn_nt(uint32_t nt, bool fine) {
+  // lists of small pieces come from small footprints, which stay in the
+  // caches: the fine variant exists for the all-cached mask only
+  if (fine && (nt & 7u) == 0) return rows_kernel<DT, OP, CKS, 0, true>;
   switch (nt & 7u) {
-    case 0: return rows_kernel<DT, OP, CKS, 0>;
-    case 1: return rows_kernel<DT, OP, CKS, 1>;
-    case 2: return rows_kernel<DT, OP, CKS, 2>;
-    case 3: return rows_kernel<DT, OP, CKS, 3>;
-    case 4: return rows_kernel<DT, OP, CKS, 4>;
-    case 5: return rows_kernel<DT, OP, CKS, 5>;
-    case 6: return rows_kernel<DT, OP, CKS, 6>;
-    default: return rows_kernel<DT, OP, CKS, 7>;
+    case 0: return rows_kernel<DT, OP, CKS, 0, false>;
+    case 1: return rows_kernel<DT, OP, CKS, 1, false>;
+    case 2: return rows_kernel<DT, OP, CKS, 2, false>;
+    case 3: return rows_kernel<DT, OP, CKS, 3, false>;
+    case 4: return rows_kernel<DT, OP, CKS, 4, false>;
+    case 5: return rows_kernel<DT, OP, CKS, 5, false>;
+    case 6: return rows_kernel<DT, OP, CKS, 6, false>;
+    default: return rows_kernel<DT, OP, CKS, 7, false>;
   }
 }
 
 template <int DT, int OP>
-static RowsFn rows_fn(bool cks, uint32_t nt) {
-  return cks ? rows_fn_nt<DT, OP, true>(nt) : rows_fn_nt<DT, OP, false>(nt);
+static RowsFn rows_fn(bool cks, uint32_t nt, bool fine) {
+  return cks ? rows_fn_nt<DT, OP, true>(nt, fine) : rows_fn_nt<DT, OP, false>(nt, fine);
 }
 
 template <int DT>
-static RowsFn rows_fn_op(int op, bool cks, uint32_t nt) {
+static RowsFn rows_fn_op(int op, bool cks, uint32_t nt, bool fine) {
   switch (op) {
-    case OP_SUM: return rows_fn<DT, OP_SUM>(cks, nt);
-    case OP_MAX: return rows_fn<DT, OP_MAX>(cks, nt);
-    default: return rows_fn<DT, OP_MIN>(cks, nt);
+    case OP_SUM: return rows_fn<DT, OP_SUM>(cks, nt, fine);
+    case OP_MAX: return rows_fn<DT, OP_MAX>(cks, nt, fine);
+    default: return rows_fn<DT, OP_MIN>(cks, nt, fine);
   }
 }
 
-static RowsFn pick_rows(int dtype, int op, bool cks, uint32_t nt) {
+static RowsFn pick_rows(int dtype, int op, bool cks, uint32_t nt, bool fine) {
   switch (dtype) {
-    case DT_I32: return rows_fn_op<DT_I32>(op, cks, nt);
-    case DT_U8: return rows_fn_op<DT_U8>(op, cks, nt);
-    case DT_F32: return rows_fn_op<DT_F32>(op, cks, nt);
-    default: return rows_fn_op<DT_BF16>(op, cks, nt);
+    case DT_I32: return rows_fn_op<DT_I32>(op, cks, nt, fine);
+    case DT_U8: return rows_fn_op<DT_U8>(op, cks, nt, fine);
+    case DT_F32: return rows_fn_op<DT_F32>(op, cks, nt, fine);
+    default: return rows_fn_op<DT_BF16>(op, cks, nt, fine);
   }
 }
 
@@ -475,9 +618,9 @@ static PermFn pick_perm(int unit, int slots, bool cks, bool nt) {
   return slots > 16 ? pick_perm_slots<32>(unit, cks, nt) : pick_perm_slots<16>(unit, cks, nt);
 }
 
-hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, uint32_t grid,
+hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, bool fine, uint32_t grid,
                        hipStream_t stream) {
-  RowsFn f = pick_rows(dtype, op, cks, nt);
+  RowsFn f = pick_rows(dtype, op, cks, nt, fine);
   hipLaunchKernelGGL(f, dim3(grid), dim3(BLOCK_THREADS), 0, stream, a);
   return hipGetLastError();
 }
@@ -490,7 +633,8 @@ hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_
 
 int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_rows(dtype, op, cks, nt), BLOCK_THREADS, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_rows(dtype, op, cks, nt, false), BLOCK_THREADS, 0) !=
+      hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }

@@ -7,7 +7,7 @@
 
 namespace coll {
 
-hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, uint32_t grid,
+hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, bool fine, uint32_t grid,
                        hipStream_t stream);
 hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_t grid, hipStream_t stream);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream);

@@ -480,8 +480,8 @@ coll_algo_t resolve_algo(coll_kind_t kind, coll_algo_t algo) {
   return algo;
 }
 
-coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64_t count, int root,
-                             int chunks, Schedule& out, std::string& err) {
+coll_status_t validate_schedule_args(coll_kind_t kind, coll_algo_t algo_in, int N, int64_t count, int root,
+                                     int chunks, std::string& err) {
   if (int(kind) < 0 || int(kind) > int(COLL_K_REDUCE)) {
     err = "unknown collective";
     return COLL_ERR_INVALID_ARG;
@@ -530,6 +530,17 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
     err = "alltoall needs count divisible by nranks";
     return COLL_ERR_INVALID_ARG;
   }
+  return COLL_OK;
+}
+
+coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64_t count, int root,
+                             int chunks, Schedule& out, std::string& err) {
+  const coll_status_t st = validate_schedule_args(kind, algo_in, N, count, root, chunks, err);
+  if (st != COLL_OK) return st;
+  const coll_algo_t algo = resolve_algo(kind, algo_in);
+  const bool rooted =
+      kind == COLL_K_BROADCAST || kind == COLL_K_SCATTER || kind == COLL_K_GATHER || kind == COLL_K_REDUCE;
+  const bool pipe = algo_pipelined(algo);
   out = Schedule{};
   out.kind = kind;
   out.algo = algo;

@@ -56,6 +56,11 @@ coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size,
 
 // Validates (kind, algo, N, count, root, chunks) and builds the in-place
 // schedule.  Returns COLL_OK or an error status with a message in `err`.
+// The argument checks of build_schedule alone, with no rows built: the same
+// status and message build_schedule would give for these arguments.
+coll_status_t validate_schedule_args(coll_kind_t kind, coll_algo_t algo, int N, int64_t count, int root,
+                                     int chunks, std::string& err);
+
 // COLL_ALGO_AUTO must be resolved with choose_algo first.
 coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo, int N, int64_t count, int root,
                              int chunks, Schedule& out, std::string& err);
