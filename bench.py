@@ -410,7 +410,7 @@ def main() -> int:
                     help="write the traffic summary under profiles/ from rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
     if args.summarize_counters:
-        out = summarize_counters(*args.summarize_counters, "void coll::rows_kernel<2, 0, false, 1>", TRAFFIC_FILE)
+        out = summarize_counters(*args.summarize_counters, "void coll::rows_kernel<2, 0, false, 1, false>", TRAFFIC_FILE)
         print(json.dumps(out))
         return 0
     if args.gpus != 1:
