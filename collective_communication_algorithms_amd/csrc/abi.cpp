@@ -29,8 +29,8 @@ std::atomic<int64_t> opt_group{0};     // 0: automatic
 std::atomic<int64_t> opt_grid{0};      // 0: automatic
 std::atomic<int64_t> opt_nt{-1};       // -1: automatic, else an NT_* mask
 std::atomic<int64_t> opt_reverse{1};
-std::atomic<int64_t> opt_alpha_ns{1180};   // COLL_ALGO_AUTO: fitted per-step cost on MI355X
-std::atomic<int64_t> opt_beta_gbps{7000};  // COLL_ALGO_AUTO: fitted schedule-byte rate on MI355X
+std::atomic<int64_t> opt_alpha_ns{1060};   // COLL_ALGO_AUTO: fitted per-step cost on MI355X
+std::atomic<int64_t> opt_beta_gbps{8200};  // COLL_ALGO_AUTO: fitted schedule-byte rate on MI355X
 
 // Working sets up to the 256 MiB memory-side cache of MI355X stay there between
 // steps when accessed normally; larger ones stream, and then nontemporal source

@@ -223,8 +223,8 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          256 MiB memory-side cache, else source loads only.
  * COLL_OPT_REVERSE         1: odd steps walk their columns backwards, so data
  *                          written last is read first [1]; 0: always forwards.
- * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1180].
- * COLL_OPT_MODEL_BETA_GBPS schedule-byte rate used by COLL_ALGO_AUTO, in GB/s [7000].
+ * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
+ * COLL_OPT_MODEL_BETA_GBPS schedule-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
  * Every setting other than the model constants gives bit-identical results;
  * they only change the speed. */
 typedef enum {

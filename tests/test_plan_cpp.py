@@ -178,7 +178,7 @@ def test_auto_picks_the_least_predicted_time(kind, N):
     computed here from coll_plan's own counts (first candidate on ties)."""
     from collective_communication_algorithms_amd import coll_set_option
     try:
-        for alpha_ns, beta_gbps in ((1180, 7000), (10 ** 8, 7000), (0, 1)):
+        for alpha_ns, beta_gbps in ((1060, 8200), (10 ** 8, 8200), (0, 1)):
             coll_set_option("model_alpha_ns", alpha_ns)
             coll_set_option("model_beta_gbps", beta_gbps)
             for count in (N, 64 * N, (1 << 20) * N):
@@ -189,8 +189,8 @@ def test_auto_picks_the_least_predicted_time(kind, N):
                 got = coll_plan(kind, "auto", N, count, dtype, 0, 1)
                 assert got == coll_plan(kind, want, N, count, dtype, 0, 1), (kind, N, count, alpha_ns, want)
     finally:
-        coll_set_option("model_alpha_ns", 1180)
-        coll_set_option("model_beta_gbps", 7000)
+        coll_set_option("model_alpha_ns", 1060)
+        coll_set_option("model_beta_gbps", 8200)
 
 
 def test_auto_extremes():
@@ -203,5 +203,5 @@ def test_auto_extremes():
         assert coll_plan("alltoall", "auto", 32, 32 * 4096, "bfloat16") == coll_plan("alltoall", "pairwise", 32, 32 * 4096, "bfloat16")
         assert coll_plan("scatter", "auto", 8, 8 << 20, "uint8") == coll_plan("scatter", "linear", 8, 8 << 20, "uint8")
     finally:
-        coll_set_option("model_alpha_ns", 1180)
-        coll_set_option("model_beta_gbps", 7000)
+        coll_set_option("model_alpha_ns", 1060)
+        coll_set_option("model_beta_gbps", 8200)
