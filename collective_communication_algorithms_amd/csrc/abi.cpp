@@ -322,9 +322,11 @@ coll_status_t check_buffers(void* const* send, void* const* recv, int N, int64_t
   return COLL_OK;
 }
 
-// Blocked grid (schedules with reduce rows): column groups of this many tiles,
-// one per work group, for column spaces of at least this many bytes.
-constexpr uint32_t BLOCKED_GROUP_TILES = 4;
+// Blocked grid: column groups of this many tiles (schedules with reduce rows /
+// copy-only schedules), one per work group, for column spaces of at least
+// BLOCKED_MIN_COLSPACE bytes.
+constexpr uint32_t BLOCKED_GROUP_TILES_REDUCE = 4;
+constexpr uint32_t BLOCKED_GROUP_TILES_COPY = 8;
 constexpr uint64_t BLOCKED_MIN_COLSPACE = uint64_t(32) << 20;
 
 uint32_t pick_group_tiles(uint64_t colspace, uint64_t max_groups) {
@@ -413,17 +415,18 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     const Phase& ph = b.phases[pi];
     if (ph.kind == Phase::ROWS) {
       const uint64_t resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, ntmask));
-      // one launch for all steps: the resident work groups; one launch per
-      // step: several waves of them.  Large schedules with reduce rows take
-      // one column group per work group instead: a work group then carries
-      // its 16 KiB of columns through every step back to back, so each step
-      // reads what the step before left in the L2 and the memory-side cache
-      // (measured: Ring / RHD / DBT AllReduce 8 x 256 MiB 15-22 % faster,
-      // Tree Reduce 18 %, 64-rank ReduceScatter 9-24 %; copy-only schedules
-      // gain nothing consistent, so they keep the resident grid).
-      const bool blocked = !step_mode && has_reduce && ph.colspace >= BLOCKED_MIN_COLSPACE;
+      // one launch per step: several waves of resident work groups.  One
+      // launch for all steps: for large column spaces one column group per
+      // work group, so a work group carries its columns through every step
+      // back to back and each step reads what the step before left in the
+      // L2 and the memory-side cache (measured at 8 x 256 MiB: Ring / RHD /
+      // DBT AllReduce 15-22 % faster than a resident-sized grid, Tree Reduce
+      // 18 %, 64-rank ReduceScatter 9-24 %, AllGather 8-12 %); smaller ones
+      // keep a resident-sized grid.
+      const bool blocked = !step_mode && ph.colspace >= BLOCKED_MIN_COLSPACE;
       uint64_t cap = step_mode ? 4 * resident : resident;
-      uint32_t gt = blocked ? BLOCKED_GROUP_TILES : pick_group_tiles(ph.colspace, resident);
+      uint32_t gt = blocked ? (has_reduce ? BLOCKED_GROUP_TILES_REDUCE : BLOCKED_GROUP_TILES_COPY)
+                            : pick_group_tiles(ph.colspace, resident);
       if (blocked) cap = uint64_t(1) << 20;
       if (opt_group.load() > 0) gt = uint32_t(opt_group.load());
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
