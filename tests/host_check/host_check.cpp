@@ -1,0 +1,236 @@
+// Host-side invariants of schedule generation, binding and work-list layout,
+// built with AddressSanitizer and UndefinedBehaviorSanitizer by the CPU tests.
+// No GPU: only plan.cpp and bind.cpp are linked.
+//
+// For every shape in a grid of (collective, algorithm, N, count, root, k,
+// element size, in place) it checks:
+//   * build_schedule accepts the arguments and check_schedule finds no hazard;
+//   * bind_schedule: per row, the items of a row-kernel step cover the row's
+//     destination bytes exactly once;
+//   * build_worklist, for several launch shapes: the pieces of every item
+//     cover its columns exactly once, each piece lies inside one column group
+//     and sits in its owner's list, each list is in step order, the wave mask
+//     is the set of waves whose bytes the piece touches, and every
+//     ITEM_BATCH_NEXT run has at most RUN_MAX members of one step, each inside
+//     one tile, with no two members writing common bytes of one rank.
+// Prints one line per failure and "host_check: N shapes, M lists, ok" at the end.
+#include <cstdio>
+#include <cstdlib>
+#include <algorithm>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "bind.h"
+#include "plan.h"
+
+using namespace coll;
+
+namespace {
+
+int failures = 0;
+
+#define CHECK(cond, ...)                  \
+  do {                                    \
+    if (!(cond)) {                        \
+      ++failures;                         \
+      if (failures < 50) {                \
+        std::printf("FAIL %s: ", #cond);  \
+        std::printf(__VA_ARGS__);         \
+        std::printf("\n");                \
+      }                                   \
+    }                                     \
+  } while (0)
+
+struct Shape {
+  coll_kind_t kind;
+  coll_algo_t algo;
+  int N;
+  int64_t count;
+  int root, k, sz;
+  bool inplace;
+};
+
+std::string name(const Shape& s) {
+  char b[160];
+  std::snprintf(b, sizeof b, "kind %d algo %d N %d count %lld root %d k %d sz %d inplace %d", int(s.kind),
+                int(s.algo), s.N, (long long)s.count, s.root, s.k, s.sz, int(s.inplace));
+  return b;
+}
+
+uint32_t mask_of(uint64_t c0, uint64_t c1) {
+  uint32_t m = 0;
+  for (uint64_t t = c0 / TILE_BYTES; t <= (c1 - 1) / TILE_BYTES; ++t)
+    for (uint32_t w = 0; w < BLOCK_THREADS / 64; ++w) {
+      const uint64_t lo = t * TILE_BYTES + w * WAVE_BYTES, hi = lo + WAVE_BYTES;
+      if (c0 < hi && lo < c1) m |= 1u << w;
+    }
+  return m;
+}
+
+void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nlists) {
+  for (size_t pi = 0; pi < b.phases.size(); ++pi) {
+    const Phase& ph = b.phases[pi];
+    if (ph.kind != Phase::ROWS) continue;
+    for (uint32_t G : {1u, 3u, 257u})
+      for (uint32_t gt : {1u, 4u})
+        for (int rev = 0; rev < 2; ++rev)
+          for (int per_step = 0; per_step < 2; ++per_step) {
+            std::vector<uint32_t> off;
+            std::vector<DevItem> list;
+            build_worklist(b, ph, G, gt, rev != 0, per_step != 0, off, list);
+            ++nlists;
+            const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
+            const uint32_t launches = per_step ? ph.s1 - ph.s0 : 1;
+            CHECK(off.size() == size_t(launches) * (G + 1), "%s: offsets", name(sh).c_str());
+            if (off.size() != size_t(launches) * (G + 1)) continue;
+            // coverage: the pieces of item (step, dst rank, col0..col1, row) re-assemble it.
+            // Pieces carry no item index; match them to items by (row, dst_rank, src/dst delta, flags).
+            std::map<std::vector<int64_t>, std::vector<std::pair<uint64_t, uint64_t>>> got, want;
+            for (uint32_t s = ph.s0; s < ph.s1; ++s) {
+              const DevStep& d = b.steps[s];
+              for (uint32_t i = 0; i < d.nitems; ++i) {
+                const DevItem& it = b.items[d.item0 + i];
+                if (it.col1 <= it.col0) continue;
+                std::vector<int64_t> key{int64_t(s), it.row, it.src_rank, it.dst_rank, it.src_delta, it.dst_delta,
+                                         int64_t(it.flags & ~uint32_t(ITEM_BATCH_NEXT))};
+                want[key].push_back({it.col0, it.col1});
+              }
+            }
+            for (uint32_t j = 0; j < launches; ++j) {
+              for (uint32_t w = 0; w < G; ++w) {
+                const uint32_t a = off[size_t(j) * (G + 1) + w], z = off[size_t(j) * (G + 1) + w + 1];
+                CHECK(a <= z && z <= list.size(), "%s: list bounds", name(sh).c_str());
+                if (!(a <= z && z <= list.size())) continue;
+                uint32_t last_step = 0;
+                for (uint32_t e = a; e < z; ++e) {
+                  const DevItem& p = list[e];
+                  CHECK(p.col0 < p.col1, "%s: empty piece", name(sh).c_str());
+                  const uint64_t g = p.col0 / gbytes;
+                  CHECK((p.col1 - 1) / gbytes == g, "%s: piece crosses a group", name(sh).c_str());
+                  CHECK(p.pad == mask_of(p.col0, p.col1), "%s: wave mask %u vs %u", name(sh).c_str(), p.pad,
+                        mask_of(p.col0, p.col1));
+                  // step of the piece: its row's step (copies of undefined-by-rows output: step 0)
+                  CHECK(p.row == NO_ROW || p.row < sched.rows.size(), "%s: row index", name(sh).c_str());
+                  if (p.row != NO_ROW && p.row >= sched.rows.size()) continue;
+                  const uint32_t ps = p.row == NO_ROW ? 0u : uint32_t(sched.rows[p.row].step);
+                  // owner: group g mod G; in per-step launches of reversed (odd) steps, mirrored
+                  uint32_t owner = uint32_t(g % G);
+                  if (per_step && rev && (ps & 1u)) owner = G - 1 - owner;
+                  CHECK(owner == w, "%s: piece of step %u in the wrong list", name(sh).c_str(), ps);
+                  CHECK(ps >= last_step, "%s: list not in step order", name(sh).c_str());
+                  last_step = ps;
+                  std::vector<int64_t> key{int64_t(ps), p.row, p.src_rank, p.dst_rank, p.src_delta, p.dst_delta,
+                                           int64_t(p.flags & ~uint32_t(ITEM_BATCH_NEXT))};
+                  got[key].push_back({p.col0, p.col1});
+                  // runs
+                  if (p.flags & ITEM_BATCH_NEXT) {
+                    CHECK(e + 1 < z, "%s: run flag on the last entry", name(sh).c_str());
+                    CHECK(p.col0 / TILE_BYTES == (p.col1 - 1) / TILE_BYTES, "%s: run member spans tiles",
+                          name(sh).c_str());
+                  }
+                }
+                // run structure: members of one run, same step, one tile, disjoint writes, <= RUN_MAX
+                uint32_t e = a;
+                while (e < z) {
+                  uint32_t n = 1;
+                  while (e + n < z && (list[e + n - 1].flags & ITEM_BATCH_NEXT)) ++n;
+                  CHECK(n <= RUN_MAX, "%s: run of %u", name(sh).c_str(), n);
+                  for (uint32_t x = e; x < e + n; ++x)
+                    for (uint32_t y = x + 1; y < e + n; ++y) {
+                      const DevItem& p = list[x];
+                      const DevItem& q = list[y];
+                      CHECK(!(p.dst_rank == q.dst_rank && p.col0 < q.col1 && q.col0 < p.col1),
+                            "%s: run members write common bytes", name(sh).c_str());
+                      CHECK(q.col0 / TILE_BYTES == (q.col1 - 1) / TILE_BYTES, "%s: run member spans tiles",
+                            name(sh).c_str());
+                    }
+                  e += n;
+                }
+              }
+            }
+            // compare coverage
+            for (auto& kv : want) {
+              auto w = kv.second;
+              auto it = got.find(kv.first);
+              CHECK(it != got.end(), "%s: item without pieces", name(sh).c_str());
+              if (it == got.end()) continue;
+              auto g = it->second;
+              std::sort(w.begin(), w.end());
+              std::sort(g.begin(), g.end());
+              // merge adjacent pieces and compare with the merged items
+              auto merge = [](std::vector<std::pair<uint64_t, uint64_t>> v) {
+                std::vector<std::pair<uint64_t, uint64_t>> out;
+                for (auto& x : v) {
+                  if (!out.empty() && out.back().second == x.first) out.back().second = x.second;
+                  else out.push_back(x);
+                }
+                return out;
+              };
+              uint64_t wb = 0, gb = 0;
+              for (auto& x : w) wb += x.second - x.first;
+              for (auto& x : g) gb += x.second - x.first;
+              CHECK(wb == gb, "%s: covered %llu of %llu bytes", name(sh).c_str(), (unsigned long long)gb,
+                    (unsigned long long)wb);
+              CHECK(merge(w) == merge(g), "%s: pieces do not re-assemble the items", name(sh).c_str());
+            }
+            CHECK(got.size() == want.size(), "%s: pieces of unknown items", name(sh).c_str());
+          }
+  }
+}
+
+}  // namespace
+
+int main() {
+  std::vector<Shape> shapes;
+  const coll_kind_t kinds[] = {COLL_K_ALLREDUCE, COLL_K_REDUCESCATTER, COLL_K_ALLGATHER, COLL_K_BROADCAST,
+                               COLL_K_SCATTER,   COLL_K_GATHER,        COLL_K_ALLTOALL,  COLL_K_REDUCE};
+  for (coll_kind_t kind : kinds)
+    for (int a = 1; a <= int(COLL_ALGO_BIDIR_RING); ++a) {
+      if (a == int(COLL_ALGO_AUTO)) continue;
+      for (int N : {1, 2, 3, 5, 8, 13, 16})
+        for (int64_t count : {int64_t(0), int64_t(1), int64_t(7), int64_t(1000), int64_t(4099), int64_t(65536 + 77)})
+          for (int sz : {1, 2, 4})
+            for (int inplace = 0; inplace < 2; ++inplace) {
+              const int root = N / 2;
+              for (int k : {1, 3}) {
+                Shape s{kind, coll_algo_t(a), N, count, root, k, sz, inplace != 0};
+                if (kind == COLL_K_ALLTOALL) {
+                  if (inplace || count % N) continue;
+                }
+                std::string err;
+                if (validate_schedule_args(kind, s.algo, N, count, root, k, err) != COLL_OK) continue;
+                if (!algo_pipelined(s.algo) && k != 1) continue;
+                shapes.push_back(s);
+              }
+            }
+    }
+  int nlists = 0;
+  for (const Shape& sh : shapes) {
+    Schedule s;
+    std::string err;
+    const coll_status_t st = build_schedule(sh.kind, sh.algo, sh.N, sh.count, sh.root, sh.k, s, err);
+    CHECK(st == COLL_OK, "%s: build_schedule %d (%s)", name(sh).c_str(), int(st), err.c_str());
+    if (st != COLL_OK) continue;
+    const std::string hz = check_schedule(s);
+    CHECK(hz.empty(), "%s: hazard %s", name(sh).c_str(), hz.c_str());
+    const Bound b = bind_schedule(s, sh.sz, sh.inplace);
+    // row-kernel steps: per row, the items cover the destination bytes once
+    if (sh.kind != COLL_K_ALLTOALL) {
+      std::map<uint32_t, uint64_t> bytes;
+      for (const Phase& ph : b.phases)
+        if (ph.kind == Phase::ROWS)
+          for (uint32_t st2 = ph.s0; st2 < ph.s1; ++st2)
+            for (uint32_t i = 0; i < b.steps[st2].nitems; ++i) {
+              const DevItem& it = b.items[b.steps[st2].item0 + i];
+              if (it.row != NO_ROW) bytes[it.row] += it.col1 - it.col0;
+            }
+      for (size_t r = 0; r < s.rows.size(); ++r)
+        CHECK(bytes[uint32_t(r)] == uint64_t(s.rows[r].n) * uint64_t(sh.sz), "%s: row %zu covered %llu of %lld",
+              name(sh).c_str(), r, (unsigned long long)bytes[uint32_t(r)], (long long)(s.rows[r].n * sh.sz));
+    }
+    check_lists(sh, s, b, nlists);
+  }
+  std::printf("host_check: %zu shapes, %d lists, %s\n", shapes.size(), nlists, failures ? "FAILED" : "ok");
+  return failures ? 1 : 0;
+}
