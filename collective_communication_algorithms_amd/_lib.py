@@ -23,7 +23,7 @@ ALGOS = {"default": 0, "ring": 1, "rhd": 2, "dbt": 3, "binomial": 4, "chain_pipe
 KINDS = {"allreduce": 0, "reducescatter": 1, "allgather": 2, "broadcast": 3, "scatter": 4, "gather": 5,
          "alltoall": 6, "reduce": 7}
 OPTIONS = {"exec": 0, "group_tiles": 1, "max_grid": 2, "nontemporal": 3, "reverse": 4, "model_alpha_ns": 5,
-           "model_beta_gbps": 6}
+           "model_beta_gbps": 6, "cache_bytes": 7}
 MAX_RANKS = 128
 
 COLLECTIVES = ("coll_allreduce", "coll_reducescatter", "coll_allgather", "coll_broadcast", "coll_scatter",
@@ -76,6 +76,10 @@ def load() -> ctypes.CDLL:
     lib.coll_set_checksums.restype = ctypes.c_int
     lib.coll_set_option.argtypes = [ctypes.c_int, ctypes.c_int64]
     lib.coll_set_option.restype = ctypes.c_int
+    lib.coll_get_option.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
+    lib.coll_get_option.restype = ctypes.c_int
+    lib.coll_cache_info.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.coll_cache_info.restype = ctypes.c_int
     lib.coll_status_string.argtypes = [ctypes.c_int]
     lib.coll_status_string.restype = ctypes.c_char_p
     lib.coll_last_error.argtypes = []

@@ -150,6 +150,19 @@ def coll_set_option(name, value):
     check(_lib.load().coll_set_option(OPTIONS[name], int(value)))
 
 
+def coll_get_option(name):
+    v = ctypes.c_int64(0)
+    check(_lib.load().coll_get_option(OPTIONS[name], ctypes.byref(v)))
+    return v.value
+
+
+def coll_cache_info():
+    """(schedules cached, device bytes they hold)."""
+    n, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    check(_lib.load().coll_cache_info(ctypes.byref(n), ctypes.byref(b)))
+    return n.value, b.value
+
+
 def coll_finalize():
     _lib.load().coll_finalize()
 

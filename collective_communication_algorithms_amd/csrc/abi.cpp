@@ -31,6 +31,7 @@ std::atomic<int64_t> opt_nt{-1};       // -1: automatic, else an NT_* mask
 std::atomic<int64_t> opt_reverse{1};
 std::atomic<int64_t> opt_alpha_ns{1060};   // COLL_ALGO_AUTO: fitted per-step cost on MI355X
 std::atomic<int64_t> opt_beta_gbps{8200};  // COLL_ALGO_AUTO: fitted schedule-byte rate on MI355X
+std::atomic<int64_t> opt_cache_bytes{int64_t(1) << 31};  // device memory the schedule cache may hold
 
 // Working sets up to the 256 MiB memory-side cache of MI355X stay there between
 // steps when accessed normally; larger ones stream, and then nontemporal source
@@ -97,14 +98,17 @@ struct DevList {                // work lists of one row phase for one launch sh
   bool fine = false;            // small pieces: launch the row kernel's fine variant
   uint32_t* d_off = nullptr;
   DevItem* d_list = nullptr;
+  uint64_t bytes = 0;           // device memory held
 };
 
 struct Entry {
   Bound bound;
+  int dev = 0;
   DevItem* d_items = nullptr;
   DevStep* d_steps = nullptr;
   std::vector<DevList> lists;
   uint64_t last_use = 0;
+  uint64_t bytes = 0;           // device memory held by the tables and lists
 };
 
 struct DevInfo {
@@ -116,7 +120,8 @@ std::unordered_map<Key, std::unique_ptr<Entry>, KeyHash> g_cache;
 std::unordered_map<int, DevInfo> g_dev;
 std::unordered_map<uint64_t, int> g_occ;  // (kernel variant, device) -> blocks per CU
 uint64_t g_tick = 0;
-constexpr size_t CACHE_CAP = 512;
+constexpr size_t CACHE_CAP = 512;  // schedules kept
+uint64_t g_cache_bytes = 0;        // device memory they hold (COLL_OPT_CACHE_BYTES caps it)
 std::map<std::vector<int64_t>, coll_algo_t> g_auto;  // COLL_ALGO_AUTO decisions
 
 CostModel cost_model() {
@@ -151,6 +156,39 @@ void free_entry(Entry& e) {
   e.lists.clear();
   e.d_items = nullptr;
   e.d_steps = nullptr;
+  g_cache_bytes -= e.bytes;
+  e.bytes = 0;
+}
+
+// Drops the least recently used schedule other than `keep`; its tables may
+// still be read by queued work, so its device is synchronised first.
+// Returns false when there is nothing to drop.
+bool evict_lru(const Entry* keep, coll_status_t& st) {
+  st = COLL_OK;
+  auto lru = g_cache.end();
+  for (auto i = g_cache.begin(); i != g_cache.end(); ++i)
+    if (i->second.get() != keep && (lru == g_cache.end() || i->second->last_use < lru->second->last_use)) lru = i;
+  if (lru == g_cache.end()) return false;
+  int cur = 0;
+  hipError_t he = hipGetDevice(&cur);
+  if (he == hipSuccess && lru->second->dev != cur) he = hipSetDevice(lru->second->dev);
+  if (he == hipSuccess) he = hipDeviceSynchronize();
+  if (lru->second->dev != cur) (void)hipSetDevice(cur);
+  if (he != hipSuccess) {
+    st = hip_fail(he, "hipDeviceSynchronize");
+    return false;
+  }
+  free_entry(*lru->second);
+  g_cache.erase(lru);
+  return true;
+}
+
+// Keeps the cache within COLL_OPT_CACHE_BYTES of device memory (`keep` stays).
+coll_status_t trim_cache(const Entry* keep) {
+  coll_status_t st = COLL_OK;
+  while (g_cache_bytes > uint64_t(opt_cache_bytes.load()) && evict_lru(keep, st)) {
+  }
+  return st;
 }
 
 // The work lists of phase `pi` for this launch shape, built and uploaded on first use.
@@ -166,6 +204,8 @@ coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool revers
     DevList& l = e.lists.front();
     if (l.d_off) (void)hipFree(l.d_off);
     if (l.d_list) (void)hipFree(l.d_list);
+    e.bytes -= l.bytes;
+    g_cache_bytes -= l.bytes;
     e.lists.erase(e.lists.begin());
   }
   std::vector<uint32_t> off;
@@ -203,9 +243,12 @@ coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool revers
     (void)hipFree(l.d_list);
     return hip_fail(he, "hipMemcpy");
   }
+  l.bytes = off.size() * sizeof(uint32_t) + std::max<size_t>(list.size(), 1) * sizeof(DevItem);
+  e.bytes += l.bytes;
+  g_cache_bytes += l.bytes;
   e.lists.push_back(l);
   out = &e.lists.back();
-  return COLL_OK;
+  return trim_cache(&e);
 }
 
 coll_status_t device_info(int dev, DevInfo*& out) {
@@ -247,15 +290,9 @@ coll_status_t get_entry(const Key& k, Entry*& out) {
     return COLL_OK;
   }
   if (g_cache.size() >= CACHE_CAP) {
-    // evict the least recently used schedule; its tables may still be read by
-    // queued work, so wait for the device first
-    auto lru = g_cache.begin();
-    for (auto i = g_cache.begin(); i != g_cache.end(); ++i)
-      if (i->second->last_use < lru->second->last_use) lru = i;
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-    free_entry(*lru->second);
-    g_cache.erase(lru);
+    coll_status_t st = COLL_OK;
+    evict_lru(nullptr, st);
+    if (st != COLL_OK) return st;
   }
   Schedule s;
   std::string err;
@@ -282,10 +319,13 @@ coll_status_t get_entry(const Key& k, Entry*& out) {
       return hip_fail(he, "hipMemcpy");
     }
   }
+  e->dev = k.dev;
+  if (e->d_items) e->bytes = b.items.size() * sizeof(DevItem) + b.steps.size() * sizeof(DevStep);
+  g_cache_bytes += e->bytes;
   e->last_use = ++g_tick;
   out = e.get();
   g_cache.emplace(k, std::move(e));
-  return COLL_OK;
+  return trim_cache(out);
 }
 
 // Pointer checks: non-null, element-aligned, no overlap between distinct rank
@@ -598,8 +638,34 @@ coll_status_t coll_set_option(coll_option_t key, int64_t value) {
       if (value < -1 || value > 7) return fail(COLL_ERR_INVALID_ARG, "nontemporal mask in [-1, 7]");
       opt_nt = value;
       return COLL_OK;
+    case COLL_OPT_CACHE_BYTES:
+      if (value < 0) return fail(COLL_ERR_INVALID_ARG, "cache budget below 0");
+      opt_cache_bytes = value;
+      return COLL_OK;
   }
   return fail(COLL_ERR_INVALID_ARG, "unknown option");
+}
+
+coll_status_t coll_get_option(coll_option_t key, int64_t* value) {
+  if (!value) return fail(COLL_ERR_INVALID_ARG, "value is NULL");
+  switch (key) {
+    case COLL_OPT_EXEC: *value = opt_exec.load(); return COLL_OK;
+    case COLL_OPT_GROUP_TILES: *value = opt_group.load(); return COLL_OK;
+    case COLL_OPT_MAX_GRID: *value = opt_grid.load(); return COLL_OK;
+    case COLL_OPT_NONTEMPORAL: *value = opt_nt.load(); return COLL_OK;
+    case COLL_OPT_REVERSE: *value = opt_reverse.load(); return COLL_OK;
+    case COLL_OPT_MODEL_ALPHA_NS: *value = opt_alpha_ns.load(); return COLL_OK;
+    case COLL_OPT_MODEL_BETA_GBPS: *value = opt_beta_gbps.load(); return COLL_OK;
+    case COLL_OPT_CACHE_BYTES: *value = opt_cache_bytes.load(); return COLL_OK;
+  }
+  return fail(COLL_ERR_INVALID_ARG, "unknown option");
+}
+
+coll_status_t coll_cache_info(int64_t* schedules, int64_t* device_bytes) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (schedules) *schedules = int64_t(g_cache.size());
+  if (device_bytes) *device_bytes = int64_t(g_cache_bytes);
+  return COLL_OK;
 }
 
 const char* coll_status_string(coll_status_t s) {
@@ -619,6 +685,7 @@ void coll_finalize(void) {
   std::lock_guard<std::mutex> lock(g_mu);
   for (auto& kv : g_cache) free_entry(*kv.second);
   g_cache.clear();
+  g_cache_bytes = 0;
   g_occ.clear();
   g_dev.clear();
 }

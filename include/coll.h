@@ -215,8 +215,12 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          work group owns fixed columns, so the steps need
  *                          no synchronisation between work groups.
  *                          1: one launch per step (the launches order the steps).
- * COLL_OPT_GROUP_TILES     4 KiB column tiles per work-group column group, 1..64 [0: automatic].
- * COLL_OPT_MAX_GRID        cap on work groups per launch [0: automatic].
+ * COLL_OPT_GROUP_TILES     4 KiB column tiles per work-group column group, 1..64
+ *                          [0: automatic: for column spaces of 32 MiB or more one
+ *                          group per work group, 4 tiles with reduce rows and 8
+ *                          without; smaller ones up to 8 tiles over a grid of the
+ *                          work groups that fit on the device at once].
+ * COLL_OPT_MAX_GRID        cap on work groups per launch, up to 2^20 [0: automatic].
  * COLL_OPT_NONTEMPORAL     bit mask of nontemporal accesses: 1 source loads,
  *                          2 old-destination loads, 4 stores; -1: automatic
  *                          [-1]: none while all rank buffers together fit the
@@ -225,8 +229,13 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          written last is read first [1]; 0: always forwards.
  * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
  * COLL_OPT_MODEL_BETA_GBPS schedule-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
+ * COLL_OPT_CACHE_BYTES     device memory the schedule cache may hold, in bytes
+ *                          [2^31]; least recently used schedules are dropped
+ *                          (after synchronising their device) when a call
+ *                          takes it above; 0 keeps only the schedule in use.
+ *                          A lower value applies from the next call on.
  * Every setting other than the model constants gives bit-identical results;
- * they only change the speed. */
+ * they only change the speed or the memory held. */
 typedef enum {
   COLL_OPT_EXEC = 0,
   COLL_OPT_GROUP_TILES = 1,
@@ -234,9 +243,15 @@ typedef enum {
   COLL_OPT_NONTEMPORAL = 3,
   COLL_OPT_REVERSE = 4,
   COLL_OPT_MODEL_ALPHA_NS = 5,
-  COLL_OPT_MODEL_BETA_GBPS = 6
+  COLL_OPT_MODEL_BETA_GBPS = 6,
+  COLL_OPT_CACHE_BYTES = 7
 } coll_option_t;
 coll_status_t coll_set_option(coll_option_t key, int64_t value);
+/* The current value of an option; INVALID_ARG for an unknown key or NULL value. */
+coll_status_t coll_get_option(coll_option_t key, int64_t* value);
+/* Schedules in the cache and the device bytes their tables and work lists
+ * hold, summed over devices (either pointer may be NULL). */
+coll_status_t coll_cache_info(int64_t* schedules, int64_t* device_bytes);
 
 const char* coll_status_string(coll_status_t status);
 const char* coll_last_error(void);   /* thread-local detail of the last error */

@@ -118,3 +118,28 @@ def test_plan_capacity_protocol():
     n2 = ctypes.c_size_t(10)
     assert lib.coll_plan(0, 1, 8, 64, 2, 0, 1, rows, ctypes.byref(n2), None) == INV
     assert n2.value == 112
+
+
+def test_option_getter_and_cache_info():
+    """Options read back what was set (defaults first); the cache starts empty."""
+    import collective_communication_algorithms_amd as coll
+    want = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "model_alpha_ns": 1060,
+            "model_beta_gbps": 8200, "cache_bytes": 1 << 31}
+    saved = {k: coll.coll_get_option(k) for k in want}
+    try:
+        for k, v in want.items():
+            coll.coll_set_option(k, v)
+            assert coll.coll_get_option(k) == v
+        coll.coll_set_option("cache_bytes", 12345)
+        assert coll.coll_get_option("cache_bytes") == 12345
+        with pytest.raises(coll.CollError):
+            coll.coll_set_option("cache_bytes", -1)
+    finally:
+        for k, v in saved.items():
+            coll.coll_set_option(k, v)
+    lib = _lib.load()
+    assert lib.coll_get_option(99, ctypes.byref(ctypes.c_int64())) == INV
+    assert lib.coll_get_option(0, None) == INV
+    n, b = coll.coll_cache_info()
+    assert n >= 0 and b >= 0
+    assert lib.coll_cache_info(None, None) == OK

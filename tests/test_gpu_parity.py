@@ -311,3 +311,30 @@ def test_auto_algorithm_matches_the_oracle():
         for i, regs in enumerate(defined_regions(kind, N, count, 0)):
             for lo, hi in regs:
                 assert np.array_equal(got[i][lo:hi].view(np.uint8), want[i][lo:hi].view(np.uint8)), (kind, chosen)
+
+
+def test_cache_budget_evicts_and_results_stay_exact():
+    """With a zero device-memory budget every call drops the previous schedule
+    (after synchronising) and keeps only its own; results stay bit-exact,
+    also when the same shapes come back."""
+    import collective_communication_algorithms_amd as coll
+    saved = coll.coll_get_option("cache_bytes")
+    try:
+        coll.coll_finalize()
+        coll.coll_set_option("cache_bytes", 0)
+        a8 = si.rank_arrays(11, 8, 8 * 3001, "float32")
+        b8 = si.rank_arrays(12, 8, 70001, "uint8")
+        for _ in range(2):
+            for algo in ("ring", "rhd", "dbt"):
+                assert_parity("allreduce", algo, a8, "float32", checksums=True)
+                assert coll.coll_cache_info()[0] == 1
+            assert_parity("broadcast", "bidir_ring", b8, "uint8", root=3, k=4)
+            assert_parity("alltoall", "bruck", a8, "float32")
+            assert coll.coll_cache_info()[0] == 1
+        coll.coll_set_option("cache_bytes", saved)
+        assert_parity("allreduce", "ring", a8, "float32")
+        assert_parity("allreduce", "dbt", a8, "float32")
+        n, b = coll.coll_cache_info()
+        assert n == 3 and b > 0      # the AllToAll of the last round stays, the two AllReduces join it
+    finally:
+        coll.coll_set_option("cache_bytes", saved)
