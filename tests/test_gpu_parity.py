@@ -338,3 +338,16 @@ def test_cache_budget_evicts_and_results_stay_exact():
         assert n == 3 and b > 0      # the AllToAll of the last round stays, the two AllReduces join it
     finally:
         coll.coll_set_option("cache_bytes", saved)
+
+
+@pytest.mark.parametrize("algo,N,B", [("bruck", 96, 37), ("bruck", 128, 16), ("ring", 80, 24), ("bruck", 64, 1000),
+                                      ("ring", 33, 257), ("bruck", 17, 4096 + 3)])
+def test_alltoall_permutation_kernel_shapes(algo, N, B):
+    """The permutation kernel at group sizes that take 16- and 32-slot variants
+    (up to and beyond 64 rows per group) and ragged block widths: the block
+    transpose, bit for bit."""
+    a = si.rank_arrays(13, N, N * B, "int32")
+    got, _ = assert_parity("alltoall", algo, a, "int32", checksums=True)
+    for j in (0, N // 3, N - 1):
+        for i in (0, N // 2, N - 1):
+            assert np.array_equal(got[j][i * B:(i + 1) * B], a[i][j * B:(j + 1) * B])
