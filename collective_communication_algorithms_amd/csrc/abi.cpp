@@ -501,7 +501,10 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       // every staged AllToAll step permutes groups of N rows; each of the 4 waves
       // holds ceil(N/4) rows, 2^lg units per lane of each
       const uint32_t ipw = uint32_t(N + 3) / 4;
-      const int slots = ipw <= 16 ? 16 : 32;
+      // slots per lane: measured at 32 ranks (5-8 rows per wave) 8 slots, one
+      // unit per row, beat 16 (Bruck 7.5 vs 8.0 ms); at 8 and 16 ranks 16 slots
+      // beat 8 (0.68 vs 0.72 ms, 1.63 vs 1.77 ms)
+      const int slots = ipw > 4 && ipw <= 8 ? 8 : ipw <= 16 ? 16 : 32;
       uint32_t lg = 0;
       while ((ipw << (lg + 1)) <= uint32_t(slots) && (64u << (lg + 1)) <= std::max<uint32_t>(a.ncols_units, 64)) ++lg;
       a.lg_upl = lg;

@@ -615,6 +615,7 @@ static PermFn pick_perm_slots(int unit, bool cks, bool nt) {
 }
 
 static PermFn pick_perm(int unit, int slots, bool cks, bool nt) {
+  if (slots <= 8) return pick_perm_slots<8>(unit, cks, nt);
   return slots > 16 ? pick_perm_slots<32>(unit, cks, nt) : pick_perm_slots<16>(unit, cks, nt);
 }
 
