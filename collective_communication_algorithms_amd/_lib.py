@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.coll_set_checksums.restype = ctypes.c_int
     lib.coll_set_option.argtypes = [ctypes.c_int, ctypes.c_int64]
     lib.coll_set_option.restype = ctypes.c_int
+    lib.coll_check.argtypes = [ctypes.c_void_p]
+    lib.coll_check.restype = ctypes.c_int
     lib.coll_get_option.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64)]
     lib.coll_get_option.restype = ctypes.c_int
     lib.coll_cache_info.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]

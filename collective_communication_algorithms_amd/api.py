@@ -150,6 +150,18 @@ def coll_set_option(name, value):
     check(_lib.load().coll_set_option(OPTIONS[name], int(value)))
 
 
+def coll_check(stream=None, device=None):
+    """Wait for the stream's work (the current stream of ``device``, default
+    the current device, when None) and raise CollError if it failed."""
+    import torch
+    if stream is None:
+        dev = torch.cuda.current_device() if device is None else device
+        handle = _stream_handle(dev, None)
+    else:
+        handle = ctypes.c_void_p(stream.cuda_stream)
+    check(_lib.load().coll_check(handle))
+
+
 def coll_get_option(name):
     v = ctypes.c_int64(0)
     check(_lib.load().coll_get_option(OPTIONS[name], ctypes.byref(v)))

@@ -649,6 +649,13 @@ coll_status_t coll_set_option(coll_option_t key, int64_t value) {
   return fail(COLL_ERR_INVALID_ARG, "unknown option");
 }
 
+coll_status_t coll_check(void* stream) {
+  hipError_t he = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (he == hipSuccess) he = hipGetLastError();
+  if (he != hipSuccess) return hip_fail(he, "stream work");
+  return COLL_OK;
+}
+
 coll_status_t coll_get_option(coll_option_t key, int64_t* value) {
   if (!value) return fail(COLL_ERR_INVALID_ARG, "value is NULL");
   switch (key) {

@@ -253,6 +253,13 @@ coll_status_t coll_get_option(coll_option_t key, int64_t* value);
  * hold, summed over devices (either pointer may be NULL). */
 coll_status_t coll_cache_info(int64_t* schedules, int64_t* device_bytes);
 
+/* Waits for the work enqueued on `stream` (a hipStream_t; NULL: the null
+ * stream) and reports whether it failed: COLL_ERR_HIP with the HIP error text
+ * in coll_last_error(), else COLL_OK.  No kernel of this library waits on a
+ * flag written by another work group (every column has one owner), so no call
+ * can hang on one and there is no time-out status. */
+coll_status_t coll_check(void* stream);
+
 const char* coll_status_string(coll_status_t status);
 const char* coll_last_error(void);   /* thread-local detail of the last error */
 void coll_finalize(void);            /* frees the schedule cache; call with no work in flight */

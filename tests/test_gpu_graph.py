@@ -1,0 +1,57 @@
+"""Collective calls captured in a HIP graph (through torch.cuda.CUDAGraph) and
+replayed: after one eager call has built and cached the schedule, a call only
+launches kernels, which capture records.  Every replay, with eager work and
+synchronisation between replays, must give the eager result bit for bit."""
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+
+def test_captured_collectives_replay_exactly(gpu_device):
+    import torch
+    import collective_communication_algorithms_amd as coll
+    N, count = 8, 8 * 20000 + 8
+    a = si.rank_arrays(15, N, count, "float32")
+    u = si.rank_arrays(16, N, 1 << 18, "uint8")
+    pristine = torch.stack([si.host_to_tensor(x, "float32", gpu_device) for x in a])
+    pu = torch.stack([si.host_to_tensor(x, "uint8", gpu_device) for x in u])
+    live, lu = pristine.clone(), pu.clone()
+    recv = torch.empty_like(pristine)
+
+    def work():
+        coll.coll_allreduce(list(live), algo="ring")
+        coll.coll_allreduce(list(live), algo="dbt", op="max")
+        coll.coll_broadcast(list(lu), algo="bidir_ring", root=5, chunks=3)
+        coll.coll_alltoall(list(pristine), list(recv), algo="bruck")
+
+    # eager reference (also builds and caches every schedule before capture)
+    work()
+    torch.cuda.synchronize()
+    want = (live.clone(), lu.clone(), recv.clone())
+    live.copy_(pristine)
+    lu.copy_(pu)
+    recv.zero_()
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        live.copy_(pristine)          # eager work between replays
+        lu.copy_(pu)
+        recv.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, w, name in ((live, want[0], "allreduce"), (lu, want[1], "broadcast"), (recv, want[2], "alltoall")):
+            assert torch.equal(got.view(torch.uint8), w.view(torch.uint8)), (rep, name)
+    coll.coll_check()

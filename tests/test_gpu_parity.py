@@ -351,3 +351,16 @@ def test_alltoall_permutation_kernel_shapes(algo, N, B):
     for j in (0, N // 3, N - 1):
         for i in (0, N // 2, N - 1):
             assert np.array_equal(got[j][i * B:(i + 1) * B], a[i][j * B:(j + 1) * B])
+
+
+def test_coll_check_after_calls():
+    """coll_check waits for the stream's work and reports success."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    a = si.rank_arrays(14, 8, 8 * 1000, "float32")
+    t = [si.host_to_tensor(x, "float32", "cuda:0") for x in a]
+    side = torch.cuda.Stream()
+    coll.coll_allreduce(t, algo="dbt", stream=side)
+    coll.coll_check(stream=side)
+    coll.coll_allreduce(t, algo="ring")
+    coll.coll_check()
