@@ -3,6 +3,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -32,6 +34,19 @@ std::atomic<int64_t> opt_reverse{1};
 std::atomic<int64_t> opt_alpha_ns{1060};   // COLL_ALGO_AUTO: fitted per-step cost on MI355X
 std::atomic<int64_t> opt_beta_gbps{8200};  // COLL_ALGO_AUTO: fitted schedule-byte rate on MI355X
 std::atomic<int64_t> opt_cache_bytes{int64_t(1) << 31};  // device memory the schedule cache may hold
+std::atomic<bool> g_debug{false};      // COLL_DEBUG: one line per call on stderr
+
+const char* kind_name(coll_kind_t k) {
+  static const char* n[] = {"allreduce", "reducescatter", "allgather", "broadcast", "scatter", "gather",
+                            "alltoall", "reduce"};
+  return int(k) >= 0 && int(k) < 8 ? n[int(k)] : "?";
+}
+
+const char* algo_name(coll_algo_t a) {
+  static const char* n[] = {"default", "ring", "rhd", "dbt", "binomial", "chain_pipe", "binomial_pipe",
+                            "pairwise", "bruck", "linear", "scatter_allgather", "auto", "bidir_ring"};
+  return int(a) >= 0 && int(a) < 13 ? n[int(a)] : "?";
+}
 
 // Working sets up to the 256 MiB memory-side cache of MI355X stay there between
 // steps when accessed normally; larger ones stream, and then nontemporal source
@@ -451,6 +466,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   const int dt = int(dtype) == COLL_INT32 ? DT_I32 : int(dtype) == COLL_UINT8 ? DT_U8
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
   const bool has_reduce = kind == COLL_K_ALLREDUCE || kind == COLL_K_REDUCESCATTER || kind == COLL_K_REDUCE;
+  std::string dbg;  // launch shapes, for COLL_DEBUG
   for (size_t pi = 0; pi < b.phases.size(); ++pi) {
     const Phase& ph = b.phases[pi];
     if (ph.kind == Phase::ROWS) {
@@ -486,6 +502,10 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         he = launch_rows(a, dt, int(op), cks, ntmask, L->fine, grid, stream);
         if (he != hipSuccess) return hip_fail(he, "row kernel launch");
       }
+      if (g_debug.load())
+        dbg += " | rows steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
+               std::to_string(grid) + " group_tiles " + std::to_string(gt) + (L->fine ? " fine" : "") + " nt " +
+               std::to_string(ntmask) + " launches " + std::to_string(L->launches);
     } else {
       PermArgs a{};
       a.items = e->d_items;
@@ -521,8 +541,15 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         he = launch_perm(a, unit, slots, cks, grid, stream);
         if (he != hipSuccess) return hip_fail(he, "permutation kernel launch");
       }
+      if (g_debug.load())
+        dbg += " | perm steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
+               std::to_string(grid) + " unit " + std::to_string(unit) + " slots " + std::to_string(slots);
     }
   }
+  if (g_debug.load())
+    std::fprintf(stderr, "coll: %s algo %s N %d count %lld dtype-size %d %s steps %lld rows %lld sched_bytes %lld%s\n",
+                 kind_name(kind), algo_name(ra), N, (long long)count, sz, inplace ? "in-place" : "out-of-place",
+                 (long long)b.counts.steps, (long long)b.counts.rows, (long long)b.counts.hbm_bytes, dbg.c_str());
   t_last = b.counts;
   return COLL_OK;
 }
@@ -739,3 +766,39 @@ coll_status_t coll_calib_spin(float* out, uint32_t iters, uint32_t grid, void* s
 }
 
 }  // extern "C"
+
+namespace {
+
+// Initial option values from the environment (read once, when the library is
+// loaded): COLL_EXEC, COLL_GROUP_TILES, COLL_MAX_GRID, COLL_NONTEMPORAL,
+// COLL_REVERSE, COLL_MODEL_ALPHA_NS, COLL_MODEL_BETA_GBPS, COLL_CACHE_BYTES
+// (integers, as for coll_set_option; an invalid one is reported on stderr and
+// ignored), and COLL_DEBUG (set and not "0": one line per call on stderr).
+struct EnvOptions {
+  EnvOptions() {
+    static const struct {
+      const char* name;
+      coll_option_t key;
+    } vars[] = {{"COLL_EXEC", COLL_OPT_EXEC},
+                {"COLL_GROUP_TILES", COLL_OPT_GROUP_TILES},
+                {"COLL_MAX_GRID", COLL_OPT_MAX_GRID},
+                {"COLL_NONTEMPORAL", COLL_OPT_NONTEMPORAL},
+                {"COLL_REVERSE", COLL_OPT_REVERSE},
+                {"COLL_MODEL_ALPHA_NS", COLL_OPT_MODEL_ALPHA_NS},
+                {"COLL_MODEL_BETA_GBPS", COLL_OPT_MODEL_BETA_GBPS},
+                {"COLL_CACHE_BYTES", COLL_OPT_CACHE_BYTES}};
+    for (const auto& v : vars) {
+      const char* s = std::getenv(v.name);
+      if (!s || !*s) continue;
+      char* end = nullptr;
+      const long long x = std::strtoll(s, &end, 10);
+      if (*end != '\0' || coll_set_option(v.key, int64_t(x)) != COLL_OK)
+        std::fprintf(stderr, "coll: ignoring %s=%s\n", v.name, s);
+    }
+    const char* d = std::getenv("COLL_DEBUG");
+    coll::g_debug = d && *d && std::strcmp(d, "0") != 0;
+  }
+};
+EnvOptions g_env_options;
+
+}  // namespace

@@ -143,3 +143,18 @@ def test_option_getter_and_cache_info():
     n, b = coll.coll_cache_info()
     assert n >= 0 and b >= 0
     assert lib.coll_cache_info(None, None) == OK
+
+
+def test_environment_sets_initial_options():
+    """COLL_* variables give the options' initial values when the library loads;
+    an invalid value is reported and ignored."""
+    import subprocess
+    import sys
+    code = ("import collective_communication_algorithms_amd as c; "
+            "print(c.coll_get_option('group_tiles'), c.coll_get_option('cache_bytes'), c.coll_get_option('exec'), "
+            "c.coll_get_option('nontemporal'))")
+    env = dict(os.environ, COLL_GROUP_TILES="4", COLL_CACHE_BYTES="1000", COLL_EXEC="7", COLL_NONTEMPORAL="x")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["4", "1000", "0", "-1"]
+    assert "ignoring COLL_EXEC=7" in r.stderr and "ignoring COLL_NONTEMPORAL=x" in r.stderr

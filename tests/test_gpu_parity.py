@@ -364,3 +364,24 @@ def test_coll_check_after_calls():
     coll.coll_check(stream=side)
     coll.coll_allreduce(t, algo="ring")
     coll.coll_check()
+
+
+def test_debug_lines(gpu_device):
+    """COLL_DEBUG=1 prints one line per call: the collective, the resolved
+    algorithm, the schedule's counts and each launch's shape."""
+    import os
+    import subprocess
+    import sys
+    code = ("import torch, collective_communication_algorithms_amd as c; "
+            "t = [torch.ones(1 << 16, device='cuda:0') for _ in range(8)]; "
+            "c.coll_allreduce(t, algo='auto'); c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); "
+            "torch.cuda.synchronize(); print(float(t[0][0]))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=120,
+                       env=dict(os.environ, COLL_DEBUG="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("coll: ")]
+    assert len(lines) == 2, r.stderr[-2000:]
+    assert lines[0].startswith("coll: allreduce algo ") and "auto" not in lines[0] and "| rows" in lines[0]
+    assert lines[1].startswith("coll: alltoall algo bruck") and "| perm" in lines[1]
+    assert r.stdout.strip() == "8.0"
