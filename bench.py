@@ -32,11 +32,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_kernel_ring_allreduc
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code (comments and blank space removed), so
-    that the committed counter summary is dropped whenever the kernels change."""
+    """Hash of the code (comments and blank space removed) that decides what the
+    row kernel does: the kernels and their launch shapes and work lists, so
+    that the committed counter summary is dropped whenever any of it changes."""
     import re
     h = hashlib.sha256()
-    for f in ("kernels.hip", "device_types.h"):
+    for f in ("kernels.hip", "device_types.h", "abi.cpp", "bind.cpp"):
         with open(os.path.join(ROOT, "collective_communication_algorithms_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)

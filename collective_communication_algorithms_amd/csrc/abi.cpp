@@ -108,7 +108,7 @@ struct KeyHash {
 struct DevList {                // work lists of one row phase for one launch shape
   size_t phase = 0;
   uint32_t G = 0, gt = 0;
-  bool reverse = false, per_step = false;
+  bool reverse = false, per_step = false, group_major = false;
   uint32_t launches = 0;
   bool fine = false;            // small pieces: launch the row kernel's fine variant
   uint32_t* d_off = nullptr;
@@ -207,9 +207,11 @@ coll_status_t trim_cache(const Entry* keep) {
 }
 
 // The work lists of phase `pi` for this launch shape, built and uploaded on first use.
-coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool reverse, bool per_step, DevList*& out) {
+coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool reverse, bool per_step, bool group_major,
+                       DevList*& out) {
   for (DevList& l : e.lists)
-    if (l.phase == pi && l.G == G && l.gt == gt && l.reverse == reverse && l.per_step == per_step) {
+    if (l.phase == pi && l.G == G && l.gt == gt && l.reverse == reverse && l.per_step == per_step &&
+        l.group_major == group_major) {
       out = &l;
       return COLL_OK;
     }
@@ -226,13 +228,14 @@ coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool revers
   std::vector<uint32_t> off;
   std::vector<DevItem> list;
   const Phase& ph = e.bound.phases[pi];
-  build_worklist(e.bound, ph, G, gt, reverse, per_step, off, list);
+  build_worklist(e.bound, ph, G, gt, reverse, per_step, group_major, off, list);
   DevList l;
   l.phase = pi;
   l.G = G;
   l.gt = gt;
   l.reverse = reverse;
   l.per_step = per_step;
+  l.group_major = group_major;
   l.launches = per_step ? ph.s1 - ph.s0 : 1;
   // the fine variant pays off when pieces are small: some runs, or pieces of
   // less than one tile on average
@@ -483,14 +486,49 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       uint64_t cap = step_mode ? 4 * resident : resident;
       uint32_t gt = blocked ? (has_reduce ? BLOCKED_GROUP_TILES_REDUCE : BLOCKED_GROUP_TILES_COPY)
                             : pick_group_tiles(ph.colspace, resident);
-      if (blocked) cap = uint64_t(1) << 20;
+      if (blocked) {
+        cap = uint64_t(1) << 20;
+        // 4-byte reductions over few ranks: a resident grid whose work groups
+        // take their groups one at a time (group-major lists) keeps the data
+        // in flight small enough for the caches.  A group averaging two or
+        // more pieces per step (halving-doubling, tree): 4-tile groups, 2 work
+        // groups per CU; one piece per step (Ring): 8-tile groups, 3 per CU
+        // once that gives every work group at least two groups, else 2 per CU
+        // (8 x 32 MiB: 1,024 groups on 768 work groups leave a third of them
+        // twice the work, 164 us against 150 on 512).  Grids are whole
+        // multiples of the CU count (2.5 per CU measured 10 % slower) and group
+        // sizes powers of two (11-tile groups, which would spread the columns
+        // evenly over 768 work groups, measured 12-16 % slower).  Measured at
+        // 8 x 256 MiB fp32 against one group per work group: DBT 1.158 ->
+        // 1.040 ms, RHD 1.207 -> 1.066, Ring 1.164 -> 1.130, Reduce 0.683 ->
+        // 0.655; bf16 and 64-rank schedules were as fast or faster with one
+        // group per work group, so they keep it.
+        if (has_reduce && sz == 4 && N <= 16 && opt_group.load() == 0) {
+          const uint64_t gb = uint64_t(gt) * TILE_BYTES;
+          uint64_t pieces = 0;
+          for (uint32_t s = ph.s0; s < ph.s1; ++s)
+            for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+              const DevItem& it = b.items[b.steps[s].item0 + i];
+              if (it.col1 > it.col0) pieces += (it.col1 - 1) / gb - it.col0 / gb + 1;
+            }
+          const uint64_t groups = (ph.colspace + gb - 1) / gb;
+          const bool multi = pieces >= 2 * groups * uint64_t(ph.s1 - ph.s0);
+          if (multi) {
+            cap = uint64_t(di->cus) * 2u;
+          } else {
+            gt = 8;
+            const uint64_t g8 = (ph.colspace + 8 * TILE_BYTES - 1) / (8 * TILE_BYTES);
+            cap = uint64_t(di->cus) * (g8 >= 6 * uint64_t(di->cus) ? 3u : 2u);
+          }
+        }
+      }
       if (opt_group.load() > 0) gt = uint32_t(opt_group.load());
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
       const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
       const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
       const uint32_t grid = uint32_t(std::min(groups, cap));
       DevList* L = nullptr;
-      st = get_list(*e, pi, grid, gt, opt_reverse.load() != 0, step_mode, L);
+      st = get_list(*e, pi, grid, gt, opt_reverse.load() != 0, step_mode, blocked, L);
       if (st != COLL_OK) return st;
       RowsArgs a{};
       a.list = L->d_list;

@@ -260,37 +260,40 @@ uint32_t wave_mask(const DevItem& x) {
 }
 
 void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
-                    bool per_step, std::vector<uint32_t>& off, std::vector<DevItem>& list) {
+                    bool per_step, bool group_major, std::vector<uint32_t>& off, std::vector<DevItem>& list) {
   const uint64_t gbytes = uint64_t(group_tiles) * TILE_BYTES;
   const uint32_t launches = per_step ? ph.s1 - ph.s0 : 1;
   off.clear();
   list.clear();
-  std::vector<std::vector<DevItem>> per(G);
-  // per work group: the entries of its current run (indices into per[w]) and the run's step
-  std::vector<std::vector<size_t>> run(G);
-  std::vector<uint32_t> run_step(G, ~0u);
+  struct Piece {
+    uint64_t group;
+    uint32_t step;
+    DevItem it;
+  };
+  std::vector<std::vector<Piece>> raw(G);
+  std::vector<DevItem> per;
+  // the entries of the current run (indices into per) and the run's step
+  std::vector<size_t> run;
+  uint32_t run_step = ~0u;
   auto one_tile = [](const DevItem& x) { return x.col0 / TILE_BYTES == (x.col1 - 1) / TILE_BYTES; };
-  auto push = [&](uint32_t w, uint32_t s, const DevItem& q) {
-    std::vector<DevItem>& P = per[w];
-    std::vector<size_t>& R = run[w];
-    bool join = !R.empty() && run_step[w] == s && R.size() < RUN_MAX && one_tile(q) && one_tile(P[R.back()]);
-    for (size_t i = 0; join && i < R.size(); ++i) {
-      const DevItem& p = P[R[i]];
+  auto push = [&](uint32_t s, const DevItem& q) {
+    bool join = !run.empty() && run_step == s && run.size() < RUN_MAX && one_tile(q) && one_tile(per[run.back()]);
+    for (size_t i = 0; join && i < run.size(); ++i) {
+      const DevItem& p = per[run[i]];
       // two accumulations into the same bytes must stay one after the other
       if (p.dst_rank == q.dst_rank && p.col0 < q.col1 && q.col0 < p.col1) join = false;
     }
     if (join) {
-      P[R.back()].flags |= ITEM_BATCH_NEXT;
-      R.push_back(P.size());
+      per[run.back()].flags |= ITEM_BATCH_NEXT;
+      run.push_back(per.size());
     } else {
-      R.assign(1, P.size());
-      run_step[w] = s;
+      run.assign(1, per.size());
+      run_step = s;
     }
-    P.push_back(q);
+    per.push_back(q);
   };
   for (uint32_t j = 0; j < launches; ++j) {
-    for (auto& v : per) v.clear();
-    for (auto& v : run) v.clear();
+    for (auto& v : raw) v.clear();
     const uint32_t sa = per_step ? ph.s0 + j : ph.s0, sb = per_step ? sa + 1 : ph.s1;
     for (uint32_t s = sa; s < sb; ++s) {
       const DevStep& st = b.steps[s];
@@ -309,13 +312,23 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
           if (per_step && rev) owner = G - 1 - owner;
           piece.flags &= ~uint32_t(ITEM_BATCH_NEXT);
           piece.pad = wave_mask(piece);
-          push(owner, s, piece);
+          raw[owner].push_back({g, s, piece});
         }
       }
     }
     for (uint32_t w = 0; w < G; ++w) {
+      // group-major: a work group takes each of its column groups through every
+      // step before the next group (the columns of different groups never
+      // meet, so any interleaving of groups is correct); step-major: every
+      // group one step at a time
+      if (group_major)
+        std::stable_sort(raw[w].begin(), raw[w].end(), [](const Piece& x, const Piece& y) { return x.group < y.group; });
+      per.clear();
+      run.clear();
+      run_step = ~0u;
+      for (const Piece& p : raw[w]) push(p.step, p.it);
       off.push_back(uint32_t(list.size()));
-      list.insert(list.end(), per[w].begin(), per[w].end());
+      list.insert(list.end(), per.begin(), per.end());
     }
     off.push_back(uint32_t(list.size()));
   }

@@ -40,12 +40,16 @@ Bound bind_schedule(const Schedule& s, int elem_size, bool inplace);
 //  one launch per step (per_step true): the same, except that with `reverse`
 //    odd steps hand group g to work group G-1-(g mod G), which reverses the
 //    order groups are dispatched in (the launches order the steps).
-// A list keeps step order and row order; with `reverse`, odd steps are listed
-// back to front (items too, unless the step accumulates several rows into one
-// destination).  Launch j gives work group w the pieces
-// off[j*(G+1) + w] .. off[j*(G+1) + w + 1] of `list`.
+// A list keeps step order and row order within each column group; with
+// `reverse`, odd steps are listed back to front (items too, unless the step
+// accumulates several rows into one destination).  `group_major` lists a work
+// group's groups one after the other, each through all its steps (its
+// columns' data stays cached from one step to the next); otherwise all its
+// groups go step by step.  Launch j gives work group w the pieces
+// off[j*(G+1) + w] .. off[j*(G+1) + w + 1] of `list`.  Runs (ITEM_BATCH_NEXT)
+// are marked on the final order.
 void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
-                    bool per_step, std::vector<uint32_t>& off, std::vector<DevItem>& list);
+                    bool per_step, bool group_major, std::vector<uint32_t>& off, std::vector<DevItem>& list);
 
 // The regions of rank i's receive buffer whose final value the collective
 // defines (element ranges).

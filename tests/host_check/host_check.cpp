@@ -7,9 +7,10 @@
 //   * build_schedule accepts the arguments and check_schedule finds no hazard;
 //   * bind_schedule: per row, the items of a row-kernel step cover the row's
 //     destination bytes exactly once;
-//   * build_worklist, for several launch shapes: the pieces of every item
-//     cover its columns exactly once, each piece lies inside one column group
-//     and sits in its owner's list, each list is in step order, the wave mask
+//   * build_worklist, for several launch shapes, step-major and group-major:
+//     the pieces of every item cover its columns exactly once, each piece lies
+//     inside one column group and sits in its owner's list, each group's
+//     pieces are in step order (group-major lists: groups in order), the wave mask
 //     is the set of waves whose bytes the piece touches, and every
 //     ITEM_BATCH_NEXT run has at most RUN_MAX members of one step, each inside
 //     one tile, with no two members writing common bytes of one rank.
@@ -75,10 +76,11 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
     for (uint32_t G : {1u, 3u, 257u})
       for (uint32_t gt : {1u, 4u})
         for (int rev = 0; rev < 2; ++rev)
-          for (int per_step = 0; per_step < 2; ++per_step) {
+          for (int per_step = 0; per_step < 2; ++per_step)
+            for (int gm = 0; gm < 2; ++gm) {
             std::vector<uint32_t> off;
             std::vector<DevItem> list;
-            build_worklist(b, ph, G, gt, rev != 0, per_step != 0, off, list);
+            build_worklist(b, ph, G, gt, rev != 0, per_step != 0, gm != 0, off, list);
             ++nlists;
             const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
             const uint32_t launches = per_step ? ph.s1 - ph.s0 : 1;
@@ -102,7 +104,8 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
                 const uint32_t a = off[size_t(j) * (G + 1) + w], z = off[size_t(j) * (G + 1) + w + 1];
                 CHECK(a <= z && z <= list.size(), "%s: list bounds", name(sh).c_str());
                 if (!(a <= z && z <= list.size())) continue;
-                uint32_t last_step = 0;
+                std::map<uint64_t, uint32_t> last_step;   // per column group
+                uint64_t last_group = 0;
                 for (uint32_t e = a; e < z; ++e) {
                   const DevItem& p = list[e];
                   CHECK(p.col0 < p.col1, "%s: empty piece", name(sh).c_str());
@@ -118,8 +121,12 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
                   uint32_t owner = uint32_t(g % G);
                   if (per_step && rev && (ps & 1u)) owner = G - 1 - owner;
                   CHECK(owner == w, "%s: piece of step %u in the wrong list", name(sh).c_str(), ps);
-                  CHECK(ps >= last_step, "%s: list not in step order", name(sh).c_str());
-                  last_step = ps;
+                  CHECK(ps >= last_step[g], "%s: a group's pieces not in step order", name(sh).c_str());
+                  last_step[g] = ps;
+                  if (gm) {
+                    CHECK(g >= last_group, "%s: group-major list not in group order", name(sh).c_str());
+                    last_group = g;
+                  }
                   std::vector<int64_t> key{int64_t(ps), p.row, p.src_rank, p.dst_rank, p.src_delta, p.dst_delta,
                                            int64_t(p.flags & ~uint32_t(ITEM_BATCH_NEXT))};
                   got[key].push_back({p.col0, p.col1});
