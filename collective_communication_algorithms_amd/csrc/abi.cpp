@@ -107,7 +107,8 @@ struct KeyHash {
 
 struct DevList {                // work lists of one row phase for one launch shape
   size_t phase = 0;
-  uint32_t G = 0, gt = 0;
+  uint64_t cap = 0;             // grid cap asked for
+  uint32_t G = 0, gt = 0;       // grid used, group tiles
   bool reverse = false, per_step = false, group_major = false;
   uint32_t launches = 0;
   bool fine = false;            // small pieces: launch the row kernel's fine variant
@@ -206,11 +207,19 @@ coll_status_t trim_cache(const Entry* keep) {
   return st;
 }
 
-// The work lists of phase `pi` for this launch shape, built and uploaded on first use.
-coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool reverse, bool per_step, bool group_major,
+// The work lists of phase `pi` for a grid of at most `cap` work groups and
+// column groups of `gt` tiles, built and uploaded on first use.  The grid is
+// one work group per column group while that fits in `cap`, else `cap`.  When
+// each group has a work group of its own, groups are also split at the rows'
+// boundaries (group_cuts): a group holding the end of one row and the start of
+// the next would make its work group run both rows' chains of pieces one after
+// the other, twice the round trips of any other work group (8 x 64 MiB uint8
+// Broadcast in 13 chunks: 160 -> 138 us).  With several groups per work group
+// a split adds as many pieces to some list as it saves, so there it is not done.
+coll_status_t get_list(Entry& e, size_t pi, uint64_t cap, uint32_t gt, bool reverse, bool per_step, bool group_major,
                        DevList*& out) {
   for (DevList& l : e.lists)
-    if (l.phase == pi && l.G == G && l.gt == gt && l.reverse == reverse && l.per_step == per_step &&
+    if (l.phase == pi && l.cap == cap && l.gt == gt && l.reverse == reverse && l.per_step == per_step &&
         l.group_major == group_major) {
       out = &l;
       return COLL_OK;
@@ -228,9 +237,15 @@ coll_status_t get_list(Entry& e, size_t pi, uint32_t G, uint32_t gt, bool revers
   std::vector<uint32_t> off;
   std::vector<DevItem> list;
   const Phase& ph = e.bound.phases[pi];
-  build_worklist(e.bound, ph, G, gt, reverse, per_step, group_major, off, list);
+  const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
+  const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
+  std::vector<uint64_t> cuts = group_cuts(ph, gbytes);
+  if (groups + cuts.size() > cap) cuts.clear();
+  const uint32_t G = uint32_t(std::min(groups + cuts.size(), cap));
+  build_worklist(e.bound, ph, G, gt, reverse, per_step, group_major, cuts, off, list);
   DevList l;
   l.phase = pi;
+  l.cap = cap;
   l.G = G;
   l.gt = gt;
   l.reverse = reverse;
@@ -488,7 +503,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
                             : pick_group_tiles(ph.colspace, resident);
       if (blocked) {
         cap = uint64_t(1) << 20;
-        // 4-byte reductions over few ranks: a resident grid whose work groups
+        // fp32 / int32 / bf16 reductions: a resident grid whose work groups
         // take their groups one at a time (group-major lists) keeps the data
         // in flight small enough for the caches.  A group averaging two or
         // more pieces per step (halving-doubling, tree): 4-tile groups, 2 work
@@ -501,9 +516,11 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         // evenly over 768 work groups, measured 12-16 % slower).  Measured at
         // 8 x 256 MiB fp32 against one group per work group: DBT 1.158 ->
         // 1.040 ms, RHD 1.207 -> 1.066, Ring 1.164 -> 1.130, Reduce 0.683 ->
-        // 0.655; bf16 and 64-rank schedules were as fast or faster with one
-        // group per work group, so they keep it.
-        if (has_reduce && sz == 4 && N <= 16 && opt_group.load() == 0) {
+        // 0.655; bf16: DBT 1.130 -> 1.055, RHD 1.182 -> 1.081, Ring 1.190 ->
+        // 1.151; bf16 64 x 256 MiB ReduceScatter: RHD 7.06 -> 6.81 ms, Ring
+        // 6.85 -> 6.79.  uint8 reductions are not measured and keep one group
+        // per work group.
+        if (has_reduce && sz >= 2 && opt_group.load() == 0) {
           const uint64_t gb = uint64_t(gt) * TILE_BYTES;
           uint64_t pieces = 0;
           for (uint32_t s = ph.s0; s < ph.s1; ++s)
@@ -524,12 +541,10 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       }
       if (opt_group.load() > 0) gt = uint32_t(opt_group.load());
       if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
-      const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
-      const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
-      const uint32_t grid = uint32_t(std::min(groups, cap));
       DevList* L = nullptr;
-      st = get_list(*e, pi, grid, gt, opt_reverse.load() != 0, step_mode, blocked, L);
+      st = get_list(*e, pi, std::max<uint64_t>(cap, 1), gt, opt_reverse.load() != 0, step_mode, blocked, L);
       if (st != COLL_OK) return st;
+      const uint32_t grid = L->G;
       RowsArgs a{};
       a.list = L->d_list;
       a.sums = t_sums;

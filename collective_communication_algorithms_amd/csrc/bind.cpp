@@ -242,6 +242,17 @@ Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
     p.colspace = rows_cols;
     b.phases.push_back(p);
   }
+  for (Phase& p : b.phases) {
+    if (p.kind != Phase::ROWS) continue;
+    for (uint32_t s = p.s0; s < p.s1; ++s)
+      for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+        const DevItem& it = b.items[b.steps[s].item0 + i];
+        for (uint64_t c : {it.col0, it.col1})
+          if (c > 0 && c < p.colspace) p.bounds.push_back(c);
+      }
+    std::sort(p.bounds.begin(), p.bounds.end());
+    p.bounds.erase(std::unique(p.bounds.begin(), p.bounds.end()), p.bounds.end());
+  }
   return b;
 }
 
@@ -259,8 +270,16 @@ uint32_t wave_mask(const DevItem& x) {
   return m;
 }
 
+std::vector<uint64_t> group_cuts(const Phase& ph, uint64_t gbytes) {
+  std::vector<uint64_t> cuts;
+  for (uint64_t c : ph.bounds)
+    if (c % gbytes) cuts.push_back(c);
+  return cuts;
+}
+
 void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
-                    bool per_step, bool group_major, std::vector<uint32_t>& off, std::vector<DevItem>& list) {
+                    bool per_step, bool group_major, const std::vector<uint64_t>& cuts, std::vector<uint32_t>& off,
+                    std::vector<DevItem>& list) {
   const uint64_t gbytes = uint64_t(group_tiles) * TILE_BYTES;
   const uint32_t launches = per_step ? ph.s1 - ph.s0 : 1;
   off.clear();
@@ -271,6 +290,7 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
     DevItem it;
   };
   std::vector<std::vector<Piece>> raw(G);
+  std::vector<Piece> cut;  // pieces of one item
   std::vector<DevItem> per;
   // the entries of the current run (indices into per) and the run's step
   std::vector<size_t> run;
@@ -302,17 +322,27 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
       for (uint32_t n = 0; n < st.nitems; ++n) {
         const DevItem& it = b.items[st.item0 + (back ? st.nitems - 1 - n : n)];
         if (it.col1 <= it.col0) continue;
-        const uint64_t g0 = it.col0 / gbytes, g1 = (it.col1 - 1) / gbytes;
-        for (uint64_t k = 0; k <= g1 - g0; ++k) {
-          const uint64_t g = rev ? g1 - k : g0 + k;
+        // group of column c: its tile group plus the cuts at or below c
+        size_t ci = size_t(std::upper_bound(cuts.begin(), cuts.end(), it.col0) - cuts.begin());
+        cut.clear();
+        for (uint64_t c0 = it.col0; c0 < it.col1;) {
+          const uint64_t q = c0 / gbytes;
+          uint64_t c1 = std::min(it.col1, (q + 1) * gbytes);
+          if (ci < cuts.size() && cuts[ci] < c1) c1 = cuts[ci];
           DevItem piece = it;
-          piece.col0 = std::max(it.col0, g * gbytes);
-          piece.col1 = std::min(it.col1, (g + 1) * gbytes);
-          uint32_t owner = uint32_t(g % G);
+          piece.col0 = c0;
+          piece.col1 = c1;
+          cut.push_back({q + ci, s, piece});
+          c0 = c1;
+          while (ci < cuts.size() && cuts[ci] <= c0) ++ci;
+        }
+        for (size_t k = 0; k < cut.size(); ++k) {
+          Piece p = cut[rev ? cut.size() - 1 - k : k];
+          uint32_t owner = uint32_t(p.group % G);
           if (per_step && rev) owner = G - 1 - owner;
-          piece.flags &= ~uint32_t(ITEM_BATCH_NEXT);
-          piece.pad = wave_mask(piece);
-          raw[owner].push_back({g, s, piece});
+          p.it.flags &= ~uint32_t(ITEM_BATCH_NEXT);
+          p.it.pad = wave_mask(p.it);
+          raw[owner].push_back(p);
         }
       }
     }

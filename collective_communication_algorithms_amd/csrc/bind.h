@@ -14,6 +14,7 @@ struct Phase {
   enum Kind { ROWS, PERM } kind = ROWS;
   uint32_t s0 = 0, s1 = 0;     // DevStep range
   uint64_t colspace = 0;       // ROWS: largest column byte; PERM: block bytes
+  std::vector<uint64_t> bounds;  // ROWS: columns in (0, colspace) where a row starts or ends, sorted
 };
 
 struct Bound {
@@ -31,9 +32,17 @@ struct Bound {
 // send to receive in the first step.
 Bound bind_schedule(const Schedule& s, int elem_size, bool inplace);
 
+// The row boundaries of a phase that fall inside column groups of `gbytes`
+// bytes (sorted).
+std::vector<uint64_t> group_cuts(const Phase& ph, uint64_t gbytes);
+
 // Work lists of one row phase on a grid of G work groups, with column groups
-// of `group_tiles` 4 KiB tiles.  Every item is cut at group boundaries and
-// each piece goes to the list of the work group that owns its group.
+// of `group_tiles` 4 KiB tiles, each group that a column of `cuts` (sorted)
+// falls inside split there in two; groups are numbered in column order.  With
+// the cuts of group_cuts, no group holds two rows that end or start inside it,
+// so a group never has two chains of pieces to run one after the other.
+// Every item is cut at group boundaries and each piece goes to the list of the
+// work group that owns its group.
 //  one launch for the phase (per_step false): group g belongs to work group
 //    g mod G in every step, so each column is only ever touched by one work
 //    group and the steps need no synchronisation between work groups;
@@ -49,7 +58,8 @@ Bound bind_schedule(const Schedule& s, int elem_size, bool inplace);
 // off[j*(G+1) + w] .. off[j*(G+1) + w + 1] of `list`.  Runs (ITEM_BATCH_NEXT)
 // are marked on the final order.
 void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
-                    bool per_step, bool group_major, std::vector<uint32_t>& off, std::vector<DevItem>& list);
+                    bool per_step, bool group_major, const std::vector<uint64_t>& cuts, std::vector<uint32_t>& off,
+                    std::vector<DevItem>& list);
 
 // The regions of rank i's receive buffer whose final value the collective
 // defines (element ranges).

@@ -192,25 +192,73 @@ struct ItemView {
   uint32_t shift;    // (-row start) mod 4
 };
 
+// Element e of a 16-byte unit held in four words (selects, no indexing into
+// registers).
+template <int DT>
+__device__ __forceinline__ uint32_t elem_of(u32x4 v, int e) {
+  constexpr int SZ = elem_size<DT>();
+  const int byte = e * SZ;
+  const uint32_t w = byte < 4 ? v.x : byte < 8 ? v.y : byte < 12 ? v.z : v.w;
+  if constexpr (SZ == 4) return w;
+  else if constexpr (SZ == 2) return (w >> (8 * (byte & 3))) & 0xffffu;
+  else return (w >> (8 * (byte & 3))) & 0xffu;
+}
+
 // One 16-byte column unit x of the item, clipped to [lo, hi).
+//  vec: the unit is 16-byte aligned on every side, so it is loaded whole even
+//    when the row covers it only in part (an aligned 16-byte block never
+//    crosses a page, so the bytes outside the row are as readable as the ones
+//    inside; this thread is the only one that touches the unit in any step, so
+//    nothing else writes them meanwhile); only the row's elements are stored.
+//  otherwise: element by element, in batches of up to 8 whose loads are all
+//    issued before the batch's first store (a store may alias a later load's
+//    address, so a load placed after it would wait a full memory round trip).
 template <int DT, int OP, bool CKS, int NTM>
 __device__ __forceinline__ void do_unit(const ItemView& v, uint64_t x, uint64_t lo, uint64_t hi, bool vec,
                                         uint64_t& acc) {
   if (x + 16 <= lo || x >= hi) return;
-  if (vec && x >= lo && x + 16 <= hi) {
+  constexpr int SZ = elem_size<DT>(), E = 16 / SZ;
+  if (vec) {
     u32x4 s = ld16<(NTM & NT_SRC) != 0>(v.src + x);
     if (v.reduce) s = combine16<DT, OP>(ld16<(NTM & NT_DSRC) != 0>(v.dsrc + x), s);
-    st16<(NTM & NT_DST) != 0>(v.dst + x, s);
-    if constexpr (CKS) acc += words16(s, v.shift * 8u);
+    if (x >= lo && x + 16 <= hi) {
+      st16<(NTM & NT_DST) != 0>(v.dst + x, s);
+      if constexpr (CKS) acc += words16(s, v.shift * 8u);
+      return;
+    }
+    // the row's bytes of this unit: [r0, r1) counted from x
+    const uint32_t r0 = lo > x ? uint32_t(lo - x) : 0u, r1 = hi < x + 16 ? uint32_t(hi - x) : 16u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (uint32_t(e * SZ) >= r0 && uint32_t(e * SZ) < r1) {
+        const uint32_t val = elem_of<DT>(s, e);
+        st_elem<DT>(v.dst + x + e * SZ, val);
+        if constexpr (CKS) acc += uint64_t(val << (8u * ((uint32_t(e * SZ) + v.shift) & 3u)));
+      }
+    }
     return;
   }
-  constexpr int SZ = elem_size<DT>();
-  const uint64_t a0 = x > lo ? x : lo, a1 = x + 16 < hi ? x + 16 : hi;
-  for (uint64_t y = a0; y < a1; y += SZ) {
-    uint32_t s = ld_elem<DT>(v.src + y);
-    if (v.reduce) s = combine_elem<DT, OP>(ld_elem<DT>(v.dsrc + y), s);
-    st_elem<DT>(v.dst + y, s);
-    if constexpr (CKS) acc += uint64_t(s << (8u * uint32_t((y + v.shift) & 3u)));
+  const uint32_t r0 = lo > x ? uint32_t(lo - x) : 0u, r1 = hi < x + 16 ? uint32_t(hi - x) : 16u;
+  constexpr int B = E < 8 ? E : 8;  // elements per batch of loads (bounds the registers held)
+#pragma unroll
+  for (int e0 = 0; e0 < E; e0 += B) {
+    uint32_t s[B], d[B];
+#pragma unroll
+    for (int e = 0; e < B; ++e) {
+      const uint32_t b = uint32_t((e0 + e) * SZ);
+      const bool in = b >= r0 && b < r1;
+      s[e] = in ? ld_elem<DT>(v.src + x + b) : 0u;
+      d[e] = in && v.reduce ? ld_elem<DT>(v.dsrc + x + b) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < B; ++e) {
+      const uint32_t b = uint32_t((e0 + e) * SZ);
+      if (b >= r0 && b < r1) {
+        const uint32_t val = v.reduce ? combine_elem<DT, OP>(d[e], s[e]) : s[e];
+        st_elem<DT>(v.dst + x + b, val);
+        if constexpr (CKS) acc += uint64_t(val << (8u * ((b + v.shift) & 3u)));
+      }
+    }
   }
 }
 
@@ -310,7 +358,7 @@ __device__ __forceinline__ void do_run(const RowsArgs& a, const DevItem (&r)[RUN
         st16<(NTM & NT_DST) != 0>(v.dst + x, y);
         if constexpr (CKS) acc += words16(y, v.shift * 8u);
       } else {
-        do_unit<DT, OP, CKS, NTM>(v, x, r[k].col0, r[k].col1, false, acc);
+        do_unit<DT, OP, CKS, NTM>(v, x, r[k].col0, r[k].col1, a.bases16 && (r[k].flags & ITEM_VEC), acc);
       }
       if constexpr (CKS) add_row_sum(a.sums, r[k].row, acc);
     }

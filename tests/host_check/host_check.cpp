@@ -7,9 +7,11 @@
 //   * build_schedule accepts the arguments and check_schedule finds no hazard;
 //   * bind_schedule: per row, the items of a row-kernel step cover the row's
 //     destination bytes exactly once;
-//   * build_worklist, for several launch shapes, step-major and group-major:
-//     the pieces of every item cover its columns exactly once, each piece lies
-//     inside one column group and sits in its owner's list, each group's
+//   * build_worklist, for several launch shapes, step-major and group-major,
+//     with uniform column groups and with groups split at the rows' boundaries
+//     (group_cuts): the pieces of every item cover its columns exactly once,
+//     each piece lies inside one column group and sits in its owner's list,
+//     with split groups every row boundary is a group boundary, each group's
 //     pieces are in step order (group-major lists: groups in order), the wave mask
 //     is the set of waves whose bytes the piece touches, and every
 //     ITEM_BATCH_NEXT run has at most RUN_MAX members of one step, each inside
@@ -77,12 +79,44 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
       for (uint32_t gt : {1u, 4u})
         for (int rev = 0; rev < 2; ++rev)
           for (int per_step = 0; per_step < 2; ++per_step)
-            for (int gm = 0; gm < 2; ++gm) {
+            for (int gm = 0; gm < 2; ++gm)
+              for (int snap = 0; snap < (gm && !per_step ? 2 : 1); ++snap) {
             std::vector<uint32_t> off;
             std::vector<DevItem> list;
-            build_worklist(b, ph, G, gt, rev != 0, per_step != 0, gm != 0, off, list);
-            ++nlists;
             const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
+            std::vector<uint64_t> cuts;
+            if (snap) {
+              cuts = group_cuts(ph, gbytes);
+              // the cuts: exactly the row boundaries strictly inside a group, sorted, once each
+              std::vector<uint64_t> want_cuts;
+              for (uint32_t s = ph.s0; s < ph.s1; ++s)
+                for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+                  const DevItem& it = b.items[b.steps[s].item0 + i];
+                  if (it.col1 <= it.col0) continue;
+                  for (uint64_t c : {it.col0, it.col1})
+                    if (c % gbytes && c < ph.colspace) want_cuts.push_back(c);
+                }
+              std::sort(want_cuts.begin(), want_cuts.end());
+              want_cuts.erase(std::unique(want_cuts.begin(), want_cuts.end()), want_cuts.end());
+              CHECK(cuts == want_cuts, "%s: group cuts", name(sh).c_str());
+            }
+            // group of a column: its tile group plus the cuts at or below it
+            auto group_of = [&](uint64_t c) {
+              return c / gbytes + uint64_t(std::upper_bound(cuts.begin(), cuts.end(), c) - cuts.begin());
+            };
+            // split groups: every row boundary is a group boundary
+            if (snap)
+              for (uint32_t s = ph.s0; s < ph.s1; ++s)
+                for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+                  const DevItem& it = b.items[b.steps[s].item0 + i];
+                  if (it.col1 <= it.col0) continue;
+                  for (uint64_t c : {it.col0, it.col1})
+                    if (c > 0 && c < ph.colspace)
+                      CHECK(group_of(c - 1) != group_of(c), "%s: row boundary %llu inside a group", name(sh).c_str(),
+                            (unsigned long long)c);
+                }
+            build_worklist(b, ph, G, gt, rev != 0, per_step != 0, gm != 0, cuts, off, list);
+            ++nlists;
             const uint32_t launches = per_step ? ph.s1 - ph.s0 : 1;
             CHECK(off.size() == size_t(launches) * (G + 1), "%s: offsets", name(sh).c_str());
             if (off.size() != size_t(launches) * (G + 1)) continue;
@@ -109,8 +143,8 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
                 for (uint32_t e = a; e < z; ++e) {
                   const DevItem& p = list[e];
                   CHECK(p.col0 < p.col1, "%s: empty piece", name(sh).c_str());
-                  const uint64_t g = p.col0 / gbytes;
-                  CHECK((p.col1 - 1) / gbytes == g, "%s: piece crosses a group", name(sh).c_str());
+                  const uint64_t g = group_of(p.col0);
+                  CHECK(group_of(p.col1 - 1) == g, "%s: piece crosses a group", name(sh).c_str());
                   CHECK(p.pad == mask_of(p.col0, p.col1), "%s: wave mask %u vs %u", name(sh).c_str(), p.pad,
                         mask_of(p.col0, p.col1));
                   // step of the piece: its row's step (copies of undefined-by-rows output: step 0)

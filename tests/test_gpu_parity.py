@@ -232,6 +232,30 @@ def test_launch_shapes(exec_mode, group_tiles, max_grid, reverse):
     assert_parity("broadcast", "binomial_pipe", si.rank_arrays(2, 8, 300001, "uint8"), "uint8", k=8)
 
 
+@pytest.mark.parametrize("dtype", ["uint8", "bfloat16", "float32", "int32"])
+@pytest.mark.parametrize("kind,algo,N,count,k", [
+    ("broadcast", "chain_pipe", 8, (1 << 20) + 7, 13),
+    ("broadcast", "bidir_ring", 8, (1 << 20) + 3, 9),
+    ("allreduce", "ring", 8, 8 * 65536 + 77, 1),
+    ("allreduce", "dbt", 8, 8 * 65536 + 13, 1),
+    ("reducescatter", "ring", 5, 5 * 40000 + 3, 1),
+    ("allgather", "ring", 7, 7 * 30000 + 5, 1),
+])
+def test_groups_split_at_row_boundaries(kind, algo, N, count, k, dtype):
+    """Row boundaries that fall inside 16-byte units, at sizes where every column
+    group gets a work group of its own, so the groups are split at those
+    boundaries and two work groups write the two sides of one unit.  Three calls
+    in a row, each bit for bit against the oracle (with row checksums)."""
+    if kind in ("allreduce", "reducescatter") and dtype == "uint8":
+        pytest.skip("uint8 is a data-movement type here")
+    a = si.rank_arrays(17, N, count, dtype, sigma=0.02 if dtype == "bfloat16" else 1.0)
+    sz = np.dtype(np.uint16 if dtype == "bfloat16" else dtype).itemsize
+    chunks = k if kind == "broadcast" else 2 if algo == "dbt" else N
+    assert any((c * count // chunks) * sz % 16 for c in range(1, chunks)), "no boundary inside a unit"
+    for _ in range(3):
+        assert_parity(kind, algo, a, dtype, root=2 % N, k=k, checksums=True)
+
+
 @pytest.mark.parametrize("nt", list(range(-1, 8)))
 def test_nontemporal_switch(nt):
     import collective_communication_algorithms_amd as coll
