@@ -52,10 +52,15 @@ const char* algo_name(coll_algo_t a) {
 // steps when accessed normally; larger ones stream, and then nontemporal source
 // loads (whose data is consumed once per step) keep the cache for the stores
 // the next step reads back.  Measured on the Ring / Halving-Doubling / tree
-// AllReduce, Broadcast and ReduceScatter / AllGather sweeps.
+// AllReduce, Broadcast and ReduceScatter / AllGather sweeps.  AllToAll never
+// reads back what it writes, so there the stores are nontemporal too (32 x
+// 128 MiB bf16 Pairwise 1.67 -> 1.61 ms; the Bruck rounds are unchanged).
 constexpr uint64_t CACHE_RESIDENT_BYTES = uint64_t(256) << 20;
 
-uint32_t auto_nt(uint64_t footprint) { return footprint <= CACHE_RESIDENT_BYTES ? 0u : NT_SRC; }
+uint32_t auto_nt(uint64_t footprint, bool alltoall) {
+  if (footprint <= CACHE_RESIDENT_BYTES) return 0u;
+  return alltoall ? (NT_SRC | NT_DST) : NT_SRC;
+}
 
 
 coll_status_t fail(coll_status_t st, const std::string& msg) {
@@ -467,7 +472,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (he != hipSuccess) return hip_fail(he, "checksum clear");
   }
   const uint64_t footprint = uint64_t(N) * uint64_t(count) * uint64_t(sz) * (inplace ? 1u : 2u);
-  const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint) : uint32_t(opt_nt.load());
+  const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint, kind == COLL_K_ALLTOALL) : uint32_t(opt_nt.load());
   const bool step_mode = opt_exec.load() == 1;
 
   RankPtrs ptrs;

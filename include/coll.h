@@ -216,15 +216,24 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          no synchronisation between work groups.
  *                          1: one launch per step (the launches order the steps).
  * COLL_OPT_GROUP_TILES     4 KiB column tiles per work-group column group, 1..64
- *                          [0: automatic: for column spaces of 32 MiB or more one
- *                          group per work group, 4 tiles with reduce rows and 8
- *                          without; smaller ones up to 8 tiles over a grid of the
- *                          work groups that fit on the device at once].
+ *                          [0: automatic.  Column spaces of 32 MiB or more:
+ *                          int32 / fp32 / bf16 reductions use 4-tile groups on
+ *                          2 work groups per CU (schedules whose groups see two
+ *                          or more rows per step) or 8-tile groups on 3 per CU
+ *                          (2 when that leaves a work group a single group),
+ *                          each work group taking its groups one at a time;
+ *                          other schedules one group per work group, 8 tiles
+ *                          (4 with reduce rows).  Smaller column spaces: up to 8
+ *                          tiles over a grid of the work groups that fit on the
+ *                          device at once.  Whenever every group has a work
+ *                          group of its own, groups are also split where a row
+ *                          starts or ends inside them].
  * COLL_OPT_MAX_GRID        cap on work groups per launch, up to 2^20 [0: automatic].
  * COLL_OPT_NONTEMPORAL     bit mask of nontemporal accesses: 1 source loads,
  *                          2 old-destination loads, 4 stores; -1: automatic
  *                          [-1]: none while all rank buffers together fit the
- *                          256 MiB memory-side cache, else source loads only.
+ *                          256 MiB memory-side cache, else source loads only
+ *                          (AllToAll: source loads and stores).
  * COLL_OPT_REVERSE         1: odd steps walk their columns backwards, so data
  *                          written last is read first [1]; 0: always forwards.
  * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
