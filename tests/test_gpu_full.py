@@ -76,6 +76,17 @@ def test_allreduce_n8_256MiB(algo, dtype, sigma):
     assert np.linalg.norm(y - y64) / np.linalg.norm(y64) <= (1e-5 if dtype == "float32" else 1e-2)
 
 
+@pytest.mark.parametrize("algo", ["ring", "rhd", "dbt"])
+@pytest.mark.parametrize("dtype,sigma", [("float32", 1.0), ("bfloat16", 0.02), ("int32", 1.0)])
+def test_allreduce_n8_40MiB_ragged(algo, dtype, sigma):
+    """A column space between 32 and 48 MiB with a ragged count: the large-grid
+    launch shapes whose Ring grid has 2 work groups per CU (fewer than 6
+    column groups per CU), on a capped grid with chunk boundaries that fall
+    inside 16-byte units."""
+    count = (40 << 20) // si.ITEMSIZE[dtype] + 3
+    check_sampled("allreduce", algo, 8, count, dtype, 7, sigma=sigma)
+
+
 @pytest.mark.parametrize("algo,k", [("binomial", 1), ("chain_pipe", 1), ("chain_pipe", 8), ("chain_pipe", 13),
                                     ("chain_pipe", 64), ("binomial_pipe", 1), ("binomial_pipe", 8),
                                     ("binomial_pipe", 64), ("bidir_ring", 1), ("bidir_ring", 8),
