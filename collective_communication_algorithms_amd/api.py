@@ -26,6 +26,13 @@ def _dtype_name(t) -> str:
         raise CollError(_lib.COLL_ERR_INVALID_ARG, f"unsupported dtype {t.dtype}") from None
 
 
+def _code(table, name, what):
+    try:
+        return table[name]
+    except (KeyError, TypeError):
+        raise CollError(_lib.COLL_ERR_INVALID_ARG, f"unknown {what} {name!r}") from None
+
+
 def _ptr_array(tensors):
     arr = (ctypes.c_void_p * len(tensors))()
     for i, t in enumerate(tensors):
@@ -53,20 +60,23 @@ def _check_tensors(send, recv):
 
 def _stream_handle(device, stream):
     import torch
+    idx = device.index if isinstance(device, torch.device) else int(device)
     if stream is None:
-        idx = device.index if isinstance(device, torch.device) else int(device)
         raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)   # skips building a Stream object
         return ctypes.c_void_p(raw(idx) if raw is not None else torch.cuda.current_stream(idx).cuda_stream)
+    if getattr(stream, "device_index", idx) != idx:
+        raise CollError(_lib.COLL_ERR_INVALID_ARG, "the stream belongs to another device than the rank buffers")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
 def _collective(name, send, recv, op, algo, root, chunks, stream):
     import torch
+    op_code, algo_code = _code(OPS, op, "op"), _code(ALGOS, algo, "algorithm")
     _check_tensors(send, recv)
     fn = getattr(_lib.load(), name)
     idx = send[0].get_device()
     args = (_ptr_array(send), _ptr_array(recv) if recv is not None else None, len(send), send[0].numel(),
-            DTYPES[_dtype_name(send[0])], OPS[op], ALGOS[algo], int(root), int(chunks))
+            DTYPES[_dtype_name(send[0])], op_code, algo_code, int(root), int(chunks))
     # the library works on the current device: make it the tensors' one
     if torch._C._cuda_getDevice() == idx:
         st = fn(*args, _stream_handle(idx, stream))
@@ -117,13 +127,12 @@ def coll_plan(kind, algo, nranks, count, dtype, root=0, chunks=1):
     """(rows, counts) of the in-place schedule; rows are tuples
     (step, src, dst, src_off, dst_off, n, reduce, local, from_send, staged)."""
     lib = _lib.load()
+    k, a, d = _code(KINDS, kind, "collective"), _code(ALGOS, algo, "algorithm"), _code(DTYPES, dtype, "dtype")
     n = ctypes.c_size_t(0)
     counts = CollCounts()
-    check(lib.coll_plan(KINDS[kind], ALGOS[algo], nranks, count, DTYPES[dtype], root, chunks, None,
-                        ctypes.byref(n), ctypes.byref(counts)))
+    check(lib.coll_plan(k, a, nranks, count, d, root, chunks, None, ctypes.byref(n), ctypes.byref(counts)))
     rows = (CollRow * max(n.value, 1))()
-    check(lib.coll_plan(KINDS[kind], ALGOS[algo], nranks, count, DTYPES[dtype], root, chunks, rows,
-                        ctypes.byref(n), ctypes.byref(counts)))
+    check(lib.coll_plan(k, a, nranks, count, d, root, chunks, rows, ctypes.byref(n), ctypes.byref(counts)))
     out = [(r.step, r.src, r.dst, r.src_off, r.dst_off, r.n, r.reduce, r.local, r.from_send, r.staged)
            for r in rows[:n.value]]
     return out, {"steps": counts.steps, "rows": counts.rows, "crit_bytes": counts.crit_bytes,
@@ -147,7 +156,7 @@ def coll_set_checksums(sums=None):
 
 
 def coll_set_option(name, value):
-    check(_lib.load().coll_set_option(OPTIONS[name], int(value)))
+    check(_lib.load().coll_set_option(_code(OPTIONS, name, "option"), int(value)))
 
 
 def coll_check(stream=None, device=None):
@@ -164,7 +173,7 @@ def coll_check(stream=None, device=None):
 
 def coll_get_option(name):
     v = ctypes.c_int64(0)
-    check(_lib.load().coll_get_option(OPTIONS[name], ctypes.byref(v)))
+    check(_lib.load().coll_get_option(_code(OPTIONS, name, "option"), ctypes.byref(v)))
     return v.value
 
 

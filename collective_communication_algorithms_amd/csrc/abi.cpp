@@ -124,6 +124,7 @@ struct DevList {                // work lists of one row phase for one launch sh
 
 struct Entry {
   Bound bound;
+  std::vector<int8_t> multi;    // per phase: groups average two or more pieces per step (-1: not known yet)
   int dev = 0;
   DevItem* d_items = nullptr;
   DevStep* d_steps = nullptr;
@@ -508,11 +509,13 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
                             : pick_group_tiles(ph.colspace, resident);
       if (blocked) {
         cap = uint64_t(1) << 20;
-        // fp32 / int32 / bf16 reductions: a resident grid whose work groups
-        // take their groups one at a time (group-major lists) keeps the data
-        // in flight small enough for the caches.  A group averaging two or
-        // more pieces per step (halving-doubling, tree): 4-tile groups, 2 work
-        // groups per CU; one piece per step (Ring): 8-tile groups, 3 per CU
+        // fp32 / int32 / bf16 reductions, and copy-only schedules over 16 or
+        // more ranks whose groups see several pieces per step: a resident grid
+        // whose work groups take their groups one at a time (group-major
+        // lists) keeps the data in flight small enough for the caches.  A
+        // group averaging two or more pieces per step (halving-doubling, tree,
+        // RHD AllGather): 4-tile groups, 2 work groups per CU; a reduction
+        // with one piece per step (Ring): 8-tile groups, 3 per CU
         // once that gives every work group at least two groups, else 2 per CU
         // (8 x 32 MiB: 1,024 groups on 768 work groups leave a third of them
         // twice the work, 164 us against 150 on 512).  Grids are whole
@@ -524,20 +527,30 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         // 0.655; bf16: DBT 1.130 -> 1.055, RHD 1.182 -> 1.081, Ring 1.190 ->
         // 1.151; bf16 64 x 256 MiB ReduceScatter: RHD 7.06 -> 6.81 ms, Ring
         // 6.85 -> 6.79.  uint8 reductions are not measured and keep one group
-        // per work group.
-        if (has_reduce && sz >= 2 && opt_group.load() == 0) {
-          const uint64_t gb = uint64_t(gt) * TILE_BYTES;
-          uint64_t pieces = 0;
-          for (uint32_t s = ph.s0; s < ph.s1; ++s)
-            for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
-              const DevItem& it = b.items[b.steps[s].item0 + i];
-              if (it.col1 > it.col0) pieces += (it.col1 - 1) / gb - it.col0 / gb + 1;
-            }
-          const uint64_t groups = (ph.colspace + gb - 1) / gb;
-          const bool multi = pieces >= 2 * groups * uint64_t(ph.s1 - ph.s0);
-          if (multi) {
+        // per work group.  Copy-only: bf16 RHD AllGather 64 x 256 MiB 6.19 ->
+        // 5.36 ms, 16 x 128 MiB 0.638 -> 0.606; at 8 ranks (RHD AllGather,
+        // binomial Broadcast) within 3 % either way, so they keep one group
+        // per work group, and so do copy schedules with one piece per step
+        // (Ring AllGather 64 x 256 MiB: 4.77 ms, 6.45 on the small grid).
+        const bool reduce_rule = has_reduce && sz >= 2;
+        const bool copy_rule = !has_reduce && N >= 16;
+        if ((reduce_rule || copy_rule) && opt_group.load() == 0) {
+          if (e->multi.size() != b.phases.size()) e->multi.assign(b.phases.size(), int8_t(-1));
+          if (e->multi[pi] < 0) {
+            const uint64_t gb = uint64_t(BLOCKED_GROUP_TILES_REDUCE) * TILE_BYTES;
+            uint64_t pieces = 0;
+            for (uint32_t s = ph.s0; s < ph.s1; ++s)
+              for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+                const DevItem& it = b.items[b.steps[s].item0 + i];
+                if (it.col1 > it.col0) pieces += (it.col1 - 1) / gb - it.col0 / gb + 1;
+              }
+            const uint64_t groups = (ph.colspace + gb - 1) / gb;
+            e->multi[pi] = pieces >= 2 * groups * uint64_t(ph.s1 - ph.s0) ? 1 : 0;
+          }
+          if (e->multi[pi]) {
+            gt = BLOCKED_GROUP_TILES_REDUCE;
             cap = uint64_t(di->cus) * 2u;
-          } else {
+          } else if (reduce_rule) {
             gt = 8;
             const uint64_t g8 = (ph.colspace + 8 * TILE_BYTES - 1) / (8 * TILE_BYTES);
             cap = uint64_t(di->cus) * (g8 >= 6 * uint64_t(di->cus) ? 3u : 2u);

@@ -222,8 +222,10 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          or more rows per step) or 8-tile groups on 3 per CU
  *                          (2 when that leaves a work group a single group),
  *                          each work group taking its groups one at a time;
- *                          other schedules one group per work group, 8 tiles
- *                          (4 with reduce rows).  Smaller column spaces: up to 8
+ *                          copy-only schedules over 16 or more ranks whose
+ *                          groups see two or more rows per step do the same
+ *                          with 4-tile groups on 2 per CU; other schedules one
+ *                          group per work group, 8 tiles (4 with reduce rows).  Smaller column spaces: up to 8
  *                          tiles over a grid of the work groups that fit on the
  *                          device at once.  Whenever every group has a work
  *                          group of its own, groups are also split where a row

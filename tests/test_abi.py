@@ -96,6 +96,26 @@ def test_options_and_strings():
     assert lib.coll_calib_copy(None, None, 16, None) == INV
 
 
+def test_unknown_names_raise_coll_error():
+    """The binding turns an unknown collective, algorithm, op, dtype or option
+    name into CollError(INVALID_ARG), before it looks at any tensor."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    t = [torch.zeros(8)]
+    for kw in ({"op": "product"}, {"algo": "mesh"}, {"op": None}):
+        with pytest.raises(coll.CollError) as e:
+            coll.coll_allreduce(t, **kw)
+        assert e.value.status == INV
+    for args in (("allsum", "ring", 8, 64, "float32"), ("allreduce", "tree", 8, 64, "float32"),
+                 ("allreduce", "ring", 8, 64, "float64")):
+        with pytest.raises(coll.CollError):
+            coll.coll_plan(*args)
+    with pytest.raises(coll.CollError):
+        coll.coll_set_option("grid_size", 1)
+    with pytest.raises(coll.CollError):
+        coll.coll_get_option("grid_size")
+
+
 def test_spin_argument_errors():
     """The stand-in compute kernel rejects bad arguments before any HIP call."""
     lib = _lib.load()
