@@ -260,7 +260,7 @@ def test_dbt_trees_n8_shape():
     assert r2 == 1 and {u: c for u, c in t2.items() if c} == {1: [5], 5: [3, 7], 3: [2, 4], 7: [6, 0]}
 
 
-# --- every plan is hazard free; the checker catches planted conflicts ------------
+# --- every plan is hazard free; the hazard check catches planted conflicts -------
 
 @pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 7, 8, 9, 16, 32])
 def test_all_plans_are_hazard_free(N):
