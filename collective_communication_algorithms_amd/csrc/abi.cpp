@@ -791,6 +791,15 @@ const char* coll_last_error(void) { return t_err.c_str(); }
 
 void coll_finalize(void) {
   std::lock_guard<std::mutex> lock(g_mu);
+  // queued calls may still read the tables: wait for every device that holds some
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  std::vector<int> devs;
+  for (auto& kv : g_cache)
+    if (std::find(devs.begin(), devs.end(), kv.second->dev) == devs.end()) devs.push_back(kv.second->dev);
+  for (int d : devs)
+    if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
+  if (have_cur && !devs.empty()) (void)hipSetDevice(cur);
   for (auto& kv : g_cache) free_entry(*kv.second);
   g_cache.clear();
   g_cache_bytes = 0;

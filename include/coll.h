@@ -273,7 +273,8 @@ coll_status_t coll_check(void* stream);
 
 const char* coll_status_string(coll_status_t status);
 const char* coll_last_error(void);   /* thread-local detail of the last error */
-void coll_finalize(void);            /* frees the schedule cache; call with no work in flight */
+void coll_finalize(void);            /* frees the schedule cache after waiting for every device
+                                        that holds part of it (work queued there finishes first) */
 
 /* ------------------------------------------------------------------------- */
 /* Calibration kernels: plain streams over `bytes` bytes (multiple of 16) for

@@ -409,3 +409,67 @@ def test_debug_lines(gpu_device):
     assert lines[0].startswith("coll: allreduce algo ") and "auto" not in lines[0] and "| rows" in lines[0]
     assert lines[1].startswith("coll: alltoall algo bruck") and "| perm" in lines[1]
     assert r.stdout.strip() == "8.0"
+
+
+def test_concurrent_calls_from_threads():
+    """Four host threads, each with its own stream and buffers, issue calls at
+    the same time (the library serialises its host work; each thread's
+    current stream is its own): every result equals the oracle's."""
+    import threading
+    import torch
+    import collective_communication_algorithms_amd as coll
+    dev = torch.device("cuda:0")
+    cases = [("allreduce", "ring", "float32", 8, 8 * 5000 + 1), ("allreduce", "dbt", "bfloat16", 8, 30011),
+             ("reducescatter", "rhd", "int32", 16, 16 * 3001), ("broadcast", "bidir_ring", "uint8", 8, 200003)]
+    errors = []
+
+    def worker(tid):
+        try:
+            kind, algo, dtype, N, count = cases[tid]
+            a = si.rank_arrays(40 + tid, N, count, dtype, sigma=0.02 if dtype == "bfloat16" else 1.0)
+            want = run_plan(make_plan(kind, algo, N, count, 1), dtype, "sum", a)
+            s = torch.cuda.Stream(dev)
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    t = [si.host_to_tensor(x, dtype, dev) for x in a]
+                    coll.COLLECTIVE_FNS[kind](t, op="sum", algo=algo, root=1)
+                    s.synchronize()
+                    got = [si.tensor_to_host(x, dtype) for x in t]
+                    for i, regs in enumerate(defined_regions(kind, N, count, 1)):
+                        for lo, hi in regs:
+                            assert np.array_equal(got[i][lo:hi].view(np.uint8), want[i][lo:hi].view(np.uint8)), \
+                                (tid, kind, algo, i)
+        except BaseException as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=100)
+    assert not any(th.is_alive() for th in threads)
+    assert not errors, errors[0]
+
+
+def test_finalize_waits_for_queued_work():
+    """coll_finalize right after a large call, with no synchronisation between:
+    the call's tables stay valid until it has finished, and the result is the
+    oracle's; the next call builds its schedule again."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    dev = torch.device("cuda:0")
+    N, count = 8, (16 << 20) // 4 + 5
+    a = si.rank_arrays(51, N, count, "float32")
+    want = run_plan(make_plan("allreduce", "ring", N, count), "float32", "sum", a)
+    t = [si.host_to_tensor(x, "float32", dev) for x in a]
+    torch.cuda.synchronize()
+    coll.coll_allreduce(t, algo="ring")
+    coll.coll_finalize()
+    torch.cuda.synchronize()
+    assert coll.coll_cache_info()[0] == 0
+    got = [si.tensor_to_host(x, "float32") for x in t]
+    assert all(np.array_equal(g.view(np.uint32), w.view(np.uint32)) for g, w in zip(got, want))
+    t = [si.host_to_tensor(x, "float32", dev) for x in a]
+    coll.coll_allreduce(t, algo="ring")
+    torch.cuda.synchronize()
+    assert np.array_equal(si.tensor_to_host(t[3], "float32").view(np.uint32), want[3].view(np.uint32))
