@@ -2,8 +2,10 @@
 
     python bench.py [--steps K] [--warmup W] [--algo ring|rhd|dbt] [--exec persistent|step]
 
-A step is one whole AllReduce call (all 2(N-1) schedule steps) over the 8 rank
-buffers, in place, inputs resident in HBM.  Prints one JSON line:
+A step is one whole AllReduce call (all 2(N-1) schedule steps, with the per-row
+checksums unless --no-checksums) over the 8 rank buffers, in place, inputs
+resident in HBM.  The per-call HIP events also hold the clearing of the checksum
+slots (a kernel of about a microsecond).  Prints one JSON line:
   value        busbw in GB/s = algbw * 2(N-1)/N, algbw = M / time per call
                ("集合通信算法延迟公式", @tbl-model-algo-busbw-coef)
   roofline     algorithmic bytes per launch (every row reads its source, a
@@ -29,6 +31,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "busbw GB/s & % HBM peak, Ring AllReduce fp32 N=8 M=256MiB (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_kernel_ring_allreduce_fp32_n8_256MiB.json")
+# the row kernel variant the default run times: fp32, sum, per-row checksums,
+# nontemporal source loads, not the fine variant
+HEADLINE_KERNEL = "void coll::rows_kernel<2, 0, true, 1, false>"
 
 
 def kernel_source_hash() -> str:
@@ -60,17 +65,19 @@ def load_traffic(per_launch_bytes_expected: float):
 
 
 def cpu_baseline(inputs_host, N: int, count: int, algo: str, cols=None, gpu_sample=None,
-                 min_seconds: float = 10.0, max_calls: int = 40):
+                 min_seconds: float = 10.0, max_calls: int = 40, gpu_sums=None):
     """The oracle as it stands, timed on the host on the same inputs: calls of
     the whole workload repeated until ``min_seconds`` of CPU work (at most
     ``max_calls``), the mean per call reported.  With ``cols`` / ``gpu_sample``
     (the GPU's result of one call on the same inputs at those columns) it also
-    reports whether the first call's result agrees with it bit for bit."""
+    reports whether the first call's result agrees with it bit for bit, and
+    with ``gpu_sums`` (that call's per-row checksums, in the library's row
+    order) whether every row's checksum equals the oracle's."""
     import numpy as np
     from oracle.schedules import make_plan
     from oracle.simulate import run_plan
     plan = make_plan("allreduce", algo, N, count)
-    times, out = [], None
+    times, out, osums = [], None, None
     while not times or (sum(times) < min_seconds and len(times) < max_calls):
         t0 = time.perf_counter()
         res_i = run_plan(plan, "float32", "sum", inputs_host)
@@ -78,6 +85,8 @@ def cpu_baseline(inputs_host, N: int, count: int, algo: str, cols=None, gpu_samp
         if out is None:
             out = res_i
         del res_i
+    if gpu_sums is not None:
+        _, osums = run_plan(plan, "float32", "sum", inputs_host, trace=True)
     dt = sum(times) / len(times)
     M = count * 4
     busbw = M / dt * 2 * (N - 1) / N / 1e9
@@ -87,6 +96,16 @@ def cpu_baseline(inputs_host, N: int, count: int, algo: str, cols=None, gpu_samp
     if cols is not None:
         res["matches_gpu"] = all(np.array_equal(o[cols].view(np.uint32), g.view(np.uint32))
                                  for o, g in zip(out, gpu_sample))
+    if gpu_sums is not None:
+        import collective_communication_algorithms_amd as coll
+        rows, _ = coll.coll_plan("allreduce", algo, N, count, "float32")
+        want, idx = {}, 0
+        for st, srows in enumerate(plan.steps):
+            for r in srows:
+                want[(st, r.src, r.dst, r.src_off, r.dst_off, r.n)] = int(osums[idx])
+                idx += 1
+        res["checksums_match_gpu"] = len(rows) == len(gpu_sums) and all(
+            int(gpu_sums[j]) == want.get(tuple(r[:6])) for j, r in enumerate(rows))
     return res
 
 
@@ -517,6 +536,8 @@ def main() -> int:
     ap.add_argument("--nranks", type=int, default=8)
     ap.add_argument("--mib", type=int, default=256, help="MiB per rank")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-checksums", action="store_true",
+                    help="time the calls without the per-row checksums (the default computes them)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only measure the plain copy (1R+1W) and add (2R+1W) streams and exit")
     ap.add_argument("--sweep", metavar="OUT_JSONL", help="time every configuration's calls and exit")
@@ -535,7 +556,7 @@ def main() -> int:
                     help="write the traffic summary under profiles/ from rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
     if args.summarize_counters:
-        out = summarize_counters(*args.summarize_counters, "void coll::rows_kernel<2, 0, false, 1, false>", TRAFFIC_FILE)
+        out = summarize_counters(*args.summarize_counters, HEADLINE_KERNEL, TRAFFIC_FILE)
         print(json.dumps(out))
         return 0
     if args.gpus != 1:
@@ -585,9 +606,17 @@ def main() -> int:
                                      np.arange(count // N - 4096, count // N + 4096)]))
     cols_t = torch.from_numpy(cols).to(dev)
     sample_in = np.stack([r.index_select(0, cols_t).cpu().numpy() for r in ranks]).astype(np.float64)
+    # per-row checksums (the u64 wrap-sum of each row's destination words after
+    # the row) are part of every timed call unless --no-checksums
+    sums = None
+    if not args.no_checksums:
+        plan_rows, _ = coll.coll_plan("allreduce", args.algo, N, count, "float32")
+        sums = torch.zeros(len(plan_rows), dtype=torch.int64, device=dev)
+        coll.coll_set_checksums(sums)
     coll.coll_allreduce(ranks, algo=args.algo)
     torch.cuda.synchronize()
     gpu_sample = [r.index_select(0, cols_t).cpu().numpy() for r in ranks]
+    gpu_sums = sums.cpu().numpy().view(np.uint64).copy() if sums is not None else None
     exact = sample_in.sum(axis=0)
     u = 2.0 ** -24
     bound = (N * u / (1 - N * u)) * np.abs(sample_in).sum(axis=0)
@@ -616,6 +645,8 @@ def main() -> int:
     total_ms = t_all0.elapsed_time(t_all1)
     per_call = [s.elapsed_time(e) for s, e in ev]
     ms = total_ms / args.steps
+    if sums is not None:
+        coll.coll_set_checksums(None)
     if not bool(torch.isfinite(ranks[0][:1024]).all()):
         print("bench.py: values overflowed", file=sys.stderr)
         return 1
@@ -645,7 +676,7 @@ def main() -> int:
         "data": "synthetic: N(0,1) fp32 per rank from torch's seeded device generator",
         "config": {"workload": f"{args.algo}_allreduce_fp32_n{N}_{args.mib}MiB", "nranks": N,
                    "bytes_per_rank": M, "algo": args.algo, "op": "sum", "inplace": True,
-                   "exec": args.exec, "schedule_steps": stats["steps"]},
+                   "exec": args.exec, "schedule_steps": stats["steps"], "checksums": sums is not None},
         "algbw_GBps": round(algbw, 2),
         "hbm_pct_of_peak": round(100 * hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -660,11 +691,15 @@ def main() -> int:
     del buf, ranks
     torch.cuda.empty_cache()
     if host_inputs is not None:
-        result["cpu_baseline"] = cpu_baseline(host_inputs, N, count, args.algo, cols, gpu_sample)
+        result["cpu_baseline"] = cpu_baseline(host_inputs, N, count, args.algo, cols, gpu_sample, gpu_sums=gpu_sums)
         if not result["cpu_baseline"]["matches_gpu"]:
             print("bench.py: GPU result differs from the oracle on sampled columns", file=sys.stderr)
             return 1
-        result["parity"] = "bit-exact vs the oracle on %d sampled columns per rank" % len(cols)
+        if result["cpu_baseline"].get("checksums_match_gpu") is False:
+            print("bench.py: GPU row checksums differ from the oracle's", file=sys.stderr)
+            return 1
+        result["parity"] = "bit-exact vs the oracle on %d sampled columns per rank" % len(cols) + (
+            ", every row checksum equal to the oracle's" if gpu_sums is not None else "")
     print(json.dumps(result))
     return 0
 

@@ -142,6 +142,21 @@ std::unordered_map<Key, std::unique_ptr<Entry>, KeyHash> g_cache;
 std::unordered_map<int, DevInfo> g_dev;
 std::unordered_map<uint64_t, int> g_occ;  // (kernel variant, device) -> blocks per CU
 uint64_t g_tick = 0;
+
+// Partial row-checksum slots (SUM_LANES per row), one buffer per (device,
+// caller's checksum buffer): calls that share a checksum buffer are ordered by
+// the caller anyway, and calls with different buffers never share slots.
+struct SumScratch {
+  int dev = 0;
+  const uint64_t* user = nullptr;
+  uint64_t* d = nullptr;
+  size_t cap = 0;               // slots
+  uint64_t last_use = 0;
+  bool clean = false;           // every slot is zero once the queued work is done (the fold
+                                // kernel zeroes what it reads); else the next call clears them
+};
+std::vector<SumScratch> g_sum_scratch;
+constexpr size_t SUM_SCRATCH_MAX = 16;  // buffers kept; the least recently used goes first
 constexpr size_t CACHE_CAP = 512;  // schedules kept
 uint64_t g_cache_bytes = 0;        // device memory they hold (COLL_OPT_CACHE_BYTES caps it)
 std::map<std::vector<int64_t>, coll_algo_t> g_auto;  // COLL_ALGO_AUTO decisions
@@ -211,6 +226,54 @@ coll_status_t trim_cache(const Entry* keep) {
   while (g_cache_bytes > uint64_t(opt_cache_bytes.load()) && evict_lru(keep, st)) {
   }
   return st;
+}
+
+// Frees one partial-slot buffer after its device has finished the work queued
+// on it (the kernels that use it may still be running).
+void free_sum_scratch(SumScratch& s) {
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  if (s.d) {
+    if (hipSetDevice(s.dev) == hipSuccess) (void)hipDeviceSynchronize();
+    (void)hipFree(s.d);
+    if (have_cur) (void)hipSetDevice(cur);
+  }
+  s.d = nullptr;
+  s.cap = 0;
+}
+
+// Partial checksum slots for `n` slots on device `dev`, for the caller's
+// buffer `user` (allocated, or grown, on first use).
+coll_status_t sum_scratch(int dev, const uint64_t* user, size_t n, SumScratch*& out) {
+  SumScratch* hit = nullptr;
+  for (SumScratch& s : g_sum_scratch)
+    if (s.dev == dev && s.user == user) hit = &s;
+  if (!hit) {
+    if (g_sum_scratch.size() >= SUM_SCRATCH_MAX) {
+      auto lru = g_sum_scratch.begin();
+      for (auto i = g_sum_scratch.begin(); i != g_sum_scratch.end(); ++i)
+        if (i->last_use < lru->last_use) lru = i;
+      free_sum_scratch(*lru);
+      g_sum_scratch.erase(lru);
+    }
+    g_sum_scratch.push_back(SumScratch{});
+    hit = &g_sum_scratch.back();
+    hit->dev = dev;
+    hit->user = user;
+  }
+  hit->last_use = ++g_tick;
+  if (hit->cap < n) {
+    free_sum_scratch(*hit);
+    hipError_t he = hipMalloc(reinterpret_cast<void**>(&hit->d), n * sizeof(uint64_t));
+    if (he != hipSuccess) {
+      hit->d = nullptr;
+      return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
+    }
+    hit->cap = n;
+    hit->clean = false;
+  }
+  out = hit;
+  return COLL_OK;
 }
 
 // The work lists of phase `pi` for a grid of at most `cap` work groups and
@@ -467,10 +530,23 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   const Bound& b = e->bound;
 
   const bool cks = t_sums != nullptr;
+  uint64_t* partial = nullptr;  // SUM_LANES slots per row, folded into t_sums after the kernels
+  SumScratch* scratch = nullptr;
+  bool capturing = false;
   if (cks) {
     if (size_t(b.nrows) > t_sums_cap) return fail(COLL_ERR_INVALID_ARG, "checksum buffer smaller than the schedule");
-    he = launch_fill_u64(t_sums, uint64_t(b.nrows), 0, stream);
-    if (he != hipSuccess) return hip_fail(he, "checksum clear");
+    st = sum_scratch(dev, t_sums, std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES, scratch);
+    if (st != COLL_OK) return st;
+    partial = scratch->d;
+    // a call being captured into a graph runs later, once per replay: it
+    // clears the slots itself and leaves the flag to the calls that run now
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    capturing = hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+    if (!scratch->clean || capturing) {
+      he = launch_fill_u64(partial, scratch->cap, 0, stream);
+      if (he != hipSuccess) return hip_fail(he, "checksum clear");
+    }
+    if (!capturing) scratch->clean = false;  // until this call's fold is queued
   }
   const uint64_t footprint = uint64_t(N) * uint64_t(count) * uint64_t(sz) * (inplace ? 1u : 2u);
   const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint, kind == COLL_K_ALLTOALL) : uint32_t(opt_nt.load());
@@ -565,7 +641,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       const uint32_t grid = L->G;
       RowsArgs a{};
       a.list = L->d_list;
-      a.sums = t_sums;
+      a.sums = partial;
       a.bases16 = bases16;
       a.p = ptrs;
       for (uint32_t j = 0; j < L->launches; ++j) {
@@ -581,7 +657,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       PermArgs a{};
       a.items = e->d_items;
       a.steps = e->d_steps;
-      a.sums = t_sums;
+      a.sums = partial;
       a.nontemporal = ntmask;
       a.p = ptrs;
       if (ph.colspace >= (uint64_t(1) << 31))
@@ -616,6 +692,11 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         dbg += " | perm steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
                std::to_string(grid) + " unit " + std::to_string(unit) + " slots " + std::to_string(slots);
     }
+  }
+  if (cks) {
+    he = launch_fold_sums(partial, t_sums, uint64_t(b.nrows), stream);
+    if (he != hipSuccess) return hip_fail(he, "checksum fold");
+    if (!capturing) scratch->clean = true;
   }
   if (g_debug.load())
     std::fprintf(stderr, "coll: %s algo %s N %d count %lld dtype-size %d %s steps %lld rows %lld sched_bytes %lld%s\n",
@@ -801,6 +882,8 @@ void coll_finalize(void) {
     if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
   if (have_cur && !devs.empty()) (void)hipSetDevice(cur);
   for (auto& kv : g_cache) free_entry(*kv.second);
+  for (SumScratch& s : g_sum_scratch) free_sum_scratch(s);
+  g_sum_scratch.clear();
   g_cache.clear();
   g_cache_bytes = 0;
   g_occ.clear();

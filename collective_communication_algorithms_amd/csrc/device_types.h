@@ -70,13 +70,20 @@ constexpr int TILE_BYTES = 4096;      // 256 threads x 16 bytes
 constexpr int BLOCK_THREADS = 256;
 constexpr int WAVE_BYTES = TILE_BYTES / (BLOCK_THREADS / 64);  // one wave's bytes of a tile
 
+// Row checksums are accumulated in SUM_LANES partial slots per row: a wave adds
+// its piece's sum to slot row * SUM_LANES + (work-group index mod SUM_LANES), so
+// that the device-scope atomics of one row spread over SUM_LANES addresses (8
+// cache lines) instead of meeting on one; a fold kernel then writes each row's
+// total.
+constexpr uint32_t SUM_LANES = 64;
+
 // Nontemporal hints, per operand of a row.
 enum : uint32_t { NT_SRC = 1u << 0, NT_DSRC = 1u << 1, NT_DST = 1u << 2, NT_ALL = 7u };
 
 struct RowsArgs {                     // row kernel (copy / recv_and_reduce)
   const DevItem* list;                // this launch's work list (pieces inside one column group)
   const uint32_t* off;                // G + 1 offsets into `list`, one slice per work group
-  uint64_t* sums;                     // per-row checksums or nullptr
+  uint64_t* sums;                     // partial row checksums (SUM_LANES per row) or nullptr
   uint32_t bases16;                   // all rank base pointers 16-byte aligned
   uint32_t pad;
   RankPtrs p;
@@ -85,7 +92,7 @@ struct RowsArgs {                     // row kernel (copy / recv_and_reduce)
 struct PermArgs {                     // staged permutation kernel (AllToAll)
   const DevItem* items;
   const DevStep* steps;
-  uint64_t* sums;
+  uint64_t* sums;                     // partial row checksums (SUM_LANES per row) or nullptr
   uint32_t s0, s1;
   uint32_t lg_upl;                    // log2 of the units each lane holds per row and tile
   uint32_t ncols_units;               // block width in units

@@ -151,16 +151,42 @@ __device__ __forceinline__ uint64_t words16(u32x4 v, uint32_t rot) {
   return uint64_t(rotl32(v.x, rot)) + rotl32(v.y, rot) + rotl32(v.z, rot) + rotl32(v.w, rot);
 }
 
-__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// One shift-and-add step of a scan inside every row of 16 lanes: lane i adds
+// lane i - N of its row (0 when that lane lies before the row's first), on a
+// u64 held as two u32 halves.
+template <int N>
+__device__ __forceinline__ void row_shr_add(uint32_t& lo, uint32_t& hi) {
+  const uint32_t l = uint32_t(__builtin_amdgcn_update_dpp(0, int(lo), 0x110 + N, 0xf, 0xf, true));
+  const uint32_t h = uint32_t(__builtin_amdgcn_update_dpp(0, int(hi), 0x110 + N, 0xf, 0xf, true));
+  const uint32_t s = lo + l;
+  hi += h + (s < lo ? 1u : 0u);
+  lo = s;
 }
 
+// Sum of a u64 over the 64 lanes of a wave (every lane active), with DPP
+// moves instead of LDS permutes: the scan leaves each row's total in its last
+// lane, and the four totals are read into scalar registers.
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+  row_shr_add<1>(lo, hi);
+  row_shr_add<2>(lo, hi);
+  row_shr_add<4>(lo, hi);
+  row_shr_add<8>(lo, hi);
+  uint64_t t = 0;
+#pragma unroll
+  for (int r = 15; r < 64; r += 16)
+    t += (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(hi), r))) << 32) |
+         uint32_t(__builtin_amdgcn_readlane(int(lo), r));
+  return t;
+}
+
+// Adds a wave's part of a row checksum to the row's partial slot for this
+// work group.
 __device__ __forceinline__ void add_row_sum(uint64_t* sums, uint32_t row, uint64_t v) {
   v = wave_sum(v);
   if ((threadIdx.x & 63u) == 0 && row != NO_ROW)
-    __hip_atomic_fetch_add(sums + row, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(sums + uint64_t(row) * SUM_LANES + (blockIdx.x & (SUM_LANES - 1u)), v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- element loads / stores for the unaligned edges ------------------------------
@@ -574,6 +600,19 @@ __global__ void fill_u64_kernel(uint64_t* p, uint64_t n, uint64_t value) {
     *gptr<uint64_t>(reinterpret_cast<char*>(p + i)) = value;
 }
 
+// One wave per row: lane p loads partial slot p and sets it back to zero for
+// the next call, the wave sums the loaded values.
+__global__ __launch_bounds__(BLOCK_THREADS) void fold_sums_kernel(uint64_t* partial, uint64_t* out, uint64_t nrows) {
+  static_assert(SUM_LANES == 64, "one lane per partial slot");
+  const uint64_t r = uint64_t(blockIdx.x) * (BLOCK_THREADS / 64) + (threadIdx.x >> 6);
+  if (r >= nrows) return;  // uniform across the wave
+  char* slot = reinterpret_cast<char*>(partial + r * SUM_LANES + (threadIdx.x & 63u));
+  const uint64_t v = *gptr<uint64_t>(slot);
+  *gptr<uint64_t>(slot) = 0;
+  const uint64_t t = wave_sum(v);
+  if ((threadIdx.x & 63u) == 0) *gptr<uint64_t>(reinterpret_cast<char*>(out + r)) = t;
+}
+
 template <bool ADD>
 __global__ __launch_bounds__(BLOCK_THREADS) void calib_kernel(char* dst, const char* a, const char* b, uint64_t units) {
   const uint64_t stride = uint64_t(gridDim.x) * BLOCK_THREADS;
@@ -722,6 +761,14 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t 
   if (n == 0) return hipSuccess;
   const uint32_t grid = uint32_t(n < 256 * 1024 ? (n + BLOCK_THREADS - 1) / BLOCK_THREADS : 1024);
   hipLaunchKernelGGL(fill_u64_kernel, dim3(grid), dim3(BLOCK_THREADS), 0, stream, p, n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hipStream_t stream) {
+  if (nrows == 0) return hipSuccess;
+  const uint64_t rows_per_block = BLOCK_THREADS / 64;
+  const uint32_t grid = uint32_t((nrows + rows_per_block - 1) / rows_per_block);
+  hipLaunchKernelGGL(fold_sums_kernel, dim3(grid), dim3(BLOCK_THREADS), 0, stream, partial, out, nrows);
   return hipGetLastError();
 }
 

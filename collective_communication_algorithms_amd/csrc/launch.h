@@ -11,6 +11,9 @@ hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t 
                        hipStream_t stream);
 hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_t grid, hipStream_t stream);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream);
+// out[r] = the u64 wrap-sum of partial[r * SUM_LANES .. r * SUM_LANES + SUM_LANES), r < nrows;
+// the slots read are set back to zero
+hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hipStream_t stream);
 hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, uint32_t grid, hipStream_t stream);
 hipError_t launch_spin(float* out, uint32_t iters, uint32_t grid, hipStream_t stream);
 int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt);

@@ -202,12 +202,17 @@ coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t c
 coll_status_t coll_get_stats(coll_counts_t* last);
 
 /* Per-row checksums.  When `dev_sums` is non-NULL (a device array of
- * `capacity` uint64), every later collective call on this thread first clears
- * dev_sums[0 .. rows) and then adds, for schedule row r (in coll_plan's order),
- * the sum modulo 2^64 of the little-endian uint32 words of the row's
+ * `capacity` uint64), every later collective call on this thread writes
+ * dev_sums[0 .. rows), stream-ordered: for schedule row r (in coll_plan's
+ * order), the sum modulo 2^64 of the little-endian uint32 words of the row's
  * destination region right after the row (words counted from the region's
- * first byte, the last one zero-padded).  A call with more rows than
- * `capacity` fails with COLL_ERR_INVALID_ARG.  NULL switches checksums off. */
+ * first byte, the last one zero-padded).  The kernels accumulate into 64
+ * partial slots per row in a library buffer kept per (device, dev_sums),
+ * allocated on the first call that needs it or needs more (outside graph
+ * capture, like the schedule), and a last kernel folds them into dev_sums;
+ * calls that share dev_sums must be ordered with each other.  A call with more
+ * rows than `capacity` fails with COLL_ERR_INVALID_ARG.  NULL switches
+ * checksums off. */
 coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
 
 /* Process-wide execution options (defaults in brackets).

@@ -29,6 +29,22 @@ def test_cpu_baseline_repeats_the_oracle_and_compares_with_a_sample():
     bad[1][3] += np.float32(1)
     r = bench.cpu_baseline(a, N, count, "ring", cols, bad, min_seconds=0.0, max_calls=1)
     assert r["matches_gpu"] is False and r["sample"].startswith("1 calls")
+    # row checksums, in the library's row order (coll_plan runs on the host)
+    import collective_communication_algorithms_amd as coll
+    plan = make_plan("allreduce", "ring", N, count)
+    _, osums = run_plan(plan, "float32", "sum", a, trace=True)
+    by_row, idx = {}, 0
+    for st, srows in enumerate(plan.steps):
+        for q in srows:
+            by_row[(st, q.src, q.dst, q.src_off, q.dst_off, q.n)] = int(osums[idx])
+            idx += 1
+    rows, _ = coll.coll_plan("allreduce", "ring", N, count, "float32")
+    sums = np.array([by_row[tuple(q[:6])] for q in rows], dtype=np.uint64)
+    r = bench.cpu_baseline(a, N, count, "ring", cols, sample, min_seconds=0.0, max_calls=1, gpu_sums=sums)
+    assert r["checksums_match_gpu"] is True
+    sums[5] += np.uint64(1)
+    r = bench.cpu_baseline(a, N, count, "ring", cols, sample, min_seconds=0.0, max_calls=1, gpu_sums=sums)
+    assert r["checksums_match_gpu"] is False
 
 
 def test_summarize_counters_scales_by_the_copy_kernel(tmp_path):

@@ -55,3 +55,46 @@ def test_captured_collectives_replay_exactly(gpu_device):
         for got, w, name in ((live, want[0], "allreduce"), (lu, want[1], "broadcast"), (recv, want[2], "alltoall")):
             assert torch.equal(got.view(torch.uint8), w.view(torch.uint8)), (rep, name)
     coll.coll_check()
+
+
+def test_captured_calls_with_checksums_replay_exactly(gpu_device):
+    """Row checksums under capture: a captured call clears its partial slots
+    itself, so every replay gives the eager checksums, also with checksummed
+    eager calls on the same buffers between replays."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    N, count = 8, 8 * 30000 + 5
+    a = si.rank_arrays(17, N, count, "float32")
+    pristine = torch.stack([si.host_to_tensor(x, "float32", gpu_device) for x in a])
+    live = pristine.clone()
+    rows, _ = coll.coll_plan("allreduce", "ring", N, count, "float32")
+    sums = torch.full((len(rows),), -1, dtype=torch.int64, device=gpu_device)
+    coll.coll_set_checksums(sums)
+    try:
+        coll.coll_allreduce(list(live), algo="ring")          # eager: builds the schedule and the slots
+        torch.cuda.synchronize()
+        want, want_sums = live.clone(), sums.clone()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        live.copy_(pristine)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                coll.coll_allreduce(list(live), algo="ring")
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for rep in range(4):
+            live.copy_(pristine)                               # an eager checksummed call between replays
+            sums.fill_(-1)
+            coll.coll_allreduce(list(live), algo="ring")
+            torch.cuda.synchronize()
+            assert torch.equal(sums, want_sums) and torch.equal(live.view(torch.int32), want.view(torch.int32)), rep
+            live.copy_(pristine)
+            sums.fill_(-1)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(sums, want_sums), ("replay", rep)
+            assert torch.equal(live.view(torch.int32), want.view(torch.int32)), ("replay", rep)
+    finally:
+        coll.coll_set_checksums(None)
