@@ -473,3 +473,40 @@ def test_finalize_waits_for_queued_work():
     coll.coll_allreduce(t, algo="ring")
     torch.cuda.synchronize()
     assert np.array_equal(si.tensor_to_host(t[3], "float32").view(np.uint32), want[3].view(np.uint32))
+
+
+def test_checksum_buffers_grow_and_are_evicted():
+    """20 caller checksum buffers, alive at once, used in turn with a small and
+    a large schedule: the library's partial-slot buffers grow, more than it
+    keeps are evicted and rebuilt, and every call's checksums still equal the
+    oracle's."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    from oracle.schedules import make_plan as mk
+    dev = torch.device("cuda:0")
+    shapes = [("ring", 4, 4 * 700 + 3), ("rhd", 16, 16 * 900 + 5)]
+    wants = []
+    for algo, N, count in shapes:
+        a = si.rank_arrays(60 + N, N, count, "int32")
+        plan = mk("allreduce", algo, N, count)
+        _, wsums = run_plan(plan, "int32", "sum", a, trace=True)
+        by_row, idx = {}, 0
+        for st, srows in enumerate(plan.steps):
+            for r in srows:
+                by_row[(st, r.src, r.dst, r.src_off, r.dst_off, r.n)] = int(wsums[idx])
+                idx += 1
+        rows, _ = coll.coll_plan("allreduce", algo, N, count, "int32")
+        wants.append((algo, a, np.array([by_row[tuple(r[:6])] for r in rows], dtype=np.uint64)))
+    bufs = [torch.full((512,), -1, dtype=torch.int64, device=dev) for _ in range(20)]
+    try:
+        for rnd in range(2):
+            for i, sums in enumerate(bufs):
+                algo, a, want = wants[(i + rnd) % 2]
+                coll.coll_set_checksums(sums)
+                t = [si.host_to_tensor(x, "int32", dev) for x in a]
+                coll.coll_allreduce(t, algo=algo)
+                torch.cuda.synchronize()
+                got = sums[:len(want)].cpu().numpy().view(np.uint64)
+                assert np.array_equal(got, want), (rnd, i, algo)
+    finally:
+        coll.coll_set_checksums(None)
