@@ -436,6 +436,8 @@ coll_status_t check_buffers(void* const* send, void* const* recv, int N, int64_t
                             bool& inplace) {
   if (!send) return fail(COLL_ERR_INVALID_ARG, "sendbufs is NULL");
   inplace = true;
+  // nothing is read or written: empty buffers may share any pointer
+  if (count == 0) return COLL_OK;
   if (recv) {
     int same = 0;
     for (int i = 0; i < N; ++i) same += recv[i] == send[i];
@@ -443,7 +445,6 @@ coll_status_t check_buffers(void* const* send, void* const* recv, int N, int64_t
     inplace = same == N;
   }
   if (a2a && inplace) return fail(COLL_ERR_INVALID_ARG, "alltoall must be out of place");
-  if (count == 0) return COLL_OK;
   // all rank buffers have the same length, so sorting the start addresses
   // and comparing neighbours finds any overlap
   uint64_t starts[2 * COLL_MAX_RANKS];

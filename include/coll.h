@@ -26,6 +26,10 @@
  *   recvbufs == NULL, or recvbufs[i] == sendbufs[i] for every i: in place.
  *                Mixing the two, or any overlap between distinct rank buffers,
  *                is COLL_ERR_INVALID_ARG.  AllToAll must be out of place.
+ *   count == 0   nothing is read or written: once the scalar arguments are
+ *                valid the call returns COLL_OK without looking at the rank
+ *                pointers (no NULL, alignment or aliasing check; empty
+ *                framework tensors may all share one pointer, often NULL).
  *   chunk c of a rank buffer = elements [c*count/N, (c+1)*count/N) (floor).
  *   op     ignored by collectives that do not reduce.
  *   root   used by broadcast / scatter / gather / reduce only; 0 <= root < N.
@@ -37,8 +41,8 @@
  *
  * Ownership: the caller owns every buffer and keeps it alive until the stream
  * work has finished.  The library never allocates, frees or retains user
- * memory; it owns only its schedule cache (host and device copies), freed by
- * coll_finalize().
+ * memory; it owns only its schedule cache (host and device copies) and, while
+ * checksums are on, its partial checksum slots, all freed by coll_finalize().
  *
  * Errors: every argument is checked on the host before anything is enqueued,
  * so an error return leaves no partial work.  No exception crosses the ABI.

@@ -71,6 +71,10 @@ INV, UNS, OK = _lib.COLL_ERR_INVALID_ARG, _lib.COLL_ERR_UNSUPPORTED, _lib.COLL_O
     (dict(name="coll_allreduce", send=bufs(4, 16), recv=None, N=4, count=0), OK),
     (dict(name="coll_gather", send=bufs(4, 16), recv=bufs(4, 16, base=1 << 40), N=4, count=0,
           algo="binomial"), OK),
+    # count 0: the rank pointers are not looked at (empty tensors report NULL)
+    (dict(name="coll_alltoall", send=[0] * 4, recv=[0] * 4, N=4, count=0), OK),
+    (dict(name="coll_alltoall", send=bufs(4, 16), recv=None, N=4, count=0), OK),
+    (dict(name="coll_allreduce", send=[1 << 32, 0], recv=[1 << 32, 1 << 33], N=2, count=0), OK),
 ])
 def test_argument_errors(case, want):
     name = case.pop("name")
