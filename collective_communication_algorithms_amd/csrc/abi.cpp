@@ -465,23 +465,6 @@ coll_status_t check_buffers(void* const* send, void* const* recv, int N, int64_t
   return COLL_OK;
 }
 
-// Blocked grid: column groups of this many tiles (schedules with reduce rows /
-// copy-only schedules), one per work group, for column spaces of at least
-// BLOCKED_MIN_COLSPACE bytes.
-constexpr uint32_t BLOCKED_GROUP_TILES_REDUCE = 4;
-constexpr uint32_t BLOCKED_GROUP_TILES_COPY = 8;
-constexpr uint64_t BLOCKED_MIN_COLSPACE = uint64_t(32) << 20;
-
-uint32_t pick_group_tiles(uint64_t colspace, uint64_t max_groups) {
-  const int64_t forced = opt_group.load();
-  if (forced > 0) return uint32_t(forced);
-  // enough groups to give every resident work group at least one, up to 8 tiles per group
-  const uint64_t tiles = (colspace + TILE_BYTES - 1) / TILE_BYTES;
-  uint32_t gt = 8;
-  while (gt > 1 && tiles / gt < max_groups) gt >>= 1;
-  return gt;
-}
-
 coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N, size_t count_in, coll_dtype_t dtype,
                   coll_op_t op, coll_algo_t algo, int root, int chunks, void* stream_v) {
   const int sz = elem_size(dtype);
@@ -571,73 +554,25 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   for (size_t pi = 0; pi < b.phases.size(); ++pi) {
     const Phase& ph = b.phases[pi];
     if (ph.kind == Phase::ROWS) {
-      const uint64_t resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, ntmask));
-      // one launch per step: several waves of resident work groups.  One
-      // launch for all steps: for large column spaces one column group per
-      // work group, so a work group carries its columns through every step
-      // back to back and each step reads what the step before left in the
-      // L2 and the memory-side cache (measured at 8 x 256 MiB: Ring / RHD /
-      // DBT AllReduce 15-22 % faster than a resident-sized grid, Tree Reduce
-      // 18 %, 64-rank ReduceScatter 9-24 %, AllGather 8-12 %); smaller ones
-      // keep a resident-sized grid.
-      const bool blocked = !step_mode && ph.colspace >= BLOCKED_MIN_COLSPACE;
-      uint64_t cap = step_mode ? 4 * resident : resident;
-      uint32_t gt = blocked ? (has_reduce ? BLOCKED_GROUP_TILES_REDUCE : BLOCKED_GROUP_TILES_COPY)
-                            : pick_group_tiles(ph.colspace, resident);
-      if (blocked) {
-        cap = uint64_t(1) << 20;
-        // fp32 / int32 / bf16 reductions, and copy-only schedules over 16 or
-        // more ranks whose groups see several pieces per step: a resident grid
-        // whose work groups take their groups one at a time (group-major
-        // lists) keeps the data in flight small enough for the caches.  A
-        // group averaging two or more pieces per step (halving-doubling, tree,
-        // RHD AllGather): 4-tile groups, 2 work groups per CU; a reduction
-        // with one piece per step (Ring): 8-tile groups, 3 per CU
-        // once that gives every work group at least two groups, else 2 per CU
-        // (8 x 32 MiB: 1,024 groups on 768 work groups leave a third of them
-        // twice the work, 164 us against 150 on 512).  Grids are whole
-        // multiples of the CU count (2.5 per CU measured 10 % slower) and group
-        // sizes powers of two (11-tile groups, which would spread the columns
-        // evenly over 768 work groups, measured 12-16 % slower).  Measured at
-        // 8 x 256 MiB fp32 against one group per work group: DBT 1.158 ->
-        // 1.040 ms, RHD 1.207 -> 1.066, Ring 1.164 -> 1.130, Reduce 0.683 ->
-        // 0.655; bf16: DBT 1.130 -> 1.055, RHD 1.182 -> 1.081, Ring 1.190 ->
-        // 1.151; bf16 64 x 256 MiB ReduceScatter: RHD 7.06 -> 6.81 ms, Ring
-        // 6.85 -> 6.79.  uint8 reductions are not measured and keep one group
-        // per work group.  Copy-only: bf16 RHD AllGather 64 x 256 MiB 6.19 ->
-        // 5.36 ms, 16 x 128 MiB 0.638 -> 0.606; at 8 ranks (RHD AllGather,
-        // binomial Broadcast) within 3 % either way, so they keep one group
-        // per work group, and so do copy schedules with one piece per step
-        // (Ring AllGather 64 x 256 MiB: 4.77 ms, 6.45 on the small grid).
-        const bool reduce_rule = has_reduce && sz >= 2;
-        const bool copy_rule = !has_reduce && N >= 16;
-        if ((reduce_rule || copy_rule) && opt_group.load() == 0) {
-          if (e->multi.size() != b.phases.size()) e->multi.assign(b.phases.size(), int8_t(-1));
-          if (e->multi[pi] < 0) {
-            const uint64_t gb = uint64_t(BLOCKED_GROUP_TILES_REDUCE) * TILE_BYTES;
-            uint64_t pieces = 0;
-            for (uint32_t s = ph.s0; s < ph.s1; ++s)
-              for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
-                const DevItem& it = b.items[b.steps[s].item0 + i];
-                if (it.col1 > it.col0) pieces += (it.col1 - 1) / gb - it.col0 / gb + 1;
-              }
-            const uint64_t groups = (ph.colspace + gb - 1) / gb;
-            e->multi[pi] = pieces >= 2 * groups * uint64_t(ph.s1 - ph.s0) ? 1 : 0;
-          }
-          if (e->multi[pi]) {
-            gt = BLOCKED_GROUP_TILES_REDUCE;
-            cap = uint64_t(di->cus) * 2u;
-          } else if (reduce_rule) {
-            gt = 8;
-            const uint64_t g8 = (ph.colspace + 8 * TILE_BYTES - 1) / (8 * TILE_BYTES);
-            cap = uint64_t(di->cus) * (g8 >= 6 * uint64_t(di->cus) ? 3u : 2u);
-          }
-        }
-      }
-      if (opt_group.load() > 0) gt = uint32_t(opt_group.load());
-      if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
+      RowsShapeInput in;
+      in.colspace = ph.colspace;
+      in.has_reduce = has_reduce;
+      in.elem_size = sz;
+      in.nranks = N;
+      in.cus = uint32_t(di->cus);
+      in.resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, ntmask));
+      in.per_step = step_mode;
+      in.forced_group_tiles = opt_group.load();
+      in.forced_grid = opt_grid.load();
+      const RowsShape shape = rows_shape(in, [&] {
+        if (e->multi.size() != b.phases.size()) e->multi.assign(b.phases.size(), int8_t(-1));
+        if (e->multi[pi] < 0) e->multi[pi] = several_pieces_per_step(b, ph) ? 1 : 0;
+        return e->multi[pi] != 0;
+      });
+      const uint32_t gt = shape.group_tiles;
       DevList* L = nullptr;
-      st = get_list(*e, pi, std::max<uint64_t>(cap, 1), gt, opt_reverse.load() != 0, step_mode, blocked, L);
+      st = get_list(*e, pi, std::max<uint64_t>(shape.cap, 1), gt, opt_reverse.load() != 0, step_mode,
+                    shape.group_major, L);
       if (st != COLL_OK) return st;
       const uint32_t grid = L->G;
       RowsArgs a{};

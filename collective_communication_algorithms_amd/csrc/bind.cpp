@@ -270,6 +270,25 @@ uint32_t wave_mask(const DevItem& x) {
   return m;
 }
 
+bool several_pieces_per_step(const Bound& b, const Phase& ph) {
+  const uint64_t gb = uint64_t(BLOCKED_GROUP_TILES_REDUCE) * TILE_BYTES;
+  uint64_t pieces = 0;
+  for (uint32_t s = ph.s0; s < ph.s1; ++s)
+    for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+      const DevItem& it = b.items[b.steps[s].item0 + i];
+      if (it.col1 > it.col0) pieces += (it.col1 - 1) / gb - it.col0 / gb + 1;
+    }
+  const uint64_t groups = (ph.colspace + gb - 1) / gb;
+  return pieces >= 2 * groups * uint64_t(ph.s1 - ph.s0);
+}
+
+uint32_t resident_group_tiles(uint64_t colspace, uint64_t max_groups) {
+  const uint64_t tiles = (colspace + TILE_BYTES - 1) / TILE_BYTES;
+  uint32_t gt = 8;
+  while (gt > 1 && tiles / gt < max_groups) gt >>= 1;
+  return gt;
+}
+
 std::vector<uint64_t> group_cuts(const Phase& ph, uint64_t gbytes) {
   std::vector<uint64_t> cuts;
   for (uint64_t c : ph.bounds)

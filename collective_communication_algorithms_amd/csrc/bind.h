@@ -61,6 +61,98 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
                     bool per_step, bool group_major, const std::vector<uint64_t>& cuts, std::vector<uint32_t>& off,
                     std::vector<DevItem>& list);
 
+// ---- launch shape of a row phase ----------------------------------------------
+
+// Column spaces of at least BLOCKED_MIN_COLSPACE bytes get large grids: one
+// column group per work group (BLOCKED_GROUP_TILES_COPY tiles for copy-only
+// schedules, BLOCKED_GROUP_TILES_REDUCE with reduce rows), or the cache window
+// of rows_shape.  Smaller ones get a grid of the work groups that fit on the
+// device at once.
+constexpr uint32_t BLOCKED_GROUP_TILES_REDUCE = 4;
+constexpr uint32_t BLOCKED_GROUP_TILES_COPY = 8;
+constexpr uint64_t BLOCKED_MIN_COLSPACE = uint64_t(32) << 20;
+
+struct RowsShapeInput {
+  uint64_t colspace = 0;
+  bool has_reduce = false;
+  int elem_size = 4;
+  int nranks = 1;
+  uint32_t cus = 1;                 // compute units of the device
+  uint64_t resident = 1;            // work groups of the kernel that fit on the device at once
+  bool per_step = false;            // one launch per step
+  int64_t forced_group_tiles = 0;   // > 0: the caller's group size
+  int64_t forced_grid = 0;          // > 0: the caller's grid cap
+};
+
+struct RowsShape {
+  uint32_t group_tiles = 8;
+  uint64_t cap = 1;                 // grid cap: one work group per group up to this many
+  bool group_major = false;         // a work group takes its groups one at a time through all steps
+};
+
+// Whether the phase's 4-tile column groups average two or more pieces per
+// step (halving-doubling, trees, RHD AllGather, binomial Broadcast) or not
+// (Ring, chains).
+bool several_pieces_per_step(const Bound& b, const Phase& ph);
+
+// Group size for a grid of `max_groups` work groups: enough groups to give
+// each of them one, up to 8 tiles per group.
+uint32_t resident_group_tiles(uint64_t colspace, uint64_t max_groups);
+
+// The launch shape of a row phase.  `several()` answers several_pieces_per_step
+// and is called only when the choice depends on it.
+//
+// Large column spaces (one launch for all steps): fp32 / int32 / bf16
+// reductions, and copy-only schedules over 16 or more ranks whose groups see
+// several pieces per step, use a resident grid whose work groups take their
+// groups one at a time (group-major lists), which keeps the data in flight
+// small enough for the caches.  Several pieces per step: 4-tile groups, 2 work
+// groups per CU; a reduction with one piece per step (Ring): 8-tile groups, 3
+// per CU once that gives every work group at least two groups, else 2 per CU
+// (8 x 32 MiB: 1,024 groups on 768 work groups leave a third of them twice the
+// work, 164 us against 150 on 512).  Grids are whole multiples of the CU count
+// (2.5 per CU measured 10 % slower) and group sizes powers of two (11-tile
+// groups, which would spread the columns evenly over 768 work groups, measured
+// 12-16 % slower).  Measured at 8 x 256 MiB fp32 against one group per work
+// group: DBT 1.158 -> 1.040 ms, RHD 1.207 -> 1.066, Ring 1.164 -> 1.130, Reduce
+// 0.683 -> 0.655; bf16: DBT 1.130 -> 1.055, RHD 1.182 -> 1.081, Ring 1.190 ->
+// 1.151; bf16 64 x 256 MiB ReduceScatter: RHD 7.06 -> 6.81 ms, Ring 6.85 ->
+// 6.79.  Copy-only: bf16 RHD AllGather 64 x 256 MiB 6.19 -> 5.36 ms, 16 x 128
+// MiB 0.638 -> 0.606; at 8 ranks (RHD AllGather, binomial Broadcast) within 3 %
+// either way, so they keep one group per work group, and so do copy schedules
+// with one piece per step (Ring AllGather 64 x 256 MiB: 4.77 ms, 6.45 on the
+// small grid) and uint8 reductions (not measured).  One group per work group
+// itself beat a resident-sized grid at 8 x 256 MiB by 15-22 % (AllReduce), 18 %
+// (Tree Reduce), 9-24 % (64-rank ReduceScatter), 3-7 % (64-rank AllGather).
+// One launch per step: 4 resident grids' worth of groups per launch.
+template <class Several>
+RowsShape rows_shape(const RowsShapeInput& in, Several&& several) {
+  RowsShape r;
+  const bool blocked = !in.per_step && in.colspace >= BLOCKED_MIN_COLSPACE;
+  r.group_major = blocked;
+  r.cap = in.per_step ? 4 * in.resident : in.resident;
+  r.group_tiles = blocked ? (in.has_reduce ? BLOCKED_GROUP_TILES_REDUCE : BLOCKED_GROUP_TILES_COPY)
+                          : resident_group_tiles(in.colspace, in.resident);
+  if (blocked) {
+    r.cap = uint64_t(1) << 20;
+    const bool reduce_rule = in.has_reduce && in.elem_size >= 2;
+    const bool copy_rule = !in.has_reduce && in.nranks >= 16;
+    if ((reduce_rule || copy_rule) && in.forced_group_tiles <= 0) {
+      if (several()) {
+        r.group_tiles = BLOCKED_GROUP_TILES_REDUCE;
+        r.cap = uint64_t(in.cus) * 2u;
+      } else if (reduce_rule) {
+        r.group_tiles = 8;
+        const uint64_t g8 = (in.colspace + 8 * TILE_BYTES - 1) / (8 * TILE_BYTES);
+        r.cap = uint64_t(in.cus) * (g8 >= 6 * uint64_t(in.cus) ? 3u : 2u);
+      }
+    }
+  }
+  if (in.forced_group_tiles > 0) r.group_tiles = uint32_t(in.forced_group_tiles);
+  if (in.forced_grid > 0) r.cap = uint64_t(in.forced_grid);
+  return r;
+}
+
 // The regions of rank i's receive buffer whose final value the collective
 // defines (element ranges).
 std::vector<std::pair<int64_t, int64_t>> defined_output(const Schedule& s, int rank);

@@ -16,6 +16,10 @@
 //     is the set of waves whose bytes the piece touches, and every
 //     ITEM_BATCH_NEXT run has at most RUN_MAX members of one step, each inside
 //     one tile, with no two members writing common bytes of one rank.
+//   * rows_shape picks the measured launch shapes (group size, grid cap, list
+//     order) for the configurations its rules were measured on, asks whether
+//     groups see several pieces per step only when a rule depends on it, and
+//     several_pieces_per_step classifies real schedules as expected.
 // Prints one line per failure and "host_check: N shapes, M lists, ok" at the end.
 #include <cstdio>
 #include <cstdlib>
@@ -222,7 +226,88 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
 
 }  // namespace
 
+void check_launch_shapes() {
+  struct Case {
+    const char* what;
+    coll_kind_t kind;
+    coll_algo_t algo;
+    int N, k;
+    int64_t bytes;       // per rank
+    int sz;
+    bool per_step;
+    int64_t forced_gt, forced_grid;
+    int several;         // expected several_pieces_per_step, -1: not asked
+    uint32_t gt;
+    uint64_t cap;
+    bool group_major;
+  };
+  const uint64_t big = uint64_t(1) << 20;
+  const Case cases[] = {
+      {"Ring AR fp32 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, false, 0, 0, 0, 8, 768, true},
+      {"Ring AR fp32 8x32MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 32 << 20, 4, false, 0, 0, 0, 8, 512, true},
+      {"DBT AR fp32 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_DBT, 8, 1, 256 << 20, 4, false, 0, 0, 1, 4, 512, true},
+      {"RHD AR bf16 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RHD, 8, 1, 256 << 20, 2, false, 0, 0, 1, 4, 512, true},
+      {"tree Reduce fp32 8x256MiB", COLL_K_REDUCE, COLL_ALGO_BINOMIAL, 8, 1, 256 << 20, 4, false, 0, 0, 1, 4, 512,
+       true},
+      {"Ring RS bf16 64x256MiB", COLL_K_REDUCESCATTER, COLL_ALGO_RING, 64, 1, 256 << 20, 2, false, 0, 0, 0, 8, 768,
+       true},
+      {"RHD AG bf16 64x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RHD, 64, 1, 256 << 20, 2, false, 0, 0, 1, 4, 512, true},
+      {"Ring AG bf16 64x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 64, 1, 256 << 20, 2, false, 0, 0, 0, 8, big, true},
+      {"binomial Bcast u8 8x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 8, 1, 64 << 20, 1, false, 0, 0, -1, 8, big,
+       true},
+      {"binomial Bcast u8 16x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 16, 1, 64 << 20, 1, false, 0, 0, 1, 4, 512,
+       true},
+      {"chain Bcast k=8 u8 16x64MiB", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 16, 8, 64 << 20, 1, false, 0, 0, 0, 8,
+       big, true},
+      {"Ring AR u8 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 1, false, 0, 0, -1, 4, big, true},
+      {"Ring AR fp32 8x16MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 16 << 20, 4, false, 0, 0, -1, 2, 2048, false},
+      {"Ring AR fp32 8x256MiB per step", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, true, 0, 0, -1, 8, 8192,
+       false},
+      {"Ring AR fp32 8x256MiB forced", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, false, 2, 100, -1, 2, 100,
+       true},
+  };
+  for (const Case& c : cases) {
+    Schedule s;
+    std::string err;
+    const int64_t count = c.bytes / c.sz;
+    CHECK(build_schedule(c.kind, c.algo, c.N, count, 0, c.k, s, err) == COLL_OK, "%s: build (%s)", c.what,
+          err.c_str());
+    const Bound b = bind_schedule(s, c.sz, true);
+    CHECK(!b.phases.empty() && b.phases[0].kind == Phase::ROWS, "%s: no row phase", c.what);
+    if (b.phases.empty()) continue;
+    const Phase& ph = b.phases[0];
+    RowsShapeInput in;
+    in.colspace = ph.colspace;
+    in.has_reduce = c.kind == COLL_K_ALLREDUCE || c.kind == COLL_K_REDUCESCATTER || c.kind == COLL_K_REDUCE;
+    in.elem_size = c.sz;
+    in.nranks = c.N;
+    in.cus = 256;
+    in.resident = 2048;
+    in.per_step = c.per_step;
+    in.forced_group_tiles = c.forced_gt;
+    in.forced_grid = c.forced_grid;
+    int asked = 0;
+    bool several = false;
+    const RowsShape r = rows_shape(in, [&] {
+      ++asked;
+      several = several_pieces_per_step(b, ph);
+      return several;
+    });
+    if (c.several < 0) {
+      CHECK(asked == 0, "%s: asked about pieces per step", c.what);
+    } else {
+      CHECK(asked == 1, "%s: asked %d times about pieces per step", c.what, asked);
+      CHECK(several == (c.several != 0), "%s: several pieces per step %d", c.what, int(several));
+    }
+    CHECK(r.group_tiles == c.gt, "%s: group tiles %u, want %u", c.what, r.group_tiles, c.gt);
+    CHECK(r.cap == c.cap, "%s: grid cap %llu, want %llu", c.what, (unsigned long long)r.cap,
+          (unsigned long long)c.cap);
+    CHECK(r.group_major == c.group_major, "%s: group-major %d", c.what, int(r.group_major));
+  }
+}
+
 int main() {
+  check_launch_shapes();
   std::vector<Shape> shapes;
   const coll_kind_t kinds[] = {COLL_K_ALLREDUCE, COLL_K_REDUCESCATTER, COLL_K_ALLGATHER, COLL_K_BROADCAST,
                                COLL_K_SCATTER,   COLL_K_GATHER,        COLL_K_ALLTOALL,  COLL_K_REDUCE};
