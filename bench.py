@@ -681,6 +681,10 @@ def main() -> int:
         "hbm_pct_of_peak": round(100 * hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        # bytes the row kernel actually moved through the memory fabric (the
+        # committed rocprofv3 counters, scaled) per mean launch time
+        "fabric_traffic_GBps": round(traffic / (launch_ms * 1e-3) / 1e9, 1) if traffic else None,
+        "fabric_pct_of_peak": round(100 * traffic / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2) if traffic else None,
         "cpu_baseline": None,
         "alpha_beta_page_model_ms": round(pred_ms, 4),
         "parity": "within the binary32 error bound of the fp64 sum on %d sampled columns per rank" % len(cols),
