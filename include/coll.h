@@ -17,7 +17,7 @@
  *        Binary Tree AllReduce, Ring AllGather / ReduceScatter, Pairwise and
  *        Bruck AllToAll, busbw coefficients.
  *
- * Conventions shared by all seven collective calls
+ * Conventions shared by all eight collective calls
  *   sendbufs[i], recvbufs[i]  device pointers of virtual rank i, each holding
  *                `count` elements of `dtype` (the pages' message size M =
  *                count * sizeof(dtype) bytes per rank).  Pointers must be
@@ -111,7 +111,7 @@ typedef enum {
 #define COLL_MAX_RANKS 128
 
 /* ------------------------------------------------------------------------- */
-/* The seven collectives.  Same parameters for all; see the conventions above. */
+/* The eight collectives.  Same parameters for all; see the conventions above. */
 
 /* [P3] AllReduce: every rank ends with the elementwise reduction over ranks.
  * Input all of buf_i; output all of buf_i.  algo: RING (default), RHD, DBT. */
@@ -234,9 +234,9 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          copy-only schedules over 16 or more ranks whose
  *                          groups see two or more rows per step do the same
  *                          with 4-tile groups on 2 per CU; other schedules one
- *                          group per work group, 8 tiles (4 with reduce rows).  Smaller column spaces: up to 8
- *                          tiles over a grid of the work groups that fit on the
- *                          device at once.  Whenever every group has a work
+ *                          group per work group, 8 tiles (4 with reduce rows).
+ *                          Smaller column spaces: up to 8 tiles over a grid of
+ *                          the work groups that fit on the device at once.  Whenever every group has a work
  *                          group of its own, groups are also split where a row
  *                          starts or ends inside them].
  * COLL_OPT_MAX_GRID        cap on work groups per launch, up to 2^20 [0: automatic].
@@ -282,8 +282,9 @@ coll_status_t coll_check(void* stream);
 
 const char* coll_status_string(coll_status_t status);
 const char* coll_last_error(void);   /* thread-local detail of the last error */
-void coll_finalize(void);            /* frees the schedule cache after waiting for every device
-                                        that holds part of it (work queued there finishes first) */
+void coll_finalize(void);            /* frees the schedule cache and the checksum slots after
+                                        waiting for every device that holds part of them (work
+                                        queued there finishes first) */
 
 /* ------------------------------------------------------------------------- */
 /* Calibration kernels: plain streams over `bytes` bytes (multiple of 16) for
