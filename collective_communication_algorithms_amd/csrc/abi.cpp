@@ -117,6 +117,7 @@ struct DevList {                // work lists of one row phase for one launch sh
   bool reverse = false, per_step = false, group_major = false;
   uint32_t launches = 0;
   bool fine = false;            // small pieces: launch the row kernel's fine variant
+  bool fwd = false;             // launch the forwarding variant (most entries take an operand from registers)
   uint32_t* d_off = nullptr;
   DevItem* d_list = nullptr;
   uint64_t bytes = 0;           // device memory held
@@ -330,6 +331,16 @@ coll_status_t get_list(Entry& e, size_t pi, uint64_t cap, uint32_t gt, bool reve
     piece_bytes += x.col1 - x.col0;
   }
   l.fine = runs || (!list.empty() && piece_bytes < uint64_t(TILE_BYTES) * list.size());
+  // The forwarding variant holds 8 tiles of results in registers, which halves
+  // the work groups a CU can hold.  It pays on the large grids of group-major
+  // lists where most entries forward (chains: Ring AllReduce / AllGather, chain
+  // pipelines, about 90 % of their entries; 8 x 256 MiB fp32 Ring 1.150 -> 0.948
+  // ms), not where few do (trees and halving-doubling, 30-50 %: 9-14 % slower at
+  // 8 x 256 MiB), nor on resident grids, which are sized for the plain kernel's
+  // occupancy (Ring AllReduce 8 x 1-8 MiB: 22-100 % slower).
+  size_t marked = 0;
+  for (const DevItem& x : list) marked += (x.flags & (ITEM_SRC_FWD | ITEM_DSRC_FWD)) != 0;
+  l.fwd = group_major && marked > 0 && marked * 10 >= list.size() * 6;
   hipError_t he = hipMalloc(reinterpret_cast<void**>(&l.d_off), off.size() * sizeof(uint32_t));
   if (he != hipSuccess) return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
   he = hipMalloc(reinterpret_cast<void**>(&l.d_list), std::max<size_t>(list.size(), 1) * sizeof(DevItem));
@@ -582,12 +593,13 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.p = ptrs;
       for (uint32_t j = 0; j < L->launches; ++j) {
         a.off = L->d_off + size_t(j) * (grid + 1);
-        he = launch_rows(a, dt, int(op), cks, ntmask, L->fine, grid, stream);
+        he = launch_rows(a, dt, int(op), cks, ntmask, L->fine, L->fwd, grid, stream);
         if (he != hipSuccess) return hip_fail(he, "row kernel launch");
       }
       if (g_debug.load())
         dbg += " | rows steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
-               std::to_string(grid) + " group_tiles " + std::to_string(gt) + (L->fine ? " fine" : "") + " nt " +
+               std::to_string(grid) + " group_tiles " + std::to_string(gt) + (L->fine ? " fine" : "") +
+               (L->fwd && !L->fine && ntmask <= 1 ? " forwarding" : "") + " nt " +
                std::to_string(ntmask) + " launches " + std::to_string(L->launches);
     } else {
       PermArgs a{};

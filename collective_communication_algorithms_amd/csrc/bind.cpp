@@ -359,7 +359,7 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
           Piece p = cut[rev ? cut.size() - 1 - k : k];
           uint32_t owner = uint32_t(p.group % G);
           if (per_step && rev) owner = G - 1 - owner;
-          p.it.flags &= ~uint32_t(ITEM_BATCH_NEXT);
+          p.it.flags &= ~uint32_t(ITEM_BATCH_NEXT | ITEM_SRC_FWD | ITEM_DSRC_FWD | ITEM_NO_STORE);
           p.it.pad = wave_mask(p.it);
           raw[owner].push_back(p);
         }
@@ -376,6 +376,48 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
       run.clear();
       run_step = ~0u;
       for (const Piece& p : raw[w]) push(p.step, p.it);
+      // forwarding: an entry that reads, over the same whole-tile columns, the
+      // bytes the entry before it wrote (its source in a later step, or its old
+      // destination value) may take them from the registers of the threads that
+      // stored them; no other work group writes these columns, and nothing else
+      // in this list comes between the two
+      for (size_t i = 1; i < per.size(); ++i) {
+        const DevItem& p = per[i - 1];
+        DevItem& q = per[i];
+        if (!fwd_eligible(p.col0, p.col1, p.flags) || !fwd_eligible(q.col0, q.col1, q.flags)) continue;
+        if (p.col0 != q.col0 || p.col1 != q.col1 || (p.flags & ITEM_BATCH_NEXT)) continue;
+        if (!(q.flags & ITEM_SRC_SEND) && q.src_rank == p.dst_rank && q.src_delta == p.dst_delta &&
+            raw[w][i].step > raw[w][i - 1].step)
+          q.flags |= ITEM_SRC_FWD;
+        if ((q.flags & ITEM_REDUCE) && !(q.flags & ITEM_DSRC_SEND) && q.dst_rank == p.dst_rank &&
+            q.dst_delta == p.dst_delta)
+          q.flags |= ITEM_DSRC_FWD;
+      }
+      // stores no one needs: the destination bytes of an eligible entry that a
+      // later entry over the same columns overwrites before any entry between
+      // them loads them (an operand taken from registers is no load; a load from
+      // the rank's send buffer counts, which in place is the same memory).  In
+      // Ring AllReduce these are the partial sums of the ReduceScatter half,
+      // which the AllGather half overwrites: N-2 of each column's 2(N-1) stores.
+      for (size_t i = 0; i < per.size(); ++i) {
+        DevItem& p = per[i];
+        if (!fwd_eligible(p.col0, p.col1, p.flags)) continue;
+        const uint64_t width = p.col1 - p.col0;
+        auto meets = [&](uint16_t rank, int64_t delta) {
+          return rank == p.dst_rank && uint64_t(delta > p.dst_delta ? delta - p.dst_delta : p.dst_delta - delta) < width;
+        };
+        for (size_t j = i + 1; j < per.size(); ++j) {
+          const DevItem& q = per[j];
+          if (!fwd_eligible(q.col0, q.col1, q.flags) || q.col0 != p.col0 || q.col1 != p.col1) break;
+          const bool loads = (!(q.flags & ITEM_SRC_FWD) && meets(q.src_rank, q.src_delta)) ||
+                             ((q.flags & ITEM_REDUCE) && !(q.flags & ITEM_DSRC_FWD) && meets(q.dst_rank, q.dst_delta));
+          if (loads) break;
+          if (meets(q.dst_rank, q.dst_delta)) {
+            if (q.dst_delta == p.dst_delta) p.flags |= ITEM_NO_STORE;
+            break;
+          }
+        }
+      }
       off.push_back(uint32_t(list.size()));
       list.insert(list.end(), per.begin(), per.end());
     }

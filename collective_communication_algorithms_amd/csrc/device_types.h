@@ -31,7 +31,16 @@ enum : uint32_t {
   ITEM_BATCH_NEXT = 1u << 6, // work lists only: the next entry of this list joins this one's
                              // run (same step, both inside one tile, no common destination
                              // bytes); a run's loads are all issued before its stores
+  ITEM_SRC_FWD = 1u << 7,    // work lists only: the source bytes are the previous entry's
+                             // destination bytes (same columns, an earlier step), still held
+                             // in the registers of the thread that stored them
+  ITEM_DSRC_FWD = 1u << 8,   // work lists only: the old destination value is the previous
+                             // entry's result over the same columns, still in registers
+  ITEM_NO_STORE = 1u << 9,   // work lists only: a later entry of the list overwrites this
+                             // entry's destination bytes (same columns) before any entry
+                             // loads them; the forwarding variant does not store them
 };
+
 
 constexpr uint32_t NO_ROW = 0xFFFFFFFFu;
 
@@ -69,6 +78,15 @@ enum Op : int { OP_SUM = 0, OP_MAX = 1, OP_MIN = 2 };
 constexpr int TILE_BYTES = 4096;      // 256 threads x 16 bytes
 constexpr int BLOCK_THREADS = 256;
 constexpr int WAVE_BYTES = TILE_BYTES / (BLOCK_THREADS / 64);  // one wave's bytes of a tile
+
+// Pieces of whole tiles, at most FWD_TILES of them, 16-byte aligned on both
+// sides: the forwarding variant of the row kernel keeps the units it stored for
+// such a piece in registers, for the next entry of its list to use.
+constexpr uint32_t FWD_TILES = 8;
+constexpr bool fwd_eligible(uint64_t col0, uint64_t col1, uint32_t flags) {
+  return (flags & ITEM_VEC) != 0 && col1 > col0 && col0 % TILE_BYTES == 0 && col1 % TILE_BYTES == 0 &&
+         (col1 - col0) / TILE_BYTES <= FWD_TILES;
+}
 
 // Row checksums are accumulated in SUM_LANES partial slots per row: a wave adds
 // its piece's sum to slot row * SUM_LANES + (work-group index mod SUM_LANES), so

@@ -345,6 +345,40 @@ __device__ __forceinline__ void do_piece(const RowsArgs& a, const DevItem& it, u
   if (t1 >= m1) do_unit<DT, OP, CKS, NTM>(v, t1 * TILE_BYTES + tofs, it.col0, it.col1, true, acc);
 }
 
+// A piece of at most FWD_TILES whole tiles (fwd_eligible), for the forwarding
+// variant: `held[k]` holds the unit this thread stored in tile k of the
+// previous eligible piece of its list.  An ITEM_SRC_FWD / ITEM_DSRC_FWD piece
+// takes its source / old destination from there instead of loading what this
+// thread itself just stored; every other operand is loaded, all loads first.
+// The piece's results replace `held`; an ITEM_NO_STORE piece does not store them.
+template <int DT, int OP, bool CKS, int NTM>
+__device__ __forceinline__ void do_piece_fwd(const RowsArgs& a, const DevItem& it, uint64_t tofs,
+                                             u32x4 (&held)[FWD_TILES], uint64_t& acc) {
+  const ItemView v = view_of(a, it);
+  const uint32_t nt = uint32_t((it.col1 - it.col0) / TILE_BYTES);
+  const uint64_t x0 = it.col0 + tofs;
+  const bool fs = (it.flags & ITEM_SRC_FWD) != 0, fd = (it.flags & ITEM_DSRC_FWD) != 0;
+  const bool store = (it.flags & ITEM_NO_STORE) == 0;
+  u32x4 s[FWD_TILES], d[FWD_TILES];
+#pragma unroll
+  for (uint32_t k = 0; k < FWD_TILES; ++k) {
+    if (k < nt) {
+      if (!fs) s[k] = ld16<(NTM & NT_SRC) != 0>(v.src + x0 + uint64_t(k) * TILE_BYTES);
+      if (v.reduce && !fd) d[k] = ld16<(NTM & NT_DSRC) != 0>(v.dsrc + x0 + uint64_t(k) * TILE_BYTES);
+    }
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < FWD_TILES; ++k) {
+    if (k < nt) {
+      u32x4 y = fs ? held[k] : s[k];
+      if (v.reduce) y = combine16<DT, OP>(fd ? held[k] : d[k], y);
+      if (store) st16<(NTM & NT_DST) != 0>(v.dst + x0 + uint64_t(k) * TILE_BYTES, y);
+      held[k] = y;
+      if constexpr (CKS) acc += words16(y, v.shift * 8u);
+    }
+  }
+}
+
 __device__ __forceinline__ bool one_tile(const DevItem& it) {
   return it.col0 / TILE_BYTES == (it.col1 - 1) / TILE_BYTES;
 }
@@ -448,7 +482,7 @@ __device__ __forceinline__ DevItem lane_get(const LaneList& c, uint32_t e) {
 // ITEM_BATCH_NEXT-linked pieces (each inside one tile, as the host builds
 // them) is processed together.  Both orders are correct: runs never hold two
 // pieces with common destination bytes.
-template <int DT, int OP, bool CKS, int NTM, bool FINE>
+template <int DT, int OP, bool CKS, int NTM, bool FINE, bool FWD>
 __global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
   const uint32_t e0 = cload(a.off + blockIdx.x), e1 = cload(a.off + blockIdx.x + 1);
   if (e0 >= e1) return;
@@ -488,12 +522,16 @@ __global__ __launch_bounds__(BLOCK_THREADS) void rows_kernel(const RowsArgs a) {
       e += n;
     }
   } else {
+    u32x4 held[FWD_TILES];  // FWD: this thread's units of the last eligible piece
     DevItem next = cload(a.list + e0);
     for (uint32_t e = e0; e < e1; ++e) {
       const DevItem it = next;
       if (e + 1 < e1) next = cload(a.list + e + 1);
       uint64_t acc = 0;
-      do_piece<DT, OP, CKS, NTM>(a, it, tofs, acc);
+      if (FWD && a.bases16 && fwd_eligible(it.col0, it.col1, it.flags))
+        do_piece_fwd<DT, OP, CKS, NTM>(a, it, tofs, held, acc);
+      else
+        do_piece<DT, OP, CKS, NTM>(a, it, tofs, acc);
       if constexpr (CKS) add_row_sum(a.sums, it.row, acc);
     }
   }
@@ -643,42 +681,46 @@ __global__ __launch_bounds__(BLOCK_THREADS) void calib_kernel(char* dst, const c
 typedef void (*RowsFn)(RowsArgs);
 
 template <int DT, int OP, bool CKS>
-static RowsFn rows_fn_nt(uint32_t nt, bool fine) {
+static RowsFn rows_fn_nt(uint32_t nt, bool fine, bool fwd) {
   // lists of small pieces come from small footprints, which stay in the
-  // caches: the fine variant exists for the all-cached mask only
-  if (fine && (nt & 7u) == 0) return rows_kernel<DT, OP, CKS, 0, true>;
+  // caches: the fine variant exists for the all-cached mask only; the
+  // forwarding variant for the masks the automatic policy picks outside
+  // AllToAll (none, source loads)
+  if (fine && (nt & 7u) == 0) return rows_kernel<DT, OP, CKS, 0, true, false>;
+  if (fwd && (nt & 7u) == 0) return rows_kernel<DT, OP, CKS, 0, false, true>;
+  if (fwd && (nt & 7u) == 1) return rows_kernel<DT, OP, CKS, 1, false, true>;
   switch (nt & 7u) {
-    case 0: return rows_kernel<DT, OP, CKS, 0, false>;
-    case 1: return rows_kernel<DT, OP, CKS, 1, false>;
-    case 2: return rows_kernel<DT, OP, CKS, 2, false>;
-    case 3: return rows_kernel<DT, OP, CKS, 3, false>;
-    case 4: return rows_kernel<DT, OP, CKS, 4, false>;
-    case 5: return rows_kernel<DT, OP, CKS, 5, false>;
-    case 6: return rows_kernel<DT, OP, CKS, 6, false>;
-    default: return rows_kernel<DT, OP, CKS, 7, false>;
+    case 0: return rows_kernel<DT, OP, CKS, 0, false, false>;
+    case 1: return rows_kernel<DT, OP, CKS, 1, false, false>;
+    case 2: return rows_kernel<DT, OP, CKS, 2, false, false>;
+    case 3: return rows_kernel<DT, OP, CKS, 3, false, false>;
+    case 4: return rows_kernel<DT, OP, CKS, 4, false, false>;
+    case 5: return rows_kernel<DT, OP, CKS, 5, false, false>;
+    case 6: return rows_kernel<DT, OP, CKS, 6, false, false>;
+    default: return rows_kernel<DT, OP, CKS, 7, false, false>;
   }
 }
 
 template <int DT, int OP>
-static RowsFn rows_fn(bool cks, uint32_t nt, bool fine) {
-  return cks ? rows_fn_nt<DT, OP, true>(nt, fine) : rows_fn_nt<DT, OP, false>(nt, fine);
+static RowsFn rows_fn(bool cks, uint32_t nt, bool fine, bool fwd) {
+  return cks ? rows_fn_nt<DT, OP, true>(nt, fine, fwd) : rows_fn_nt<DT, OP, false>(nt, fine, fwd);
 }
 
 template <int DT>
-static RowsFn rows_fn_op(int op, bool cks, uint32_t nt, bool fine) {
+static RowsFn rows_fn_op(int op, bool cks, uint32_t nt, bool fine, bool fwd) {
   switch (op) {
-    case OP_SUM: return rows_fn<DT, OP_SUM>(cks, nt, fine);
-    case OP_MAX: return rows_fn<DT, OP_MAX>(cks, nt, fine);
-    default: return rows_fn<DT, OP_MIN>(cks, nt, fine);
+    case OP_SUM: return rows_fn<DT, OP_SUM>(cks, nt, fine, fwd);
+    case OP_MAX: return rows_fn<DT, OP_MAX>(cks, nt, fine, fwd);
+    default: return rows_fn<DT, OP_MIN>(cks, nt, fine, fwd);
   }
 }
 
-static RowsFn pick_rows(int dtype, int op, bool cks, uint32_t nt, bool fine) {
+static RowsFn pick_rows(int dtype, int op, bool cks, uint32_t nt, bool fine, bool fwd) {
   switch (dtype) {
-    case DT_I32: return rows_fn_op<DT_I32>(op, cks, nt, fine);
-    case DT_U8: return rows_fn_op<DT_U8>(op, cks, nt, fine);
-    case DT_F32: return rows_fn_op<DT_F32>(op, cks, nt, fine);
-    default: return rows_fn_op<DT_BF16>(op, cks, nt, fine);
+    case DT_I32: return rows_fn_op<DT_I32>(op, cks, nt, fine, fwd);
+    case DT_U8: return rows_fn_op<DT_U8>(op, cks, nt, fine, fwd);
+    case DT_F32: return rows_fn_op<DT_F32>(op, cks, nt, fine, fwd);
+    default: return rows_fn_op<DT_BF16>(op, cks, nt, fine, fwd);
   }
 }
 
@@ -706,9 +748,9 @@ static PermFn pick_perm(int unit, int slots, bool cks, bool nt) {
   return slots > 16 ? pick_perm_slots<32>(unit, cks, nt) : pick_perm_slots<16>(unit, cks, nt);
 }
 
-hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, bool fine, uint32_t grid,
-                       hipStream_t stream) {
-  RowsFn f = pick_rows(dtype, op, cks, nt, fine);
+hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, bool fine, bool fwd,
+                       uint32_t grid, hipStream_t stream) {
+  RowsFn f = pick_rows(dtype, op, cks, nt, fine, fwd);
   hipLaunchKernelGGL(f, dim3(grid), dim3(BLOCK_THREADS), 0, stream, a);
   return hipGetLastError();
 }
@@ -721,7 +763,8 @@ hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_
 
 int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_rows(dtype, op, cks, nt, false), BLOCK_THREADS, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_rows(dtype, op, cks, nt, false, false), BLOCK_THREADS,
+                                                   0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;

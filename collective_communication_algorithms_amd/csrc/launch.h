@@ -7,8 +7,10 @@
 
 namespace coll {
 
-hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, bool fine, uint32_t grid,
-                       hipStream_t stream);
+// fine: the variant for lists of small pieces; fwd: the variant that keeps
+// stored units in registers for ITEM_SRC_FWD / ITEM_DSRC_FWD entries
+hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, bool fine, bool fwd,
+                       uint32_t grid, hipStream_t stream);
 hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_t grid, hipStream_t stream);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream);
 // out[r] = the u64 wrap-sum of partial[r * SUM_LANES .. r * SUM_LANES + SUM_LANES), r < nrows;

@@ -11,11 +11,24 @@
 //     with uniform column groups and with groups split at the rows' boundaries
 //     (group_cuts): the pieces of every item cover its columns exactly once,
 //     each piece lies inside one column group and sits in its owner's list,
-//     with split groups every row boundary is a group boundary, each group's
+//     with split groups every row boundary is a group boundary, every
+//     forwarding mark (ITEM_SRC_FWD / ITEM_DSRC_FWD) names bytes the entry
+//     just before it in the same list wrote, over the same whole-tile columns
+//     (a source: in an earlier step), each group's
 //     pieces are in step order (group-major lists: groups in order), the wave mask
 //     is the set of waves whose bytes the piece touches, and every
 //     ITEM_BATCH_NEXT run has at most RUN_MAX members of one step, each inside
-//     one tile, with no two members writing common bytes of one rank.
+//     one tile, with no two members writing common bytes of one rank;
+//   * symbolic execution of every such list: each byte of every rank buffer
+//     holds a 32-bit symbol, a copy moves it and a reduction replaces the old
+//     destination symbol d by mix(d, s), which depends on the order of its
+//     operands.  Running a launch's lists one work group after another, the
+//     way the forwarding variant of the row kernel takes them (forwarded
+//     operands from the previous piece's results, ITEM_NO_STORE stores
+//     skipped), and again the way the plain variant does (every operand
+//     loaded, every store made), must end in the same memory as running the
+//     phase's items step by step; and within one launch no byte that a work
+//     group writes is read or written by another (column ownership).
 //   * rows_shape picks the measured launch shapes (group size, grid cap, list
 //     order) for the configurations its rules were measured on, asks whether
 //     groups see several pieces per step only when a rule depends on it, and
@@ -25,6 +38,7 @@
 #include <cstdlib>
 #include <algorithm>
 #include <map>
+#include <numeric>
 #include <string>
 #include <vector>
 
@@ -36,6 +50,9 @@ using namespace coll;
 namespace {
 
 int failures = 0;
+long long fwd_marks = 0;       // forwarding marks checked
+long long no_store_marks = 0;  // ITEM_NO_STORE marks checked
+long long exec_lists = 0;      // launches' lists executed symbolically
 
 #define CHECK(cond, ...)                  \
   do {                                    \
@@ -75,10 +92,244 @@ uint32_t mask_of(uint64_t c0, uint64_t c1) {
   return m;
 }
 
+// ---- symbolic execution ------------------------------------------------------
+
+uint32_t mix(uint32_t d, uint32_t s) {
+  uint32_t h = (d ^ 0x9E3779B9u) * 0x85EBCA6Bu;
+  h ^= h >> 13;
+  return h + s * 0xC2B2AE35u + 1u;
+}
+
+// Rank buffers as symbols, one array: buffer id 2*rank (send) or 2*rank + 1
+// (receive) starts at base[id]; in place a rank's send and receive buffers are
+// the same memory.  One symbol stands for q bytes: every item boundary and
+// delta of the schedule, and the tile size, are multiples of q, so every item
+// and every piece moves such a unit whole.
+struct Mem {
+  bool inplace = false;
+  uint64_t q = 1;
+  std::vector<uint64_t> base;
+  std::vector<uint32_t> v;
+  uint64_t id(bool send, int rank) const { return uint64_t(2 * rank) + ((send && !inplace) ? 0 : 1); }
+  // index into v of the unit at column c of an item's operand
+  uint64_t src(const DevItem& it, uint64_t c) const {
+    return base[id((it.flags & ITEM_SRC_SEND) != 0, it.src_rank)] + uint64_t(int64_t(c) + it.src_delta) / q;
+  }
+  uint64_t dsrc(const DevItem& it, uint64_t c) const {
+    return base[id((it.flags & ITEM_DSRC_SEND) != 0, it.dst_rank)] + uint64_t(int64_t(c) + it.dst_delta) / q;
+  }
+  uint64_t dst(const DevItem& it, uint64_t c) const {
+    return base[id(false, it.dst_rank)] + uint64_t(int64_t(c) + it.dst_delta) / q;
+  }
+};
+
+template <class F>
+void for_row_items(const Bound& b, F&& f) {
+  for (const Phase& ph : b.phases) {
+    if (ph.kind != Phase::ROWS) continue;
+    for (uint32_t s = ph.s0; s < ph.s1; ++s)
+      for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+        const DevItem& it = b.items[b.steps[s].item0 + i];
+        if (it.col1 > it.col0) f(it);
+      }
+  }
+}
+
+Mem initial_mem(const Bound& b, int N, bool inplace) {
+  Mem m;
+  m.inplace = inplace;
+  m.q = TILE_BYTES;
+  auto g = [&](int64_t x) { m.q = std::gcd(m.q, uint64_t(x < 0 ? -x : x)); };
+  for_row_items(b, [&](const DevItem& it) {
+    g(int64_t(it.col0));
+    g(int64_t(it.col1));
+    g(it.src_delta);
+    g(it.dst_delta);
+  });
+  std::vector<uint64_t> ext(size_t(2 * N), 0);
+  m.base.assign(ext.size() + 1, 0);  // all zero while measuring: index = unit offset
+  for_row_items(b, [&](const DevItem& it) {
+    const uint64_t c = it.col1 - m.q;
+    uint64_t& e1 = ext[m.id((it.flags & ITEM_SRC_SEND) != 0, it.src_rank)];
+    e1 = std::max(e1, m.src(it, c) + 1);
+    uint64_t& e2 = ext[m.id((it.flags & ITEM_DSRC_SEND) != 0, it.dst_rank)];
+    e2 = std::max(e2, m.dsrc(it, c) + 1);
+    uint64_t& e3 = ext[m.id(false, it.dst_rank)];
+    e3 = std::max(e3, m.dst(it, c) + 1);
+  });
+  for (size_t i = 0; i < ext.size(); ++i) m.base[i + 1] = m.base[i] + ext[i];
+  m.v.resize(m.base.back());
+  for (uint64_t x = 0; x < m.v.size(); ++x) {
+    uint64_t z = x + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    m.v[x] = uint32_t(z ^ (z >> 31));
+  }
+  return m;
+}
+
+// The phase's items step by step, in item order.
+void run_steps(Mem& m, const Bound& b, const Phase& ph) {
+  for (uint32_t s = ph.s0; s < ph.s1; ++s)
+    for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+      const DevItem& it = b.items[b.steps[s].item0 + i];
+      for (uint64_t c = it.col0; c < it.col1; c += m.q) {
+        uint32_t y = m.v[m.src(it, c)];
+        if (it.flags & ITEM_REDUCE) y = mix(m.v[m.dsrc(it, c)], y);
+        m.v[m.dst(it, c)] = y;
+      }
+    }
+}
+
+// The units of v that a phase's items write, as sorted disjoint ranges.
+std::vector<std::pair<uint64_t, uint64_t>> written_units(const Mem& m, const Bound& b, const Phase& ph) {
+  std::vector<std::pair<uint64_t, uint64_t>> r;
+  for (uint32_t s = ph.s0; s < ph.s1; ++s)
+    for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+      const DevItem& it = b.items[b.steps[s].item0 + i];
+      if (it.col1 > it.col0) r.push_back({m.dst(it, it.col0), m.dst(it, it.col1 - m.q) + 1});
+    }
+  std::sort(r.begin(), r.end());
+  std::vector<std::pair<uint64_t, uint64_t>> out;
+  for (auto& x : r) {
+    if (!out.empty() && x.first <= out.back().second) out.back().second = std::max(out.back().second, x.second);
+    else out.push_back(x);
+  }
+  return out;
+}
+
+// Which work group of the current launch touched each unit: tag = (launch
+// generation << 16) | (work group + 1); readers' tag ends in 0xFFFF once two
+// work groups have read the unit.
+struct Owners {
+  std::vector<uint64_t> rd, wr;
+  uint64_t gen = 0;
+  explicit Owners(const Mem& m) : rd(m.v.size(), 0), wr(m.v.size(), 0) {}
+  bool read(uint64_t i, uint32_t w) {
+    const uint64_t tag = (gen << 16) | (w + 1);
+    const uint64_t ww = wr[i];
+    if ((ww >> 16) == gen && ww != tag) return false;
+    uint64_t& r = rd[i];
+    if ((r >> 16) != gen) r = tag;
+    else if (r != tag) r = (gen << 16) | 0xFFFF;
+    return true;
+  }
+  bool write(uint64_t i, uint32_t w) {
+    const uint64_t tag = (gen << 16) | (w + 1);
+    const uint64_t ww = wr[i], r = rd[i];
+    if ((ww >> 16) == gen && ww != tag) return false;
+    if ((r >> 16) == gen && r != tag) return false;
+    wr[i] = tag;
+    return true;
+  }
+};
+
+// Runs one phase's launches on `m` (the memory before the phase), each
+// launch's work groups one after the other, as the forwarding variant (fwd) or
+// the plain variant takes the lists; compares the units the phase writes with
+// `after` and puts `before`'s values back there.
+void check_exec(const Shape& sh, uint32_t G, const std::vector<uint32_t>& off, const std::vector<DevItem>& list,
+                const Mem& before, const Mem& after, const std::vector<std::pair<uint64_t, uint64_t>>& written,
+                Owners& own, Mem& m, bool fwd) {
+  const uint32_t launches = uint32_t(off.size() / (G + 1));
+  bool race = false, stale = false;
+  std::vector<uint32_t> held, next;
+  for (uint32_t j = 0; j < launches; ++j) {
+    ++own.gen;
+    for (uint32_t w = 0; w < G; ++w) {
+      bool have = false;
+      uint64_t h0 = 0, h1 = 0;
+      for (uint32_t e = off[size_t(j) * (G + 1) + w]; e < off[size_t(j) * (G + 1) + w + 1]; ++e) {
+        const DevItem& it = list[e];
+        const bool f = fwd && fwd_eligible(it.col0, it.col1, it.flags);
+        const bool fs = f && (it.flags & ITEM_SRC_FWD), fd = f && (it.flags & ITEM_DSRC_FWD);
+        const bool store = !(f && (it.flags & ITEM_NO_STORE));
+        if ((fs || fd) && !(have && h0 == it.col0 && h1 == it.col1)) stale = true;
+        next.assign(size_t((it.col1 - it.col0) / m.q), 0);
+        for (uint64_t c = it.col0; c < it.col1; c += m.q) {
+          const size_t k = size_t((c - it.col0) / m.q);
+          uint32_t y;
+          if (fs && !stale) {
+            y = held[k];
+          } else {
+            const uint64_t i = m.src(it, c);
+            race = race || !own.read(i, w);
+            y = m.v[i];
+          }
+          if (it.flags & ITEM_REDUCE) {
+            uint32_t d;
+            if (fd && !stale) {
+              d = held[k];
+            } else {
+              const uint64_t i = m.dsrc(it, c);
+              race = race || !own.read(i, w);
+              d = m.v[i];
+            }
+            y = mix(d, y);
+          }
+          if (store) {
+            const uint64_t i = m.dst(it, c);
+            race = race || !own.write(i, w);
+            m.v[i] = y;
+          }
+          next[k] = y;
+        }
+        if (f) {
+          held.swap(next);
+          have = true;
+          h0 = it.col0;
+          h1 = it.col1;
+        }
+      }
+    }
+  }
+  ++exec_lists;
+  bool same = true;
+  for (auto& r : written) {
+    same = same && std::equal(m.v.begin() + r.first, m.v.begin() + r.second, after.v.begin() + r.first);
+    std::copy(before.v.begin() + r.first, before.v.begin() + r.second, m.v.begin() + r.first);
+  }
+  const char* how = fwd ? "forwarding" : "plain";
+  CHECK(!stale, "%s: %s variant: a forwarded operand with no matching piece before it", name(sh).c_str(), how);
+  CHECK(!race, "%s: %s variant: two work groups of one launch touch a unit one of them writes", name(sh).c_str(),
+        how);
+  CHECK(same, "%s: %s variant, G %u: lists end in other memory than the steps", name(sh).c_str(), how, G);
+}
+
+// Which lists to execute symbolically, and how (--exec=...; every list of
+// every shape takes about 20 minutes at -O2):
+//   small (default): shapes of up to 1,000 elements, every launch layout;
+//   sample: also shapes of up to 4,099 elements on grids of 3 and 257 work
+//     groups, group-major lists in reversed order and step-major lists in step
+//     order, and larger ones in the layout of large reductions (257 work
+//     groups, 4-tile groups split at row boundaries, group-major) in the
+//     forwarding variant only;
+//   all: everything;  none: nothing.
+enum ExecMode { EXEC_NONE, EXEC_SMALL, EXEC_SAMPLE, EXEC_ALL } exec_mode = EXEC_SMALL;
+bool exec_shape(const Shape& sh) {
+  return exec_mode == EXEC_ALL || exec_mode == EXEC_SAMPLE || (exec_mode == EXEC_SMALL && sh.count <= 1000);
+}
+bool exec_filter(const Shape& sh, uint32_t G, uint32_t gt, bool rev, bool per_step, bool gm, bool snap, bool fwd) {
+  if (!exec_shape(sh)) return false;
+  if (exec_mode == EXEC_ALL || sh.count <= 1000) return true;
+  if (sh.count <= 4099) return G != 1 && rev == gm;
+  return fwd && G == 257 && gt == 4 && gm && !per_step && rev && snap;
+}
+
 void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nlists) {
+  // memory before and after each row phase, items run step by step
+  std::vector<Mem> mems;
+  mems.push_back(exec_shape(sh) ? initial_mem(b, sh.N, sh.inplace) : Mem{});
+  Owners own(mems[0]);
+  for (const Phase& ph : b.phases) {
+    mems.push_back(mems.back());
+    if (ph.kind == Phase::ROWS && exec_shape(sh)) run_steps(mems.back(), b, ph);
+  }
   for (size_t pi = 0; pi < b.phases.size(); ++pi) {
     const Phase& ph = b.phases[pi];
     if (ph.kind != Phase::ROWS) continue;
+    Mem work = mems[pi];
+    const auto written = exec_shape(sh) ? written_units(work, b, ph) : std::vector<std::pair<uint64_t, uint64_t>>{};
     for (uint32_t G : {1u, 3u, 257u})
       for (uint32_t gt : {1u, 4u})
         for (int rev = 0; rev < 2; ++rev)
@@ -166,7 +417,33 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
                     last_group = g;
                   }
                   std::vector<int64_t> key{int64_t(ps), p.row, p.src_rank, p.dst_rank, p.src_delta, p.dst_delta,
-                                           int64_t(p.flags & ~uint32_t(ITEM_BATCH_NEXT))};
+                                           int64_t(p.flags & ~uint32_t(ITEM_BATCH_NEXT | ITEM_SRC_FWD |
+                                                                       ITEM_DSRC_FWD | ITEM_NO_STORE))};
+                  if (p.flags & ITEM_NO_STORE) {
+                    ++no_store_marks;
+                    CHECK(fwd_eligible(p.col0, p.col1, p.flags), "%s: store skipped on a piece the forwarding "
+                          "variant does not hold", name(sh).c_str());
+                  }
+                  // forwarding marks
+                  if (p.flags & (ITEM_SRC_FWD | ITEM_DSRC_FWD)) {
+                    ++fwd_marks;
+                    CHECK(e > a, "%s: forwarding mark on a list's first entry", name(sh).c_str());
+                    if (e > a) {
+                      const DevItem& q = list[e - 1];
+                      const uint32_t qs = q.row == NO_ROW ? 0u : uint32_t(sched.rows[q.row].step);
+                      CHECK(fwd_eligible(q.col0, q.col1, q.flags) && fwd_eligible(p.col0, p.col1, p.flags) &&
+                                q.col0 == p.col0 && q.col1 == p.col1 && !(q.flags & ITEM_BATCH_NEXT),
+                            "%s: forwarding between pieces that are not the same whole tiles", name(sh).c_str());
+                      if (p.flags & ITEM_SRC_FWD)
+                        CHECK(!(p.flags & ITEM_SRC_SEND) && p.src_rank == q.dst_rank && p.src_delta == q.dst_delta &&
+                                  ps > qs,
+                              "%s: source forwarded from a piece that did not write it", name(sh).c_str());
+                      if (p.flags & ITEM_DSRC_FWD)
+                        CHECK((p.flags & ITEM_REDUCE) && !(p.flags & ITEM_DSRC_SEND) && p.dst_rank == q.dst_rank &&
+                                  p.dst_delta == q.dst_delta && ps >= qs,
+                              "%s: old destination forwarded from a piece that did not write it", name(sh).c_str());
+                    }
+                  }
                   got[key].push_back({p.col0, p.col1});
                   // runs
                   if (p.flags & ITEM_BATCH_NEXT) {
@@ -220,6 +497,9 @@ void check_lists(const Shape& sh, const Schedule& sched, const Bound& b, int& nl
               CHECK(merge(w) == merge(g), "%s: pieces do not re-assemble the items", name(sh).c_str());
             }
             CHECK(got.size() == want.size(), "%s: pieces of unknown items", name(sh).c_str());
+            for (bool fwd : {true, false})
+              if (exec_filter(sh, G, gt, rev != 0, per_step != 0, gm != 0, snap != 0, fwd))
+                check_exec(sh, G, off, list, mems[pi], mems[pi + 1], written, own, work, fwd);
           }
   }
 }
@@ -306,7 +586,18 @@ void check_launch_shapes() {
   }
 }
 
-int main() {
+int main(int argc, char** argv) {
+  for (int i = 1; i < argc; ++i) {
+    const std::string a = argv[i];
+    if (a == "--exec=none") exec_mode = EXEC_NONE;
+    else if (a == "--exec=small") exec_mode = EXEC_SMALL;
+    else if (a == "--exec=sample") exec_mode = EXEC_SAMPLE;
+    else if (a == "--exec=all") exec_mode = EXEC_ALL;
+    else {
+      std::printf("unknown argument %s\n", a.c_str());
+      return 2;
+    }
+  }
   check_launch_shapes();
   std::vector<Shape> shapes;
   const coll_kind_t kinds[] = {COLL_K_ALLREDUCE, COLL_K_REDUCESCATTER, COLL_K_ALLGATHER, COLL_K_BROADCAST,
@@ -357,6 +648,10 @@ int main() {
     }
     check_lists(sh, s, b, nlists);
   }
-  std::printf("host_check: %zu shapes, %d lists, %s\n", shapes.size(), nlists, failures ? "FAILED" : "ok");
+  CHECK(fwd_marks > 0, "no forwarding mark was made");
+  CHECK(no_store_marks > 0, "no store was skipped");
+  CHECK(exec_mode == EXEC_NONE || exec_lists > 0, "no list was executed");
+  std::printf("host_check: %zu shapes, %d lists, %lld forwarding marks, %lld skipped stores, %lld list executions, %s\n",
+              shapes.size(), nlists, fwd_marks, no_store_marks, exec_lists, failures ? "FAILED" : "ok");
   return failures ? 1 : 0;
 }
