@@ -83,6 +83,10 @@ std::vector<std::pair<int64_t, int64_t>> defined_output(const Schedule& s, int r
 Bound bind_schedule(const Schedule& s, int sz, bool inplace) {
   Bound b;
   b.nrows = int64_t(s.rows.size());
+  b.defined.resize(size_t(s.N));
+  for (int rank = 0; rank < s.N; ++rank)
+    for (auto& reg : defined_output(s, rank))
+      if (reg.second > reg.first) b.defined[size_t(rank)].push_back({uint64_t(reg.first * sz), uint64_t(reg.second * sz)});
   b.counts = count_schedule(s, sz);
   const bool a2a = s.kind == COLL_K_ALLTOALL;
   // staged AllToAll steps (Bruck's and the Ring's rounds, the final rotation)
@@ -331,6 +335,22 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
     }
     per.push_back(q);
   };
+  // stores outside the defined output may be dropped only where nothing after
+  // this list can read them (see below)
+  bool zero_deltas = true;
+  for (uint32_t s = ph.s0; s < ph.s1; ++s)
+    for (uint32_t i = 0; i < b.steps[s].nitems; ++i) {
+      const DevItem& it = b.items[b.steps[s].item0 + i];
+      zero_deltas = zero_deltas && it.src_delta == 0 && it.dst_delta == 0;
+    }
+  const bool dead_at_end = group_major && !per_step && zero_deltas && ph.s1 == b.steps.size() &&
+                           b.defined.size() > 0;
+  auto defined_meets = [&](const DevItem& p) {
+    if (p.dst_rank >= b.defined.size()) return true;
+    for (auto& r : b.defined[p.dst_rank])
+      if (r.first < p.col1 && p.col0 < r.second) return true;
+    return false;
+  };
   for (uint32_t j = 0; j < launches; ++j) {
     for (auto& v : raw) v.clear();
     const uint32_t sa = per_step ? ph.s0 + j : ph.s0, sb = per_step ? sa + 1 : ph.s1;
@@ -416,6 +436,29 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
             if (q.dst_delta == p.dst_delta) p.flags |= ITEM_NO_STORE;
             break;
           }
+        }
+      }
+      // stores no one reads before the call ends: in a group-major list of the
+      // call's last phase, run in one launch, an eligible entry whose
+      // destination bytes lie outside its rank's defined output and which no
+      // later entry of its column group loads (the ReduceScatter partial sums
+      // that stay on the ranks that do not own the chunk).  With every delta
+      // zero a column is the same bytes on every rank, so entries of other
+      // column groups, which other work groups or later parts of this list
+      // run, never touch these bytes.
+      if (dead_at_end) {
+        for (size_t i = 0; i < per.size(); ++i) {
+          DevItem& p = per[i];
+          if ((p.flags & ITEM_NO_STORE) || !fwd_eligible(p.col0, p.col1, p.flags) || defined_meets(p)) continue;
+          bool live = false;
+          for (size_t j = i + 1; j < per.size() && raw[w][j].group == raw[w][i].group && !live; ++j) {
+            const DevItem& q = per[j];
+            const bool overlap = p.col0 < q.col1 && q.col0 < p.col1;
+            const bool same = q.col0 == p.col0 && q.col1 == p.col1;
+            live = overlap && ((q.src_rank == p.dst_rank && !(same && (q.flags & ITEM_SRC_FWD) && fwd_eligible(q.col0, q.col1, q.flags))) ||
+                               (q.dst_rank == p.dst_rank));
+          }
+          if (!live) p.flags |= ITEM_NO_STORE;
         }
       }
       off.push_back(uint32_t(list.size()));

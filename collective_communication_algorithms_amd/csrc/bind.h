@@ -24,6 +24,9 @@ struct Bound {
   coll_counts_t counts{};      // as executed
   int64_t nrows = 0;           // schedule rows (checksum slots)
   int perm_unit = 16;          // PERM: bytes per unit (16, 8, 4, 2 or 1)
+  // per rank, the byte ranges of its receive buffer whose final value the
+  // collective defines (sorted); the rest is left unspecified
+  std::vector<std::vector<std::pair<uint64_t, uint64_t>>> defined;
 };
 
 // In place (`inplace`) or out of place.  Out of place, a row reads from the send
@@ -56,7 +59,11 @@ std::vector<uint64_t> group_cuts(const Phase& ph, uint64_t gbytes);
 // columns' data stays cached from one step to the next); otherwise all its
 // groups go step by step.  Launch j gives work group w the pieces
 // off[j*(G+1) + w] .. off[j*(G+1) + w + 1] of `list`.  Runs (ITEM_BATCH_NEXT)
-// are marked on the final order.
+// are marked on the final order, and so are the forwarding variant's marks:
+// ITEM_SRC_FWD / ITEM_DSRC_FWD, and ITEM_NO_STORE on a store that a later entry
+// over the same columns overwrites before any load, or (group-major lists of
+// the call's last phase, one launch) on a store outside its rank's defined
+// output that no later entry of its column group loads.
 void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_tiles, bool reverse,
                     bool per_step, bool group_major, const std::vector<uint64_t>& cuts, std::vector<uint32_t>& off,
                     std::vector<DevItem>& list);
