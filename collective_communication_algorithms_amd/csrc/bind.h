@@ -109,29 +109,29 @@ uint32_t resident_group_tiles(uint64_t colspace, uint64_t max_groups);
 // The launch shape of a row phase.  `several()` answers several_pieces_per_step
 // and is called only when the choice depends on it.
 //
-// Large column spaces (one launch for all steps): fp32 / int32 / bf16
-// reductions, and copy-only schedules over 16 or more ranks whose groups see
-// several pieces per step, use a resident grid whose work groups take their
-// groups one at a time (group-major lists), which keeps the data in flight
-// small enough for the caches.  Several pieces per step: 4-tile groups, 2 work
-// groups per CU; a reduction with one piece per step (Ring): 8-tile groups, 3
-// per CU once that gives every work group at least two groups, else 2 per CU
-// (8 x 32 MiB: 1,024 groups on 768 work groups leave a third of them twice the
-// work, 164 us against 150 on 512).  Grids are whole multiples of the CU count
-// (2.5 per CU measured 10 % slower) and group sizes powers of two (11-tile
-// groups, which would spread the columns evenly over 768 work groups, measured
-// 12-16 % slower).  Measured at 8 x 256 MiB fp32 against one group per work
-// group: DBT 1.158 -> 1.040 ms, RHD 1.207 -> 1.066, Ring 1.164 -> 1.130, Reduce
-// 0.683 -> 0.655; bf16: DBT 1.130 -> 1.055, RHD 1.182 -> 1.081, Ring 1.190 ->
-// 1.151; bf16 64 x 256 MiB ReduceScatter: RHD 7.06 -> 6.81 ms, Ring 6.85 ->
-// 6.79.  Copy-only: bf16 RHD AllGather 64 x 256 MiB 6.19 -> 5.36 ms, 16 x 128
-// MiB 0.638 -> 0.606; at 8 ranks (RHD AllGather, binomial Broadcast) within 3 %
-// either way, so they keep one group per work group, and so do copy schedules
-// with one piece per step (Ring AllGather 64 x 256 MiB: 4.77 ms, 6.45 on the
-// small grid) and uint8 reductions (not measured).  One group per work group
-// itself beat a resident-sized grid at 8 x 256 MiB by 15-22 % (AllReduce), 18 %
-// (Tree Reduce), 9-24 % (64-rank ReduceScatter), 3-7 % (64-rank AllGather).
-// One launch per step: 4 resident grids' worth of groups per launch.
+// Large column spaces (one launch for all steps) take their groups in
+// group-major lists.  fp32 / int32 / bf16 reductions, and copy-only schedules
+// over 16 or more ranks, whose groups see several pieces per step (trees,
+// halving-doubling) use a resident grid of 2 work groups per CU with 4-tile
+// groups, which keeps the data in flight small enough for the caches.
+// Measured at 8 x 256 MiB fp32 against one group per work group: DBT 1.158 ->
+// 1.040 ms, RHD 1.207 -> 1.066, Reduce 0.683 -> 0.655; bf16: DBT 1.130 ->
+// 1.055, RHD 1.182 -> 1.081; bf16 64 x 256 MiB ReduceScatter RHD 7.06 -> 6.81
+// ms.  Copy-only: bf16 RHD AllGather 64 x 256 MiB 6.19 -> 5.36 ms, 16 x 128 MiB
+// 0.638 -> 0.606; at 8 ranks (RHD AllGather, binomial Broadcast) within 3 %
+// either way, so they keep one group per work group.  Grids are whole
+// multiples of the CU count (2.5 per CU measured 10 % slower).  Reductions with
+// one piece per step (Ring), which the forwarding variant of the row kernel
+// runs, take 8-tile groups, one per work group: their operands pass from step
+// to step in registers, so a small grid keeps nothing in the caches that
+// matters (Ring AllReduce fp32 8 x 32 MiB 97.6 -> 87.0 us against 2 per CU, 8 x
+// 256 MiB 0.870 -> 0.851 ms against 3 per CU; 64-rank bf16 ReduceScatter 3.17
+// -> 3.10 ms).  Copy schedules with one piece per step and uint8 reductions
+// (not measured) keep one group per work group as well.  One group per work
+// group itself beat a resident-sized grid at 8 x 256 MiB by 15-22 %
+// (AllReduce), 18 % (Tree Reduce), 9-24 % (64-rank ReduceScatter), 3-7 %
+// (64-rank AllGather).  One launch per step: 4 resident grids' worth of groups
+// per launch.
 template <class Several>
 RowsShape rows_shape(const RowsShapeInput& in, Several&& several) {
   RowsShape r;
@@ -150,8 +150,6 @@ RowsShape rows_shape(const RowsShapeInput& in, Several&& several) {
         r.cap = uint64_t(in.cus) * 2u;
       } else if (reduce_rule) {
         r.group_tiles = 8;
-        const uint64_t g8 = (in.colspace + 8 * TILE_BYTES - 1) / (8 * TILE_BYTES);
-        r.cap = uint64_t(in.cus) * (g8 >= 6 * uint64_t(in.cus) ? 3u : 2u);
       }
     }
   }
