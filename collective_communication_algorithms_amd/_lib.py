@@ -39,7 +39,7 @@ class CollRow(ctypes.Structure):
 
 class CollCounts(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("rows", ctypes.c_int64), ("crit_bytes", ctypes.c_int64),
-                ("hbm_bytes", ctypes.c_int64)]
+                ("hbm_bytes", ctypes.c_int64), ("moved_bytes", ctypes.c_int64)]
 
 
 class CollError(RuntimeError):

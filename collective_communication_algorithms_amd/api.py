@@ -130,20 +130,21 @@ def coll_plan(kind, algo, nranks, count, dtype, root=0, chunks=1):
     k, a, d = _code(KINDS, kind, "collective"), _code(ALGOS, algo, "algorithm"), _code(DTYPES, dtype, "dtype")
     n = ctypes.c_size_t(0)
     counts = CollCounts()
-    check(lib.coll_plan(k, a, nranks, count, d, root, chunks, None, ctypes.byref(n), ctypes.byref(counts)))
+    check(lib.coll_plan(k, a, nranks, count, d, root, chunks, None, ctypes.byref(n), None))
     rows = (CollRow * max(n.value, 1))()
     check(lib.coll_plan(k, a, nranks, count, d, root, chunks, rows, ctypes.byref(n), ctypes.byref(counts)))
     out = [(r.step, r.src, r.dst, r.src_off, r.dst_off, r.n, r.reduce, r.local, r.from_send, r.staged)
            for r in rows[:n.value]]
     return out, {"steps": counts.steps, "rows": counts.rows, "crit_bytes": counts.crit_bytes,
-                 "hbm_bytes": counts.hbm_bytes}
+                 "hbm_bytes": counts.hbm_bytes, "moved_bytes": counts.moved_bytes}
 
 
 def coll_get_stats():
     lib = _lib.load()
     c = CollCounts()
     check(lib.coll_get_stats(ctypes.byref(c)))
-    return {"steps": c.steps, "rows": c.rows, "crit_bytes": c.crit_bytes, "hbm_bytes": c.hbm_bytes}
+    return {"steps": c.steps, "rows": c.rows, "crit_bytes": c.crit_bytes, "hbm_bytes": c.hbm_bytes,
+            "moved_bytes": c.moved_bytes}
 
 
 def coll_set_checksums(sums=None):

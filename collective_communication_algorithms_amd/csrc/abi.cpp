@@ -118,6 +118,7 @@ struct DevList {                // work lists of one row phase for one launch sh
   uint32_t launches = 0;
   bool fine = false;            // small pieces: launch the row kernel's fine variant
   bool fwd = false;             // launch the forwarding variant (most entries take an operand from registers)
+  uint64_t fwd_saved = 0;       // bytes that variant neither loads nor stores
   uint32_t* d_off = nullptr;
   DevItem* d_list = nullptr;
   uint64_t bytes = 0;           // device memory held
@@ -169,15 +170,67 @@ CostModel cost_model() {
   return m;
 }
 
-coll_status_t auto_algo(coll_kind_t kind, int N, int64_t count, int sz, int root, coll_algo_t& out) {
-  const std::vector<int64_t> key{int64_t(kind), N, count, sz, root, opt_alpha_ns.load(), opt_beta_gbps.load()};
+// Compute units assumed when planning without a device (coll_plan): MI355X's.
+constexpr uint32_t PLAN_CUS = 256;
+
+// Whether a row phase's launches run the forwarding variant with its marks
+// honoured: the variant exists for the nontemporal masks of ordinary
+// footprints (none, source loads; without either, a list of small pieces takes
+// the fine variant instead), and it honours its marks only when every rank
+// buffer is 16-byte aligned.
+bool forwarding_runs(bool fwd, bool fine, uint32_t ntmask, bool bases16) {
+  return fwd && bases16 && (ntmask == NT_SRC || (ntmask == 0 && !fine));
+}
+
+// Bytes a call moves through memory, as planned for an in-place call on
+// 16-byte-aligned buffers with the current options on a device of `cus`
+// compute units: the schedule's bytes, less, in every row phase whose lists the
+// forwarding variant runs, the operands it takes from registers and the stores
+// it skips.  Only large column spaces get group-major lists, so only they build
+// lists here.
+int64_t planned_moved_bytes(const Schedule& s, int sz, uint32_t cus) {
+  const Bound b = bind_schedule(s, sz, true);
+  int64_t moved = b.counts.hbm_bytes;
+  const bool a2a = s.kind == COLL_K_ALLTOALL;
+  const uint64_t footprint = uint64_t(s.N) * uint64_t(s.count) * uint64_t(sz);
+  const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint, a2a) : uint32_t(opt_nt.load());
+  const bool has_reduce =
+      s.kind == COLL_K_ALLREDUCE || s.kind == COLL_K_REDUCESCATTER || s.kind == COLL_K_REDUCE;
+  for (const Phase& ph : b.phases) {
+    if (ph.kind != Phase::ROWS) continue;
+    RowsShapeInput in;
+    in.colspace = ph.colspace;
+    in.has_reduce = has_reduce;
+    in.elem_size = sz;
+    in.nranks = s.N;
+    in.cus = cus;
+    in.resident = uint64_t(cus) * 8u;  // only resident grids use it, and they never forward
+    in.per_step = opt_exec.load() == 1;
+    in.forced_group_tiles = opt_group.load();
+    in.forced_grid = opt_grid.load();
+    const RowsShape shape = rows_shape(in, [&] { return several_pieces_per_step(b, ph); });
+    if (!shape.group_major) continue;
+    const RowsList rl = plan_rows_list(b, ph, std::max<uint64_t>(shape.cap, 1), shape.group_tiles,
+                                       opt_reverse.load() != 0, in.per_step, shape.group_major);
+    if (forwarding_runs(rl.fwd, rl.fine, ntmask, true)) moved -= int64_t(rl.fwd_saved);
+  }
+  return moved;
+}
+
+coll_status_t auto_algo(coll_kind_t kind, int N, int64_t count, int sz, int root, uint32_t cus, coll_algo_t& out) {
+  const std::vector<int64_t> key{int64_t(kind), N, count, sz, root, opt_alpha_ns.load(), opt_beta_gbps.load(),
+                                 int64_t(cus), opt_nt.load(), opt_exec.load(), opt_group.load(), opt_grid.load(),
+                                 opt_reverse.load()};
   auto it = g_auto.find(key);
   if (it != g_auto.end()) {
     out = it->second;
     return COLL_OK;
   }
   std::string err;
-  const coll_status_t st = choose_algo(kind, N, count, sz, root, cost_model(), out, err);
+  const std::function<int64_t(const Schedule&)> moved = [&](const Schedule& s) {
+    return planned_moved_bytes(s, sz, cus);
+  };
+  const coll_status_t st = choose_algo(kind, N, count, sz, root, cost_model(), out, err, &moved);
   if (st != COLL_OK) return fail(st, err);
   if (g_auto.size() > 4096) g_auto.clear();
   g_auto[key] = out;
@@ -278,14 +331,7 @@ coll_status_t sum_scratch(int dev, const uint64_t* user, size_t n, SumScratch*& 
 }
 
 // The work lists of phase `pi` for a grid of at most `cap` work groups and
-// column groups of `gt` tiles, built and uploaded on first use.  The grid is
-// one work group per column group while that fits in `cap`, else `cap`.  When
-// each group has a work group of its own, groups are also split at the rows'
-// boundaries (group_cuts): a group holding the end of one row and the start of
-// the next would make its work group run both rows' chains of pieces one after
-// the other, twice the round trips of any other work group (8 x 64 MiB uint8
-// Broadcast in 13 chunks: 160 -> 138 us).  With several groups per work group
-// a split adds as many pieces to some list as it saves, so there it is not done.
+// column groups of `gt` tiles (plan_rows_list), built and uploaded on first use.
 coll_status_t get_list(Entry& e, size_t pi, uint64_t cap, uint32_t gt, bool reverse, bool per_step, bool group_major,
                        DevList*& out) {
   for (DevList& l : e.lists)
@@ -304,43 +350,22 @@ coll_status_t get_list(Entry& e, size_t pi, uint64_t cap, uint32_t gt, bool reve
     g_cache_bytes -= l.bytes;
     e.lists.erase(e.lists.begin());
   }
-  std::vector<uint32_t> off;
-  std::vector<DevItem> list;
   const Phase& ph = e.bound.phases[pi];
-  const uint64_t gbytes = uint64_t(gt) * TILE_BYTES;
-  const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
-  std::vector<uint64_t> cuts = group_cuts(ph, gbytes);
-  if (groups + cuts.size() > cap) cuts.clear();
-  const uint32_t G = uint32_t(std::min(groups + cuts.size(), cap));
-  build_worklist(e.bound, ph, G, gt, reverse, per_step, group_major, cuts, off, list);
+  RowsList rl = plan_rows_list(e.bound, ph, cap, gt, reverse, per_step, group_major);
+  const std::vector<uint32_t>& off = rl.off;
+  const std::vector<DevItem>& list = rl.list;
   DevList l;
   l.phase = pi;
   l.cap = cap;
-  l.G = G;
+  l.G = rl.G;
   l.gt = gt;
   l.reverse = reverse;
   l.per_step = per_step;
   l.group_major = group_major;
   l.launches = per_step ? ph.s1 - ph.s0 : 1;
-  // the fine variant pays off when pieces are small: some runs, or pieces of
-  // less than one tile on average
-  uint64_t piece_bytes = 0;
-  bool runs = false;
-  for (const DevItem& x : list) {
-    runs = runs || (x.flags & ITEM_BATCH_NEXT);
-    piece_bytes += x.col1 - x.col0;
-  }
-  l.fine = runs || (!list.empty() && piece_bytes < uint64_t(TILE_BYTES) * list.size());
-  // The forwarding variant holds 8 tiles of results in registers, which halves
-  // the work groups a CU can hold.  It pays on the large grids of group-major
-  // lists where most entries forward (chains: Ring AllReduce / AllGather, chain
-  // pipelines, about 90 % of their entries; 8 x 256 MiB fp32 Ring 1.150 -> 0.948
-  // ms), not where few do (trees and halving-doubling, 30-50 %: 9-14 % slower at
-  // 8 x 256 MiB), nor on resident grids, which are sized for the plain kernel's
-  // occupancy (Ring AllReduce 8 x 1-8 MiB: 22-100 % slower).
-  size_t marked = 0;
-  for (const DevItem& x : list) marked += (x.flags & (ITEM_SRC_FWD | ITEM_DSRC_FWD)) != 0;
-  l.fwd = group_major && marked > 0 && marked * 10 >= list.size() * 6;
+  l.fine = rl.fine;
+  l.fwd = rl.fwd;
+  l.fwd_saved = rl.fwd_saved;
   hipError_t he = hipMalloc(reinterpret_cast<void**>(&l.d_off), off.size() * sizeof(uint32_t));
   if (he != hipSuccess) return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
   he = hipMalloc(reinterpret_cast<void**>(&l.d_list), std::max<size_t>(list.size(), 1) * sizeof(DevItem));
@@ -511,7 +536,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   if (st != COLL_OK) return st;
   coll_algo_t chosen = algo;
   if (automatic) {
-    st = auto_algo(kind, N, count, sz, root, chosen);
+    st = auto_algo(kind, N, count, sz, root, uint32_t(di->cus), chosen);
     if (st != COLL_OK) return st;
   }
   const coll_algo_t ra = resolve_algo(kind, chosen);
@@ -562,6 +587,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
   const bool has_reduce = kind == COLL_K_ALLREDUCE || kind == COLL_K_REDUCESCATTER || kind == COLL_K_REDUCE;
   std::string dbg;  // launch shapes, for COLL_DEBUG
+  int64_t saved = 0;  // bytes the forwarding variant neither loads nor stores
   for (size_t pi = 0; pi < b.phases.size(); ++pi) {
     const Phase& ph = b.phases[pi];
     if (ph.kind == Phase::ROWS) {
@@ -596,10 +622,12 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         he = launch_rows(a, dt, int(op), cks, ntmask, L->fine, L->fwd, grid, stream);
         if (he != hipSuccess) return hip_fail(he, "row kernel launch");
       }
+      const bool fwd_on = forwarding_runs(L->fwd, L->fine, ntmask, bases16);
+      if (fwd_on) saved += int64_t(L->fwd_saved);
       if (g_debug.load())
         dbg += " | rows steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
                std::to_string(grid) + " group_tiles " + std::to_string(gt) + (L->fine ? " fine" : "") +
-               (L->fwd && !L->fine && ntmask <= 1 ? " forwarding" : "") + " nt " +
+               (fwd_on ? " forwarding" : "") + " nt " +
                std::to_string(ntmask) + " launches " + std::to_string(L->launches);
     } else {
       PermArgs a{};
@@ -651,6 +679,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
                  kind_name(kind), algo_name(ra), N, (long long)count, sz, inplace ? "in-place" : "out-of-place",
                  (long long)b.counts.steps, (long long)b.counts.rows, (long long)b.counts.hbm_bytes, dbg.c_str());
   t_last = b.counts;
+  t_last.moved_bytes = b.counts.hbm_bytes - saved;
   return COLL_OK;
 }
 
@@ -694,7 +723,10 @@ coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t c
     if (algo == COLL_ALGO_AUTO) {
       coll_status_t st = build_schedule(kind, COLL_ALGO_DEFAULT, nranks, 0, root, 1, s, err);
       if (st != COLL_OK) return fail(st, err);
-      st = choose_algo(kind, nranks, int64_t(count), sz, root, cost_model(), algo, err);
+      const std::function<int64_t(const Schedule&)> moved = [&](const Schedule& x) {
+        return planned_moved_bytes(x, sz, PLAN_CUS);
+      };
+      st = choose_algo(kind, nranks, int64_t(count), sz, root, cost_model(), algo, err, &moved);
       if (st != COLL_OK) return fail(st, err);
       chunks = 1;
     }
@@ -702,7 +734,10 @@ coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t c
     if (st != COLL_OK) return fail(st, err);
     const size_t cap = *nrows;
     *nrows = s.rows.size();
-    if (counts) *counts = count_schedule(s, sz);
+    if (counts) {
+      *counts = count_schedule(s, sz);
+      counts->moved_bytes = planned_moved_bytes(s, sz, PLAN_CUS);
+    }
     if (rows) {
       if (cap < s.rows.size()) return fail(COLL_ERR_INVALID_ARG, "row capacity too small");
       for (size_t i = 0; i < s.rows.size(); ++i) {

@@ -468,4 +468,49 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
   }
 }
 
+RowsList plan_rows_list(const Bound& b, const Phase& ph, uint64_t cap, uint32_t group_tiles, bool reverse,
+                        bool per_step, bool group_major) {
+  RowsList r;
+  const uint64_t gbytes = uint64_t(group_tiles) * TILE_BYTES;
+  const uint64_t groups = std::max<uint64_t>(1, (ph.colspace + gbytes - 1) / gbytes);
+  // Groups split at row boundaries when every group (split halves included)
+  // gets a work group of its own.  A group holding the end of one row and the
+  // start of the next would give its work group two chains of pieces to run one
+  // after the other, twice the round trips of any other work group (8 x 64 MiB
+  // uint8 Broadcast in 13 chunks: 160 -> 138 us).  With several groups per work
+  // group a split adds as many pieces to some list as it saves.
+  std::vector<uint64_t> cuts = group_cuts(ph, gbytes);
+  if (groups + cuts.size() > cap) cuts.clear();
+  r.G = uint32_t(std::min(groups + cuts.size(), cap));
+  build_worklist(b, ph, r.G, group_tiles, reverse, per_step, group_major, cuts, r.off, r.list);
+  // the fine variant pays off when pieces are small: some runs, or pieces of
+  // less than one tile on average
+  uint64_t piece_bytes = 0;
+  bool runs = false;
+  size_t marked = 0;
+  for (const DevItem& x : r.list) {
+    runs = runs || (x.flags & ITEM_BATCH_NEXT);
+    piece_bytes += x.col1 - x.col0;
+    marked += (x.flags & (ITEM_SRC_FWD | ITEM_DSRC_FWD)) != 0;
+  }
+  r.fine = runs || (!r.list.empty() && piece_bytes < uint64_t(TILE_BYTES) * r.list.size());
+  // The forwarding variant holds 8 tiles of results in registers, which halves
+  // the work groups a CU can hold.  It pays on the large grids of group-major
+  // lists where most entries forward (chains: Ring AllReduce / AllGather, chain
+  // pipelines, about 90 % of their entries; 8 x 256 MiB fp32 Ring 1.150 -> 0.948
+  // ms), not where few do (trees and halving-doubling, 30-50 %: 9-14 % slower at
+  // 8 x 256 MiB), nor on resident grids, which are sized for the plain kernel's
+  // occupancy (Ring AllReduce 8 x 1-8 MiB: 22-100 % slower).
+  r.fwd = group_major && marked > 0 && marked * 10 >= r.list.size() * 6;
+  if (r.fwd)
+    for (const DevItem& x : r.list) {
+      if (!fwd_eligible(x.col0, x.col1, x.flags)) continue;
+      const uint64_t w = x.col1 - x.col0;
+      if (x.flags & ITEM_SRC_FWD) r.fwd_saved += w;
+      if ((x.flags & ITEM_REDUCE) && (x.flags & ITEM_DSRC_FWD)) r.fwd_saved += w;
+      if (x.flags & ITEM_NO_STORE) r.fwd_saved += w;
+    }
+  return r;
+}
+
 }  // namespace coll

@@ -68,6 +68,21 @@ void build_worklist(const Bound& b, const Phase& ph, uint32_t G, uint32_t group_
                     bool per_step, bool group_major, const std::vector<uint64_t>& cuts, std::vector<uint32_t>& off,
                     std::vector<DevItem>& list);
 
+// The host side of one row phase's launches: the work lists of build_worklist
+// on a grid of G = min(column groups (+ row-boundary cuts when they fit), cap)
+// work groups, and the row-kernel variant that runs them.
+struct RowsList {
+  uint32_t G = 1;
+  bool fine = false;        // the fine variant (runs, or pieces of under one tile on average)
+  bool fwd = false;         // the forwarding variant (group-major, at least 60 % of entries forward)
+  uint64_t fwd_saved = 0;   // bytes the forwarding variant neither loads nor stores
+  std::vector<uint32_t> off;
+  std::vector<DevItem> list;
+};
+
+RowsList plan_rows_list(const Bound& b, const Phase& ph, uint64_t cap, uint32_t group_tiles, bool reverse,
+                        bool per_step, bool group_major);
+
 // ---- launch shape of a row phase ----------------------------------------------
 
 // Column spaces of at least BLOCKED_MIN_COLSPACE bytes get large grids: one

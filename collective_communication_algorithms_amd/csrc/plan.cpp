@@ -593,7 +593,7 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
 }
 
 coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size, int root, const CostModel& m,
-                          coll_algo_t& out, std::string& err) {
+                          coll_algo_t& out, std::string& err, const std::function<int64_t(const Schedule&)>* bytes) {
   std::vector<coll_algo_t> cand;
   switch (kind) {
     case COLL_K_ALLREDUCE: cand = {COLL_ALGO_DBT, COLL_ALGO_RHD, COLL_ALGO_RING}; break;
@@ -625,7 +625,8 @@ coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size,
       continue;
     }
     const coll_counts_t c = count_schedule(s, elem_size);
-    const double t = double(c.steps) * m.alpha_s + double(c.hbm_bytes) / m.beta_Bps;
+    const double moved = bytes ? double((*bytes)(s)) : double(c.hbm_bytes);
+    const double t = double(c.steps) * m.alpha_s + moved / m.beta_Bps;
     if (!have || t < best) {
       best = t;
       out = a;
@@ -645,6 +646,7 @@ coll_counts_t count_schedule(const Schedule& s, int elem_size) {
       const Row& r = s.rows[size_t(i)];
       edge[{r.src, r.dst}] += r.n;
       c.hbm_bytes += (r.reduce ? 3 : 2) * r.n * elem_size;
+      c.moved_bytes += (r.reduce ? 3 : 2) * r.n * elem_size;
     }
     if (!st.local) {
       int64_t m = 0;

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <cstdint>
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -49,10 +50,12 @@ struct CostModel {
 };
 
 // COLL_ALGO_AUTO: among the collective's candidate algorithms valid for N, the
-// one whose schedule minimises steps * alpha + schedule bytes / beta (first
-// candidate on ties).  Returns COLL_OK and the algorithm, or an error.
+// one whose schedule minimises steps * alpha + bytes / beta (first candidate on
+// ties), where bytes is `bytes(schedule)` if given, else the schedule's bytes.
+// Returns COLL_OK and the algorithm, or an error.
 coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size, int root, const CostModel& m,
-                          coll_algo_t& out, std::string& err);
+                          coll_algo_t& out, std::string& err,
+                          const std::function<int64_t(const Schedule&)>* bytes = nullptr);
 
 // Validates (kind, algo, N, count, root, chunks) and builds the in-place
 // schedule.  Returns COLL_OK or an error status with a message in `err`.

@@ -191,18 +191,29 @@ typedef struct {
  * for Ring AllReduce); rows: schedule rows; crit_bytes: per step the largest
  * byte total on one (src, dst) edge, summed over steps (the beta term of
  * [P3]'s alpha-beta model); hbm_bytes: bytes the rows read and write (copy
- * 2*n*size, reduce 3*n*size). */
-typedef struct { int64_t steps, rows, crit_bytes, hbm_bytes; } coll_counts_t;
+ * 2*n*size, reduce 3*n*size); moved_bytes: the part of hbm_bytes that goes
+ * through memory: the rest is operands the row kernel passes from one step to
+ * the next in registers and stores it skips because a later step overwrites
+ * them, or they lie outside the defined output and nothing reads them again
+ * (only lists over 32 MiB or more of columns whose entries mostly form such
+ * chains, as Ring's do, run that way). */
+typedef struct { int64_t steps, rows, crit_bytes, hbm_bytes, moved_bytes; } coll_counts_t;
 
 /* Build the in-place schedule of a collective.  rows may be NULL; *nrows is
  * the capacity on input and the number of rows on output (COLL_ERR_INVALID_ARG
  * if the capacity is too small, with *nrows set to what is needed).  counts
- * may be NULL.  Validation as for the collective calls (without pointers). */
+ * may be NULL; its moved_bytes is planned for an in-place call on 16-byte
+ * aligned buffers with the current options on MI355X's 256 compute units.
+ * Validation as for the collective calls (without pointers).  COLL_ALGO_AUTO
+ * picks the candidate that minimises steps * alpha + moved_bytes / beta
+ * (COLL_OPT_MODEL_ALPHA_NS / _BETA_GBPS), planned so here and for the calling
+ * device's compute units in a collective call. */
 coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t count, coll_dtype_t dtype,
                         int root, int chunks, coll_row_t* rows, size_t* nrows, coll_counts_t* counts);
 
 /* Counts of the last successful collective call on this thread, as executed
- * (an out-of-place call adds local copies to hbm_bytes). */
+ * (an out-of-place call adds local copies to hbm_bytes; moved_bytes counts
+ * what the launched kernels moved). */
 coll_status_t coll_get_stats(coll_counts_t* last);
 
 /* Per-row checksums.  When `dev_sums` is non-NULL (a device array of
@@ -248,7 +259,7 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  * COLL_OPT_REVERSE         1: odd steps walk their columns backwards, so data
  *                          written last is read first [1]; 0: always forwards.
  * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
- * COLL_OPT_MODEL_BETA_GBPS schedule-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
+ * COLL_OPT_MODEL_BETA_GBPS moved-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
  * COLL_OPT_CACHE_BYTES     device memory the schedule cache may hold, in bytes
  *                          [2^31]; least recently used schedules are dropped
  *                          (after synchronising their device) when a call

@@ -296,6 +296,37 @@ def test_repeated_calls_reuse_cached_schedules():
     assert np.array_equal(got, ((s + (1 << 31)) % (1 << 32)) - (1 << 31))
     st = coll.coll_get_stats()
     assert st["steps"] == 14 and st["hbm_bytes"] == 35 * count * 4
+    assert st["moved_bytes"] == st["hbm_bytes"]  # 256 KiB per rank: nothing forwards
+
+
+@pytest.mark.gpu
+def test_forwarding_moves_what_the_plan_says():
+    """Ring AllReduce 8 x 64 MiB fp32 in place: the launched lists forward, and
+    the call moves 2NM bytes (each input read once, each result written once),
+    as coll_plan plans it; the result is the exact sum (integer-valued floats).
+    Misaligned rank buffers keep the plain path: every schedule byte moves."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    N, M = 8, 64 << 20
+    count = M // 4
+    buf = torch.empty((N, count + 4), dtype=torch.float32, device="cuda:0")
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    buf.copy_(torch.randint(-1000, 1000, buf.shape, generator=g, device="cuda:0").float())
+    want = buf[:, :count].sum(dim=0)
+    ranks = [buf[i, :count] for i in range(N)]
+    coll.coll_allreduce(ranks, algo="ring")
+    torch.cuda.synchronize()
+    st = coll.coll_get_stats()
+    _, plan = coll.coll_plan("allreduce", "ring", N, count, "float32")
+    assert st["moved_bytes"] == plan["moved_bytes"] == 2 * N * M
+    for r in ranks:
+        assert torch.equal(r, want)
+    # 4-byte offset: rank bases are no longer 16-byte aligned
+    ranks = [buf[i, 1:count + 1] for i in range(N)]
+    coll.coll_allreduce(ranks, algo="ring")
+    torch.cuda.synchronize()
+    st = coll.coll_get_stats()
+    assert st["moved_bytes"] == st["hbm_bytes"] == 5 * (N - 1) * M
 
 
 @pytest.mark.parametrize("N", [3, 5, 6, 7, 12, 13])
