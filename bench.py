@@ -204,7 +204,11 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
              "t_med_us": round(med * 1e3, 2), "t_min_us": round(mn * 1e3, 2),
              "algbw_GBps": round(algbw, 3), "busbw_GBps": round(algbw * model.busbw_coef(kind, N), 3),
              "sched_TBps": round(st["hbm_bytes"] / (med * 1e-3) / 1e12, 3),
-             "pct_of_8TBps": round(100 * st["hbm_bytes"] / (med * 1e-3) / 8e12, 2)}
+             "pct_of_8TBps": round(100 * st["hbm_bytes"] / (med * 1e-3) / 8e12, 2),
+             # what the launched kernels moved through memory (operands passed in
+             # registers and skipped stores left out), and its rate
+             "moved_bytes": st["moved_bytes"],
+             "moved_TBps": round(st["moved_bytes"] / (med * 1e-3) / 1e12, 3)}
         try:
             mk = "broadcast" if kind == "broadcast" else kind
             r["ab_page_us"] = round(model.time(mk, algo, N, M, 5e-6, 450e9, k) * 1e6, 2)
@@ -685,6 +689,9 @@ def main() -> int:
         # committed rocprofv3 counters, scaled) per mean launch time
         "fabric_traffic_GBps": round(traffic / (launch_ms * 1e-3) / 1e9, 1) if traffic else None,
         "fabric_pct_of_peak": round(100 * traffic / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2) if traffic else None,
+        # the library's own count of the bytes the launched kernels moved (the
+        # schedule bytes less operands passed in registers and skipped stores)
+        "moved_bytes_per_call": stats["moved_bytes"],
         "cpu_baseline": None,
         "alpha_beta_page_model_ms": round(pred_ms, 4),
         "parity": "within the binary32 error bound of the fp64 sum on %d sampled columns per rank" % len(cols),
