@@ -33,7 +33,7 @@ METRIC = "busbw GB/s & % HBM peak, Ring AllReduce fp32 N=8 M=256MiB (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_kernel_ring_allreduce_fp32_n8_256MiB.json")
 # the row kernel variant the default run times: fp32, sum, per-row checksums,
 # nontemporal source loads, not the fine variant
-HEADLINE_KERNEL = "void coll::rows_kernel<2, 0, true, 1, false, true>"
+HEADLINE_KERNEL = "void coll::rows_kernel<2, 0, true, 5, false, true>"
 
 
 def kernel_source_hash() -> str:

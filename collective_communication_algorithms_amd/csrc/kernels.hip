@@ -684,11 +684,12 @@ template <int DT, int OP, bool CKS>
 static RowsFn rows_fn_nt(uint32_t nt, bool fine, bool fwd) {
   // lists of small pieces come from small footprints, which stay in the
   // caches: the fine variant exists for the all-cached mask only; the
-  // forwarding variant for the masks the automatic policy picks outside
-  // AllToAll (none, source loads)
+  // forwarding variant for the masks the automatic policy picks for it (none,
+  // source loads, source loads and stores)
   if (fine && (nt & 7u) == 0) return rows_kernel<DT, OP, CKS, 0, true, false>;
   if (fwd && (nt & 7u) == 0) return rows_kernel<DT, OP, CKS, 0, false, true>;
-  if (fwd && (nt & 7u) == 1) return rows_kernel<DT, OP, CKS, 1, false, true>;
+  if (fwd && (nt & 7u) == NT_SRC) return rows_kernel<DT, OP, CKS, NT_SRC, false, true>;
+  if (fwd && (nt & 7u) == (NT_SRC | NT_DST)) return rows_kernel<DT, OP, CKS, NT_SRC | NT_DST, false, true>;
   switch (nt & 7u) {
     case 0: return rows_kernel<DT, OP, CKS, 0, false, false>;
     case 1: return rows_kernel<DT, OP, CKS, 1, false, false>;
