@@ -492,8 +492,10 @@ def single_call(args, dev) -> int:
             for i in (0, N - 1):
                 ok &= bool(torch.equal(out[j][i * B:(i + 1) * B], pristine[i][j * B:(j + 1) * B]))
     else:
-        got = out.index_select(1, cols_t).cpu().numpy()
-        src = pristine.index_select(1, cols_t).cpu().numpy()
+        # copies: compare bit patterns (numpy has no bfloat16)
+        bits = (lambda t: t.view(torch.int16)) if dtype == "bfloat16" else (lambda t: t)
+        got = bits(out.index_select(1, cols_t)).cpu().numpy()
+        src = bits(pristine.index_select(1, cols_t)).cpu().numpy()
         for i in range(N):
             if kind == "broadcast":
                 ok &= bool(np.array_equal(got[i], src[root]))
