@@ -255,7 +255,9 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          2 old-destination loads, 4 stores; -1: automatic
  *                          [-1]: none while all rank buffers together fit the
  *                          256 MiB memory-side cache, else source loads only
- *                          (AllToAll: source loads and stores).
+ *                          (AllToAll, and the row lists of reducing calls
+ *                          that pass results between steps in registers:
+ *                          source loads and stores).
  * COLL_OPT_REVERSE         1: odd steps walk their columns backwards, so data
  *                          written last is read first [1]; 0: always forwards.
  * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
