@@ -28,8 +28,10 @@ def _defaults(gpu_device):
     yield
 
 
-def sample_columns(count, N, stride=4097, edge=65536, around=256):
+def sample_columns(count, N, stride=4097, edge=65536, around=256, extra=()):
     parts = [np.arange(0, count, stride), np.arange(0, min(edge, count)), np.arange(max(0, count - edge), count)]
+    for c in extra:
+        parts.append(np.arange(max(0, c - around), min(count, c + around)))
     for c in range(1, N):
         b = c * count // N
         parts.append(np.arange(max(0, b - around), min(count, b + around)))
@@ -42,13 +44,13 @@ def gather_cols(tensors, cols, dtype):
     return [si.tensor_to_host(t.index_select(0, idx), dtype) for t in tensors]
 
 
-def check_sampled(kind, algo, N, count, dtype, workload, sigma=1.0, root=0, k=1):
+def check_sampled(kind, algo, N, count, dtype, workload, sigma=1.0, root=0, k=1, extra=()):
     import torch
     import collective_communication_algorithms_amd as coll
     dev = torch.device("cuda:0")
     buf = torch.empty((N, count), dtype=si.to_torch_dtype(dtype), device=dev)
     ranks = si.device_rank_tensors(workload, N, count, dtype, dev, sigma=sigma, out=buf)
-    cols = sample_columns(count, N)
+    cols = sample_columns(count, N, extra=extra)
     before = gather_cols(ranks, cols, dtype)
     coll.COLLECTIVE_FNS[kind](ranks, op="sum", algo=algo, root=root, chunks=k)
     torch.cuda.synchronize()
@@ -142,3 +144,14 @@ def test_alltoall_n32_512x4096(algo):
             assert np.array_equal(got[j][i * S:(i + 1) * S], red_in[i][j * S:(j + 1) * S])
     del sbuf, rbuf, send, recv
     torch.cuda.empty_cache()
+
+
+def test_columns_past_4GiB():
+    """Rank buffers of 4.5 GiB and a few bytes: column offsets past 2^32 bytes
+    in the schedules, the work lists and the row kernel's addresses.  Chain
+    Broadcast of uint8 over 3 ranks and Ring AllReduce of int32 over 2 ranks,
+    checked on sampled columns (around byte 2^32 too) against the oracle."""
+    nb = (9 << 29) + 77
+    check_sampled("broadcast", "chain_pipe", 3, nb, "uint8", 2, root=1, extra=(1 << 32,))
+    n4 = (9 << 29) // 4 + 5
+    check_sampled("allreduce", "ring", 2, n4, "int32", 3, extra=((1 << 32) // 4,))
