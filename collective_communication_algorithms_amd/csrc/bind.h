@@ -89,10 +89,14 @@ RowsList plan_rows_list(const Bound& b, const Phase& ph, uint64_t cap, uint32_t 
 // column group per work group (BLOCKED_GROUP_TILES_COPY tiles for copy-only
 // schedules, BLOCKED_GROUP_TILES_REDUCE with reduce rows), or the cache window
 // of rows_shape.  Smaller ones get a grid of the work groups that fit on the
-// device at once.
+// device at once.  8 MiB: against the earlier 32 MiB, 8 ranks x 8-24 MiB ran
+// 9-51 % faster in nearly every collective (Ring AllReduce fp32 16 MiB 78.0 ->
+// 52.6 us, Ring AllGather bf16 32 ranks x 16 MiB 187 -> 91 us, chain Broadcast
+// 16 MiB 39.9 -> 25.7 us; binomial Gather 16 MiB 11.5 -> 12.2 us); at 2 MiB
+// the large grid made Ring AllReduce slower (20 -> 31 us).
 constexpr uint32_t BLOCKED_GROUP_TILES_REDUCE = 4;
 constexpr uint32_t BLOCKED_GROUP_TILES_COPY = 8;
-constexpr uint64_t BLOCKED_MIN_COLSPACE = uint64_t(32) << 20;
+constexpr uint64_t BLOCKED_MIN_COLSPACE = uint64_t(8) << 20;
 
 struct RowsShapeInput {
   uint64_t colspace = 0;

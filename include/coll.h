@@ -195,7 +195,7 @@ typedef struct {
  * through memory: the rest is operands the row kernel passes from one step to
  * the next in registers and stores it skips because a later step overwrites
  * them, or they lie outside the defined output and nothing reads them again
- * (only lists over 32 MiB or more of columns whose entries mostly form such
+ * (only lists over 8 MiB or more of columns whose entries mostly form such
  * chains, as Ring's do, run that way). */
 typedef struct { int64_t steps, rows, crit_bytes, hbm_bytes, moved_bytes; } coll_counts_t;
 
@@ -236,18 +236,16 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          no synchronisation between work groups.
  *                          1: one launch per step (the launches order the steps).
  * COLL_OPT_GROUP_TILES     4 KiB column tiles per work-group column group, 1..64
- *                          [0: automatic.  Column spaces of 32 MiB or more:
- *                          int32 / fp32 / bf16 reductions use 4-tile groups on
- *                          2 work groups per CU (schedules whose groups see two
- *                          or more rows per step) or 8-tile groups on 3 per CU
- *                          (2 when that leaves a work group a single group),
- *                          each work group taking its groups one at a time;
- *                          copy-only schedules over 16 or more ranks whose
- *                          groups see two or more rows per step do the same
- *                          with 4-tile groups on 2 per CU; other schedules one
- *                          group per work group, 8 tiles (4 with reduce rows).
- *                          Smaller column spaces: up to 8 tiles over a grid of
- *                          the work groups that fit on the device at once.  Whenever every group has a work
+ *                          [0: automatic.  Column spaces of 8 MiB or more:
+ *                          int32 / fp32 / bf16 reductions whose groups see two
+ *                          or more rows per step (trees, halving-doubling),
+ *                          and copy-only schedules over 16 or more ranks that
+ *                          do, use 4-tile groups on 2 work groups per CU, each
+ *                          work group taking its groups one at a time; other
+ *                          schedules one group per work group, 8 tiles (4 for
+ *                          uint8 reductions).  Smaller column spaces: up to 8
+ *                          tiles over a grid of the work groups that fit on
+ *                          the device at once.  Whenever every group has a work
  *                          group of its own, groups are also split where a row
  *                          starts or ends inside them].
  * COLL_OPT_MAX_GRID        cap on work groups per launch, up to 2^20 [0: automatic].

@@ -1,4 +1,4 @@
-"""Seeded random calls at large sizes (column spaces of 32 to 96 MiB, where
+"""Seeded random calls at large sizes (column spaces of 8 to 96 MiB, where
 the large-grid launch shapes apply: the cache window, the copy-only rule, and
 groups split at row boundaries when every group has a work group of its own),
 checked on sampled columns the oracle computes exactly (every collective but
@@ -36,7 +36,7 @@ def draw(i):
         else int(rng.integers(2, 21))
     dtype = str(rng.choice(["int32", "uint8", "float32", "bfloat16"]))
     sz = si.ITEMSIZE[dtype]
-    count = int(rng.integers(32 << 20, 96 << 20)) // sz
+    count = int(rng.integers(8 << 20, 96 << 20)) // sz
     op = str(rng.choice(["sum", "max", "min"]))
     root = int(rng.integers(0, N))
     k = int(rng.integers(1, 18)) if algo in PIPELINED else 1

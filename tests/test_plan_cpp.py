@@ -210,7 +210,7 @@ def test_auto_extremes():
 
 @pytest.mark.parametrize("kind", list(CANDIDATES))
 def test_moved_bytes_are_the_schedule_bytes_on_small_columns(kind):
-    """Below 32 MiB of columns no list runs in the forwarding variant: every
+    """Below 8 MiB of columns no list runs in the forwarding variant: every
     operand is loaded and every result stored."""
     N = 8
     for algo in CANDIDATES[kind]:
@@ -265,7 +265,7 @@ def test_moved_bytes_follow_the_options():
 def test_auto_picks_ring_on_large_columns():
     """With the default model, Ring wins once its chains forward (8 x 64 MiB
     fp32: Ring 208 us, DBT 257, RHD 265 measured on MI355X), and the fewer
-    steps of RHD / DBT win below 32 MiB, where nothing forwards."""
+    steps of RHD / DBT win below 8 MiB, where nothing forwards."""
     big = coll_plan("allreduce", "auto", 8, (64 << 20) // 4, "float32", 0, 1)
     assert big == coll_plan("allreduce", "ring", 8, (64 << 20) // 4, "float32", 0, 1)
     small = coll_plan("allreduce", "auto", 8, (1 << 20) // 4, "float32", 0, 1)
