@@ -172,6 +172,13 @@ RowsShape rows_shape(const RowsShapeInput& in, Several&& several) {
       }
     }
   }
+  // fewer 8-tile groups than 2 per CU (8 x 8 MiB: 256): 4-tile groups, twice
+  // as many (8 ranks x 8 MiB: Ring AllReduce fp32 31.0 -> 28.4 us, Ring
+  // ReduceScatter bf16 26.6 -> 22.6, Ring AllGather 18.4 -> 17.1, chain
+  // Broadcast 18.4 -> 17.0; at 16 MiB and up 8 tiles are as fast or faster)
+  if (blocked && in.forced_group_tiles <= 0 && r.group_tiles == 8 &&
+      (in.colspace + 8 * TILE_BYTES - 1) / (8 * TILE_BYTES) < 2 * uint64_t(in.cus))
+    r.group_tiles = 4;
   if (in.forced_group_tiles > 0) r.group_tiles = uint32_t(in.forced_group_tiles);
   if (in.forced_grid > 0) r.cap = uint64_t(in.forced_grid);
   return r;

@@ -565,6 +565,8 @@ void check_launch_shapes() {
       {"Ring AR u8 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 1, false, 0, 0, -1, 4, big, true},
       {"Ring AR fp32 8x16MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 16 << 20, 4, false, 0, 0, 0, 8, big, true},
       {"Ring AR fp32 8x4MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 4 << 20, 4, false, 0, 0, -1, 1, 2048, false},
+      {"Ring AR fp32 8x8MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 8 << 20, 4, false, 0, 0, 0, 4, big, true},
+      {"chain Bcast u8 8x8MiB", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 8, 1, 8 << 20, 1, false, 0, 0, -1, 4, big, true},
       {"Ring AR fp32 8x256MiB per step", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, true, 0, 0, -1, 8, 8192,
        false},
       {"Ring AR fp32 8x256MiB forced", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, false, 2, 100, -1, 2, 100,
