@@ -541,3 +541,19 @@ def test_checksum_buffers_grow_and_are_evicted():
                 assert np.array_equal(got, want), (rnd, i, algo)
     finally:
         coll.coll_set_checksums(None)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind,factor", [("allreduce", lambda N: 2 * N), ("reducescatter", lambda N: N + 1),
+                                         ("allgather", lambda N: N)])
+def test_ring_chains_forward_at_16MiB(kind, factor):
+    """Ring over 8 ranks x 16 MiB fp32 in place, on the large grid: bit-exact
+    against the oracle, and the launched kernels move the closed-form bytes
+    (AllReduce 2NM, ReduceScatter (N+1)M, AllGather NM), as coll_plan plans."""
+    import collective_communication_algorithms_amd as coll
+    N, count = 8, (16 << 20) // 4
+    a = si.rank_arrays(77, N, count, "float32")
+    assert_parity(kind, "ring", a, "float32")
+    st = coll.coll_get_stats()
+    _, plan = coll.coll_plan(kind, "ring", N, count, "float32")
+    assert st["moved_bytes"] == plan["moved_bytes"] == factor(N) * count * 4, (st, plan)
