@@ -42,7 +42,7 @@ def kernel_source_hash() -> str:
     that the committed counter summary is dropped whenever any of it changes."""
     import re
     h = hashlib.sha256()
-    for f in ("kernels.hip", "device_types.h", "abi.cpp", "bind.cpp"):
+    for f in ("kernels.hip", "device_types.h", "abi.cpp", "bind.h", "bind.cpp"):
         with open(os.path.join(ROOT, "collective_communication_algorithms_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)

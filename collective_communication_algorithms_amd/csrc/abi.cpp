@@ -214,6 +214,7 @@ int64_t planned_moved_bytes(const Schedule& s, int sz, uint32_t cus) {
     if (ph.kind != Phase::ROWS) continue;
     RowsShapeInput in;
     in.colspace = ph.colspace;
+    in.segment = phase_segment(ph);
     in.has_reduce = has_reduce;
     in.elem_size = sz;
     in.nranks = s.N;
@@ -607,6 +608,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (ph.kind == Phase::ROWS) {
       RowsShapeInput in;
       in.colspace = ph.colspace;
+      in.segment = phase_segment(ph);
       in.has_reduce = has_reduce;
       in.elem_size = sz;
       in.nranks = N;

@@ -286,6 +286,8 @@ bool several_pieces_per_step(const Bound& b, const Phase& ph) {
   return pieces >= 2 * groups * uint64_t(ph.s1 - ph.s0);
 }
 
+uint64_t phase_segment(const Phase& ph) { return ph.colspace / (uint64_t(ph.bounds.size()) + 1); }
+
 uint32_t resident_group_tiles(uint64_t colspace, uint64_t max_groups) {
   const uint64_t tiles = (colspace + TILE_BYTES - 1) / TILE_BYTES;
   uint32_t gt = 8;

@@ -97,9 +97,16 @@ RowsList plan_rows_list(const Bound& b, const Phase& ph, uint64_t cap, uint32_t 
 constexpr uint32_t BLOCKED_GROUP_TILES_REDUCE = 4;
 constexpr uint32_t BLOCKED_GROUP_TILES_COPY = 8;
 constexpr uint64_t BLOCKED_MIN_COLSPACE = uint64_t(8) << 20;
+// Long pieces (see rows_shape): at least this many bytes of columns, and rows
+// that start or end no more often than every LONG_PIECE_REDUCE bytes
+// (reductions) or LONG_PIECE_COPY bytes (copies) on average.
+constexpr uint64_t LONG_PIECE_MIN_COLSPACE = uint64_t(64) << 20;
+constexpr uint64_t LONG_PIECE_REDUCE = uint64_t(8) << 20;
+constexpr uint64_t LONG_PIECE_COPY = uint64_t(16) << 20;
 
 struct RowsShapeInput {
   uint64_t colspace = 0;
+  uint64_t segment = 0;             // mean bytes between the phase's row boundaries (phase_segment)
   bool has_reduce = false;
   int elem_size = 4;
   int nranks = 1;
@@ -120,6 +127,10 @@ struct RowsShape {
 // step (halving-doubling, trees, RHD AllGather, binomial Broadcast) or not
 // (Ring, chains).
 bool several_pieces_per_step(const Bound& b, const Phase& ph);
+
+// The mean length in bytes of the column ranges between a row phase's row
+// boundaries: colspace / (boundaries + 1).
+uint64_t phase_segment(const Phase& ph);
 
 // Group size for a grid of `max_groups` work groups: enough groups to give
 // each of them one, up to 8 tiles per group.
@@ -152,7 +163,12 @@ uint32_t resident_group_tiles(uint64_t colspace, uint64_t max_groups);
 // (64-rank AllGather).  One launch per step: 4 resident grids' worth of groups
 // per launch.
 template <class Several>
-RowsShape rows_shape(const RowsShapeInput& in, Several&& several) {
+RowsShape rows_shape(const RowsShapeInput& in, Several&& several_pieces) {
+  int known = -1;  // several_pieces(), asked at most once
+  auto several = [&] {
+    if (known < 0) known = several_pieces() ? 1 : 0;
+    return known != 0;
+  };
   RowsShape r;
   const bool blocked = !in.per_step && in.colspace >= BLOCKED_MIN_COLSPACE;
   r.group_major = blocked;
@@ -178,6 +194,21 @@ RowsShape rows_shape(const RowsShapeInput& in, Several&& several) {
   // Broadcast 18.4 -> 17.0; at 16 MiB and up 8 tiles are as fast or faster)
   if (blocked && in.forced_group_tiles <= 0 && r.group_tiles == 8 &&
       (in.colspace + 8 * TILE_BYTES - 1) / (8 * TILE_BYTES) < 2 * uint64_t(in.cus))
+    r.group_tiles = 4;
+  // Long pieces, one per step: 4-tile groups, one per work group, against 8
+  // tiles.  Reductions, pieces of 8 MiB and more: Ring AllReduce fp32 8 x 256
+  // MiB 831 -> 808 us, bf16 833 -> 782, fp32 8 x 128 MiB 431 -> 404, bf16 16 x
+  // 192 MiB 1290 -> 1215, fp32 32 x 256 MiB 3397 -> 3309, Ring ReduceScatter
+  // fp32 8 x 128 MiB 253 -> 244.  Copies, pieces of 16 MiB and more: Ring
+  // AllGather bf16 8 x 256 MiB 412 -> 396, 8 x 128 MiB 197.5 -> 192.3, chain
+  // Broadcast uint8 8 x 256 MiB 420 -> 400.  Shorter pieces keep 8 tiles: 64 x
+  // 256 MiB bf16 (4 MiB pieces) ReduceScatter 3144 against 3534 us, AllGather
+  // 3219 against 3350; AllGather bf16 32 x 256 MiB (8 MiB) 1622 against 1663,
+  // 8 x 96 MiB (12 MiB) 141 against 144; chain Broadcast 8 x 96 MiB 143
+  // against 145.
+  if (blocked && in.forced_group_tiles <= 0 && r.group_tiles == 8 && r.cap == (uint64_t(1) << 20) &&
+      in.colspace >= LONG_PIECE_MIN_COLSPACE &&
+      in.segment >= (in.has_reduce ? LONG_PIECE_REDUCE : LONG_PIECE_COPY) && !several())
     r.group_tiles = 4;
   if (in.forced_group_tiles > 0) r.group_tiles = uint32_t(in.forced_group_tiles);
   if (in.forced_grid > 0) r.cap = uint64_t(in.forced_grid);

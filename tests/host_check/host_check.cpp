@@ -546,7 +546,7 @@ void check_launch_shapes() {
   };
   const uint64_t big = uint64_t(1) << 20;
   const Case cases[] = {
-      {"Ring AR fp32 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, false, 0, 0, 0, 8, big, true},
+      {"Ring AR fp32 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, false, 0, 0, 0, 4, big, true},
       {"Ring AR fp32 8x32MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 32 << 20, 4, false, 0, 0, 0, 8, big, true},
       {"DBT AR fp32 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_DBT, 8, 1, 256 << 20, 4, false, 0, 0, 1, 4, 512, true},
       {"RHD AR bf16 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RHD, 8, 1, 256 << 20, 2, false, 0, 0, 1, 4, 512, true},
@@ -556,13 +556,23 @@ void check_launch_shapes() {
        true},
       {"RHD AG bf16 64x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RHD, 64, 1, 256 << 20, 2, false, 0, 0, 1, 4, 512, true},
       {"Ring AG bf16 64x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 64, 1, 256 << 20, 2, false, 0, 0, 0, 8, big, true},
-      {"binomial Bcast u8 8x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 8, 1, 64 << 20, 1, false, 0, 0, -1, 8, big,
+      {"binomial Bcast u8 8x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 8, 1, 64 << 20, 1, false, 0, 0, 1, 8, big,
        true},
       {"binomial Bcast u8 16x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 16, 1, 64 << 20, 1, false, 0, 0, 1, 4, 512,
        true},
       {"chain Bcast k=8 u8 16x64MiB", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 16, 8, 64 << 20, 1, false, 0, 0, 0, 8,
        big, true},
       {"Ring AR u8 8x256MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 1, false, 0, 0, -1, 4, big, true},
+      {"Ring AR fp32 8x64MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 64 << 20, 4, false, 0, 0, 0, 4, big, true},
+      {"Ring AR bf16 16x192MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 16, 1, 192 << 20, 2, false, 0, 0, 0, 4, big, true},
+      {"Ring AR fp32 8x48MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 48 << 20, 4, false, 0, 0, 0, 8, big, true},
+      {"Ring AG bf16 8x128MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 8, 1, 128 << 20, 2, false, 0, 0, 0, 4, big, true},
+      {"Ring AG bf16 8x96MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 8, 1, 96 << 20, 2, false, 0, 0, -1, 8, big, true},
+      {"Ring AG bf16 32x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 32, 1, 256 << 20, 2, false, 0, 0, 0, 8, big, true},
+      {"chain Bcast k=8 u8 8x256MiB", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 8, 8, 256 << 20, 1, false, 0, 0, 0, 4,
+       big, true},
+      {"binomial Bcast u8 8x256MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 8, 1, 256 << 20, 1, false, 0, 0, 1, 8,
+       big, true},
       {"Ring AR fp32 8x16MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 16 << 20, 4, false, 0, 0, 0, 8, big, true},
       {"Ring AR fp32 8x4MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 4 << 20, 4, false, 0, 0, -1, 1, 2048, false},
       {"Ring AR fp32 8x8MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 8 << 20, 4, false, 0, 0, 0, 4, big, true},
@@ -584,6 +594,7 @@ void check_launch_shapes() {
     const Phase& ph = b.phases[0];
     RowsShapeInput in;
     in.colspace = ph.colspace;
+    in.segment = phase_segment(ph);
     in.has_reduce = c.kind == COLL_K_ALLREDUCE || c.kind == COLL_K_REDUCESCATTER || c.kind == COLL_K_REDUCE;
     in.elem_size = c.sz;
     in.nranks = c.N;
