@@ -216,6 +216,7 @@ int64_t planned_moved_bytes(const Schedule& s, int sz, uint32_t cus) {
     in.colspace = ph.colspace;
     in.segment = phase_segment(ph);
     in.has_reduce = has_reduce;
+    in.checksums = t_sums != nullptr;
     in.elem_size = sz;
     in.nranks = s.N;
     in.cus = cus;
@@ -610,6 +611,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       in.colspace = ph.colspace;
       in.segment = phase_segment(ph);
       in.has_reduce = has_reduce;
+      in.checksums = cks;
       in.elem_size = sz;
       in.nranks = N;
       in.cus = uint32_t(di->cus);

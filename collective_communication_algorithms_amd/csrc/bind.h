@@ -97,10 +97,12 @@ RowsList plan_rows_list(const Bound& b, const Phase& ph, uint64_t cap, uint32_t 
 constexpr uint32_t BLOCKED_GROUP_TILES_REDUCE = 4;
 constexpr uint32_t BLOCKED_GROUP_TILES_COPY = 8;
 constexpr uint64_t BLOCKED_MIN_COLSPACE = uint64_t(8) << 20;
-// Long pieces (see rows_shape): at least this many bytes of columns, and rows
-// that start or end no more often than every LONG_PIECE_REDUCE bytes
-// (reductions) or LONG_PIECE_COPY bytes (copies) on average.
-constexpr uint64_t LONG_PIECE_MIN_COLSPACE = uint64_t(64) << 20;
+// Long pieces (see rows_shape): at least LONG_PIECE_MIN_COLSPACE_* bytes of
+// columns, and rows that start or end no more often than every
+// LONG_PIECE_REDUCE bytes (reductions) or LONG_PIECE_COPY bytes (copies) on
+// average.
+constexpr uint64_t LONG_PIECE_MIN_COLSPACE_REDUCE = uint64_t(64) << 20;
+constexpr uint64_t LONG_PIECE_MIN_COLSPACE_COPY = uint64_t(128) << 20;
 constexpr uint64_t LONG_PIECE_REDUCE = uint64_t(8) << 20;
 constexpr uint64_t LONG_PIECE_COPY = uint64_t(16) << 20;
 
@@ -108,6 +110,7 @@ struct RowsShapeInput {
   uint64_t colspace = 0;
   uint64_t segment = 0;             // mean bytes between the phase's row boundaries (phase_segment)
   bool has_reduce = false;
+  bool checksums = false;           // the kernels also compute per-row checksums
   int elem_size = 4;
   int nranks = 1;
   uint32_t cus = 1;                 // compute units of the device
@@ -201,13 +204,19 @@ RowsShape rows_shape(const RowsShapeInput& in, Several&& several_pieces) {
   // 192 MiB 1290 -> 1215, fp32 32 x 256 MiB 3397 -> 3309, Ring ReduceScatter
   // fp32 8 x 128 MiB 253 -> 244.  Copies, pieces of 16 MiB and more: Ring
   // AllGather bf16 8 x 256 MiB 412 -> 396, 8 x 128 MiB 197.5 -> 192.3, chain
-  // Broadcast uint8 8 x 256 MiB 420 -> 400.  Shorter pieces keep 8 tiles: 64 x
+  // Broadcast uint8 8 x 256 MiB 420 -> 400, 8 x 128 MiB in one piece 198 ->
+  // 192; but in 64 MiB of columns copies keep 8 tiles (chain Broadcast 8 x 64
+  // MiB in one piece 87 against 96 us, Ring AllGather bf16 4 x 64 MiB 48
+  // against 51).  Shorter pieces keep 8 tiles: 64 x
   // 256 MiB bf16 (4 MiB pieces) ReduceScatter 3144 against 3534 us, AllGather
   // 3219 against 3350; AllGather bf16 32 x 256 MiB (8 MiB) 1622 against 1663,
   // 8 x 96 MiB (12 MiB) 141 against 144; chain Broadcast 8 x 96 MiB 143
-  // against 145.
-  if (blocked && in.forced_group_tiles <= 0 && r.group_tiles == 8 && r.cap == (uint64_t(1) << 20) &&
-      in.colspace >= LONG_PIECE_MIN_COLSPACE &&
+  // against 145.  With row checksums twice as many groups make twice as many
+  // checksum atomics, which takes the gain away (Ring AllReduce fp32 8 x 256
+  // MiB: row kernel 0.827 ms with 8 tiles, 0.828-0.832 with 4), so calls with
+  // checksums keep 8 tiles.
+  if (blocked && !in.checksums && in.forced_group_tiles <= 0 && r.group_tiles == 8 && r.cap == (uint64_t(1) << 20) &&
+      in.colspace >= (in.has_reduce ? LONG_PIECE_MIN_COLSPACE_REDUCE : LONG_PIECE_MIN_COLSPACE_COPY) &&
       in.segment >= (in.has_reduce ? LONG_PIECE_REDUCE : LONG_PIECE_COPY) && !several())
     r.group_tiles = 4;
   if (in.forced_group_tiles > 0) r.group_tiles = uint32_t(in.forced_group_tiles);

@@ -244,10 +244,11 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          work group taking its groups one at a time; other
  *                          schedules one group per work group, 8 tiles; 4 for
  *                          uint8 reductions, where 8-tile groups would number
- *                          fewer than 2 per CU, and over 64 MiB of columns or
- *                          more where rows start or end no more often than
- *                          every 8 MiB (reductions) or 16 MiB (copies) on
- *                          average.  Smaller column spaces: up to 8
+ *                          fewer than 2 per CU, and where rows start or end
+ *                          no more often than every 8 MiB over 64 MiB of
+ *                          columns or more (reductions), or every 16 MiB over
+ *                          128 MiB or more (copies), on average, in calls
+ *                          without row checksums.  Smaller column spaces: up to 8
  *                          tiles over a grid of the work groups that fit on
  *                          the device at once.  Whenever every group has a work
  *                          group of its own, groups are also split where a row

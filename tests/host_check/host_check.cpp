@@ -543,6 +543,7 @@ void check_launch_shapes() {
     uint32_t gt;
     uint64_t cap;
     bool group_major;
+    bool checksums = false;
   };
   const uint64_t big = uint64_t(1) << 20;
   const Case cases[] = {
@@ -556,7 +557,7 @@ void check_launch_shapes() {
        true},
       {"RHD AG bf16 64x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RHD, 64, 1, 256 << 20, 2, false, 0, 0, 1, 4, 512, true},
       {"Ring AG bf16 64x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 64, 1, 256 << 20, 2, false, 0, 0, 0, 8, big, true},
-      {"binomial Bcast u8 8x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 8, 1, 64 << 20, 1, false, 0, 0, 1, 8, big,
+      {"binomial Bcast u8 8x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 8, 1, 64 << 20, 1, false, 0, 0, -1, 8, big,
        true},
       {"binomial Bcast u8 16x64MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 16, 1, 64 << 20, 1, false, 0, 0, 1, 4, 512,
        true},
@@ -573,6 +574,15 @@ void check_launch_shapes() {
        big, true},
       {"binomial Bcast u8 8x256MiB", COLL_K_BROADCAST, COLL_ALGO_BINOMIAL, 8, 1, 256 << 20, 1, false, 0, 0, 1, 8,
        big, true},
+      {"chain Bcast u8 8x64MiB", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 8, 1, 64 << 20, 1, false, 0, 0, -1, 8, big,
+       true},
+      {"chain Bcast u8 8x128MiB", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 8, 1, 128 << 20, 1, false, 0, 0, 0, 4, big,
+       true},
+      {"Ring AG bf16 4x64MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 4, 1, 64 << 20, 2, false, 0, 0, -1, 8, big, true},
+      {"Ring AR fp32 8x256MiB checksums", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 256 << 20, 4, false, 0, 0, 0, 8, big,
+       true, true},
+      {"chain Bcast u8 8x128MiB checksums", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 8, 1, 128 << 20, 1, false, 0, 0, -1,
+       8, big, true, true},
       {"Ring AR fp32 8x16MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 16 << 20, 4, false, 0, 0, 0, 8, big, true},
       {"Ring AR fp32 8x4MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 4 << 20, 4, false, 0, 0, -1, 1, 2048, false},
       {"Ring AR fp32 8x8MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 8 << 20, 4, false, 0, 0, 0, 4, big, true},
@@ -595,6 +605,7 @@ void check_launch_shapes() {
     RowsShapeInput in;
     in.colspace = ph.colspace;
     in.segment = phase_segment(ph);
+    in.checksums = c.checksums;
     in.has_reduce = c.kind == COLL_K_ALLREDUCE || c.kind == COLL_K_REDUCESCATTER || c.kind == COLL_K_REDUCE;
     in.elem_size = c.sz;
     in.nranks = c.N;
