@@ -136,7 +136,8 @@ def coll_plan(kind, algo, nranks, count, dtype, root=0, chunks=1):
     out = [(r.step, r.src, r.dst, r.src_off, r.dst_off, r.n, r.reduce, r.local, r.from_send, r.staged)
            for r in rows[:n.value]]
     return out, {"steps": counts.steps, "rows": counts.rows, "crit_bytes": counts.crit_bytes,
-                 "hbm_bytes": counts.hbm_bytes, "moved_bytes": counts.moved_bytes}
+                 "hbm_bytes": counts.hbm_bytes, "moved_bytes": counts.moved_bytes,
+                 "round_trips": counts.round_trips}
 
 
 def coll_get_stats():
@@ -144,7 +145,7 @@ def coll_get_stats():
     c = CollCounts()
     check(lib.coll_get_stats(ctypes.byref(c)))
     return {"steps": c.steps, "rows": c.rows, "crit_bytes": c.crit_bytes, "hbm_bytes": c.hbm_bytes,
-            "moved_bytes": c.moved_bytes}
+            "moved_bytes": c.moved_bytes, "round_trips": c.round_trips}
 
 
 def coll_set_checksums(sums=None):

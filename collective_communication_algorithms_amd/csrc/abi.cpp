@@ -15,6 +15,7 @@
 
 #include "bind.h"
 #include "coll.h"
+#include "colprog.h"
 #include "launch.h"
 #include "plan.h"
 
@@ -26,7 +27,9 @@ thread_local coll_counts_t t_last{};
 thread_local uint64_t* t_sums = nullptr;
 thread_local size_t t_sums_cap = 0;
 
-std::atomic<int64_t> opt_exec{0};      // 0: one launch per phase, 1: one launch per step
+std::atomic<int64_t> opt_exec{0};      // 0: column kernel where it applies, else one row-kernel launch per
+                                       // phase; 1: one row-kernel launch per step; 2: one per phase
+std::atomic<int64_t> opt_col_tiles{0}; // column kernel: tiles per work group (0: automatic)
 std::atomic<int64_t> opt_group{0};     // 0: automatic
 std::atomic<int64_t> opt_grid{0};      // 0: automatic
 std::atomic<int64_t> opt_nt{-1};       // -1: automatic, else an NT_* mask
@@ -111,6 +114,7 @@ struct KeyHash {
 };
 
 struct DevList {                // work lists of one row phase for one launch shape
+  bool pinned = false;          // used by a captured call: kept until coll_finalize
   size_t phase = 0;
   uint64_t cap = 0;             // grid cap asked for
   uint32_t G = 0, gt = 0;       // grid used, group tiles
@@ -124,8 +128,24 @@ struct DevList {                // work lists of one row phase for one launch sh
   uint64_t bytes = 0;           // device memory held
 };
 
+// A schedule's column programs on the device (one per checksum mode).
+struct ColDev {
+  bool tried = false;
+  bool pinned = false;          // used by a captured call: tables kept until coll_finalize
+  ColPlan plan;                 // plan.ok false: the row kernel runs this schedule
+  uint32_t tiles = 0;           // tiles per work group of d_work
+  uint32_t nwork = 0;
+  ColWork* d_work = nullptr;
+  ColInstr* d_code = nullptr;
+  uint32_t* d_acc = nullptr;
+  uint64_t bytes = 0;           // device memory held
+};
+
 struct Entry {
+  Schedule sched;
   Bound bound;
+  ColDev col[2];                // [checksums on]
+  bool pinned = false;          // used by a captured call: never evicted before coll_finalize
   std::vector<int8_t> multi;    // per phase: groups average two or more pieces per step (-1: not known yet)
   int dev = 0;
   DevItem* d_items = nullptr;
@@ -156,8 +176,12 @@ struct SumScratch {
   uint64_t last_use = 0;
   bool clean = false;           // every slot is zero once the queued work is done (the fold
                                 // kernel zeroes what it reads); else the next call clears them
+  bool pinned = false;          // used by a captured call: neither freed nor moved before coll_finalize
 };
 std::vector<SumScratch> g_sum_scratch;
+// Device buffers a captured graph may still use, released by coll_finalize:
+// pinned tables that a later call had to replace.
+std::vector<void*> g_retired;
 constexpr size_t SUM_SCRATCH_MAX = 16;  // buffers kept; the least recently used goes first
 constexpr size_t CACHE_CAP = 512;  // schedules kept
 uint64_t g_cache_bytes = 0;        // device memory they hold (COLL_OPT_CACHE_BYTES caps it)
@@ -196,13 +220,21 @@ uint32_t rows_ntmask(uint32_t ntmask, bool fwd, bool has_reduce) {
   return ntmask;
 }
 
-// Bytes a call moves through memory, as planned for an in-place call on
-// 16-byte-aligned buffers with the current options on a device of `cus`
-// compute units: the schedule's bytes, less, in every row phase whose lists the
-// forwarding variant runs, the operands it takes from registers and the stores
-// it skips.  Only large column spaces get group-major lists, so only they build
-// lists here.
-int64_t planned_moved_bytes(const Schedule& s, int sz, uint32_t cus) {
+// Whether the column kernel may run calls (the automatic execution mode).
+bool col_mode() { return opt_exec.load() == 0; }
+
+// What a call costs, as planned for an in-place call on 16-byte-aligned
+// buffers with the current options on a device of `cus` compute units.  Where
+// the column kernel runs the schedule: one memory round trip, and the bytes
+// its programs load and store.  Elsewhere: a round trip per step, and the
+// schedule's bytes less, in every row phase whose lists the forwarding variant
+// runs, the operands it takes from registers and the stores it skips (only
+// large column spaces get group-major lists, so only they build lists here).
+PlannedCost planned_cost(const Schedule& s, int sz, uint32_t cus) {
+  if (col_mode() && s.kind != COLL_K_ALLTOALL) {
+    const ColPlan cp = compile_colplan(s, sz, true, t_sums != nullptr);
+    if (cp.ok) return PlannedCost{1, int64_t(cp.moved_bytes)};
+  }
   const Bound b = bind_schedule(s, sz, true);
   int64_t moved = b.counts.hbm_bytes;
   const bool a2a = s.kind == COLL_K_ALLTOALL;
@@ -230,35 +262,54 @@ int64_t planned_moved_bytes(const Schedule& s, int sz, uint32_t cus) {
                                        opt_reverse.load() != 0, in.per_step, shape.group_major);
     if (forwarding_runs(rl.fwd, rl.fine, rows_ntmask(ntmask, rl.fwd, has_reduce), true)) moved -= int64_t(rl.fwd_saved);
   }
-  return moved;
+  return PlannedCost{b.counts.steps, moved};
 }
 
 coll_status_t auto_algo(coll_kind_t kind, int N, int64_t count, int sz, int root, uint32_t cus, coll_algo_t& out) {
   const std::vector<int64_t> key{int64_t(kind), N, count, sz, root, opt_alpha_ns.load(), opt_beta_gbps.load(),
                                  int64_t(cus), opt_nt.load(), opt_exec.load(), opt_group.load(), opt_grid.load(),
-                                 opt_reverse.load()};
+                                 opt_reverse.load(), t_sums != nullptr ? 1 : 0};
   auto it = g_auto.find(key);
   if (it != g_auto.end()) {
     out = it->second;
     return COLL_OK;
   }
   std::string err;
-  const std::function<int64_t(const Schedule&)> moved = [&](const Schedule& s) {
-    return planned_moved_bytes(s, sz, cus);
+  const std::function<PlannedCost(const Schedule&)> cost = [&](const Schedule& s) {
+    return planned_cost(s, sz, cus);
   };
-  const coll_status_t st = choose_algo(kind, N, count, sz, root, cost_model(), out, err, &moved);
+  const coll_status_t st = choose_algo(kind, N, count, sz, root, cost_model(), out, err, &cost);
   if (st != COLL_OK) return fail(st, err);
   if (g_auto.size() > 4096) g_auto.clear();
   g_auto[key] = out;
   return COLL_OK;
 }
 
+// Frees a device buffer, or keeps it until coll_finalize when a captured
+// graph may still read it.
+void release(void* p, bool pinned) {
+  if (!p) return;
+  if (pinned) g_retired.push_back(p);
+  else (void)hipFree(p);
+}
+
+void free_col(ColDev& c) {
+  release(c.d_work, c.pinned);
+  release(c.d_code, c.pinned);
+  release(c.d_acc, c.pinned);
+  c = ColDev{};
+}
+
 void free_entry(Entry& e) {
-  if (e.d_items) (void)hipFree(e.d_items);
-  if (e.d_steps) (void)hipFree(e.d_steps);
+  release(e.d_items, e.pinned);
+  release(e.d_steps, e.pinned);
   for (DevList& l : e.lists) {
-    if (l.d_off) (void)hipFree(l.d_off);
-    if (l.d_list) (void)hipFree(l.d_list);
+    release(l.d_off, l.pinned || e.pinned);
+    release(l.d_list, l.pinned || e.pinned);
+  }
+  for (ColDev& c : e.col) {
+    c.pinned = c.pinned || e.pinned;
+    free_col(c);
   }
   e.lists.clear();
   e.d_items = nullptr;
@@ -267,14 +318,16 @@ void free_entry(Entry& e) {
   e.bytes = 0;
 }
 
-// Drops the least recently used schedule other than `keep`; its tables may
-// still be read by queued work, so its device is synchronised first.
-// Returns false when there is nothing to drop.
+// Drops the least recently used schedule other than `keep` that no captured
+// call uses; its tables may still be read by queued work, so its device is
+// synchronised first.  Returns false when there is nothing to drop.
 bool evict_lru(const Entry* keep, coll_status_t& st) {
   st = COLL_OK;
   auto lru = g_cache.end();
   for (auto i = g_cache.begin(); i != g_cache.end(); ++i)
-    if (i->second.get() != keep && (lru == g_cache.end() || i->second->last_use < lru->second->last_use)) lru = i;
+    if (i->second.get() != keep && !i->second->pinned &&
+        (lru == g_cache.end() || i->second->last_use < lru->second->last_use))
+      lru = i;
   if (lru == g_cache.end()) return false;
   int cur = 0;
   hipError_t he = hipGetDevice(&cur);
@@ -299,17 +352,21 @@ coll_status_t trim_cache(const Entry* keep) {
 }
 
 // Frees one partial-slot buffer after its device has finished the work queued
-// on it (the kernels that use it may still be running).
+// on it (the kernels that use it may still be running); a buffer a captured
+// call uses is kept until coll_finalize instead.
 void free_sum_scratch(SumScratch& s) {
-  int cur = 0;
-  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-  if (s.d) {
+  if (s.d && s.pinned) {
+    g_retired.push_back(s.d);
+  } else if (s.d) {
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
     if (hipSetDevice(s.dev) == hipSuccess) (void)hipDeviceSynchronize();
     (void)hipFree(s.d);
     if (have_cur) (void)hipSetDevice(cur);
   }
   s.d = nullptr;
   s.cap = 0;
+  s.pinned = false;
 }
 
 // Partial checksum slots for `n` slots on device `dev`, for the caller's
@@ -320,11 +377,13 @@ coll_status_t sum_scratch(int dev, const uint64_t* user, size_t n, SumScratch*& 
     if (s.dev == dev && s.user == user) hit = &s;
   if (!hit) {
     if (g_sum_scratch.size() >= SUM_SCRATCH_MAX) {
-      auto lru = g_sum_scratch.begin();
+      auto lru = g_sum_scratch.end();
       for (auto i = g_sum_scratch.begin(); i != g_sum_scratch.end(); ++i)
-        if (i->last_use < lru->last_use) lru = i;
-      free_sum_scratch(*lru);
-      g_sum_scratch.erase(lru);
+        if (!i->pinned && (lru == g_sum_scratch.end() || i->last_use < lru->last_use)) lru = i;
+      if (lru != g_sum_scratch.end()) {
+        free_sum_scratch(*lru);
+        g_sum_scratch.erase(lru);
+      }
     }
     g_sum_scratch.push_back(SumScratch{});
     hit = &g_sum_scratch.back();
@@ -356,15 +415,23 @@ coll_status_t get_list(Entry& e, size_t pi, uint64_t cap, uint32_t gt, bool reve
       out = &l;
       return COLL_OK;
     }
-  if (e.lists.size() >= 8) {  // a few launch shapes per schedule are plenty; drop the oldest
+  // a few launch shapes per schedule are plenty: drop the oldest one no
+  // captured call uses
+  size_t unpinned = 0, oldest = e.lists.size();
+  for (size_t i = 0; i < e.lists.size(); ++i)
+    if (!e.lists[i].pinned && !e.pinned) {
+      ++unpinned;
+      if (oldest == e.lists.size()) oldest = i;
+    }
+  if (unpinned >= 8 && oldest < e.lists.size()) {
     hipError_t he = hipDeviceSynchronize();
     if (he != hipSuccess) return hip_fail(he, "hipDeviceSynchronize");
-    DevList& l = e.lists.front();
-    if (l.d_off) (void)hipFree(l.d_off);
-    if (l.d_list) (void)hipFree(l.d_list);
+    DevList& l = e.lists[oldest];
+    (void)hipFree(l.d_off);
+    (void)hipFree(l.d_list);
     e.bytes -= l.bytes;
     g_cache_bytes -= l.bytes;
-    e.lists.erase(e.lists.begin());
+    e.lists.erase(e.lists.begin() + long(oldest));
   }
   const Phase& ph = e.bound.phases[pi];
   RowsList rl = plan_rows_list(e.bound, ph, cap, gt, reverse, per_step, group_major);
@@ -402,6 +469,84 @@ coll_status_t get_list(Entry& e, size_t pi, uint64_t cap, uint32_t gt, bool reve
   g_cache_bytes += l.bytes;
   e.lists.push_back(l);
   out = &e.lists.back();
+  return trim_cache(&e);
+}
+
+template <class T>
+coll_status_t upload(const std::vector<T>& v, T*& d) {
+  d = nullptr;
+  hipError_t he = hipMalloc(reinterpret_cast<void**>(&d), std::max<size_t>(v.size(), 1) * sizeof(T));
+  if (he != hipSuccess) {
+    d = nullptr;
+    return fail(COLL_ERR_NO_MEMORY, std::string("hipMalloc: ") + hipGetErrorString(he));
+  }
+  if (!v.empty()) he = hipMemcpy(d, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice);
+  if (he != hipSuccess) {
+    (void)hipFree(d);
+    d = nullptr;
+    return hip_fail(he, "hipMemcpy");
+  }
+  return COLL_OK;
+}
+
+// Column kernel: tiles per work group.  Large column spaces give each work
+// group a few tiles, so the per-group work (reading its descriptor and
+// program, flushing its checksums) is spread over more bytes; small ones one
+// tile, so that every compute unit gets work.
+uint32_t auto_col_tiles(const ColPlan& p, uint32_t cus) {
+  const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
+  uint64_t tiles = 0;
+  for (const ColSeg& sg : p.segs) tiles += (sg.s1 + tb - 1) / tb - sg.s0 / tb;
+  const uint64_t per = tiles / (uint64_t(cus) * 32u);
+  return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(per, 8)));
+}
+
+// The column programs of a schedule for this call's checksum mode, compiled
+// and uploaded on first use, with work groups of `tiles` tiles.  out->plan.ok
+// false: the row kernel runs the schedule.
+coll_status_t get_col(Entry& e, const Key& k, bool cks, uint32_t cus, ColDev*& out) {
+  ColDev& c = e.col[cks ? 1 : 0];
+  out = &c;
+  if (!c.tried) {
+    c.tried = true;
+    c.plan = compile_colplan(e.sched, k.sz, k.inplace != 0, cks);
+    if (!c.plan.ok) return COLL_OK;
+    coll_status_t st = upload(c.plan.code, c.d_code);
+    if (st == COLL_OK) st = upload(c.plan.acc_rows, c.d_acc);
+    if (st != COLL_OK) {
+      free_col(c);
+      return st;
+    }
+    c.tried = true;
+    c.bytes = std::max<size_t>(c.plan.code.size(), 1) * sizeof(ColInstr) +
+              std::max<size_t>(c.plan.acc_rows.size(), 1) * sizeof(uint32_t);
+    e.bytes += c.bytes;
+    g_cache_bytes += c.bytes;
+  }
+  if (!c.plan.ok) return COLL_OK;
+  const uint32_t tiles = opt_col_tiles.load() > 0 ? uint32_t(opt_col_tiles.load()) : auto_col_tiles(c.plan, cus);
+  if (c.d_work && c.tiles == tiles) return COLL_OK;
+  const std::vector<ColWork> w = col_works(c.plan, tiles);
+  ColWork* d = nullptr;
+  const coll_status_t st = upload(w, d);
+  if (st != COLL_OK) return st;
+  const uint64_t old = c.d_work ? std::max<uint64_t>(c.nwork, 1) * sizeof(ColWork) : 0;
+  if (c.d_work && !c.pinned) {
+    // queued calls may still read the old table
+    const hipError_t he = hipDeviceSynchronize();
+    if (he != hipSuccess) {
+      (void)hipFree(d);
+      return hip_fail(he, "hipDeviceSynchronize");
+    }
+  }
+  release(c.d_work, c.pinned);
+  c.d_work = d;
+  c.tiles = tiles;
+  c.nwork = uint32_t(w.size());
+  const uint64_t now = std::max<uint64_t>(w.size(), 1) * sizeof(ColWork);
+  c.bytes = c.bytes - old + now;
+  e.bytes = e.bytes - old + now;
+  g_cache_bytes = g_cache_bytes - old + now;
   return trim_cache(&e);
 }
 
@@ -456,6 +601,7 @@ coll_status_t get_entry(const Key& k, Entry*& out) {
   if (!hz.empty()) return fail(COLL_ERR_UNSUPPORTED, "internal schedule conflict: " + hz);
   auto e = std::make_unique<Entry>();
   e->bound = bind_schedule(s, k.sz, k.inplace != 0);
+  e->sched = std::move(s);
   const Bound& b = e->bound;
   if (!b.items.empty()) {
     hipError_t he = hipMalloc(reinterpret_cast<void**>(&e->d_items), b.items.size() * sizeof(DevItem));
@@ -517,6 +663,27 @@ coll_status_t check_buffers(void* const* send, void* const* recv, int N, int64_t
   return COLL_OK;
 }
 
+// One kernel launch of a call, planned before anything is enqueued.
+struct Launch {
+  enum Kind { COL, ROWS, PERM } kind = ROWS;
+  // COL
+  const ColWork* work = nullptr;
+  const ColInstr* code = nullptr;
+  const uint32_t* acc = nullptr;
+  ColVariant v;
+  uint32_t grid = 0;
+  bool nt = false;
+  // ROWS
+  const DevItem* list = nullptr;
+  const uint32_t* off = nullptr;
+  uint32_t launches = 0;
+  uint32_t ntmask = 0;
+  bool fine = false, fwd = false;
+  // PERM
+  uint32_t s0 = 0, s1 = 0, lg = 0, ncols = 0;
+  int unit = 16, slots = 8;
+};
+
 coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N, size_t count_in, coll_dtype_t dtype,
                   coll_op_t op, coll_algo_t algo, int root, int chunks, void* stream_v) {
   const int sz = elem_size(dtype);
@@ -538,6 +705,9 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     st = validate_schedule_args(kind, automatic ? COLL_ALGO_DEFAULT : algo, N, count, root, chunks, err);
     if (st != COLL_OK) return fail(st, err);
   }
+  // the permutation kernel addresses a block with 32-bit unit offsets
+  if (kind == COLL_K_ALLTOALL && uint64_t(count / N) * uint64_t(sz) >= (uint64_t(1) << 31))
+    return fail(COLL_ERR_UNSUPPORTED, "AllToAll blocks of 2 GiB or more");
   t_last = coll_counts_t{};
   if (count == 0) return COLL_OK;
 
@@ -565,31 +735,17 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   if (st != COLL_OK) return st;
   const Bound& b = e->bound;
 
+  // ---- plan every launch and allocate what it needs; nothing is enqueued
+  // before this part has succeeded, so an error leaves no partial work
   const bool cks = t_sums != nullptr;
-  uint64_t* partial = nullptr;  // SUM_LANES slots per row, folded into t_sums after the kernels
-  SumScratch* scratch = nullptr;
-  bool capturing = false;
-  if (cks) {
-    if (size_t(b.nrows) > t_sums_cap) return fail(COLL_ERR_INVALID_ARG, "checksum buffer smaller than the schedule");
-    st = sum_scratch(dev, t_sums, std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES, scratch);
-    if (st != COLL_OK) return st;
-    partial = scratch->d;
-    // a call being captured into a graph runs later, once per replay: it
-    // clears the slots itself and leaves the flag to the calls that run now
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    capturing = hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
-    if (!scratch->clean || capturing) {
-      he = launch_fill_u64(partial, scratch->cap, 0, stream);
-      if (he != hipSuccess) return hip_fail(he, "checksum clear");
-    }
-    if (!capturing) scratch->clean = false;  // until this call's fold is queued
-  }
+  if (cks && size_t(b.nrows) > t_sums_cap) return fail(COLL_ERR_INVALID_ARG, "checksum buffer smaller than the schedule");
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const bool capturing = hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
   const uint64_t footprint = uint64_t(N) * uint64_t(count) * uint64_t(sz) * (inplace ? 1u : 2u);
   const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint, kind == COLL_K_ALLTOALL) : uint32_t(opt_nt.load());
   const bool step_mode = opt_exec.load() == 1;
 
   RankPtrs ptrs;
-  bool bases16 = true;
   uint64_t align_or = 0;
   for (int i = 0; i < N; ++i) {
     ptrs.send[i] = reinterpret_cast<uint64_t>(send[i]);
@@ -597,95 +753,171 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     align_or |= ptrs.send[i] | ptrs.recv[i];
   }
   for (int i = N; i < COLL_MAX_RANKS; ++i) ptrs.send[i] = ptrs.recv[i] = 0;
-  bases16 = (align_or % 16) == 0;
+  const bool bases16 = (align_or % 16) == 0;
 
   const int dt = int(dtype) == COLL_INT32 ? DT_I32 : int(dtype) == COLL_UINT8 ? DT_U8
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
   const bool has_reduce = kind == COLL_K_ALLREDUCE || kind == COLL_K_REDUCESCATTER || kind == COLL_K_REDUCE;
-  std::string dbg;  // launch shapes, for COLL_DEBUG
-  int64_t saved = 0;  // bytes the forwarding variant neither loads nor stores
-  for (size_t pi = 0; pi < b.phases.size(); ++pi) {
-    const Phase& ph = b.phases[pi];
-    if (ph.kind == Phase::ROWS) {
-      RowsShapeInput in;
-      in.colspace = ph.colspace;
-      in.segment = phase_segment(ph);
-      in.has_reduce = has_reduce;
-      in.checksums = cks;
-      in.elem_size = sz;
-      in.nranks = N;
-      in.cus = uint32_t(di->cus);
-      in.resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, ntmask));
-      in.per_step = step_mode;
-      in.forced_group_tiles = opt_group.load();
-      in.forced_grid = opt_grid.load();
-      const RowsShape shape = rows_shape(in, [&] {
-        if (e->multi.size() != b.phases.size()) e->multi.assign(b.phases.size(), int8_t(-1));
-        if (e->multi[pi] < 0) e->multi[pi] = several_pieces_per_step(b, ph) ? 1 : 0;
-        return e->multi[pi] != 0;
-      });
-      const uint32_t gt = shape.group_tiles;
-      DevList* L = nullptr;
-      st = get_list(*e, pi, std::max<uint64_t>(shape.cap, 1), gt, opt_reverse.load() != 0, step_mode,
-                    shape.group_major, L);
-      if (st != COLL_OK) return st;
-      const uint32_t grid = L->G;
-      const uint32_t nt_rows = rows_ntmask(ntmask, L->fwd, has_reduce);
+  std::vector<Launch> plan;
+  std::string dbg;    // launch shapes, for COLL_DEBUG
+  int64_t moved = b.counts.hbm_bytes;
+  ColDev* cd = nullptr;
+  if (col_mode() && bases16 && kind != COLL_K_ALLTOALL) {
+    st = get_col(*e, k, cks, uint32_t(di->cus), cd);
+    if (st != COLL_OK) return st;
+    if (!cd->plan.ok) cd = nullptr;
+  }
+  if (cd) {
+    Launch L;
+    L.kind = Launch::COL;
+    L.work = cd->d_work;
+    L.code = cd->d_code;
+    L.acc = cd->d_acc;
+    L.v = cd->plan.v;
+    L.grid = cd->nwork;
+    // nothing is read twice: past the memory-side cache every access streams
+    L.nt = opt_nt.load() < 0 ? ntmask != 0 : (ntmask & (NT_SRC | NT_DST)) != 0;
+    if (L.grid) plan.push_back(L);
+    moved = int64_t(cd->plan.moved_bytes);
+    if (g_debug.load())
+      dbg += " | columns: " + std::to_string(cd->plan.segs.size()) + " segments, grid " + std::to_string(L.grid) +
+             " tiles " + std::to_string(cd->tiles) + " unit " + std::to_string(L.v.unit) + " slots " +
+             std::to_string(L.v.leaves) + (L.nt ? " nontemporal" : "");
+  } else {
+    for (size_t pi = 0; pi < b.phases.size(); ++pi) {
+      const Phase& ph = b.phases[pi];
+      Launch L;
+      if (ph.kind == Phase::ROWS) {
+        RowsShapeInput in;
+        in.colspace = ph.colspace;
+        in.segment = phase_segment(ph);
+        in.has_reduce = has_reduce;
+        in.checksums = cks;
+        in.elem_size = sz;
+        in.nranks = N;
+        in.cus = uint32_t(di->cus);
+        in.resident = uint64_t(di->cus) * uint64_t(occupancy_rows(dev, dt, int(op), cks, ntmask));
+        in.per_step = step_mode;
+        in.forced_group_tiles = opt_group.load();
+        in.forced_grid = opt_grid.load();
+        const RowsShape shape = rows_shape(in, [&] {
+          if (e->multi.size() != b.phases.size()) e->multi.assign(b.phases.size(), int8_t(-1));
+          if (e->multi[pi] < 0) e->multi[pi] = several_pieces_per_step(b, ph) ? 1 : 0;
+          return e->multi[pi] != 0;
+        });
+        DevList* D = nullptr;
+        st = get_list(*e, pi, std::max<uint64_t>(shape.cap, 1), shape.group_tiles, opt_reverse.load() != 0, step_mode,
+                      shape.group_major, D);
+        if (st != COLL_OK) return st;
+        if (capturing) D->pinned = true;
+        L.kind = Launch::ROWS;
+        L.list = D->d_list;
+        L.off = D->d_off;
+        L.grid = D->G;
+        L.launches = D->launches;
+        L.fine = D->fine;
+        L.fwd = D->fwd;
+        L.ntmask = rows_ntmask(ntmask, D->fwd, has_reduce);
+        if (forwarding_runs(D->fwd, D->fine, L.ntmask, bases16)) moved -= int64_t(D->fwd_saved);
+        if (g_debug.load())
+          dbg += " | rows steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
+                 std::to_string(L.grid) + " group_tiles " + std::to_string(shape.group_tiles) +
+                 (L.fine ? " fine" : "") + (forwarding_runs(D->fwd, D->fine, L.ntmask, bases16) ? " forwarding" : "") +
+                 " nt " + std::to_string(L.ntmask) + " launches " + std::to_string(L.launches);
+      } else {
+        L.kind = Launch::PERM;
+        int unit = b.perm_unit;
+        while (unit > 1 && (align_or % uint64_t(unit))) unit >>= 1;
+        L.unit = unit;
+        L.ncols = uint32_t(ph.colspace / uint64_t(unit));
+        // every staged AllToAll step permutes groups of N rows; each of the 4 waves
+        // holds ceil(N/4) rows, 2^lg units per lane of each
+        const uint32_t ipw = uint32_t(N + 3) / 4;
+        // slots per lane: measured at 32 ranks (5-8 rows per wave) 8 slots, one
+        // unit per row, beat 16 (Bruck 7.5 vs 8.0 ms); at 8 and 16 ranks 16 slots
+        // beat 8 (0.68 vs 0.72 ms, 1.63 vs 1.77 ms)
+        L.slots = ipw > 4 && ipw <= 8 ? 8 : ipw <= 16 ? 16 : 32;
+        uint32_t lg = 0;
+        while ((ipw << (lg + 1)) <= uint32_t(L.slots) && (64u << (lg + 1)) <= std::max<uint32_t>(L.ncols, 64)) ++lg;
+        L.lg = lg;
+        const uint64_t tu = uint64_t(64) << lg;
+        const uint64_t ntiles = (uint64_t(L.ncols) + tu - 1) / tu;
+        uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, L.slots, cks, ntmask != 0));
+        if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
+        // the same number of tiles for every work group
+        const uint64_t per_wg = std::max<uint64_t>(1, (ntiles + cap - 1) / cap);
+        L.grid = uint32_t(std::max<uint64_t>(1, (ntiles + per_wg - 1) / per_wg));
+        L.s0 = ph.s0;
+        L.s1 = ph.s1;
+        L.ntmask = ntmask;
+        if (g_debug.load())
+          dbg += " | perm steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
+                 std::to_string(L.grid) + " unit " + std::to_string(unit) + " slots " + std::to_string(L.slots);
+      }
+      plan.push_back(L);
+    }
+  }
+  uint64_t* partial = nullptr;  // SUM_LANES slots per row, folded into t_sums after the kernels
+  SumScratch* scratch = nullptr;
+  if (cks) {
+    st = sum_scratch(dev, t_sums, std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES, scratch);
+    if (st != COLL_OK) return st;
+    partial = scratch->d;
+  }
+  if (capturing) {
+    // a graph replays this call later without the library: keep what it
+    // reads until coll_finalize
+    e->pinned = true;
+    if (cd) cd->pinned = true;
+    if (scratch) scratch->pinned = true;
+  }
+
+  // ---- enqueue
+  if (cks) {
+    // a call being captured into a graph runs later, once per replay: it
+    // clears the slots itself and leaves the flag to the calls that run now
+    if (!scratch->clean || capturing) {
+      he = launch_fill_u64(partial, scratch->cap, 0, stream);
+      if (he != hipSuccess) return hip_fail(he, "checksum clear");
+    }
+    if (!capturing) scratch->clean = false;  // until this call's fold is queued
+  }
+  for (const Launch& L : plan) {
+    if (L.kind == Launch::COL) {
+      ColArgs a{};
+      a.work = L.work;
+      a.code = L.code;
+      a.acc_rows = L.acc;
+      a.sums = partial;
+      a.p = ptrs;
+      he = launch_col(a, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.nt, L.grid, stream);
+      if (he != hipSuccess) return hip_fail(he, "column kernel launch");
+    } else if (L.kind == Launch::ROWS) {
       RowsArgs a{};
-      a.list = L->d_list;
+      a.list = L.list;
       a.sums = partial;
       a.bases16 = bases16;
       a.p = ptrs;
-      for (uint32_t j = 0; j < L->launches; ++j) {
-        a.off = L->d_off + size_t(j) * (grid + 1);
-        he = launch_rows(a, dt, int(op), cks, nt_rows, L->fine, L->fwd, grid, stream);
+      for (uint32_t j = 0; j < L.launches; ++j) {
+        a.off = L.off + size_t(j) * (L.grid + 1);
+        he = launch_rows(a, dt, int(op), cks, L.ntmask, L.fine, L.fwd, L.grid, stream);
         if (he != hipSuccess) return hip_fail(he, "row kernel launch");
       }
-      const bool fwd_on = forwarding_runs(L->fwd, L->fine, nt_rows, bases16);
-      if (fwd_on) saved += int64_t(L->fwd_saved);
-      if (g_debug.load())
-        dbg += " | rows steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
-               std::to_string(grid) + " group_tiles " + std::to_string(gt) + (L->fine ? " fine" : "") +
-               (fwd_on ? " forwarding" : "") + " nt " +
-               std::to_string(nt_rows) + " launches " + std::to_string(L->launches);
     } else {
       PermArgs a{};
       a.items = e->d_items;
       a.steps = e->d_steps;
       a.sums = partial;
-      a.nontemporal = ntmask;
+      a.nontemporal = L.ntmask;
       a.p = ptrs;
-      if (ph.colspace >= (uint64_t(1) << 31))
-        return fail(COLL_ERR_UNSUPPORTED, "AllToAll blocks of 2 GiB or more");
-      int unit = b.perm_unit;
-      while (unit > 1 && (align_or % uint64_t(unit))) unit >>= 1;
-      a.ncols_units = uint32_t(ph.colspace / uint64_t(unit));
-      // every staged AllToAll step permutes groups of N rows; each of the 4 waves
-      // holds ceil(N/4) rows, 2^lg units per lane of each
-      const uint32_t ipw = uint32_t(N + 3) / 4;
-      // slots per lane: measured at 32 ranks (5-8 rows per wave) 8 slots, one
-      // unit per row, beat 16 (Bruck 7.5 vs 8.0 ms); at 8 and 16 ranks 16 slots
-      // beat 8 (0.68 vs 0.72 ms, 1.63 vs 1.77 ms)
-      const int slots = ipw > 4 && ipw <= 8 ? 8 : ipw <= 16 ? 16 : 32;
-      uint32_t lg = 0;
-      while ((ipw << (lg + 1)) <= uint32_t(slots) && (64u << (lg + 1)) <= std::max<uint32_t>(a.ncols_units, 64)) ++lg;
-      a.lg_upl = lg;
-      const uint64_t tu = uint64_t(64) << lg;
-      const uint64_t ntiles = (uint64_t(a.ncols_units) + tu - 1) / tu;
-      uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, slots, cks, ntmask != 0));
-      if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
-      // the same number of tiles for every work group
-      const uint64_t per_wg = std::max<uint64_t>(1, (ntiles + cap - 1) / cap);
-      const uint32_t grid = uint32_t(std::max<uint64_t>(1, (ntiles + per_wg - 1) / per_wg));
-      for (uint32_t s0 = ph.s0; s0 < ph.s1; s0 = step_mode ? s0 + 1 : ph.s1) {
+      a.ncols_units = L.ncols;
+      a.lg_upl = L.lg;
+      for (uint32_t s0 = L.s0; s0 < L.s1; s0 = step_mode ? s0 + 1 : L.s1) {
         a.s0 = s0;
-        a.s1 = step_mode ? s0 + 1 : ph.s1;
-        he = launch_perm(a, unit, slots, cks, grid, stream);
+        a.s1 = step_mode ? s0 + 1 : L.s1;
+        he = launch_perm(a, L.unit, L.slots, cks, L.grid, stream);
         if (he != hipSuccess) return hip_fail(he, "permutation kernel launch");
       }
-      if (g_debug.load())
-        dbg += " | perm steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
-               std::to_string(grid) + " unit " + std::to_string(unit) + " slots " + std::to_string(slots);
     }
   }
   if (cks) {
@@ -698,7 +930,8 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
                  kind_name(kind), algo_name(ra), N, (long long)count, sz, inplace ? "in-place" : "out-of-place",
                  (long long)b.counts.steps, (long long)b.counts.rows, (long long)b.counts.hbm_bytes, dbg.c_str());
   t_last = b.counts;
-  t_last.moved_bytes = b.counts.hbm_bytes - saved;
+  t_last.moved_bytes = moved;
+  t_last.round_trips = cd ? 1 : b.counts.steps;
   return COLL_OK;
 }
 
@@ -742,10 +975,10 @@ coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t c
     if (algo == COLL_ALGO_AUTO) {
       coll_status_t st = build_schedule(kind, COLL_ALGO_DEFAULT, nranks, 0, root, 1, s, err);
       if (st != COLL_OK) return fail(st, err);
-      const std::function<int64_t(const Schedule&)> moved = [&](const Schedule& x) {
-        return planned_moved_bytes(x, sz, PLAN_CUS);
+      const std::function<PlannedCost(const Schedule&)> cost = [&](const Schedule& x) {
+        return planned_cost(x, sz, PLAN_CUS);
       };
-      st = choose_algo(kind, nranks, int64_t(count), sz, root, cost_model(), algo, err, &moved);
+      st = choose_algo(kind, nranks, int64_t(count), sz, root, cost_model(), algo, err, &cost);
       if (st != COLL_OK) return fail(st, err);
       chunks = 1;
     }
@@ -755,7 +988,9 @@ coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t c
     *nrows = s.rows.size();
     if (counts) {
       *counts = count_schedule(s, sz);
-      counts->moved_bytes = planned_moved_bytes(s, sz, PLAN_CUS);
+      const PlannedCost pc = planned_cost(s, sz, PLAN_CUS);
+      counts->moved_bytes = pc.bytes;
+      counts->round_trips = pc.round_trips;
     }
     if (rows) {
       if (cap < s.rows.size()) return fail(COLL_ERR_INVALID_ARG, "row capacity too small");
@@ -796,8 +1031,12 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity) {
 coll_status_t coll_set_option(coll_option_t key, int64_t value) {
   switch (key) {
     case COLL_OPT_EXEC:
-      if (value != 0 && value != 1) return fail(COLL_ERR_INVALID_ARG, "exec mode is 0 or 1");
+      if (value < 0 || value > 2) return fail(COLL_ERR_INVALID_ARG, "exec mode is 0, 1 or 2");
       opt_exec = value;
+      return COLL_OK;
+    case COLL_OPT_COL_TILES:
+      if (value < 0 || value > 65535) return fail(COLL_ERR_INVALID_ARG, "column tiles in [0, 65535]");
+      opt_col_tiles = value;
       return COLL_OK;
     case COLL_OPT_REVERSE:
       opt_reverse = value ? 1 : 0;
@@ -848,6 +1087,7 @@ coll_status_t coll_get_option(coll_option_t key, int64_t* value) {
     case COLL_OPT_MODEL_ALPHA_NS: *value = opt_alpha_ns.load(); return COLL_OK;
     case COLL_OPT_MODEL_BETA_GBPS: *value = opt_beta_gbps.load(); return COLL_OK;
     case COLL_OPT_CACHE_BYTES: *value = opt_cache_bytes.load(); return COLL_OK;
+    case COLL_OPT_COL_TILES: *value = opt_col_tiles.load(); return COLL_OK;
   }
   return fail(COLL_ERR_INVALID_ARG, "unknown option");
 }
@@ -883,9 +1123,25 @@ void coll_finalize(void) {
   for (int d : devs)
     if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
   if (have_cur && !devs.empty()) (void)hipSetDevice(cur);
-  for (auto& kv : g_cache) free_entry(*kv.second);
-  for (SumScratch& s : g_sum_scratch) free_sum_scratch(s);
+  for (auto& kv : g_cache) {
+    kv.second->pinned = false;
+    for (DevList& l : kv.second->lists) l.pinned = false;
+    for (ColDev& c : kv.second->col) c.pinned = false;
+    free_entry(*kv.second);
+  }
+  for (SumScratch& s : g_sum_scratch) {
+    s.pinned = false;
+    free_sum_scratch(s);
+  }
   g_sum_scratch.clear();
+  // buffers that captured graphs kept: the caller has stopped replaying them
+  int ndev = 0;
+  if (!g_retired.empty() && hipGetDeviceCount(&ndev) == hipSuccess)
+    for (int d = 0; d < ndev; ++d)
+      if (hipSetDevice(d) == hipSuccess) (void)hipDeviceSynchronize();
+  if (have_cur && !g_retired.empty()) (void)hipSetDevice(cur);
+  for (void* p : g_retired) (void)hipFree(p);
+  g_retired.clear();
   g_cache.clear();
   g_cache_bytes = 0;
   g_occ.clear();
@@ -936,8 +1192,8 @@ namespace {
 
 // Initial option values from the environment (read once, when the library is
 // loaded): COLL_EXEC, COLL_GROUP_TILES, COLL_MAX_GRID, COLL_NONTEMPORAL,
-// COLL_REVERSE, COLL_MODEL_ALPHA_NS, COLL_MODEL_BETA_GBPS, COLL_CACHE_BYTES
-// (integers, as for coll_set_option; an invalid one is reported on stderr and
+// COLL_REVERSE, COLL_MODEL_ALPHA_NS, COLL_MODEL_BETA_GBPS, COLL_CACHE_BYTES,
+// COLL_COL_TILES (integers, as for coll_set_option; an invalid one is reported on stderr and
 // ignored), and COLL_DEBUG (set and not "0": one line per call on stderr).
 struct EnvOptions {
   EnvOptions() {
@@ -951,7 +1207,8 @@ struct EnvOptions {
                 {"COLL_REVERSE", COLL_OPT_REVERSE},
                 {"COLL_MODEL_ALPHA_NS", COLL_OPT_MODEL_ALPHA_NS},
                 {"COLL_MODEL_BETA_GBPS", COLL_OPT_MODEL_BETA_GBPS},
-                {"COLL_CACHE_BYTES", COLL_OPT_CACHE_BYTES}};
+                {"COLL_CACHE_BYTES", COLL_OPT_CACHE_BYTES},
+                {"COLL_COL_TILES", COLL_OPT_COL_TILES}};
     for (const auto& v : vars) {
       const char* s = std::getenv(v.name);
       if (!s || !*s) continue;

@@ -1,0 +1,61 @@
+// Compiling a schedule into column programs (see device_types.h), and the
+// tables the column kernel walks.  Host-only C++.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "device_types.h"
+#include "plan.h"
+
+namespace coll {
+
+// Register capacities of the column kernel's variants: `unit` bytes per lane
+// and column, at most `leaves` leaves and slots, and `accs` checksum
+// accumulators (0: the variant computes no checksums).  Every list of a
+// program holds at most 64 instructions (one per lane).
+struct ColVariant {
+  int unit = 16;
+  int leaves = 8;
+  int accs = 0;
+};
+
+struct ColPlan {
+  bool ok = false;
+  std::string why;               // when not ok: the first reason
+  ColVariant v;
+  uint64_t colspace = 0;         // bytes of columns (count * element size)
+  std::vector<ColSeg> segs;
+  std::vector<ColInstr> code;
+  std::vector<uint32_t> acc_rows;
+  uint64_t moved_bytes = 0;      // leaf loads and stores: bytes each segment moves, summed
+  uint32_t max_leaves = 0, max_slots = 0, max_ops = 0, max_stores = 0;
+};
+
+constexpr int COL_LIST_MAX = 64;
+
+// Compiles the in-place or out-of-place call of schedule `s` (element size
+// `sz`) into one program per segment, and picks the smallest variant that
+// holds every program.  Not ok (with a reason) for AllToAll, for schedules
+// whose rows change offset, for more than `max_segments` segments, and for
+// programs no variant holds; the row kernel runs those.
+//
+// Semantics of a segment, column by column (the pages' step model: every send
+// of a step leaves from the state before the step): each rank starts with its
+// input (the send buffer's value; in place that is the receive buffer); per
+// step, every covering row's source value is taken first, then the rows are
+// applied in row order, a copy setting the destination's value, a reduce row
+// replacing it with combine(destination, source).  A rank's final value is
+// stored when the collective defines its output there and a row wrote it, or
+// (out of place) when no row did; in place, a rank whose final value is its
+// own input needs no store (the kernel stores nothing before a program's
+// end).  Stores outside the defined output are not made: the contract leaves
+// those bytes unspecified.
+ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums, size_t max_segments = 8192);
+
+// Work groups: each segment's tiles (64 lanes x unit bytes, on the global tile
+// grid), `tiles_per_group` consecutive tiles per work group.
+std::vector<ColWork> col_works(const ColPlan& p, uint32_t tiles_per_group);
+
+}  // namespace coll

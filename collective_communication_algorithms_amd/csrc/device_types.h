@@ -107,6 +107,58 @@ struct RowsArgs {                     // row kernel (copy / recv_and_reduce)
   RankPtrs p;
 };
 
+// ---- column programs --------------------------------------------------------
+//
+// Every schedule but AllToAll keeps each element at its column, so a column's
+// final values depend only on that column's inputs, through the rows that
+// cover it.  Between two consecutive row boundaries (a *segment*) the same rows
+// cover every column, so the host can run the schedule there once, on
+// symbols, and write down what it computes: a *column program*.  The column
+// kernel then runs that program on every column of the segment.  It loads each
+// input the program needs once (a leaf, into a register slot), combines in the
+// rows' exact order (so the float association is the schedule's), adds every
+// row's result to that row's checksum, and stores only the defined outputs.
+enum : uint32_t {
+  CI_COMBINE = 1u << 0,  // op: y = A (+) B (a recv_and_reduce row); else the op's value is A (a copy row)
+  CI_A_Y = 1u << 1,      // op: A is y, not slot `a`; store: the value is y, not slot `a`
+  CI_B_Y = 1u << 2,      // op: B is y, not slot `b`
+  CI_WRITE = 1u << 3,    // op: y also goes to slot `out` (it is needed after y changes)
+  CI_CKS = 1u << 4,      // op: the value's words go to the checksum of the op's row
+};
+
+struct ColInstr {        // 8 bytes
+  uint8_t flags;         // CI_* (ops, stores)
+  uint8_t a, b, out;     // slots: A / stored value, B, result
+  uint32_t arg;          // load / store: rank; op: (-row start byte) mod 4 for its checksum
+};
+
+struct ColSeg {          // 40 bytes: one segment's program
+  uint64_t s0, s1;       // column bytes [s0, s1)
+  uint32_t loads, ops, stores, acc;  // first instruction of each list; first checksum row
+  uint16_t nload, nop, nstore, pad;  // leaf k is loaded into slot k; op k feeds checksum acc + k
+};
+
+struct ColWork {         // 48 bytes: one work group's tiles and its segment's program
+  uint64_t c0;           // column byte of its first tile (a multiple of the tile size)
+  uint64_t s0, s1;       // the segment's column bytes
+  uint32_t loads, ops, stores, acc;
+  uint16_t nload, nop, nstore;
+  uint16_t ntiles;       // consecutive tiles from c0
+};
+
+struct ColArgs {
+  const ColWork* work;
+  const ColInstr* code;
+  const uint32_t* acc_rows;  // per segment, the schedule row of op k's checksum
+  uint64_t* sums;            // partial row checksums (SUM_LANES per row) or nullptr
+  RankPtrs p;
+};
+
+// Threads of a column-kernel work group (one wave).  Lane r also holds rank
+// r's buffer addresses, so programs name at most COL_THREADS ranks.
+constexpr int COL_THREADS = 64;
+static_assert(COL_THREADS <= COLL_MAX_RANKS, "lane r reads rank r's pointers");
+
 struct PermArgs {                     // staged permutation kernel (AllToAll)
   const DevItem* items;
   const DevStep* steps;

@@ -593,7 +593,7 @@ coll_status_t build_schedule(coll_kind_t kind, coll_algo_t algo_in, int N, int64
 }
 
 coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size, int root, const CostModel& m,
-                          coll_algo_t& out, std::string& err, const std::function<int64_t(const Schedule&)>* bytes) {
+                          coll_algo_t& out, std::string& err, const std::function<PlannedCost(const Schedule&)>* cost) {
   std::vector<coll_algo_t> cand;
   switch (kind) {
     case COLL_K_ALLREDUCE: cand = {COLL_ALGO_DBT, COLL_ALGO_RHD, COLL_ALGO_RING}; break;
@@ -624,9 +624,15 @@ coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size,
       if (!have && a == cand.back()) return st;
       continue;
     }
-    const coll_counts_t c = count_schedule(s, elem_size);
-    const double moved = bytes ? double((*bytes)(s)) : double(c.hbm_bytes);
-    const double t = double(c.steps) * m.alpha_s + moved / m.beta_Bps;
+    PlannedCost pc;
+    if (cost) {
+      pc = (*cost)(s);
+    } else {
+      const coll_counts_t c = count_schedule(s, elem_size);
+      pc.round_trips = c.steps;
+      pc.bytes = c.hbm_bytes;
+    }
+    const double t = double(pc.round_trips) * m.alpha_s + double(pc.bytes) / m.beta_Bps;
     if (!have || t < best) {
       best = t;
       out = a;
@@ -639,6 +645,7 @@ coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size,
 coll_counts_t count_schedule(const Schedule& s, int elem_size) {
   coll_counts_t c{};
   c.steps = s.counted_steps();
+  c.round_trips = c.steps;
   c.rows = int64_t(s.rows.size());
   for (const Step& st : s.steps) {
     std::map<std::pair<int, int>, int64_t> edge;

@@ -49,13 +49,21 @@ struct CostModel {
   double beta_Bps = 7.0e12;
 };
 
+// What a schedule costs as it would run: the dependent memory round trips
+// (a step each for the row kernel, one for the column kernel) and the bytes
+// its kernels move.
+struct PlannedCost {
+  int64_t round_trips = 0;
+  int64_t bytes = 0;
+};
+
 // COLL_ALGO_AUTO: among the collective's candidate algorithms valid for N, the
-// one whose schedule minimises steps * alpha + bytes / beta (first candidate on
-// ties), where bytes is `bytes(schedule)` if given, else the schedule's bytes.
-// Returns COLL_OK and the algorithm, or an error.
+// one whose schedule minimises round_trips * alpha + bytes / beta (first
+// candidate on ties), with the cost `cost(schedule)` if given, else the
+// schedule's steps and bytes.  Returns COLL_OK and the algorithm, or an error.
 coll_status_t choose_algo(coll_kind_t kind, int N, int64_t count, int elem_size, int root, const CostModel& m,
                           coll_algo_t& out, std::string& err,
-                          const std::function<int64_t(const Schedule&)>* bytes = nullptr);
+                          const std::function<PlannedCost(const Schedule&)>* cost = nullptr);
 
 // Validates (kind, algo, N, count, root, chunks) and builds the in-place
 // schedule.  Returns COLL_OK or an error status with a message in `err`.

@@ -90,9 +90,10 @@ typedef enum {
   COLL_ALGO_BRUCK = 8,         /* [P3] Bruck AllToAll, ceil(log2 N) rounds plus rotations      */
   COLL_ALGO_LINEAR = 9,        /* [P1] naive Scatter: the root sends each chunk directly      */
   COLL_ALGO_SCATTER_ALLGATHER = 10, /* [P1] Broadcast as binomial Scatter + Ring AllGather    */
-  COLL_ALGO_AUTO = 11,         /* the candidate with the least predicted time, t = steps * alpha
-                                  + schedule bytes / beta ([P3]'s alpha-beta model with this
-                                  device's fitted constants, COLL_OPT_MODEL_*); ties go to the
+  COLL_ALGO_AUTO = 11,         /* the candidate with the least predicted time, t = round_trips *
+                                  alpha + moved_bytes / beta (coll_counts_t; [P3]'s alpha-beta
+                                  model with this device's fitted constants, COLL_OPT_MODEL_*,
+                                  over what the kernels that run it take); ties go to the
                                   first of: AllReduce DBT, RHD, Ring; ReduceScatter / AllGather
                                   RHD, Ring; Broadcast binomial, chain, Scatter+AllGather,
                                   bidirectional ring; Scatter binomial, linear; AllToAll
@@ -192,12 +193,16 @@ typedef struct {
  * byte total on one (src, dst) edge, summed over steps (the beta term of
  * [P3]'s alpha-beta model); hbm_bytes: bytes the rows read and write (copy
  * 2*n*size, reduce 3*n*size); moved_bytes: the part of hbm_bytes that goes
- * through memory: the rest is operands the row kernel passes from one step to
- * the next in registers and stores it skips because a later step overwrites
- * them, or they lie outside the defined output and nothing reads them again
- * (only lists over 8 MiB or more of columns whose entries mostly form such
- * chains, as Ring's do, run that way). */
-typedef struct { int64_t steps, rows, crit_bytes, hbm_bytes, moved_bytes; } coll_counts_t;
+ * through memory.  The column kernel (COLL_OPT_EXEC) loads each input its
+ * programs need once and stores each defined output once: an in-place
+ * AllReduce moves 2NM for every algorithm, ReduceScatter (N+1)M, AllGather
+ * and Broadcast NM.  The row kernel moves the schedule's bytes, less the
+ * operands its forwarding variant passes from step to step in registers and
+ * the stores it skips (lists over 8 MiB or more of columns whose entries
+ * mostly form chains, as Ring's do).  round_trips: dependent memory round
+ * trips of the kernels: 1 for the column kernel, a step each for the row
+ * kernel (the alpha term of COLL_ALGO_AUTO). */
+typedef struct { int64_t steps, rows, crit_bytes, hbm_bytes, moved_bytes, round_trips; } coll_counts_t;
 
 /* Build the in-place schedule of a collective.  rows may be NULL; *nrows is
  * the capacity on input and the number of rows on output (COLL_ERR_INVALID_ARG
@@ -231,10 +236,16 @@ coll_status_t coll_get_stats(coll_counts_t* last);
 coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
 
 /* Process-wide execution options (defaults in brackets).
- * COLL_OPT_EXEC            0: one launch runs every step of a call [0]; each
- *                          work group owns fixed columns, so the steps need
- *                          no synchronisation between work groups.
- *                          1: one launch per step (the launches order the steps).
+ * COLL_OPT_EXEC            0: automatic [0]: every collective but AllToAll, on
+ *                          16-byte aligned buffers, runs in the column kernel
+ *                          (its schedule compiled per column segment, see
+ *                          above); where that does not apply, one row-kernel
+ *                          launch runs every step of the call (each work
+ *                          group owns fixed columns, so the steps need no
+ *                          synchronisation between work groups).
+ *                          1: the row kernel, one launch per step (the
+ *                          launches order the steps).
+ *                          2: the row kernel, one launch for every step.
  * COLL_OPT_GROUP_TILES     4 KiB column tiles per work-group column group, 1..64
  *                          [0: automatic.  Column spaces of 8 MiB or more:
  *                          int32 / fp32 / bf16 reductions whose groups see two
@@ -265,6 +276,8 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          written last is read first [1]; 0: always forwards.
  * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
  * COLL_OPT_MODEL_BETA_GBPS moved-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
+ * COLL_OPT_COL_TILES       column kernel: tiles (64 lanes x 16 or 4 bytes) per
+ *                          work group, up to 65535 [0: automatic, 1..8 by size].
  * COLL_OPT_CACHE_BYTES     device memory the schedule cache may hold, in bytes
  *                          [2^31]; least recently used schedules are dropped
  *                          (after synchronising their device) when a call
@@ -280,7 +293,8 @@ typedef enum {
   COLL_OPT_REVERSE = 4,
   COLL_OPT_MODEL_ALPHA_NS = 5,
   COLL_OPT_MODEL_BETA_GBPS = 6,
-  COLL_OPT_CACHE_BYTES = 7
+  COLL_OPT_CACHE_BYTES = 7,
+  COLL_OPT_COL_TILES = 8
 } coll_option_t;
 coll_status_t coll_set_option(coll_option_t key, int64_t value);
 /* The current value of an option; INVALID_ARG for an unknown key or NULL value. */

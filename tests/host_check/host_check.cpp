@@ -30,6 +30,15 @@
 //     phase's items step by step (in the call's last phase: the same defined
 //     output); and within one launch no byte that a work group writes is read
 //     or written by another (column ownership).
+//   * column programs (compile_colplan), with checksums and without: run on
+//     symbols for every column of every segment (leaves into their slots, ops
+//     reading their operands from y or a slot, stores), every store lands a
+//     rank's final symbol from the schedule run row by row (snapshot per
+//     step), every defined output byte whose final value is not its own
+//     input (out of place: every defined byte) is stored exactly once and
+//     nothing else is,
+//     and each op's value is the symbol of its row's destination right after
+//     the row, so the kernel's checksums are the rows' checksums;
 //   * rows_shape picks the measured launch shapes (group size, grid cap, list
 //     order) for the configurations its rules were measured on, asks whether
 //     groups see several pieces per step only when a rule depends on it, and
@@ -44,6 +53,7 @@
 #include <vector>
 
 #include "bind.h"
+#include "colprog.h"
 #include "plan.h"
 
 using namespace coll;
@@ -568,6 +578,7 @@ void check_launch_shapes() {
       {"Ring AR bf16 16x192MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 16, 1, 192 << 20, 2, false, 0, 0, 0, 4, big, true},
       {"Ring AR fp32 8x48MiB", COLL_K_ALLREDUCE, COLL_ALGO_RING, 8, 1, 48 << 20, 4, false, 0, 0, 0, 8, big, true},
       {"Ring AG bf16 8x128MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 8, 1, 128 << 20, 2, false, 0, 0, 0, 4, big, true},
+      {"Ring AG bf16 8x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 8, 1, 256 << 20, 2, false, 0, 0, 0, 4, big, true},
       {"Ring AG bf16 8x96MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 8, 1, 96 << 20, 2, false, 0, 0, -1, 8, big, true},
       {"Ring AG bf16 32x256MiB", COLL_K_ALLGATHER, COLL_ALGO_RING, 32, 1, 256 << 20, 2, false, 0, 0, 0, 8, big, true},
       {"chain Bcast k=8 u8 8x256MiB", COLL_K_BROADCAST, COLL_ALGO_CHAIN_PIPE, 8, 8, 256 << 20, 1, false, 0, 0, 0, 4,
@@ -634,6 +645,158 @@ void check_launch_shapes() {
   }
 }
 
+// ---- column programs ---------------------------------------------------------
+
+long long col_plans = 0;     // programs compiled and executed
+long long col_fallbacks = 0; // shapes the column kernel leaves to the row kernel
+
+// Element symbols: input of rank r at element e; reductions mix(d, s).
+uint32_t input_sym(int r, int64_t e) { return uint32_t(r) * 0x9E3779B1u + uint32_t(e) * 0x7FEB352Du + 1u; }
+
+void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
+  if (s.count > 5000) return;
+  const ColPlan p = compile_colplan(s, sh.sz, sh.inplace, cks);
+  if (!p.ok) {
+    CHECK(sh.kind == COLL_K_ALLTOALL || sh.N > 64, "%s: no column program (%s)", name(sh).c_str(), p.why.c_str());
+    ++col_fallbacks;
+    return;
+  }
+  ++col_plans;
+  const int N = s.N;
+  const int64_t count = s.count;
+  // the schedule row by row: final symbols, which elements a row wrote, and
+  // each row's destination symbols right after it
+  std::vector<std::vector<uint32_t>> cur(size_t(N), std::vector<uint32_t>(static_cast<size_t>(count)));
+  std::vector<std::vector<char>> wrote(size_t(N), std::vector<char>(static_cast<size_t>(count), 0));
+  for (int r = 0; r < N; ++r)
+    for (int64_t e = 0; e < count; ++e) cur[size_t(r)][size_t(e)] = input_sym(r, e);
+  std::vector<std::vector<uint32_t>> after(s.rows.size());
+  for (const Step& st : s.steps) {
+    std::vector<std::vector<uint32_t>> snap;
+    for (int64_t i = st.first; i < st.first + st.nrows; ++i) {
+      const Row& r = s.rows[size_t(i)];
+      snap.emplace_back(cur[size_t(r.src)].begin() + r.src_off, cur[size_t(r.src)].begin() + r.src_off + r.n);
+    }
+    for (int64_t i = st.first; i < st.first + st.nrows; ++i) {
+      const Row& r = s.rows[size_t(i)];
+      const std::vector<uint32_t>& sv = snap[size_t(i - st.first)];
+      for (int64_t e = 0; e < r.n; ++e) {
+        uint32_t& d = cur[size_t(r.dst)][size_t(r.dst_off + e)];
+        d = r.reduce ? mix(d, sv[size_t(e)]) : sv[size_t(e)];
+        wrote[size_t(r.dst)][size_t(r.dst_off + e)] = 1;
+      }
+      after[size_t(i)].assign(cur[size_t(r.dst)].begin() + r.dst_off, cur[size_t(r.dst)].begin() + r.dst_off + r.n);
+    }
+  }
+  std::vector<std::vector<int>> stored(size_t(N), std::vector<int>(static_cast<size_t>(count), 0));
+  std::vector<int64_t> row_elems(s.rows.size(), 0);
+  for (const ColSeg& sg : p.segs) {
+    CHECK(sg.s0 % uint64_t(sh.sz) == 0 && sg.s1 % uint64_t(sh.sz) == 0 && sg.s0 < sg.s1 && sg.s1 <= p.colspace,
+          "%s: segment bytes", name(sh).c_str());
+    CHECK(int(sg.nload) <= p.v.leaves && sg.nload <= COL_LIST_MAX && sg.nop <= COL_LIST_MAX &&
+              sg.nstore <= COL_LIST_MAX && (!cks || int(sg.nop) <= p.v.accs),
+          "%s: program exceeds its variant", name(sh).c_str());
+    for (int64_t e = int64_t(sg.s0) / sh.sz; e < int64_t(sg.s1) / sh.sz; ++e) {
+      std::vector<uint32_t> slot(size_t(p.v.leaves), 0xDEADBEEFu);
+      std::vector<char> full(size_t(p.v.leaves), 0);
+      for (uint32_t j = 0; j < sg.nload; ++j) {
+        const ColInstr& in = p.code[sg.loads + j];
+        CHECK(in.a == j && in.arg < uint32_t(N), "%s: leaf %u", name(sh).c_str(), j);
+        slot[j] = input_sym(int(in.arg), e);
+        full[j] = 1;
+      }
+      uint32_t y = 0xBADC0DEu;
+      bool yset = false;
+      for (uint32_t k = 0; k < sg.nop; ++k) {
+        const ColInstr& in = p.code[sg.ops + k];
+        auto opnd = [&](uint8_t ybit, uint8_t sl) {
+          if (in.flags & ybit) {
+            CHECK(yset, "%s: y read before set", name(sh).c_str());
+            return y;
+          }
+          CHECK(sl < p.v.leaves && full[sl], "%s: empty slot %u read", name(sh).c_str(), unsigned(sl));
+          return slot[sl < p.v.leaves ? sl : 0];
+        };
+        uint32_t v;
+        if (in.flags & CI_COMBINE) {
+          const uint32_t A = opnd(CI_A_Y, in.a), B = opnd(CI_B_Y, in.b);
+          y = mix(A, B);
+          yset = true;
+          v = y;
+          if (in.flags & CI_WRITE) {
+            CHECK(in.out < p.v.leaves, "%s: slot %u", name(sh).c_str(), unsigned(in.out));
+            slot[in.out < p.v.leaves ? in.out : 0] = y;
+            full[in.out < p.v.leaves ? in.out : 0] = 1;
+          }
+        } else {
+          v = opnd(CI_A_Y, in.a);
+        }
+        CHECK(((in.flags & CI_CKS) != 0) == cks, "%s: checksum flag", name(sh).c_str());
+        if (cks) {
+          const uint32_t row = p.acc_rows[sg.acc + k];
+          const Row& r = s.rows[row];
+          CHECK(r.dst_off <= e && e < r.dst_off + r.n, "%s: op row does not cover its column", name(sh).c_str());
+          CHECK(in.arg == uint32_t((((-(r.dst_off * sh.sz)) % 4) + 4) % 4), "%s: checksum shift", name(sh).c_str());
+          if (r.dst_off <= e && e < r.dst_off + r.n) {
+            CHECK(after[row][size_t(e - r.dst_off)] == v, "%s: op %u (row %u) value at element %lld",
+                  name(sh).c_str(), k, row, (long long)e);
+            ++row_elems[row];
+          }
+        }
+      }
+      for (uint32_t j = 0; j < sg.nstore; ++j) {
+        const ColInstr& in = p.code[sg.stores + j];
+        const uint32_t v = (in.flags & CI_A_Y) ? y : slot[in.a < p.v.leaves ? in.a : 0];
+        CHECK(!(in.flags & CI_A_Y) || yset, "%s: store of an unset y", name(sh).c_str());
+        CHECK(in.arg < uint32_t(N), "%s: store rank", name(sh).c_str());
+        if (in.arg >= uint32_t(N)) continue;
+        CHECK(v == cur[in.arg][size_t(e)], "%s: rank %u element %lld stored the wrong value", name(sh).c_str(),
+              in.arg, (long long)e);
+        ++stored[in.arg][size_t(e)];
+      }
+    }
+  }
+  // every defined element the schedule changed (out of place: every defined
+  // element) is stored once, and nothing else is
+  for (int r = 0; r < N; ++r) {
+    std::vector<char> def(static_cast<size_t>(count), 0);
+    for (auto& d : defined_output(s, r))
+      for (int64_t e = d.first; e < d.second; ++e) def[size_t(e)] = 1;
+    for (int64_t e = 0; e < count; ++e) {
+      const bool changed = wrote[size_t(r)][size_t(e)] && cur[size_t(r)][size_t(e)] != input_sym(r, e);
+      const int want = def[size_t(e)] && (changed || !sh.inplace) ? 1 : 0;
+      CHECK(stored[size_t(r)][size_t(e)] == want, "%s: rank %d element %lld stored %d times, want %d",
+            name(sh).c_str(), r, (long long)e, stored[size_t(r)][size_t(e)], want);
+    }
+  }
+  if (cks)
+    for (size_t r = 0; r < s.rows.size(); ++r)
+      CHECK(row_elems[r] == s.rows[r].n, "%s: row %zu checksummed over %lld of %lld elements", name(sh).c_str(), r,
+            (long long)row_elems[r], (long long)s.rows[r].n);
+  // tiles: each segment's bytes are covered by its work groups' tiles exactly
+  const std::vector<ColWork> w = col_works(p, 3);
+  const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
+  std::vector<uint64_t> covered(p.segs.size(), 0);
+  std::map<uint64_t, size_t> seg_at;  // segments start at distinct columns
+  for (size_t k = 0; k < p.segs.size(); ++k) seg_at[p.segs[k].s0] = k;
+  for (const ColWork& c : w) {
+    auto it = seg_at.find(c.s0);
+    CHECK(it != seg_at.end() && c.c0 % tb == 0 && c.ntiles >= 1 && c.ntiles <= 3, "%s: work", name(sh).c_str());
+    if (it == seg_at.end()) continue;
+    const size_t segi = it->second;
+    const ColSeg& sg = p.segs[segi];
+    CHECK(c.s0 == sg.s0 && c.s1 == sg.s1 && c.loads == sg.loads && c.ops == sg.ops && c.stores == sg.stores &&
+              c.acc == sg.acc && c.nload == sg.nload && c.nop == sg.nop && c.nstore == sg.nstore,
+          "%s: a work group's program is not its segment's", name(sh).c_str());
+    const uint64_t lo = std::max<uint64_t>(c.c0, sg.s0), hi = std::min<uint64_t>(c.c0 + c.ntiles * tb, sg.s1);
+    CHECK(lo < hi, "%s: a work group with no bytes of its segment", name(sh).c_str());
+    if (lo < hi) covered[segi] += hi - lo;
+  }
+  for (size_t k = 0; k < p.segs.size(); ++k)
+    CHECK(covered[k] == p.segs[k].s1 - p.segs[k].s0, "%s: segment %zu covered %llu bytes", name(sh).c_str(), k,
+          (unsigned long long)covered[k]);
+}
+
 int main(int argc, char** argv) {
   for (int i = 1; i < argc; ++i) {
     const std::string a = argv[i];
@@ -695,11 +858,18 @@ int main(int argc, char** argv) {
               name(sh).c_str(), r, (unsigned long long)bytes[uint32_t(r)], (long long)(s.rows[r].n * sh.sz));
     }
     check_lists(sh, s, b, nlists);
+    if (exec_mode != EXEC_NONE || sh.count <= 1000) {
+      check_colplan(sh, s, false);
+      check_colplan(sh, s, true);
+    }
   }
   CHECK(fwd_marks > 0, "no forwarding mark was made");
   CHECK(no_store_marks > 0, "no store was skipped");
   CHECK(exec_mode == EXEC_NONE || exec_lists > 0, "no list was executed");
-  std::printf("host_check: %zu shapes, %d lists, %lld forwarding marks, %lld skipped stores, %lld list executions, %s\n",
-              shapes.size(), nlists, fwd_marks, no_store_marks, exec_lists, failures ? "FAILED" : "ok");
+  CHECK(col_plans > 0, "no column program was checked");
+  std::printf("host_check: %zu shapes, %d lists, %lld forwarding marks, %lld skipped stores, %lld list executions, "
+              "%lld column programs (%lld shapes left to the row kernel), %s\n",
+              shapes.size(), nlists, fwd_marks, no_store_marks, exec_lists, col_plans, col_fallbacks,
+              failures ? "FAILED" : "ok");
   return failures ? 1 : 0;
 }

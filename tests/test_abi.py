@@ -89,7 +89,11 @@ def test_argument_errors(case, want):
 def test_options_and_strings():
     lib = _lib.load()
     assert lib.coll_set_option(0, 7) == INV
-    assert lib.coll_set_option(0, 2) == INV
+    assert lib.coll_set_option(0, 3) == INV
+    assert lib.coll_set_option(0, 2) == OK
+    assert lib.coll_set_option(0, 0) == OK
+    assert lib.coll_set_option(8, 65536) == INV
+    assert lib.coll_set_option(8, 0) == OK
     assert lib.coll_set_option(3, 8) == INV
     assert lib.coll_set_option(3, -1) == OK
     assert lib.coll_set_option(99, 0) == INV
@@ -148,7 +152,7 @@ def test_option_getter_and_cache_info():
     """Options read back what was set (defaults first); the cache starts empty."""
     import collective_communication_algorithms_amd as coll
     want = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "model_alpha_ns": 1060,
-            "model_beta_gbps": 8200, "cache_bytes": 1 << 31}
+            "model_beta_gbps": 8200, "cache_bytes": 1 << 31, "col_tiles": 0}
     saved = {k: coll.coll_get_option(k) for k in want}
     try:
         for k, v in want.items():

@@ -23,9 +23,10 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 @pytest.fixture(autouse=True)
 def _defaults(gpu_device):
     import collective_communication_algorithms_amd as coll
-    for k, v in {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1}.items():
+    for k, v in {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "col_tiles": 0}.items():
         coll.coll_set_option(k, v)
     yield
+    coll.coll_set_option("exec", 0)
 
 
 def sample_columns(count, N, stride=4097, edge=65536, around=256, extra=()):
@@ -144,6 +145,21 @@ def test_alltoall_n32_512x4096(algo):
             assert np.array_equal(got[j][i * S:(i + 1) * S], red_in[i][j * S:(j + 1) * S])
     del sbuf, rbuf, send, recv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind,algo,N,count,dtype,k", [
+    ("allreduce", "ring", 8, (256 << 20) // 4, "float32", 1),
+    ("allgather", "ring", 8, (256 << 20) // 2, "bfloat16", 1),
+    ("broadcast", "chain_pipe", 8, 128 << 20, "uint8", 1),
+])
+def test_row_kernel_long_pieces(kind, algo, N, count, dtype, k):
+    """The row kernel (exec 2) at full size without checksums, where one-piece-
+    per-step schedules take 4-tile column groups (pieces of 16 MiB and more over
+    128 MiB of columns for copies, 8 MiB over 64 MiB for reductions; the host
+    check pins that these three shapes get them): bit-exact on sampled columns."""
+    import collective_communication_algorithms_amd as coll
+    coll.coll_set_option("exec", 2)
+    check_sampled(kind, algo, N, count, dtype, 3, k=k)
 
 
 def test_columns_past_4GiB():

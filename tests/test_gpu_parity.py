@@ -18,7 +18,7 @@ from tests.gpu_util import assert_parity, gpu_run
 pytestmark = pytest.mark.gpu
 
 
-DEFAULT_OPTIONS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1}
+DEFAULT_OPTIONS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "col_tiles": 0}
 
 
 @pytest.fixture(autouse=True)
@@ -213,14 +213,17 @@ def test_bf16_rounding_ties():
 # --- execution modes and launch shapes give identical results ------------------------
 
 @pytest.mark.parametrize("reverse", [0, 1])
-@pytest.mark.parametrize("exec_mode", [0, 1])
+@pytest.mark.parametrize("exec_mode", [0, 1, 2])
 @pytest.mark.parametrize("group_tiles,max_grid", [(0, 0), (1, 0), (2, 5), (8, 3), (16, 1), (4, 7)])
 def test_launch_shapes(exec_mode, group_tiles, max_grid, reverse):
+    """Column kernel (exec 0; group_tiles doubles as its tiles per work group)
+    and row kernel (per step, one launch) at many launch shapes: bit-exact."""
     import collective_communication_algorithms_amd as coll
     coll.coll_set_option("exec", exec_mode)
     coll.coll_set_option("reverse", reverse)
     coll.coll_set_option("group_tiles", group_tiles)
     coll.coll_set_option("max_grid", max_grid)
+    coll.coll_set_option("col_tiles", group_tiles)
     N, count = 8, (3 << 20) // 4 + 12345
     a = si.rank_arrays(3, N, count, "float32")
     for algo in ("ring", "rhd", "dbt"):
@@ -269,7 +272,7 @@ def test_nontemporal_switch(nt):
     assert_parity("alltoall", "ring", b, "bfloat16")
 
 
-@pytest.mark.parametrize("exec_mode", [0, 1])
+@pytest.mark.parametrize("exec_mode", [0, 1, 2])
 def test_many_step_schedules(exec_mode):
     """Pipelines with many chunks and 64-rank rings: hundreds of steps in one call."""
     import collective_communication_algorithms_amd as coll
@@ -296,17 +299,21 @@ def test_repeated_calls_reuse_cached_schedules():
     assert np.array_equal(got, ((s + (1 << 31)) % (1 << 32)) - (1 << 31))
     st = coll.coll_get_stats()
     assert st["steps"] == 14 and st["hbm_bytes"] == 35 * count * 4
-    assert st["moved_bytes"] == st["hbm_bytes"]  # 256 KiB per rank: nothing forwards
+    # the column kernel: every input read once, every result written once
+    assert st["moved_bytes"] == 2 * N * count * 4 and st["round_trips"] == 1
 
 
 @pytest.mark.gpu
-def test_forwarding_moves_what_the_plan_says():
-    """Ring AllReduce 8 x 64 MiB fp32 in place: the launched lists forward, and
-    the call moves 2NM bytes (each input read once, each result written once),
-    as coll_plan plans it; the result is the exact sum (integer-valued floats).
-    Misaligned rank buffers keep the plain path: every schedule byte moves."""
+@pytest.mark.parametrize("exec_mode", [0, 2])
+def test_forwarding_moves_what_the_plan_says(exec_mode):
+    """Ring AllReduce 8 x 64 MiB fp32 in place: in the column kernel (exec 0) or
+    the row kernel's forwarding lists (exec 2) the call moves 2NM bytes (each
+    input read once, each result written once), as coll_plan plans it; the
+    result is the exact sum (integer-valued floats).  Misaligned rank buffers
+    run the row kernel's plain path: every schedule byte moves."""
     import torch
     import collective_communication_algorithms_amd as coll
+    coll.coll_set_option("exec", exec_mode)
     N, M = 8, 64 << 20
     count = M // 4
     buf = torch.empty((N, count + 4), dtype=torch.float32, device="cuda:0")
@@ -319,6 +326,7 @@ def test_forwarding_moves_what_the_plan_says():
     st = coll.coll_get_stats()
     _, plan = coll.coll_plan("allreduce", "ring", N, count, "float32")
     assert st["moved_bytes"] == plan["moved_bytes"] == 2 * N * M
+    assert st["round_trips"] == plan["round_trips"] == (1 if exec_mode == 0 else 14)
     for r in ranks:
         assert torch.equal(r, want)
     # 4-byte offset: rank bases are no longer 16-byte aligned
@@ -423,23 +431,26 @@ def test_coll_check_after_calls():
 
 def test_debug_lines(gpu_device):
     """COLL_DEBUG=1 prints one line per call: the collective, the resolved
-    algorithm, the schedule's counts and each launch's shape."""
+    algorithm, the schedule's counts and each launch's shape (the column
+    kernel's segments and grid, or the row and permutation kernels' launches)."""
     import os
     import subprocess
     import sys
     code = ("import torch, collective_communication_algorithms_amd as c; "
             "t = [torch.ones(1 << 16, device='cuda:0') for _ in range(8)]; "
-            "c.coll_allreduce(t, algo='auto'); c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); "
+            "c.coll_allreduce(t, algo='auto'); c.coll_set_option('exec', 2); c.coll_allreduce(t, algo='ring'); "
+            "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); "
             "torch.cuda.synchronize(); print(float(t[0][0]))")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=120,
                        env=dict(os.environ, COLL_DEBUG="1"))
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stderr.splitlines() if ln.startswith("coll: ")]
-    assert len(lines) == 2, r.stderr[-2000:]
-    assert lines[0].startswith("coll: allreduce algo ") and "auto" not in lines[0] and "| rows" in lines[0]
-    assert lines[1].startswith("coll: alltoall algo bruck") and "| perm" in lines[1]
-    assert r.stdout.strip() == "8.0"
+    assert len(lines) == 3, r.stderr[-2000:]
+    assert lines[0].startswith("coll: allreduce algo ") and "algo auto" not in lines[0] and "| columns:" in lines[0]
+    assert lines[1].startswith("coll: allreduce algo ring") and "| rows" in lines[1]
+    assert lines[2].startswith("coll: alltoall algo bruck") and "| perm" in lines[2]
+    assert r.stdout.strip() == "64.0"
 
 
 def test_concurrent_calls_from_threads():
@@ -544,13 +555,16 @@ def test_checksum_buffers_grow_and_are_evicted():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("exec_mode", [0, 2])
 @pytest.mark.parametrize("kind,factor", [("allreduce", lambda N: 2 * N), ("reducescatter", lambda N: N + 1),
                                          ("allgather", lambda N: N)])
-def test_ring_chains_forward_at_16MiB(kind, factor):
-    """Ring over 8 ranks x 16 MiB fp32 in place, on the large grid: bit-exact
-    against the oracle, and the launched kernels move the closed-form bytes
-    (AllReduce 2NM, ReduceScatter (N+1)M, AllGather NM), as coll_plan plans."""
+def test_ring_chains_forward_at_16MiB(kind, factor, exec_mode):
+    """Ring over 8 ranks x 16 MiB fp32 in place, in the column kernel and in
+    the row kernel's large grid: bit-exact against the oracle, and the launched
+    kernels move the closed-form bytes (AllReduce 2NM, ReduceScatter (N+1)M,
+    AllGather NM), as coll_plan plans."""
     import collective_communication_algorithms_amd as coll
+    coll.coll_set_option("exec", exec_mode)
     N, count = 8, (16 << 20) // 4
     a = si.rank_arrays(77, N, count, "float32")
     assert_parity(kind, "ring", a, "float32")

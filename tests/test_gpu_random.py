@@ -1,7 +1,8 @@
 """Seeded random calls through the C-ABI against the oracle: every collective
 and algorithm, 1 to 72 ranks, empty and ragged counts, every dtype and op, in
 and out of place, buffers off 16-byte alignment, checksums on and off, and
-random launch options.  Bit-exact on every defined element and every row
+random launch options (column kernel or row kernel, tiles per work group,
+group sizes, grid caps, nontemporal masks).  Bit-exact on every defined element and every row
 checksum.  Case i draws everything from numpy's PCG64 seeded with 7000 + i."""
 
 import numpy as np
@@ -13,9 +14,9 @@ from tests.gpu_util import assert_parity
 
 pytestmark = pytest.mark.gpu
 
-DEFAULTS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1}
-OPTION_CHOICES = {"exec": [0, 0, 0, 1], "group_tiles": [0, 0, 0, 1, 2, 8], "max_grid": [0, 0, 0, 3, 64, 1000],
-                  "nontemporal": [-1, -1, 0, 1, 5, 7], "reverse": [0, 1]}
+DEFAULTS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "col_tiles": 0}
+OPTION_CHOICES = {"exec": [0, 0, 0, 1, 2], "group_tiles": [0, 0, 0, 1, 2, 8], "max_grid": [0, 0, 0, 3, 64, 1000],
+                  "nontemporal": [-1, -1, 0, 1, 5, 7], "reverse": [0, 1], "col_tiles": [0, 0, 1, 3]}
 PIPELINED = ("chain_pipe", "binomial_pipe", "bidir_ring")
 
 

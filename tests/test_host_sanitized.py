@@ -25,7 +25,7 @@ CSRC = os.path.join(ROOT, "collective_communication_algorithms_amd", "csrc")
 
 
 SOURCES = [os.path.join(ROOT, "tests", "host_check", "host_check.cpp"), os.path.join(CSRC, "plan.cpp"),
-           os.path.join(CSRC, "bind.cpp")]
+           os.path.join(CSRC, "bind.cpp"), os.path.join(CSRC, "colprog.cpp")]
 INCLUDES = [f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
 
 

@@ -166,7 +166,7 @@ def expected_auto(kind, N, count, dtype, alpha, beta):
             _, c = coll_plan(kind, algo, N, count, dtype, 0, 1)
         except CollError:
             continue
-        t = c["steps"] * alpha + c["moved_bytes"] / beta
+        t = c["round_trips"] * alpha + c["moved_bytes"] / beta
         if best is None or t < best[0]:
             best = (t, algo)
     return best[1]
@@ -175,21 +175,25 @@ def expected_auto(kind, N, count, dtype, alpha, beta):
 @pytest.mark.parametrize("kind", list(CANDIDATES))
 @pytest.mark.parametrize("N", [1, 2, 5, 8, 32])
 def test_auto_picks_the_least_predicted_time(kind, N):
-    """COLL_ALGO_AUTO = argmin over the candidates of steps * alpha + moved bytes /
-    beta, computed here from coll_plan's own counts (first candidate on ties)."""
+    """COLL_ALGO_AUTO = argmin over the candidates of round trips * alpha + moved
+    bytes / beta, computed here from coll_plan's own counts (first candidate on
+    ties), under the column kernel (exec 0) and the row kernel (exec 2)."""
     from collective_communication_algorithms_amd import coll_set_option
     try:
-        for alpha_ns, beta_gbps in ((1060, 8200), (10 ** 8, 8200), (0, 1)):
-            coll_set_option("model_alpha_ns", alpha_ns)
-            coll_set_option("model_beta_gbps", beta_gbps)
-            for count in (N, 64 * N, (1 << 20) * N):
-                dtype = "bfloat16"
-                if kind == "alltoall" and count % N:
-                    continue
-                want = expected_auto(kind, N, count, dtype, alpha_ns * 1e-9, beta_gbps * 1e9)
-                got = coll_plan(kind, "auto", N, count, dtype, 0, 1)
-                assert got == coll_plan(kind, want, N, count, dtype, 0, 1), (kind, N, count, alpha_ns, want)
+        for exec_mode in (0, 2):
+            coll_set_option("exec", exec_mode)
+            for alpha_ns, beta_gbps in ((1060, 8200), (10 ** 8, 8200), (0, 1)):
+                coll_set_option("model_alpha_ns", alpha_ns)
+                coll_set_option("model_beta_gbps", beta_gbps)
+                for count in (N, 64 * N, (1 << 20) * N):
+                    dtype = "bfloat16"
+                    if kind == "alltoall" and count % N:
+                        continue
+                    want = expected_auto(kind, N, count, dtype, alpha_ns * 1e-9, beta_gbps * 1e9)
+                    got = coll_plan(kind, "auto", N, count, dtype, 0, 1)
+                    assert got == coll_plan(kind, want, N, count, dtype, 0, 1), (kind, N, count, alpha_ns, want)
     finally:
+        coll_set_option("exec", 0)
         coll_set_option("model_alpha_ns", 1060)
         coll_set_option("model_beta_gbps", 8200)
 
@@ -202,24 +206,70 @@ def test_auto_extremes():
         assert coll_plan("alltoall", "auto", 32, 32 * 4096, "bfloat16") == coll_plan("alltoall", "bruck", 32, 32 * 4096, "bfloat16")
         coll_set_option("model_alpha_ns", 0)
         assert coll_plan("alltoall", "auto", 32, 32 * 4096, "bfloat16") == coll_plan("alltoall", "pairwise", 32, 32 * 4096, "bfloat16")
+        # the row kernel moves the binomial tree's staging bytes; the column
+        # kernel moves each chunk once for either algorithm (a tie: binomial)
+        coll_set_option("exec", 2)
         assert coll_plan("scatter", "auto", 8, 8 << 20, "uint8") == coll_plan("scatter", "linear", 8, 8 << 20, "uint8")
+        coll_set_option("exec", 0)
+        assert coll_plan("scatter", "auto", 8, 8 << 20, "uint8") == coll_plan("scatter", "binomial", 8, 8 << 20, "uint8")
     finally:
+        coll_set_option("exec", 0)
         coll_set_option("model_alpha_ns", 1060)
         coll_set_option("model_beta_gbps", 8200)
 
 
 @pytest.mark.parametrize("kind", list(CANDIDATES))
 def test_moved_bytes_are_the_schedule_bytes_on_small_columns(kind):
-    """Below 8 MiB of columns no list runs in the forwarding variant: every
-    operand is loaded and every result stored."""
+    """Row kernel (exec 2): below 8 MiB of columns no list runs in the
+    forwarding variant, so every operand is loaded and every result stored,
+    and every step is a round trip."""
+    from collective_communication_algorithms_amd import coll_set_option
     N = 8
-    for algo in CANDIDATES[kind]:
-        for count in (N * 1000, (4 << 20) // 4 // N * N):
+    try:
+        coll_set_option("exec", 2)
+        for algo in CANDIDATES[kind]:
+            for count in (N * 1000, (4 << 20) // 4 // N * N):
+                try:
+                    _, c = coll_plan(kind, algo, N, count, "float32", 0, 1)
+                except CollError:
+                    continue
+                assert c["moved_bytes"] == c["hbm_bytes"], (kind, algo, count)
+                assert c["round_trips"] == c["steps"], (kind, algo, count)
+    finally:
+        coll_set_option("exec", 0)
+
+
+@pytest.mark.parametrize("N", [2, 3, 8, 16])
+def test_column_kernel_moved_bytes_closed_forms(N):
+    """Column kernel (exec 0, the default), in place, any algorithm: each input
+    a program needs is loaded once and each defined output stored once, in one
+    round trip.  AllReduce 2NM (every input read, every result written);
+    ReduceScatter (N+1)M (every input read, one chunk written per rank);
+    AllGather and Broadcast NM (each chunk / the root read once, written to
+    the N-1 others); Scatter and Gather 2(N-1)M/N (each chunk but the root's
+    own read once and written once); Reduce (N+1)M.  Ragged chunks count by
+    their elements."""
+    count = 1000 * N + 7
+    sz = 4
+    M = count * sz
+    want = {"allreduce": 2 * N * M, "reducescatter": (N + 1) * M, "allgather": N * M, "broadcast": N * M,
+            "reduce": (N + 1) * M}
+    for kind, algos in CANDIDATES.items():
+        if kind == "alltoall":
+            continue
+        for algo in algos:
             try:
-                _, c = coll_plan(kind, algo, N, count, "float32", 0, 1)
+                _, c = coll_plan(kind, algo, N, count, "float32", 1 % N, 3)
             except CollError:
                 continue
-            assert c["moved_bytes"] == c["hbm_bytes"], (kind, algo, count)
+            assert c["round_trips"] == 1, (kind, algo)
+            if kind in want:
+                assert c["moved_bytes"] == want[kind], (kind, algo, c["moved_bytes"], want[kind])
+            else:
+                # scatter / gather: every chunk except the root's, once each way
+                root = 1 % N
+                lo, hi = root * count // N, (root + 1) * count // N
+                assert c["moved_bytes"] == 2 * (count - (hi - lo)) * sz, (kind, algo)
 
 
 @pytest.mark.parametrize("N", [8, 16])
@@ -253,7 +303,7 @@ def test_moved_bytes_follow_the_options():
         coll_set_option("exec", 1)
         _, c = coll_plan("allreduce", "ring", 8, count, "float32", 0, 1)
         assert c["moved_bytes"] == c["hbm_bytes"]
-        coll_set_option("exec", 0)
+        coll_set_option("exec", 2)
         coll_set_option("nontemporal", 7)
         _, c = coll_plan("allreduce", "ring", 8, count, "float32", 0, 1)
         assert c["moved_bytes"] == c["hbm_bytes"]
@@ -262,13 +312,29 @@ def test_moved_bytes_follow_the_options():
         coll_set_option("nontemporal", -1)
 
 
-def test_auto_picks_ring_on_large_columns():
-    """With the default model, Ring wins once its chains forward (8 x 64 MiB
-    fp32: Ring 208 us, DBT 257, RHD 265 measured on MI355X), and the fewer
-    steps of RHD / DBT win below 8 MiB, where nothing forwards."""
-    big = coll_plan("allreduce", "auto", 8, (64 << 20) // 4, "float32", 0, 1)
-    assert big == coll_plan("allreduce", "ring", 8, (64 << 20) // 4, "float32", 0, 1)
-    small = coll_plan("allreduce", "auto", 8, (1 << 20) // 4, "float32", 0, 1)
-    assert small != coll_plan("allreduce", "ring", 8, (1 << 20) // 4, "float32", 0, 1)
-    rs = coll_plan("reducescatter", "auto", 16, (64 << 20) // 2, "bfloat16", 0, 1)
-    assert rs == coll_plan("reducescatter", "ring", 16, (64 << 20) // 2, "bfloat16", 0, 1)
+def test_auto_picks_ring_on_large_columns_in_the_row_kernel():
+    """Row kernel (exec 2), default model: Ring wins once its chains forward
+    (8 x 64 MiB fp32: Ring 208 us, DBT 257, RHD 265 measured on MI355X), and
+    the fewer steps of RHD / DBT win below 8 MiB, where nothing forwards."""
+    from collective_communication_algorithms_amd import coll_set_option
+    try:
+        coll_set_option("exec", 2)
+        big = coll_plan("allreduce", "auto", 8, (64 << 20) // 4, "float32", 0, 1)
+        assert big == coll_plan("allreduce", "ring", 8, (64 << 20) // 4, "float32", 0, 1)
+        small = coll_plan("allreduce", "auto", 8, (1 << 20) // 4, "float32", 0, 1)
+        assert small != coll_plan("allreduce", "ring", 8, (1 << 20) // 4, "float32", 0, 1)
+        rs = coll_plan("reducescatter", "auto", 16, (64 << 20) // 2, "bfloat16", 0, 1)
+        assert rs == coll_plan("reducescatter", "ring", 16, (64 << 20) // 2, "bfloat16", 0, 1)
+    finally:
+        coll_set_option("exec", 0)
+
+
+def test_auto_in_the_column_kernel_ties_to_the_first_candidate():
+    """Column kernel: Ring, RHD and DBT AllReduce all move 2NM in one round
+    trip, so the tie goes to the first candidate (DBT); ReduceScatter RHD and
+    Ring both move (N+1)M (RHD first when N = 2^n)."""
+    for count in ((1 << 10), (64 << 20) // 4):
+        assert coll_plan("allreduce", "auto", 8, count, "float32", 0, 1) == \
+            coll_plan("allreduce", "dbt", 8, count, "float32", 0, 1)
+    assert coll_plan("reducescatter", "auto", 16, (64 << 20) // 2, "bfloat16", 0, 1) == \
+        coll_plan("reducescatter", "rhd", 16, (64 << 20) // 2, "bfloat16", 0, 1)
