@@ -1,19 +1,23 @@
 """Headline benchmark: Ring AllReduce, fp32, 8 virtual ranks x 256 MiB, one GPU.
 
-    python bench.py [--steps K] [--warmup W] [--algo ring|rhd|dbt] [--exec persistent|step]
+    python bench.py [--steps K] [--warmup W] [--algo ring|rhd|dbt] [--exec auto|rows|step]
 
-A step is one whole AllReduce call (all 2(N-1) schedule steps, with the per-row
-checksums unless --no-checksums) over the 8 rank buffers, in place, inputs
-resident in HBM.  The per-call HIP events also hold the clearing of the checksum
-slots (a kernel of about a microsecond).  Prints one JSON line:
-  value        busbw in GB/s = algbw * 2(N-1)/N, algbw = M / time per call
-               ("集合通信算法延迟公式", @tbl-model-algo-busbw-coef)
-  roofline     algorithmic bytes per launch (every row reads its source, a
-               reduce row also its destination, and writes its destination:
-               5(N-1)M for this call) / the row kernel's mean launch time,
-               against MI355X's 8 TB/s HBM peak
-  cpu_baseline the CPU oracle on the same inputs, one core
-Extra per-call detail goes to stderr.
+A step is one whole AllReduce call (every row of the schedule's 2(N-1) steps,
+with the per-row checksums unless --no-checksums) over the 8 rank buffers, in
+place, inputs resident in HBM.  Before every call (warm-up and timed) the
+inputs are restored from a pristine device copy, untimed; each timed call is
+bracketed by HIP events on its stream.  Prints one JSON line:
+  value         busbw in GB/s = algbw * 2(N-1)/N, algbw = M / median call time
+                ("集合通信算法延迟公式", @tbl-model-algo-busbw-coef)
+  ms_per_step   the median call time (minimum and every call's time beside it)
+  hbm_pct_of_peak  bytes the call moves through memory / median call time, as
+                a percentage of MI355X's 8 TB/s HBM peak
+  roofline      the column kernel's algorithmic bytes per launch (each rank's
+                input read once and its result written once: 2NM; what the
+                schedule's steps pass from row to row stays in registers) over
+                its mean launch time, timed live by the library's own HIP
+                events (COLL_OPT_TIMING) in a second pass of restored calls
+  cpu_baseline  the CPU oracle on the same inputs, one core
 """
 
 from __future__ import annotations
@@ -30,19 +34,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "busbw GB/s & % HBM peak, Ring AllReduce fp32 N=8 M=256MiB (1 GPU)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_kernel_ring_allreduce_fp32_n8_256MiB.json")
-# the row kernel variant the default run times: fp32, sum, per-row checksums,
-# nontemporal source loads, not the fine variant
-HEADLINE_KERNEL = "void coll::rows_kernel<2, 0, true, 5, false, true>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_col_kernel_ring_allreduce_fp32_n8_256MiB.json")
+# the column kernel variant the default run times: fp32, sum, 16-byte units,
+# 8 register slots, 16 checksum accumulators, nontemporal loads and stores
+HEADLINE_KERNEL = "void coll::(anonymous namespace)::col_kernel<2, 0, 16, 8, 16, 5>"
 
 
 def kernel_source_hash() -> str:
     """Hash of the code (comments and blank space removed) that decides what the
-    row kernel does: the kernels and their launch shapes and work lists, so
-    that the committed counter summary is dropped whenever any of it changes."""
+    column kernel does: the kernel, its programs and launch shapes, so that the
+    committed counter summary is dropped whenever any of it changes."""
     import re
     h = hashlib.sha256()
-    for f in ("kernels.hip", "device_types.h", "abi.cpp", "bind.h", "bind.cpp"):
+    for f in ("colkernel.hip", "device_common.h", "device_types.h", "colprog.h", "colprog.cpp", "abi.cpp"):
         with open(os.path.join(ROOT, "collective_communication_algorithms_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -90,9 +94,14 @@ def cpu_baseline(inputs_host, N: int, count: int, algo: str, cols=None, gpu_samp
     dt = sum(times) / len(times)
     M = count * 4
     busbw = M / dt * 2 * (N - 1) / N / 1e9
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     res = {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"{len(times)} calls of the full workload ({N} x {M >> 20} MiB fp32, one {algo} "
-                     f"AllReduce each), numpy single-threaded, {sum(times):.1f} s in all, {dt:.2f} s per call"}
+                     f"AllReduce each), numpy single-threaded, {sum(times):.1f} s in all, {dt:.2f} s per call",
+           "host_cpu_count": os.cpu_count(), "host_cpus_in_affinity": affinity}
     if cols is not None:
         res["matches_gpu"] = all(np.array_equal(o[cols].view(np.uint32), g.view(np.uint32))
                                  for o, g in zip(out, gpu_sample))
@@ -536,9 +545,10 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--algo", default="ring", choices=["ring", "rhd", "dbt"])
-    ap.add_argument("--exec", default="persistent", choices=["persistent", "step"])
+    ap.add_argument("--exec", default="auto", choices=["auto", "rows", "step"],
+                    help="auto: the column kernel; rows: the row kernel in one launch; step: a launch per step")
     ap.add_argument("--nranks", type=int, default=8)
     ap.add_argument("--mib", type=int, default=256, help="MiB per rank")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -569,8 +579,8 @@ def main() -> int:
         print("bench.py: the collectives run between N virtual ranks in one GPU's memory; "
               "--gpus above 1 is not supported", file=sys.stderr)
         return 2
-    if args.steps < 1 or args.steps > 40:
-        print("bench.py: --steps must be in [1, 40] (in-place sums grow 8x per call)", file=sys.stderr)
+    if args.steps < 1 or args.steps > 200:
+        print("bench.py: --steps must be in [1, 200]", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -593,15 +603,21 @@ def main() -> int:
         return single_call(args, dev)
     N, M = args.nranks, args.mib << 20
     count = M // 4
-    coll.coll_set_option("exec", 1 if args.exec == "step" else 0)
+    coll.coll_set_option("exec", {"auto": 0, "step": 1, "rows": 2}[args.exec])
 
-    # inputs: 8 rank buffers of N(0,1) fp32 drawn by torch's seeded generator on the device
-    buf = torch.empty((N, count), dtype=torch.float32, device=dev)
-    ranks = si.device_rank_tensors(3, N, count, "float32", dev, out=buf)
+    # inputs: 8 rank buffers of N(0,1) fp32 drawn by torch's seeded generator on
+    # the device, and a pristine copy every call is restored from
+    pristine = torch.empty((N, count), dtype=torch.float32, device=dev)
+    si.device_rank_tensors(3, N, count, "float32", dev, out=pristine)
+    buf = pristine.clone()
+    ranks = list(buf)
     torch.cuda.synchronize()
     host_inputs = None
     if not args.no_cpu_baseline:
-        host_inputs = [r.cpu().numpy() for r in ranks]
+        host_inputs = [r.cpu().numpy() for r in pristine]
+
+    def restore():
+        buf.copy_(pristine)
 
     # before timing: one call on the fresh inputs, checked on sampled columns
     # against the definition (the fp64 sum over ranks) within the binary32
@@ -611,7 +627,7 @@ def main() -> int:
                                      np.arange(count - 65536, count),
                                      np.arange(count // N - 4096, count // N + 4096)]))
     cols_t = torch.from_numpy(cols).to(dev)
-    sample_in = np.stack([r.index_select(0, cols_t).cpu().numpy() for r in ranks]).astype(np.float64)
+    sample_in = np.stack([r.index_select(0, cols_t).cpu().numpy() for r in pristine]).astype(np.float64)
     # per-row checksums (the u64 wrap-sum of each row's destination words after
     # the row) are part of every timed call unless --no-checksums
     sums = None
@@ -632,40 +648,60 @@ def main() -> int:
     stats = coll.coll_get_stats()
 
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        coll.coll_allreduce(ranks, algo=args.algo)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
+
+    def timed_calls(k):
+        ts = []
+        for _ in range(k):
+            restore()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            coll.coll_allreduce(ranks, algo=args.algo)
+            e.record(stream)
+            e.synchronize()
+            ts.append(s.elapsed_time(e))
+        return ts
+
+    timed_calls(args.warmup)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    t_all0.record(stream)
-    for s, e in ev:
-        s.record(stream)
-        coll.coll_allreduce(ranks, algo=args.algo)
-        e.record(stream)
-    t_all1.record(stream)
+    per_call = timed_calls(args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    total_ms = t_all0.elapsed_time(t_all1)
-    per_call = [s.elapsed_time(e) for s, e in ev]
-    ms = total_ms / args.steps
+    ms = float(np.median(per_call))
+    ms_min = float(np.min(per_call))
+    # second pass: the data-moving kernels alone, between the library's events
+    coll.coll_set_option("timing", 1)
+    kernel_ms = []
+    for _ in range(args.steps):
+        restore()
+        coll.coll_allreduce(ranks, algo=args.algo)
+        kernel_ms.append(coll.coll_last_kernel_ms())
+    coll.coll_set_option("timing", 0)
+    # the earlier protocol, for reference: calls back to back on the same
+    # buffers, no restore, mean time
+    restore()
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(args.steps):
+        coll.coll_allreduce(ranks, algo=args.algo)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    back_to_back_ms = b0.elapsed_time(b1) / args.steps
     if sums is not None:
         coll.coll_set_checksums(None)
-    if not bool(torch.isfinite(ranks[0][:1024]).all()):
-        print("bench.py: values overflowed", file=sys.stderr)
-        return 1
 
     algbw = M / (ms * 1e-3) / 1e9
     busbw = algbw * 2 * (N - 1) / N
-    hbm_bytes = stats["hbm_bytes"]                      # 5(N-1)M: schedule bytes of one call
-    launches = 1 if args.exec == "persistent" else stats["steps"]
-    launch_ms = float(np.mean(per_call)) / launches
-    achieved = hbm_bytes / launches / (launch_ms * 1e-3) / 1e9
-    traffic = load_traffic(hbm_bytes / launches)
+    moved = stats["moved_bytes"]           # what the kernels move: 2NM here
+    hbm_bytes = stats["hbm_bytes"]         # 5(N-1)M: the schedule's row bytes
+    launches = stats["steps"] if args.exec == "step" else 1
+    launch_ms = float(np.mean(kernel_ms)) / launches
+    achieved = moved / launches / (launch_ms * 1e-3) / 1e9
+    traffic = load_traffic(moved / launches)
     from collective_communication_algorithms_amd import model
     pred_ms = model.time("allreduce", args.algo, N, M, 5e-6, 450e9) * 1e3
+    engine = {"auto": "column kernel", "rows": "row kernel, one launch", "step": "row kernel, a launch per step"}
 
     result = {
         "metric": METRIC,
@@ -682,26 +718,28 @@ def main() -> int:
         "data": "synthetic: N(0,1) fp32 per rank from torch's seeded device generator",
         "config": {"workload": f"{args.algo}_allreduce_fp32_n{N}_{args.mib}MiB", "nranks": N,
                    "bytes_per_rank": M, "algo": args.algo, "op": "sum", "inplace": True,
-                   "exec": args.exec, "schedule_steps": stats["steps"], "checksums": sums is not None},
+                   "exec": engine[args.exec], "schedule_steps": stats["steps"], "checksums": sums is not None},
+        "ms_min": round(ms_min, 4),
+        "per_call_ms": [round(x, 4) for x in per_call],
+        "timing": "each call alone between HIP events after an untimed restore of its inputs; median and min",
         "algbw_GBps": round(algbw, 2),
-        "hbm_pct_of_peak": round(100 * hbm_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "moved_bytes_per_call": moved,
+        "hbm_pct_of_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
-        # bytes the row kernel actually moved through the memory fabric (the
-        # committed rocprofv3 counters, scaled) per mean launch time
-        "fabric_traffic_GBps": round(traffic / (launch_ms * 1e-3) / 1e9, 1) if traffic else None,
-        "fabric_pct_of_peak": round(100 * traffic / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2) if traffic else None,
-        # the library's own count of the bytes the launched kernels moved (the
-        # schedule bytes less operands passed in registers and skipped stores)
-        "moved_bytes_per_call": stats["moved_bytes"],
+        "kernel_ms_mean": round(launch_ms, 4),
+        # the schedule's row bytes (every row reading its operands and writing
+        # its destination through memory) per median call: a rate no kernel
+        # moves, kept for comparison with the pages' step model
+        "schedule_bytes_per_call": hbm_bytes,
+        "schedule_rate_GBps": round(hbm_bytes / (ms * 1e-3) / 1e9, 1),
+        "back_to_back_mean_ms": round(back_to_back_ms, 4),
         "cpu_baseline": None,
         "alpha_beta_page_model_ms": round(pred_ms, 4),
         "parity": "within the binary32 error bound of the fp64 sum on %d sampled columns per rank" % len(cols),
         "wall_s_timed_region": round(wall, 4),
     }
-    print(json.dumps({"per_call_ms": [round(x, 4) for x in per_call], "launch_ms_mean": launch_ms,
-                      "schedule_hbm_bytes": hbm_bytes}), file=sys.stderr)
-    del buf, ranks
+    del buf, ranks, pristine
     torch.cuda.empty_cache()
     if host_inputs is not None:
         result["cpu_baseline"] = cpu_baseline(host_inputs, N, count, args.algo, cols, gpu_sample, gpu_sums=gpu_sums)

@@ -161,6 +161,14 @@ def coll_set_option(name, value):
     check(_lib.load().coll_set_option(_code(OPTIONS, name, "option"), int(value)))
 
 
+def coll_last_kernel_ms() -> float:
+    """Milliseconds between the HIP events around the data-moving kernels of
+    this thread's last call made with the "timing" option on (waits for it)."""
+    ms = ctypes.c_float()
+    check(_lib.load().coll_last_kernel_ms(ctypes.byref(ms)))
+    return float(ms.value)
+
+
 def coll_check(stream=None, device=None):
     """Wait for the stream's work (the current stream of ``device``, default
     the current device, when None) and raise CollError if it failed."""

@@ -16,13 +16,17 @@
 //     arithmetic as the row kernel, so float results keep the schedule's
 //     association), a copy row passes a value on; `y` holds the last result,
 //     other values live in slots;
-//   * adds every op's value to its row's checksum (same words, same rotation
-//     as the row kernel);
+//   * adds every op's value to its checksum accumulator (same words, same
+//     rotation as the row kernel; a row whose value an op carries already
+//     shares that op's sum);
 //   * stores each rank's final value where the collective defines it.
 // What the schedule's steps would have passed through memory stays in
 // registers, so the kernel moves each leaf once and each stored output once:
 // for an in-place AllReduce over N ranks of M bytes, 2NM bytes.  No work group
-// reads or writes another's columns, so nothing waits on anything.
+// reads or writes another's columns, so nothing waits on anything.  Row
+// checksums: each work group stores its per-op totals to slots of its own,
+// and a fold kernel adds up each row's slots (device-scope atomics from one
+// work group per KiB of columns cost more than the whole copy).
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -262,15 +266,54 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
     }
   }
   if constexpr (NA > 0) {
+    // op k's wave total goes to lane k, which stores it in this work group's
+    // own slot: no atomics, every slot written once per call
+    uint64_t mine = 0;
     for (uint32_t k = 0; k < nop; ++k) {
       const uint64_t tot = wave_sum(acc.get(k));
-      if (lane == 0) {
-        const uint32_t row = cload(a.acc_rows + wk.acc + k);
-        __hip_atomic_fetch_add(a.sums + uint64_t(row) * SUM_LANES + (blockIdx.x & (SUM_LANES - 1u)), tot,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      if (lane == k) mine = tot;
     }
+    if (lane < nop) *gptr<uint64_t>(reinterpret_cast<char*>(a.partial + wk.part + lane)) = mine;
   }
+}
+
+// Row checksums from the column kernel's partial sums, in two launches: work
+// group (r, q) adds slice q (of COL_FOLD_SLICES) of the slots row r's ColRefs
+// name into tmp[r * COL_FOLD_SLICES + q]; then one wave per row adds its
+// slices into out[r].  A row of the headline call has 8,000-33,000 slots,
+// which one work group per row would take longer to add than the slices do.
+__global__ __launch_bounds__(BLOCK_THREADS) void col_fold_kernel(const ColRef* refs, const uint32_t* row_off,
+                                                                  const uint64_t* partial, uint64_t* tmp) {
+  __shared__ uint64_t wsum[BLOCK_THREADS / 64];
+  const uint32_t r = blockIdx.x / COL_FOLD_SLICES, q = blockIdx.x % COL_FOLD_SLICES;
+  const uint32_t i0 = cload(row_off + r), i1 = cload(row_off + r + 1);
+  uint64_t acc = 0;
+  for (uint32_t i = i0; i < i1; ++i) {
+    const ColRef c = cload(refs + i);
+    const uint32_t w0 = uint32_t((uint64_t(c.count) * q) / COL_FOLD_SLICES);
+    const uint32_t w1 = uint32_t((uint64_t(c.count) * (q + 1)) / COL_FOLD_SLICES);
+    for (uint32_t w = w0 + threadIdx.x; w < w1; w += BLOCK_THREADS)
+      acc += *gptr<uint64_t>(reinterpret_cast<const char*>(partial + c.first + uint64_t(w) * c.stride));
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63u) == 0) wsum[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t t = 0;
+    for (int k = 0; k < BLOCK_THREADS / 64; ++k) t += wsum[k];
+    *gptr<uint64_t>(reinterpret_cast<char*>(tmp + blockIdx.x)) = t;
+  }
+}
+
+__global__ __launch_bounds__(BLOCK_THREADS) void col_fold_rows_kernel(const uint64_t* tmp, uint64_t* out,
+                                                                       uint64_t nrows) {
+  static_assert(COL_FOLD_SLICES <= 64, "one lane per slice");
+  const uint64_t r = uint64_t(blockIdx.x) * (BLOCK_THREADS / 64) + (threadIdx.x >> 6);
+  if (r >= nrows) return;  // uniform across the wave
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint64_t v = lane < COL_FOLD_SLICES ? *gptr<uint64_t>(reinterpret_cast<const char*>(tmp + r * COL_FOLD_SLICES + lane)) : 0;
+  const uint64_t t = wave_sum(v);
+  if (lane == 0) *gptr<uint64_t>(reinterpret_cast<char*>(out + r)) = t;
 }
 
 typedef void (*ColFn)(ColArgs);
@@ -310,6 +353,20 @@ ColFn pick_col(int dtype, int op, int unit, int leaves, int accs, bool nt) {
 hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool nt, uint32_t grid,
                       hipStream_t stream) {
   hipLaunchKernelGGL(pick_col(dtype, op, unit, leaves, accs, nt), dim3(grid), dim3(COL_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,
+                           uint64_t* out, uint64_t nrows, hipStream_t stream) {
+  if (nrows == 0) return hipSuccess;
+  if (nrows * COL_FOLD_SLICES > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(col_fold_kernel, dim3(uint32_t(nrows * COL_FOLD_SLICES)), dim3(BLOCK_THREADS), 0, stream, refs,
+                     row_off, partial, tmp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint64_t per = BLOCK_THREADS / 64;
+  hipLaunchKernelGGL(col_fold_rows_kernel, dim3(uint32_t((nrows + per - 1) / per)), dim3(BLOCK_THREADS), 0, stream,
+                     tmp, out, nrows);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 #include "colprog.h"
 
 #include <algorithm>
+#include <map>
 
 #include "bind.h"
 
@@ -36,7 +37,7 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
     p.why = w;
     p.segs.clear();
     p.code.clear();
-    p.acc_rows.clear();
+    p.refs.clear();
     return p;
   };
   if (s.kind == COLL_K_ALLTOALL) return fail("AllToAll rows move data between offsets");
@@ -158,9 +159,28 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
         live[size_t(nodes[n].a)] = 1;
         live[size_t(nodes[n].b)] = 1;
       }
+    // with checksums: one op per combine, and one per copy whose value and
+    // rotation no op before it carries; `carrier[i]`: the op whose value is
+    // event i's row's checksum over this segment
     std::vector<Event> ops;
-    for (const Event& e : ev)
-      if (checksums || (e.combine && live[size_t(e.node)])) ops.push_back(e);
+    std::vector<int> carrier(ev.size(), -1);
+    std::map<std::pair<int, uint32_t>, int> carried;  // (value, shift) -> op
+    for (size_t i = 0; i < ev.size(); ++i) {
+      const Event& e = ev[i];
+      if (checksums) {
+        auto key = std::make_pair(e.node, e.shift);
+        auto it = carried.find(key);
+        if (!e.combine && it != carried.end()) {
+          carrier[i] = it->second;
+          continue;
+        }
+        carrier[i] = int(ops.size());
+        carried[key] = int(ops.size());
+        ops.push_back(e);
+      } else if (e.combine && live[size_t(e.node)]) {
+        ops.push_back(e);
+      }
+    }
     if (ops.empty() && stores.empty()) continue;  // nothing to load, compute or store
 
     // positions: op i at i, store j at ops.size() + j; the last use of each value
@@ -198,7 +218,6 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
       }
     const int nload = int(owner.size());
     sg.ops = uint32_t(p.code.size());
-    sg.acc = uint32_t(p.acc_rows.size());
     int y = -1;
     for (int i = 0; i < K; ++i) {
       const Event& e = ops[size_t(i)];
@@ -238,10 +257,7 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
       } else {
         operand(e.node, CI_A_Y, in.a);
       }
-      if (checksums) {
-        in.flags |= CI_CKS;
-        p.acc_rows.push_back(e.row);
-      }
+      if (checksums) in.flags |= CI_CKS;
       p.code.push_back(in);
     }
     sg.stores = uint32_t(p.code.size());
@@ -267,6 +283,9 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
     p.max_ops = std::max<uint32_t>(p.max_ops, uint32_t(K));
     p.max_stores = std::max<uint32_t>(p.max_stores, uint32_t(stores.size()));
     p.moved_bytes += uint64_t(nload + int(stores.size())) * (sg.s1 - sg.s0);
+    if (checksums)
+      for (size_t i = 0; i < ev.size(); ++i)
+        p.refs.push_back(ColRowRef{ev[i].row, uint32_t(p.segs.size()), uint32_t(carrier[i])});
     p.segs.push_back(sg);
   }
   for (const ColVariant& v : kVariants) {
@@ -279,30 +298,50 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
   return fail("no kernel variant holds the programs");
 }
 
-std::vector<ColWork> col_works(const ColPlan& p, uint32_t tiles_per_group) {
-  std::vector<ColWork> w;
+ColTables col_tables(const ColPlan& p, uint32_t tiles_per_group, size_t nrows) {
+  ColTables t;
   const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
   const uint32_t per = std::max<uint32_t>(1, std::min<uint32_t>(tiles_per_group, 65535));
+  const bool cks = p.v.accs > 0;
+  std::vector<uint64_t> base(p.segs.size()), groups(p.segs.size());
   for (size_t k = 0; k < p.segs.size(); ++k) {
     const ColSeg& sg = p.segs[k];
     const uint64_t t0 = sg.s0 / tb, t1 = (sg.s1 + tb - 1) / tb;
-    for (uint64_t t = t0; t < t1; t += per) {
+    base[k] = t.partials;
+    groups[k] = 0;
+    for (uint64_t q = t0; q < t1; q += per) {
       ColWork c{};
-      c.c0 = t * tb;
+      c.c0 = q * tb;
       c.s0 = sg.s0;
       c.s1 = sg.s1;
       c.loads = sg.loads;
       c.ops = sg.ops;
       c.stores = sg.stores;
-      c.acc = sg.acc;
+      c.part = uint32_t(cks ? t.partials : 0);
       c.nload = sg.nload;
       c.nop = sg.nop;
       c.nstore = sg.nstore;
-      c.ntiles = uint16_t(std::min<uint64_t>(per, t1 - t));
-      w.push_back(c);
+      c.ntiles = uint16_t(std::min<uint64_t>(per, t1 - q));
+      t.work.push_back(c);
+      ++groups[k];
+      if (cks) t.partials += sg.nop;
     }
   }
-  return w;
+  if (cks) {
+    t.row_off.assign(nrows + 1, 0);
+    for (const ColRowRef& r : p.refs) ++t.row_off[r.row + 1];
+    for (size_t r = 0; r < nrows; ++r) t.row_off[r + 1] += t.row_off[r];
+    t.refs.resize(p.refs.size());
+    std::vector<uint32_t> fill(t.row_off.begin(), t.row_off.end() - 1);
+    for (const ColRowRef& r : p.refs) {
+      ColRef c{};
+      c.first = uint32_t(base[r.seg] + r.op);
+      c.count = uint32_t(groups[r.seg]);
+      c.stride = p.segs[r.seg].nop;
+      t.refs[fill[r.row]++] = c;
+    }
+  }
+  return t;
 }
 
 }  // namespace coll

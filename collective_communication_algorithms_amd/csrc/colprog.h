@@ -21,6 +21,13 @@ struct ColVariant {
   int accs = 0;
 };
 
+// With checksums: row `row`'s checksum over segment `seg` is the sum of op
+// `op`'s values there (several rows may share an op: a copy carries the value
+// of the op that made it, with the same rotation).
+struct ColRowRef {
+  uint32_t row, seg, op;
+};
+
 struct ColPlan {
   bool ok = false;
   std::string why;               // when not ok: the first reason
@@ -28,7 +35,7 @@ struct ColPlan {
   uint64_t colspace = 0;         // bytes of columns (count * element size)
   std::vector<ColSeg> segs;
   std::vector<ColInstr> code;
-  std::vector<uint32_t> acc_rows;
+  std::vector<ColRowRef> refs;   // checksums only; one per (row, segment it covers)
   uint64_t moved_bytes = 0;      // leaf loads and stores: bytes each segment moves, summed
   uint32_t max_leaves = 0, max_slots = 0, max_ops = 0, max_stores = 0;
 };
@@ -54,8 +61,18 @@ constexpr int COL_LIST_MAX = 64;
 // those bytes unspecified.
 ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums, size_t max_segments = 8192);
 
-// Work groups: each segment's tiles (64 lanes x unit bytes, on the global tile
-// grid), `tiles_per_group` consecutive tiles per work group.
-std::vector<ColWork> col_works(const ColPlan& p, uint32_t tiles_per_group);
+// The kernel's tables for work groups of `tiles_per_group` consecutive tiles
+// (64 lanes x unit bytes each, on the global tile grid) of one segment.  With
+// checksums, work group w of segment k stores its nop partial sums at
+// partial[base_k + w * nop ...]; row r's ColRefs are refs[row_off[r] ..
+// row_off[r + 1]).
+struct ColTables {
+  std::vector<ColWork> work;
+  std::vector<uint32_t> row_off;  // nrows + 1 (checksums), else empty
+  std::vector<ColRef> refs;
+  uint64_t partials = 0;          // partial-sum slots the work groups write
+};
+
+ColTables col_tables(const ColPlan& p, uint32_t tiles_per_group, size_t nrows);
 
 }  // namespace coll

@@ -134,25 +134,39 @@ struct ColInstr {        // 8 bytes
 
 struct ColSeg {          // 40 bytes: one segment's program
   uint64_t s0, s1;       // column bytes [s0, s1)
-  uint32_t loads, ops, stores, acc;  // first instruction of each list; first checksum row
-  uint16_t nload, nop, nstore, pad;  // leaf k is loaded into slot k; op k feeds checksum acc + k
+  uint32_t loads, ops, stores;  // first instruction of each list
+  uint32_t pad0;
+  uint16_t nload, nop, nstore, pad;  // leaf k is loaded into slot k
 };
 
 struct ColWork {         // 48 bytes: one work group's tiles and its segment's program
   uint64_t c0;           // column byte of its first tile (a multiple of the tile size)
   uint64_t s0, s1;       // the segment's column bytes
-  uint32_t loads, ops, stores, acc;
+  uint32_t loads, ops, stores;
+  uint32_t part;         // checksums: its nop partial sums go to partial[part .. part + nop)
   uint16_t nload, nop, nstore;
   uint16_t ntiles;       // consecutive tiles from c0
+};
+
+// Row checksums of the column kernel: every work group stores op k's wave
+// total to its own slot (no atomics); a row's checksum is the sum of the
+// slots of the ops that carry its value, over the work groups of every
+// segment it covers.  One ColRef per (row, segment): `count` slots from
+// `first`, `stride` apart (a segment's work groups store their nop partial
+// sums one after the other).
+struct ColRef {          // 16 bytes
+  uint32_t first, count, stride, pad;
 };
 
 struct ColArgs {
   const ColWork* work;
   const ColInstr* code;
-  const uint32_t* acc_rows;  // per segment, the schedule row of op k's checksum
-  uint64_t* sums;            // partial row checksums (SUM_LANES per row) or nullptr
+  uint64_t* partial;         // checksums: partial sums, one per (work group, op); else nullptr
   RankPtrs p;
 };
+
+// Slices of a row's partial sums the checksum fold adds in parallel.
+constexpr uint32_t COL_FOLD_SLICES = 32;
 
 // Threads of a column-kernel work group (one wave).  Lane r also holds rank
 // r's buffer addresses, so programs name at most COL_THREADS ranks.

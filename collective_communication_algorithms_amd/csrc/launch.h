@@ -16,12 +16,16 @@ hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t 
 // out[r] = the u64 wrap-sum of partial[r * SUM_LANES .. r * SUM_LANES + SUM_LANES), r < nrows;
 // the slots read are set back to zero
 hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hipStream_t stream);
-hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, uint32_t grid, hipStream_t stream);
+hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, hipStream_t stream);
 hipError_t launch_spin(float* out, uint32_t iters, uint32_t grid, hipStream_t stream);
 // column kernel: the variant of (unit, leaves, accs) (ColVariant), nontemporal
 // loads and stores when `nt`; one work group of COL_THREADS per ColWork
 hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool nt, uint32_t grid,
                       hipStream_t stream);
+// out[r] = the sum of the partial slots row r's ColRefs name, r < nrows, by way
+// of tmp (nrows * COL_FOLD_SLICES slots)
+hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,
+                           uint64_t* out, uint64_t nrows, hipStream_t stream);
 int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt);
 int perm_blocks_per_cu(int unit, int slots, bool cks, bool nt);
 

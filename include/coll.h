@@ -278,6 +278,10 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  * COLL_OPT_MODEL_BETA_GBPS moved-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
  * COLL_OPT_COL_TILES       column kernel: tiles (64 lanes x 16 or 4 bytes) per
  *                          work group, up to 65535 [0: automatic, 1..8 by size].
+ * COLL_OPT_TIMING          1: every call made outside graph capture records a
+ *                          HIP event before its first data-moving kernel and
+ *                          one after its last (not around the checksum
+ *                          clearing or folding), for coll_last_kernel_ms [0].
  * COLL_OPT_CACHE_BYTES     device memory the schedule cache may hold, in bytes
  *                          [2^31]; least recently used schedules are dropped
  *                          (after synchronising their device) when a call
@@ -294,7 +298,8 @@ typedef enum {
   COLL_OPT_MODEL_ALPHA_NS = 5,
   COLL_OPT_MODEL_BETA_GBPS = 6,
   COLL_OPT_CACHE_BYTES = 7,
-  COLL_OPT_COL_TILES = 8
+  COLL_OPT_COL_TILES = 8,
+  COLL_OPT_TIMING = 9
 } coll_option_t;
 coll_status_t coll_set_option(coll_option_t key, int64_t value);
 /* The current value of an option; INVALID_ARG for an unknown key or NULL value. */
@@ -302,6 +307,12 @@ coll_status_t coll_get_option(coll_option_t key, int64_t* value);
 /* Schedules in the cache and the device bytes their tables and work lists
  * hold, summed over devices (either pointer may be NULL). */
 coll_status_t coll_cache_info(int64_t* schedules, int64_t* device_bytes);
+
+/* The time between the events of the last call this thread made with
+ * COLL_OPT_TIMING on, in ms (waits for that call's kernels; [P3]'s step
+ * model is checked against such times).  INVALID_ARG for NULL or when no call
+ * was timed; COLL_ERR_HIP when the events fail. */
+coll_status_t coll_last_kernel_ms(float* ms);
 
 /* Waits for the work enqueued on `stream` (a hipStream_t; NULL: the null
  * stream) and reports whether it failed: COLL_ERR_HIP with the HIP error text

@@ -690,12 +690,30 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
   }
   std::vector<std::vector<int>> stored(size_t(N), std::vector<int>(static_cast<size_t>(count), 0));
   std::vector<int64_t> row_elems(s.rows.size(), 0);
-  for (const ColSeg& sg : p.segs) {
+  // refs of each segment
+  std::vector<std::vector<ColRowRef>> seg_refs(p.segs.size());
+  for (const ColRowRef& r : p.refs) {
+    CHECK(r.seg < p.segs.size() && r.row < s.rows.size(), "%s: ref out of range", name(sh).c_str());
+    if (r.seg < p.segs.size() && r.row < s.rows.size()) seg_refs[r.seg].push_back(r);
+  }
+  CHECK(cks || p.refs.empty(), "%s: refs without checksums", name(sh).c_str());
+  for (size_t si = 0; si < p.segs.size(); ++si) {
+    const ColSeg& sg = p.segs[si];
     CHECK(sg.s0 % uint64_t(sh.sz) == 0 && sg.s1 % uint64_t(sh.sz) == 0 && sg.s0 < sg.s1 && sg.s1 <= p.colspace,
           "%s: segment bytes", name(sh).c_str());
     CHECK(int(sg.nload) <= p.v.leaves && sg.nload <= COL_LIST_MAX && sg.nop <= COL_LIST_MAX &&
               sg.nstore <= COL_LIST_MAX && (!cks || int(sg.nop) <= p.v.accs),
           "%s: program exceeds its variant", name(sh).c_str());
+    for (const ColRowRef& r : seg_refs[si]) {
+      CHECK(r.op < sg.nop, "%s: ref to op %u of %u", name(sh).c_str(), r.op, unsigned(sg.nop));
+      const Row& row = s.rows[r.row];
+      CHECK(row.dst_off * sh.sz <= int64_t(sg.s0) && int64_t(sg.s1) <= (row.dst_off + row.n) * sh.sz,
+            "%s: ref row does not cover its segment", name(sh).c_str());
+      if (r.op < sg.nop)
+        CHECK(p.code[sg.ops + r.op].arg == uint32_t((((-(row.dst_off * sh.sz)) % 4) + 4) % 4),
+              "%s: checksum shift", name(sh).c_str());
+    }
+    std::vector<uint32_t> opval(sg.nop);
     for (int64_t e = int64_t(sg.s0) / sh.sz; e < int64_t(sg.s1) / sh.sz; ++e) {
       std::vector<uint32_t> slot(size_t(p.v.leaves), 0xDEADBEEFu);
       std::vector<char> full(size_t(p.v.leaves), 0);
@@ -729,20 +747,18 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
             full[in.out < p.v.leaves ? in.out : 0] = 1;
           }
         } else {
+          CHECK(cks, "%s: a copy op without checksums", name(sh).c_str());
           v = opnd(CI_A_Y, in.a);
         }
         CHECK(((in.flags & CI_CKS) != 0) == cks, "%s: checksum flag", name(sh).c_str());
-        if (cks) {
-          const uint32_t row = p.acc_rows[sg.acc + k];
-          const Row& r = s.rows[row];
-          CHECK(r.dst_off <= e && e < r.dst_off + r.n, "%s: op row does not cover its column", name(sh).c_str());
-          CHECK(in.arg == uint32_t((((-(r.dst_off * sh.sz)) % 4) + 4) % 4), "%s: checksum shift", name(sh).c_str());
-          if (r.dst_off <= e && e < r.dst_off + r.n) {
-            CHECK(after[row][size_t(e - r.dst_off)] == v, "%s: op %u (row %u) value at element %lld",
-                  name(sh).c_str(), k, row, (long long)e);
-            ++row_elems[row];
-          }
-        }
+        opval[k] = v;
+      }
+      for (const ColRowRef& r : seg_refs[si]) {
+        const Row& row = s.rows[r.row];
+        if (r.op >= sg.nop || e < row.dst_off || e >= row.dst_off + row.n) continue;
+        CHECK(after[r.row][size_t(e - row.dst_off)] == opval[r.op], "%s: row %u checksum value at element %lld",
+              name(sh).c_str(), r.row, (long long)e);
+        ++row_elems[r.row];
       }
       for (uint32_t j = 0; j < sg.nstore; ++j) {
         const ColInstr& in = p.code[sg.stores + j];
@@ -773,28 +789,57 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
     for (size_t r = 0; r < s.rows.size(); ++r)
       CHECK(row_elems[r] == s.rows[r].n, "%s: row %zu checksummed over %lld of %lld elements", name(sh).c_str(), r,
             (long long)row_elems[r], (long long)s.rows[r].n);
-  // tiles: each segment's bytes are covered by its work groups' tiles exactly
-  const std::vector<ColWork> w = col_works(p, 3);
+  // tiles: each segment's bytes are covered by its work groups' tiles
+  // exactly; with checksums, the work groups' partial-sum slots are disjoint
+  // and every row's refs name exactly its ops' slots in every work group of
+  // each segment it covers
+  const ColTables t = col_tables(p, 3, s.rows.size());
   const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
   std::vector<uint64_t> covered(p.segs.size(), 0);
   std::map<uint64_t, size_t> seg_at;  // segments start at distinct columns
   for (size_t k = 0; k < p.segs.size(); ++k) seg_at[p.segs[k].s0] = k;
-  for (const ColWork& c : w) {
+  std::vector<std::vector<uint32_t>> seg_parts(p.segs.size());
+  std::vector<int> slot_writes(size_t(t.partials), 0);
+  for (const ColWork& c : t.work) {
     auto it = seg_at.find(c.s0);
     CHECK(it != seg_at.end() && c.c0 % tb == 0 && c.ntiles >= 1 && c.ntiles <= 3, "%s: work", name(sh).c_str());
     if (it == seg_at.end()) continue;
     const size_t segi = it->second;
     const ColSeg& sg = p.segs[segi];
     CHECK(c.s0 == sg.s0 && c.s1 == sg.s1 && c.loads == sg.loads && c.ops == sg.ops && c.stores == sg.stores &&
-              c.acc == sg.acc && c.nload == sg.nload && c.nop == sg.nop && c.nstore == sg.nstore,
+              c.nload == sg.nload && c.nop == sg.nop && c.nstore == sg.nstore,
           "%s: a work group's program is not its segment's", name(sh).c_str());
     const uint64_t lo = std::max<uint64_t>(c.c0, sg.s0), hi = std::min<uint64_t>(c.c0 + c.ntiles * tb, sg.s1);
     CHECK(lo < hi, "%s: a work group with no bytes of its segment", name(sh).c_str());
     if (lo < hi) covered[segi] += hi - lo;
+    if (cks) {
+      seg_parts[segi].push_back(c.part);
+      for (uint32_t k = 0; k < c.nop; ++k)
+        if (uint64_t(c.part) + k < t.partials) ++slot_writes[c.part + k];
+        else CHECK(false, "%s: partial slot out of range", name(sh).c_str());
+    }
   }
   for (size_t k = 0; k < p.segs.size(); ++k)
     CHECK(covered[k] == p.segs[k].s1 - p.segs[k].s0, "%s: segment %zu covered %llu bytes", name(sh).c_str(), k,
           (unsigned long long)covered[k]);
+  if (cks) {
+    for (size_t q = 0; q < slot_writes.size(); ++q)
+      CHECK(slot_writes[q] == 1, "%s: partial slot %zu written %d times", name(sh).c_str(), q, slot_writes[q]);
+    CHECK(t.row_off.size() == s.rows.size() + 1 && t.row_off.back() == t.refs.size(), "%s: row offsets",
+          name(sh).c_str());
+    // the slots each row adds, from its ColRefs, against its refs
+    for (size_t r = 0; r < s.rows.size() && t.row_off.size() == s.rows.size() + 1; ++r) {
+      std::vector<uint64_t> got, want;
+      for (uint32_t i = t.row_off[r]; i < t.row_off[r + 1]; ++i)
+        for (uint32_t w = 0; w < t.refs[i].count; ++w) got.push_back(uint64_t(t.refs[i].first) + uint64_t(w) * t.refs[i].stride);
+      for (const ColRowRef& rf : p.refs)
+        if (rf.row == r)
+          for (uint32_t part : seg_parts[rf.seg]) want.push_back(uint64_t(part) + rf.op);
+      std::sort(got.begin(), got.end());
+      std::sort(want.begin(), want.end());
+      CHECK(got == want, "%s: row %zu adds the wrong partial slots", name(sh).c_str(), r);
+    }
+  }
 }
 
 int main(int argc, char** argv) {

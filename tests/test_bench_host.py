@@ -23,6 +23,7 @@ def test_cpu_baseline_repeats_the_oracle_and_compares_with_a_sample():
     sample = [np.ascontiguousarray(w[cols]) for w in want]
     r = bench.cpu_baseline(a, N, count, "ring", cols, sample, min_seconds=0.05, max_calls=3)
     assert (r["kind"], r["cores"], r["unit"]) == ("oracle", 1, "GB/s") and r["value"] > 0
+    assert r["host_cpu_count"] == os.cpu_count() and r["host_cpus_in_affinity"] == len(os.sched_getaffinity(0))
     assert r["matches_gpu"] is True
     assert r["sample"].split()[0] in ("1", "2", "3") and "calls of the full workload" in r["sample"]
     bad = [s.copy() for s in sample]
