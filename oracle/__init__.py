@@ -24,7 +24,11 @@ Modules
 Every function here is pinned by a ``-m "not gpu"`` test against something other
 than itself: the pages' printed 8-node tables, closed-form step and byte counts,
 brute-force semantics on tiny inputs, torch's bfloat16 conversion, and
-fp64 error bounds.  No function is left "parity unpinned".
+fp64 error bounds.  ``run_plan_columns`` is pinned to ``run_plan`` on whole
+buffers, ``defined_regions`` to the buffer contract written out per element and
+to the collectives' definitions, and the uint8 element rule to every pair of
+bytes (tests/test_oracle_columns_regions.py, each with a planted mistake it
+catches).  No function is left "parity unpinned".
 """
 
 from . import numerics, schedules, simulate  # noqa: F401
