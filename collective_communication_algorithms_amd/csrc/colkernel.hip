@@ -7,8 +7,8 @@
 // step structure of every algorithm here: Ring ReduceScatter / AllGather,
 // Recursive Halving-Doubling, Double Binary Tree, Tree Reduce; "一对多通信：
 // Broadcast 与 Scatter" the Broadcast, Scatter and Gather trees and pipelines).
-// A work group is one wave; lane l takes `unit` bytes of every tile
-// [c0 + t * 64 * unit, ...) of its segment.  Per tile it
+// A work group is one wave; lane l takes bytes [16l, 16l + 16) of every
+// 1 KiB tile of its segment.  Per tile it
 //   * loads the program's leaves (each rank input the program needs, once)
 //     into register slots, all loads in flight together;
 //   * runs the ops in the rows' order: a recv_and_reduce row combines its old
@@ -36,39 +36,28 @@
 namespace coll {
 namespace {
 
-template <int UNIT>
-struct ColUnitT;
-template <>
-struct ColUnitT<16> {
-  typedef u32x4 T;
-};
-template <>
-struct ColUnitT<4> {
-  typedef uint32_t T;
-};
-
-// NL slots of UNIT bytes in registers, indexed by a wave-uniform slot number:
+// NL slots of 16 bytes in registers, indexed by a wave-uniform slot number:
 // the compiler moves them with relative register addressing, which it does
 // for vectors of up to 32 dwords, so larger files are two such halves.
-template <int UNIT, int NL>
+template <int NL>
 struct Slots {
-  static constexpr int DW = NL * UNIT / 4;             // dwords
+  static constexpr int DW = NL * 4;                    // dwords
   static constexpr int HALF = DW > 32 ? DW / 2 : DW;   // dwords per part
   static_assert(DW <= 64 && DW % 4 == 0, "at most two 32-dword parts");
   typedef uint32_t V __attribute__((ext_vector_type(HALF)));
   V lo, hi;  // hi is unused when DW <= 32
 };
 
-template <int UNIT, int NL>
-__device__ __forceinline__ uint32_t slot_word(const Slots<UNIT, NL>& s, uint32_t i) {
-  typedef Slots<UNIT, NL> S;
+template <int NL>
+__device__ __forceinline__ uint32_t slot_word(const Slots<NL>& s, uint32_t i) {
+  typedef Slots<NL> S;
   if constexpr (S::DW <= 32) return s.lo[i];
   else return i < uint32_t(S::HALF) ? s.lo[i] : s.hi[i - S::HALF];
 }
 
-template <int UNIT, int NL>
-__device__ __forceinline__ void slot_word_set(Slots<UNIT, NL>& s, uint32_t i, uint32_t v) {
-  typedef Slots<UNIT, NL> S;
+template <int NL>
+__device__ __forceinline__ void slot_word_set(Slots<NL>& s, uint32_t i, uint32_t v) {
+  typedef Slots<NL> S;
   if constexpr (S::DW <= 32) {
     s.lo[i] = v;
   } else {
@@ -77,96 +66,51 @@ __device__ __forceinline__ void slot_word_set(Slots<UNIT, NL>& s, uint32_t i, ui
   }
 }
 
-template <int UNIT, int NL>
-__device__ __forceinline__ typename ColUnitT<UNIT>::T slot_get(const Slots<UNIT, NL>& s, uint32_t k) {
-  if constexpr (UNIT == 16) {
-    u32x4 r;
-    r.x = slot_word(s, 4 * k);
-    r.y = slot_word(s, 4 * k + 1);
-    r.z = slot_word(s, 4 * k + 2);
-    r.w = slot_word(s, 4 * k + 3);
-    return r;
-  } else {
-    return slot_word(s, k);
-  }
+template <int NL>
+__device__ __forceinline__ u32x4 slot_get(const Slots<NL>& s, uint32_t k) {
+  u32x4 r;
+  r.x = slot_word(s, 4 * k);
+  r.y = slot_word(s, 4 * k + 1);
+  r.z = slot_word(s, 4 * k + 2);
+  r.w = slot_word(s, 4 * k + 3);
+  return r;
 }
 
-template <int UNIT, int NL>
-__device__ __forceinline__ void slot_set(Slots<UNIT, NL>& s, uint32_t k, typename ColUnitT<UNIT>::T v) {
-  if constexpr (UNIT == 16) {
-    slot_word_set(s, 4 * k, v.x);
-    slot_word_set(s, 4 * k + 1, v.y);
-    slot_word_set(s, 4 * k + 2, v.z);
-    slot_word_set(s, 4 * k + 3, v.w);
-  } else {
-    slot_word_set(s, k, v);
-  }
+template <int NL>
+__device__ __forceinline__ void slot_set(Slots<NL>& s, uint32_t k, u32x4 v) {
+  slot_word_set(s, 4 * k, v.x);
+  slot_word_set(s, 4 * k + 1, v.y);
+  slot_word_set(s, 4 * k + 2, v.z);
+  slot_word_set(s, 4 * k + 3, v.w);
 }
 
-template <int UNIT, bool NT>
-__device__ __forceinline__ typename ColUnitT<UNIT>::T ld_u(const char* p) {
-  if constexpr (UNIT == 16) return ld16<NT>(p);
-  else if constexpr (NT) return __builtin_nontemporal_load(gptr<uint32_t>(p));
-  else return *gptr<uint32_t>(p);
-}
-
-template <int UNIT, bool NT>
-__device__ __forceinline__ void st_u(char* p, typename ColUnitT<UNIT>::T v) {
-  if constexpr (UNIT == 16) st16<NT>(p, v);
-  else if constexpr (NT) __builtin_nontemporal_store(v, gptr<uint32_t>(p));
-  else *gptr<uint32_t>(p) = v;
-}
-
-template <int DT, int OP, int UNIT>
-__device__ __forceinline__ typename ColUnitT<UNIT>::T combine_u(typename ColUnitT<UNIT>::T d,
-                                                               typename ColUnitT<UNIT>::T s) {
-  if constexpr (UNIT == 16) return combine16<DT, OP>(d, s);
-  else return combine_word<DT, OP>(d, s);
-}
-
-// Element e of a unit.
-template <int DT, int UNIT>
-__device__ __forceinline__ uint32_t elem_u(typename ColUnitT<UNIT>::T v, int e) {
-  if constexpr (UNIT == 16) {
-    return elem_of<DT>(v, e);
-  } else {
-    constexpr int SZ = elem_size<DT>();
-    if constexpr (SZ == 4) return v;
-    else if constexpr (SZ == 2) return (v >> (16 * e)) & 0xffffu;
-    else return (v >> (8 * e)) & 0xffu;
-  }
-}
-
-// The row-checksum words of the unit at column x (a multiple of UNIT), over
-// the bytes of [s0, s1) in it, rotated by the row start's misalignment `shift`.
-template <int DT, int UNIT>
-__device__ __forceinline__ uint64_t unit_words(typename ColUnitT<UNIT>::T v, uint64_t x, uint64_t s0, uint64_t s1,
-                                               bool full, uint32_t shift) {
-  if (full) {
-    if constexpr (UNIT == 16) return words16(v, shift * 8u);
-    else return rotl32(v, shift * 8u);
-  }
-  constexpr int SZ = elem_size<DT>(), E = UNIT / SZ;
-  const uint32_t r0 = s0 > x ? uint32_t(s0 - x) : 0u, r1 = s1 < x + UNIT ? uint32_t(s1 - x) : uint32_t(UNIT);
+// The row-checksum words of the 16-byte unit at column x (a multiple of 16),
+// over the bytes of [s0, s1) in it, rotated by the row start's misalignment
+// `shift`.
+template <int DT>
+__device__ __forceinline__ uint64_t unit_words(u32x4 v, uint64_t x, uint64_t s0, uint64_t s1, bool full,
+                                               uint32_t shift) {
+  if (full) return words16(v, shift * 8u);
+  constexpr int SZ = elem_size<DT>(), E = 16 / SZ;
+  const uint32_t r0 = s0 > x ? uint32_t(s0 - x) : 0u, r1 = s1 < x + 16 ? uint32_t(s1 - x) : 16u;
   uint64_t acc = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t b = uint32_t(e * SZ);
-    if (b >= r0 && b < r1) acc += uint64_t(elem_u<DT, UNIT>(v, e) << (8u * ((b + shift) & 3u)));
+    if (b >= r0 && b < r1) acc += uint64_t(elem_of<DT>(v, e) << (8u * ((b + shift) & 3u)));
   }
   return acc;
 }
 
 // Stores the unit's bytes that lie in [s0, s1), element by element.
-template <int DT, int UNIT>
-__device__ __forceinline__ void store_part(char* p, typename ColUnitT<UNIT>::T v, uint64_t x, uint64_t s0,
-                                           uint64_t s1) {
-  constexpr int SZ = elem_size<DT>(), E = UNIT / SZ;
-  const uint32_t r0 = s0 > x ? uint32_t(s0 - x) : 0u, r1 = s1 < x + UNIT ? uint32_t(s1 - x) : uint32_t(UNIT);
+template <int DT>
+__device__ __forceinline__ void store_part(char* p, u32x4 v, uint64_t x, uint64_t s0, uint64_t s1) {
+  constexpr int SZ = elem_size<DT>(), E = 16 / SZ;
+  const uint32_t r0 = s0 > x ? uint32_t(s0 - x) : 0u, r1 = s1 < x + 16 ? uint32_t(s1 - x) : 16u;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t b = uint32_t(e * SZ);
-    if (b >= r0 && b < r1) st_elem<DT>(p + b, elem_u<DT, UNIT>(v, e));
+    if (b >= r0 && b < r1) st_elem<DT>(p + b, elem_of<DT>(v, e));
   }
 }
 
@@ -198,11 +142,12 @@ struct Accs {
 template <>
 struct Accs<0> {};
 
-// UNIT bytes per lane and column; NL register slots; NA checksum
-// accumulators (0: no checksums); NTM: nontemporal loads (NT_SRC) / stores (NT_DST).
-template <int DT, int OP, int UNIT, int NL, int NA, int NTM>
+// 16 bytes per lane and column; NL register slots; NA checksum accumulators
+// (0: no checksums); NTM: nontemporal loads (NT_SRC) / stores (NT_DST).
+template <int DT, int OP, int NL, int NA, int NTM>
 __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
-  typedef typename ColUnitT<UNIT>::T U;
+  typedef u32x4 U;
+  constexpr uint64_t UNIT = 16;
   constexpr uint64_t TB = uint64_t(COL_THREADS) * UNIT;
   const ColWork wk = cload(a.work + blockIdx.x);
   const uint32_t lane = threadIdx.x;
@@ -229,14 +174,14 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
     const uint64_t x = wk.c0 + uint64_t(t) * TB + uint64_t(lane) * UNIT;
     const bool any = x < s1 && x + UNIT > s0;
     const bool full = x >= s0 && x + UNIT <= s1;
-    Slots<UNIT, NL> v;
+    Slots<NL> v;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       if (uint32_t(j) < nload) {
         const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(ld_w1), j));
         const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
         U u{};
-        if (any) u = ld_u<UNIT, (NTM & NT_SRC) != 0>(base + x);
+        if (any) u = ld16<(NTM & NT_SRC) != 0>(base + x);
         slot_set(v, uint32_t(j), u);
       }
     }
@@ -247,13 +192,13 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
       U val = A;
       if (w0 & CI_COMBINE) {
         const U B = (w0 & CI_B_Y) ? y : slot_get(v, (w0 >> 16) & 0xffu);
-        y = combine_u<DT, OP, UNIT>(A, B);
+        y = combine16<DT, OP>(A, B);
         if (w0 & CI_WRITE) slot_set(v, w0 >> 24, y);
         val = y;
       }
       if constexpr (NA > 0) {
         const uint32_t shift = uint32_t(__builtin_amdgcn_readlane(int(op_w1), int(k))) & 3u;
-        if (any) acc.add(k, unit_words<DT, UNIT>(val, x, s0, s1, full, shift));
+        if (any) acc.add(k, unit_words<DT>(val, x, s0, s1, full, shift));
       }
     }
     for (uint32_t j = 0; j < nstore; ++j) {
@@ -261,8 +206,8 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
       const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(st_w1), int(j)));
       const U val = (w0 & CI_A_Y) ? y : slot_get(v, (w0 >> 8) & 0xffu);
       char* base = reinterpret_cast<char*>(lane_u64(rp_lo, rp_hi, rk));
-      if (full) st_u<UNIT, (NTM & NT_DST) != 0>(base + x, val);
-      else if (any) store_part<DT, UNIT>(base + x, val, x, s0, s1);
+      if (full) st16<(NTM & NT_DST) != 0>(base + x, val);
+      else if (any) store_part<DT>(base + x, val, x, s0, s1);
     }
   }
   if constexpr (NA > 0) {
@@ -318,16 +263,16 @@ __global__ __launch_bounds__(BLOCK_THREADS) void col_fold_rows_kernel(const uint
 
 typedef void (*ColFn)(ColArgs);
 
-template <int DT, int OP, int UNIT, int NL, int NA>
+template <int DT, int OP, int NL, int NA>
 ColFn col_fn_nt(bool nt) {
-  return nt ? col_kernel<DT, OP, UNIT, NL, NA, NT_SRC | NT_DST> : col_kernel<DT, OP, UNIT, NL, NA, 0>;
+  return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST> : col_kernel<DT, OP, NL, NA, 0>;
 }
 
 template <int DT, int OP>
 ColFn col_fn_variant(int unit, int leaves, int accs, bool nt) {
-  if (unit == 4) return col_fn_nt<DT, OP, 4, 64, 0>(nt);
-  if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 16, 8, 16>(nt) : col_fn_nt<DT, OP, 16, 8, 0>(nt);
-  return accs ? col_fn_nt<DT, OP, 16, 16, 32>(nt) : col_fn_nt<DT, OP, 16, 16, 0>(nt);
+  (void)unit;  // every variant takes 16-byte units
+  if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 8, 16>(nt) : col_fn_nt<DT, OP, 8, 0>(nt);
+  return accs ? col_fn_nt<DT, OP, 16, 32>(nt) : col_fn_nt<DT, OP, 16, 0>(nt);
 }
 
 template <int DT>

@@ -25,8 +25,12 @@ struct Event {          // one covering row, in execution order
 
 uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz)) % 4) + 4) % 4); }
 
-// Variants the column kernel is built in (see kernels.hip), smallest first.
-const ColVariant kVariants[] = {{16, 8, 0}, {16, 8, 16}, {16, 16, 0}, {16, 16, 32}, {4, 64, 0}};
+// Variants the column kernel is built in (colkernel.hip), smallest first.  A
+// 64-slot variant of 4-byte units was built and measured: its 64-leaf
+// programs are bound by instruction issue (64-rank ReduceScatter bf16 x 256
+// MiB: Ring 10.6 ms, halving-doubling 11.2 ms, against 3.07 / 6.86 ms in the
+// row kernel), so programs that need more than 16 slots run in the row kernel.
+const ColVariant kVariants[] = {{16, 8, 0}, {16, 8, 16}, {16, 16, 0}, {16, 16, 32}};
 
 }  // namespace
 

@@ -657,7 +657,7 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
   if (s.count > 5000) return;
   const ColPlan p = compile_colplan(s, sh.sz, sh.inplace, cks);
   if (!p.ok) {
-    CHECK(sh.kind == COLL_K_ALLTOALL || sh.N > 64, "%s: no column program (%s)", name(sh).c_str(), p.why.c_str());
+    CHECK(sh.kind == COLL_K_ALLTOALL || sh.N > 16, "%s: no column program (%s)", name(sh).c_str(), p.why.c_str());
     ++col_fallbacks;
     return;
   }
