@@ -27,7 +27,7 @@ OPTIONS = {"exec": 0, "group_tiles": 1, "max_grid": 2, "nontemporal": 3, "revers
 MAX_RANKS = 128
 
 COLLECTIVES = ("coll_allreduce", "coll_reducescatter", "coll_allgather", "coll_broadcast", "coll_scatter",
-               "coll_gather", "coll_alltoall", "coll_reduce")
+               "coll_gather", "coll_alltoall", "coll_reduce", "coll_allreduce_noalloc")
 
 
 class CollRow(ctypes.Structure):

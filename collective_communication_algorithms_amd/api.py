@@ -118,6 +118,12 @@ def coll_reduce(send, recv=None, op="sum", algo="default", root=0, chunks=1, str
     _collective("coll_reduce", send, recv, op, algo, root, chunks, stream)
 
 
+def coll_allreduce_noalloc(send, recv=None, op="sum", algo="default", root=0, chunks=1, stream=None):
+    """coll_allreduce without any device allocation (the library's fixed
+    scratch array; the column kernel only)."""
+    _collective("coll_allreduce_noalloc", send, recv, op, algo, root, chunks, stream)
+
+
 COLLECTIVE_FNS = {"allreduce": coll_allreduce, "reducescatter": coll_reducescatter, "allgather": coll_allgather,
                   "broadcast": coll_broadcast, "scatter": coll_scatter, "gather": coll_gather,
                   "alltoall": coll_alltoall, "reduce": coll_reduce}

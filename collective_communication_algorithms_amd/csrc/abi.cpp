@@ -693,6 +693,32 @@ coll_status_t check_buffers(void* const* send, void* const* recv, int N, int64_t
   return COLL_OK;
 }
 
+// Every check of a collective call's arguments that needs no HIP call: sizes,
+// pointers, aliasing, the algorithm and scalars (no rows built), also when
+// there is nothing to move.
+coll_status_t check_call(coll_kind_t kind, void* const* send, void* const* recv, int N, size_t count_in,
+                         coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks, int& sz,
+                         int64_t& count, bool& inplace) {
+  sz = elem_size(dtype);
+  if (!sz) return fail(COLL_ERR_INVALID_ARG, "unknown dtype");
+  if (int(op) < 0 || int(op) > 2) return fail(COLL_ERR_INVALID_ARG, "unknown op");
+  if (N < 1) return fail(COLL_ERR_INVALID_ARG, "nranks must be at least 1");
+  if (N > COLL_MAX_RANKS) return fail(COLL_ERR_UNSUPPORTED, "nranks above COLL_MAX_RANKS");
+  if (count_in > (size_t(1) << 44) / size_t(sz)) return fail(COLL_ERR_INVALID_ARG, "count too large");
+  count = int64_t(count_in);
+  inplace = true;
+  coll_status_t st = check_buffers(send, recv, N, count, sz, kind == COLL_K_ALLTOALL, inplace);
+  if (st != COLL_OK) return st;
+  const bool automatic = algo == COLL_ALGO_AUTO;
+  std::string err;
+  st = validate_schedule_args(kind, automatic ? COLL_ALGO_DEFAULT : algo, N, count, root, automatic ? 1 : chunks, err);
+  if (st != COLL_OK) return fail(st, err);
+  // the permutation kernel addresses a block with 32-bit unit offsets
+  if (kind == COLL_K_ALLTOALL && uint64_t(count / N) * uint64_t(sz) >= (uint64_t(1) << 31))
+    return fail(COLL_ERR_UNSUPPORTED, "AllToAll blocks of 2 GiB or more");
+  return COLL_OK;
+}
+
 // One kernel launch of a call, planned before anything is enqueued.
 struct Launch {
   enum Kind { COL, ROWS, PERM } kind = ROWS;
@@ -717,28 +743,13 @@ struct Launch {
 
 coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N, size_t count_in, coll_dtype_t dtype,
                   coll_op_t op, coll_algo_t algo, int root, int chunks, void* stream_v) {
-  const int sz = elem_size(dtype);
-  if (!sz) return fail(COLL_ERR_INVALID_ARG, "unknown dtype");
-  if (int(op) < 0 || int(op) > 2) return fail(COLL_ERR_INVALID_ARG, "unknown op");
-  if (N < 1) return fail(COLL_ERR_INVALID_ARG, "nranks must be at least 1");
-  if (N > COLL_MAX_RANKS) return fail(COLL_ERR_UNSUPPORTED, "nranks above COLL_MAX_RANKS");
-  if (count_in > (size_t(1) << 44) / size_t(sz)) return fail(COLL_ERR_INVALID_ARG, "count too large");
-  const int64_t count = int64_t(count_in);
+  int sz = 0;
+  int64_t count = 0;
   bool inplace = true;
-  coll_status_t st = check_buffers(send, recv, N, count, sz, kind == COLL_K_ALLTOALL, inplace);
+  coll_status_t st = check_call(kind, send, recv, N, count_in, dtype, op, algo, root, chunks, sz, count, inplace);
   if (st != COLL_OK) return st;
   const bool automatic = algo == COLL_ALGO_AUTO;
   if (automatic) chunks = 1;
-  // validate the algorithm and the scalars (no rows built), also when there
-  // is nothing to move, and before any HIP call
-  {
-    std::string err;
-    st = validate_schedule_args(kind, automatic ? COLL_ALGO_DEFAULT : algo, N, count, root, chunks, err);
-    if (st != COLL_OK) return fail(st, err);
-  }
-  // the permutation kernel addresses a block with 32-bit unit offsets
-  if (kind == COLL_K_ALLTOALL && uint64_t(count / N) * uint64_t(sz) >= (uint64_t(1) << 31))
-    return fail(COLL_ERR_UNSUPPORTED, "AllToAll blocks of 2 GiB or more");
   t_last = coll_counts_t{};
   if (count == 0) return COLL_OK;
 
@@ -1000,6 +1011,157 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   return COLL_OK;
 }
 
+
+// ---- the allocation-free AllReduce -------------------------------------------------
+
+// What a device's allocation-free scratch holds: the tables of the last call
+// that uploaded, and where they lie in it (byte offsets).  The host copies
+// stay alive as long as they are the scratch's contents.
+struct NoallocState {
+  bool valid = false;
+  std::vector<int64_t> key;       // schedule key, checksum mode, tiles
+  ColPlan plan;
+  ColTables tables;
+  coll_counts_t counts{};         // the schedule's
+  size_t nrows = 0;
+  uint32_t tiles = 0;
+  uint64_t off_code = 0, off_work = 0, off_row_off = 0, off_refs = 0, off_part = 0, off_tmp = 0, end = 0;
+};
+std::unordered_map<int, NoallocState> g_noalloc;
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// The layout of a plan's tables in the scratch with `tiles` per work group.
+void noalloc_layout(NoallocState& n, size_t nrows, bool cks) {
+  uint64_t o = 0;
+  n.off_code = o;
+  o = align256(o + n.plan.code.size() * sizeof(ColInstr));
+  n.off_work = o;
+  o = align256(o + n.tables.work.size() * sizeof(ColWork));
+  n.off_row_off = o;
+  o = align256(o + (cks ? n.tables.row_off.size() * sizeof(uint32_t) : 0));
+  n.off_refs = o;
+  o = align256(o + (cks ? n.tables.refs.size() * sizeof(ColRef) : 0));
+  n.off_part = o;
+  o = align256(o + (cks ? n.tables.partials * sizeof(uint64_t) : 0));
+  n.off_tmp = o;
+  o = align256(o + (cks ? std::max<size_t>(nrows, 1) * COL_FOLD_SLICES * sizeof(uint64_t) : 0));
+  n.end = o;
+}
+
+coll_status_t run_noalloc(void* const* send, void* const* recv, int N, size_t count_in, coll_dtype_t dtype,
+                          coll_op_t op, coll_algo_t algo, int root, int chunks, void* stream_v) {
+  const coll_kind_t kind = COLL_K_ALLREDUCE;
+  int sz = 0;
+  int64_t count = 0;
+  bool inplace = true;
+  coll_status_t st = check_call(kind, send, recv, N, count_in, dtype, op, algo, root, chunks, sz, count, inplace);
+  if (st != COLL_OK) return st;
+  t_last = coll_counts_t{};
+  if (count == 0) return COLL_OK;
+  uint64_t align_or = 0;
+  RankPtrs ptrs;
+  for (int i = 0; i < N; ++i) {
+    ptrs.send[i] = reinterpret_cast<uint64_t>(send[i]);
+    ptrs.recv[i] = reinterpret_cast<uint64_t>(inplace ? send[i] : recv[i]);
+    align_or |= ptrs.send[i] | ptrs.recv[i];
+  }
+  for (int i = N; i < COLL_MAX_RANKS; ++i) ptrs.send[i] = ptrs.recv[i] = 0;
+  if (align_or % 16) return fail(COLL_ERR_UNSUPPORTED, "the allocation-free AllReduce needs 16-byte aligned rank buffers");
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevInfo* di = nullptr;
+  st = device_info(dev, di);
+  if (st != COLL_OK) return st;
+  coll_algo_t chosen = algo;
+  if (algo == COLL_ALGO_AUTO) {
+    st = auto_algo(kind, N, count, sz, root, uint32_t(di->cus), chosen);
+    if (st != COLL_OK) return st;
+  }
+  const coll_algo_t ra = resolve_algo(kind, chosen);
+  const bool cks = t_sums != nullptr;
+  void* base = nullptr;
+  he = noalloc_scratch(&base);
+  if (he != hipSuccess) return hip_fail(he, "hipGetSymbolAddress");
+  NoallocState& cur = g_noalloc[dev];
+  const std::vector<int64_t> key{int64_t(ra), N, count, sz, inplace ? 1 : 0, cks ? 1 : 0, opt_col_tiles.load()};
+  if (!cur.valid || cur.key != key) {
+    NoallocState n;
+    n.key = key;
+    Schedule s;
+    std::string err;
+    st = build_schedule(kind, ra, N, count, 0, 1, s, err);
+    if (st != COLL_OK) return fail(st, err);
+    n.plan = compile_colplan(s, sz, inplace, cks);
+    if (!n.plan.ok)
+      return fail(COLL_ERR_UNSUPPORTED, "the allocation-free AllReduce runs the column kernel only: " + n.plan.why);
+    // tiles per work group: the automatic choice, more while the tables and
+    // partial sums exceed the scratch
+    uint32_t tiles = opt_col_tiles.load() > 0 ? uint32_t(opt_col_tiles.load()) : auto_col_tiles(n.plan, uint32_t(di->cus));
+    for (;;) {
+      n.tables = col_tables(n.plan, tiles, s.rows.size());
+      noalloc_layout(n, s.rows.size(), cks);
+      if (n.end <= COLL_NOALLOC_SCRATCH_BYTES || tiles >= 65535) break;
+      tiles = std::min<uint32_t>(65535, tiles * 2);
+    }
+    if (n.end > COLL_NOALLOC_SCRATCH_BYTES)
+      return fail(COLL_ERR_INVALID_ARG, "the allocation-free AllReduce needs " + std::to_string(n.end) +
+                                            " bytes of scratch, more than COLL_NOALLOC_SCRATCH_BYTES");
+    n.tiles = tiles;
+    n.counts = count_schedule(s, sz);
+    n.nrows = s.rows.size();
+    n.valid = true;
+    if (cks && n.nrows > t_sums_cap) return fail(COLL_ERR_INVALID_ARG, "checksum buffer smaller than the schedule");
+    // the scratch's old tables may still be read by work queued on this
+    // stream: wait for it before replacing them (and their host copies)
+    if (cur.valid) {
+      he = hipStreamSynchronize(stream);
+      if (he != hipSuccess) return hip_fail(he, "hipStreamSynchronize");
+    }
+    cur = NoallocState{};
+    char* b = static_cast<char*>(base);
+    auto put = [&](uint64_t off, const void* src, size_t bytes) {
+      return bytes ? hipMemcpyAsync(b + off, src, bytes, hipMemcpyHostToDevice, stream) : hipSuccess;
+    };
+    he = put(n.off_code, n.plan.code.data(), n.plan.code.size() * sizeof(ColInstr));
+    if (he == hipSuccess) he = put(n.off_work, n.tables.work.data(), n.tables.work.size() * sizeof(ColWork));
+    if (he == hipSuccess && cks) he = put(n.off_row_off, n.tables.row_off.data(), n.tables.row_off.size() * sizeof(uint32_t));
+    if (he == hipSuccess && cks) he = put(n.off_refs, n.tables.refs.data(), n.tables.refs.size() * sizeof(ColRef));
+    if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync");
+    cur = std::move(n);
+  }
+  if (cks && cur.nrows > t_sums_cap) return fail(COLL_ERR_INVALID_ARG, "checksum buffer smaller than the schedule");
+  char* b = static_cast<char*>(base);
+  ColArgs a{};
+  a.work = reinterpret_cast<const ColWork*>(b + cur.off_work);
+  a.code = reinterpret_cast<const ColInstr*>(b + cur.off_code);
+  a.partial = cks ? reinterpret_cast<uint64_t*>(b + cur.off_part) : nullptr;
+  a.p = ptrs;
+  const uint64_t footprint = uint64_t(N) * uint64_t(count) * uint64_t(sz) * (inplace ? 1u : 2u);
+  const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint, false) : uint32_t(opt_nt.load());
+  const bool nt = opt_nt.load() < 0 ? ntmask != 0 : (ntmask & (NT_SRC | NT_DST)) != 0;
+  const int dt = int(dtype) == COLL_INT32 ? DT_I32 : int(dtype) == COLL_UINT8 ? DT_U8
+               : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
+  const uint32_t grid = uint32_t(cur.tables.work.size());
+  if (grid) {
+    he = launch_col(a, dt, int(op), cur.plan.v.unit, cur.plan.v.leaves, cur.plan.v.accs, nt, grid, stream);
+    if (he != hipSuccess) return hip_fail(he, "column kernel launch");
+  }
+  if (cks) {
+    he = launch_col_fold(reinterpret_cast<const ColRef*>(b + cur.off_refs),
+                         reinterpret_cast<const uint32_t*>(b + cur.off_row_off),
+                         reinterpret_cast<const uint64_t*>(b + cur.off_part), reinterpret_cast<uint64_t*>(b + cur.off_tmp),
+                         t_sums, uint64_t(cur.nrows), stream);
+    if (he != hipSuccess) return hip_fail(he, "checksum fold");
+  }
+  t_last = cur.counts;
+  t_last.moved_bytes = int64_t(cur.plan.moved_bytes);
+  t_last.round_trips = 1;
+  return COLL_OK;
+}
 }  // namespace
 }  // namespace coll
 
@@ -1027,6 +1189,18 @@ COLL_ENTRY(coll_scatter, COLL_K_SCATTER)
 COLL_ENTRY(coll_gather, COLL_K_GATHER)
 COLL_ENTRY(coll_alltoall, COLL_K_ALLTOALL)
 COLL_ENTRY(coll_reduce, COLL_K_REDUCE)
+
+coll_status_t coll_allreduce_noalloc(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                                     coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                                     void* stream) {
+  try {
+    return run_noalloc(sendbufs, recvbufs, nranks, count, dtype, op, algo, root, chunks, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(COLL_ERR_NO_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(COLL_ERR_INVALID_ARG, "unexpected host exception");
+  }
+}
 
 coll_status_t coll_plan(coll_kind_t kind, coll_algo_t algo, int nranks, size_t count, coll_dtype_t dtype, int root,
                         int chunks, coll_row_t* rows, size_t* nrows, coll_counts_t* counts) {

@@ -29,6 +29,9 @@
 // work group per KiB of columns cost more than the whole copy).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "device_common.h"
 #include "device_types.h"
 #include "launch.h"
@@ -293,7 +296,34 @@ ColFn pick_col(int dtype, int op, int unit, int leaves, int accs, bool nt) {
   }
 }
 
+// Device memory of coll_allreduce_noalloc: its programs, work table, row
+// references, partial checksum sums and fold slices, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy until the process
+// ends.  In host code the name stands for no device address: host code uses
+// the per-device address from noalloc_scratch() only.
+static __device__ __align__(256) uint8_t scratch[COLL_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;  // device -> address of that device's scratch
+
 }  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
 
 hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool nt, uint32_t grid,
                       hipStream_t stream) {

@@ -26,6 +26,9 @@ hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves,
 // of tmp (nrows * COL_FOLD_SLICES slots)
 hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,
                            uint64_t* out, uint64_t nrows, hipStream_t stream);
+// The address of the current device's allocation-free scratch
+// (COLL_NOALLOC_SCRATCH_BYTES, 256-byte aligned), taken once per device.
+hipError_t noalloc_scratch(void** out);
 int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt);
 int perm_blocks_per_cu(int unit, int slots, bool cks, bool nt);
 

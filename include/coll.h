@@ -173,6 +173,28 @@ coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nr
                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                             void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): an
+ * AllReduce with the same arguments, results and row checksums as
+ * coll_allreduce, that calls no hipMalloc, hipFree or other allocating
+ * routine.  It runs the column kernel only, with its programs, work table and
+ * checksum partial sums in a library array of COLL_NOALLOC_SCRATCH_BYTES per
+ * GPU (held until the process ends); the schedule is compiled on the host.
+ * The array keeps the last call's tables: a call for the same schedule,
+ * options and checksum mode uploads nothing, any other uploads its tables
+ * (hipMemcpyAsync on `stream`) and first waits for `stream`.  Calls that
+ * overlap on one GPU (other streams or threads) race on the array.
+ * Errors: as coll_allreduce; COLL_ERR_UNSUPPORTED when the column kernel does
+ * not run the call (rank buffers not 16-byte aligned, or a schedule whose
+ * programs need more than 16 register slots, e.g. Ring or halving-doubling
+ * over more than 16 ranks); COLL_ERR_INVALID_ARG when its tables and partial
+ * sums do not fit the array even with the fewest work groups (the message
+ * says how many bytes they need).  Not in coll_get_stats' schedule cache. */
+#define COLL_NOALLOC_SCRATCH_BYTES (16u << 20)
+coll_status_t coll_allreduce_noalloc(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
+                                     coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
+                                     void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Schedules and statistics (host only; no GPU needed). */
 
