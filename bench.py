@@ -424,10 +424,10 @@ def overlap(out_path: str, dev) -> None:
                          "coll_max_grid": max_grid, "ratio": ratio, "spin_iters": iters,
                          "t_compute_ms": round(t_comp, 4), "t_comm_ms": round(t_comm, 4),
                          "t_both_ms": round(t_both, 4),
-                         "model_overlap_ms": round(model.estimate_iteration_time(t_comp, t_comm, True), 4),
-                         "model_no_overlap_ms": round(model.estimate_iteration_time(t_comp, t_comm, False), 4),
+                         "model_overlap_ms": round(model.overlapped_time(t_comp, t_comm), 4),
+                         "model_no_overlap_ms": round(model.serial_time(t_comp, t_comm), 4),
                          "hidden_fraction": round(model.hidden_fraction(t_comp, t_comm, t_both), 3),
-                         "both_over_model": round(t_both / model.estimate_iteration_time(t_comp, t_comm, True), 3)}
+                         "both_over_model": round(t_both / model.overlapped_time(t_comp, t_comm), 3)}
                     with open(out_path, "a") as fh:
                         fh.write(json.dumps(r) + "\n")
                     print(json.dumps(r), file=sys.stderr, flush=True)

@@ -109,14 +109,16 @@ def best_chunks(algo: str, N: int, M: float, alpha: float, beta: float, kmax: in
     return min(range(1, kmax + 1), key=lambda k: (time("broadcast", algo, N, M, alpha, beta, k), k))
 
 
-def estimate_iteration_time(compute: float, comm: float, overlap: bool = True) -> float:
-    """One iteration of compute plus a collective (the HCCL blog, Overlap的性能收益).
+def overlapped_time(compute: float, comm: float) -> float:
+    """Wall time of compute and a collective that run concurrently on two
+    streams: the longer of the two (the HCCL blog, 延迟掩盖：计算与通信的Overlap,
+    Overlap的性能收益: with overlap only the part of the collective that
+    outlasts the compute remains visible).  Times in any one unit."""
+    return max(compute, comm)
 
-    Without overlap the two add.  With the collective on its own stream, only
-    the part of it that outlasts the compute shows: compute + max(0, comm -
-    compute).  Times in any one unit."""
-    if overlap:
-        return compute + max(0.0, comm - compute)
+
+def serial_time(compute: float, comm: float) -> float:
+    """Wall time of compute followed by the collective on one stream."""
     return compute + comm
 
 

@@ -115,19 +115,27 @@ typedef enum {
 /* The eight collectives.  Same parameters for all; see the conventions above. */
 
 /* [P3] AllReduce: every rank ends with the elementwise reduction over ranks.
- * Input all of buf_i; output all of buf_i.  algo: RING (default), RHD, DBT. */
+ * Input all of buf_i; output all of buf_i.  algo: RING (default; [P3] Ring
+ * AllReduce：带宽最优, eq:model-algo-ring-ar: ReduceScatter then AllGather,
+ * 2(N-1) steps), RHD ([P3] Recursive Halving-Doubling, eq:model-algo-rhd-ar:
+ * 2 log2 N steps), DBT ([P3] Double Binary Tree, eq:model-algo-dbt-ar). */
 coll_status_t coll_allreduce(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                              coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                              void* stream);
 
 /* [P3] ReduceScatter: rank i ends with chunk i of the reduction; its other
- * chunks are left unspecified.  algo: RING (default), RHD. */
+ * chunks are left unspecified.  algo: RING (default; [P3] Ring
+ * ReduceScatter, eq:model-algo-ring-reducescatter: N-1 steps of M/N), RHD
+ * ([P3] Recursive Halving-Doubling, eq:model-algo-rhd-rs: log2 N halving
+ * rounds; N = 2^n). */
 coll_status_t coll_reducescatter(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                                  coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                                  void* stream);
 
 /* [P3] AllGather: rank i contributes chunk i of its buffer; every rank ends
- * with all N chunks.  algo: RING (default), RHD. */
+ * with all N chunks.  algo: RING (default; [P3] Ring AllGather,
+ * eq:model-algo-ring-allgather: N-1 steps of M/N), RHD ([P3] Recursive
+ * Halving-Doubling, eq:model-algo-rhd-ag: log2 N doubling rounds; N = 2^n). */
 coll_status_t coll_allgather(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                              coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                              void* stream);
@@ -163,12 +171,15 @@ coll_status_t coll_reduce(void* const* sendbufs, void* const* recvbufs, int nran
                           coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                           void* stream);
 
-/* [P3] AllToAll: send_i holds N blocks of count/N elements, block j meant for
- * rank j; afterwards block i of recv_j = block j of send_i.  Out of place only;
- * count must be a multiple of N.  algo: PAIRWISE (default), BRUCK, RING
- * (eq:model-algo-a2a-ring: N-1 rounds between neighbours i -> i+1; round t
- * forwards the N-t blocks still in transit, so each link carries (N-1)M/2
- * bytes in all, against the printed formula's (N-1)M/N). */
+/* [P3] AllToAll (AllToAll 算法怎么选): send_i holds N blocks of count/N
+ * elements, block j meant for rank j; afterwards block i of recv_j = block j
+ * of send_i.  Out of place only; count must be a multiple of N.  algo:
+ * PAIRWISE (default; eq:model-algo-a2a-pairwise: in round k rank i sends to
+ * i+k, N-1 rounds), BRUCK (eq:model-algo-a2a-bruck: ceil(log2 N) rounds with
+ * local rotations), RING (eq:model-algo-a2a-ring: N-1 rounds between
+ * neighbours i -> i+1; round t forwards the N-t blocks still in transit, so
+ * each link carries (N-1)M/2 bytes in all, against the printed formula's
+ * (N-1)M/N). */
 coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                             void* stream);

@@ -99,8 +99,8 @@ def test_overlap_estimate_matches_printed_examples():
     inside the page), the printed function's outputs are the pin."""
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "overlap_examples.json")))
     for ex in g["examples"]:
-        assert model.estimate_iteration_time(ex["compute_ms"], ex["comm_ms"], False) == ex["no_overlap_ms"]
-        assert model.estimate_iteration_time(ex["compute_ms"], ex["comm_ms"], True) == ex["overlap_ms"]
+        assert model.serial_time(ex["compute_ms"], ex["comm_ms"]) == ex["no_overlap_ms"]
+        assert model.overlapped_time(ex["compute_ms"], ex["comm_ms"]) == ex["overlap_ms"]
 
 
 def test_hidden_fraction_limits():
