@@ -953,7 +953,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.code = L.code;
       a.partial = partial;
       a.p = ptrs;
-      he = launch_col(a, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.nt, L.grid, stream);
+      he = launch_col(a, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.v.batched, L.nt, L.grid, stream);
       if (he != hipSuccess) return hip_fail(he, "column kernel launch");
     } else if (L.kind == Launch::ROWS) {
       RowsArgs a{};
@@ -1147,7 +1147,8 @@ coll_status_t run_noalloc(void* const* send, void* const* recv, int N, size_t co
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
   const uint32_t grid = uint32_t(cur.tables.work.size());
   if (grid) {
-    he = launch_col(a, dt, int(op), cur.plan.v.unit, cur.plan.v.leaves, cur.plan.v.accs, nt, grid, stream);
+    he = launch_col(a, dt, int(op), cur.plan.v.unit, cur.plan.v.leaves, cur.plan.v.accs, cur.plan.v.batched, nt,
+                     grid, stream);
     if (he != hipSuccess) return hip_fail(he, "column kernel launch");
   }
   if (cks) {

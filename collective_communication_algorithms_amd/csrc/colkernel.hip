@@ -10,7 +10,10 @@
 // A work group is one wave; lane l takes bytes [16l, 16l + 16) of every
 // 1 KiB tile of its segment.  Per tile it
 //   * loads the program's leaves (each rank input the program needs, once)
-//     into register slots, all loads in flight together;
+//     into register slots, all loads in flight together (programs with more
+//     leaves than slots bring them in batches: an op flagged RELOAD first
+//     refills slots 0 .. m-1 (m <= 8) with the next leaves, once the batch
+//     before is consumed);
 //   * runs the ops in the rows' order: a recv_and_reduce row combines its old
 //     destination value with its source value (A (+) B, the same element
 //     arithmetic as the row kernel, so float results keep the schedule's
@@ -145,13 +148,21 @@ struct Accs {
 template <>
 struct Accs<0> {};
 
-// 16 bytes per lane and column; NL register slots; NA checksum accumulators
-// (0: no checksums); NTM: nontemporal loads (NT_SRC) / stores (NT_DST).
-template <int DT, int OP, int NL, int NA, int NTM>
+// 16 bytes per lane and column; NL slots; NA checksum accumulators (0: no
+// checksums); NTM: nontemporal loads (NT_SRC) / stores (NT_DST); BT: programs
+// may bring leaves in batches (the RELOAD path costs registers, so the other
+// variants leave it out).  Batched programs keep leaves in slots 0 .. 7 and
+// only partial results above, which are written once and read once per
+// subtree: with BT those slots live in LDS (1 KiB each per work group), so
+// the wave keeps the registers of the 8-slot variant and its occupancy.
+template <int DT, int OP, int NL, int NA, int NTM, bool BT>
 __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
   typedef u32x4 U;
   constexpr uint64_t UNIT = 16;
   constexpr uint64_t TB = uint64_t(COL_THREADS) * UNIT;
+  constexpr int NR = (BT && NL > int(COL_BATCH)) ? int(COL_BATCH) : NL;  // slots in registers
+  constexpr int NS = NL - NR;                                            // slots in LDS
+  __shared__ U lds_slot[NS > 0 ? NS : 1][COL_THREADS];
   const ColWork wk = cload(a.work + blockIdx.x);
   const uint32_t lane = threadIdx.x;
   // lane r holds rank r's buffer addresses, lane k entry k of each list
@@ -169,34 +180,85 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
     st_w0 = uint32_t(v);
     st_w1 = uint32_t(v >> 32);
   }
-  const uint32_t nload = wk.nload, nop = wk.nop, nstore = wk.nstore;
-  const uint64_t s0 = wk.s0, s1 = wk.s1;
+  // The tile loop reads the lists and addresses above with v_readlane.  Wait
+  // for them once here: the compiler cannot tell, in blocks a uniform branch
+  // may skip, that they have arrived, and would otherwise wait for every
+  // outstanding load (vmcnt(0)) before each leaf load.
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint32_t nfirst = wk.nfirst, nop = wk.nop, nstore = wk.nstore;
+  const uint64_t s0 = wk.s0, s1 = wk.s1, xs = s0 & ~(UNIT - 1);
   Accs<NA> acc;
   if constexpr (NA > 0) acc.clear();
   for (uint32_t t = 0; t < wk.ntiles; ++t) {
     const uint64_t x = wk.c0 + uint64_t(t) * TB + uint64_t(lane) * UNIT;
     const bool any = x < s1 && x + UNIT > s0;
     const bool full = x >= s0 && x + UNIT <= s1;
-    Slots<NL> v;
+    // a lane outside the segment loads the segment's first unit instead: the
+    // loads need no branch (a branch around each makes the compiler wait for
+    // every load before issuing the next), and what that lane computes is
+    // neither stored nor summed
+    const uint64_t xl = any ? x : xs;
+    Slots<NR> v;
+    auto sget = [&](uint32_t i) -> U {
+      if constexpr (NS > 0) {
+        if (i >= uint32_t(NR)) return lds_slot[i - NR][lane];
+      }
+      return slot_get(v, i);
+    };
+    auto sset = [&](uint32_t i, U u) {
+      // a batched program writes partial results only, to slots NR and up
+      // (leaves arrive by loads): the register slots are never written here
+      if constexpr (NS > 0) lds_slot[i - NR][lane] = u;
+      else slot_set(v, i, u);
+    };
+    if constexpr (BT) {
+      // a batched program's first batch (1 .. 8 leaves): slots past it load
+      // its last leaf again (a cache hit, never read), so that no slot
+      // depends on a branch
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      if (uint32_t(j) < nload) {
-        const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(ld_w1), j));
+      for (int j = 0; j < NR; ++j) {
+        const uint32_t jj = uint32_t(j) < nfirst ? uint32_t(j) : nfirst - 1u;
+        const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(ld_w1), int(jj)));
         const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
-        U u{};
-        if (any) u = ld16<(NTM & NT_SRC) != 0>(base + x);
-        slot_set(v, uint32_t(j), u);
+        slot_set(v, uint32_t(j), ld16<(NTM & NT_SRC) != 0>(base + xl));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        if (uint32_t(j) < nfirst) {
+          const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(ld_w1), j));
+          const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
+          slot_set(v, uint32_t(j), ld16<(NTM & NT_SRC) != 0>(base + xl));
+        }
       }
     }
     U y{};
+    uint32_t next = nfirst;  // leaves loaded so far
     for (uint32_t k = 0; k < nop; ++k) {
       const uint32_t w0 = uint32_t(__builtin_amdgcn_readlane(int(op_w0), int(k)));
-      const U A = (w0 & CI_A_Y) ? y : slot_get(v, (w0 >> 8) & 0xffu);
+      if (BT && (w0 & CI_RELOAD)) {
+        // before this op: the next m leaves into slots 0 .. m-1, all loads in
+        // flight together.  The batch before is consumed; saying so (an
+        // explicit wait, free here) keeps the compiler from waiting between
+        // these loads for loads it cannot tell have arrived.
+        __builtin_amdgcn_s_waitcnt(0);
+        const uint32_t m = (uint32_t(__builtin_amdgcn_readlane(int(op_w1), int(k))) >> 8) & 0xffu;
+        // (slots past m load leaf m-1 again, as for the first batch)
+#pragma unroll
+        for (uint32_t j = 0; j < COL_BATCH; ++j) {
+          const uint32_t jj = next + (j < m ? j : m - 1u);
+          const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(ld_w1), int(jj)));
+          const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
+          slot_set(v, j, ld16<(NTM & NT_SRC) != 0>(base + xl));
+        }
+        next += m;
+      }
+      const U A = (w0 & CI_A_Y) ? y : sget((w0 >> 8) & 0xffu);
       U val = A;
       if (w0 & CI_COMBINE) {
-        const U B = (w0 & CI_B_Y) ? y : slot_get(v, (w0 >> 16) & 0xffu);
+        const U B = (w0 & CI_B_Y) ? y : sget((w0 >> 16) & 0xffu);
         y = combine16<DT, OP>(A, B);
-        if (w0 & CI_WRITE) slot_set(v, w0 >> 24, y);
+        if (w0 & CI_WRITE) sset(w0 >> 24, y);
         val = y;
       }
       if constexpr (NA > 0) {
@@ -204,10 +266,17 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
         if (any) acc.add(k, unit_words<DT>(val, x, s0, s1, full, shift));
       }
     }
+    // Batched programs: every load of this tile has been consumed (each leaf
+    // an op or a store reads); an explicit wait tells the compiler so, which
+    // it cannot see across the dynamic op loop, and would otherwise wait for
+    // every outstanding load before each leaf load of the next tile's first
+    // batch.  (The other variants issue their first loads in branches of
+    // their own and measure faster without it.)
+    if constexpr (BT) __builtin_amdgcn_s_waitcnt(0);
     for (uint32_t j = 0; j < nstore; ++j) {
       const uint32_t w0 = uint32_t(__builtin_amdgcn_readlane(int(st_w0), int(j)));
       const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(st_w1), int(j)));
-      const U val = (w0 & CI_A_Y) ? y : slot_get(v, (w0 >> 8) & 0xffu);
+      const U val = (w0 & CI_A_Y) ? y : sget((w0 >> 8) & 0xffu);
       char* base = reinterpret_cast<char*>(lane_u64(rp_lo, rp_hi, rk));
       if (full) st16<(NTM & NT_DST) != 0>(base + x, val);
       else if (any) store_part<DT>(base + x, val, x, s0, s1);
@@ -266,33 +335,39 @@ __global__ __launch_bounds__(BLOCK_THREADS) void col_fold_rows_kernel(const uint
 
 typedef void (*ColFn)(ColArgs);
 
-template <int DT, int OP, int NL, int NA>
+template <int DT, int OP, int NL, int NA, bool BT>
 ColFn col_fn_nt(bool nt) {
-  return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST> : col_kernel<DT, OP, NL, NA, 0>;
+  return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT> : col_kernel<DT, OP, NL, NA, 0, BT>;
 }
 
-template <int DT, int OP>
-ColFn col_fn_variant(int unit, int leaves, int accs, bool nt) {
-  (void)unit;  // every variant takes 16-byte units
-  if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 8, 16>(nt) : col_fn_nt<DT, OP, 8, 0>(nt);
-  return accs ? col_fn_nt<DT, OP, 16, 32>(nt) : col_fn_nt<DT, OP, 16, 0>(nt);
+template <int DT, int OP, bool BT>
+ColFn col_fn_variant(int leaves, int accs, bool nt) {
+  if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 8, 16, BT>(nt) : col_fn_nt<DT, OP, 8, 0, BT>(nt);
+  return accs ? col_fn_nt<DT, OP, 16, 32, BT>(nt) : col_fn_nt<DT, OP, 16, 0, BT>(nt);
 }
 
 template <int DT>
-ColFn col_fn_op(int op, int unit, int leaves, int accs, bool nt) {
+ColFn col_fn_op(int op, int leaves, int accs, bool batched, bool nt) {
+  if (batched) {
+    switch (op) {
+      case OP_SUM: return col_fn_variant<DT, OP_SUM, true>(leaves, accs, nt);
+      case OP_MAX: return col_fn_variant<DT, OP_MAX, true>(leaves, accs, nt);
+      default: return col_fn_variant<DT, OP_MIN, true>(leaves, accs, nt);
+    }
+  }
   switch (op) {
-    case OP_SUM: return col_fn_variant<DT, OP_SUM>(unit, leaves, accs, nt);
-    case OP_MAX: return col_fn_variant<DT, OP_MAX>(unit, leaves, accs, nt);
-    default: return col_fn_variant<DT, OP_MIN>(unit, leaves, accs, nt);
+    case OP_SUM: return col_fn_variant<DT, OP_SUM, false>(leaves, accs, nt);
+    case OP_MAX: return col_fn_variant<DT, OP_MAX, false>(leaves, accs, nt);
+    default: return col_fn_variant<DT, OP_MIN, false>(leaves, accs, nt);
   }
 }
 
-ColFn pick_col(int dtype, int op, int unit, int leaves, int accs, bool nt) {
+ColFn pick_col(int dtype, int op, int leaves, int accs, bool batched, bool nt) {
   switch (dtype) {
-    case DT_I32: return col_fn_op<DT_I32>(op, unit, leaves, accs, nt);
-    case DT_U8: return col_fn_op<DT_U8>(op, unit, leaves, accs, nt);
-    case DT_F32: return col_fn_op<DT_F32>(op, unit, leaves, accs, nt);
-    default: return col_fn_op<DT_BF16>(op, unit, leaves, accs, nt);
+    case DT_I32: return col_fn_op<DT_I32>(op, leaves, accs, batched, nt);
+    case DT_U8: return col_fn_op<DT_U8>(op, leaves, accs, batched, nt);
+    case DT_F32: return col_fn_op<DT_F32>(op, leaves, accs, batched, nt);
+    default: return col_fn_op<DT_BF16>(op, leaves, accs, batched, nt);
   }
 }
 
@@ -325,9 +400,10 @@ hipError_t noalloc_scratch(void** out) {
   return hipSuccess;
 }
 
-hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool nt, uint32_t grid,
-                      hipStream_t stream) {
-  hipLaunchKernelGGL(pick_col(dtype, op, unit, leaves, accs, nt), dim3(grid), dim3(COL_THREADS), 0, stream, a);
+hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool batched, bool nt,
+                      uint32_t grid, hipStream_t stream) {
+  (void)unit;  // every variant takes 16-byte units
+  hipLaunchKernelGGL(pick_col(dtype, op, leaves, accs, batched, nt), dim3(grid), dim3(COL_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

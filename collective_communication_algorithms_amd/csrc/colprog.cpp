@@ -25,12 +25,339 @@ struct Event {          // one covering row, in execution order
 
 uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz)) % 4) + 4) % 4); }
 
-// Variants the column kernel is built in (colkernel.hip), smallest first.  A
-// 64-slot variant of 4-byte units was built and measured: its 64-leaf
-// programs are bound by instruction issue (64-rank ReduceScatter bf16 x 256
-// MiB: Ring 10.6 ms, halving-doubling 11.2 ms, against 3.07 / 6.86 ms in the
-// row kernel), so programs that need more than 16 slots run in the row kernel.
-const ColVariant kVariants[] = {{16, 8, 0}, {16, 8, 16}, {16, 16, 0}, {16, 16, 32}};
+// Variants the column kernel is built in (colkernel.hip), smallest first.
+// Programs with more leaves than 16 slots bring them in batches (batched
+// variants) rather than holding all of them: a 64-slot variant of 4-byte
+// units was built and measured, and its 64-leaf programs were bound by
+// instruction issue (64-rank ReduceScatter bf16 x 256 MiB: Ring 10.6 ms,
+// halving-doubling 11.2 ms, where batches of 8 run them in 2.9 ms).
+const ColVariant kVariants[] = {{16, 8, 0, false}, {16, 8, 16, false}, {16, 16, 0, false}, {16, 16, 32, false},
+                                {16, 8, 0, true},  {16, 8, 16, true},  {16, 16, 0, true},  {16, 16, 32, true}};
+
+
+// Register slots of the largest column-kernel variant.
+constexpr int kMaxSlots = 16;
+
+// One segment's program as instruction lists.
+struct Emitted {
+  std::vector<ColInstr> loads, ops, stores;
+  std::vector<int> pos;   // ops[] index of each input op (the program may reorder them)
+  int nfirst = 0;         // leaves loaded before the ops
+  int slots = 0;          // register slots the program uses
+};
+
+// The ops whose value stays in y until the next combine: positions of the
+// first combine after each op (K: none).
+std::vector<int> next_combine(const std::vector<Event>& ops) {
+  const int K = int(ops.size());
+  std::vector<int> nc(size_t(K), K);
+  for (int i = K - 1, nxt = K; i >= 0; --i) {
+    nc[size_t(i)] = nxt;
+    if (ops[size_t(i)].combine) nxt = i;
+  }
+  return nc;
+}
+
+// Last use of every value: op i at position i, store j at ops.size() + j.
+std::vector<int> last_uses(const std::vector<Node>& nodes, const std::vector<Event>& ops,
+                           const std::vector<std::pair<int, int>>& stores) {
+  const int K = int(ops.size());
+  std::vector<int> last(nodes.size(), -1);
+  for (int i = 0; i < K; ++i) {
+    const Event& e = ops[size_t(i)];
+    if (e.combine) {
+      last[size_t(nodes[size_t(e.node)].a)] = i;
+      last[size_t(nodes[size_t(e.node)].b)] = i;
+    } else {
+      last[size_t(e.node)] = i;
+    }
+  }
+  for (size_t j = 0; j < stores.size(); ++j) last[size_t(stores[j].second)] = K + int(j);
+  return last;
+}
+
+// Every live leaf loaded before the ops, into slots 0 .. L-1, the ops in the
+// rows' order; a value that outlives y goes to a slot no later op needs.
+bool emit_plain(const std::vector<Node>& nodes, const std::vector<char>& live, const std::vector<Event>& ops,
+                const std::vector<std::pair<int, int>>& stores, bool checksums, Emitted& em) {
+  const int K = int(ops.size());
+  const std::vector<int> last = last_uses(nodes, ops, stores);
+  const std::vector<int> next_comb = next_combine(ops);
+  bool ok = true;
+  std::vector<int> slot(nodes.size(), -1), owner;
+  for (size_t n = 0; n < nodes.size(); ++n)
+    if (nodes[n].leaf && live[n]) {
+      slot[n] = int(owner.size());
+      owner.push_back(int(n));
+      ColInstr in{};
+      in.a = uint8_t(slot[n] & 0xff);
+      in.arg = uint32_t(nodes[n].rank);
+      em.loads.push_back(in);
+    }
+  em.nfirst = int(em.loads.size());
+  int y = -1;
+  for (int i = 0; i < K; ++i) {
+    const Event& e = ops[size_t(i)];
+    ColInstr in{};
+    in.arg = e.shift;
+    auto operand = [&](int n, uint8_t ybit, uint8_t& field) {
+      if (n == y) {
+        in.flags |= ybit;
+      } else {
+        field = uint8_t(slot[size_t(n)] & 0xff);
+        if (slot[size_t(n)] < 0) ok = false;
+      }
+    };
+    if (e.combine) {
+      const Node& n = nodes[size_t(e.node)];
+      in.flags |= CI_COMBINE;
+      operand(n.a, CI_A_Y, in.a);
+      operand(n.b, CI_B_Y, in.b);
+      const int nc = next_comb[size_t(i)];
+      if (nc < K && last[size_t(e.node)] > nc) {
+        // needed after the next combine replaces y: keep it in a slot whose
+        // value is not needed after this op
+        int s = -1;
+        for (size_t q = 0; q < owner.size() && s < 0; ++q)
+          if (owner[q] < 0 || last[size_t(owner[q])] <= i) s = int(q);
+        if (s < 0) {
+          s = int(owner.size());
+          owner.push_back(-1);
+        }
+        if (owner[size_t(s)] >= 0) slot[size_t(owner[size_t(s)])] = -1;
+        owner[size_t(s)] = e.node;
+        slot[size_t(e.node)] = s;
+        in.flags |= CI_WRITE;
+        in.out = uint8_t(s & 0xff);
+      }
+      y = e.node;
+    } else {
+      operand(e.node, CI_A_Y, in.a);
+    }
+    if (checksums) in.flags |= CI_CKS;
+    em.ops.push_back(in);
+    em.pos.push_back(i);
+  }
+  for (auto& st : stores) {
+    ColInstr in{};
+    in.arg = uint32_t(st.first);
+    if (st.second == y) {
+      in.flags = CI_A_Y;
+    } else {
+      in.a = uint8_t(slot[size_t(st.second)] & 0xff);
+      if (slot[size_t(st.second)] < 0) ok = false;
+    }
+    em.stores.push_back(in);
+  }
+  em.slots = int(owner.size());
+  return ok;
+}
+
+// Programs with more leaves than slots: the combines in depth-first order
+// from the final values (each value after its operands, old destination
+// value first; a combine and
+// its operands are the schedule's, so the arithmetic is unchanged), leaves in
+// order of first use, brought in batches of up to COL_BATCH into slots 0 ..
+// COL_BATCH-1 (a RELOAD flag on the op that first needs a batch) once the
+// batch before is consumed, a batch ending early rather than between the two
+// leaf operands of one combine; values that outlive y go to slots COL_BATCH ..
+// kMaxSlots-1.  False when the order does not allow it (a
+// batch boundary between two leaves one combine needs, a copy's checksum of
+// a leaf, a stored leaf outside the last batch, more than kMaxSlots slots).
+bool emit_batched(const std::vector<Node>& nodes, const std::vector<Event>& ops_in,
+                  const std::vector<std::pair<int, int>>& stores, bool checksums, Emitted& em) {
+  const int B = int(COL_BATCH);
+  // each combine's event, and the copies' checksum events per value
+  std::vector<int> event_of(nodes.size(), -1);
+  std::vector<std::vector<int>> copies_of(nodes.size());
+  for (size_t i = 0; i < ops_in.size(); ++i) {
+    if (ops_in[i].combine) event_of[size_t(ops_in[i].node)] = int(i);
+    else if (nodes[size_t(ops_in[i].node)].leaf) return false;
+    else copies_of[size_t(ops_in[i].node)].push_back(int(i));
+  }
+  // depth-first order of the combines, from the values the events and the
+  // stores need
+  std::vector<int> order;
+  std::vector<char> seen(nodes.size(), 0);
+  std::vector<std::pair<int, int>> stack;  // (node, next child to visit)
+  auto visit = [&](int root) {
+    if (nodes[size_t(root)].leaf || seen[size_t(root)]) return;
+    stack.push_back({root, 0});
+    seen[size_t(root)] = 1;
+    while (!stack.empty()) {
+      auto& top = stack.back();
+      const Node& n = nodes[size_t(top.first)];
+      if (top.second < 2) {
+        const int c = top.second == 0 ? n.a : n.b;
+        ++top.second;
+        if (!nodes[size_t(c)].leaf && !seen[size_t(c)]) {
+          seen[size_t(c)] = 1;
+          stack.push_back({c, 0});
+        }
+      } else {
+        order.push_back(top.first);
+        stack.pop_back();
+      }
+    }
+  };
+  // roots first (the stored values, then values no combine reads), so that
+  // each subtree is finished before the next starts
+  std::vector<char> operand(nodes.size(), 0);
+  for (const Event& e : ops_in)
+    if (e.combine) {
+      operand[size_t(nodes[size_t(e.node)].a)] = 1;
+      operand[size_t(nodes[size_t(e.node)].b)] = 1;
+    }
+  for (auto& st : stores) visit(st.second);
+  for (const Event& e : ops_in)
+    if (!operand[size_t(e.node)]) visit(e.node);
+  for (const Event& e : ops_in) visit(e.node);
+  // the ops in that order, each combine followed by the copies of its value
+  std::vector<Event> ops;
+  std::vector<int> src;  // ops_in index of each op
+  for (int n : order) {
+    if (event_of[size_t(n)] < 0) return false;  // a needed value no event computes
+    ops.push_back(ops_in[size_t(event_of[size_t(n)])]);
+    src.push_back(event_of[size_t(n)]);
+    for (int c : copies_of[size_t(n)]) {
+      ops.push_back(ops_in[size_t(c)]);
+      src.push_back(c);
+    }
+  }
+  if (ops.size() != ops_in.size()) return false;
+  // leaves in order of first use
+  std::vector<int> leaves;
+  std::vector<int> leaf_idx(nodes.size(), -1);
+  auto take = [&](int n) {
+    if (nodes[size_t(n)].leaf && leaf_idx[size_t(n)] < 0) {
+      leaf_idx[size_t(n)] = int(leaves.size());
+      leaves.push_back(n);
+    }
+  };
+  for (const Event& e : ops)
+    if (e.combine) {
+      take(nodes[size_t(e.node)].a);
+      take(nodes[size_t(e.node)].b);
+    }
+  for (auto& st : stores) take(st.second);
+  const int K = int(ops.size());
+  const std::vector<int> last = last_uses(nodes, ops, stores);
+  const std::vector<int> next_comb = next_combine(ops);
+  for (int n : leaves) {
+    ColInstr in{};
+    in.a = uint8_t(leaf_idx[size_t(n)] % B);
+    in.arg = uint32_t(nodes[size_t(n)].rank);
+    em.loads.push_back(in);
+  }
+  // a batch holds up to B leaves, fewer where the next would split the two
+  // leaf operands of one combine
+  std::vector<int> pair_of(nodes.size(), -1);
+  for (const Event& e : ops)
+    if (e.combine && nodes[size_t(nodes[size_t(e.node)].a)].leaf && nodes[size_t(nodes[size_t(e.node)].b)].leaf) {
+      pair_of[size_t(nodes[size_t(e.node)].a)] = nodes[size_t(e.node)].b;
+      pair_of[size_t(nodes[size_t(e.node)].b)] = nodes[size_t(e.node)].a;
+    }
+  auto batch_size = [&](int from) {
+    int m = std::min(B, int(leaves.size()) - from);
+    if (from + m < int(leaves.size()) && m > 1 && pair_of[size_t(leaves[size_t(from + m - 1)])] == leaves[size_t(from + m)])
+      --m;
+    return m;
+  };
+  std::vector<int> slot(nodes.size(), -1), owner(size_t(kMaxSlots), -1);
+  int next_leaf = batch_size(0);  // leaves[0 .. next_leaf) are or were loaded
+  em.nfirst = next_leaf;
+  for (int q = 0; q < next_leaf; ++q) {
+    slot[size_t(leaves[size_t(q)])] = q;
+    owner[size_t(q)] = leaves[size_t(q)];
+  }
+  int y = -1, slots = next_leaf;
+  em.pos.assign(ops_in.size(), -1);
+  int reload_next = 0;  // leaves the next op brings in first
+  auto reload = [&](int at) {
+    // every loaded leaf must be consumed before op `at`
+    for (int q = 0; q < B; ++q)
+      if (owner[size_t(q)] >= 0 && last[size_t(owner[size_t(q)])] >= at) return false;
+    const int m = batch_size(next_leaf);
+    if (m <= 0 || reload_next) return false;
+    reload_next = m;
+    for (int q = 0; q < B; ++q) {
+      if (owner[size_t(q)] >= 0) slot[size_t(owner[size_t(q)])] = -1;
+      owner[size_t(q)] = -1;
+    }
+    for (int q = 0; q < m; ++q) {
+      slot[size_t(leaves[size_t(next_leaf + q)])] = q;
+      owner[size_t(q)] = leaves[size_t(next_leaf + q)];
+    }
+    slots = std::max(slots, m);
+    next_leaf += m;
+    return true;
+  };
+  for (int i = 0; i < K; ++i) {
+    const Event& e = ops[size_t(i)];
+    if (e.combine) {
+      for (int c : {nodes[size_t(e.node)].a, nodes[size_t(e.node)].b})
+        if (nodes[size_t(c)].leaf && slot[size_t(c)] < 0) {
+          if (leaf_idx[size_t(c)] != next_leaf || !reload(i)) return false;
+        }
+      // both leaf operands must be in slots now (a reload may not evict the other)
+      for (int c : {nodes[size_t(e.node)].a, nodes[size_t(e.node)].b})
+        if (c != y && slot[size_t(c)] < 0) return false;
+    }
+    ColInstr in{};
+    in.arg = e.shift;
+    auto operand = [&](int n, uint8_t ybit, uint8_t& field) {
+      if (n == y) {
+        in.flags |= ybit;
+        return true;
+      }
+      field = uint8_t(slot[size_t(n)] & 0xff);
+      return slot[size_t(n)] >= 0;
+    };
+    if (e.combine) {
+      const Node& n = nodes[size_t(e.node)];
+      in.flags |= CI_COMBINE;
+      if (!operand(n.a, CI_A_Y, in.a) || !operand(n.b, CI_B_Y, in.b)) return false;
+      const int nc = next_comb[size_t(i)];
+      if (nc < K && last[size_t(e.node)] > nc) {
+        int s = -1;
+        for (int q = B; q < kMaxSlots && s < 0; ++q)
+          if (owner[size_t(q)] < 0 || last[size_t(owner[size_t(q)])] <= i) s = q;
+        if (s < 0) return false;
+        if (owner[size_t(s)] >= 0) slot[size_t(owner[size_t(s)])] = -1;
+        owner[size_t(s)] = e.node;
+        slot[size_t(e.node)] = s;
+        slots = std::max(slots, s + 1);
+        in.flags |= CI_WRITE;
+        in.out = uint8_t(s);
+      }
+      y = e.node;
+    } else if (!operand(e.node, CI_A_Y, in.a)) {
+      return false;
+    }
+    if (checksums) in.flags |= CI_CKS;
+    if (reload_next) {
+      in.flags |= CI_RELOAD;
+      in.arg |= uint32_t(reload_next) << 8;
+    }
+    reload_next = 0;
+    em.pos[size_t(src[size_t(i)])] = int(em.ops.size());
+    em.ops.push_back(in);
+  }
+  if (next_leaf != int(leaves.size())) return false;
+  for (auto& st : stores) {
+    ColInstr in{};
+    in.arg = uint32_t(st.first);
+    if (st.second == y) {
+      in.flags = CI_A_Y;
+    } else {
+      if (slot[size_t(st.second)] < 0) return false;
+      in.a = uint8_t(slot[size_t(st.second)]);
+    }
+    em.stores.push_back(in);
+  }
+  em.slots = slots;
+  return true;
+}
 
 }  // namespace
 
@@ -187,113 +514,42 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
     }
     if (ops.empty() && stores.empty()) continue;  // nothing to load, compute or store
 
-    // positions: op i at i, store j at ops.size() + j; the last use of each value
-    const int K = int(ops.size());
-    std::vector<int> last(nodes.size(), -1);
-    for (int i = 0; i < K; ++i) {
-      const Event& e = ops[size_t(i)];
-      if (e.combine) {
-        last[size_t(nodes[size_t(e.node)].a)] = i;
-        last[size_t(nodes[size_t(e.node)].b)] = i;
-      } else {
-        last[size_t(e.node)] = i;
-      }
+    Emitted em;
+    if (!emit_plain(nodes, live, ops, stores, checksums, em)) return fail("internal: a value has no slot");
+    if (em.slots > kMaxSlots) {
+      Emitted eb;
+      if (!emit_batched(nodes, ops, stores, checksums, eb)) return fail("a program needs more than 16 slots, in batches too");
+      em = std::move(eb);
     }
-    for (size_t j = 0; j < stores.size(); ++j) last[size_t(stores[j].second)] = K + int(j);
-    std::vector<int> next_comb(size_t(K), K);  // the first combine after op i (K: none)
-    for (int i = K - 1, nxt = K; i >= 0; --i) {
-      next_comb[size_t(i)] = nxt;
-      if (ops[size_t(i)].combine) nxt = i;
-    }
-
     ColSeg sg{};
     sg.s0 = uint64_t(e0) * uint64_t(sz);
     sg.s1 = uint64_t(e1) * uint64_t(sz);
     sg.loads = uint32_t(p.code.size());
-    std::vector<int> slot(nodes.size(), -1), owner;
-    for (size_t n = 0; n < nodes.size(); ++n)
-      if (nodes[n].leaf && live[n]) {
-        slot[n] = int(owner.size());
-        owner.push_back(int(n));
-        ColInstr in{};
-        in.a = uint8_t(slot[n] & 0xff);
-        in.arg = uint32_t(nodes[n].rank);
-        p.code.push_back(in);
-      }
-    const int nload = int(owner.size());
+    p.code.insert(p.code.end(), em.loads.begin(), em.loads.end());
     sg.ops = uint32_t(p.code.size());
-    int y = -1;
-    for (int i = 0; i < K; ++i) {
-      const Event& e = ops[size_t(i)];
-      ColInstr in{};
-      in.arg = e.shift;
-      auto operand = [&](int n, uint8_t ybit, uint8_t& field) {
-        if (n == y) {
-          in.flags |= ybit;
-        } else {
-          field = uint8_t(slot[size_t(n)] & 0xff);
-          if (slot[size_t(n)] < 0) p.why = "internal: a value has no slot";
-        }
-      };
-      if (e.combine) {
-        const Node& n = nodes[size_t(e.node)];
-        in.flags |= CI_COMBINE;
-        operand(n.a, CI_A_Y, in.a);
-        operand(n.b, CI_B_Y, in.b);
-        const int nc = next_comb[size_t(i)];
-        if (nc < K && last[size_t(e.node)] > nc) {
-          // needed after the next combine replaces y: keep it in a slot whose
-          // value is not needed after this op
-          int s = -1;
-          for (size_t q = 0; q < owner.size() && s < 0; ++q)
-            if (owner[q] < 0 || last[size_t(owner[q])] <= i) s = int(q);
-          if (s < 0) {
-            s = int(owner.size());
-            owner.push_back(-1);
-          }
-          if (owner[size_t(s)] >= 0) slot[size_t(owner[size_t(s)])] = -1;
-          owner[size_t(s)] = e.node;
-          slot[size_t(e.node)] = s;
-          in.flags |= CI_WRITE;
-          in.out = uint8_t(s & 0xff);
-        }
-        y = e.node;
-      } else {
-        operand(e.node, CI_A_Y, in.a);
-      }
-      if (checksums) in.flags |= CI_CKS;
-      p.code.push_back(in);
-    }
+    p.code.insert(p.code.end(), em.ops.begin(), em.ops.end());
     sg.stores = uint32_t(p.code.size());
-    for (auto& st : stores) {
-      ColInstr in{};
-      in.arg = uint32_t(st.first);
-      if (st.second == y) {
-        in.flags = CI_A_Y;
-      } else {
-        in.a = uint8_t(slot[size_t(st.second)] & 0xff);
-        if (slot[size_t(st.second)] < 0) p.why = "internal: a stored value has no slot";
-      }
-      p.code.push_back(in);
-    }
-    if (!p.why.empty()) return fail("internal: a value has no slot");
+    p.code.insert(p.code.end(), em.stores.begin(), em.stores.end());
+    const int nload = int(em.loads.size()), K = int(em.ops.size());
+    sg.nfirst = uint16_t(em.nfirst);
+    if (em.nfirst < nload) p.batched = true;
     sg.nload = uint16_t(nload);
     sg.nop = uint16_t(K);
-    sg.nstore = uint16_t(stores.size());
-    if (nload > COL_LIST_MAX || K > COL_LIST_MAX || int(stores.size()) > COL_LIST_MAX)
+    sg.nstore = uint16_t(em.stores.size());
+    if (nload > COL_LIST_MAX || K > COL_LIST_MAX || int(em.stores.size()) > COL_LIST_MAX)
       return fail("a program list longer than 64 instructions");
     p.max_leaves = std::max<uint32_t>(p.max_leaves, uint32_t(nload));
-    p.max_slots = std::max<uint32_t>(p.max_slots, uint32_t(owner.size()));
+    p.max_slots = std::max<uint32_t>(p.max_slots, uint32_t(em.slots));
     p.max_ops = std::max<uint32_t>(p.max_ops, uint32_t(K));
-    p.max_stores = std::max<uint32_t>(p.max_stores, uint32_t(stores.size()));
-    p.moved_bytes += uint64_t(nload + int(stores.size())) * (sg.s1 - sg.s0);
+    p.max_stores = std::max<uint32_t>(p.max_stores, uint32_t(em.stores.size()));
+    p.moved_bytes += uint64_t(nload + int(em.stores.size())) * (sg.s1 - sg.s0);
     if (checksums)
       for (size_t i = 0; i < ev.size(); ++i)
-        p.refs.push_back(ColRowRef{ev[i].row, uint32_t(p.segs.size()), uint32_t(carrier[i])});
+        p.refs.push_back(ColRowRef{ev[i].row, uint32_t(p.segs.size()), uint32_t(em.pos[size_t(carrier[i])])});
     p.segs.push_back(sg);
   }
   for (const ColVariant& v : kVariants) {
-    if ((v.accs > 0) != checksums) continue;
+    if ((v.accs > 0) != checksums || v.batched != p.batched) continue;
     if (int(p.max_slots) > v.leaves || (checksums && int(p.max_ops) > v.accs) || sz > v.unit) continue;
     p.v = v;
     p.ok = true;
@@ -322,6 +578,7 @@ ColTables col_tables(const ColPlan& p, uint32_t tiles_per_group, size_t nrows) {
       c.ops = sg.ops;
       c.stores = sg.stores;
       c.part = uint32_t(cks ? t.partials : 0);
+      c.nfirst = sg.nfirst;
       c.nload = sg.nload;
       c.nop = sg.nop;
       c.nstore = sg.nstore;

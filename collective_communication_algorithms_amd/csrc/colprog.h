@@ -13,12 +13,15 @@ namespace coll {
 
 // Register capacities of the column kernel's variants: `unit` bytes per lane
 // and column, at most `leaves` leaves and slots, and `accs` checksum
-// accumulators (0: the variant computes no checksums).  Every list of a
-// program holds at most 64 instructions (one per lane).
+// accumulators (0: the variant computes no checksums); `batched` variants
+// also run programs that bring their leaves in batches (RELOAD ops), at the
+// cost of the registers that takes.  Every list of a program holds at most
+// 64 instructions (one per lane).
 struct ColVariant {
   int unit = 16;
   int leaves = 8;
   int accs = 0;
+  bool batched = false;
 };
 
 // With checksums: row `row`'s checksum over segment `seg` is the sum of op
@@ -38,6 +41,7 @@ struct ColPlan {
   std::vector<ColRowRef> refs;   // checksums only; one per (row, segment it covers)
   uint64_t moved_bytes = 0;      // leaf loads and stores: bytes each segment moves, summed
   uint32_t max_leaves = 0, max_slots = 0, max_ops = 0, max_stores = 0;
+  bool batched = false;          // some program loads its leaves in batches
 };
 
 constexpr int COL_LIST_MAX = 64;

@@ -124,28 +124,36 @@ enum : uint32_t {
   CI_B_Y = 1u << 2,      // op: B is y, not slot `b`
   CI_WRITE = 1u << 3,    // op: y also goes to slot `out` (it is needed after y changes)
   CI_CKS = 1u << 4,      // op: the value's words go to the checksum of the op's row
+  CI_RELOAD = 1u << 5,   // op: first load the next m = (arg >> 8) & 0xff leaves of the loads list
+                         // (1 <= m <= COL_BATCH) into slots 0 .. m-1
 };
+
+// Leaves a RELOAD brings in at most.
+constexpr uint32_t COL_BATCH = 8;
 
 struct ColInstr {        // 8 bytes
   uint8_t flags;         // CI_* (ops, stores)
   uint8_t a, b, out;     // slots: A / stored value, B, result
-  uint32_t arg;          // load / store: rank; op: (-row start byte) mod 4 for its checksum
+  uint32_t arg;          // load / store: rank; op: bits 0-1 (-row start byte) mod 4 for its
+                         // checksum, bits 8-15 RELOAD's leaf count
 };
 
 struct ColSeg {          // 40 bytes: one segment's program
   uint64_t s0, s1;       // column bytes [s0, s1)
   uint32_t loads, ops, stores;  // first instruction of each list
-  uint32_t pad0;
-  uint16_t nload, nop, nstore, pad;  // leaf k is loaded into slot k
+  uint16_t nfirst, pad0;  // leaves 0 .. nfirst-1 are loaded into slots 0 .. nfirst-1 before the
+                          // ops; ops flagged RELOAD bring in the rest
+  uint16_t nload, nop, nstore, pad;
 };
 
-struct ColWork {         // 48 bytes: one work group's tiles and its segment's program
+struct ColWork {         // 56 bytes: one work group's tiles and its segment's program
   uint64_t c0;           // column byte of its first tile (a multiple of the tile size)
   uint64_t s0, s1;       // the segment's column bytes
   uint32_t loads, ops, stores;
   uint32_t part;         // checksums: its nop partial sums go to partial[part .. part + nop)
   uint16_t nload, nop, nstore;
   uint16_t ntiles;       // consecutive tiles from c0
+  uint16_t nfirst, pad0, pad1, pad2;
 };
 
 // Row checksums of the column kernel: every work group stores op k's wave

@@ -20,8 +20,8 @@ hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes,
 hipError_t launch_spin(float* out, uint32_t iters, uint32_t grid, hipStream_t stream);
 // column kernel: the variant of (unit, leaves, accs) (ColVariant), nontemporal
 // loads and stores when `nt`; one work group of COL_THREADS per ColWork
-hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool nt, uint32_t grid,
-                      hipStream_t stream);
+hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool batched, bool nt,
+                      uint32_t grid, hipStream_t stream);
 // out[r] = the sum of the partial slots row r's ColRefs name, r < nrows, by way
 // of tmp (nrows * COL_FOLD_SLICES slots)
 hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,

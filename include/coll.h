@@ -196,9 +196,9 @@ coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nr
  * (hipMemcpyAsync on `stream`) and first waits for `stream`.  Calls that
  * overlap on one GPU (other streams or threads) race on the array.
  * Errors: as coll_allreduce; COLL_ERR_UNSUPPORTED when the column kernel does
- * not run the call (rank buffers not 16-byte aligned, or a schedule whose
- * programs need more than 16 register slots, e.g. Ring or halving-doubling
- * over more than 16 ranks); COLL_ERR_INVALID_ARG when its tables and partial
+ * not run the call (rank buffers not 16-byte aligned, or programs no kernel
+ * variant holds: with row checksums, more than 32 ops, as Ring over 64 ranks
+ * has); COLL_ERR_INVALID_ARG when its tables and partial
  * sums do not fit the array even with the fewest work groups (the message
  * says how many bytes they need).  Not in coll_get_stats' schedule cache. */
 #define COLL_NOALLOC_SCRATCH_BYTES (16u << 20)
@@ -309,7 +309,7 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          written last is read first [1]; 0: always forwards.
  * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
  * COLL_OPT_MODEL_BETA_GBPS moved-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
- * COLL_OPT_COL_TILES       column kernel: tiles (64 lanes x 16 or 4 bytes) per
+ * COLL_OPT_COL_TILES       column kernel: tiles (64 lanes x 16 bytes) per
  *                          work group, up to 65535 [0: automatic, 1..8 by size].
  * COLL_OPT_TIMING          1: every call made outside graph capture records a
  *                          HIP event before its first data-moving kernel and

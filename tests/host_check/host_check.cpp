@@ -649,6 +649,7 @@ void check_launch_shapes() {
 
 long long col_plans = 0;     // programs compiled and executed
 long long col_fallbacks = 0; // shapes the column kernel leaves to the row kernel
+long long col_batched = 0;   // programs that bring leaves in batches
 
 // Element symbols: input of rank r at element e; reductions mix(d, s).
 uint32_t input_sym(int r, int64_t e) { return uint32_t(r) * 0x9E3779B1u + uint32_t(e) * 0x7FEB352Du + 1u; }
@@ -701,7 +702,8 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
     const ColSeg& sg = p.segs[si];
     CHECK(sg.s0 % uint64_t(sh.sz) == 0 && sg.s1 % uint64_t(sh.sz) == 0 && sg.s0 < sg.s1 && sg.s1 <= p.colspace,
           "%s: segment bytes", name(sh).c_str());
-    CHECK(int(sg.nload) <= p.v.leaves && sg.nload <= COL_LIST_MAX && sg.nop <= COL_LIST_MAX &&
+    CHECK(int(sg.nfirst) <= p.v.leaves && (sg.nfirst == sg.nload || sg.nfirst <= COL_BATCH) &&
+              sg.nload <= COL_LIST_MAX && sg.nop <= COL_LIST_MAX &&
               sg.nstore <= COL_LIST_MAX && (!cks || int(sg.nop) <= p.v.accs),
           "%s: program exceeds its variant", name(sh).c_str());
     for (const ColRowRef& r : seg_refs[si]) {
@@ -710,23 +712,37 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
       CHECK(row.dst_off * sh.sz <= int64_t(sg.s0) && int64_t(sg.s1) <= (row.dst_off + row.n) * sh.sz,
             "%s: ref row does not cover its segment", name(sh).c_str());
       if (r.op < sg.nop)
-        CHECK(p.code[sg.ops + r.op].arg == uint32_t((((-(row.dst_off * sh.sz)) % 4) + 4) % 4),
+        CHECK((p.code[sg.ops + r.op].arg & 3u) == uint32_t((((-(row.dst_off * sh.sz)) % 4) + 4) % 4),
               "%s: checksum shift", name(sh).c_str());
     }
     std::vector<uint32_t> opval(sg.nop);
     for (int64_t e = int64_t(sg.s0) / sh.sz; e < int64_t(sg.s1) / sh.sz; ++e) {
       std::vector<uint32_t> slot(size_t(p.v.leaves), 0xDEADBEEFu);
       std::vector<char> full(size_t(p.v.leaves), 0);
-      for (uint32_t j = 0; j < sg.nload; ++j) {
-        const ColInstr& in = p.code[sg.loads + j];
-        CHECK(in.a == j && in.arg < uint32_t(N), "%s: leaf %u", name(sh).c_str(), j);
-        slot[j] = input_sym(int(in.arg), e);
+      // the kernel's loads: leaves 0 .. nfirst-1 into slots 0 .. nfirst-1,
+      // then per RELOAD op the next m into slots 0 .. m-1
+      for (uint32_t j = 0; j < sg.nload; ++j)
+        CHECK(p.code[sg.loads + j].arg < uint32_t(N), "%s: leaf %u", name(sh).c_str(), j);
+      for (uint32_t j = 0; j < sg.nfirst; ++j) {
+        slot[j] = input_sym(int(p.code[sg.loads + j].arg), e);
         full[j] = 1;
       }
+      uint32_t next = sg.nfirst;
+      if (e == int64_t(sg.s0) / sh.sz && sg.nfirst < sg.nload) ++col_batched;
       uint32_t y = 0xBADC0DEu;
       bool yset = false;
       for (uint32_t k = 0; k < sg.nop; ++k) {
         const ColInstr& in = p.code[sg.ops + k];
+        if (in.flags & CI_RELOAD) {
+          const uint32_t m = (in.arg >> 8) & 0xffu;
+          CHECK(m >= 1 && m <= COL_BATCH && next + m <= sg.nload, "%s: RELOAD of %u leaves", name(sh).c_str(),
+                unsigned(m));
+          for (uint32_t j = 0; j < m && next + j < sg.nload; ++j) {
+            slot[j] = input_sym(int(p.code[sg.loads + next + j].arg), e);
+            full[j] = 1;
+          }
+          next += m;
+        }
         auto opnd = [&](uint8_t ybit, uint8_t sl) {
           if (in.flags & ybit) {
             CHECK(yset, "%s: y read before set", name(sh).c_str());
@@ -753,6 +769,7 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
         CHECK(((in.flags & CI_CKS) != 0) == cks, "%s: checksum flag", name(sh).c_str());
         opval[k] = v;
       }
+      CHECK(next >= sg.nload, "%s: leaves listed but never loaded", name(sh).c_str());
       for (const ColRowRef& r : seg_refs[si]) {
         const Row& row = s.rows[r.row];
         if (r.op >= sg.nop || e < row.dst_off || e >= row.dst_off + row.n) continue;
@@ -807,7 +824,7 @@ void check_colplan(const Shape& sh, const Schedule& s, bool cks) {
     const size_t segi = it->second;
     const ColSeg& sg = p.segs[segi];
     CHECK(c.s0 == sg.s0 && c.s1 == sg.s1 && c.loads == sg.loads && c.ops == sg.ops && c.stores == sg.stores &&
-              c.nload == sg.nload && c.nop == sg.nop && c.nstore == sg.nstore,
+              c.nfirst == sg.nfirst && c.nload == sg.nload && c.nop == sg.nop && c.nstore == sg.nstore,
           "%s: a work group's program is not its segment's", name(sh).c_str());
     const uint64_t lo = std::max<uint64_t>(c.c0, sg.s0), hi = std::min<uint64_t>(c.c0 + c.ntiles * tb, sg.s1);
     CHECK(lo < hi, "%s: a work group with no bytes of its segment", name(sh).c_str());
@@ -877,6 +894,17 @@ int main(int argc, char** argv) {
                 shapes.push_back(s);
               }
             }
+      // more ranks than the column kernel's slots: batched leaves or the row kernel
+      for (int N : {17, 32, 64})
+        for (int64_t count : {int64_t(1), int64_t(77), int64_t(1000)})
+          for (int sz : {2, 4})
+            for (int inplace = 0; inplace < 2; ++inplace) {
+              Shape s{kind, coll_algo_t(a), N, count * (kind == COLL_K_ALLTOALL ? N : 1), N / 3, 1, sz, inplace != 0};
+              if (kind == COLL_K_ALLTOALL && inplace) continue;
+              std::string err;
+              if (validate_schedule_args(kind, s.algo, N, s.count, s.root, 1, err) != COLL_OK) continue;
+              shapes.push_back(s);
+            }
     }
   int nlists = 0;
   for (const Shape& sh : shapes) {
@@ -912,9 +940,10 @@ int main(int argc, char** argv) {
   CHECK(no_store_marks > 0, "no store was skipped");
   CHECK(exec_mode == EXEC_NONE || exec_lists > 0, "no list was executed");
   CHECK(col_plans > 0, "no column program was checked");
+  CHECK(col_batched > 0, "no batched column program was checked");
   std::printf("host_check: %zu shapes, %d lists, %lld forwarding marks, %lld skipped stores, %lld list executions, "
-              "%lld column programs (%lld shapes left to the row kernel), %s\n",
-              shapes.size(), nlists, fwd_marks, no_store_marks, exec_lists, col_plans, col_fallbacks,
+              "%lld column programs (%lld batched; %lld shapes left to the row kernel), %s\n",
+              shapes.size(), nlists, fwd_marks, no_store_marks, exec_lists, col_plans, col_batched, col_fallbacks,
               failures ? "FAILED" : "ok");
   return failures ? 1 : 0;
 }

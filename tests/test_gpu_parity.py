@@ -337,6 +337,30 @@ def test_forwarding_moves_what_the_plan_says(exec_mode):
     assert st["moved_bytes"] == st["hbm_bytes"] == 5 * (N - 1) * M
 
 
+@pytest.mark.parametrize("N", [17, 32, 64])
+@pytest.mark.parametrize("dtype,sigma", [("float32", 1.0), ("bfloat16", 0.02), ("int32", 1.0)])
+def test_batched_leaves_many_ranks(N, dtype, sigma):
+    """More ranks than the column kernel's 16 slots: its programs
+    bring the leaves in batches of 8 and combine depth-first (the schedule's
+    own combines and operand order, so floats stay bit-exact).  Reductions
+    over 17, 32 and 64 ranks against the oracle, in one round trip; and with
+    row checksums (the column kernel where the ops fit its 32 accumulators,
+    else the row kernel)."""
+    import collective_communication_algorithms_amd as coll
+    pow2 = (N & (N - 1)) == 0
+    g = np.random.default_rng(N)
+    count = 5 * N * 64 + 3
+    a = si.rank_arrays(N, N, count, dtype, sigma=sigma)
+    cases = [("allreduce", "ring"), ("allreduce", "rhd"), ("allreduce", "dbt"), ("reduce", "binomial"),
+             ("reducescatter", "ring")] + ([("reducescatter", "rhd")] if pow2 else [])
+    for kind, algo in cases:
+        root = int(g.integers(0, N)) if kind == "reduce" else 0
+        assert_parity(kind, algo, a, dtype, root=root)
+        assert coll.coll_get_stats()["round_trips"] == 1, (kind, algo)
+        if dtype != "int32":
+            assert_parity(kind, algo, a, dtype, root=root, checksums=True)
+
+
 @pytest.mark.parametrize("N", [3, 5, 6, 7, 12, 13])
 def test_non_power_of_two_rhd_dbt(N):
     """Halving-doubling with the surplus folded into a power-of-two core, and
