@@ -35,9 +35,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "busbw GB/s & % HBM peak, Ring AllReduce fp32 N=8 M=256MiB (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_col_kernel_ring_allreduce_fp32_n8_256MiB.json")
-# the column kernel variant the default run times: fp32, sum, 16-byte units,
-# 8 register slots, 16 checksum accumulators, nontemporal loads and stores
-HEADLINE_KERNEL = "void coll::(anonymous namespace)::col_kernel<2, 0, 8, 16, 5>"
+# the column kernel variant the default run times: fp32, sum, 8 register
+# slots, 16 checksum accumulators, nontemporal loads and stores, no batches
+HEADLINE_KERNEL = "void coll::(anonymous namespace)::col_kernel<2, 0, 8, 16, 5, false>"
 
 
 def kernel_source_hash() -> str:
@@ -437,8 +437,117 @@ def overlap(out_path: str, dev) -> None:
         torch.cuda.empty_cache()
 
 
+def latency(out_path: str, dev) -> None:
+    """Small calls: where their time goes (C1: Ring / RHD / DBT AllReduce over
+    4 ranks x 1,024 int32; C3's smallest: 8 ranks x 4 KiB fp32), in place.
+
+    Per call, in microseconds:
+      alone_api / alone_abi  one call between HIP events on its stream, after
+                    the previous one finished (median of 300), through the
+                    Python binding / straight through the C ABI (ctypes, the
+                    pointer arrays built once);
+      host_api / host_abi  host time per call of 2,000 calls issued back to
+                    back (the stream's time per call is reported beside it);
+      kernel        the library's own events around its kernels
+                    (COLL_OPT_TIMING, median of 200);
+      graph         a HIP graph of 20 calls captured once and replayed 50
+                    times: the device's time per call with no host in the
+                    loop (kernel launch and the kernel's dependent memory
+                    round trips)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import collective_communication_algorithms_amd as coll
+    from collective_communication_algorithms_amd import _lib
+    from collective_communication_algorithms_amd._lib import check
+
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev)
+    open(out_path, "w").close()
+
+    def between_events(fn, n):
+        ts = []
+        for _ in range(n):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            fn()
+            e.record(stream)
+            e.synchronize()
+            ts.append(s.elapsed_time(e) * 1e3)
+        return float(np.median(ts)), float(np.min(ts))
+
+    def back_to_back(fn, n=2000):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        h0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        h1 = time.perf_counter()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return (h1 - h0) / n * 1e6, e0.elapsed_time(e1) / n * 1e3
+
+    for cfg, N, count, dtype in (("C1", 4, 1024, "int32"), ("C3", 8, 1024, "float32")):
+        tdt = torch.int32 if dtype == "int32" else torch.float32
+        buf = torch.ones((N, count), dtype=tdt, device=dev)
+        ranks = list(buf)
+        arr = (ctypes.c_void_p * N)(*[t.data_ptr() for t in ranks])
+        for algo in ("ring", "rhd", "dbt"):
+            def api():
+                coll.coll_allreduce(ranks, algo=algo)
+
+            def abi(s=None):
+                check(lib.coll_allreduce(arr, None, N, count, _lib.DTYPES[dtype], _lib.OPS["sum"], _lib.ALGOS[algo],
+                                         0, 1, ctypes.c_void_p(s if s is not None else stream.cuda_stream)))
+
+            for _ in range(50):
+                api()
+            torch.cuda.synchronize()
+            host_api, stream_api = back_to_back(api)
+            host_abi, stream_abi = back_to_back(abi)
+            alone_api = between_events(api, 300)
+            alone_abi = between_events(abi, 300)
+            coll.coll_set_option("timing", 1)
+            ks = []
+            for _ in range(200):
+                abi()
+                ks.append(coll.coll_last_kernel_ms() * 1e3)
+            coll.coll_set_option("timing", 0)
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream(dev)
+            cs.wait_stream(stream)
+            with torch.cuda.graph(g, stream=cs):
+                for _ in range(20):
+                    abi(torch.cuda.current_stream(dev).cuda_stream)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(50):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            graph_us = e0.elapsed_time(e1) / 50 / 20 * 1e3
+            del g
+            r = {"config": cfg, "algo": algo, "nranks": N, "bytes_per_rank": count * 4, "dtype": dtype,
+                 "alone_api_us": round(alone_api[0], 2), "alone_api_min_us": round(alone_api[1], 2),
+                 "alone_abi_us": round(alone_abi[0], 2), "alone_abi_min_us": round(alone_abi[1], 2),
+                 "host_api_us": round(host_api, 2), "stream_api_us": round(stream_api, 2),
+                 "host_abi_us": round(host_abi, 2), "stream_abi_us": round(stream_abi, 2),
+                 "kernel_us": round(float(np.median(ks)), 2), "graph_us": round(graph_us, 2)}
+            with open(out_path, "a") as fh:
+                fh.write(json.dumps(r) + "\n")
+            print(json.dumps(r), file=sys.stderr, flush=True)
+        del buf, ranks
+
+
 def single_call(args, dev) -> int:
-    """``--call KIND``: one collective at one shape, for profiling its kernels.
+    """``--call KIND``: one collective at one shape (``--mib`` or ``--kib`` per
+    rank), for profiling its kernels.
 
     Inputs from torch's seeded device generator (workload 7).  One call on
     fresh inputs is checked on sampled columns against the collective's
@@ -455,7 +564,7 @@ def single_call(args, dev) -> int:
 
     kind, algo, N, dtype = args.call, args.call_algo, args.nranks, args.dtype
     sz = si.ITEMSIZE[dtype]
-    count = (args.mib << 20) // sz
+    count = ((args.kib << 10) if args.kib else (args.mib << 20)) // sz
     if kind == "alltoall":
         count -= count % N
     root, k = args.root % N, args.chunks
@@ -533,10 +642,29 @@ def single_call(args, dev) -> int:
         e.synchronize()
         ts.append(s.elapsed_time(e))
     ms = float(np.median(ts))
+    # the host path and the device floor of a call: 200 calls issued back to
+    # back (no restores, results not checked); the host's time per issued call
+    # and the stream's time per call
+    n_b2b = 200
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(n_b2b):
+        call()
+    h1 = time.perf_counter()
+    b1.record(stream)
+    torch.cuda.synchronize()
+    restore()
     print(json.dumps({"call": kind, "algo": algo, "dtype": dtype, "nranks": N, "bytes_per_rank": count * sz,
                       "root": root, "chunks": k, "steps": args.steps, "ms_median": round(ms, 4),
+                      "ms_min": round(float(np.min(ts)), 4),
+                      "host_us_per_issued_call": round((h1 - h0) / n_b2b * 1e6, 2),
+                      "back_to_back_us_per_call": round(b0.elapsed_time(b1) / n_b2b * 1e3, 2),
                       "schedule_steps": stats["steps"], "schedule_bytes": stats["hbm_bytes"],
                       "schedule_TBps": round(stats["hbm_bytes"] / (ms * 1e-3) / 1e12, 3),
+                      "moved_bytes": stats["moved_bytes"], "round_trips": stats["round_trips"],
+                      "moved_TBps": round(stats["moved_bytes"] / (ms * 1e-3) / 1e12, 3),
                       "check": "definition on sampled columns"}))
     return 0
 
@@ -551,6 +679,7 @@ def main() -> int:
                     help="auto: the column kernel; rows: the row kernel in one launch; step: a launch per step")
     ap.add_argument("--nranks", type=int, default=8)
     ap.add_argument("--mib", type=int, default=256, help="MiB per rank")
+    ap.add_argument("--kib", type=int, default=0, help="with --call: KiB per rank (instead of --mib)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-checksums", action="store_true",
                     help="time the calls without the per-row checksums (the default computes them)")
@@ -565,6 +694,8 @@ def main() -> int:
     ap.add_argument("--dtype", default="float32", choices=["int32", "uint8", "float32", "bfloat16"])
     ap.add_argument("--root", type=int, default=0)
     ap.add_argument("--chunks", type=int, default=1)
+    ap.add_argument("--latency", metavar="OUT_JSONL",
+                    help="time small calls (host path, kernels, graph replay) and exit")
     ap.add_argument("--overlap", metavar="OUT_JSONL",
                     help="time a collective on a side stream beside a stand-in compute kernel and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -598,6 +729,9 @@ def main() -> int:
         return 0
     if args.overlap:
         overlap(args.overlap, dev)
+        return 0
+    if args.latency:
+        latency(args.latency, dev)
         return 0
     if args.call:
         return single_call(args, dev)
