@@ -161,8 +161,8 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
     pristine device copy (not timed).  Median and minimum are reported, with
     algbw = M / t, busbw = algbw x the pages' coefficient, schedule bytes / t
     against the 8 TB/s HBM spec, the pages' alpha-beta prediction (alpha 5 us,
-    beta 450 GB/s) and a least-squares fit t = steps * alpha_g + bytes / beta_g
-    over the fp32 Ring AllReduce sizes.  The oracle is timed on the host (one
+    beta 450 GB/s) and a least-squares fit t = alpha_call + moved bytes /
+    beta_g over the fp32 Ring AllReduce sizes.  The oracle is timed on the host (one
     core) on the same inputs where that takes seconds; larger calls give none.
     """
     import numpy as np
@@ -310,13 +310,15 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
     del pristine, recv
     torch.cuda.empty_cache()
 
-    # alpha-beta fit on the fp32 Ring AllReduce sizes: t = steps * a + bytes / b
+    # the pages' alpha-beta form refitted to this engine over the fp32 Ring
+    # AllReduce sizes: one launch per call whatever the step count, so
+    # t = alpha_call + moved_bytes / beta_g
     pts = [r for r in rows if r["config"] == "C3" and r["algo"] == "ring" and r["dtype"] == "float32"]
-    A = np.array([[r["steps"], r["sched_bytes"]] for r in pts], dtype=np.float64)
+    A = np.array([[1.0, r["moved_bytes"]] for r in pts], dtype=np.float64)
     t = np.array([r["t_med_us"] * 1e-6 for r in pts])
     coef, *_ = np.linalg.lstsq(A, t, rcond=None)
-    fit = {"fit": "t = steps * alpha_g + sched_bytes / beta_g over C3 fp32 Ring",
-           "alpha_g_us": round(coef[0] * 1e6, 3), "beta_g_TBps": round(1 / coef[1] / 1e12, 3) if coef[1] > 0 else None}
+    fit = {"fit": "t = alpha_call + moved_bytes / beta_g over C3 fp32 Ring",
+           "alpha_call_us": round(coef[0] * 1e6, 3), "beta_g_TBps": round(1 / coef[1] / 1e12, 3) if coef[1] > 0 else None}
     with open(out_path, "a") as fh:
         fh.write(json.dumps(fit) + "\n")
     print(json.dumps(fit), file=sys.stderr)
