@@ -98,3 +98,83 @@ def test_captured_calls_with_checksums_replay_exactly(gpu_device):
             assert torch.equal(live.view(torch.int32), want.view(torch.int32)), ("replay", rep)
     finally:
         coll.coll_set_checksums(None)
+
+
+def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
+    """What a captured call's kernels read stays valid for every replay while
+    eager calls change the library's state underneath: the schedule cache
+    shrunk to nothing (every unpinned schedule evicted), new column tables for
+    the same schedule (another tile count), the checksum slot buffer of the
+    same caller buffer grown by a larger schedule, and more than 16 caller
+    checksum buffers (slot buffers evicted).  Replays must still give the
+    eager results and checksums bit for bit."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    dev = gpu_device
+    N, count = 8, 8 * 30000 + 5
+    a = si.rank_arrays(18, N, count, "float32")
+    pristine = torch.stack([si.host_to_tensor(x, "float32", dev) for x in a])
+    live = pristine.clone()
+    # a row-kernel call captured beside the column-kernel one: AllToAll
+    pa = torch.stack([si.host_to_tensor(x, "bfloat16", dev) for x in si.rank_arrays(19, 16, 16 * 999, "bfloat16")])
+    recv = torch.empty_like(pa)
+    rows8, _ = coll.coll_plan("allreduce", "ring", N, count, "float32")
+    rows16, _ = coll.coll_plan("allreduce", "ring", 16, 16 * 30000, "float32")
+    cap = max(len(rows8), len(rows16))
+    sums = torch.full((cap,), -1, dtype=torch.int64, device=dev)
+    old_cache = coll.coll_get_option("cache_bytes")
+
+    def work():
+        coll.coll_set_checksums(sums)
+        coll.coll_allreduce(list(live), algo="ring")
+        coll.coll_set_checksums(None)
+        coll.coll_alltoall(list(pa), list(recv), algo="bruck")
+
+    try:
+        work()
+        torch.cuda.synchronize()
+        want, want_recv = live.clone(), recv.clone()
+        want_sums = sums[:len(rows8)].clone()
+        live.copy_(pristine)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                work()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+        # eager calls that replace or free what an unpinned call would use
+        coll.coll_set_option("cache_bytes", 0)
+        other = [torch.randn(N, 4096 * (i + 1) + 3, device=dev) for i in range(4)]
+        for t in other:
+            coll.coll_allreduce(list(t), algo="dbt")
+        coll.coll_set_checksums(sums)
+        coll.coll_set_option("col_tiles", 2)
+        coll.coll_allreduce(list(live), algo="ring")        # same schedule, new column tables
+        coll.coll_set_option("col_tiles", 0)
+        big = torch.randn(16, 16 * 30000, device=dev)
+        coll.coll_allreduce(list(big), algo="ring")         # same caller buffer, larger slot buffer
+        for i in range(17):                                   # more caller buffers than slot buffers kept
+            extra = torch.zeros(len(rows8), dtype=torch.int64, device=dev)
+            coll.coll_set_checksums(extra)
+            coll.coll_allreduce(list(other[0]), algo="ring")
+        coll.coll_set_checksums(None)
+        torch.cuda.synchronize()
+
+        for rep in range(3):
+            live.copy_(pristine)
+            recv.zero_()
+            sums.fill_(-1)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(live.view(torch.int32), want.view(torch.int32)), ("allreduce", rep)
+            assert torch.equal(recv.view(torch.int16), want_recv.view(torch.int16)), ("alltoall", rep)
+            assert torch.equal(sums[:len(rows8)], want_sums), ("checksums", rep)
+        coll.coll_check()
+    finally:
+        coll.coll_set_checksums(None)
+        coll.coll_set_option("cache_bytes", old_cache)
+        coll.coll_set_option("col_tiles", 0)

@@ -361,6 +361,26 @@ def test_batched_leaves_many_ranks(N, dtype, sigma):
             assert_parity(kind, algo, a, dtype, root=root, checksums=True)
 
 
+@pytest.mark.parametrize("N,dtype,op", [(33, "uint8", "max"), (33, "bfloat16", "min"), (64, "float32", "max"),
+                                         (48, "int32", "sum"), (20, "bfloat16", "sum")])
+def test_batched_leaves_out_of_place_and_ops(N, dtype, op):
+    """Batched programs out of place (every defined output stored, leaves read
+    from the send buffers) and with max / min, over rank counts whose trees
+    are uneven (33: halving-doubling folds one surplus rank, double binary
+    tree leaves are not complementary), against the oracle."""
+    import collective_communication_algorithms_amd as coll
+    g = np.random.default_rng(N + 7)
+    count = 3 * N * 64 + 5
+    a = si.rank_arrays(N + 100, N, count, dtype, sigma=0.02 if dtype == "bfloat16" else 1.0)
+    pow2 = (N & (N - 1)) == 0
+    cases = [("allreduce", "ring"), ("allreduce", "rhd"), ("allreduce", "dbt"), ("reduce", "binomial"),
+             ("reducescatter", "ring")] + ([("reducescatter", "rhd")] if pow2 else [])
+    for kind, algo in cases:
+        root = int(g.integers(0, N)) if kind == "reduce" else 0
+        assert_parity(kind, algo, a, dtype, op=op, root=root, inplace=False)
+        assert coll.coll_get_stats()["round_trips"] == 1, (kind, algo)
+
+
 @pytest.mark.parametrize("N", [3, 5, 6, 7, 12, 13])
 def test_non_power_of_two_rhd_dbt(N):
     """Halving-doubling with the surplus folded into a power-of-two core, and
