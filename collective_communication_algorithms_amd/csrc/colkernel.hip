@@ -147,9 +147,14 @@ struct Accs {
 };
 template <>
 struct Accs<0> {};
+// NA < 0: no accumulator file; each op's words are summed across the wave
+// per tile and lane k keeps op k's running total (any op count up to 64).
+template <>
+struct Accs<-1> {};
 
 // 16 bytes per lane and column; NL slots; NA checksum accumulators (0: no
-// checksums); NTM: nontemporal loads (NT_SRC) / stores (NT_DST); BT: programs
+// checksums; -1: per-tile wave sums, for programs of more ops than an
+// accumulator file holds); NTM: nontemporal loads (NT_SRC) / stores (NT_DST); BT: programs
 // may bring leaves in batches (the RELOAD path costs registers, so the other
 // variants leave it out).  Batched programs keep leaves in slots 0 .. 7 and
 // only partial results above, which are written once and read once per
@@ -189,6 +194,7 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
   const uint64_t s0 = wk.s0, s1 = wk.s1, xs = s0 & ~(UNIT - 1);
   Accs<NA> acc;
   if constexpr (NA > 0) acc.clear();
+  uint64_t mine = 0;  // NA < 0: lane k's running total of op k
   for (uint32_t t = 0; t < wk.ntiles; ++t) {
     const uint64_t x = wk.c0 + uint64_t(t) * TB + uint64_t(lane) * UNIT;
     const bool any = x < s1 && x + UNIT > s0;
@@ -264,6 +270,11 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
       if constexpr (NA > 0) {
         const uint32_t shift = uint32_t(__builtin_amdgcn_readlane(int(op_w1), int(k))) & 3u;
         if (any) acc.add(k, unit_words<DT>(val, x, s0, s1, full, shift));
+      } else if constexpr (NA < 0) {
+        const uint32_t shift = uint32_t(__builtin_amdgcn_readlane(int(op_w1), int(k))) & 3u;
+        const uint64_t w = any ? unit_words<DT>(val, x, s0, s1, full, shift) : 0;
+        const uint64_t tot = wave_sum(w);  // every lane takes part
+        if (lane == k) mine += tot;
       }
     }
     // Batched programs: every load of this tile has been consumed (each leaf
@@ -282,13 +293,14 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
       else if (any) store_part<DT>(base + x, val, x, s0, s1);
     }
   }
-  if constexpr (NA > 0) {
+  if constexpr (NA != 0) {
     // op k's wave total goes to lane k, which stores it in this work group's
     // own slot: no atomics, every slot written once per call
-    uint64_t mine = 0;
-    for (uint32_t k = 0; k < nop; ++k) {
-      const uint64_t tot = wave_sum(acc.get(k));
-      if (lane == k) mine = tot;
+    if constexpr (NA > 0) {
+      for (uint32_t k = 0; k < nop; ++k) {
+        const uint64_t tot = wave_sum(acc.get(k));
+        if (lane == k) mine = tot;
+      }
     }
     if (lane < nop) *gptr<uint64_t>(reinterpret_cast<char*>(a.partial + wk.part + lane)) = mine;
   }
@@ -340,8 +352,13 @@ ColFn col_fn_nt(bool nt) {
   return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT> : col_kernel<DT, OP, NL, NA, 0, BT>;
 }
 
+// accs: 0, 16 (8 slots), 32 (16 slots), or more: per-tile wave sums (batched
+// programs only)
 template <int DT, int OP, bool BT>
 ColFn col_fn_variant(int leaves, int accs, bool nt) {
+  if constexpr (BT) {
+    if (accs > 32) return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT>(nt) : col_fn_nt<DT, OP, 16, -1, BT>(nt);
+  }
   if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 8, 16, BT>(nt) : col_fn_nt<DT, OP, 8, 0, BT>(nt);
   return accs ? col_fn_nt<DT, OP, 16, 32, BT>(nt) : col_fn_nt<DT, OP, 16, 0, BT>(nt);
 }

@@ -32,7 +32,8 @@ uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz))
 // instruction issue (64-rank ReduceScatter bf16 x 256 MiB: Ring 10.6 ms,
 // halving-doubling 11.2 ms, where batches of 8 run them in 2.9 ms).
 const ColVariant kVariants[] = {{16, 8, 0, false}, {16, 8, 16, false}, {16, 16, 0, false}, {16, 16, 32, false},
-                                {16, 8, 0, true},  {16, 8, 16, true},  {16, 16, 0, true},  {16, 16, 32, true}};
+                                {16, 8, 0, true},  {16, 8, 16, true},  {16, 16, 0, true},  {16, 16, 32, true},
+                                {16, 8, 64, true}, {16, 16, 64, true}};
 
 
 // Register slots of the largest column-kernel variant.

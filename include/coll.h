@@ -196,9 +196,9 @@ coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nr
  * (hipMemcpyAsync on `stream`) and first waits for `stream`.  Calls that
  * overlap on one GPU (other streams or threads) race on the array.
  * Errors: as coll_allreduce; COLL_ERR_UNSUPPORTED when the column kernel does
- * not run the call (rank buffers not 16-byte aligned, or programs no kernel
- * variant holds: with row checksums, more than 32 ops, as Ring over 64 ranks
- * has); COLL_ERR_INVALID_ARG when its tables and partial
+ * not run the call (rank buffers not 16-byte aligned, or more than 64 ranks,
+ * whose programs no kernel variant holds); COLL_ERR_INVALID_ARG when its
+ * tables and partial
  * sums do not fit the array even with the fewest work groups (the message
  * says how many bytes they need).  Not in coll_get_stats' schedule cache. */
 #define COLL_NOALLOC_SCRATCH_BYTES (16u << 20)

@@ -343,9 +343,9 @@ def test_batched_leaves_many_ranks(N, dtype, sigma):
     """More ranks than the column kernel's 16 slots: its programs
     bring the leaves in batches of 8 and combine depth-first (the schedule's
     own combines and operand order, so floats stay bit-exact).  Reductions
-    over 17, 32 and 64 ranks against the oracle, in one round trip; and with
-    row checksums (the column kernel where the ops fit its 32 accumulators,
-    else the row kernel)."""
+    over 17, 32 and 64 ranks against the oracle, in one round trip, with and
+    without row checksums (programs over 32 ops sum each op's words across
+    the wave per tile instead of holding an accumulator per op)."""
     import collective_communication_algorithms_amd as coll
     pow2 = (N & (N - 1)) == 0
     g = np.random.default_rng(N)
@@ -359,6 +359,7 @@ def test_batched_leaves_many_ranks(N, dtype, sigma):
         assert coll.coll_get_stats()["round_trips"] == 1, (kind, algo)
         if dtype != "int32":
             assert_parity(kind, algo, a, dtype, root=root, checksums=True)
+            assert coll.coll_get_stats()["round_trips"] == 1, (kind, algo, "checksums")
 
 
 @pytest.mark.parametrize("N,dtype,op", [(33, "uint8", "max"), (33, "bfloat16", "min"), (64, "float32", "max"),

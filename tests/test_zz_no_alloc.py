@@ -99,10 +99,11 @@ def test_noalloc_allocates_nothing(gpu_device):
 
 @pytest.mark.parametrize("algo", ["ring", "rhd"])
 def test_noalloc_matches_allreduce_batched_leaves(gpu_device, algo):
-    """More ranks than register slots (leaves brought in batches): 32 then 16
-    ranks, checksums off for 64 ranks' 63-op programs and on for 32."""
-    for call, (N, count, cks) in enumerate(((64, 64 * 3000 + 17, False), (32, 32 * 500 + 9, True),
-                                            (16, 16 * 100 + 1, True))):
+    """More ranks than register slots (leaves brought in batches): 64 ranks
+    with and without row checksums (63-op programs: per-tile wave sums), then
+    32 and 16."""
+    for call, (N, count, cks) in enumerate(((64, 64 * 3000 + 17, False), (64, 64 * 1000 + 3, True),
+                                            (32, 32 * 500 + 9, True), (16, 16 * 100 + 1, True))):
         host = si.rank_arrays(60 + call, N, count, "float32")
         (ref, ref_sums), (got, got_sums) = _run_both(host, "float32", algo, True, cks)
         for i in range(N):
@@ -113,19 +114,13 @@ def test_noalloc_matches_allreduce_batched_leaves(gpu_device, algo):
 
 def test_noalloc_refuses_what_it_cannot_run(gpu_device):
     import torch
-    import collective_communication_algorithms_amd as coll
     from collective_communication_algorithms_amd import _lib
     dev = torch.device("cuda:0")
     # rank buffers off 16-byte alignment
     buf = torch.zeros((8, 1024 + 1), dtype=torch.float32, device=dev)
     st = _call("coll_allreduce_noalloc", [buf[i, 1:] for i in range(8)], None, "float32", "ring")
     assert st == _lib.COLL_ERR_UNSUPPORTED and b"16-byte" in _lib.load().coll_last_error()
-    # with row checksums, programs of more ops than accumulators (Ring over 64 ranks: 63 combines)
-    b = [torch.zeros(64 * 64, dtype=torch.float32, device=dev) for _ in range(64)]
-    sums = torch.zeros(64 * 127, dtype=torch.int64, device=dev)
-    coll.coll_set_checksums(sums)
-    try:
-        st = _call("coll_allreduce_noalloc", b, None, "float32", "ring")
-    finally:
-        coll.coll_set_checksums(None)
+    # more ranks than a program list holds (65)
+    b = [torch.zeros(65 * 64, dtype=torch.float32, device=dev) for _ in range(65)]
+    st = _call("coll_allreduce_noalloc", b, None, "float32", "ring")
     assert st == _lib.COLL_ERR_UNSUPPORTED and b"column kernel" in _lib.load().coll_last_error()
