@@ -501,20 +501,31 @@ coll_status_t upload(const std::vector<T>& v, T*& d) {
   return COLL_OK;
 }
 
-// Column kernel: tiles per work group.  Column spaces of 64 tiles per CU or
-// more: 4 with row checksums, whose partial sums are then four times fewer
-// for the fold to add, else 1 (a work group that ends after one tile never
-// waits for its stores).  Measured at 8 x 256 MiB fp32 Ring AllReduce, with /
-// without checksums, 1, 2, 4, 8, 16 tiles: 0.803 / 0.732, 0.748 / 0.746,
-// 0.733 / 0.769, 0.777 / 0.785, 0.852 / 0.815 ms.  Smaller column spaces: 1,
-// so that every compute unit gets work.
+// Column kernel: tiles per work group.  Column spaces under 64 tiles per CU:
+// 1, so that every compute unit gets work.  Larger ones without checksums: 1
+// (a work group that ends after one tile never waits for its stores).  With
+// row checksums more tiles make the partial sums fewer for the fold to add,
+// but fewer, longer work groups leave a tail: 2, and 4 from 1,024 tiles per
+// CU.  Measured on Ring AllReduce fp32 over 8 ranks, each call after a
+// restore of its inputs, in TB/s of 2NM with checksums, 2 / 4 tiles: 64 MiB
+// per rank 5.25 / 3.84, 128 MiB 5.69 / 5.55, 256 MiB 5.75 / 5.81; without, 1
+// / 2 tiles: 64 MiB 5.33 / 5.43, 128 MiB 5.79 / 5.61, 256 MiB 5.78 / 5.71.
 uint32_t auto_col_tiles(const ColPlan& p, uint32_t cus) {
   const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
   uint64_t tiles = 0;
   for (const ColSeg& sg : p.segs) tiles += (sg.s1 + tb - 1) / tb - sg.s0 / tb;
-  if (tiles < uint64_t(cus) * 64u) return 1;
-  return p.v.accs > 0 ? 4 : 1;
+  if (tiles < uint64_t(cus) * 64u || p.v.accs == 0) return 1;
+  return tiles >= uint64_t(cus) * 1024u ? 4 : 2;
 }
+
+// Column kernel: nontemporal loads and stores once the call's buffers exceed
+// twice the memory-side cache (a call reads and writes each byte once).
+// Below that, part of the inputs is still in the cache from whatever wrote
+// them.  Measured as above, ordinary / nontemporal, 1 tile without
+// checksums: 48 MiB per rank (384 MiB of buffers) 5.54 / 5.14 TB/s, 64 MiB
+// 5.46 / 5.33, 80 MiB 5.45 / 5.40, 96 MiB 5.26 / 5.45, 128 MiB 5.50 / 5.79,
+// 256 MiB 5.38 / 5.78.
+constexpr uint64_t COL_NT_BYTES = 2 * CACHE_RESIDENT_BYTES;
 
 // The column programs of a schedule for this call's checksum mode, compiled
 // and uploaded on first use, with work groups of `tiles` tiles.  out->plan.ok
@@ -818,8 +829,8 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     L.refs = cd->d_refs;
     L.v = cd->plan.v;
     L.grid = cd->nwork;
-    // nothing is read twice: past the memory-side cache every access streams
-    L.nt = opt_nt.load() < 0 ? ntmask != 0 : (ntmask & (NT_SRC | NT_DST)) != 0;
+    // nothing is read twice: past twice the memory-side cache every access streams
+    L.nt = opt_nt.load() < 0 ? footprint > COL_NT_BYTES : (ntmask & (NT_SRC | NT_DST)) != 0;
     if (L.grid) plan.push_back(L);
     moved = int64_t(cd->plan.moved_bytes);
     if (g_debug.load())
@@ -1141,8 +1152,7 @@ coll_status_t run_noalloc(void* const* send, void* const* recv, int N, size_t co
   a.partial = cks ? reinterpret_cast<uint64_t*>(b + cur.off_part) : nullptr;
   a.p = ptrs;
   const uint64_t footprint = uint64_t(N) * uint64_t(count) * uint64_t(sz) * (inplace ? 1u : 2u);
-  const uint32_t ntmask = opt_nt.load() < 0 ? auto_nt(footprint, false) : uint32_t(opt_nt.load());
-  const bool nt = opt_nt.load() < 0 ? ntmask != 0 : (ntmask & (NT_SRC | NT_DST)) != 0;
+  const bool nt = opt_nt.load() < 0 ? footprint > COL_NT_BYTES : (uint32_t(opt_nt.load()) & (NT_SRC | NT_DST)) != 0;
   const int dt = int(dtype) == COLL_INT32 ? DT_I32 : int(dtype) == COLL_UINT8 ? DT_U8
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
   const uint32_t grid = uint32_t(cur.tables.work.size());

@@ -300,17 +300,23 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  * COLL_OPT_MAX_GRID        cap on work groups per launch, up to 2^20 [0: automatic].
  * COLL_OPT_NONTEMPORAL     bit mask of nontemporal accesses: 1 source loads,
  *                          2 old-destination loads, 4 stores; -1: automatic
- *                          [-1]: none while all rank buffers together fit the
- *                          256 MiB memory-side cache, else source loads only
- *                          (AllToAll, and the row lists of reducing calls
- *                          that pass results between steps in registers:
- *                          source loads and stores).
+ *                          [-1]: in the row kernel none while all rank
+ *                          buffers together fit the 256 MiB memory-side
+ *                          cache, else source loads only (AllToAll, and the
+ *                          row lists of reducing calls that pass results
+ *                          between steps in registers: source loads and
+ *                          stores); in the column kernel, where every access
+ *                          is a load or a store of its own, none up to twice
+ *                          that size, else all.  Any mask with a bit of 1 or
+ *                          4 makes the column kernel's accesses nontemporal.
  * COLL_OPT_REVERSE         1: odd steps walk their columns backwards, so data
  *                          written last is read first [1]; 0: always forwards.
  * COLL_OPT_MODEL_ALPHA_NS  per-step cost used by COLL_ALGO_AUTO, in ns [1060].
  * COLL_OPT_MODEL_BETA_GBPS moved-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
  * COLL_OPT_COL_TILES       column kernel: tiles (64 lanes x 16 bytes) per
- *                          work group, up to 65535 [0: automatic, 1..8 by size].
+ *                          work group, up to 65535 [0: automatic: 1, or with
+ *                          row checksums over 64 tiles per CU 2, over 1,024
+ *                          tiles per CU 4].
  * COLL_OPT_TIMING          1: every call made outside graph capture records a
  *                          HIP event before its first data-moving kernel and
  *                          one after its last (not around the checksum
