@@ -455,30 +455,21 @@ __global__ __launch_bounds__(BLOCK_THREADS) void fold_sums_kernel(uint64_t* part
   if ((threadIdx.x & 63u) == 0) *gptr<uint64_t>(reinterpret_cast<char*>(out + r)) = t;
 }
 
-// Plain streams for the achievable-rate ceiling.  Each work group takes
-// CALIB_UNITS consecutive 4 KiB tiles (thread t: bytes [16t, 16t + 16) of
-// each), issues all their loads, then all their stores; loads and stores are
-// nontemporal.  Measured on MI355X for a 2 GiB copy: this blocked shape 6.17
-// TB/s (one tile per work group 6.16, two 5.99, eight 4.30 with 234 VGPRs);
-// grid-stride loops over 1,024-8,192 work groups 4.30-5.15 TB/s.
-constexpr int CALIB_UNITS = 4;
+// Plain streams for the achievable-rate ceiling: one-wave work groups, one
+// 16-byte unit per lane, nontemporal loads and stores, as the column kernel
+// runs.  Measured on MI355X for a 2 GiB copy, 64-lane work groups of one 1
+// KiB tile each: 6.71 TB/s; four tiles each 6.15; 256-lane work groups of
+// four 4 KiB tiles 5.77; 32 or 64 bytes per lane (two or four adjacent
+// 16-byte accesses) 3.7 and 1.4.
+constexpr int CALIB_THREADS = 64;
 
 template <bool ADD>
-__global__ __launch_bounds__(BLOCK_THREADS) void calib_kernel(char* dst, const char* a, const char* b, uint64_t units) {
-  const uint64_t base = uint64_t(blockIdx.x) * CALIB_UNITS * BLOCK_THREADS + threadIdx.x;
-  u32x4 x[CALIB_UNITS];
-#pragma unroll
-  for (int k = 0; k < CALIB_UNITS; ++k)
-    if (base + k * BLOCK_THREADS < units) x[k] = ld16<true>(a + (base + k * BLOCK_THREADS) * 16);
-  if constexpr (ADD) {
-#pragma unroll
-    for (int k = 0; k < CALIB_UNITS; ++k)
-      if (base + k * BLOCK_THREADS < units)
-        x[k] = combine16<DT_F32, OP_SUM>(x[k], ld16<true>(b + (base + k * BLOCK_THREADS) * 16));
-  }
-#pragma unroll
-  for (int k = 0; k < CALIB_UNITS; ++k)
-    if (base + k * BLOCK_THREADS < units) st16<true>(dst + (base + k * BLOCK_THREADS) * 16, x[k]);
+__global__ __launch_bounds__(CALIB_THREADS) void calib_kernel(char* dst, const char* a, const char* b, uint64_t units) {
+  const uint64_t u = uint64_t(blockIdx.x) * CALIB_THREADS + threadIdx.x;
+  if (u >= units) return;
+  u32x4 x = ld16<true>(a + u * 16);
+  if constexpr (ADD) x = combine16<DT_F32, OP_SUM>(x, ld16<true>(b + u * 16));
+  st16<true>(dst + u * 16, x);
 }
 
 // ---- host-side dispatch ---------------------------------------------------------------
@@ -623,15 +614,15 @@ hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hi
 
 hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, hipStream_t stream) {
   const uint64_t units = bytes / 16;
-  const uint64_t g = (units + uint64_t(CALIB_UNITS) * BLOCK_THREADS - 1) / (uint64_t(CALIB_UNITS) * BLOCK_THREADS);
+  const uint64_t g = (units + CALIB_THREADS - 1) / CALIB_THREADS;
   if (g == 0) return hipSuccess;
   if (g > 0x7fffffffu) return hipErrorInvalidValue;
   const uint32_t grid = uint32_t(g);
   if (b)
-    hipLaunchKernelGGL(calib_kernel<true>, dim3(grid), dim3(BLOCK_THREADS), 0, stream, reinterpret_cast<char*>(dst),
+    hipLaunchKernelGGL(calib_kernel<true>, dim3(grid), dim3(CALIB_THREADS), 0, stream, reinterpret_cast<char*>(dst),
                        reinterpret_cast<const char*>(a), reinterpret_cast<const char*>(b), units);
   else
-    hipLaunchKernelGGL(calib_kernel<false>, dim3(grid), dim3(BLOCK_THREADS), 0, stream, reinterpret_cast<char*>(dst),
+    hipLaunchKernelGGL(calib_kernel<false>, dim3(grid), dim3(CALIB_THREADS), 0, stream, reinterpret_cast<char*>(dst),
                        reinterpret_cast<const char*>(a), nullptr, units);
   return hipGetLastError();
 }
