@@ -152,10 +152,25 @@ struct ColDev {
   uint64_t code_bytes = 0, table_bytes = 0;  // device memory held
 };
 
+// The direct copy of a Pairwise AllToAll (copy_rows_kernel): its row table
+// and, for checksums, the fold's references (one per row: its work groups'
+// slots).
+struct CopyDev {
+  bool tried = false, ok = false;
+  bool pinned = false;          // used by a captured call: tables kept until coll_finalize
+  uint32_t nrows = 0, wgs_per_row = 0;
+  uint64_t row_bytes = 0;
+  CopyRow* d_rows = nullptr;
+  uint32_t* d_row_off = nullptr;
+  ColRef* d_refs = nullptr;
+  uint64_t bytes = 0;           // device memory held
+};
+
 struct Entry {
   Schedule sched;
   Bound bound;
   ColDev col[2];                // [checksums on]
+  CopyDev copy;
   bool pinned = false;          // used by a captured call: never evicted before coll_finalize
   std::vector<int8_t> multi;    // per phase: groups average two or more pieces per step (-1: not known yet)
   int dev = 0;
@@ -241,11 +256,28 @@ bool col_mode() { return opt_exec.load() == 0; }
 // schedule's bytes less, in every row phase whose lists the forwarding variant
 // runs, the operands it takes from registers and the stores it skips (only
 // large column spaces get group-major lists, so only they build lists here).
+// Whether every row of an AllToAll reads the send buffers and writes the
+// receive buffers (no staged step), all rows of one length, a multiple of 16
+// bytes, and the direct copy's grid fits: the Pairwise schedule.  Its rows
+// are then independent and run in one launch of copy_rows_kernel.
+bool copy_eligible(const Schedule& s, int sz) {
+  if (s.kind != COLL_K_ALLTOALL || s.rows.empty()) return false;
+  const int64_t n = s.rows[0].n;
+  for (const Step& st : s.steps)
+    if (st.staged) return false;
+  for (const Row& r : s.rows)
+    if (!r.from_send || r.reduce || r.n != n) return false;
+  const uint64_t row_bytes = uint64_t(n) * uint64_t(sz);
+  if (row_bytes == 0 || row_bytes % 16u) return false;
+  return (row_bytes + 1023u) / 1024u * s.rows.size() <= 0x7fffffffu;
+}
+
 PlannedCost planned_cost(const Schedule& s, int sz, uint32_t cus) {
   if (col_mode() && s.kind != COLL_K_ALLTOALL) {
     const ColPlan cp = compile_colplan(s, sz, true, t_sums != nullptr);
     if (cp.ok) return PlannedCost{1, int64_t(cp.moved_bytes)};
   }
+  if (col_mode() && copy_eligible(s, sz)) return PlannedCost{1, count_schedule(s, sz).hbm_bytes};
   const Bound b = bind_schedule(s, sz, true);
   int64_t moved = b.counts.hbm_bytes;
   const bool a2a = s.kind == COLL_K_ALLTOALL;
@@ -312,6 +344,13 @@ void free_col(ColDev& c) {
   c = ColDev{};
 }
 
+void free_copy(CopyDev& c) {
+  release(c.d_rows, c.pinned);
+  release(c.d_row_off, c.pinned);
+  release(c.d_refs, c.pinned);
+  c = CopyDev{};
+}
+
 void free_entry(Entry& e) {
   release(e.d_items, e.pinned);
   release(e.d_steps, e.pinned);
@@ -323,6 +362,8 @@ void free_entry(Entry& e) {
     c.pinned = c.pinned || e.pinned;
     free_col(c);
   }
+  e.copy.pinned = e.copy.pinned || e.pinned;
+  free_copy(e.copy);
   e.lists.clear();
   e.d_items = nullptr;
   e.d_steps = nullptr;
@@ -591,6 +632,54 @@ coll_status_t get_col(Entry& e, const Key& k, bool cks, uint32_t cus, ColDev*& o
   return trim_cache(&e);
 }
 
+// The direct-copy tables of an AllToAll whose rows all read the send
+// buffers and write distinct blocks of the receive buffers, all of one
+// length that is a multiple of 16 bytes (Pairwise); built and uploaded on
+// first use.  out->ok false: the row kernel runs the schedule.
+coll_status_t get_copy(Entry& e, const Key& k, CopyDev*& out) {
+  CopyDev& c = e.copy;
+  out = &c;
+  if (c.tried) return COLL_OK;
+  c.tried = true;
+  const Schedule& s = e.sched;
+  if (!copy_eligible(s, k.sz)) return COLL_OK;
+  const uint64_t row_bytes = uint64_t(s.rows[0].n) * uint64_t(k.sz);
+  const uint64_t wgs = (row_bytes + 1023u) / 1024u;
+  std::vector<CopyRow> rows(s.rows.size());
+  std::vector<uint32_t> row_off(s.rows.size() + 1);
+  std::vector<ColRef> refs(s.rows.size());
+  for (size_t i = 0; i < s.rows.size(); ++i) {
+    const Row& r = s.rows[i];
+    rows[i] = CopyRow{uint32_t(r.src), uint32_t(r.dst), uint64_t(r.src_off) * uint64_t(k.sz),
+                      uint64_t(r.dst_off) * uint64_t(k.sz)};
+    row_off[i] = uint32_t(i);
+    refs[i] = ColRef{uint32_t(i * wgs), uint32_t(wgs), 1u, 0u};
+  }
+  row_off[s.rows.size()] = uint32_t(s.rows.size());
+  CopyRow* dr = nullptr;
+  uint32_t* dro = nullptr;
+  ColRef* drf = nullptr;
+  coll_status_t st = upload(rows, dr);
+  if (st == COLL_OK) st = upload(row_off, dro);
+  if (st == COLL_OK) st = upload(refs, drf);
+  if (st != COLL_OK) {
+    if (dr) (void)hipFree(dr);
+    if (dro) (void)hipFree(dro);
+    return st;
+  }
+  c.d_rows = dr;
+  c.d_row_off = dro;
+  c.d_refs = drf;
+  c.nrows = uint32_t(s.rows.size());
+  c.wgs_per_row = uint32_t(wgs);
+  c.row_bytes = row_bytes;
+  c.ok = true;
+  c.bytes = rows.size() * sizeof(CopyRow) + row_off.size() * sizeof(uint32_t) + refs.size() * sizeof(ColRef);
+  e.bytes += c.bytes;
+  g_cache_bytes += c.bytes;
+  return trim_cache(&e);
+}
+
 coll_status_t device_info(int dev, DevInfo*& out) {
   auto it = g_dev.find(dev);
   if (it == g_dev.end()) {
@@ -732,7 +821,7 @@ coll_status_t check_call(coll_kind_t kind, void* const* send, void* const* recv,
 
 // One kernel launch of a call, planned before anything is enqueued.
 struct Launch {
-  enum Kind { COL, ROWS, PERM } kind = ROWS;
+  enum Kind { COL, COPY, ROWS, PERM } kind = ROWS;
   // COL
   const ColWork* work = nullptr;
   const ColInstr* code = nullptr;
@@ -815,12 +904,27 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   std::string dbg;    // launch shapes, for COLL_DEBUG
   int64_t moved = b.counts.hbm_bytes;
   ColDev* cd = nullptr;
+  CopyDev* xd = nullptr;
   if (col_mode() && bases16 && kind != COLL_K_ALLTOALL) {
     st = get_col(*e, k, cks, uint32_t(di->cus), cd);
     if (st != COLL_OK) return st;
     if (!cd->plan.ok) cd = nullptr;
   }
-  if (cd) {
+  if (col_mode() && bases16 && kind == COLL_K_ALLTOALL) {
+    st = get_copy(*e, k, xd);
+    if (st != COLL_OK) return st;
+    if (!xd->ok) xd = nullptr;
+  }
+  if (xd) {
+    Launch L;
+    L.kind = Launch::COPY;
+    L.nt = ntmask != 0;
+    L.grid = xd->nrows * xd->wgs_per_row;
+    if (L.grid) plan.push_back(L);
+    if (g_debug.load())
+      dbg += " | copy rows: " + std::to_string(xd->nrows) + " rows of " + std::to_string(xd->row_bytes) + " bytes, grid " +
+             std::to_string(L.grid) + (L.nt ? " nontemporal" : "");
+  } else if (cd) {
     Launch L;
     L.kind = Launch::COL;
     L.work = cd->d_work;
@@ -916,8 +1020,9 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   if (cks) {
     // the row kernels' SUM_LANES slots per row, or the column kernel's partial
     // sums and the fold's slices
-    const size_t slots = cd ? size_t(cd->partials) + std::max<size_t>(size_t(b.nrows), 1) * COL_FOLD_SLICES
-                            : std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES;
+    const size_t slots = cd   ? size_t(cd->partials) + std::max<size_t>(size_t(b.nrows), 1) * COL_FOLD_SLICES
+                         : xd ? size_t(xd->nrows) * xd->wgs_per_row + std::max<size_t>(size_t(b.nrows), 1) * COL_FOLD_SLICES
+                              : std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES;
     st = sum_scratch(dev, t_sums, slots, scratch);
     if (st != COLL_OK) return st;
     partial = scratch->d;
@@ -927,11 +1032,12 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     // reads until coll_finalize
     e->pinned = true;
     if (cd) cd->pinned = true;
+    if (xd) xd->pinned = true;
     if (scratch) scratch->pinned = true;
   }
 
   // ---- enqueue
-  if (cks && !cd) {
+  if (cks && !cd && !xd) {
     // the row kernels add into zeroed slots.  A call being captured into a
     // graph runs later, once per replay: it clears the slots itself and
     // leaves the flag to the calls that run now
@@ -966,6 +1072,15 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.p = ptrs;
       he = launch_col(a, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.v.batched, L.nt, L.grid, stream);
       if (he != hipSuccess) return hip_fail(he, "column kernel launch");
+    } else if (L.kind == Launch::COPY) {
+      CopyRowsArgs a{};
+      a.rows = xd->d_rows;
+      a.partial = partial;
+      a.p = ptrs;
+      a.row_bytes = xd->row_bytes;
+      a.wgs_per_row = xd->wgs_per_row;
+      he = launch_copy_rows(a, xd->nrows, cks, L.nt, stream);
+      if (he != hipSuccess) return hip_fail(he, "copy kernel launch");
     } else if (L.kind == Launch::ROWS) {
       RowsArgs a{};
       a.list = L.list;
@@ -1000,11 +1115,12 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     te->recorded = true;
     t_last_timed = te;
   }
-  if (cks && cd) {
+  if (cks && (cd || xd)) {
     // every partial slot was written by this call: nothing to clear, but the
     // slots are no longer zero for a row-kernel call
-    he = launch_col_fold(cd->d_refs, cd->d_row_off, partial, partial + cd->partials, t_sums, uint64_t(b.nrows),
-                         stream);
+    const uint64_t nslots = cd ? cd->partials : uint64_t(xd->nrows) * xd->wgs_per_row;
+    he = launch_col_fold(cd ? cd->d_refs : xd->d_refs, cd ? cd->d_row_off : xd->d_row_off, partial, partial + nslots,
+                         t_sums, uint64_t(b.nrows), stream);
     if (he != hipSuccess) return hip_fail(he, "checksum fold");
     if (!capturing) scratch->clean = false;
   } else if (cks) {
@@ -1018,7 +1134,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
                  (long long)b.counts.steps, (long long)b.counts.rows, (long long)b.counts.hbm_bytes, dbg.c_str());
   t_last = b.counts;
   t_last.moved_bytes = moved;
-  t_last.round_trips = cd ? 1 : b.counts.steps;
+  t_last.round_trips = (cd || xd) ? 1 : b.counts.steps;
   return COLL_OK;
 }
 

@@ -181,6 +181,23 @@ constexpr uint32_t COL_FOLD_SLICES = 32;
 constexpr int COL_THREADS = 64;
 static_assert(COL_THREADS <= COLL_MAX_RANKS, "lane r reads rank r's pointers");
 
+// Copy rows that depend on nothing but the send buffers (Pairwise AllToAll:
+// every block read from its sender's send buffer, written to its receiver's
+// receive buffer), all of one length: row r copies row_bytes from rank src's
+// send buffer at src_off to rank dst's receive buffer at dst_off (bytes).
+struct CopyRow {                      // 24 bytes
+  uint32_t src, dst;
+  uint64_t src_off, dst_off;
+};
+
+struct CopyRowsArgs {
+  const CopyRow* rows;
+  uint64_t* partial;                  // checksums: one slot per work group; else nullptr
+  RankPtrs p;
+  uint64_t row_bytes;                 // a multiple of 16
+  uint32_t wgs_per_row;               // work group w copies 1 KiB tile w % wgs_per_row of row w / wgs_per_row
+};
+
 struct PermArgs {                     // staged permutation kernel (AllToAll)
   const DevItem* items;
   const DevStep* steps;

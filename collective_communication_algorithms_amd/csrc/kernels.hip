@@ -455,6 +455,32 @@ __global__ __launch_bounds__(BLOCK_THREADS) void fold_sums_kernel(uint64_t* part
   if ((threadIdx.x & 63u) == 0) *gptr<uint64_t>(reinterpret_cast<char*>(out + r)) = t;
 }
 
+// Independent copy rows (Pairwise AllToAll) in the shape of the plain copy
+// stream: a one-wave work group copies one 1 KiB tile of one row, 16 bytes
+// per lane, nontemporal when NT.  Nothing is read twice, so every block is
+// read once and written once.  With checksums each work group stores the u64
+// sum of the words it wrote to a slot of its own; the column kernel's fold
+// adds a row's slots.
+template <bool CKS, bool NT>
+__global__ __launch_bounds__(64) void copy_rows_kernel(const CopyRowsArgs a) {
+  const uint32_t r = blockIdx.x / a.wgs_per_row, q = blockIdx.x % a.wgs_per_row;
+  const CopyRow row = cload(a.rows + r);
+  const uint64_t off = uint64_t(q) * 1024u + uint64_t(threadIdx.x) * 16u;
+  // lanes past the row's end (its last tile) copy nothing; they load the
+  // row's last unit so that the load needs no branch
+  const bool in = off < a.row_bytes;
+  const uint64_t offl = in ? off : a.row_bytes - 16u;
+  const char* src = reinterpret_cast<const char*>(a.p.send[row.src]) + row.src_off;
+  char* dst = reinterpret_cast<char*>(a.p.recv[row.dst]) + row.dst_off;
+  const u32x4 v = ld16<NT>(src + offl);
+  if (in) st16<NT>(dst + off, v);
+  if constexpr (CKS) {
+    // rows start at multiples of 16 bytes: no rotation
+    const uint64_t t = wave_sum(in ? words16(v, 0) : 0);
+    if (threadIdx.x == 0) *gptr<uint64_t>(reinterpret_cast<char*>(a.partial + blockIdx.x)) = t;
+  }
+}
+
 // Plain streams for the achievable-rate ceiling: one-wave work groups, one
 // 16-byte unit per lane, nontemporal loads and stores, as the column kernel
 // runs.  Measured on MI355X for a 2 GiB copy, 64-lane work groups of one 1
@@ -609,6 +635,17 @@ hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hi
   const uint64_t rows_per_block = BLOCK_THREADS / 64;
   const uint32_t grid = uint32_t((nrows + rows_per_block - 1) / rows_per_block);
   hipLaunchKernelGGL(fold_sums_kernel, dim3(grid), dim3(BLOCK_THREADS), 0, stream, partial, out, nrows);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const CopyRowsArgs& a, uint64_t nrows, bool cks, bool nt, hipStream_t stream) {
+  const uint64_t g = nrows * uint64_t(a.wgs_per_row);
+  if (g == 0) return hipSuccess;
+  if (g > 0x7fffffffu || a.row_bytes % 16u) return hipErrorInvalidValue;
+  const uint32_t grid = uint32_t(g);
+  auto fn = cks ? (nt ? copy_rows_kernel<true, true> : copy_rows_kernel<true, false>)
+                : (nt ? copy_rows_kernel<false, true> : copy_rows_kernel<false, false>);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

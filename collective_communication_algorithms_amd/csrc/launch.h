@@ -13,6 +13,9 @@ hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t 
                        uint32_t grid, hipStream_t stream);
 hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_t grid, hipStream_t stream);
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream);
+// nrows rows of a.row_bytes (a multiple of 16), a.wgs_per_row 1 KiB tiles each;
+// with cks one partial checksum slot per work group
+hipError_t launch_copy_rows(const CopyRowsArgs& a, uint64_t nrows, bool cks, bool nt, hipStream_t stream);
 // out[r] = the u64 wrap-sum of partial[r * SUM_LANES .. r * SUM_LANES + SUM_LANES), r < nrows;
 // the slots read are set back to zero
 hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hipStream_t stream);

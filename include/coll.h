@@ -179,7 +179,9 @@ coll_status_t coll_reduce(void* const* sendbufs, void* const* recvbufs, int nran
  * local rotations), RING (eq:model-algo-a2a-ring: N-1 rounds between
  * neighbours i -> i+1; round t forwards the N-t blocks still in transit, so
  * each link carries (N-1)M/2 bytes in all, against the printed formula's
- * (N-1)M/N). */
+ * (N-1)M/N).  Pairwise rounds read only the send buffers, so with blocks of
+ * a multiple of 16 bytes on 16-byte aligned buffers they run as one direct
+ * copy of every block (one launch, coll_get_stats().round_trips 1). */
 coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                             void* stream);
@@ -272,7 +274,9 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  * COLL_OPT_EXEC            0: automatic [0]: every collective but AllToAll, on
  *                          16-byte aligned buffers, runs in the column kernel
  *                          (its schedule compiled per column segment, see
- *                          above); where that does not apply, one row-kernel
+ *                          above), and a Pairwise AllToAll whose blocks are
+ *                          multiples of 16 bytes in one direct copy; where
+ *                          neither applies, one row-kernel
  *                          launch runs every step of the call (each work
  *                          group owns fixed columns, so the steps need no
  *                          synchronisation between work groups).

@@ -21,20 +21,24 @@ def test_captured_collectives_replay_exactly(gpu_device):
     pu = torch.stack([si.host_to_tensor(x, "uint8", gpu_device) for x in u])
     live, lu = pristine.clone(), pu.clone()
     recv = torch.empty_like(pristine)
+    ps = list(pristine[:, :N * 20000])   # 80,000-byte blocks: the direct copy path
+    recv2 = torch.empty((N, N * 20000), dtype=torch.float32, device=gpu_device)
 
     def work():
         coll.coll_allreduce(list(live), algo="ring")
         coll.coll_allreduce(list(live), algo="dbt", op="max")
         coll.coll_broadcast(list(lu), algo="bidir_ring", root=5, chunks=3)
         coll.coll_alltoall(list(pristine), list(recv), algo="bruck")
+        coll.coll_alltoall(ps, list(recv2), algo="pairwise")
 
     # eager reference (also builds and caches every schedule before capture)
     work()
     torch.cuda.synchronize()
-    want = (live.clone(), lu.clone(), recv.clone())
+    want = (live.clone(), lu.clone(), recv.clone(), recv2.clone())
     live.copy_(pristine)
     lu.copy_(pu)
     recv.zero_()
+    recv2.zero_()
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
@@ -49,10 +53,12 @@ def test_captured_collectives_replay_exactly(gpu_device):
         live.copy_(pristine)          # eager work between replays
         lu.copy_(pu)
         recv.zero_()
+        recv2.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for got, w, name in ((live, want[0], "allreduce"), (lu, want[1], "broadcast"), (recv, want[2], "alltoall")):
+        for got, w, name in ((live, want[0], "allreduce"), (lu, want[1], "broadcast"), (recv, want[2], "alltoall"),
+                             (recv2, want[3], "alltoall pairwise")):
             assert torch.equal(got.view(torch.uint8), w.view(torch.uint8)), (rep, name)
     coll.coll_check()
 
@@ -106,7 +112,8 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
     shrunk to nothing (every unpinned schedule evicted), new column tables for
     the same schedule (another tile count), the checksum slot buffer of the
     same caller buffer grown by a larger schedule, and more than 16 caller
-    checksum buffers (slot buffers evicted).  Replays must still give the
+    checksum buffers (slot buffers evicted); a checksummed Pairwise AllToAll
+    run as one direct copy beside them.  Replays must still give the
     eager results and checksums bit for bit."""
     import torch
     import collective_communication_algorithms_amd as coll
@@ -118,6 +125,11 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
     # a row-kernel call captured beside the column-kernel one: AllToAll
     pa = torch.stack([si.host_to_tensor(x, "bfloat16", dev) for x in si.rank_arrays(19, 16, 16 * 999, "bfloat16")])
     recv = torch.empty_like(pa)
+    # and a checksummed Pairwise AllToAll that runs as one direct copy (2,000-byte blocks)
+    pd = torch.stack([si.host_to_tensor(x, "bfloat16", dev) for x in si.rank_arrays(20, 16, 16 * 1000, "bfloat16")])
+    recv_d = torch.empty_like(pd)
+    rows_d, _ = coll.coll_plan("alltoall", "pairwise", 16, 16 * 1000, "bfloat16")
+    sums_d = torch.full((len(rows_d),), -1, dtype=torch.int64, device=dev)
     rows8, _ = coll.coll_plan("allreduce", "ring", N, count, "float32")
     rows16, _ = coll.coll_plan("allreduce", "ring", 16, 16 * 30000, "float32")
     cap = max(len(rows8), len(rows16))
@@ -129,12 +141,17 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
         coll.coll_allreduce(list(live), algo="ring")
         coll.coll_set_checksums(None)
         coll.coll_alltoall(list(pa), list(recv), algo="bruck")
+        coll.coll_set_checksums(sums_d)
+        coll.coll_alltoall(list(pd), list(recv_d), algo="pairwise")
+        coll.coll_set_checksums(None)
 
     try:
         work()
         torch.cuda.synchronize()
         want, want_recv = live.clone(), recv.clone()
         want_sums = sums[:len(rows8)].clone()
+        want_d, want_sums_d = recv_d.clone(), sums_d.clone()
+        assert coll.coll_get_stats()["round_trips"] == 1
         live.copy_(pristine)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -150,6 +167,7 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
         other = [torch.randn(N, 4096 * (i + 1) + 3, device=dev) for i in range(4)]
         for t in other:
             coll.coll_allreduce(list(t), algo="dbt")
+            coll.coll_alltoall(list(t[:, :4096]), list(torch.empty_like(t[:, :4096])), algo="pairwise")
         coll.coll_set_checksums(sums)
         coll.coll_set_option("col_tiles", 2)
         coll.coll_allreduce(list(live), algo="ring")        # same schedule, new column tables
@@ -166,13 +184,17 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
         for rep in range(3):
             live.copy_(pristine)
             recv.zero_()
+            recv_d.zero_()
             sums.fill_(-1)
+            sums_d.fill_(-1)
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(live.view(torch.int32), want.view(torch.int32)), ("allreduce", rep)
             assert torch.equal(recv.view(torch.int16), want_recv.view(torch.int16)), ("alltoall", rep)
             assert torch.equal(sums[:len(rows8)], want_sums), ("checksums", rep)
+            assert torch.equal(recv_d.view(torch.int16), want_d.view(torch.int16)), ("pairwise", rep)
+            assert torch.equal(sums_d, want_sums_d), ("pairwise checksums", rep)
         coll.coll_check()
     finally:
         coll.coll_set_checksums(None)

@@ -382,6 +382,27 @@ def test_batched_leaves_out_of_place_and_ops(N, dtype, op):
         assert coll.coll_get_stats()["round_trips"] == 1, (kind, algo)
 
 
+@pytest.mark.parametrize("N,B,dtype", [(32, 512, "bfloat16"), (8, 4104, "bfloat16"), (5, 1000, "float32"),
+                                       (16, 32, "uint8"), (3, 7, "int32"), (12, 33, "bfloat16")])
+def test_pairwise_alltoall_direct_copy(N, B, dtype):
+    """Pairwise AllToAll: every block is read from its sender's send buffer and
+    written to its receiver's receive buffer, so the rows run in one launch
+    of the copy kernel (one round trip) when a block is a multiple of 16
+    bytes, the row kernel otherwise (a round trip per round) and under
+    COLL_OPT_EXEC 2.  Bit-exact against the oracle with row checksums, blocks
+    that end inside a 1 KiB tile included."""
+    import collective_communication_algorithms_amd as coll
+    a = si.rank_arrays(N + 200, N, N * B, dtype)
+    direct = (B * si.ITEMSIZE[dtype]) % 16 == 0
+    assert_parity("alltoall", "pairwise", a, dtype, checksums=True)
+    st = coll.coll_get_stats()
+    assert st["round_trips"] == (1 if direct else N - 1), st
+    assert st["moved_bytes"] == 2 * N * N * B * si.ITEMSIZE[dtype]
+    coll.coll_set_option("exec", 2)
+    assert_parity("alltoall", "pairwise", a, dtype, checksums=True)
+    assert coll.coll_get_stats()["round_trips"] == N - 1
+
+
 @pytest.mark.parametrize("N", [3, 5, 6, 7, 12, 13])
 def test_non_power_of_two_rhd_dbt(N):
     """Halving-doubling with the surplus folded into a power-of-two core, and
@@ -477,24 +498,27 @@ def test_coll_check_after_calls():
 def test_debug_lines(gpu_device):
     """COLL_DEBUG=1 prints one line per call: the collective, the resolved
     algorithm, the schedule's counts and each launch's shape (the column
-    kernel's segments and grid, or the row and permutation kernels' launches)."""
+    kernel's segments and grid, the direct copy of a Pairwise AllToAll, or the
+    row and permutation kernels' launches)."""
     import os
     import subprocess
     import sys
     code = ("import torch, collective_communication_algorithms_amd as c; "
             "t = [torch.ones(1 << 16, device='cuda:0') for _ in range(8)]; "
             "c.coll_allreduce(t, algo='auto'); c.coll_set_option('exec', 2); c.coll_allreduce(t, algo='ring'); "
-            "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); "
+            "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); c.coll_set_option('exec', 0); "
+            "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='pairwise'); "
             "torch.cuda.synchronize(); print(float(t[0][0]))")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=120,
                        env=dict(os.environ, COLL_DEBUG="1"))
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stderr.splitlines() if ln.startswith("coll: ")]
-    assert len(lines) == 3, r.stderr[-2000:]
+    assert len(lines) == 4, r.stderr[-2000:]
     assert lines[0].startswith("coll: allreduce algo ") and "algo auto" not in lines[0] and "| columns:" in lines[0]
     assert lines[1].startswith("coll: allreduce algo ring") and "| rows" in lines[1]
     assert lines[2].startswith("coll: alltoall algo bruck") and "| perm" in lines[2]
+    assert lines[3].startswith("coll: alltoall algo pairwise") and "| copy rows:" in lines[3]
     assert r.stdout.strip() == "64.0"
 
 
