@@ -152,11 +152,12 @@ struct ColDev {
   uint64_t code_bytes = 0, table_bytes = 0;  // device memory held
 };
 
-// The direct copy of a Pairwise AllToAll (copy_rows_kernel): its row table
-// and, for checksums, the fold's references (one per row: its work groups'
-// slots).
+// The direct copy of an AllToAll's leading independent rows
+// (copy_rows_kernel): its row table and, for checksums, the fold's
+// references (one per row: its work groups' slots).
 struct CopyDev {
   bool tried = false, ok = false;
+  bool whole = false;           // every row of the schedule (Pairwise); else the rows of phase 0
   bool pinned = false;          // used by a captured call: tables kept until coll_finalize
   uint32_t nrows = 0, wgs_per_row = 0;
   uint64_t row_bytes = 0;
@@ -256,20 +257,29 @@ bool col_mode() { return opt_exec.load() == 0; }
 // schedule's bytes less, in every row phase whose lists the forwarding variant
 // runs, the operands it takes from registers and the stores it skips (only
 // large column spaces get group-major lists, so only they build lists here).
-// Whether every row of an AllToAll reads the send buffers and writes the
-// receive buffers (no staged step), all rows of one length, a multiple of 16
-// bytes, and the direct copy's grid fits: the Pairwise schedule.  Its rows
-// are then independent and run in one launch of copy_rows_kernel.
-bool copy_eligible(const Schedule& s, int sz) {
-  if (s.kind != COLL_K_ALLTOALL || s.rows.empty()) return false;
+// The rows of an AllToAll's steps before its first staged step, when every
+// one of them reads the send buffers and writes the receive buffers, all of
+// one length, a multiple of 16 bytes, and the direct copy's grid fits: they
+// are then independent and run in one launch of copy_rows_kernel.  That is
+// every row of the Pairwise schedule, and the first rotation of Bruck's and
+// of the Ring AllToAll (the rounds after it run in the permutation kernel).
+// 0: none.
+size_t copy_prefix_rows(const Schedule& s, int sz) {
+  if (s.kind != COLL_K_ALLTOALL || s.rows.empty()) return 0;
+  size_t nrows = 0;
+  for (const Step& st : s.steps) {
+    if (st.staged) break;
+    nrows = size_t(st.first + st.nrows);
+  }
+  if (nrows == 0) return 0;
   const int64_t n = s.rows[0].n;
-  for (const Step& st : s.steps)
-    if (st.staged) return false;
-  for (const Row& r : s.rows)
-    if (!r.from_send || r.reduce || r.n != n) return false;
+  for (size_t i = 0; i < nrows; ++i) {
+    const Row& r = s.rows[i];
+    if (!r.from_send || r.reduce || r.n != n) return 0;
+  }
   const uint64_t row_bytes = uint64_t(n) * uint64_t(sz);
-  if (row_bytes == 0 || row_bytes % 16u) return false;
-  return (row_bytes + 1023u) / 1024u * s.rows.size() <= 0x7fffffffu;
+  if (row_bytes == 0 || row_bytes % 16u) return 0;
+  return (row_bytes + 1023u) / 1024u * nrows <= 0x7fffffffu ? nrows : 0;
 }
 
 PlannedCost planned_cost(const Schedule& s, int sz, uint32_t cus) {
@@ -277,7 +287,7 @@ PlannedCost planned_cost(const Schedule& s, int sz, uint32_t cus) {
     const ColPlan cp = compile_colplan(s, sz, true, t_sums != nullptr);
     if (cp.ok) return PlannedCost{1, int64_t(cp.moved_bytes)};
   }
-  if (col_mode() && copy_eligible(s, sz)) return PlannedCost{1, count_schedule(s, sz).hbm_bytes};
+  if (col_mode() && copy_prefix_rows(s, sz) == s.rows.size()) return PlannedCost{1, count_schedule(s, sz).hbm_bytes};
   const Bound b = bind_schedule(s, sz, true);
   int64_t moved = b.counts.hbm_bytes;
   const bool a2a = s.kind == COLL_K_ALLTOALL;
@@ -632,30 +642,41 @@ coll_status_t get_col(Entry& e, const Key& k, bool cks, uint32_t cus, ColDev*& o
   return trim_cache(&e);
 }
 
-// The direct-copy tables of an AllToAll whose rows all read the send
-// buffers and write distinct blocks of the receive buffers, all of one
-// length that is a multiple of 16 bytes (Pairwise); built and uploaded on
-// first use.  out->ok false: the row kernel runs the schedule.
+// The direct-copy tables of an AllToAll's leading independent rows
+// (copy_prefix_rows); built and uploaded on first use.  They replace the
+// schedule's first phase, which must cover exactly those rows' steps.
+// out->ok false: the row kernel runs them.
 coll_status_t get_copy(Entry& e, const Key& k, CopyDev*& out) {
   CopyDev& c = e.copy;
   out = &c;
   if (c.tried) return COLL_OK;
   c.tried = true;
   const Schedule& s = e.sched;
-  if (!copy_eligible(s, k.sz)) return COLL_OK;
+  const size_t n0 = copy_prefix_rows(s, k.sz);
+  if (n0 == 0) return COLL_OK;
+  const bool whole = n0 == s.rows.size();
+  if (!whole) {
+    // the rows kernel's first phase is these rows' steps, the rest staged
+    const Bound& b = e.bound;
+    if (b.phases.size() != 2 || b.phases[0].kind != Phase::ROWS || b.phases[1].kind != Phase::PERM) return COLL_OK;
+    const uint32_t s1 = b.phases[0].s1;
+    if (b.phases[0].s0 != 0 || s1 == 0 || s1 > s.steps.size() ||
+        size_t(s.steps[s1 - 1].first + s.steps[s1 - 1].nrows) != n0)
+      return COLL_OK;
+  }
   const uint64_t row_bytes = uint64_t(s.rows[0].n) * uint64_t(k.sz);
   const uint64_t wgs = (row_bytes + 1023u) / 1024u;
-  std::vector<CopyRow> rows(s.rows.size());
-  std::vector<uint32_t> row_off(s.rows.size() + 1);
-  std::vector<ColRef> refs(s.rows.size());
-  for (size_t i = 0; i < s.rows.size(); ++i) {
+  std::vector<CopyRow> rows(n0);
+  std::vector<uint32_t> row_off(n0 + 1);
+  std::vector<ColRef> refs(n0);
+  for (size_t i = 0; i < n0; ++i) {
     const Row& r = s.rows[i];
     rows[i] = CopyRow{uint32_t(r.src), uint32_t(r.dst), uint64_t(r.src_off) * uint64_t(k.sz),
                       uint64_t(r.dst_off) * uint64_t(k.sz)};
     row_off[i] = uint32_t(i);
     refs[i] = ColRef{uint32_t(i * wgs), uint32_t(wgs), 1u, 0u};
   }
-  row_off[s.rows.size()] = uint32_t(s.rows.size());
+  row_off[n0] = uint32_t(n0);
   CopyRow* dr = nullptr;
   uint32_t* dro = nullptr;
   ColRef* drf = nullptr;
@@ -670,7 +691,8 @@ coll_status_t get_copy(Entry& e, const Key& k, CopyDev*& out) {
   c.d_rows = dr;
   c.d_row_off = dro;
   c.d_refs = drf;
-  c.nrows = uint32_t(s.rows.size());
+  c.nrows = uint32_t(n0);
+  c.whole = whole;
   c.wgs_per_row = uint32_t(wgs);
   c.row_bytes = row_bytes;
   c.ok = true;
@@ -701,12 +723,12 @@ int occupancy_rows(int dev, int dt, int op, bool cks, uint32_t nt) {
   return n;
 }
 
-int occupancy_perm(int dev, int unit, int slots, bool cks, bool nt) {
-  const uint64_t key = (uint64_t(dev) << 32) | (uint64_t(1) << 31) |
+int occupancy_perm(int dev, int unit, int slots, bool hoist, bool cks, bool nt) {
+  const uint64_t key = (uint64_t(dev) << 32) | (uint64_t(1) << 31) | (uint64_t(hoist) << 20) |
                        uint64_t(slots * 256 + unit * 4 + (cks ? 2 : 0) + (nt ? 1 : 0));
   auto it = g_occ.find(key);
   if (it != g_occ.end()) return it->second;
-  const int n = perm_blocks_per_cu(unit, slots, cks, nt);
+  const int n = perm_blocks_per_cu(unit, slots, hoist, cks, nt);
   g_occ[key] = n;
   return n;
 }
@@ -839,6 +861,7 @@ struct Launch {
   // PERM
   uint32_t s0 = 0, s1 = 0, lg = 0, ncols = 0;
   int unit = 16, slots = 8;
+  bool hoist = false;           // descriptors once per group (groups over 32 rows)
 };
 
 coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N, size_t count_in, coll_dtype_t dtype,
@@ -915,6 +938,9 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (st != COLL_OK) return st;
     if (!xd->ok) xd = nullptr;
   }
+  // a copy of leading rows that are not the whole schedule stands for phase 0
+  const bool copy_part = xd && !xd->whole;
+  const uint64_t n0 = xd ? xd->nrows : 0;  // rows the direct copy makes
   if (xd) {
     Launch L;
     L.kind = Launch::COPY;
@@ -924,6 +950,8 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (g_debug.load())
       dbg += " | copy rows: " + std::to_string(xd->nrows) + " rows of " + std::to_string(xd->row_bytes) + " bytes, grid " +
              std::to_string(L.grid) + (L.nt ? " nontemporal" : "");
+  }
+  if (xd && xd->whole) {
   } else if (cd) {
     Launch L;
     L.kind = Launch::COL;
@@ -942,7 +970,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
              " tiles " + std::to_string(cd->tiles) + " unit " + std::to_string(L.v.unit) + " slots " +
              std::to_string(L.v.leaves) + (L.nt ? " nontemporal" : "");
   } else {
-    for (size_t pi = 0; pi < b.phases.size(); ++pi) {
+    for (size_t pi = copy_part ? 1 : 0; pi < b.phases.size(); ++pi) {
       const Phase& ph = b.phases[pi];
       Launch L;
       if (ph.kind == Phase::ROWS) {
@@ -995,12 +1023,13 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         // unit per row, beat 16 (Bruck 7.5 vs 8.0 ms); at 8 and 16 ranks 16 slots
         // beat 8 (0.68 vs 0.72 ms, 1.63 vs 1.77 ms)
         L.slots = ipw > 4 && ipw <= 8 ? 8 : ipw <= 16 ? 16 : 32;
+        L.hoist = N > 32;
         uint32_t lg = 0;
         while ((ipw << (lg + 1)) <= uint32_t(L.slots) && (64u << (lg + 1)) <= std::max<uint32_t>(L.ncols, 64)) ++lg;
         L.lg = lg;
         const uint64_t tu = uint64_t(64) << lg;
         const uint64_t ntiles = (uint64_t(L.ncols) + tu - 1) / tu;
-        uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, L.slots, cks, ntmask != 0));
+        uint64_t cap = uint64_t(di->cus) * uint64_t(occupancy_perm(dev, unit, L.slots, L.hoist, cks, ntmask != 0));
         if (opt_grid.load() > 0) cap = uint64_t(opt_grid.load());
         // the same number of tiles for every work group
         const uint64_t per_wg = std::max<uint64_t>(1, (ntiles + cap - 1) / cap);
@@ -1010,22 +1039,27 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
         L.ntmask = ntmask;
         if (g_debug.load())
           dbg += " | perm steps " + std::to_string(ph.s0) + ".." + std::to_string(ph.s1) + " grid " +
-                 std::to_string(L.grid) + " unit " + std::to_string(unit) + " slots " + std::to_string(L.slots);
+                 std::to_string(L.grid) + " unit " + std::to_string(unit) + " slots " + std::to_string(L.slots) +
+                 (L.hoist ? " hoisted" : "");
       }
       plan.push_back(L);
     }
   }
   uint64_t* partial = nullptr;  // SUM_LANES slots per row, folded into t_sums after the kernels
+  uint64_t* copy_partial = nullptr;  // the direct copy's slot per work group, then the fold's slices
   SumScratch* scratch = nullptr;
+  const uint64_t copy_slots = xd ? uint64_t(xd->nrows) * xd->wgs_per_row : 0;
   if (cks) {
     // the row kernels' SUM_LANES slots per row, or the column kernel's partial
-    // sums and the fold's slices
-    const size_t slots = cd   ? size_t(cd->partials) + std::max<size_t>(size_t(b.nrows), 1) * COL_FOLD_SLICES
-                         : xd ? size_t(xd->nrows) * xd->wgs_per_row + std::max<size_t>(size_t(b.nrows), 1) * COL_FOLD_SLICES
-                              : std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES;
+    // sums and the fold's slices; a direct copy's slots and slices after the
+    // row kernels' slots, if any
+    const size_t rows_slots = (cd || (xd && xd->whole)) ? 0 : std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES;
+    const size_t slots = cd ? size_t(cd->partials) + std::max<size_t>(size_t(b.nrows), 1) * COL_FOLD_SLICES
+                            : rows_slots + (xd ? size_t(copy_slots) + size_t(n0) * COL_FOLD_SLICES : 0);
     st = sum_scratch(dev, t_sums, slots, scratch);
     if (st != COLL_OK) return st;
     partial = scratch->d;
+    if (xd) copy_partial = partial + rows_slots;
   }
   if (capturing) {
     // a graph replays this call later without the library: keep what it
@@ -1037,7 +1071,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
   }
 
   // ---- enqueue
-  if (cks && !cd && !xd) {
+  if (cks && !cd && !(xd && xd->whole)) {
     // the row kernels add into zeroed slots.  A call being captured into a
     // graph runs later, once per replay: it clears the slots itself and
     // leaves the flag to the calls that run now
@@ -1075,7 +1109,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     } else if (L.kind == Launch::COPY) {
       CopyRowsArgs a{};
       a.rows = xd->d_rows;
-      a.partial = partial;
+      a.partial = copy_partial;
       a.p = ptrs;
       a.row_bytes = xd->row_bytes;
       a.wgs_per_row = xd->wgs_per_row;
@@ -1104,7 +1138,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       for (uint32_t s0 = L.s0; s0 < L.s1; s0 = step_mode ? s0 + 1 : L.s1) {
         a.s0 = s0;
         a.s1 = step_mode ? s0 + 1 : L.s1;
-        he = launch_perm(a, L.unit, L.slots, cks, L.grid, stream);
+        he = launch_perm(a, L.unit, L.slots, L.hoist, cks, L.grid, stream);
         if (he != hipSuccess) return hip_fail(he, "permutation kernel launch");
       }
     }
@@ -1115,12 +1149,21 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     te->recorded = true;
     t_last_timed = te;
   }
-  if (cks && (cd || xd)) {
+  if (cks && copy_part) {
+    // the row kernels' rows after the copy's, then the copy's rows; the copy's
+    // slots are not zero for a later row-kernel call
+    he = launch_fold_sums(partial + n0 * SUM_LANES, t_sums + n0, uint64_t(b.nrows) - n0, stream);
+    if (he == hipSuccess)
+      he = launch_col_fold(xd->d_refs, xd->d_row_off, copy_partial, copy_partial + copy_slots, t_sums, n0, stream);
+    if (he != hipSuccess) return hip_fail(he, "checksum fold");
+    if (!capturing) scratch->clean = false;
+  } else if (cks && (cd || xd)) {
     // every partial slot was written by this call: nothing to clear, but the
     // slots are no longer zero for a row-kernel call
-    const uint64_t nslots = cd ? cd->partials : uint64_t(xd->nrows) * xd->wgs_per_row;
-    he = launch_col_fold(cd ? cd->d_refs : xd->d_refs, cd ? cd->d_row_off : xd->d_row_off, partial, partial + nslots,
-                         t_sums, uint64_t(b.nrows), stream);
+    const uint64_t nslots = cd ? cd->partials : copy_slots;
+    he = launch_col_fold(cd ? cd->d_refs : xd->d_refs, cd ? cd->d_row_off : xd->d_row_off,
+                         cd ? partial : copy_partial, (cd ? partial : copy_partial) + nslots, t_sums,
+                         uint64_t(b.nrows), stream);
     if (he != hipSuccess) return hip_fail(he, "checksum fold");
     if (!capturing) scratch->clean = false;
   } else if (cks) {
@@ -1134,7 +1177,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
                  (long long)b.counts.steps, (long long)b.counts.rows, (long long)b.counts.hbm_bytes, dbg.c_str());
   t_last = b.counts;
   t_last.moved_bytes = moved;
-  t_last.round_trips = (cd || xd) ? 1 : b.counts.steps;
+  t_last.round_trips = (cd || (xd && xd->whole)) ? 1 : b.counts.steps;
   return COLL_OK;
 }
 

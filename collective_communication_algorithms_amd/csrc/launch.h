@@ -11,7 +11,10 @@ namespace coll {
 // stored units in registers for ITEM_SRC_FWD / ITEM_DSRC_FWD entries
 hipError_t launch_rows(const RowsArgs& a, int dtype, int op, bool cks, uint32_t nt, bool fine, bool fwd,
                        uint32_t grid, hipStream_t stream);
-hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool cks, uint32_t grid, hipStream_t stream);
+// hoist: descriptors read once per group, loads unconditional (groups over 32 rows)
+hipError_t launch_perm(const PermArgs& a, int unit, int slots, bool hoist, bool cks, uint32_t grid,
+                       hipStream_t stream);
+
 hipError_t launch_fill_u64(uint64_t* p, uint64_t n, uint64_t value, hipStream_t stream);
 // nrows rows of a.row_bytes (a multiple of 16), a.wgs_per_row 1 KiB tiles each;
 // with cks one partial checksum slot per work group
@@ -33,6 +36,6 @@ hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const ui
 // (COLL_NOALLOC_SCRATCH_BYTES, 256-byte aligned), taken once per device.
 hipError_t noalloc_scratch(void** out);
 int rows_blocks_per_cu(int dtype, int op, bool cks, uint32_t nt);
-int perm_blocks_per_cu(int unit, int slots, bool cks, bool nt);
+int perm_blocks_per_cu(int unit, int slots, bool hoist, bool cks, bool nt);
 
 }  // namespace coll

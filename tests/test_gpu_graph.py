@@ -23,6 +23,7 @@ def test_captured_collectives_replay_exactly(gpu_device):
     recv = torch.empty_like(pristine)
     ps = list(pristine[:, :N * 20000])   # 80,000-byte blocks: the direct copy path
     recv2 = torch.empty((N, N * 20000), dtype=torch.float32, device=gpu_device)
+    recv3 = torch.empty_like(recv2)   # Bruck: its first rotation as a direct copy
 
     def work():
         coll.coll_allreduce(list(live), algo="ring")
@@ -30,15 +31,17 @@ def test_captured_collectives_replay_exactly(gpu_device):
         coll.coll_broadcast(list(lu), algo="bidir_ring", root=5, chunks=3)
         coll.coll_alltoall(list(pristine), list(recv), algo="bruck")
         coll.coll_alltoall(ps, list(recv2), algo="pairwise")
+        coll.coll_alltoall(ps, list(recv3), algo="bruck")
 
     # eager reference (also builds and caches every schedule before capture)
     work()
     torch.cuda.synchronize()
-    want = (live.clone(), lu.clone(), recv.clone(), recv2.clone())
+    want = (live.clone(), lu.clone(), recv.clone(), recv2.clone(), recv3.clone())
     live.copy_(pristine)
     lu.copy_(pu)
     recv.zero_()
     recv2.zero_()
+    recv3.zero_()
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
@@ -54,11 +57,12 @@ def test_captured_collectives_replay_exactly(gpu_device):
         lu.copy_(pu)
         recv.zero_()
         recv2.zero_()
+        recv3.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for got, w, name in ((live, want[0], "allreduce"), (lu, want[1], "broadcast"), (recv, want[2], "alltoall"),
-                             (recv2, want[3], "alltoall pairwise")):
+                             (recv2, want[3], "alltoall pairwise"), (recv3, want[4], "alltoall bruck copy")):
             assert torch.equal(got.view(torch.uint8), w.view(torch.uint8)), (rep, name)
     coll.coll_check()
 
@@ -130,6 +134,10 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
     recv_d = torch.empty_like(pd)
     rows_d, _ = coll.coll_plan("alltoall", "pairwise", 16, 16 * 1000, "bfloat16")
     sums_d = torch.full((len(rows_d),), -1, dtype=torch.int64, device=dev)
+    # and a checksummed Bruck AllToAll: its first rotation a direct copy, its rounds in the permutation kernel
+    recv_b = torch.empty_like(pd)
+    rows_b, _ = coll.coll_plan("alltoall", "bruck", 16, 16 * 1000, "bfloat16")
+    sums_b = torch.full((len(rows_b),), -1, dtype=torch.int64, device=dev)
     rows8, _ = coll.coll_plan("allreduce", "ring", N, count, "float32")
     rows16, _ = coll.coll_plan("allreduce", "ring", 16, 16 * 30000, "float32")
     cap = max(len(rows8), len(rows16))
@@ -143,6 +151,8 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
         coll.coll_alltoall(list(pa), list(recv), algo="bruck")
         coll.coll_set_checksums(sums_d)
         coll.coll_alltoall(list(pd), list(recv_d), algo="pairwise")
+        coll.coll_set_checksums(sums_b)
+        coll.coll_alltoall(list(pd), list(recv_b), algo="bruck")
         coll.coll_set_checksums(None)
 
     try:
@@ -151,7 +161,7 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
         want, want_recv = live.clone(), recv.clone()
         want_sums = sums[:len(rows8)].clone()
         want_d, want_sums_d = recv_d.clone(), sums_d.clone()
-        assert coll.coll_get_stats()["round_trips"] == 1
+        want_b, want_sums_b = recv_b.clone(), sums_b.clone()
         live.copy_(pristine)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -185,8 +195,10 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
             live.copy_(pristine)
             recv.zero_()
             recv_d.zero_()
+            recv_b.zero_()
             sums.fill_(-1)
             sums_d.fill_(-1)
+            sums_b.fill_(-1)
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
@@ -195,6 +207,8 @@ def test_captured_calls_outlive_eviction_growth_and_new_tables(gpu_device):
             assert torch.equal(sums[:len(rows8)], want_sums), ("checksums", rep)
             assert torch.equal(recv_d.view(torch.int16), want_d.view(torch.int16)), ("pairwise", rep)
             assert torch.equal(sums_d, want_sums_d), ("pairwise checksums", rep)
+            assert torch.equal(recv_b.view(torch.int16), want_b.view(torch.int16)), ("bruck", rep)
+            assert torch.equal(sums_b, want_sums_b), ("bruck checksums", rep)
         coll.coll_check()
     finally:
         coll.coll_set_checksums(None)

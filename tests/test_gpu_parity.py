@@ -403,6 +403,55 @@ def test_pairwise_alltoall_direct_copy(N, B, dtype):
     assert coll.coll_get_stats()["round_trips"] == N - 1
 
 
+@pytest.mark.parametrize("algo", ["bruck", "ring"])
+def test_alltoall_rotation_copy_then_rounds(gpu_device, algo):
+    """Bruck and the Ring AllToAll start with a local rotation whose rows read
+    only the send buffers: with blocks of a multiple of 16 bytes it runs as a
+    direct copy, the rounds after it in the permutation kernel.  Bit-exact
+    against the oracle with row checksums (the copy's rows folded from its
+    own slots, the rounds' from the row kernels'), for blocks that qualify and
+    blocks that do not; then the same checksum buffer serves, in turn, a
+    larger schedule run wholly by the row kernels and the mixed call again."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    for N, B, dtype in ((32, 512, "bfloat16"), (5, 1000, "float32"), (12, 32, "uint8"), (12, 24, "uint8"),
+                        (17, 33, "bfloat16"), (3, 4, "int32")):
+        a = si.rank_arrays(N + 300, N, N * B, dtype)
+        assert_parity("alltoall", algo, a, dtype, checksums=True)
+        assert_parity("alltoall", algo, a, dtype)
+
+    def call(N, B, dtype, seed, sums):
+        host = si.rank_arrays(seed, N, N * B, dtype)
+        send = [si.host_to_tensor(x, dtype, gpu_device) for x in host]
+        recv = [torch.empty_like(t) for t in send]
+        coll.coll_set_checksums(sums)
+        try:
+            coll.coll_alltoall(send, recv, algo=algo)
+        finally:
+            coll.coll_set_checksums(None)
+        torch.cuda.synchronize()
+        plan = make_plan("alltoall", algo, N, N * B)
+        want, wsums = run_plan(plan, dtype, "sum", host, trace=True)
+        for i in range(N):
+            assert np.array_equal(si.tensor_to_host(recv[i], dtype).view(np.uint8), want[i].view(np.uint8)), (N, i)
+        rows, _ = coll.coll_plan("alltoall", algo, N, N * B, dtype)
+        key = {}
+        idx = 0
+        for st, srows in enumerate(plan.steps):
+            for r in srows:
+                key[(st, r.src, r.dst, r.src_off, r.dst_off, r.n)] = wsums[idx]
+                idx += 1
+        got = sums.cpu().numpy().view(np.uint64)
+        for j, r in enumerate(rows):
+            assert int(got[j]) == key[r[:6]], (N, B, j, r)
+
+    sums = torch.full((40 * 40 * 8,), -1, dtype=torch.int64, device=gpu_device)
+    call(16, 64, "bfloat16", 1, sums)      # mixed: copy, then rounds
+    call(24, 17, "bfloat16", 2, sums)      # 34-byte blocks: row kernels only, more rows
+    call(16, 64, "bfloat16", 3, sums)
+    call(24, 17, "bfloat16", 4, sums)
+
+
 @pytest.mark.parametrize("N", [3, 5, 6, 7, 12, 13])
 def test_non_power_of_two_rhd_dbt(N):
     """Halving-doubling with the surplus folded into a power-of-two core, and
@@ -498,8 +547,8 @@ def test_coll_check_after_calls():
 def test_debug_lines(gpu_device):
     """COLL_DEBUG=1 prints one line per call: the collective, the resolved
     algorithm, the schedule's counts and each launch's shape (the column
-    kernel's segments and grid, the direct copy of a Pairwise AllToAll, or the
-    row and permutation kernels' launches)."""
+    kernel's segments and grid, the direct copy of a Pairwise AllToAll or of
+    Bruck's first rotation, or the row and permutation kernels' launches)."""
     import os
     import subprocess
     import sys
@@ -508,17 +557,22 @@ def test_debug_lines(gpu_device):
             "c.coll_allreduce(t, algo='auto'); c.coll_set_option('exec', 2); c.coll_allreduce(t, algo='ring'); "
             "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); c.coll_set_option('exec', 0); "
             "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='pairwise'); "
+            "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); "
             "torch.cuda.synchronize(); print(float(t[0][0]))")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root, timeout=120,
                        env=dict(os.environ, COLL_DEBUG="1"))
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stderr.splitlines() if ln.startswith("coll: ")]
-    assert len(lines) == 4, r.stderr[-2000:]
+    assert len(lines) == 5, r.stderr[-2000:]
     assert lines[0].startswith("coll: allreduce algo ") and "algo auto" not in lines[0] and "| columns:" in lines[0]
     assert lines[1].startswith("coll: allreduce algo ring") and "| rows" in lines[1]
     assert lines[2].startswith("coll: alltoall algo bruck") and "| perm" in lines[2]
     assert lines[3].startswith("coll: alltoall algo pairwise") and "| copy rows:" in lines[3]
+    assert lines[3].count(" | ") == 1
+    # Bruck: the first rotation as a direct copy, the rounds in the permutation kernel
+    assert lines[4].startswith("coll: alltoall algo bruck") and "| copy rows:" in lines[4] and "| perm" in lines[4]
+    assert "| rows" not in lines[4]
     assert r.stdout.strip() == "64.0"
 
 
