@@ -17,6 +17,9 @@ bracketed by HIP events on its stream.  Prints one JSON line:
                 schedule's steps pass from row to row stays in registers) over
                 its mean launch time, timed live by the library's own HIP
                 events (COLL_OPT_TIMING) in a second pass of restored calls
+  access_pattern_ceiling  the same buffers under the kernel's memory access
+                pattern alone (8 loads, a sum, 8 stores per 1 KiB tile), and
+                the column kernel's rate as a fraction of it
   cpu_baseline  the CPU oracle on the same inputs, one core
 """
 
@@ -36,8 +39,9 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "busbw GB/s & % HBM peak, Ring AllReduce fp32 N=8 M=256MiB (1 GPU)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_col_kernel_ring_allreduce_fp32_n8_256MiB.json")
 # the column kernel variant the default run times: fp32, sum, 8 register
-# slots, 16 checksum accumulators, nontemporal loads and stores, no batches
-HEADLINE_KERNEL = "void coll::(anonymous namespace)::col_kernel<2, 0, 8, 16, 5, false>"
+# slots, 16 checksum accumulators, nontemporal loads and stores, no batches,
+# room for 16 ranks' buffer addresses
+HEADLINE_KERNEL = "void coll::(anonymous namespace)::col_kernel<2, 0, 8, 16, 5, false, 16>"
 
 
 def kernel_source_hash() -> str:
@@ -326,7 +330,11 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
 
 def calibrate(dev, gib: int = 2, reps: int = 10) -> dict:
     """Achievable HBM rate of plain streams: copy reads and writes each byte
-    once (2 x bytes moved), add reads two operands and writes one (3 x bytes)."""
+    once (2 x bytes moved), add reads two operands and writes one (3 x bytes);
+    and of the column kernel's access patterns without its programs (loads of
+    one 1 KiB tile from each of L buffers, stores to each of S buffers, per
+    one-wave work group): a fill, an 8-rank AllReduce in place, Reduce and
+    Broadcast over 8 ranks, a 64-rank ReduceScatter and AllGather segment."""
     import torch
     import collective_communication_algorithms_amd as coll
     n = (gib << 30) // 4
@@ -346,7 +354,34 @@ def calibrate(dev, gib: int = 2, reps: int = 10) -> dict:
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / reps
         out[name] = {"bytes": moved * n * 4, "ms": round(ms, 4), "GBps": round(moved * n * 4 / ms / 1e6, 1)}
-    return {"calibration": out, "buffer_GiB": gib}
+    # the column kernel's access patterns without its programs, over one 2 GiB
+    # pool cut into the buffers each pattern names (coll_calib_pattern)
+    del a, b, c
+    pool = torch.zeros((2 << 30) // 4, device=dev)
+    pats = {}
+    for name, nl, ns, nbuf, loads_of, stores_of in (
+            ("fill", 0, 1, 1, lambda v: [], lambda v: v[:1]),
+            ("allreduce_8_ranks_in_place", 8, 8, 8, lambda v: v, lambda v: v),
+            ("reduce_8_ranks", 8, 1, 8, lambda v: v, lambda v: v[:1]),
+            ("broadcast_8_ranks", 1, 7, 8, lambda v: v[:1], lambda v: v[1:]),
+            ("reducescatter_64_ranks", 64, 1, 64, lambda v: v, lambda v: v[:1]),
+            ("allgather_64_ranks", 1, 63, 64, lambda v: v[:1], lambda v: v[1:])):
+        views = list(pool.view(nbuf, -1))
+        ld, st = loads_of(views), stores_of(views)
+        nbytes = views[0].numel() * 4
+        coll.coll_calib_pattern(ld, st)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            coll.coll_calib_pattern(ld, st)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        moved = (nl + ns) * nbytes
+        pats[name] = {"loads": nl, "stores": ns, "bytes_per_buffer": nbytes, "bytes": moved, "ms": round(ms, 4),
+                      "GBps": round(moved / ms / 1e6, 1)}
+    return {"calibration": out, "buffer_GiB": gib, "access_patterns": pats}
 
 
 def overlap(out_path: str, dev) -> None:
@@ -813,6 +848,22 @@ def main() -> int:
         coll.coll_allreduce(ranks, algo=args.algo)
         kernel_ms.append(coll.coll_last_kernel_ms())
     coll.coll_set_option("timing", 0)
+    # the same buffers under the kernel's access pattern alone: a tile of each
+    # of the N ranks loaded, summed and stored back to each (no program, no
+    # checksums), one-wave work groups of one 1 KiB tile, as the kernel runs
+    pattern = None
+    if N == 8:
+        coll.coll_calib_pattern(ranks, ranks)
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for _ in range(args.steps):
+            coll.coll_calib_pattern(ranks, ranks)
+        p1.record(stream)
+        torch.cuda.synchronize()
+        pattern_ms = p0.elapsed_time(p1) / args.steps
+        pattern = {"pattern": "8 loads + 8 stores per 1 KiB tile, in place on the call's buffers (coll_calib_pattern)",
+                   "ms": round(pattern_ms, 4), "GBps": round(2 * N * M / pattern_ms / 1e6, 1)}
     # the earlier protocol, for reference: calls back to back on the same
     # buffers, no restore, mean time
     restore()
@@ -864,6 +915,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "kernel_ms_mean": round(launch_ms, 4),
+        "access_pattern_ceiling": (dict(pattern, kernel_frac=round(achieved / pattern["GBps"], 4))
+                                   if pattern else None),
         # the schedule's row bytes (every row reading its operands and writing
         # its destination through memory) per median call: a rate no kernel
         # moves, kept for comparison with the pages' step model

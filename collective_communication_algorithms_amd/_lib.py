@@ -97,6 +97,9 @@ def load() -> ctypes.CDLL:
     lib.coll_calib_add.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_void_p]
     lib.coll_calib_add.restype = ctypes.c_int
+    lib.coll_calib_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                       ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
+    lib.coll_calib_pattern.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -1104,7 +1104,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.code = L.code;
       a.partial = partial;
       a.p = ptrs;
-      he = launch_col(a, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.v.batched, L.nt, L.grid, stream);
+      he = launch_col(a, N, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.v.batched, L.nt, L.grid, stream);
       if (he != hipSuccess) return hip_fail(he, "column kernel launch");
     } else if (L.kind == Launch::COPY) {
       CopyRowsArgs a{};
@@ -1316,7 +1316,7 @@ coll_status_t run_noalloc(void* const* send, void* const* recv, int N, size_t co
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
   const uint32_t grid = uint32_t(cur.tables.work.size());
   if (grid) {
-    he = launch_col(a, dt, int(op), cur.plan.v.unit, cur.plan.v.leaves, cur.plan.v.accs, cur.plan.v.batched, nt,
+    he = launch_col(a, N, dt, int(op), cur.plan.v.unit, cur.plan.v.leaves, cur.plan.v.accs, cur.plan.v.batched, nt,
                      grid, stream);
     if (he != hipSuccess) return hip_fail(he, "column kernel launch");
   }
@@ -1333,6 +1333,11 @@ coll_status_t run_noalloc(void* const* send, void* const* recv, int N, size_t co
   return COLL_OK;
 }
 }  // namespace
+
+// the calls' error reporting, for the calibration entry points (calib.cpp)
+coll_status_t report_error(coll_status_t st, const char* msg) { return fail(st, msg); }
+coll_status_t report_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+
 }  // namespace coll
 
 using namespace coll;
@@ -1570,35 +1575,6 @@ void coll_finalize(void) {
   g_cache_bytes = 0;
   g_occ.clear();
   g_dev.clear();
-}
-
-static coll_status_t calib(void* dst, const void* a, const void* b, size_t bytes, void* stream) {
-  if (!dst || !a) return fail(COLL_ERR_INVALID_ARG, "NULL buffer");
-  if (bytes % 16 || (reinterpret_cast<uint64_t>(dst) | reinterpret_cast<uint64_t>(a) | reinterpret_cast<uint64_t>(b)) % 16)
-    return fail(COLL_ERR_INVALID_ARG, "calibration needs 16-byte sizes and pointers");
-  if (bytes == 0) return COLL_OK;
-  const hipError_t he = launch_calib(dst, a, b, bytes, reinterpret_cast<hipStream_t>(stream));
-  if (he != hipSuccess) return hip_fail(he, "calibration launch");
-  return COLL_OK;
-}
-
-coll_status_t coll_calib_copy(void* dst, const void* src, size_t bytes, void* stream) {
-  return calib(dst, src, nullptr, bytes, stream);
-}
-
-coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t bytes, void* stream) {
-  if (!b) return fail(COLL_ERR_INVALID_ARG, "NULL buffer");
-  return calib(dst, a, b, bytes, stream);
-}
-
-coll_status_t coll_calib_spin(float* out, uint32_t iters, uint32_t grid, void* stream) {
-  if (!out) return fail(COLL_ERR_INVALID_ARG, "NULL buffer");
-  if (reinterpret_cast<uint64_t>(out) % 4) return fail(COLL_ERR_INVALID_ARG, "out must be 4-byte aligned");
-  if (grid < 1 || grid > COLL_SPIN_MAX_GRID) return fail(COLL_ERR_INVALID_ARG, "grid outside [1, COLL_SPIN_MAX_GRID]");
-  if (iters > COLL_SPIN_MAX_ITERS) return fail(COLL_ERR_INVALID_ARG, "iters above COLL_SPIN_MAX_ITERS");
-  const hipError_t he = launch_spin(out, iters, grid, reinterpret_cast<hipStream_t>(stream));
-  if (he != hipSuccess) return hip_fail(he, "spin launch");
-  return COLL_OK;
 }
 
 }  // extern "C"

@@ -160,8 +160,8 @@ struct Accs<-1> {};
 // only partial results above, which are written once and read once per
 // subtree: with BT those slots live in LDS (1 KiB each per work group), so
 // the wave keeps the registers of the 8-slot variant and its occupancy.
-template <int DT, int OP, int NL, int NA, int NTM, bool BT>
-__global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
+template <int DT, int OP, int NL, int NA, int NTM, bool BT, int P>
+__global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P> a) {
   typedef u32x4 U;
   constexpr uint64_t UNIT = 16;
   constexpr uint64_t TB = uint64_t(COL_THREADS) * UNIT;
@@ -171,7 +171,8 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColArgs a) {
   const ColWork wk = cload(a.work + blockIdx.x);
   const uint32_t lane = threadIdx.x;
   // lane r holds rank r's buffer addresses, lane k entry k of each list
-  const uint64_t sp = a.p.send[lane], rp = a.p.recv[lane];  // COL_THREADS <= COLL_MAX_RANKS
+  static_assert(P <= COL_THREADS, "lane r holds rank r's addresses");
+  const uint64_t sp = lane < uint32_t(P) ? a.send[lane] : 0, rp = lane < uint32_t(P) ? a.recv[lane] : 0;
   const uint32_t sp_lo = uint32_t(sp), sp_hi = uint32_t(sp >> 32), rp_lo = uint32_t(rp), rp_hi = uint32_t(rp >> 32);
   uint32_t ld_w1 = 0, op_w0 = 0, op_w1 = 0, st_w0 = 0, st_w1 = 0;
   if (lane < wk.nload) ld_w1 = *gptr<uint32_t>(reinterpret_cast<const char*>(a.code + wk.loads + lane) + 4);
@@ -345,47 +346,67 @@ __global__ __launch_bounds__(BLOCK_THREADS) void col_fold_rows_kernel(const uint
   if (lane == 0) *gptr<uint64_t>(reinterpret_cast<char*>(out + r)) = t;
 }
 
-typedef void (*ColFn)(ColArgs);
+template <int P>
+using ColFn = void (*)(ColLaunchArgs<P>);
 
-template <int DT, int OP, int NL, int NA, bool BT>
-ColFn col_fn_nt(bool nt) {
-  return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT> : col_kernel<DT, OP, NL, NA, 0, BT>;
+template <int DT, int OP, int NL, int NA, bool BT, int P>
+ColFn<P> col_fn_nt(bool nt) {
+  return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT, P> : col_kernel<DT, OP, NL, NA, 0, BT, P>;
 }
 
 // accs: 0, 16 (8 slots), 32 (16 slots), or more: per-tile wave sums (batched
 // programs only)
-template <int DT, int OP, bool BT>
-ColFn col_fn_variant(int leaves, int accs, bool nt) {
+template <int DT, int OP, bool BT, int P>
+ColFn<P> col_fn_variant(int leaves, int accs, bool nt) {
   if constexpr (BT) {
-    if (accs > 32) return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT>(nt) : col_fn_nt<DT, OP, 16, -1, BT>(nt);
+    if (accs > 32) return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 16, -1, BT, P>(nt);
   }
-  if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 8, 16, BT>(nt) : col_fn_nt<DT, OP, 8, 0, BT>(nt);
-  return accs ? col_fn_nt<DT, OP, 16, 32, BT>(nt) : col_fn_nt<DT, OP, 16, 0, BT>(nt);
+  if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 8, 16, BT, P>(nt) : col_fn_nt<DT, OP, 8, 0, BT, P>(nt);
+  return accs ? col_fn_nt<DT, OP, 16, 32, BT, P>(nt) : col_fn_nt<DT, OP, 16, 0, BT, P>(nt);
 }
 
-template <int DT>
-ColFn col_fn_op(int op, int leaves, int accs, bool batched, bool nt) {
-  if (batched) {
-    switch (op) {
-      case OP_SUM: return col_fn_variant<DT, OP_SUM, true>(leaves, accs, nt);
-      case OP_MAX: return col_fn_variant<DT, OP_MAX, true>(leaves, accs, nt);
-      default: return col_fn_variant<DT, OP_MIN, true>(leaves, accs, nt);
+// batched programs (over 16 leaves) only come with over 16 ranks: P = 64
+template <int DT, int P>
+ColFn<P> col_fn_op(int op, int leaves, int accs, bool batched, bool nt) {
+  if constexpr (P > 16) {
+    if (batched) {
+      switch (op) {
+        case OP_SUM: return col_fn_variant<DT, OP_SUM, true, P>(leaves, accs, nt);
+        case OP_MAX: return col_fn_variant<DT, OP_MAX, true, P>(leaves, accs, nt);
+        default: return col_fn_variant<DT, OP_MIN, true, P>(leaves, accs, nt);
+      }
     }
   }
   switch (op) {
-    case OP_SUM: return col_fn_variant<DT, OP_SUM, false>(leaves, accs, nt);
-    case OP_MAX: return col_fn_variant<DT, OP_MAX, false>(leaves, accs, nt);
-    default: return col_fn_variant<DT, OP_MIN, false>(leaves, accs, nt);
+    case OP_SUM: return col_fn_variant<DT, OP_SUM, false, P>(leaves, accs, nt);
+    case OP_MAX: return col_fn_variant<DT, OP_MAX, false, P>(leaves, accs, nt);
+    default: return col_fn_variant<DT, OP_MIN, false, P>(leaves, accs, nt);
   }
 }
 
-ColFn pick_col(int dtype, int op, int leaves, int accs, bool batched, bool nt) {
+template <int P>
+ColFn<P> pick_col(int dtype, int op, int leaves, int accs, bool batched, bool nt) {
   switch (dtype) {
-    case DT_I32: return col_fn_op<DT_I32>(op, leaves, accs, batched, nt);
-    case DT_U8: return col_fn_op<DT_U8>(op, leaves, accs, batched, nt);
-    case DT_F32: return col_fn_op<DT_F32>(op, leaves, accs, batched, nt);
-    default: return col_fn_op<DT_BF16>(op, leaves, accs, batched, nt);
+    case DT_I32: return col_fn_op<DT_I32, P>(op, leaves, accs, batched, nt);
+    case DT_U8: return col_fn_op<DT_U8, P>(op, leaves, accs, batched, nt);
+    case DT_F32: return col_fn_op<DT_F32, P>(op, leaves, accs, batched, nt);
+    default: return col_fn_op<DT_BF16, P>(op, leaves, accs, batched, nt);
   }
+}
+
+template <int P>
+hipError_t launch_col_p(const ColArgs& a, int dtype, int op, int leaves, int accs, bool batched, bool nt,
+                        uint32_t grid, hipStream_t stream) {
+  ColLaunchArgs<P> c;
+  c.work = a.work;
+  c.code = a.code;
+  c.partial = a.partial;
+  for (int i = 0; i < P; ++i) {
+    c.send[i] = a.p.send[i];
+    c.recv[i] = a.p.recv[i];
+  }
+  hipLaunchKernelGGL(pick_col<P>(dtype, op, leaves, accs, batched, nt), dim3(grid), dim3(COL_THREADS), 0, stream, c);
+  return hipGetLastError();
 }
 
 // Device memory of coll_allreduce_noalloc: its programs, work table, row
@@ -417,11 +438,12 @@ hipError_t noalloc_scratch(void** out) {
   return hipSuccess;
 }
 
-hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool batched, bool nt,
-                      uint32_t grid, hipStream_t stream) {
+hipError_t launch_col(const ColArgs& a, int nranks, int dtype, int op, int unit, int leaves, int accs, bool batched,
+                      bool nt, uint32_t grid, hipStream_t stream) {
   (void)unit;  // every variant takes 16-byte units
-  hipLaunchKernelGGL(pick_col(dtype, op, leaves, accs, batched, nt), dim3(grid), dim3(COL_THREADS), 0, stream, a);
-  return hipGetLastError();
+  if (nranks < 1 || nranks > COL_THREADS) return hipErrorInvalidValue;
+  if (nranks <= 16 && !batched) return launch_col_p<16>(a, dtype, op, leaves, accs, batched, nt, grid, stream);
+  return launch_col_p<64>(a, dtype, op, leaves, accs, batched, nt, grid, stream);
 }
 
 hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,

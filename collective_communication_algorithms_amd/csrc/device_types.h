@@ -173,6 +173,21 @@ struct ColArgs {
   RankPtrs p;
 };
 
+// What a column-kernel launch passes: ColArgs with room for P ranks' buffer
+// addresses (lane r of a work group reads rank r's).  The host time of a
+// launch grows with its argument block, so calls over at most 16 ranks pass
+// 16 addresses a side (280 bytes in all), the others 64 (1,048 bytes), not
+// the 128 of RankPtrs (2,072 bytes): measured on MI355X, the host time per
+// 4-rank AllReduce call through the C ABI fell from 5.1 to 4.7 us.
+template <int P>
+struct ColLaunchArgs {
+  const ColWork* work;
+  const ColInstr* code;
+  uint64_t* partial;
+  uint64_t send[P];
+  uint64_t recv[P];
+};
+
 // Slices of a row's partial sums the checksum fold adds in parallel.
 constexpr uint32_t COL_FOLD_SLICES = 32;
 

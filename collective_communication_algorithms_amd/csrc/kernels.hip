@@ -533,6 +533,42 @@ __global__ __launch_bounds__(CALIB_THREADS) void calib_kernel(char* dst, const c
   st16<true>(dst + u * 16, x);
 }
 
+// Access patterns of the column kernel's programs, without the programs:
+// one-wave work groups, one 1 KiB tile per buffer (16 B per lane), L loads at
+// the same offset of L buffers (all in flight together, eight at a time),
+// their u32 word sum, then S stores of it at the same offset of S buffers;
+// nontemporal.  L = 0 stores a constant (a fill).  Buffers may repeat (in
+// place: the stores go where the loads came from).  Lane r holds load
+// buffer r's and store buffer r's addresses.
+template <int L, int S>
+__global__ __launch_bounds__(64) void calib_pattern_kernel(const RankPtrs p) {
+  const uint32_t lane = threadIdx.x;
+  const uint64_t lp = p.send[lane], sp = p.recv[lane];
+  const uint32_t lp_lo = uint32_t(lp), lp_hi = uint32_t(lp >> 32), sp_lo = uint32_t(sp), sp_hi = uint32_t(sp >> 32);
+  const uint64_t off = uint64_t(blockIdx.x) * 1024u + uint64_t(lane) * 16u;
+  u32x4 acc = {lane, uint32_t(blockIdx.x), 0u, 0u};
+  if constexpr (L > 0) acc = u32x4{0u, 0u, 0u, 0u};
+  constexpr int B = L < 8 ? L : 8;
+#pragma unroll
+  for (int b = 0; b < L; b += B) {
+    u32x4 v[B > 0 ? B : 1];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const uint64_t base = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(lp_lo), b + j))) |
+                            (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(lp_hi), b + j))) << 32);
+      v[j] = ld16<true>(reinterpret_cast<const char*>(base) + off);
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) acc += v[j];
+  }
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const uint64_t base = uint64_t(uint32_t(__builtin_amdgcn_readlane(int(sp_lo), k))) |
+                          (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(sp_hi), k))) << 32);
+    st16<true>(reinterpret_cast<char*>(base) + off, acc);
+  }
+}
+
 // ---- host-side dispatch ---------------------------------------------------------------
 
 typedef void (*RowsFn)(RowsArgs);
@@ -684,6 +720,22 @@ hipError_t launch_copy_rows(const CopyRowsArgs& a, uint64_t nrows, bool cks, boo
   auto fn = cks ? (nt ? copy_rows_kernel<true, true> : copy_rows_kernel<true, false>)
                 : (nt ? copy_rows_kernel<false, true> : copy_rows_kernel<false, false>);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_calib_pattern(const RankPtrs& p, int nloads, int nstores, uint64_t bytes, hipStream_t stream) {
+  void (*f)(RankPtrs) = nullptr;
+  if (nloads == 0 && nstores == 1) f = calib_pattern_kernel<0, 1>;
+  else if (nloads == 8 && nstores == 8) f = calib_pattern_kernel<8, 8>;
+  else if (nloads == 8 && nstores == 1) f = calib_pattern_kernel<8, 1>;
+  else if (nloads == 1 && nstores == 7) f = calib_pattern_kernel<1, 7>;
+  else if (nloads == 64 && nstores == 1) f = calib_pattern_kernel<64, 1>;
+  else if (nloads == 1 && nstores == 63) f = calib_pattern_kernel<1, 63>;
+  if (!f || bytes % 1024u) return hipErrorInvalidValue;
+  const uint64_t g = bytes / 1024u;
+  if (g == 0) return hipSuccess;
+  if (g > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(f, dim3(uint32_t(g)), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

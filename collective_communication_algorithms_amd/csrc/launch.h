@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "coll.h"
 #include "device_types.h"
 
 namespace coll {
@@ -22,12 +23,20 @@ hipError_t launch_copy_rows(const CopyRowsArgs& a, uint64_t nrows, bool cks, boo
 // out[r] = the u64 wrap-sum of partial[r * SUM_LANES .. r * SUM_LANES + SUM_LANES), r < nrows;
 // the slots read are set back to zero
 hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hipStream_t stream);
+// (nloads, nstores) in {(0,1), (8,8), (8,1), (1,7), (64,1), (1,63)}; p.send[0 .. nloads)
+// the load buffers, p.recv[0 .. nstores) the store buffers; bytes a multiple of 1024
+hipError_t launch_calib_pattern(const RankPtrs& p, int nloads, int nstores, uint64_t bytes, hipStream_t stream);
 hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, hipStream_t stream);
+// the C ABI's error reporting (the message coll_last_error returns), for entry
+// points outside abi.cpp
+coll_status_t report_error(coll_status_t st, const char* msg);
+coll_status_t report_hip_error(hipError_t e, const char* what);
 hipError_t launch_spin(float* out, uint32_t iters, uint32_t grid, hipStream_t stream);
 // column kernel: the variant of (unit, leaves, accs) (ColVariant), nontemporal
-// loads and stores when `nt`; one work group of COL_THREADS per ColWork
-hipError_t launch_col(const ColArgs& a, int dtype, int op, int unit, int leaves, int accs, bool batched, bool nt,
-                      uint32_t grid, hipStream_t stream);
+// loads and stores when `nt`; one work group of COL_THREADS per ColWork; the
+// first nranks (1 .. COL_THREADS) addresses of a.p are passed
+hipError_t launch_col(const ColArgs& a, int nranks, int dtype, int op, int unit, int leaves, int accs, bool batched,
+                      bool nt, uint32_t grid, hipStream_t stream);
 // out[r] = the sum of the partial slots row r's ColRefs name, r < nrows, by way
 // of tmp (nrows * COL_FOLD_SLICES slots)
 hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,

@@ -378,6 +378,21 @@ void coll_finalize(void);            /* frees the schedule cache and the checksu
 coll_status_t coll_calib_copy(void* dst, const void* src, size_t bytes, void* stream);
 coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t bytes, void* stream);
 
+/* The column kernel's access patterns without its programs, as ceilings for
+ * it: one-wave work groups, one 1 KiB tile of each buffer per work group;
+ * the tile is loaded from each of the nloads buffers (all loads in flight,
+ * eight at a time), summed as u32 words, and the sum stored to each of the
+ * nstores buffers at the same offset; nontemporal; nloads 0 stores a
+ * constant.  (nloads, nstores): (0, 1) a fill, (8, 8) an 8-rank AllReduce
+ * (pass the same buffers twice for in place), (8, 1) an 8-rank Reduce, (1, 7)
+ * an 8-rank Broadcast, (64, 1) a 64-rank ReduceScatter segment, (1, 63) a
+ * 64-rank AllGather segment.  Each buffer holds `bytes` bytes (a multiple of
+ * 1024), 16-byte aligned, owned by the caller; the stores overwrite them.
+ * Errors: UNSUPPORTED for any other pair; INVALID_ARG for NULL or misaligned
+ * buffers or sizes. */
+coll_status_t coll_calib_pattern(void* const* loads, int nloads, void* const* stores, int nstores, size_t bytes,
+                                 void* stream);
+
 /* A stand-in for compute, for measuring how far a collective on a side stream
  * hides behind it ([P2] 延迟掩盖：计算与通信的Overlap; Overlap的性能收益).
  * `grid` work groups of 256 threads each run `iters` rounds of four dependent

@@ -137,6 +137,27 @@ def test_spin_argument_errors():
     assert lib.coll_calib_spin(ctypes.c_void_p(aligned), (1 << 28) + 1, 1, None) == INV
 
 
+def test_calib_pattern_argument_errors():
+    """The access-pattern calibration rejects unknown load / store counts,
+    NULL or misaligned buffers and sizes off 1 KiB before any HIP call."""
+    lib = _lib.load()
+    buf = ctypes.create_string_buffer(64)
+    addr = ctypes.addressof(buf)
+    aligned = addr + (-addr) % 16
+    UNS = _lib.COLL_ERR_UNSUPPORTED
+    one = (ctypes.c_void_p * 64)(*([aligned] * 64))
+    bad = (ctypes.c_void_p * 64)(*([aligned + 4] * 64))
+    null = (ctypes.c_void_p * 64)(*([None] * 64))
+    assert lib.coll_calib_pattern(one, 2, one, 2, 1024, None) == UNS
+    assert lib.coll_calib_pattern(one, 8, one, 7, 1024, None) == UNS
+    assert lib.coll_calib_pattern(one, 8, None, 8, 1024, None) == INV
+    assert lib.coll_calib_pattern(None, 8, one, 8, 1024, None) == INV
+    assert lib.coll_calib_pattern(null, 64, one, 1, 1024, None) == INV
+    assert lib.coll_calib_pattern(one, 1, bad, 63, 1024, None) == INV
+    assert lib.coll_calib_pattern(one, 8, one, 8, 1000, None) == INV
+    assert lib.coll_calib_pattern(None, 0, one, 1, 0, None) == OK     # nothing to do
+
+
 def test_plan_capacity_protocol():
     lib = _lib.load()
     n = ctypes.c_size_t(0)
