@@ -968,7 +968,8 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (g_debug.load())
       dbg += " | columns: " + std::to_string(cd->plan.segs.size()) + " segments, grid " + std::to_string(L.grid) +
              " tiles " + std::to_string(cd->tiles) + " unit " + std::to_string(L.v.unit) + " slots " +
-             std::to_string(L.v.leaves) + (L.nt ? " nontemporal" : "");
+             std::to_string(L.v.leaves) + (L.v.accs ? " checksum ops " + std::to_string(L.v.accs) : "") +
+             (L.v.batched ? " batched" : "") + (L.nt ? " nontemporal" : "");
   } else {
     for (size_t pi = copy_part ? 1 : 0; pi < b.phases.size(); ++pi) {
       const Phase& ph = b.phases[pi];

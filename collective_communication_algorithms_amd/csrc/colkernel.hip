@@ -125,25 +125,16 @@ __device__ __forceinline__ uint64_t lane_u64(uint32_t lo, uint32_t hi, uint32_t 
          (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(hi), int(lane)))) << 32);
 }
 
-// NA u64 checksum accumulators, indexed by the wave-uniform op number; in
-// parts of 16 (32 dwords), like the slots.
+// NA u64 checksum accumulators (NA <= 16: 32 dwords), indexed by the
+// wave-uniform op number, like the slots.
 template <int NA>
 struct Accs {
-  static constexpr int HALF = NA > 16 ? NA / 2 : NA;
-  static_assert(NA <= 32, "at most two 16-entry parts");
-  typedef uint64_t V __attribute__((ext_vector_type(HALF)));
-  V lo, hi;
-  __device__ __forceinline__ void clear() {
-    lo = 0;
-    hi = 0;
-  }
-  __device__ __forceinline__ void add(uint32_t k, uint64_t v) {
-    if (NA <= 16 || k < uint32_t(HALF)) lo[k] += v;
-    else hi[k - HALF] += v;
-  }
-  __device__ __forceinline__ uint64_t get(uint32_t k) const {
-    return (NA <= 16 || k < uint32_t(HALF)) ? lo[k] : hi[k - HALF];
-  }
+  static_assert(NA <= 16, "one 32-dword file");
+  typedef uint64_t V __attribute__((ext_vector_type(NA)));
+  V lo;
+  __device__ __forceinline__ void clear() { lo = 0; }
+  __device__ __forceinline__ void add(uint32_t k, uint64_t v) { lo[k] += v; }
+  __device__ __forceinline__ uint64_t get(uint32_t k) const { return lo[k]; }
 };
 template <>
 struct Accs<0> {};
@@ -153,8 +144,10 @@ template <>
 struct Accs<-1> {};
 
 // 16 bytes per lane and column; NL slots; NA checksum accumulators (0: no
-// checksums; -1: per-tile wave sums, for programs of more ops than an
-// accumulator file holds); NTM: nontemporal loads (NT_SRC) / stores (NT_DST); BT: programs
+// checksums; 16: a per-lane file; -1: per-tile wave sums, for every program
+// a 16-entry file with 8 slots does not hold: larger files cost more in
+// occupancy than the sums cost in instructions); NTM: nontemporal loads
+// (NT_SRC) / stores (NT_DST); BT: programs
 // may bring leaves in batches (the RELOAD path costs registers, so the other
 // variants leave it out).  Batched programs keep leaves in slots 0 .. 7 and
 // only partial results above, which are written once and read once per
@@ -354,15 +347,15 @@ ColFn<P> col_fn_nt(bool nt) {
   return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT, P> : col_kernel<DT, OP, NL, NA, 0, BT, P>;
 }
 
-// accs: 0, 16 (8 slots), 32 (16 slots), or more: per-tile wave sums (batched
-// programs only)
+// accs: 0; 16 (8 slots, unbatched programs); more: per-tile wave sums
 template <int DT, int OP, bool BT, int P>
 ColFn<P> col_fn_variant(int leaves, int accs, bool nt) {
-  if constexpr (BT) {
-    if (accs > 32) return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 16, -1, BT, P>(nt);
+  if (accs > 16 || (BT && accs > 0))
+    return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 16, -1, BT, P>(nt);
+  if constexpr (!BT) {
+    if (accs > 0) return col_fn_nt<DT, OP, 8, 16, BT, P>(nt);
   }
-  if (leaves <= 8) return accs ? col_fn_nt<DT, OP, 8, 16, BT, P>(nt) : col_fn_nt<DT, OP, 8, 0, BT, P>(nt);
-  return accs ? col_fn_nt<DT, OP, 16, 32, BT, P>(nt) : col_fn_nt<DT, OP, 16, 0, BT, P>(nt);
+  return leaves <= 8 ? col_fn_nt<DT, OP, 8, 0, BT, P>(nt) : col_fn_nt<DT, OP, 16, 0, BT, P>(nt);
 }
 
 // batched programs (over 16 leaves) only come with over 16 ranks: P = 64

@@ -31,9 +31,18 @@ uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz))
 // units was built and measured, and its 64-leaf programs were bound by
 // instruction issue (64-rank ReduceScatter bf16 x 256 MiB: Ring 10.6 ms,
 // halving-doubling 11.2 ms, where batches of 8 run them in 2.9 ms).
-const ColVariant kVariants[] = {{16, 8, 0, false}, {16, 8, 16, false}, {16, 16, 0, false}, {16, 16, 32, false},
-                                {16, 8, 0, true},  {16, 8, 16, true},  {16, 16, 0, true},  {16, 16, 32, true},
-                                {16, 8, 64, true}, {16, 16, 64, true}};
+// Checksums: a file of 16 per-lane accumulators for programs of up to 8
+// leaves and 16 ops, per-tile wave sums for every other program.  Larger
+// accumulator files cost occupancy more than the sums cost instructions:
+// measured on MI355X with row checksums, files of 32 (16 slots, 191-260
+// VGPRs) against per-tile sums (104-114 VGPRs): AllReduce fp32 16 x 64 MiB
+// Ring 0.620 against 0.451 ms, 32 x 64 MiB halving-doubling 1.392 against
+// 0.840 ms, ReduceScatter bf16 32 x 256 MiB Ring 4.756 against 1.917 ms; the
+// 16-accumulator file stays where it fits (Ring AllReduce fp32 8 x 256 MiB
+// 0.744 against 0.786 ms).
+const ColVariant kVariants[] = {{16, 8, 0, false}, {16, 8, 16, false}, {16, 16, 0, false}, {16, 8, 64, false},
+                                {16, 16, 64, false}, {16, 8, 0, true}, {16, 16, 0, true}, {16, 8, 64, true},
+                                {16, 16, 64, true}};
 
 
 // Register slots of the largest column-kernel variant.

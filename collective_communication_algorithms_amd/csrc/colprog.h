@@ -13,9 +13,9 @@ namespace coll {
 
 // Register capacities of the column kernel's variants: `unit` bytes per lane
 // and column, at most `leaves` leaves and slots, and checksums of up to
-// `accs` ops (0: the variant computes no checksums; 16 and 32 are
-// accumulator files, 64 per-tile wave sums, for batched programs only);
-// `batched` variants
+// `accs` ops (0: the variant computes no checksums; 16 a per-lane
+// accumulator file, 8 slots and unbatched programs only; 64 per-tile wave
+// sums); `batched` variants
 // also run programs that bring their leaves in batches (RELOAD ops), at the
 // cost of the registers that takes.  Every list of a program holds at most
 // 64 instructions (one per lane).
