@@ -347,15 +347,19 @@ ColFn<P> col_fn_nt(bool nt) {
   return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT, P> : col_kernel<DT, OP, NL, NA, 0, BT, P>;
 }
 
-// accs: 0; 16 (8 slots, unbatched programs); more: per-tile wave sums
+// Unbatched programs hold at most 8 slots; accs 16 (a per-lane file) or
+// more (per-tile wave sums).  Batched programs: 8 slots, or 16 with slots 8
+// and up in LDS; accs: per-tile wave sums.
 template <int DT, int OP, bool BT, int P>
 ColFn<P> col_fn_variant(int leaves, int accs, bool nt) {
-  if (accs > 16 || (BT && accs > 0))
-    return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 16, -1, BT, P>(nt);
-  if constexpr (!BT) {
-    if (accs > 0) return col_fn_nt<DT, OP, 8, 16, BT, P>(nt);
+  if constexpr (BT) {
+    if (accs > 0) return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 16, -1, BT, P>(nt);
+    return leaves <= 8 ? col_fn_nt<DT, OP, 8, 0, BT, P>(nt) : col_fn_nt<DT, OP, 16, 0, BT, P>(nt);
+  } else {
+    (void)leaves;
+    if (accs > 16) return col_fn_nt<DT, OP, 8, -1, BT, P>(nt);
+    return accs > 0 ? col_fn_nt<DT, OP, 8, 16, BT, P>(nt) : col_fn_nt<DT, OP, 8, 0, BT, P>(nt);
   }
-  return leaves <= 8 ? col_fn_nt<DT, OP, 8, 0, BT, P>(nt) : col_fn_nt<DT, OP, 16, 0, BT, P>(nt);
 }
 
 // batched programs (over 16 leaves) only come with over 16 ranks: P = 64

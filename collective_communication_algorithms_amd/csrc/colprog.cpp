@@ -1,6 +1,7 @@
 #include "colprog.h"
 
 #include <algorithm>
+#include <cstdlib>
 #include <map>
 
 #include "bind.h"
@@ -26,8 +27,8 @@ struct Event {          // one covering row, in execution order
 uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz)) % 4) + 4) % 4); }
 
 // Variants the column kernel is built in (colkernel.hip), smallest first.
-// Programs with more leaves than 16 slots bring them in batches (batched
-// variants) rather than holding all of them: a 64-slot variant of 4-byte
+// Programs over 8 slots bring their leaves in batches (batched variants,
+// kPlainSlots) rather than holding all of them: a 64-slot variant of 4-byte
 // units was built and measured, and its 64-leaf programs were bound by
 // instruction issue (64-rank ReduceScatter bf16 x 256 MiB: Ring 10.6 ms,
 // halving-doubling 11.2 ms, where batches of 8 run them in 2.9 ms).
@@ -40,13 +41,20 @@ uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz))
 // 0.840 ms, ReduceScatter bf16 32 x 256 MiB Ring 4.756 against 1.917 ms; the
 // 16-accumulator file stays where it fits (Ring AllReduce fp32 8 x 256 MiB
 // 0.744 against 0.786 ms).
-const ColVariant kVariants[] = {{16, 8, 0, false}, {16, 8, 16, false}, {16, 16, 0, false}, {16, 8, 64, false},
-                                {16, 16, 64, false}, {16, 8, 0, true}, {16, 16, 0, true}, {16, 8, 64, true},
-                                {16, 16, 64, true}};
+const ColVariant kVariants[] = {{16, 8, 0, false}, {16, 8, 16, false}, {16, 8, 64, false}, {16, 8, 0, true},
+                                {16, 16, 0, true}, {16, 8, 64, true}, {16, 16, 64, true}};
 
 
 // Register slots of the largest column-kernel variant.
 constexpr int kMaxSlots = 16;
+// Programs over this many slots run batched: leaves in 8 register slots,
+// partial results in 8 more in LDS.  Measured on MI355X against holding 9-16
+// slots in registers (116-127 VGPRs, 4 waves per SIMD, against 92-114 and
+// 4-5), no checksums / checksums: ReduceScatter bf16 16 x 256 MiB 1.091 ->
+// 0.777 / 1.36 -> 0.95 ms, Reduce fp32 16 x 64 MiB 0.291 -> 0.190 ms,
+// AllReduce fp32 16 x 64 MiB halving-doubling 0.431 -> 0.384 / 0.511 ->
+// 0.409 ms, Ring 0.399 -> 0.382 ms.
+constexpr int kPlainSlots = 8;
 
 // One segment's program as instruction lists.
 struct Emitted {
@@ -526,7 +534,7 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
 
     Emitted em;
     if (!emit_plain(nodes, live, ops, stores, checksums, em)) return fail("internal: a value has no slot");
-    if (em.slots > kMaxSlots) {
+    if (em.slots > kPlainSlots) {
       Emitted eb;
       if (!emit_batched(nodes, ops, stores, checksums, eb)) return fail("a program needs more than 16 slots, in batches too");
       em = std::move(eb);

@@ -337,15 +337,15 @@ def test_forwarding_moves_what_the_plan_says(exec_mode):
     assert st["moved_bytes"] == st["hbm_bytes"] == 5 * (N - 1) * M
 
 
-@pytest.mark.parametrize("N", [17, 32, 64])
+@pytest.mark.parametrize("N", [9, 12, 16, 17, 32, 64])
 @pytest.mark.parametrize("dtype,sigma", [("float32", 1.0), ("bfloat16", 0.02), ("int32", 1.0)])
 def test_batched_leaves_many_ranks(N, dtype, sigma):
-    """More ranks than the column kernel's 16 slots: its programs
+    """More ranks than the column kernel's 8 register slots: its programs
     bring the leaves in batches of 8 and combine depth-first (the schedule's
-    own combines and operand order, so floats stay bit-exact).  Reductions
-    over 17, 32 and 64 ranks against the oracle, in one round trip, with and
-    without row checksums (programs over 32 ops sum each op's words across
-    the wave per tile instead of holding an accumulator per op)."""
+    own combines and operand order, so floats stay bit-exact), partial
+    results in LDS slots.  Reductions over 9 to 64 ranks against the oracle,
+    in one round trip, with and without row checksums (summed across the wave
+    per tile)."""
     import collective_communication_algorithms_amd as coll
     pow2 = (N & (N - 1)) == 0
     g = np.random.default_rng(N)
