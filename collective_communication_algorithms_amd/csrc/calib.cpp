@@ -37,12 +37,17 @@ coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t byt
 }
 
 coll_status_t coll_calib_pattern(void* const* loads, int nloads, void* const* stores, int nstores, size_t bytes,
-                                 void* stream) {
+                                 int groups_per_cu, void* stream) {
   const bool known = (nloads == 0 && nstores == 1) || (nloads == 8 && nstores == 8) || (nloads == 8 && nstores == 1) ||
                      (nloads == 1 && nstores == 7) || (nloads == 64 && nstores == 1) || (nloads == 1 && nstores == 63);
   if (!known) return report_error(COLL_ERR_UNSUPPORTED, "no calibration pattern with these load and store counts");
   if ((nloads > 0 && !loads) || !stores) return report_error(COLL_ERR_INVALID_ARG, "NULL buffer list");
   if (bytes % 1024) return report_error(COLL_ERR_INVALID_ARG, "pattern calibration needs a multiple of 1024 bytes");
+  if (groups_per_cu != 0 && (groups_per_cu < COLL_CALIB_MIN_GROUPS || groups_per_cu > COLL_CALIB_MAX_GROUPS))
+    return report_error(COLL_ERR_INVALID_ARG, "groups_per_cu outside 0 or [COLL_CALIB_MIN_GROUPS, COLL_CALIB_MAX_GROUPS]");
+  // the largest multiple of 512 bytes (the LDS allocation granule) of which
+  // groups_per_cu fit in a CU's 160 KiB
+  const uint32_t lds = groups_per_cu ? (uint32_t(160u * 1024u) / uint32_t(groups_per_cu)) & ~511u : 0u;
   RankPtrs p;
   for (int i = 0; i < COLL_MAX_RANKS; ++i) p.send[i] = p.recv[i] = 0;
   for (int i = 0; i < nloads; ++i) p.send[i] = reinterpret_cast<uint64_t>(loads[i]);
@@ -52,7 +57,7 @@ coll_status_t coll_calib_pattern(void* const* loads, int nloads, void* const* st
     if ((p.send[i] | p.recv[i]) % 16) return report_error(COLL_ERR_INVALID_ARG, "calibration needs 16-byte aligned buffers");
   }
   if (bytes == 0) return COLL_OK;
-  const hipError_t he = launch_calib_pattern(p, nloads, nstores, bytes, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t he = launch_calib_pattern(p, nloads, nstores, bytes, lds, reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return report_hip_error(he, "calibration launch");
   return COLL_OK;
 }

@@ -222,7 +222,32 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
         const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
         slot_set(v, uint32_t(j), ld16<(NTM & NT_SRC) != 0>(base + xl));
       }
+    } else if constexpr (NA > 0) {
+      // the 16-accumulator variant (5 waves per SIMD where the plain one
+      // holds 8): leaves in pairs, one branch per pair (a slot past the
+      // leaves loads the last leaf again), which the compiler issues with
+      // at most two loads in flight per wave.  Measured on MI355X with row
+      // checksums: Ring AllReduce fp32 8 x 256 MiB 0.741 -> 0.726 ms, bf16
+      // 0.830 -> 0.750 ms, tree Reduce 0.461 -> 0.425 ms, AllGather bf16
+      // 8 x 256 MiB 0.403 -> 0.418 ms (one leaf, loaded twice); pairs
+      // without checksums were slower (0.737 -> 0.758 ms), and so were all
+      // eight loads in flight together (0.764 ms).
+#pragma unroll
+      for (int j0 = 0; j0 < NR; j0 += 2) {
+        if (uint32_t(j0) < nfirst) {
+#pragma unroll
+          for (int j = j0; j < j0 + 2; ++j) {
+            const uint32_t jj = uint32_t(j) < nfirst ? uint32_t(j) : nfirst - 1u;
+            const uint32_t rk = uint32_t(__builtin_amdgcn_readlane(int(ld_w1), int(jj)));
+            const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
+            slot_set(v, uint32_t(j), ld16<(NTM & NT_SRC) != 0>(base + xl));
+          }
+        }
+      }
     } else {
+      // one branch per leaf: the compiler waits for each load before the
+      // next, which keeps one load in flight per wave; at the plain
+      // variant's occupancy that beats issuing them together
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
         if (uint32_t(j) < nfirst) {

@@ -539,7 +539,8 @@ __global__ __launch_bounds__(CALIB_THREADS) void calib_kernel(char* dst, const c
 // their u32 word sum, then S stores of it at the same offset of S buffers;
 // nontemporal.  L = 0 stores a constant (a fill).  Buffers may repeat (in
 // place: the stores go where the loads came from).  Lane r holds load
-// buffer r's and store buffer r's addresses.
+// buffer r's and store buffer r's addresses.  A launch may reserve LDS it
+// never touches, to cap the work groups a CU holds at once.
 template <int L, int S>
 __global__ __launch_bounds__(64) void calib_pattern_kernel(const RankPtrs p) {
   const uint32_t lane = threadIdx.x;
@@ -723,7 +724,8 @@ hipError_t launch_copy_rows(const CopyRowsArgs& a, uint64_t nrows, bool cks, boo
   return hipGetLastError();
 }
 
-hipError_t launch_calib_pattern(const RankPtrs& p, int nloads, int nstores, uint64_t bytes, hipStream_t stream) {
+hipError_t launch_calib_pattern(const RankPtrs& p, int nloads, int nstores, uint64_t bytes, uint32_t lds_bytes,
+                                hipStream_t stream) {
   void (*f)(RankPtrs) = nullptr;
   if (nloads == 0 && nstores == 1) f = calib_pattern_kernel<0, 1>;
   else if (nloads == 8 && nstores == 8) f = calib_pattern_kernel<8, 8>;
@@ -735,7 +737,7 @@ hipError_t launch_calib_pattern(const RankPtrs& p, int nloads, int nstores, uint
   const uint64_t g = bytes / 1024u;
   if (g == 0) return hipSuccess;
   if (g > 0x7fffffffu) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(f, dim3(uint32_t(g)), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(f, dim3(uint32_t(g)), dim3(64), lds_bytes, stream, p);
   return hipGetLastError();
 }
 

@@ -24,8 +24,10 @@ hipError_t launch_copy_rows(const CopyRowsArgs& a, uint64_t nrows, bool cks, boo
 // the slots read are set back to zero
 hipError_t launch_fold_sums(uint64_t* partial, uint64_t* out, uint64_t nrows, hipStream_t stream);
 // (nloads, nstores) in {(0,1), (8,8), (8,1), (1,7), (64,1), (1,63)}; p.send[0 .. nloads)
-// the load buffers, p.recv[0 .. nstores) the store buffers; bytes a multiple of 1024
-hipError_t launch_calib_pattern(const RankPtrs& p, int nloads, int nstores, uint64_t bytes, hipStream_t stream);
+// the load buffers, p.recv[0 .. nstores) the store buffers; bytes a multiple of 1024;
+// lds_bytes of LDS reserved per work group (unused; caps the groups per CU)
+hipError_t launch_calib_pattern(const RankPtrs& p, int nloads, int nstores, uint64_t bytes, uint32_t lds_bytes,
+                                hipStream_t stream);
 hipError_t launch_calib(void* dst, const void* a, const void* b, uint64_t bytes, hipStream_t stream);
 // the C ABI's error reporting (the message coll_last_error returns), for entry
 // points outside abi.cpp
