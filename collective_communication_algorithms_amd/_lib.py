@@ -98,7 +98,7 @@ def load() -> ctypes.CDLL:
                                    ctypes.c_void_p]
     lib.coll_calib_add.restype = ctypes.c_int
     lib.coll_calib_pattern.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
-                                       ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
+                                       ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     lib.coll_calib_pattern.restype = ctypes.c_int
     _lib = lib
     return lib

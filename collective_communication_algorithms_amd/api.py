@@ -217,17 +217,18 @@ def coll_calib_spin(out, iters, grid, stream=None):
                                       _stream_handle(out.device, stream)))
 
 
-def coll_calib_pattern(loads, stores, stream=None):
+def coll_calib_pattern(loads, stores, groups_per_cu=0, stream=None):
     """The column kernel's access pattern over GPU tensors: every tile of
     each tensor in ``loads`` summed and stored to each tensor in ``stores``
-    (all of one size in bytes; see include/coll.h for the supported counts)."""
+    (all of one size in bytes; see include/coll.h for the supported counts),
+    with at most ``groups_per_cu`` work groups per CU when nonzero."""
     ts = list(loads) + list(stores)
     nbytes = ts[0].numel() * ts[0].element_size()
     if any(t.numel() * t.element_size() != nbytes for t in ts):
         raise CollError(_lib.COLL_ERR_INVALID_ARG, "calibration buffers must all have one size")
     lp = (ctypes.c_void_p * max(len(loads), 1))(*[t.data_ptr() for t in loads])
     sp = (ctypes.c_void_p * len(stores))(*[t.data_ptr() for t in stores])
-    check(_lib.load().coll_calib_pattern(lp if loads else None, len(loads), sp, len(stores), nbytes,
+    check(_lib.load().coll_calib_pattern(lp if loads else None, len(loads), sp, len(stores), nbytes, int(groups_per_cu),
                                          _stream_handle(ts[0].device, stream)))
 
 

@@ -388,10 +388,15 @@ coll_status_t coll_calib_add(void* dst, const void* a, const void* b, size_t byt
  * an 8-rank Broadcast, (64, 1) a 64-rank ReduceScatter segment, (1, 63) a
  * 64-rank AllGather segment.  Each buffer holds `bytes` bytes (a multiple of
  * 1024), 16-byte aligned, owned by the caller; the stores overwrite them.
- * Errors: UNSUPPORTED for any other pair; INVALID_ARG for NULL or misaligned
- * buffers or sizes. */
+ * groups_per_cu: 0 for no cap, or COLL_CALIB_MIN_GROUPS .. COLL_CALIB_MAX_GROUPS
+ * to hold each CU to at most that many work groups at once (by reserving
+ * LDS the kernel never touches, 160 KiB per CU).  Errors: UNSUPPORTED for
+ * any other pair; INVALID_ARG for NULL or misaligned buffers or sizes, or
+ * groups_per_cu out of range. */
+#define COLL_CALIB_MIN_GROUPS 3
+#define COLL_CALIB_MAX_GROUPS 32
 coll_status_t coll_calib_pattern(void* const* loads, int nloads, void* const* stores, int nstores, size_t bytes,
-                                 void* stream);
+                                 int groups_per_cu, void* stream);
 
 /* A stand-in for compute, for measuring how far a collective on a side stream
  * hides behind it ([P2] 延迟掩盖：计算与通信的Overlap; Overlap的性能收益).

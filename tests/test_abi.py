@@ -148,14 +148,16 @@ def test_calib_pattern_argument_errors():
     one = (ctypes.c_void_p * 64)(*([aligned] * 64))
     bad = (ctypes.c_void_p * 64)(*([aligned + 4] * 64))
     null = (ctypes.c_void_p * 64)(*([None] * 64))
-    assert lib.coll_calib_pattern(one, 2, one, 2, 1024, None) == UNS
-    assert lib.coll_calib_pattern(one, 8, one, 7, 1024, None) == UNS
-    assert lib.coll_calib_pattern(one, 8, None, 8, 1024, None) == INV
-    assert lib.coll_calib_pattern(None, 8, one, 8, 1024, None) == INV
-    assert lib.coll_calib_pattern(null, 64, one, 1, 1024, None) == INV
-    assert lib.coll_calib_pattern(one, 1, bad, 63, 1024, None) == INV
-    assert lib.coll_calib_pattern(one, 8, one, 8, 1000, None) == INV
-    assert lib.coll_calib_pattern(None, 0, one, 1, 0, None) == OK     # nothing to do
+    assert lib.coll_calib_pattern(one, 2, one, 2, 1024, 0, None) == UNS
+    assert lib.coll_calib_pattern(one, 8, one, 7, 1024, 0, None) == UNS
+    assert lib.coll_calib_pattern(one, 8, None, 8, 1024, 0, None) == INV
+    assert lib.coll_calib_pattern(None, 8, one, 8, 1024, 0, None) == INV
+    assert lib.coll_calib_pattern(null, 64, one, 1, 1024, 0, None) == INV
+    assert lib.coll_calib_pattern(one, 1, bad, 63, 1024, 0, None) == INV
+    assert lib.coll_calib_pattern(one, 8, one, 8, 1000, 0, None) == INV
+    assert lib.coll_calib_pattern(None, 0, one, 1, 0, 0, None) == OK     # nothing to do
+    for groups in (-1, 1, 2, 33):
+        assert lib.coll_calib_pattern(one, 8, one, 8, 1024, groups, None) == INV
 
 
 def test_plan_capacity_protocol():

@@ -2,7 +2,8 @@
 ceilings compute what they claim, so that their rates are rates of real
 work: the copy and add streams, and every access pattern of
 coll_calib_pattern (each store buffer ends with the u32 word sum, per 16-byte
-unit, of the load buffers; a fill writes every unit)."""
+unit, of the load buffers; a fill writes every unit), with and without a cap
+on the work groups per CU."""
 
 import numpy as np
 import pytest
@@ -25,8 +26,9 @@ def test_copy_and_add_streams(gpu_device):
     assert torch.equal(c, a + b)
 
 
-@pytest.mark.parametrize("nl,ns", [(0, 1), (8, 8), (8, 1), (1, 7), (64, 1), (1, 63)])
-def test_access_patterns(gpu_device, nl, ns):
+@pytest.mark.parametrize("nl,ns,groups", [(0, 1, 0), (8, 8, 0), (8, 8, 4), (8, 8, 32), (8, 1, 0), (1, 7, 0),
+                                          (64, 1, 3), (1, 63, 0)])
+def test_access_patterns(gpu_device, nl, ns, groups):
     import torch
     import collective_communication_algorithms_amd as coll
     nbuf = max(nl, ns + (1 if nl == 1 else 0), 1)
@@ -42,7 +44,7 @@ def test_access_patterns(gpu_device, nl, ns):
     in_place = nl == ns
     loads = views[:nl]
     stores = views[:ns] if in_place else (views[nbuf - ns:] if nl else views[:ns])
-    coll.coll_calib_pattern(loads, stores)
+    coll.coll_calib_pattern(loads, stores, groups_per_cu=groups)
     torch.cuda.synchronize()
     got = t.cpu().numpy().view(np.uint32)
     src = host[:, :1024]
