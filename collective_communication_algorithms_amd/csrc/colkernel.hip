@@ -138,10 +138,85 @@ struct Accs {
 };
 template <>
 struct Accs<0> {};
-// NA < 0: no accumulator file; each op's words are summed across the wave
-// per tile and lane k keeps op k's running total (any op count up to 64).
+// NA < 0: no accumulator file; each op's words are reduced across the wave
+// per tile as the ops arrive (any op count up to 64), like the digits of a
+// binary counter: a level-j group holds the partial sums of 2^j consecutive
+// ops, two lanes per pair of ops apart.  Merging the level-j groups A (the
+// earlier ops) and B pairs every lane with a partner (level 0: l ^ 7 by
+// row_half_mirror, 1: l ^ 1 and 2: l ^ 2 by quad permutes, 3: l ^ 8 by
+// row_ror:8, 4: l ^ 16 and 5: l ^ 32 by the permlane swaps): a lane whose
+// level bit is clear keeps A's words plus its partner's, the other B's.
+// Each level pairs lanes that hold the same op, so after six levels lane l
+// holds the wave total of op op_of_lane(l).  A 64-op group costs 63 merges
+// of a few instructions each, against 64 full wave sums.
 template <>
-struct Accs<-1> {};
+struct Accs<-1> {
+  uint64_t l[6];  // the pending group at each level
+};
+
+// The lane that carries op o after six merge levels (the inverse of the
+// level bits chosen above: op bit 0 is lane bit 2, op bits 1 and 2 are lane
+// bits 0 and 1, op bits 3 .. 5 are lane bits 3 .. 5).
+__device__ __forceinline__ uint32_t op_of_lane(uint32_t lane) {
+  return ((lane >> 2) & 1u) | ((lane & 3u) << 1) | (lane & 0x38u);
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t partner_word(uint32_t v) {
+  // row_half_mirror, quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:8
+  constexpr int ctrl = J == 0 ? 0x141 : J == 1 ? 0xB1 : J == 2 ? 0x4E : 0x128;
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), ctrl, 0xf, 0xf, false));
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t merge_level(uint64_t a, uint64_t b, uint32_t lane) {
+  if constexpr (J < 4) {
+    constexpr uint32_t bit = J == 0 ? 4u : J == 1 ? 1u : J == 2 ? 2u : 8u;
+    const bool second = (lane & bit) != 0;
+    const uint64_t keep = second ? b : a, give = second ? a : b;
+    const uint64_t got = uint64_t(partner_word<J>(uint32_t(give))) |
+                         (uint64_t(partner_word<J>(uint32_t(give >> 32))) << 32);
+    return keep + got;
+  } else {
+    // the swap exchanges the second half of rows (J = 4: the odd 16-lane
+    // rows; J = 5: the upper 32 lanes) of its first operand with the first
+    // half of its second: afterwards the two registers hold, lane for lane,
+    // A's words and its partner's where the level bit is clear, B's where it
+    // is set
+    const auto lo = J == 4 ? __builtin_amdgcn_permlane16_swap(uint32_t(a), uint32_t(b), false, false)
+                           : __builtin_amdgcn_permlane32_swap(uint32_t(a), uint32_t(b), false, false);
+    const auto hi = J == 4 ? __builtin_amdgcn_permlane16_swap(uint32_t(a >> 32), uint32_t(b >> 32), false, false)
+                           : __builtin_amdgcn_permlane32_swap(uint32_t(a >> 32), uint32_t(b >> 32), false, false);
+    return ((uint64_t(hi[0]) << 32) | lo[0]) + ((uint64_t(hi[1]) << 32) | lo[1]);
+  }
+}
+
+// Op k's words c enter at level 0; every set bit of k below the first clear
+// one completes a group, which merges with the pending group of its level.
+// A completed 64-op group is added to the lane's running total.
+template <int J>
+__device__ __forceinline__ void push_op(Accs<-1>& s, uint64_t c, uint32_t k, uint32_t lane, uint64_t& total) {
+  if constexpr (J == 6) {
+    total += c;
+  } else {
+    if (k & (1u << J)) push_op<J + 1>(s, merge_level<J>(s.l[J], c, lane), k, lane, total);
+    else s.l[J] = c;
+  }
+}
+
+// After n ops (n <= 64): the pending groups (one per set bit of n, earlier
+// ops at higher levels) and a partial group carried up from below merge
+// into one 64-op group whose missing ops are zero.
+template <int J>
+__device__ __forceinline__ uint64_t flush_ops(const Accs<-1>& s, uint32_t n, uint64_t c, uint32_t lane) {
+  if constexpr (J == 6) {
+    return c;
+  } else {
+    if (n & (1u << J)) c = merge_level<J>(s.l[J], c, lane);
+    else if (n & ((1u << J) - 1u)) c = merge_level<J>(c, 0, lane);
+    return flush_ops<J + 1>(s, n, c, lane);
+  }
+}
 
 // 16 bytes per lane and column; NL slots; NA checksum accumulators (0: no
 // checksums; 16: a per-lane file; -1: per-tile wave sums, for every program
@@ -188,7 +263,9 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
   const uint64_t s0 = wk.s0, s1 = wk.s1, xs = s0 & ~(UNIT - 1);
   Accs<NA> acc;
   if constexpr (NA > 0) acc.clear();
-  uint64_t mine = 0;  // NA < 0: lane k's running total of op k
+  if constexpr (NA < 0)
+    for (int j = 0; j < 6; ++j) acc.l[j] = 0;
+  uint64_t mine = 0;  // NA < 0: lane l's running total of op op_of_lane(l)
   for (uint32_t t = 0; t < wk.ntiles; ++t) {
     const uint64_t x = wk.c0 + uint64_t(t) * TB + uint64_t(lane) * UNIT;
     const bool any = x < s1 && x + UNIT > s0;
@@ -292,10 +369,10 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
       } else if constexpr (NA < 0) {
         const uint32_t shift = uint32_t(__builtin_amdgcn_readlane(int(op_w1), int(k))) & 3u;
         const uint64_t w = any ? unit_words<DT>(val, x, s0, s1, full, shift) : 0;
-        const uint64_t tot = wave_sum(w);  // every lane takes part
-        if (lane == k) mine += tot;
+        push_op<0>(acc, w, k, lane, mine);  // every lane takes part
       }
     }
+    if constexpr (NA < 0) mine += flush_ops<0>(acc, nop, 0, lane);
     // Batched programs: every load of this tile has been consumed (each leaf
     // an op or a store reads); an explicit wait tells the compiler so, which
     // it cannot see across the dynamic op loop, and would otherwise wait for
@@ -312,16 +389,17 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
       else if (any) store_part<DT>(base + x, val, x, s0, s1);
     }
   }
-  if constexpr (NA != 0) {
-    // op k's wave total goes to lane k, which stores it in this work group's
-    // own slot: no atomics, every slot written once per call
-    if constexpr (NA > 0) {
-      for (uint32_t k = 0; k < nop; ++k) {
-        const uint64_t tot = wave_sum(acc.get(k));
-        if (lane == k) mine = tot;
-      }
+  // op k's wave total goes to one lane, which stores it in this work group's
+  // own slot: no atomics, every slot written once per call
+  if constexpr (NA > 0) {
+    for (uint32_t k = 0; k < nop; ++k) {
+      const uint64_t tot = wave_sum(acc.get(k));
+      if (lane == k) mine = tot;
     }
     if (lane < nop) *gptr<uint64_t>(reinterpret_cast<char*>(a.partial + wk.part + lane)) = mine;
+  } else if constexpr (NA < 0) {
+    const uint32_t o = op_of_lane(lane);  // a permutation of 0 .. 63
+    if (o < nop) *gptr<uint64_t>(reinterpret_cast<char*>(a.partial + wk.part + o)) = mine;
   }
 }
 

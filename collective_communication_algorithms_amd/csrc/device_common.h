@@ -116,8 +116,50 @@ __device__ __forceinline__ uint32_t combine_word(uint32_t d, uint32_t s) {
   }
 }
 
+// Two binary32 values to a word of two bfloat16 (lo in the low half) with
+// the hardware's conversion (v_cvt_pk_bf16_f32): round to nearest even, the
+// same bits as bf16_rne for every value but NaN, whose sign and payload the
+// hardware keeps.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// bfloat16 sum of 16 bytes: the eight binary32 sums converted in pairs by the
+// hardware, which costs about half the instructions of rounding on the bit
+// pattern.  Where any lane of the wave holds a NaN sum (a branch no wave
+// takes on finite data) the whole wave rounds by bf16_rne instead, which
+// gives the same bits for every other value and 0x7FC0 for every NaN (the
+// ballot covers the active lanes, so any exec mask is fine).
+__device__ __forceinline__ u32x4 sum16_bf16(u32x4 d, u32x4 s) {
+  float lo[4], hi[4];
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w}, sw[4] = {s.x, s.y, s.z, s.w};
+  uint64_t nan = 0;  // lanes with a NaN sum, kept in scalar registers
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = __uint_as_float(dw[i] << 16) + __uint_as_float(sw[i] << 16);
+    hi[i] = __uint_as_float(dw[i] & 0xffff0000u) + __uint_as_float(sw[i] & 0xffff0000u);
+    nan |= __builtin_amdgcn_ballot_w64(__builtin_isunordered(lo[i], hi[i]));
+  }
+  u32x4 r;
+  r.x = cvt_pk_bf16(lo[0], hi[0]);
+  r.y = cvt_pk_bf16(lo[1], hi[1]);
+  r.z = cvt_pk_bf16(lo[2], hi[2]);
+  r.w = cvt_pk_bf16(lo[3], hi[3]);
+  if (nan) {
+    r.x = bf16_rne(lo[0]) | (bf16_rne(hi[0]) << 16);
+    r.y = bf16_rne(lo[1]) | (bf16_rne(hi[1]) << 16);
+    r.z = bf16_rne(lo[2]) | (bf16_rne(hi[2]) << 16);
+    r.w = bf16_rne(lo[3]) | (bf16_rne(hi[3]) << 16);
+  }
+  return r;
+}
+
 template <int DT, int OP>
 __device__ __forceinline__ u32x4 combine16(u32x4 d, u32x4 s) {
+  if constexpr (DT == DT_BF16 && OP == OP_SUM) return sum16_bf16(d, s);
   u32x4 r;
   r.x = combine_word<DT, OP>(d.x, s.x);
   r.y = combine_word<DT, OP>(d.y, s.y);

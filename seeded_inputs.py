@@ -10,7 +10,9 @@ Recipe: rank r of workload w uses numpy ``Generator(PCG64(1000 * w + r))``.
   uint8   uniform in [0, 255]
   float32 standard normal scaled by sigma
   bf16    float32 standard normal scaled by sigma, converted to bfloat16 by
-          torch's CPU conversion (a library routine), stored as uint16 bits
+          torch's CPU conversion (a library routine), stored as uint16 bits;
+          plant_bf16_specials writes NaN / infinity / extreme patterns into
+          seeded places of such buffers
 
 Large device-resident workloads use ``device_rank_tensors``: torch's own
 seeded generator on the device, same seeds.  Those inputs come from PyTorch's
@@ -57,6 +59,27 @@ def rank_array(workload: int, rank: int, count: int, dtype: str,
 
 def rank_arrays(workload: int, nranks: int, count: int, dtype: str, **kw) -> list:
     return [rank_array(workload, r, count, dtype, **kw) for r in range(nranks)]
+
+
+# bfloat16 bit patterns outside the normal range of the other inputs: quiet and
+# signalling NaNs of either sign with payloads, the infinities, the largest
+# finite values (two of them add past the range), subnormals and signed zeros
+BF16_SPECIALS = np.array([0x7FC1, 0xFFC0, 0x7F81, 0xFFFF, 0x7FA5, 0x7F80, 0xFF80, 0x7F7F, 0xFF7F, 0x7F7F,
+                          0x0001, 0x8001, 0x007F, 0x8000, 0x0000], dtype=np.uint16)
+
+
+def plant_bf16_specials(arrays: list, seed: int, nplant: int) -> list:
+    """Copies of bfloat16 rank buffers with ``nplant`` entries of BF16_SPECIALS
+    written at seeded (rank, position) pairs, so that most of the buffer stays
+    ordinary and a few places meet NaN, infinity and overflow."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = [np.array(a, dtype=np.uint16, copy=True) for a in arrays]
+    ranks = rng.integers(0, len(out), size=nplant)
+    pos = rng.integers(0, len(out[0]), size=nplant)
+    vals = rng.choice(BF16_SPECIALS, size=nplant)
+    for r, i, v in zip(ranks, pos, vals):
+        out[int(r)][int(i)] = v
+    return out
 
 
 def to_torch_dtype(dtype: str):

@@ -285,6 +285,30 @@ def test_many_step_schedules(exec_mode):
     assert_parity("allreduce", "ring", b, "bfloat16", checksums=True)
 
 
+@pytest.mark.parametrize("exec_mode", [0, 2])
+def test_bf16_sums_with_nan_infinity_and_overflow(exec_mode):
+    """bfloat16 sums where a few inputs are NaN (either sign, with payloads),
+    infinite, the largest finite values or subnormal: every NaN result is
+    0x7FC0 and every other result the round to nearest even of the binary32
+    sum, bit for bit with the oracle, row checksums included.  Most tiles hold
+    none of these values (the kernels' usual rounding); the few that do take
+    the NaN path.  exec 0: the column kernel (8 ranks: the per-lane checksum
+    file; 64 ranks: batched leaves and merged wave sums); exec 2: the row
+    kernels."""
+    import collective_communication_algorithms_amd as coll
+    coll.coll_set_option("exec", exec_mode)
+    with np.errstate(over="ignore", invalid="ignore"):
+        a = si.plant_bf16_specials(si.rank_arrays(6, 8, 8 * 4096 + 37, "bfloat16", sigma=0.5), 61, 24)
+        for algo in ("ring", "rhd", "dbt"):
+            got, _ = assert_parity("allreduce", algo, a, "bfloat16", checksums=True)
+            assert np.any(got[0] == 0x7FC0) and np.any((got[0] & 0x7FFF) == 0x7F80), algo
+            assert np.count_nonzero((got[0] & 0x7F80) == 0x7F80) < 100, algo   # most results stay finite
+        assert_parity("reduce", "binomial", a, "bfloat16", root=3, checksums=True)
+        b = si.plant_bf16_specials(si.rank_arrays(7, 64, 64 * 300 + 17, "bfloat16", sigma=0.5), 62, 16)
+        assert_parity("reducescatter", "ring", b, "bfloat16", checksums=True)
+        assert_parity("allreduce", "rhd", b, "bfloat16", checksums=True)
+
+
 def test_repeated_calls_reuse_cached_schedules():
     import torch
     import collective_communication_algorithms_amd as coll
