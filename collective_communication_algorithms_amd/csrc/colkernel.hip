@@ -153,6 +153,9 @@ template <>
 struct Accs<-1> {
   uint64_t l[6];  // the pending group at each level
 };
+// NA = -2: the same merged sums, with the leaves loaded in pairs (below).
+template <>
+struct Accs<-2> : Accs<-1> {};
 
 // The lane that carries op o after six merge levels (the inverse of the
 // level bits chosen above: op bit 0 is lane bit 2, op bits 1 and 2 are lane
@@ -299,16 +302,17 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
         const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
         slot_set(v, uint32_t(j), ld16<(NTM & NT_SRC) != 0>(base + xl));
       }
-    } else if constexpr (NA > 0) {
-      // the 16-accumulator variant (5 waves per SIMD where the plain one
-      // holds 8): leaves in pairs, one branch per pair (a slot past the
-      // leaves loads the last leaf again), which the compiler issues with
-      // at most two loads in flight per wave.  Measured on MI355X with row
-      // checksums: Ring AllReduce fp32 8 x 256 MiB 0.741 -> 0.726 ms, bf16
-      // 0.830 -> 0.750 ms, tree Reduce 0.461 -> 0.425 ms, AllGather bf16
-      // 8 x 256 MiB 0.403 -> 0.418 ms (one leaf, loaded twice); pairs
-      // without checksums were slower (0.737 -> 0.758 ms), and so were all
-      // eight loads in flight together (0.764 ms).
+    } else if constexpr (NA > 0 || NA == -2) {
+      // the checksum variants of up to 16 ops (4-6 waves per SIMD where the
+      // plain one holds 8): leaves in pairs, one branch per pair (a slot
+      // past the leaves loads the last leaf again), which the compiler
+      // issues with at most two loads in flight per wave.  Measured on
+      // MI355X with row checksums: Ring AllReduce fp32 8 x 256 MiB 0.741 ->
+      // 0.726 ms, bf16 0.830 -> 0.750 ms, tree Reduce 0.461 -> 0.425 ms;
+      // pairs without checksums were slower (0.737 -> 0.758 ms), and so
+      // were all eight loads in flight together (0.764 ms).  Single-leaf
+      // programs load one at a time (NA = -1): AllGather bf16 8 x 256 MiB
+      // 0.418 ms in pairs (the leaf loaded twice), 0.394 ms alone.
 #pragma unroll
       for (int j0 = 0; j0 < NR; j0 += 2) {
         if (uint32_t(j0) < nfirst) {
@@ -450,18 +454,20 @@ ColFn<P> col_fn_nt(bool nt) {
   return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT, P> : col_kernel<DT, OP, NL, NA, 0, BT, P>;
 }
 
-// Unbatched programs hold at most 8 slots; accs 16 (a per-lane file) or
-// more (per-tile wave sums).  Batched programs: 8 slots, or 16 with slots 8
-// and up in LDS; accs: per-tile wave sums.
+// Unbatched programs hold at most 8 slots; checksums of up to 8 ops: merged
+// wave sums, the leaves in pairs (one leaf: alone); 9 .. 16 ops: a per-lane
+// file; more: merged wave sums.  Batched programs: 8 slots, or 16 with slots
+// 8 and up in LDS; checksums: merged wave sums.
 template <int DT, int OP, bool BT, int P>
 ColFn<P> col_fn_variant(int leaves, int accs, bool nt) {
   if constexpr (BT) {
     if (accs > 0) return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 16, -1, BT, P>(nt);
     return leaves <= 8 ? col_fn_nt<DT, OP, 8, 0, BT, P>(nt) : col_fn_nt<DT, OP, 16, 0, BT, P>(nt);
   } else {
-    (void)leaves;
     if (accs > 16) return col_fn_nt<DT, OP, 8, -1, BT, P>(nt);
-    return accs > 0 ? col_fn_nt<DT, OP, 8, 16, BT, P>(nt) : col_fn_nt<DT, OP, 8, 0, BT, P>(nt);
+    if (accs > 8) return col_fn_nt<DT, OP, 8, 16, BT, P>(nt);
+    if (accs > 0) return leaves <= 1 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 8, -2, BT, P>(nt);
+    return col_fn_nt<DT, OP, 8, 0, BT, P>(nt);
   }
 }
 

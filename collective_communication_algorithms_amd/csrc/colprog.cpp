@@ -33,16 +33,24 @@ uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz))
 // instruction issue (64-rank ReduceScatter bf16 x 256 MiB: Ring 10.6 ms,
 // halving-doubling 11.2 ms, where batches of 8 run them in 2.9 ms).
 // Checksums: a file of 16 per-lane accumulators for programs of up to 8
-// leaves and 16 ops, per-tile wave sums for every other program.  Larger
-// accumulator files cost occupancy more than the sums cost instructions:
-// measured on MI355X with row checksums, files of 32 (16 slots, 191-260
-// VGPRs) against per-tile sums (104-114 VGPRs): AllReduce fp32 16 x 64 MiB
-// Ring 0.620 against 0.451 ms, 32 x 64 MiB halving-doubling 1.392 against
-// 0.840 ms, ReduceScatter bf16 32 x 256 MiB Ring 4.756 against 1.917 ms; the
-// 16-accumulator file stays where it fits (Ring AllReduce fp32 8 x 256 MiB
-// 0.744 against 0.786 ms).
-const ColVariant kVariants[] = {{16, 8, 0, false}, {16, 8, 16, false}, {16, 8, 64, false}, {16, 8, 0, true},
-                                {16, 16, 0, true}, {16, 8, 64, true}, {16, 16, 64, true}};
+// leaves and 16 ops, wave sums merged across lanes as the ops arrive for the
+// others (colkernel.hip).  Larger accumulator files cost occupancy more than
+// the sums cost instructions: measured on MI355X with row checksums, files of
+// 32 (16 slots, 191-260 VGPRs) against per-tile sums (104-114 VGPRs):
+// AllReduce fp32 16 x 64 MiB Ring 0.620 against 0.451 ms, 32 x 64 MiB
+// halving-doubling 1.392 against 0.840 ms, ReduceScatter bf16 32 x 256 MiB
+// Ring 4.756 against 1.917 ms.  The 16-accumulator file (97 VGPRs for fp32)
+// stays where it wins: Ring AllReduce fp32 8 x 256 MiB 0.724 ms against 0.758
+// ms with merged sums (80 VGPRs): a wave that stores 8 buffers runs best at
+// the file's lower occupancy, as the plain 8-load, 8-store pattern does at 4
+// work groups per CU.  Programs of up to 8 ops and at most 2 stores run
+// faster merged (bf16 8 x 256 MiB tree Reduce 0.464 -> 0.426 ms, Ring
+// ReduceScatter 0.454 -> 0.416 ms), and so do single-leaf programs
+// (AllGather bf16 8 x 256 MiB 0.418 -> 0.394 ms, its leaf loaded alone: the
+// {1 slot, 8 ops} entry).
+const ColVariant kVariants[] = {{16, 8, 0, false},  {16, 1, 8, false}, {16, 8, 8, false, 2}, {16, 8, 16, false},
+                                {16, 8, 64, false}, {16, 8, 0, true},  {16, 16, 0, true},    {16, 8, 64, true},
+                                {16, 16, 64, true}};
 
 
 // Register slots of the largest column-kernel variant.
@@ -568,7 +576,9 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
   }
   for (const ColVariant& v : kVariants) {
     if ((v.accs > 0) != checksums || v.batched != p.batched) continue;
-    if (int(p.max_slots) > v.leaves || (checksums && int(p.max_ops) > v.accs) || sz > v.unit) continue;
+    if (int(p.max_slots) > v.leaves || (checksums && int(p.max_ops) > v.accs) || sz > v.unit ||
+        int(p.max_stores) > v.stores)
+      continue;
     p.v = v;
     p.ok = true;
     return p;

@@ -14,16 +14,19 @@ namespace coll {
 // Register capacities of the column kernel's variants: `unit` bytes per lane
 // and column, at most `leaves` leaves and slots, and checksums of up to
 // `accs` ops (0: the variant computes no checksums; 16 a per-lane
-// accumulator file, 8 slots and unbatched programs only; 64 per-tile wave
-// sums); `batched` variants
+// accumulator file, 8 slots and unbatched programs only; 8 and 64 wave sums
+// merged across lanes); `batched` variants
 // also run programs that bring their leaves in batches (RELOAD ops), at the
 // cost of the registers that takes.  Every list of a program holds at most
 // 64 instructions (one per lane).
+constexpr int COL_LIST_MAX_STORES = 64;  // one store per lane
+
 struct ColVariant {
   int unit = 16;
   int leaves = 8;
   int accs = 0;
   bool batched = false;
+  int stores = COL_LIST_MAX_STORES;  // the variant is picked for programs of at most this many stores
 };
 
 // With checksums: row `row`'s checksum over segment `seg` is the sum of op
