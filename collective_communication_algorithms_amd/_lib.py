@@ -23,7 +23,7 @@ ALGOS = {"default": 0, "ring": 1, "rhd": 2, "dbt": 3, "binomial": 4, "chain_pipe
 KINDS = {"allreduce": 0, "reducescatter": 1, "allgather": 2, "broadcast": 3, "scatter": 4, "gather": 5,
          "alltoall": 6, "reduce": 7}
 OPTIONS = {"exec": 0, "group_tiles": 1, "max_grid": 2, "nontemporal": 3, "reverse": 4, "model_alpha_ns": 5,
-           "model_beta_gbps": 6, "cache_bytes": 7, "col_tiles": 8, "timing": 9}
+           "model_beta_gbps": 6, "cache_bytes": 7, "col_tiles": 8, "timing": 9, "a2a_direct": 10}
 MAX_RANKS = 128
 
 COLLECTIVES = ("coll_allreduce", "coll_reducescatter", "coll_allgather", "coll_broadcast", "coll_scatter",

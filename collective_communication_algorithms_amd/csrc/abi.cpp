@@ -46,6 +46,7 @@ std::atomic<int64_t> opt_reverse{1};
 std::atomic<int64_t> opt_alpha_ns{1060};   // COLL_ALGO_AUTO: fitted per-step cost on MI355X
 std::atomic<int64_t> opt_beta_gbps{8200};  // COLL_ALGO_AUTO: fitted schedule-byte rate on MI355X
 std::atomic<int64_t> opt_cache_bytes{int64_t(1) << 31};  // device memory the schedule cache may hold
+std::atomic<int64_t> opt_a2a_direct{1};  // 1: an AllToAll of whole-block rows as one direct copy of its blocks
 std::atomic<bool> g_debug{false};      // COLL_DEBUG: one line per call on stderr
 
 const char* kind_name(coll_kind_t k) {
@@ -157,9 +158,10 @@ struct ColDev {
 // references (one per row: its work groups' slots).
 struct CopyDev {
   bool tried = false, ok = false;
-  bool whole = false;           // every row of the schedule (Pairwise); else the rows of phase 0
+  bool whole = false;           // the whole schedule; else the rows of phase 0
   bool pinned = false;          // used by a captured call: tables kept until coll_finalize
-  uint32_t nrows = 0, wgs_per_row = 0;
+  uint32_t nrows = 0, wgs_per_row = 0;  // copy rows
+  uint32_t nfold = 0;           // schedule rows whose checksums the copy's slots make
   uint64_t row_bytes = 0;
   CopyRow* d_rows = nullptr;
   uint32_t* d_row_off = nullptr;
@@ -171,7 +173,7 @@ struct Entry {
   Schedule sched;
   Bound bound;
   ColDev col[2];                // [checksums on]
-  CopyDev copy;
+  CopyDev copy[2];              // [COLL_OPT_A2A_DIRECT]
   bool pinned = false;          // used by a captured call: never evicted before coll_finalize
   std::vector<int8_t> multi;    // per phase: groups average two or more pieces per step (-1: not known yet)
   int dev = 0;
@@ -282,12 +284,75 @@ size_t copy_prefix_rows(const Schedule& s, int sz) {
   return (row_bytes + 1023u) / 1024u * nrows <= 0x7fffffffu ? nrows : 0;
 }
 
+// The send block each row of an AllToAll carries (block j of rank i: i * N +
+// j), when every row moves one whole block of count / N elements: the
+// schedule run on block identities with the pages' step model (every source
+// of a step is read before any row of it writes).  Empty when a row moves
+// anything else, reads a block no row has written, two rows of a step write
+// one block, or the receive buffers end other than the AllToAll defines
+// (block i of recv_j = block j of send_i).  Since the rows only move
+// blocks, a row's destination after it holds exactly the block it carries.
+std::vector<uint32_t> alltoall_carried(const Schedule& s) {
+  if (s.kind != COLL_K_ALLTOALL || s.rows.empty() || s.N < 1) return {};
+  const int64_t N = s.N, B = s.count / N;
+  if (B <= 0 || N * N >= int64_t(0xffffffff)) return {};
+  constexpr uint32_t NONE = 0xffffffffu;
+  std::vector<uint32_t> recv(size_t(N * N), NONE), carried(s.rows.size(), NONE);
+  std::vector<uint8_t> hit(size_t(N * N), 0);
+  for (const Step& st : s.steps) {
+    const size_t r0 = size_t(st.first), r1 = size_t(st.first + st.nrows);
+    for (size_t i = r0; i < r1; ++i) {
+      const Row& r = s.rows[i];
+      if (r.reduce || r.n != B || r.src < 0 || r.src >= N || r.dst < 0 || r.dst >= N || r.src_off < 0 ||
+          r.dst_off < 0 || r.src_off % B || r.dst_off % B || r.src_off / B >= N || r.dst_off / B >= N)
+        return {};
+      const size_t from = size_t(int64_t(r.src) * N + r.src_off / B);
+      const uint32_t id = r.from_send ? uint32_t(from) : recv[from];
+      if (id == NONE) return {};
+      carried[i] = id;
+    }
+    for (size_t i = r0; i < r1; ++i) {
+      const Row& r = s.rows[i];
+      const size_t to = size_t(int64_t(r.dst) * N + r.dst_off / B);
+      if (hit[to]) return {};
+      hit[to] = 1;
+      recv[to] = carried[i];
+    }
+    for (size_t i = r0; i < r1; ++i) hit[size_t(int64_t(s.rows[i].dst) * N + s.rows[i].dst_off / B)] = 0;
+  }
+  for (int64_t i = 0; i < N; ++i)
+    for (int64_t j = 0; j < N; ++j)
+      if (recv[size_t(j * N + i)] != uint32_t(i * N + j)) return {};
+  return carried;
+}
+
+// Copy rows of the one direct copy that runs a whole AllToAll, or 0.
+// Pairwise's rows are that copy as they stand; with COLL_OPT_A2A_DIRECT, any
+// AllToAll whose rows each move one whole block runs as the copy of its N * N
+// blocks (`carried`: the block each row carries).  Blocks must be multiples
+// of 16 bytes, and the copy's grid must fit.
+uint64_t whole_copy_rows(const Schedule& s, int sz, bool direct, std::vector<uint32_t>* carried) {
+  if (s.kind != COLL_K_ALLTOALL || s.rows.empty()) return 0;
+  if (copy_prefix_rows(s, sz) == s.rows.size()) return s.rows.size();
+  if (!direct) return 0;
+  const uint64_t n = uint64_t(s.N) * uint64_t(s.N), row_bytes = uint64_t(s.count / s.N) * uint64_t(sz);
+  if (row_bytes == 0 || row_bytes % 16u || (row_bytes + 1023u) / 1024u * n > 0x7fffffffu) return 0;
+  std::vector<uint32_t> c = alltoall_carried(s);
+  if (c.empty()) return 0;
+  if (carried) *carried = std::move(c);
+  return n;
+}
+
 PlannedCost planned_cost(const Schedule& s, int sz, uint32_t cus) {
   if (col_mode() && s.kind != COLL_K_ALLTOALL) {
     const ColPlan cp = compile_colplan(s, sz, true, t_sums != nullptr);
     if (cp.ok) return PlannedCost{1, int64_t(cp.moved_bytes)};
   }
-  if (col_mode() && copy_prefix_rows(s, sz) == s.rows.size()) return PlannedCost{1, count_schedule(s, sz).hbm_bytes};
+  if (col_mode() && s.kind == COLL_K_ALLTOALL) {
+    // every block read once and written once
+    const uint64_t n = whole_copy_rows(s, sz, opt_a2a_direct.load() != 0, nullptr);
+    if (n) return PlannedCost{1, int64_t(2 * n * uint64_t(s.count / s.N) * uint64_t(sz))};
+  }
   const Bound b = bind_schedule(s, sz, true);
   int64_t moved = b.counts.hbm_bytes;
   const bool a2a = s.kind == COLL_K_ALLTOALL;
@@ -321,7 +386,7 @@ PlannedCost planned_cost(const Schedule& s, int sz, uint32_t cus) {
 coll_status_t auto_algo(coll_kind_t kind, int N, int64_t count, int sz, int root, uint32_t cus, coll_algo_t& out) {
   const std::vector<int64_t> key{int64_t(kind), N, count, sz, root, opt_alpha_ns.load(), opt_beta_gbps.load(),
                                  int64_t(cus), opt_nt.load(), opt_exec.load(), opt_group.load(), opt_grid.load(),
-                                 opt_reverse.load(), t_sums != nullptr ? 1 : 0};
+                                 opt_reverse.load(), t_sums != nullptr ? 1 : 0, opt_a2a_direct.load()};
   auto it = g_auto.find(key);
   if (it != g_auto.end()) {
     out = it->second;
@@ -372,8 +437,10 @@ void free_entry(Entry& e) {
     c.pinned = c.pinned || e.pinned;
     free_col(c);
   }
-  e.copy.pinned = e.copy.pinned || e.pinned;
-  free_copy(e.copy);
+  for (CopyDev& c : e.copy) {
+    c.pinned = c.pinned || e.pinned;
+    free_copy(c);
+  }
   e.lists.clear();
   e.d_items = nullptr;
   e.d_steps = nullptr;
@@ -642,19 +709,22 @@ coll_status_t get_col(Entry& e, const Key& k, bool cks, uint32_t cus, ColDev*& o
   return trim_cache(&e);
 }
 
-// The direct-copy tables of an AllToAll's leading independent rows
-// (copy_prefix_rows); built and uploaded on first use.  They replace the
-// schedule's first phase, which must cover exactly those rows' steps.
-// out->ok false: the row kernel runs them.
-coll_status_t get_copy(Entry& e, const Key& k, CopyDev*& out) {
-  CopyDev& c = e.copy;
+// The direct-copy tables of a whole AllToAll (whole_copy_rows) or of its
+// leading independent rows (copy_prefix_rows); built and uploaded on first
+// use.  Leading rows replace the schedule's first phase, which must cover
+// exactly those rows' steps.  out->ok false: the row kernels run them.
+coll_status_t get_copy(Entry& e, const Key& k, bool direct, CopyDev*& out) {
+  CopyDev& c = e.copy[direct ? 1 : 0];
   out = &c;
   if (c.tried) return COLL_OK;
   c.tried = true;
   const Schedule& s = e.sched;
-  const size_t n0 = copy_prefix_rows(s, k.sz);
+  std::vector<uint32_t> carried;
+  const uint64_t nwhole = whole_copy_rows(s, k.sz, direct, &carried);
+  const bool mapped = !carried.empty();  // the copy rows are the blocks, not the schedule's rows
+  const size_t n0 = nwhole ? size_t(nwhole) : copy_prefix_rows(s, k.sz);
   if (n0 == 0) return COLL_OK;
-  const bool whole = n0 == s.rows.size();
+  const bool whole = nwhole != 0;
   if (!whole) {
     // the rows kernel's first phase is these rows' steps, the rest staged
     const Bound& b = e.bound;
@@ -666,17 +736,34 @@ coll_status_t get_copy(Entry& e, const Key& k, CopyDev*& out) {
   }
   const uint64_t row_bytes = uint64_t(s.rows[0].n) * uint64_t(k.sz);
   const uint64_t wgs = (row_bytes + 1023u) / 1024u;
+  const size_t nfold = mapped ? s.rows.size() : n0;
   std::vector<CopyRow> rows(n0);
-  std::vector<uint32_t> row_off(n0 + 1);
-  std::vector<ColRef> refs(n0);
-  for (size_t i = 0; i < n0; ++i) {
-    const Row& r = s.rows[i];
-    rows[i] = CopyRow{uint32_t(r.src), uint32_t(r.dst), uint64_t(r.src_off) * uint64_t(k.sz),
-                      uint64_t(r.dst_off) * uint64_t(k.sz)};
-    row_off[i] = uint32_t(i);
-    refs[i] = ColRef{uint32_t(i * wgs), uint32_t(wgs), 1u, 0u};
+  std::vector<uint32_t> row_off(nfold + 1);
+  std::vector<ColRef> refs(nfold);
+  if (mapped) {
+    // send block j of rank i is copy row ((j - i) mod N) * N + i, Pairwise's
+    // order (round k: every rank's block k ahead); each schedule row folds
+    // the slots of the block it carries
+    const int64_t N = s.N, B = s.count / N;
+    const auto copy_row = [N](int64_t i, int64_t j) { return uint64_t(((j - i + N) % N) * N + i); };
+    for (int64_t i = 0; i < N; ++i)
+      for (int64_t j = 0; j < N; ++j)
+        rows[copy_row(i, j)] = CopyRow{uint32_t(i), uint32_t(j), uint64_t(j * B) * uint64_t(k.sz),
+                                       uint64_t(i * B) * uint64_t(k.sz)};
+    for (size_t r = 0; r < nfold; ++r) {
+      row_off[r] = uint32_t(r);
+      refs[r] = ColRef{uint32_t(copy_row(carried[r] / N, carried[r] % N) * wgs), uint32_t(wgs), 1u, 0u};
+    }
+  } else {
+    for (size_t i = 0; i < n0; ++i) {
+      const Row& r = s.rows[i];
+      rows[i] = CopyRow{uint32_t(r.src), uint32_t(r.dst), uint64_t(r.src_off) * uint64_t(k.sz),
+                        uint64_t(r.dst_off) * uint64_t(k.sz)};
+      row_off[i] = uint32_t(i);
+      refs[i] = ColRef{uint32_t(i * wgs), uint32_t(wgs), 1u, 0u};
+    }
   }
-  row_off[n0] = uint32_t(n0);
+  row_off[nfold] = uint32_t(nfold);
   CopyRow* dr = nullptr;
   uint32_t* dro = nullptr;
   ColRef* drf = nullptr;
@@ -692,6 +779,7 @@ coll_status_t get_copy(Entry& e, const Key& k, CopyDev*& out) {
   c.d_row_off = dro;
   c.d_refs = drf;
   c.nrows = uint32_t(n0);
+  c.nfold = uint32_t(nfold);
   c.whole = whole;
   c.wgs_per_row = uint32_t(wgs);
   c.row_bytes = row_bytes;
@@ -934,13 +1022,13 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (!cd->plan.ok) cd = nullptr;
   }
   if (col_mode() && bases16 && kind == COLL_K_ALLTOALL) {
-    st = get_copy(*e, k, xd);
+    st = get_copy(*e, k, opt_a2a_direct.load() != 0, xd);
     if (st != COLL_OK) return st;
     if (!xd->ok) xd = nullptr;
   }
   // a copy of leading rows that are not the whole schedule stands for phase 0
   const bool copy_part = xd && !xd->whole;
-  const uint64_t n0 = xd ? xd->nrows : 0;  // rows the direct copy makes
+  const uint64_t n0 = xd ? xd->nfold : 0;  // schedule rows the direct copy makes
   if (xd) {
     Launch L;
     L.kind = Launch::COPY;
@@ -949,9 +1037,11 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (L.grid) plan.push_back(L);
     if (g_debug.load())
       dbg += " | copy rows: " + std::to_string(xd->nrows) + " rows of " + std::to_string(xd->row_bytes) + " bytes, grid " +
-             std::to_string(L.grid) + (L.nt ? " nontemporal" : "");
+             std::to_string(L.grid) + (L.nt ? " nontemporal" : "") +
+             (xd->nfold != xd->nrows ? ", the blocks of " + std::to_string(xd->nfold) + " schedule rows" : "");
   }
   if (xd && xd->whole) {
+    moved = int64_t(2 * uint64_t(xd->nrows) * xd->row_bytes);  // every block read once, written once
   } else if (cd) {
     Launch L;
     L.kind = Launch::COL;
@@ -1484,6 +1574,10 @@ coll_status_t coll_set_option(coll_option_t key, int64_t value) {
       if (value < 0) return fail(COLL_ERR_INVALID_ARG, "cache budget below 0");
       opt_cache_bytes = value;
       return COLL_OK;
+    case COLL_OPT_A2A_DIRECT:
+      if (value != 0 && value != 1) return fail(COLL_ERR_INVALID_ARG, "a2a_direct is 0 or 1");
+      opt_a2a_direct = value;
+      return COLL_OK;
   }
   return fail(COLL_ERR_INVALID_ARG, "unknown option");
 }
@@ -1518,6 +1612,7 @@ coll_status_t coll_get_option(coll_option_t key, int64_t* value) {
     case COLL_OPT_CACHE_BYTES: *value = opt_cache_bytes.load(); return COLL_OK;
     case COLL_OPT_COL_TILES: *value = opt_col_tiles.load(); return COLL_OK;
     case COLL_OPT_TIMING: *value = opt_timing.load(); return COLL_OK;
+    case COLL_OPT_A2A_DIRECT: *value = opt_a2a_direct.load(); return COLL_OK;
   }
   return fail(COLL_ERR_INVALID_ARG, "unknown option");
 }
@@ -1601,7 +1696,8 @@ struct EnvOptions {
                 {"COLL_MODEL_BETA_GBPS", COLL_OPT_MODEL_BETA_GBPS},
                 {"COLL_CACHE_BYTES", COLL_OPT_CACHE_BYTES},
                 {"COLL_COL_TILES", COLL_OPT_COL_TILES},
-                {"COLL_TIMING", COLL_OPT_TIMING}};
+                {"COLL_TIMING", COLL_OPT_TIMING},
+                {"COLL_A2A_DIRECT", COLL_OPT_A2A_DIRECT}};
     for (const auto& v : vars) {
       const char* s = std::getenv(v.name);
       if (!s || !*s) continue;

@@ -179,9 +179,11 @@ coll_status_t coll_reduce(void* const* sendbufs, void* const* recvbufs, int nran
  * local rotations), RING (eq:model-algo-a2a-ring: N-1 rounds between
  * neighbours i -> i+1; round t forwards the N-t blocks still in transit, so
  * each link carries (N-1)M/2 bytes in all, against the printed formula's
- * (N-1)M/N).  Pairwise rounds read only the send buffers, so with blocks of
- * a multiple of 16 bytes on 16-byte aligned buffers they run as one direct
- * copy of every block (one launch, coll_get_stats().round_trips 1). */
+ * (N-1)M/N).  Every row of these schedules moves one whole block, so with
+ * blocks of a multiple of 16 bytes on 16-byte aligned buffers a call runs as
+ * one direct copy of every block whatever the algorithm (one launch,
+ * coll_get_stats().round_trips 1, moved_bytes 2 * N * count * element size),
+ * the rows' checksums those of the blocks they carry (COLL_OPT_A2A_DIRECT). */
 coll_status_t coll_alltoall(void* const* sendbufs, void* const* recvbufs, int nranks, size_t count,
                             coll_dtype_t dtype, coll_op_t op, coll_algo_t algo, int root, int chunks,
                             void* stream);
@@ -274,9 +276,10 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  * COLL_OPT_EXEC            0: automatic [0]: every collective but AllToAll, on
  *                          16-byte aligned buffers, runs in the column kernel
  *                          (its schedule compiled per column segment, see
- *                          above), and a Pairwise AllToAll whose blocks are
- *                          multiples of 16 bytes in one direct copy; where
- *                          neither applies, one row-kernel
+ *                          above), and an AllToAll whose blocks are
+ *                          multiples of 16 bytes in one direct copy
+ *                          (COLL_OPT_A2A_DIRECT); where neither applies,
+ *                          one row-kernel
  *                          launch runs every step of the call (each work
  *                          group owns fixed columns, so the steps need no
  *                          synchronisation between work groups).
@@ -330,6 +333,20 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  *                          (after synchronising their device) when a call
  *                          takes it above; 0 keeps only the schedule in use.
  *                          A lower value applies from the next call on.
+ * COLL_OPT_A2A_DIRECT      with COLL_OPT_EXEC 0 and 16-byte aligned buffers:
+ *                          1: an AllToAll whose every row moves one whole
+ *                          block (Pairwise, Bruck, the Ring AllToAll) and
+ *                          whose blocks are multiples of 16 bytes runs as one
+ *                          direct copy of its N * N blocks, each read once and
+ *                          written once [1].  An AllToAll only moves blocks,
+ *                          so the host runs the schedule on block identities
+ *                          (every source of a step read before any row of it
+ *                          writes, the pages' step model) and each row's
+ *                          checksum is that of the send block it carries,
+ *                          summed by the copy.  0: only the rows a direct copy
+ *                          makes as they stand (all of Pairwise; Bruck's and
+ *                          the Ring AllToAll's first rotation), the rounds
+ *                          after them in the permutation kernel.
  * Every setting other than the model constants gives bit-identical results;
  * they only change the speed or the memory held. */
 typedef enum {
@@ -342,7 +359,8 @@ typedef enum {
   COLL_OPT_MODEL_BETA_GBPS = 6,
   COLL_OPT_CACHE_BYTES = 7,
   COLL_OPT_COL_TILES = 8,
-  COLL_OPT_TIMING = 9
+  COLL_OPT_TIMING = 9,
+  COLL_OPT_A2A_DIRECT = 10
 } coll_option_t;
 coll_status_t coll_set_option(coll_option_t key, int64_t value);
 /* The current value of an option; INVALID_ARG for an unknown key or NULL value. */

@@ -175,7 +175,7 @@ def test_option_getter_and_cache_info():
     """Options read back what was set (defaults first); the cache starts empty."""
     import collective_communication_algorithms_amd as coll
     want = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "model_alpha_ns": 1060,
-            "model_beta_gbps": 8200, "cache_bytes": 1 << 31, "col_tiles": 0}
+            "model_beta_gbps": 8200, "cache_bytes": 1 << 31, "col_tiles": 0, "a2a_direct": 1}
     saved = {k: coll.coll_get_option(k) for k in want}
     try:
         for k, v in want.items():
@@ -185,6 +185,8 @@ def test_option_getter_and_cache_info():
         assert coll.coll_get_option("cache_bytes") == 12345
         with pytest.raises(coll.CollError):
             coll.coll_set_option("cache_bytes", -1)
+        with pytest.raises(coll.CollError):
+            coll.coll_set_option("a2a_direct", 2)
     finally:
         for k, v in saved.items():
             coll.coll_set_option(k, v)

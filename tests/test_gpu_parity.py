@@ -18,7 +18,8 @@ from tests.gpu_util import assert_parity, gpu_run
 pytestmark = pytest.mark.gpu
 
 
-DEFAULT_OPTIONS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "col_tiles": 0}
+DEFAULT_OPTIONS = {"exec": 0, "group_tiles": 0, "max_grid": 0, "nontemporal": -1, "reverse": 1, "col_tiles": 0,
+                   "a2a_direct": 1}
 
 
 @pytest.fixture(autouse=True)
@@ -428,21 +429,32 @@ def test_pairwise_alltoall_direct_copy(N, B, dtype):
 
 
 @pytest.mark.parametrize("algo", ["bruck", "ring"])
-def test_alltoall_rotation_copy_then_rounds(gpu_device, algo):
+@pytest.mark.parametrize("direct", [0, 1])
+def test_alltoall_rotation_copy_then_rounds(gpu_device, algo, direct):
     """Bruck and the Ring AllToAll start with a local rotation whose rows read
-    only the send buffers: with blocks of a multiple of 16 bytes it runs as a
-    direct copy, the rounds after it in the permutation kernel.  Bit-exact
-    against the oracle with row checksums (the copy's rows folded from its
-    own slots, the rounds' from the row kernels'), for blocks that qualify and
-    blocks that do not; then the same checksum buffer serves, in turn, a
-    larger schedule run wholly by the row kernels and the mixed call again."""
+    only the send buffers.  direct 0: with blocks of a multiple of 16 bytes
+    the rotation runs as a direct copy, the rounds after it in the
+    permutation kernel; direct 1 (the default): the whole schedule runs as one
+    direct copy of its blocks, each row's checksum that of the block it
+    carries.  Bit-exact against the oracle with row checksums (the copy's rows
+    folded from its own slots, the rounds' from the row kernels'), for blocks
+    that qualify and blocks that do not (those run every round); then the
+    same checksum buffer serves, in turn, a larger schedule run wholly by the
+    row kernels and the copy's call again."""
     import torch
     import collective_communication_algorithms_amd as coll
+    coll.coll_set_option("a2a_direct", direct)
     for N, B, dtype in ((32, 512, "bfloat16"), (5, 1000, "float32"), (12, 32, "uint8"), (12, 24, "uint8"),
                         (17, 33, "bfloat16"), (3, 4, "int32")):
         a = si.rank_arrays(N + 300, N, N * B, dtype)
         assert_parity("alltoall", algo, a, dtype, checksums=True)
         assert_parity("alltoall", algo, a, dtype)
+        st = coll.coll_get_stats()
+        if direct and (B * si.ITEMSIZE[dtype]) % 16 == 0:
+            # one copy: every block read once and written once
+            assert st["round_trips"] == 1 and st["moved_bytes"] == 2 * N * N * B * si.ITEMSIZE[dtype], (N, B, st)
+        else:
+            assert st["round_trips"] > 1, (N, B, st)
 
     def call(N, B, dtype, seed, sums):
         host = si.rank_arrays(seed, N, N * B, dtype)
@@ -470,7 +482,7 @@ def test_alltoall_rotation_copy_then_rounds(gpu_device, algo):
             assert int(got[j]) == key[r[:6]], (N, B, j, r)
 
     sums = torch.full((40 * 40 * 8,), -1, dtype=torch.int64, device=gpu_device)
-    call(16, 64, "bfloat16", 1, sums)      # mixed: copy, then rounds
+    call(16, 64, "bfloat16", 1, sums)      # 128-byte blocks: the copy (of every block, or of the rotation before the rounds)
     call(24, 17, "bfloat16", 2, sums)      # 34-byte blocks: row kernels only, more rows
     call(16, 64, "bfloat16", 3, sums)
     call(24, 17, "bfloat16", 4, sums)
@@ -571,7 +583,7 @@ def test_coll_check_after_calls():
 def test_debug_lines(gpu_device):
     """COLL_DEBUG=1 prints one line per call: the collective, the resolved
     algorithm, the schedule's counts and each launch's shape (the column
-    kernel's segments and grid, the direct copy of a Pairwise AllToAll or of
+    kernel's segments and grid, the direct copy of an AllToAll's blocks or of
     Bruck's first rotation, or the row and permutation kernels' launches)."""
     import os
     import subprocess
@@ -581,6 +593,7 @@ def test_debug_lines(gpu_device):
             "c.coll_allreduce(t, algo='auto'); c.coll_set_option('exec', 2); c.coll_allreduce(t, algo='ring'); "
             "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); c.coll_set_option('exec', 0); "
             "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='pairwise'); "
+            "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); c.coll_set_option('a2a_direct', 0); "
             "c.coll_alltoall(t, [torch.empty_like(x) for x in t], algo='bruck'); "
             "torch.cuda.synchronize(); print(float(t[0][0]))")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -588,15 +601,18 @@ def test_debug_lines(gpu_device):
                        env=dict(os.environ, COLL_DEBUG="1"))
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [ln for ln in r.stderr.splitlines() if ln.startswith("coll: ")]
-    assert len(lines) == 5, r.stderr[-2000:]
+    assert len(lines) == 6, r.stderr[-2000:]
     assert lines[0].startswith("coll: allreduce algo ") and "algo auto" not in lines[0] and "| columns:" in lines[0]
     assert lines[1].startswith("coll: allreduce algo ring") and "| rows" in lines[1]
     assert lines[2].startswith("coll: alltoall algo bruck") and "| perm" in lines[2]
     assert lines[3].startswith("coll: alltoall algo pairwise") and "| copy rows:" in lines[3]
     assert lines[3].count(" | ") == 1
-    # Bruck: the first rotation as a direct copy, the rounds in the permutation kernel
-    assert lines[4].startswith("coll: alltoall algo bruck") and "| copy rows:" in lines[4] and "| perm" in lines[4]
-    assert "| rows" not in lines[4]
+    # Bruck: one direct copy of its 64 blocks, standing for all 128 + 3 * 32 rows
+    assert lines[4].startswith("coll: alltoall algo bruck") and "| copy rows: 64 rows" in lines[4]
+    assert "the blocks of 224 schedule rows" in lines[4] and lines[4].count(" | ") == 1
+    # without COLL_OPT_A2A_DIRECT: the first rotation as a direct copy, the rounds in the permutation kernel
+    assert lines[5].startswith("coll: alltoall algo bruck") and "| copy rows: 64 rows" in lines[5] and "| perm" in lines[5]
+    assert "| rows" not in lines[5]
     assert r.stdout.strip() == "64.0"
 
 

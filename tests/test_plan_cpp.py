@@ -227,6 +227,34 @@ def test_auto_extremes():
         coll_set_option("model_beta_gbps", 8200)
 
 
+def test_alltoall_runs_as_one_copy_of_its_blocks():
+    """Every row of Pairwise, Bruck and the Ring AllToAll moves one whole
+    block, so with blocks of a multiple of 16 bytes the library plans each as
+    one direct copy of the N * N blocks: one round trip, every block read and
+    written once.  Without COLL_OPT_A2A_DIRECT only Pairwise does; blocks of
+    another length keep every round."""
+    from collective_communication_algorithms_amd import coll_set_option
+    try:
+        for N, B, dtype, sz in ((32, 512, "bfloat16", 2), (5, 1000, "float32", 4), (12, 32, "uint8", 1),
+                                (17, 64, "bfloat16", 2), (3, 4, "int32", 4), (64, 8, "bfloat16", 2)):
+            for algo in ("pairwise", "bruck", "ring"):
+                c = coll_plan("alltoall", algo, N, N * B, dtype)[1]
+                assert c["round_trips"] == 1 and c["moved_bytes"] == 2 * N * N * B * sz, (N, B, algo, c)
+                coll_set_option("a2a_direct", 0)
+                c0 = coll_plan("alltoall", algo, N, N * B, dtype)[1]
+                coll_set_option("a2a_direct", 1)
+                if algo == "pairwise":
+                    assert c0 == c, (N, B)
+                else:
+                    assert c0["round_trips"] > 1 and c0["moved_bytes"] > c["moved_bytes"], (N, B, algo, c0)
+        for N, B, dtype in ((12, 24, "uint8"), (17, 33, "bfloat16")):
+            for algo in ("bruck", "ring"):
+                c = coll_plan("alltoall", algo, N, N * B, dtype)[1]
+                assert c["round_trips"] > 1, (N, B, algo, c)
+    finally:
+        coll_set_option("a2a_direct", 1)
+
+
 @pytest.mark.parametrize("kind", list(CANDIDATES))
 def test_moved_bytes_are_the_schedule_bytes_on_small_columns(kind):
     """Row kernel (exec 2): below 8 MiB of columns no list runs in the
