@@ -605,8 +605,9 @@ def single_call(args, dev) -> int:
     definition (copies and integer reductions exactly, floating-point sums
     within the binary32 error bound of the fp64 sum); then ``--warmup`` untimed
     and ``--steps`` timed calls, each alone between HIP events, on inputs
-    restored before each call.  Prints one JSON line with the median time and
-    the schedule bytes per second."""
+    restored before each call; with ``--checksums`` every call also computes
+    the per-row checksums.  Prints one JSON line with the median time and the
+    schedule bytes per second."""
     import numpy as np
     import torch
 
@@ -625,8 +626,21 @@ def single_call(args, dev) -> int:
     recv = torch.empty_like(send) if kind == "alltoall" else None
     fn = coll.COLLECTIVE_FNS[kind]
 
+    sums = None
+    if args.checksums:
+        # one slot per schedule row, set for every call below (the definition
+        # check included)
+        nrows = coll.coll_plan(kind, algo, N, count, dtype, root, k)[1]["rows"]
+        sums = torch.zeros(max(nrows, 1), dtype=torch.int64, device=dev)
+
     def call():
-        fn(list(send), list(recv) if recv is not None else None, algo=algo, root=root, chunks=k)
+        if sums is not None:
+            coll.coll_set_checksums(sums)
+        try:
+            fn(list(send), list(recv) if recv is not None else None, algo=algo, root=root, chunks=k)
+        finally:
+            if sums is not None:
+                coll.coll_set_checksums(None)
 
     def restore():
         send.copy_(pristine)
@@ -708,7 +722,8 @@ def single_call(args, dev) -> int:
     torch.cuda.synchronize()
     restore()
     print(json.dumps({"call": kind, "algo": algo, "dtype": dtype, "nranks": N, "bytes_per_rank": count * sz,
-                      "root": root, "chunks": k, "steps": args.steps, "ms_median": round(ms, 4),
+                      "root": root, "chunks": k, "checksums": sums is not None, "steps": args.steps,
+                      "ms_median": round(ms, 4),
                       "ms_min": round(float(np.min(ts)), 4),
                       "host_us_per_issued_call": round((h1 - h0) / n_b2b * 1e6, 2),
                       "back_to_back_us_per_call": round(b0.elapsed_time(b1) / n_b2b * 1e3, 2),
@@ -742,6 +757,7 @@ def main() -> int:
                                        "alltoall", "reduce"],
                     help="time one collective at one shape (with --call-algo, --nranks, --mib, --dtype) and exit")
     ap.add_argument("--call-algo", default="default")
+    ap.add_argument("--checksums", action="store_true", help="with --call: every call computes the per-row checksums")
     ap.add_argument("--dtype", default="float32", choices=["int32", "uint8", "float32", "bfloat16"])
     ap.add_argument("--root", type=int, default=0)
     ap.add_argument("--chunks", type=int, default=1)

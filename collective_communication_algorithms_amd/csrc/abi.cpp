@@ -162,6 +162,7 @@ struct CopyDev {
   bool pinned = false;          // used by a captured call: tables kept until coll_finalize
   uint32_t nrows = 0, wgs_per_row = 0;  // copy rows
   uint32_t nfold = 0;           // schedule rows whose checksums the copy's slots make
+  uint32_t* d_idx = nullptr;    // a whole AllToAll's rows: the copy row (block) each carries; refs are per block
   uint64_t row_bytes = 0;
   CopyRow* d_rows = nullptr;
   uint32_t* d_row_off = nullptr;
@@ -420,6 +421,7 @@ void free_col(ColDev& c) {
 }
 
 void free_copy(CopyDev& c) {
+  release(c.d_idx, c.pinned);
   release(c.d_rows, c.pinned);
   release(c.d_row_off, c.pinned);
   release(c.d_refs, c.pinned);
@@ -737,54 +739,60 @@ coll_status_t get_copy(Entry& e, const Key& k, bool direct, CopyDev*& out) {
   const uint64_t row_bytes = uint64_t(s.rows[0].n) * uint64_t(k.sz);
   const uint64_t wgs = (row_bytes + 1023u) / 1024u;
   const size_t nfold = mapped ? s.rows.size() : n0;
+  // the fold's references: one per copy row (its work groups' slots); a
+  // mapped schedule's rows then take their block's sum through idx
   std::vector<CopyRow> rows(n0);
-  std::vector<uint32_t> row_off(nfold + 1);
-  std::vector<ColRef> refs(nfold);
+  std::vector<uint32_t> row_off(n0 + 1), idx;
+  std::vector<ColRef> refs(n0);
+  for (size_t i = 0; i < n0; ++i) {
+    row_off[i] = uint32_t(i);
+    refs[i] = ColRef{uint32_t(i * wgs), uint32_t(wgs), 1u, 0u};
+  }
+  row_off[n0] = uint32_t(n0);
   if (mapped) {
     // send block j of rank i is copy row ((j - i) mod N) * N + i, Pairwise's
-    // order (round k: every rank's block k ahead); each schedule row folds
-    // the slots of the block it carries
+    // order (round k: every rank's block k ahead)
     const int64_t N = s.N, B = s.count / N;
-    const auto copy_row = [N](int64_t i, int64_t j) { return uint64_t(((j - i + N) % N) * N + i); };
+    const auto copy_row = [N](int64_t i, int64_t j) { return uint32_t(((j - i + N) % N) * N + i); };
     for (int64_t i = 0; i < N; ++i)
       for (int64_t j = 0; j < N; ++j)
         rows[copy_row(i, j)] = CopyRow{uint32_t(i), uint32_t(j), uint64_t(j * B) * uint64_t(k.sz),
                                        uint64_t(i * B) * uint64_t(k.sz)};
-    for (size_t r = 0; r < nfold; ++r) {
-      row_off[r] = uint32_t(r);
-      refs[r] = ColRef{uint32_t(copy_row(carried[r] / N, carried[r] % N) * wgs), uint32_t(wgs), 1u, 0u};
-    }
+    idx.resize(nfold);
+    for (size_t r = 0; r < nfold; ++r) idx[r] = copy_row(carried[r] / N, carried[r] % N);
   } else {
     for (size_t i = 0; i < n0; ++i) {
       const Row& r = s.rows[i];
       rows[i] = CopyRow{uint32_t(r.src), uint32_t(r.dst), uint64_t(r.src_off) * uint64_t(k.sz),
                         uint64_t(r.dst_off) * uint64_t(k.sz)};
-      row_off[i] = uint32_t(i);
-      refs[i] = ColRef{uint32_t(i * wgs), uint32_t(wgs), 1u, 0u};
     }
   }
-  row_off[nfold] = uint32_t(nfold);
   CopyRow* dr = nullptr;
   uint32_t* dro = nullptr;
   ColRef* drf = nullptr;
+  uint32_t* dix = nullptr;
   coll_status_t st = upload(rows, dr);
   if (st == COLL_OK) st = upload(row_off, dro);
   if (st == COLL_OK) st = upload(refs, drf);
+  if (st == COLL_OK && mapped) st = upload(idx, dix);
   if (st != COLL_OK) {
     if (dr) (void)hipFree(dr);
     if (dro) (void)hipFree(dro);
+    if (drf) (void)hipFree(drf);
     return st;
   }
   c.d_rows = dr;
   c.d_row_off = dro;
   c.d_refs = drf;
+  c.d_idx = dix;
   c.nrows = uint32_t(n0);
   c.nfold = uint32_t(nfold);
   c.whole = whole;
   c.wgs_per_row = uint32_t(wgs);
   c.row_bytes = row_bytes;
   c.ok = true;
-  c.bytes = rows.size() * sizeof(CopyRow) + row_off.size() * sizeof(uint32_t) + refs.size() * sizeof(ColRef);
+  c.bytes = rows.size() * sizeof(CopyRow) + (row_off.size() + idx.size()) * sizeof(uint32_t) +
+            refs.size() * sizeof(ColRef);
   e.bytes += c.bytes;
   g_cache_bytes += c.bytes;
   return trim_cache(&e);
@@ -1145,8 +1153,11 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     // sums and the fold's slices; a direct copy's slots and slices after the
     // row kernels' slots, if any
     const size_t rows_slots = (cd || (xd && xd->whole)) ? 0 : std::max<size_t>(size_t(b.nrows), 1) * SUM_LANES;
+    // (a whole AllToAll's copy: its blocks' fold slices and sums, which its
+    // rows then gather)
+    const size_t copy_fold = !xd ? 0 : xd->d_idx ? size_t(xd->nrows) * (COL_FOLD_SLICES + 1) : size_t(n0) * COL_FOLD_SLICES;
     const size_t slots = cd ? size_t(cd->partials) + std::max<size_t>(size_t(b.nrows), 1) * COL_FOLD_SLICES
-                            : rows_slots + (xd ? size_t(copy_slots) + size_t(n0) * COL_FOLD_SLICES : 0);
+                            : rows_slots + (xd ? size_t(copy_slots) + copy_fold : 0);
     st = sum_scratch(dev, t_sums, slots, scratch);
     if (st != COLL_OK) return st;
     partial = scratch->d;
@@ -1246,6 +1257,15 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     he = launch_fold_sums(partial + n0 * SUM_LANES, t_sums + n0, uint64_t(b.nrows) - n0, stream);
     if (he == hipSuccess)
       he = launch_col_fold(xd->d_refs, xd->d_row_off, copy_partial, copy_partial + copy_slots, t_sums, n0, stream);
+    if (he != hipSuccess) return hip_fail(he, "checksum fold");
+    if (!capturing) scratch->clean = false;
+  } else if (cks && xd && xd->d_idx) {
+    // each block's sum once, then every row takes the sum of the block it
+    // carries
+    uint64_t* tmp = copy_partial + copy_slots;
+    uint64_t* block_sums = tmp + uint64_t(xd->nrows) * COL_FOLD_SLICES;
+    he = launch_col_fold(xd->d_refs, xd->d_row_off, copy_partial, tmp, block_sums, xd->nrows, stream);
+    if (he == hipSuccess) he = launch_gather_sums(xd->d_idx, block_sums, t_sums, uint64_t(b.nrows), stream);
     if (he != hipSuccess) return hip_fail(he, "checksum fold");
     if (!capturing) scratch->clean = false;
   } else if (cks && (cd || xd)) {

@@ -446,6 +446,17 @@ __global__ __launch_bounds__(BLOCK_THREADS) void col_fold_rows_kernel(const uint
   if (lane == 0) *gptr<uint64_t>(reinterpret_cast<char*>(out + r)) = t;
 }
 
+// Row checksums equal to others already folded: out[r] = src[idx[r]] (the
+// rows of an AllToAll run as one direct copy take the sums of the blocks they
+// carry).  Every idx[r] indexes src; the host builds both.
+__global__ __launch_bounds__(BLOCK_THREADS) void gather_sums_kernel(const uint32_t* idx, const uint64_t* src,
+                                                                     uint64_t* out, uint64_t n) {
+  const uint64_t r = uint64_t(blockIdx.x) * BLOCK_THREADS + threadIdx.x;
+  if (r >= n) return;
+  const uint32_t i = *gptr<uint32_t>(reinterpret_cast<const char*>(idx + r));
+  *gptr<uint64_t>(reinterpret_cast<char*>(out + r)) = *gptr<uint64_t>(reinterpret_cast<const char*>(src + i));
+}
+
 template <int P>
 using ColFn = void (*)(ColLaunchArgs<P>);
 
@@ -550,6 +561,15 @@ hipError_t launch_col(const ColArgs& a, int nranks, int dtype, int op, int unit,
   if (nranks < 1 || nranks > COL_THREADS) return hipErrorInvalidValue;
   if (nranks <= 16 && !batched) return launch_col_p<16>(a, dtype, op, leaves, accs, batched, nt, grid, stream);
   return launch_col_p<64>(a, dtype, op, leaves, accs, batched, nt, grid, stream);
+}
+
+hipError_t launch_gather_sums(const uint32_t* idx, const uint64_t* src, uint64_t* out, uint64_t n,
+                              hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const uint64_t grid = (n + BLOCK_THREADS - 1) / BLOCK_THREADS;
+  if (grid > 0x7fffffffu) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_sums_kernel, dim3(uint32_t(grid)), dim3(BLOCK_THREADS), 0, stream, idx, src, out, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,

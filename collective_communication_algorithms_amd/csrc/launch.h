@@ -43,6 +43,9 @@ hipError_t launch_col(const ColArgs& a, int nranks, int dtype, int op, int unit,
 // of tmp (nrows * COL_FOLD_SLICES slots)
 hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,
                            uint64_t* out, uint64_t nrows, hipStream_t stream);
+// out[r] = src[idx[r]] for r < n (row checksums copied from others).
+hipError_t launch_gather_sums(const uint32_t* idx, const uint64_t* src, uint64_t* out, uint64_t n,
+                              hipStream_t stream);
 // The address of the current device's allocation-free scratch
 // (COLL_NOALLOC_SCRATCH_BYTES, 256-byte aligned), taken once per device.
 hipError_t noalloc_scratch(void** out);
