@@ -216,12 +216,14 @@ def sweep(out_path: str, dev, quick: bool = False) -> None:
              "steps": cnt["steps"], "sched_bytes": st["hbm_bytes"], "crit_bytes": cnt["crit_bytes"],
              "t_med_us": round(med * 1e3, 2), "t_min_us": round(mn * 1e3, 2),
              "algbw_GBps": round(algbw, 3), "busbw_GBps": round(algbw * model.busbw_coef(kind, N), 3),
+             # the bytes the schedule's rows stand for, over the call's time
+             # (above the HBM peak wherever the kernels keep them in registers)
              "sched_TBps": round(st["hbm_bytes"] / (med * 1e-3) / 1e12, 3),
-             "pct_of_8TBps": round(100 * st["hbm_bytes"] / (med * 1e-3) / 8e12, 2),
              # what the launched kernels moved through memory (operands passed in
-             # registers and skipped stores left out), and its rate
+             # registers and skipped stores left out), its rate and share of 8 TB/s
              "moved_bytes": st["moved_bytes"],
-             "moved_TBps": round(st["moved_bytes"] / (med * 1e-3) / 1e12, 3)}
+             "moved_TBps": round(st["moved_bytes"] / (med * 1e-3) / 1e12, 3),
+             "moved_pct_of_8TBps": round(100 * st["moved_bytes"] / (med * 1e-3) / 8e12, 2)}
         try:
             mk = "broadcast" if kind == "broadcast" else kind
             r["ab_page_us"] = round(model.time(mk, algo, N, M, 5e-6, 450e9, k) * 1e6, 2)
