@@ -622,19 +622,28 @@ coll_status_t upload(const std::vector<T>& v, T*& d) {
 }
 
 // Column kernel: tiles per work group.  Column spaces under 64 tiles per CU:
-// 1, so that every compute unit gets work.  Larger ones without checksums: 1
-// (a work group that ends after one tile never waits for its stores).  With
-// row checksums more tiles make the partial sums fewer for the fold to add,
-// but fewer, longer work groups leave a tail: 2, and 4 from 1,024 tiles per
-// CU.  Measured on Ring AllReduce fp32 over 8 ranks, each call after a
-// restore of its inputs, in TB/s of 2NM with checksums, 2 / 4 tiles: 64 MiB
-// per rank 5.25 / 3.84, 128 MiB 5.69 / 5.55, 256 MiB 5.75 / 5.81; without, 1
-// / 2 tiles: 64 MiB 5.33 / 5.43, 128 MiB 5.79 / 5.61, 256 MiB 5.78 / 5.71.
+// 1, so that every compute unit gets work.  Without checksums: 2 from 128 up
+// to 512 tiles per CU for unbatched programs, else 1 (a work group that ends
+// after one tile never waits for its stores, which pays where the whole call
+// fits the memory-side cache and where it streams; batched programs hold
+// fewer waves per CU and lose with 2: ReduceScatter bf16 32 x 64 MiB 0.389
+// against 0.422 ms).  With row checksums more tiles make the
+// partial sums fewer for the fold to add, but fewer, longer work groups leave
+// a tail: 2, and 4 from 1,024 tiles per CU.  Measured on Ring AllReduce fp32
+// over 8 ranks, each call after a restore of its inputs, ms per call with
+// checksums, 2 / 4 tiles: 64 MiB per rank 0.195 / 0.225, 128 MiB 0.364 /
+// 0.371, 256 MiB 5.75 / 5.81 TB/s; without, 1 / 2 tiles: 16 MiB 0.0421 /
+// 0.0426 ms, 24 MiB 0.0688 / 0.0704, 32 MiB 0.1022 / 0.0921, 48 MiB 0.1421 /
+// 0.1343, 64 MiB 0.1946 / 0.1921, 96 MiB 0.302 / 0.289, 128 MiB 0.367 /
+// 0.377, 256 MiB 5.78 / 5.71 TB/s; 8 ranks x 64 MiB, 1 / 2 tiles: Ring
+// ReduceScatter bf16 0.1256 / 0.1215 ms, AllGather 0.0975 / 0.0954, tree
+// Reduce fp32 0.1228 / 0.1199, Broadcast 0.0975 / 0.0959.
 uint32_t auto_col_tiles(const ColPlan& p, uint32_t cus) {
   const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
   uint64_t tiles = 0;
   for (const ColSeg& sg : p.segs) tiles += (sg.s1 + tb - 1) / tb - sg.s0 / tb;
-  if (tiles < uint64_t(cus) * 64u || p.v.accs == 0) return 1;
+  if (tiles < uint64_t(cus) * 64u) return 1;
+  if (p.v.accs == 0) return !p.batched && tiles >= uint64_t(cus) * 128u && tiles < uint64_t(cus) * 512u ? 2 : 1;
   return tiles >= uint64_t(cus) * 1024u ? 4 : 2;
 }
 
