@@ -623,7 +623,8 @@ coll_status_t upload(const std::vector<T>& v, T*& d) {
 
 // Column kernel: tiles per work group.  Column spaces under 64 tiles per CU:
 // 1, so that every compute unit gets work.  Without checksums: 2 from 128 up
-// to 512 tiles per CU for unbatched programs, else 1 (a work group that ends
+// to 512 tiles per CU for unbatched programs, 4 above for single-leaf ones,
+// else 1 (a work group that ends
 // after one tile never waits for its stores, which pays where the whole call
 // fits the memory-side cache and where it streams; batched programs hold
 // fewer waves per CU and lose with 2: ReduceScatter bf16 32 x 64 MiB 0.389
@@ -637,13 +638,22 @@ coll_status_t upload(const std::vector<T>& v, T*& d) {
 // 0.1343, 64 MiB 0.1946 / 0.1921, 96 MiB 0.302 / 0.289, 128 MiB 0.367 /
 // 0.377, 256 MiB 5.78 / 5.71 TB/s; 8 ranks x 64 MiB, 1 / 2 tiles: Ring
 // ReduceScatter bf16 0.1256 / 0.1215 ms, AllGather 0.0975 / 0.0954, tree
-// Reduce fp32 0.1228 / 0.1199, Broadcast 0.0975 / 0.0959.
+// Reduce fp32 0.1228 / 0.1199, Broadcast 0.0975 / 0.0959.  From 512 tiles
+// per CU single-leaf programs (AllGather, Broadcast: one load, many stores)
+// take 4: 256 MiB per rank, 1 / 2 / 4 / 8 tiles, Broadcast uint8 8 ranks
+// 0.420 / 0.414 / 0.389 / 0.402 ms, AllGather bf16 8 ranks 0.406 / 0.417 /
+// 0.390 / 0.403 ms, 64 ranks 3.336 / 3.276 / 3.304 / 3.396 ms; the Ring
+// AllReduce fp32 8 ranks 0.738 / 0.743 / 0.770 / 0.793 ms.
 uint32_t auto_col_tiles(const ColPlan& p, uint32_t cus) {
   const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
   uint64_t tiles = 0;
   for (const ColSeg& sg : p.segs) tiles += (sg.s1 + tb - 1) / tb - sg.s0 / tb;
   if (tiles < uint64_t(cus) * 64u) return 1;
-  if (p.v.accs == 0) return !p.batched && tiles >= uint64_t(cus) * 128u && tiles < uint64_t(cus) * 512u ? 2 : 1;
+  if (p.v.accs == 0) {
+    if (p.batched || tiles < uint64_t(cus) * 128u) return 1;
+    if (tiles < uint64_t(cus) * 512u) return 2;
+    return p.max_leaves <= 1 ? 4 : 1;  // single-leaf programs: 1 load, many stores per tile
+  }
   return tiles >= uint64_t(cus) * 1024u ? 4 : 2;
 }
 

@@ -322,10 +322,11 @@ coll_status_t coll_set_checksums(uint64_t* dev_sums, size_t capacity);
  * COLL_OPT_MODEL_BETA_GBPS moved-byte rate used by COLL_ALGO_AUTO, in GB/s [8200].
  * COLL_OPT_COL_TILES       column kernel: tiles (64 lanes x 16 bytes) per
  *                          work group, up to 65535 [0: automatic: 1 under 64
- *                          tiles per CU; without row checksums 2 from 128 to
- *                          511 tiles per CU for programs that hold all their
- *                          leaves in registers, else 1; with them 2, from
- *                          1,024 tiles per CU 4].
+ *                          tiles per CU; without row checksums, for programs
+ *                          that hold all their leaves in registers, 2 from
+ *                          128 to 511 tiles per CU and 4 above for programs
+ *                          of one leaf (AllGather, Broadcast), else 1; with
+ *                          them 2, from 1,024 tiles per CU 4].
  * COLL_OPT_TIMING          1: every call made outside graph capture records a
  *                          HIP event before its first data-moving kernel and
  *                          one after its last (not around the checksum
