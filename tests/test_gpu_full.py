@@ -147,6 +147,58 @@ def test_alltoall_n32_512x4096(algo):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("algo", ["pairwise", "bruck", "ring"])
+def test_alltoall_row_checksums_n32_128MiB(algo):
+    """C5 at full size with row checksums, in the default launch (every
+    algorithm one direct copy of the blocks): every row's checksum equals the
+    oracle's.  An AllToAll row only moves a block, so its checksum is that of
+    the send block it carries; which block that is comes from the oracle's own
+    plan run on blocks holding their ids (a row's checksum over a one-element
+    int32 block is the element), and the block's checksum from the oracle's
+    row_checksum over the full-size send block."""
+    import torch
+    import collective_communication_algorithms_amd as coll
+    from oracle.simulate import run_plan
+    dev = torch.device("cuda:0")
+    N, B = 32, (128 << 20) // 2 // 32
+    count = N * B
+    ids = [np.arange(i * N, (i + 1) * N, dtype=np.int32) for i in range(N)]
+    _, carried = run_plan(make_plan("alltoall", algo, N, N), "int32", "sum", ids, trace=True)
+    sbuf = torch.empty((N, count), dtype=torch.bfloat16, device=dev)
+    send = si.device_rank_tensors(9, N, count, "bfloat16", dev, out=sbuf)
+    rbuf = torch.empty_like(sbuf)
+    rows, cnt = coll.coll_plan("alltoall", algo, N, count, "bfloat16")
+    assert len(rows) == len(carried)
+    sums = torch.full((len(rows),), -1, dtype=torch.int64, device=dev)
+    coll.coll_set_checksums(sums)
+    try:
+        coll.coll_alltoall(send, [rbuf[i] for i in range(N)], algo=algo)
+    finally:
+        coll.coll_set_checksums(None)
+    torch.cuda.synchronize()
+    st = coll.coll_get_stats()
+    assert st["round_trips"] == 1 and st["moved_bytes"] == 2 * N * count * 2
+    host = sbuf.view(torch.int16).cpu().numpy().view(np.uint16)
+    block_sum = {}
+    for b in sorted({int(c) for c in carried}):
+        i, j = divmod(b, N)
+        block_sum[b] = numerics.row_checksum(host[i, j * B:(j + 1) * B])
+    got = sums.cpu().numpy().view(np.uint64)
+    plan = make_plan("alltoall", algo, N, count)
+    want_by_key = {}
+    for idx, r in enumerate(r for st_rows in plan.steps for r in st_rows):
+        want_by_key[(r.step, r.src, r.dst, r.src_off, r.dst_off, r.n)] = block_sum[int(carried[idx])]
+    for j, r in enumerate(rows):
+        assert int(got[j]) == want_by_key[tuple(r[:6])], (algo, j, r)
+    # and the receive buffers: recv_j block i = send_i block j, on sampled blocks
+    rhost = rbuf.view(torch.int16)
+    for j in (0, 13, 31):
+        for i in (0, 7, 31):
+            assert torch.equal(rhost[j, i * B:(i + 1) * B].cpu(), sbuf.view(torch.int16)[i, j * B:(j + 1) * B].cpu())
+    del sbuf, rbuf, send, sums
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("kind,algo,N,count,dtype,k", [
     ("allreduce", "ring", 8, (256 << 20) // 4, "float32", 1),
     ("allgather", "ring", 8, (256 << 20) // 2, "bfloat16", 1),
