@@ -644,17 +644,30 @@ coll_status_t upload(const std::vector<T>& v, T*& d) {
 // 0.420 / 0.414 / 0.389 / 0.402 ms, AllGather bf16 8 ranks 0.406 / 0.417 /
 // 0.390 / 0.403 ms, 64 ranks 3.336 / 3.276 / 3.304 / 3.396 ms; the Ring
 // AllReduce fp32 8 ranks 0.738 / 0.743 / 0.770 / 0.793 ms.
-uint32_t auto_col_tiles(const ColPlan& p, uint32_t cus) {
+uint64_t col_tile_count(const ColPlan& p) {
   const uint64_t tb = uint64_t(COL_THREADS) * uint64_t(p.v.unit);
   uint64_t tiles = 0;
   for (const ColSeg& sg : p.segs) tiles += (sg.s1 + tb - 1) / tb - sg.s0 / tb;
+  return tiles;
+}
+
+uint32_t auto_col_tiles(const ColPlan& p, uint32_t cus) {
+  const uint64_t tiles = col_tile_count(p);
   if (tiles < uint64_t(cus) * 64u) return 1;
-  if (p.v.accs == 0) {
+  if (p.v.accs <= 0) {
     if (p.batched || tiles < uint64_t(cus) * 128u) return 1;
     if (tiles < uint64_t(cus) * 512u) return 2;
     return p.max_leaves <= 1 ? 4 : 1;  // single-leaf programs: 1 load, many stores per tile
   }
   return tiles >= uint64_t(cus) * 1024u ? 4 : 2;
+}
+
+// The column kernel's paired variant without checksums (4 waves per SIMD)
+// pays from 128 tiles per CU; below, the plain variant runs the same programs
+// (Ring AllReduce fp32 8 x 16 MiB, 64 tiles per CU: 0.0422 ms plain, 0.0446 ms
+// paired).
+void fit_col_variant(ColPlan& p, uint32_t cus) {
+  if (p.ok && p.v.accs < 0 && col_tile_count(p) < uint64_t(cus) * 128u) p.v.accs = 0;
 }
 
 // Column kernel: nontemporal loads and stores once the call's buffers exceed
@@ -676,6 +689,7 @@ coll_status_t get_col(Entry& e, const Key& k, bool cks, uint32_t cus, ColDev*& o
     c.tried = true;
     c.plan = compile_colplan(e.sched, k.sz, k.inplace != 0, cks);
     if (!c.plan.ok) return COLL_OK;
+    fit_col_variant(c.plan, cus);
     const coll_status_t st = upload(c.plan.code, c.d_code);
     if (st != COLL_OK) {
       free_col(c);
@@ -1085,7 +1099,8 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
     if (g_debug.load())
       dbg += " | columns: " + std::to_string(cd->plan.segs.size()) + " segments, grid " + std::to_string(L.grid) +
              " tiles " + std::to_string(cd->tiles) + " unit " + std::to_string(L.v.unit) + " slots " +
-             std::to_string(L.v.leaves) + (L.v.accs ? " checksum ops " + std::to_string(L.v.accs) : "") +
+             std::to_string(L.v.leaves) + (L.v.accs > 0 ? " checksum ops " + std::to_string(L.v.accs) : "") +
+             (L.v.accs < 0 ? " paired" : "") +
              (L.v.batched ? " batched" : "") + (L.nt ? " nontemporal" : "");
   } else {
     for (size_t pi = copy_part ? 1 : 0; pi < b.phases.size(); ++pi) {
@@ -1398,6 +1413,7 @@ coll_status_t run_noalloc(void* const* send, void* const* recv, int N, size_t co
     n.plan = compile_colplan(s, sz, inplace, cks);
     if (!n.plan.ok)
       return fail(COLL_ERR_UNSUPPORTED, "the allocation-free AllReduce runs the column kernel only: " + n.plan.why);
+    fit_col_variant(n.plan, uint32_t(di->cus));
     // tiles per work group: the automatic choice, more while the tables and
     // partial sums exceed the scratch
     uint32_t tiles = opt_col_tiles.load() > 0 ? uint32_t(opt_col_tiles.load()) : auto_col_tiles(n.plan, uint32_t(di->cus));

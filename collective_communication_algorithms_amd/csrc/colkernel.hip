@@ -156,6 +156,10 @@ struct Accs<-1> {
 // NA = -2: the same merged sums, with the leaves loaded in pairs (below).
 template <>
 struct Accs<-2> : Accs<-1> {};
+// NA = -3: no checksums, the leaves loaded in pairs, launched at most 16 work
+// groups per CU (COL_PAIRED_LDS).
+template <>
+struct Accs<-3> {};
 
 // The lane that carries op o after six merge levels (the inverse of the
 // level bits chosen above: op bit 0 is lane bit 2, op bits 1 and 2 are lane
@@ -264,11 +268,13 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
   __builtin_amdgcn_s_waitcnt(0);
   const uint32_t nfirst = wk.nfirst, nop = wk.nop, nstore = wk.nstore;
   const uint64_t s0 = wk.s0, s1 = wk.s1, xs = s0 & ~(UNIT - 1);
+  constexpr bool MERGED = NA == -1 || NA == -2;            // checksums as merged wave sums
+  constexpr bool PAIRS = NA > 0 || NA == -2 || NA == -3;    // leaves loaded in pairs
   Accs<NA> acc;
   if constexpr (NA > 0) acc.clear();
-  if constexpr (NA < 0)
+  if constexpr (MERGED)
     for (int j = 0; j < 6; ++j) acc.l[j] = 0;
-  uint64_t mine = 0;  // NA < 0: lane l's running total of op op_of_lane(l)
+  uint64_t mine = 0;  // MERGED: lane l's running total of op op_of_lane(l)
   for (uint32_t t = 0; t < wk.ntiles; ++t) {
     const uint64_t x = wk.c0 + uint64_t(t) * TB + uint64_t(lane) * UNIT;
     const bool any = x < s1 && x + UNIT > s0;
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
         const char* base = reinterpret_cast<const char*>(lane_u64(sp_lo, sp_hi, rk));
         slot_set(v, uint32_t(j), ld16<(NTM & NT_SRC) != 0>(base + xl));
       }
-    } else if constexpr (NA > 0 || NA == -2) {
+    } else if constexpr (PAIRS) {
       // the checksum variants of up to 16 ops (4-6 waves per SIMD where the
       // plain one holds 8): leaves in pairs, one branch per pair (a slot
       // past the leaves loads the last leaf again), which the compiler
@@ -370,13 +376,13 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
       if constexpr (NA > 0) {
         const uint32_t shift = uint32_t(__builtin_amdgcn_readlane(int(op_w1), int(k))) & 3u;
         if (any) acc.add(k, unit_words<DT>(val, x, s0, s1, full, shift));
-      } else if constexpr (NA < 0) {
+      } else if constexpr (MERGED) {
         const uint32_t shift = uint32_t(__builtin_amdgcn_readlane(int(op_w1), int(k))) & 3u;
         const uint64_t w = any ? unit_words<DT>(val, x, s0, s1, full, shift) : 0;
         push_op<0>(acc, w, k, lane, mine);  // every lane takes part
       }
     }
-    if constexpr (NA < 0) mine += flush_ops<0>(acc, nop, 0, lane);
+    if constexpr (MERGED) mine += flush_ops<0>(acc, nop, 0, lane);
     // Batched programs: every load of this tile has been consumed (each leaf
     // an op or a store reads); an explicit wait tells the compiler so, which
     // it cannot see across the dynamic op loop, and would otherwise wait for
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(COL_THREADS) void col_kernel(const ColLaunchArgs<P>
       if (lane == k) mine = tot;
     }
     if (lane < nop) *gptr<uint64_t>(reinterpret_cast<char*>(a.partial + wk.part + lane)) = mine;
-  } else if constexpr (NA < 0) {
+  } else if constexpr (MERGED) {
     const uint32_t o = op_of_lane(lane);  // a permutation of 0 .. 63
     if (o < nop) *gptr<uint64_t>(reinterpret_cast<char*>(a.partial + wk.part + o)) = mine;
   }
@@ -465,7 +471,8 @@ ColFn<P> col_fn_nt(bool nt) {
   return nt ? col_kernel<DT, OP, NL, NA, NT_SRC | NT_DST, BT, P> : col_kernel<DT, OP, NL, NA, 0, BT, P>;
 }
 
-// Unbatched programs hold at most 8 slots; checksums of up to 8 ops: merged
+// Unbatched programs hold at most 8 slots; accs -1: no checksums, leaves in
+// pairs, at most 16 work groups per CU; checksums of up to 8 ops: merged
 // wave sums, the leaves in pairs (one leaf: alone); 9 .. 16 ops: a per-lane
 // file; more: merged wave sums.  Batched programs: 8 slots, or 16 with slots
 // 8 and up in LDS; checksums: merged wave sums.
@@ -475,6 +482,7 @@ ColFn<P> col_fn_variant(int leaves, int accs, bool nt) {
     if (accs > 0) return leaves <= 8 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 16, -1, BT, P>(nt);
     return leaves <= 8 ? col_fn_nt<DT, OP, 8, 0, BT, P>(nt) : col_fn_nt<DT, OP, 16, 0, BT, P>(nt);
   } else {
+    if (accs < 0) return col_fn_nt<DT, OP, 8, -3, BT, P>(nt);
     if (accs > 16) return col_fn_nt<DT, OP, 8, -1, BT, P>(nt);
     if (accs > 8) return col_fn_nt<DT, OP, 8, 16, BT, P>(nt);
     if (accs > 0) return leaves <= 1 ? col_fn_nt<DT, OP, 8, -1, BT, P>(nt) : col_fn_nt<DT, OP, 8, -2, BT, P>(nt);
@@ -522,7 +530,10 @@ hipError_t launch_col_p(const ColArgs& a, int dtype, int op, int leaves, int acc
     c.send[i] = a.p.send[i];
     c.recv[i] = a.p.recv[i];
   }
-  hipLaunchKernelGGL(pick_col<P>(dtype, op, leaves, accs, batched, nt), dim3(grid), dim3(COL_THREADS), 0, stream, c);
+  // the paired variant without checksums reserves LDS it never touches, so
+  // that a CU holds at most 16 of its work groups (4 waves per SIMD)
+  const size_t lds = accs < 0 ? COL_PAIRED_LDS : 0;
+  hipLaunchKernelGGL(pick_col<P>(dtype, op, leaves, accs, batched, nt), dim3(grid), dim3(COL_THREADS), lds, stream, c);
   return hipGetLastError();
 }
 

@@ -48,7 +48,18 @@ uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz))
 // ReduceScatter 0.454 -> 0.416 ms), and so do single-leaf programs
 // (AllGather bf16 8 x 256 MiB 0.418 -> 0.394 ms, its leaf loaded alone: the
 // {1 slot, 8 ops} entry).
-const ColVariant kVariants[] = {{16, 8, 0, false},  {16, 1, 8, false}, {16, 8, 8, false, 2}, {16, 8, 16, false},
+// Without checksums, programs of 2 or more leaves and 8 stores (the AllReduces
+// over 8 ranks) load their leaves in pairs at 4 waves per SIMD, the shape the
+// checksummed AllReduce runs at, where the plain variant holds 8 waves with one
+// load in flight.  Measured on MI355X, plain -> paired, fp32 8 x 256 MiB Ring
+// 0.736 -> 0.715 ms, halving-doubling 0.737 -> 0.722, double binary tree
+// 0.737 -> 0.717, bf16 Ring 0.740 -> 0.729; Ring 8 x 128 MiB 0.370 -> 0.348,
+// 8 x 32 MiB 0.094 -> 0.090 (pairs at 8 waves per SIMD: 0.764 ms at 256 MiB).
+// Fewer stores lose (Ring AllReduce over 4 ranks 0.353 -> 0.373 ms), and so do
+// small column spaces (abi.cpp: fit_col_variant); programs of one leaf or one
+// store keep the plain variant's occupancy.
+const ColVariant kVariants[] = {{16, 8, -1, false, COL_LIST_MAX_STORES, 8, 2},
+                                {16, 8, 0, false},  {16, 1, 8, false}, {16, 8, 8, false, 2}, {16, 8, 16, false},
                                 {16, 8, 64, false}, {16, 8, 0, true},  {16, 16, 0, true},    {16, 8, 64, true},
                                 {16, 16, 64, true}};
 
@@ -577,7 +588,7 @@ ColPlan compile_colplan(const Schedule& s, int sz, bool inplace, bool checksums,
   for (const ColVariant& v : kVariants) {
     if ((v.accs > 0) != checksums || v.batched != p.batched) continue;
     if (int(p.max_slots) > v.leaves || (checksums && int(p.max_ops) > v.accs) || sz > v.unit ||
-        int(p.max_stores) > v.stores)
+        int(p.max_stores) > v.stores || int(p.max_stores) < v.min_stores || int(p.max_leaves) < v.min_leaves)
       continue;
     p.v = v;
     p.ok = true;

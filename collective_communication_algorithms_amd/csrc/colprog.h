@@ -15,7 +15,8 @@ namespace coll {
 // and column, at most `leaves` leaves and slots, and checksums of up to
 // `accs` ops (0: the variant computes no checksums; 16 a per-lane
 // accumulator file, 8 slots and unbatched programs only; 8 and 64 wave sums
-// merged across lanes); `batched` variants
+// merged across lanes; -1 no checksums, the leaves loaded in pairs, at most 16
+// work groups per CU); `batched` variants
 // also run programs that bring their leaves in batches (RELOAD ops), at the
 // cost of the registers that takes.  Every list of a program holds at most
 // 64 instructions (one per lane).
@@ -27,6 +28,7 @@ struct ColVariant {
   int accs = 0;
   bool batched = false;
   int stores = COL_LIST_MAX_STORES;  // the variant is picked for programs of at most this many stores
+  int min_stores = 0, min_leaves = 0;  // ... and of at least this many stores and leaves
 };
 
 // With checksums: row `row`'s checksum over segment `seg` is the sum of op

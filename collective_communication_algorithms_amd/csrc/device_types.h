@@ -130,6 +130,10 @@ enum : uint32_t {
 
 // Leaves a RELOAD brings in at most.
 constexpr uint32_t COL_BATCH = 8;
+// Dynamic LDS the column kernel's paired variant without checksums reserves
+// (and never touches): 160 KiB per CU hold 16 such work groups, 4 waves per
+// SIMD, where its registers alone would allow 8
+constexpr uint32_t COL_PAIRED_LDS = 10240;
 
 struct ColInstr {        // 8 bytes
   uint8_t flags;         // CI_* (ops, stores)
