@@ -472,7 +472,8 @@ ColFn<P> col_fn_nt(bool nt) {
 }
 
 // Unbatched programs hold at most 8 slots; accs -1: no checksums, leaves in
-// pairs, at most 16 work groups per CU; checksums of up to 8 ops: merged
+// pairs, at most 16 work groups per CU (batched: the plain batched kernel,
+// fewer work groups per CU); checksums of up to 8 ops: merged
 // wave sums, the leaves in pairs (one leaf: alone); 9 .. 16 ops: a per-lane
 // file; more: merged wave sums.  Batched programs: 8 slots, or 16 with slots
 // 8 and up in LDS; checksums: merged wave sums.
@@ -530,9 +531,10 @@ hipError_t launch_col_p(const ColArgs& a, int dtype, int op, int leaves, int acc
     c.send[i] = a.p.send[i];
     c.recv[i] = a.p.recv[i];
   }
-  // the paired variant without checksums reserves LDS it never touches, so
-  // that a CU holds at most 16 of its work groups (4 waves per SIMD)
-  const size_t lds = accs < 0 ? COL_PAIRED_LDS : 0;
+  // the variants without checksums for many-store programs reserve LDS they
+  // never touch, so that a CU holds fewer of their work groups: unbatched at
+  // most 16 (4 waves per SIMD), batched fewer still
+  const size_t lds = accs >= 0 ? 0 : batched ? COL_BATCHED_CAP_LDS : COL_PAIRED_LDS;
   hipLaunchKernelGGL(pick_col<P>(dtype, op, leaves, accs, batched, nt), dim3(grid), dim3(COL_THREADS), lds, stream, c);
   return hipGetLastError();
 }
