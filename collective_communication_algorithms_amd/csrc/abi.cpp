@@ -663,11 +663,13 @@ uint32_t auto_col_tiles(const ColPlan& p, uint32_t cus) {
 }
 
 // The column kernel's paired variant without checksums (4 waves per SIMD)
-// pays from 128 tiles per CU; below, the plain variant runs the same programs
-// (Ring AllReduce fp32 8 x 16 MiB, 64 tiles per CU: 0.0422 ms plain, 0.0446 ms
-// paired).
+// and the capped batched ones pay from 128 tiles per CU; below, the plain
+// variants run the same programs (Ring AllReduce fp32 8 x 16 MiB, 64 tiles per
+// CU: 0.0422 ms plain, 0.0446 ms paired).
 void fit_col_variant(ColPlan& p, uint32_t cus) {
-  if (p.ok && p.v.accs < 0 && col_tile_count(p) < uint64_t(cus) * 128u) p.v.accs = 0;
+  if (!p.ok || (p.v.accs >= 0 && !p.v.capped) || col_tile_count(p) >= uint64_t(cus) * 128u) return;
+  if (p.v.accs < 0) p.v.accs = 0;
+  p.v.capped = false;
 }
 
 // Column kernel: nontemporal loads and stores once the call's buffers exceed
@@ -1100,7 +1102,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       dbg += " | columns: " + std::to_string(cd->plan.segs.size()) + " segments, grid " + std::to_string(L.grid) +
              " tiles " + std::to_string(cd->tiles) + " unit " + std::to_string(L.v.unit) + " slots " +
              std::to_string(L.v.leaves) + (L.v.accs > 0 ? " checksum ops " + std::to_string(L.v.accs) : "") +
-             (L.v.accs < 0 ? " paired" : "") +
+             (L.v.accs < 0 ? " paired" : "") + (L.v.capped ? " capped" : "") +
              (L.v.batched ? " batched" : "") + (L.nt ? " nontemporal" : "");
   } else {
     for (size_t pi = copy_part ? 1 : 0; pi < b.phases.size(); ++pi) {
@@ -1240,7 +1242,7 @@ coll_status_t run(coll_kind_t kind, void* const* send, void* const* recv, int N,
       a.code = L.code;
       a.partial = partial;
       a.p = ptrs;
-      he = launch_col(a, N, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.v.batched, L.nt, L.grid, stream);
+      he = launch_col(a, N, dt, int(op), L.v.unit, L.v.leaves, L.v.accs, L.v.batched, L.v.capped, L.nt, L.grid, stream);
       if (he != hipSuccess) return hip_fail(he, "column kernel launch");
     } else if (L.kind == Launch::COPY) {
       CopyRowsArgs a{};
@@ -1462,7 +1464,8 @@ coll_status_t run_noalloc(void* const* send, void* const* recv, int N, size_t co
                : int(dtype) == COLL_FLOAT32 ? DT_F32 : DT_BF16;
   const uint32_t grid = uint32_t(cur.tables.work.size());
   if (grid) {
-    he = launch_col(a, N, dt, int(op), cur.plan.v.unit, cur.plan.v.leaves, cur.plan.v.accs, cur.plan.v.batched, nt,
+    he = launch_col(a, N, dt, int(op), cur.plan.v.unit, cur.plan.v.leaves, cur.plan.v.accs, cur.plan.v.batched,
+                    cur.plan.v.capped, nt,
                      grid, stream);
     if (he != hipSuccess) return hip_fail(he, "column kernel launch");
   }

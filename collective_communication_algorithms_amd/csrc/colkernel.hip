@@ -472,8 +472,7 @@ ColFn<P> col_fn_nt(bool nt) {
 }
 
 // Unbatched programs hold at most 8 slots; accs -1: no checksums, leaves in
-// pairs, at most 16 work groups per CU (batched: the plain batched kernel,
-// fewer work groups per CU); checksums of up to 8 ops: merged
+// pairs, at most 16 work groups per CU; checksums of up to 8 ops: merged
 // wave sums, the leaves in pairs (one leaf: alone); 9 .. 16 ops: a per-lane
 // file; more: merged wave sums.  Batched programs: 8 slots, or 16 with slots
 // 8 and up in LDS; checksums: merged wave sums.
@@ -521,8 +520,8 @@ ColFn<P> pick_col(int dtype, int op, int leaves, int accs, bool batched, bool nt
 }
 
 template <int P>
-hipError_t launch_col_p(const ColArgs& a, int dtype, int op, int leaves, int accs, bool batched, bool nt,
-                        uint32_t grid, hipStream_t stream) {
+hipError_t launch_col_p(const ColArgs& a, int dtype, int op, int leaves, int accs, bool batched, bool capped,
+                        bool nt, uint32_t grid, hipStream_t stream) {
   ColLaunchArgs<P> c;
   c.work = a.work;
   c.code = a.code;
@@ -531,10 +530,10 @@ hipError_t launch_col_p(const ColArgs& a, int dtype, int op, int leaves, int acc
     c.send[i] = a.p.send[i];
     c.recv[i] = a.p.recv[i];
   }
-  // the variants without checksums for many-store programs reserve LDS they
-  // never touch, so that a CU holds fewer of their work groups: unbatched at
-  // most 16 (4 waves per SIMD), batched fewer still
-  const size_t lds = accs >= 0 ? 0 : batched ? COL_BATCHED_CAP_LDS : COL_PAIRED_LDS;
+  // the variants for many-store programs reserve LDS they never touch, so
+  // that a CU holds fewer of their work groups: the paired one at most 16 (4
+  // waves per SIMD), capped batched ones fewer still
+  const size_t lds = accs < 0 ? COL_PAIRED_LDS : capped ? COL_BATCHED_CAP_LDS : 0;
   hipLaunchKernelGGL(pick_col<P>(dtype, op, leaves, accs, batched, nt), dim3(grid), dim3(COL_THREADS), lds, stream, c);
   return hipGetLastError();
 }
@@ -569,11 +568,11 @@ hipError_t noalloc_scratch(void** out) {
 }
 
 hipError_t launch_col(const ColArgs& a, int nranks, int dtype, int op, int unit, int leaves, int accs, bool batched,
-                      bool nt, uint32_t grid, hipStream_t stream) {
+                      bool capped, bool nt, uint32_t grid, hipStream_t stream) {
   (void)unit;  // every variant takes 16-byte units
   if (nranks < 1 || nranks > COL_THREADS) return hipErrorInvalidValue;
-  if (nranks <= 16 && !batched) return launch_col_p<16>(a, dtype, op, leaves, accs, batched, nt, grid, stream);
-  return launch_col_p<64>(a, dtype, op, leaves, accs, batched, nt, grid, stream);
+  if (nranks <= 16 && !batched) return launch_col_p<16>(a, dtype, op, leaves, accs, batched, capped, nt, grid, stream);
+  return launch_col_p<64>(a, dtype, op, leaves, accs, batched, capped, nt, grid, stream);
 }
 
 hipError_t launch_gather_sums(const uint32_t* idx, const uint64_t* src, uint64_t* out, uint64_t n,

@@ -59,20 +59,24 @@ uint32_t row_shift(const Row& r, int sz) { return uint32_t((((-(r.dst_off * sz))
 // small column spaces (abi.cpp: fit_col_variant); programs of one leaf or one
 // store keep the plain variant's occupancy.
 // Batched programs of 8 or more stores (AllReduces over 9-64 ranks) likewise
-// run without checksums at fewer work groups per CU (reserved LDS): Ring
-// AllReduce fp32 16 x 64 MiB 0.384 -> 0.360 ms, halving-doubling 32 x 64 MiB
-// 0.811 -> 0.751, Ring 64 x 64 MiB 1.603 -> 1.572; one-store programs
-// (ReduceScatter) lose (64 x 256 MiB bf16 2.96 -> 3.91 ms).
+// run at fewer work groups per CU (`capped`: reserved LDS).  Without
+// checksums: Ring AllReduce fp32 16 x 64 MiB 0.384 -> 0.360 ms,
+// halving-doubling 32 x 64 MiB 0.811 -> 0.751, Ring 64 x 64 MiB 1.603 ->
+// 1.572; with them: 0.412 -> 0.395, 0.819 -> 0.809, 1.796 -> 1.770 ms.
+// One-store programs (ReduceScatter) lose (64 x 256 MiB bf16 2.96 -> 3.91 ms
+// without checksums, 3.24 -> 3.40 ms with).
 const ColVariant kVariants[] = {{16, 8, -1, false, COL_LIST_MAX_STORES, 8, 2},
                                 {16, 8, 0, false},
                                 {16, 1, 8, false},
                                 {16, 8, 8, false, 2},
                                 {16, 8, 16, false},
                                 {16, 8, 64, false},
-                                {16, 8, -1, true, COL_LIST_MAX_STORES, 8, 2},
-                                {16, 16, -1, true, COL_LIST_MAX_STORES, 8, 2},
+                                {16, 8, 0, true, COL_LIST_MAX_STORES, 8, 2, true},
+                                {16, 16, 0, true, COL_LIST_MAX_STORES, 8, 2, true},
                                 {16, 8, 0, true},
                                 {16, 16, 0, true},
+                                {16, 8, 64, true, COL_LIST_MAX_STORES, 8, 2, true},
+                                {16, 16, 64, true, COL_LIST_MAX_STORES, 8, 2, true},
                                 {16, 8, 64, true},
                                 {16, 16, 64, true}};
 

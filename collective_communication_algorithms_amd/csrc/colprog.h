@@ -29,6 +29,7 @@ struct ColVariant {
   bool batched = false;
   int stores = COL_LIST_MAX_STORES;  // the variant is picked for programs of at most this many stores
   int min_stores = 0, min_leaves = 0;  // ... and of at least this many stores and leaves
+  bool capped = false;          // batched: launched with reserved LDS, fewer work groups per CU
 };
 
 // With checksums: row `row`'s checksum over segment `seg` is the sum of op

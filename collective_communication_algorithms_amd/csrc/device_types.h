@@ -134,8 +134,8 @@ constexpr uint32_t COL_BATCH = 8;
 // (and never touches): 160 KiB per CU hold 16 such work groups, 4 waves per
 // SIMD, where its registers alone would allow 8
 constexpr uint32_t COL_PAIRED_LDS = 10240;
-// The same for batched programs without checksums that store 8 or more
-// buffers (AllReduces over 9-64 ranks), on top of their own LDS slots
+// The same for batched programs that store 8 or more buffers (AllReduces over
+// 9-64 ranks), with or without checksums, on top of their own LDS slots
 constexpr uint32_t COL_BATCHED_CAP_LDS = 13312;
 
 struct ColInstr {        // 8 bytes

@@ -38,7 +38,7 @@ hipError_t launch_spin(float* out, uint32_t iters, uint32_t grid, hipStream_t st
 // loads and stores when `nt`; one work group of COL_THREADS per ColWork; the
 // first nranks (1 .. COL_THREADS) addresses of a.p are passed
 hipError_t launch_col(const ColArgs& a, int nranks, int dtype, int op, int unit, int leaves, int accs, bool batched,
-                      bool nt, uint32_t grid, hipStream_t stream);
+                      bool capped, bool nt, uint32_t grid, hipStream_t stream);
 // out[r] = the sum of the partial slots row r's ColRefs name, r < nrows, by way
 // of tmp (nrows * COL_FOLD_SLICES slots)
 hipError_t launch_col_fold(const ColRef* refs, const uint32_t* row_off, const uint64_t* partial, uint64_t* tmp,
