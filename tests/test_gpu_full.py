@@ -147,6 +147,20 @@ def test_alltoall_n32_512x4096(algo):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("algo,N,checksums", [("ring", 8, False), ("ring", 16, False), ("ring", 16, True),
+                                              ("rhd", 32, True)])
+def test_allreduce_at_fewer_work_groups_per_cu(algo, N, checksums):
+    """The column kernel's variants that run at fewer work groups per CU engage
+    from 128 tiles per CU, 32 MiB of columns per rank: the paired one (8 ranks,
+    no checksums) and the capped batched ones (16 and 32 ranks, with and
+    without checksums).  int32 at exactly that size: whole buffers and every
+    row checksum bit for bit against the oracle."""
+    from tests.gpu_util import assert_parity
+    count = (32 << 20) // 4
+    a = si.rank_arrays(40 + N, N, count, "int32")
+    assert_parity("allreduce", algo, a, "int32", checksums=checksums)
+
+
 @pytest.mark.parametrize("algo", ["pairwise", "bruck", "ring"])
 def test_alltoall_row_checksums_n32_128MiB(algo):
     """C5 at full size with row checksums, in the default launch (every
